@@ -1,0 +1,188 @@
+"""Benchmark: decode throughput of block-quantized projections on one MI355X.
+
+Default workload: a Llama-3-8B-shaped decode step over 32 layers of Q4_K projections at batch 1
+(per layer q 4096->4096, k/v 4096->1024, o 4096->4096, gate/up 4096->14336, SwiGLU,
+down 14336->4096), seeded synthetic weights and N(0,1) activations resident in HBM.
+One step = every projection of every layer plus the SwiGLU, through the C ABI.
+
+Prints one JSON line: tokens/s for the whole step, the roofline of the dominant kernel (the
+Q4_K GEMV; achieved = algorithmic bytes / its average launch time measured with HIP events on
+the launch stream), and the CPU oracle timed on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "Q4_K GEMV HBM GB/s (% of peak); decode tokens/s for 8B-shaped and MoE layers"
+
+
+def _args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--batch", type=int, default=1, help="tokens per decode step (1 or 8)")
+    p.add_argument("--seed", type=int, default=42)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="approximate CPU time budget of the oracle sample")
+    return p.parse_args()
+
+
+def build_dense_model(tq, synth, torch, batch, seed):
+    shape = synth.LLAMA8B
+    layers = []
+    for layer in range(shape["layers"]):
+        projs = {}
+        for name, n, k in synth.dense_projections(shape):
+            w = synth.blob("q4_k", synth.rng(seed, "8b", layer, name), n, k)
+            projs[name] = (torch.from_numpy(w).to("cuda"), n, k)
+        g = synth.rng(seed, "8b-act", layer, batch)
+        x = torch.from_numpy(synth.normal_f32(g, (batch, shape["hidden"]))).to("cuda")
+        a = torch.from_numpy(synth.normal_f32(g, (batch, shape["hidden"]))).to("cuda")
+        layers.append((projs, x, a))
+    return layers
+
+
+def make_step(tq, torch, layers, batch, events=None):
+    H = 4096
+    F = 14336
+    dev = "cuda"
+    bufs = dict(q=torch.empty(batch, H, device=dev), k=torch.empty(batch, 1024, device=dev),
+                v=torch.empty(batch, 1024, device=dev), o=torch.empty(batch, H, device=dev),
+                gate=torch.empty(batch, F, device=dev), up=torch.empty(batch, F, device=dev),
+                h=torch.empty(batch, F, device=dev), down=torch.empty(batch, H, device=dev))
+
+    def gemv(name, projs, x):
+        w, n, k = projs[name]
+        if events is not None:
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            tq.gemv("q4_k", w, n, k, x, out=bufs[name])
+            e.record()
+            events.append((s, e, w.numel() + 4 * batch * (n + k)))
+        else:
+            tq.gemv("q4_k", w, n, k, x, out=bufs[name])
+
+    def step():
+        for projs, x, a in layers:
+            gemv("q", projs, x)
+            gemv("k", projs, x)
+            gemv("v", projs, x)
+            gemv("o", projs, a)
+            gemv("gate", projs, x)
+            gemv("up", projs, x)
+            tq.swiglu(bufs["gate"], bufs["up"], out=bufs["h"])
+            gemv("down", projs, bufs["h"])
+
+    return step
+
+
+def cpu_baseline(synth, batch, seed, budget_s):
+    """The oracle (as it is) on a bounded sample of the same step: a growing subset of the
+    output rows of layer 0's seven projections, scaled to a full 32-layer step."""
+    import numpy as np
+
+    import oracle
+
+    shape = synth.LLAMA8B
+    projs = []
+    for name, n, k in synth.dense_projections(shape):
+        w = synth.blob("q4_k", synth.rng(seed, "8b", 0, name), n, k)
+        x = synth.normal_f32(synth.rng(seed, "cpu-x", name, batch), (batch, k))
+        projs.append((name, w, n, k, x))
+    total_rows = sum(n for _, _, n, _, _ in projs)
+    frac = 1.0 / 64
+    elapsed = 0.0
+    while True:
+        t0 = time.perf_counter()
+        rows_done = 0
+        for name, w, n, k, x in projs:
+            r = max(1, int(n * frac))
+            oracle.gemv("q4_k", w, n, k, x, rows=np.arange(r))
+            rows_done += r
+        elapsed = time.perf_counter() - t0
+        if elapsed * 2 > budget_s or frac >= 1.0:
+            break
+        frac = min(1.0, frac * 2)
+    layer_s = elapsed * total_rows / rows_done
+    step_s = layer_s * shape["layers"]
+    return {"value": batch / step_s, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{rows_done} of {total_rows} output rows of one layer's 7 Q4_K projections "
+                      f"at batch {batch} ({elapsed:.1f} s), scaled linearly to 32 layers"}
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(no multi-GPU path in this build)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import moe_expert_ffn_q4_amd as tq
+    import synth
+
+    torch.cuda.set_device(0)
+    layers = build_dense_model(tq, synth, torch, args.batch, args.seed)
+    step = make_step(tq, torch, layers, args.batch)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1000 / args.steps
+    tokens_s = args.batch * args.steps / elapsed
+
+    # Roofline of the Q4_K GEMV: the same steps again, each GEMV launch bracketed by events
+    events = []
+    istep = make_step(tq, torch, layers, args.batch, events=events)
+    for _ in range(min(args.steps, 5)):
+        istep()
+    torch.cuda.synchronize()
+    kernel_s = sum(s.elapsed_time(e) for s, e, _ in events) / 1000
+    kernel_bytes = sum(b for _, _, b in events)
+    achieved = kernel_bytes / kernel_s / 1e9
+    step_bytes = sum(b for _, _, b in events) / min(args.steps, 5)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q4_k weights, f32 activations and accumulation",
+        "data": "synthetic (seeded random Q4_K blocks, N(0,1) activations)",
+        "config": {"workload": f"llama3-8b-shaped decode, 32 layers x 7 Q4_K projections + "
+                               f"SwiGLU, batch {args.batch}",
+                   "global_batch": args.batch, "seq_len": 1, "parallelism": "none (1 GPU)"},
+        "step_gbs": round(step_bytes / (ms_per_step / 1000) / 1e9, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "tq::k_gemv<Q4_K>", "avg_launch_us": round(kernel_s * 1e6 / len(events), 3)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(synth, args.batch, args.seed, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

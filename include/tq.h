@@ -1,0 +1,102 @@
+/*
+ * tq.h -- C ABI of libtq: block-quantized decode products and top-k MoE expert FFNs on gfx950.
+ *
+ * The operations follow the problem the pages state for decoding large quantized models: a
+ * block-quantized weight blob plus activations in, projected activations (or the routed MoE
+ * output) out ("Titan Engine" page (zingnex.cn), sections "Aggressive quantization" and "MoE
+ * expert streaming"; KTransformers page (news.fishai.com.cn), the part on quantized GPU
+ * matmul kernels and MoE expert handling; "Show HN: Llama 3.1 70B on a single RTX 3090 via
+ * NVMe-to-GPU bypassing the CPU" page (hn.213312.xyz), "Quantization support").
+ *
+ * Block formats (GGUF block layouts, little-endian; the pages name the formats, not the bits):
+ *   TQ_Q4_K  256 weights / 144 bytes: d fp16, dmin fp16, 12 bytes of packed 6-bit scales and
+ *            mins, 128 bytes of 4-bit quants; w = d*sc*q - dmin*m.
+ *   TQ_Q6_K  256 weights / 210 bytes: 128 bytes low 4 bits, 64 bytes high 2 bits, 16 int8
+ *            scales, d fp16; w = d*sc*(q - 32).
+ *   TQ_Q8_0  32 weights / 34 bytes: d fp16, 32 int8 quants; w = d*q.
+ * A weight matrix is n rows ("out") by k columns ("in"), stored row-major as n rows of k/B
+ * consecutive blocks (B = weights per block), i.e. n * tq_row_bytes(type, k) bytes.
+ *
+ * Conventions for every call below:
+ *   - Pointers are device pointers (memory the caller allocated on the current HIP device)
+ *     unless stated otherwise. The caller owns every buffer; the library allocates nothing.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Every call only
+ *     enqueues work on it and returns; results are ready when the stream is synchronized.
+ *   - Arguments are checked before anything is enqueued. On a non-TQ_OK status nothing was
+ *     enqueued and no output was touched; tq_last_error() returns a description (thread-local).
+ *   - A device fault inside a kernel surfaces at the caller's next synchronization (HIP rules).
+ *   - Activations and outputs are fp32, token-major: x[t][k], y[t][n].
+ *   - Calls on one stream are deterministic: the same inputs give bitwise-identical outputs.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { TQ_Q4_K = 1, TQ_Q6_K = 2, TQ_Q8_0 = 3 };                 /* block formats */
+enum { TQ_F32 = 0, TQ_BF16 = 1 };                                /* dequant output types */
+enum {                                                           /* status codes */
+  TQ_OK = 0,
+  TQ_EINVAL = 1,       /* null pointer, unknown enum value, negative count */
+  TQ_ESHAPE = 2,       /* k not a multiple of the block size, n/batch/tokens out of range */
+  TQ_EALIGN = 3,       /* a pointer is not aligned as required */
+  TQ_ENOSPC = 4,       /* workspace smaller than tq_moe_workspace_bytes() */
+  TQ_EUNSUPPORTED = 5, /* valid request this build does not handle */
+  TQ_EDEVICE = 6       /* a HIP runtime call failed (launch, copy, event) */
+};
+enum { TQ_PATH_AUTO = 0, TQ_PATH_F32 = 1, TQ_PATH_BF16_MFMA = 2 }; /* MoE expert-product path */
+
+/* Weights per block (256, 256, 32) and bytes per block (144, 210, 34); 0 for an unknown type. */
+int64_t tq_block_weights(int type);
+int64_t tq_block_bytes(int type);
+/* Bytes of one row of k weights; -1 if type is unknown or k is not a multiple of the block. */
+int64_t tq_row_bytes(int type, int64_t k);
+
+/*
+ * tq_dequant -- expand a blob to dense values (the block decode of the formats above).
+ *   w     [n rows of tq_row_bytes(type,k)] blob, 16-byte aligned.
+ *   out   [n][k] of out_type: TQ_F32 holds each weight's exact value rounded once to nearest
+ *         even (bitwise equal to the exact value for Q6_K and Q8_0); TQ_BF16 holds the
+ *         nearest-even bf16 rounding of that fp32 value, as uint16 bit patterns. 4-byte aligned.
+ *   n >= 0, k >= 0 with k % tq_block_weights(type) == 0; n*k == 0 enqueues nothing.
+ */
+int tq_dequant(int type, const void *w, int64_t n, int64_t k, int out_type, void *out,
+               void *stream);
+
+/*
+ * tq_gemv -- y[t][r] = sum_c w[r][c] * x[t][c] for t < batch, r < n (decode-time GEMV and
+ * small-batch GEMM over quantized weights), fp32 multiply-adds.
+ *   w          blob of n x k weights, 16-byte aligned.
+ *   x          [batch][k] fp32, 4-byte aligned; y [batch][n] fp32, 4-byte aligned; y must not
+ *              overlap w or x.
+ *   workspace  device scratch of at least tq_gemv_workspace_bytes(type, n, k, batch) bytes,
+ *              256-byte aligned, contents irrelevant; it lets the k dimension be split across
+ *              workgroups (partial sums are added by a second kernel in a fixed order, so results
+ *              stay deterministic). NULL or too small: no split (slower when n is small).
+ *              Calls that run concurrently must not share a workspace.
+ *   n >= 1, k >= block size with k % block == 0, 1 <= batch <= 4096. Weights are streamed once
+ *   per group of up to 8 tokens.
+ */
+size_t tq_gemv_workspace_bytes(int type, int64_t n, int64_t k, int64_t batch);
+int tq_gemv(int type, const void *w, int64_t n, int64_t k, const float *x, int64_t batch,
+            float *y, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * tq_swiglu -- h[i] = silu(g[i]) * u[i], silu(z) = z / (1 + exp(-z)), for i < count (the
+ * gated activation between a SwiGLU FFN's gate/up and down projections). fp32, 4-byte
+ * aligned; h may alias g or u. count >= 0.
+ */
+int tq_swiglu(const float *g, const float *u, int64_t count, float *h, void *stream);
+
+/* Text of the last non-TQ_OK status returned on this thread ("" if none). */
+const char *tq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,165 @@
+"""Python binding of libtq (block-quantized decode GEMV and top-k MoE expert FFN on gfx950).
+
+Argument marshalling only: every call forwards device pointers, sizes and the current HIP stream
+to the C ABI declared in ``include/tq.h``; all computation happens in the library's kernels.
+PyTorch supplies device memory and streams. The library must be built
+(``python -m moe_expert_ffn_q4_amd.build``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtq.so")
+
+Q4_K, Q6_K, Q8_0 = 1, 2, 3
+TYPES = {"q4_k": Q4_K, "q6_k": Q6_K, "q8_0": Q8_0}
+F32, BF16 = 0, 1
+PATH_AUTO, PATH_F32, PATH_BF16_MFMA = 0, 1, 2
+STATUS = {0: "TQ_OK", 1: "TQ_EINVAL", 2: "TQ_ESHAPE", 3: "TQ_EALIGN", 4: "TQ_ENOSPC",
+          5: "TQ_EUNSUPPORTED", 6: "TQ_EDEVICE"}
+
+
+class TQError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """The loaded libtq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libtq.so not found at {LIB_PATH}; build it with "
+                               "`python -m moe_expert_ffn_q4_amd.build`")
+        _lib = C.CDLL(LIB_PATH)
+        _declare(_lib)
+    return _lib
+
+
+_vp, _i64, _int = C.c_void_p, C.c_int64, C.c_int
+
+
+class Expert(C.Structure):
+    _fields_ = [("gate", _vp), ("up", _vp), ("down", _vp)]
+
+
+class MoeDesc(C.Structure):
+    _fields_ = [("type", _int), ("hidden", _i64), ("ffn", _i64), ("n_experts", _i64),
+                ("top_k", _i64), ("router_w", _vp), ("experts", C.POINTER(Expert)),
+                ("shared", C.POINTER(Expert)), ("renormalize", _int),
+                ("experts_on_host", _int), ("copy_stream", _vp), ("path", _int)]
+
+
+class MoeRouting(C.Structure):
+    _fields_ = [("topk_ids", _vp), ("topk_w", _vp), ("logits", _vp), ("counts", _vp),
+                ("offsets", _vp), ("pairs", _vp)]
+
+
+def _declare(L: C.CDLL) -> None:
+    L.tq_block_weights.argtypes = [_int]
+    L.tq_block_weights.restype = _i64
+    L.tq_block_bytes.argtypes = [_int]
+    L.tq_block_bytes.restype = _i64
+    L.tq_row_bytes.argtypes = [_int, _i64]
+    L.tq_row_bytes.restype = _i64
+    L.tq_last_error.argtypes = []
+    L.tq_last_error.restype = C.c_char_p
+    L.tq_dequant.argtypes = [_int, _vp, _i64, _i64, _int, _vp, _vp]
+    L.tq_dequant.restype = _int
+    L.tq_gemv_workspace_bytes.argtypes = [_int, _i64, _i64, _i64]
+    L.tq_gemv_workspace_bytes.restype = C.c_size_t
+    L.tq_gemv.argtypes = [_int, _vp, _i64, _i64, _vp, _i64, _vp, _vp, C.c_size_t, _vp]
+    L.tq_gemv.restype = _int
+    L.tq_swiglu.argtypes = [_vp, _vp, _i64, _vp, _vp]
+    L.tq_swiglu.restype = _int
+    if hasattr(L, "tq_moe_ffn"):
+        L.tq_moe_workspace_bytes.argtypes = [C.POINTER(MoeDesc), _i64]
+        L.tq_moe_workspace_bytes.restype = C.c_size_t
+        L.tq_moe_ffn.argtypes = [C.POINTER(MoeDesc), _vp, _i64, _vp, _vp, C.c_size_t,
+                                 C.POINTER(MoeRouting), _vp]
+        L.tq_moe_ffn.restype = _int
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise TQError(rc, lib().tq_last_error().decode())
+
+
+def _type(t) -> int:
+    return TYPES[t] if isinstance(t, str) else int(t)
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else t.data_ptr()
+
+
+def row_bytes(t, k: int) -> int:
+    return int(lib().tq_row_bytes(_type(t), k))
+
+
+def dequant(t, w: torch.Tensor, n: int, k: int, out_dtype: str = "f32", out=None, stream=None):
+    """Dense [n][k] weights: fp32 values, or bf16 bit patterns as int16 ('bf16')."""
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.float32 if out_dtype == "f32" else torch.int16,
+                          device=w.device)
+    _check(lib().tq_dequant(_type(t), _ptr(w), n, k, F32 if out_dtype == "f32" else BF16,
+                            _ptr(out), _stream(stream)))
+    return out
+
+
+_workspaces: dict = {}
+
+
+def workspace(nbytes: int, device=None) -> torch.Tensor:
+    """A zero-filled device scratch buffer of at least nbytes, reused across calls (one per
+    device; calls on one stream may share it)."""
+    dev = torch.device(device if device is not None else "cuda")
+    if dev.index is None:
+        dev = torch.device(dev.type, torch.cuda.current_device())
+    key = (dev.type, dev.index)
+    buf = _workspaces.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        _workspaces[key] = buf
+    return buf
+
+
+def gemv_workspace_bytes(t, n: int, k: int, batch: int) -> int:
+    return int(lib().tq_gemv_workspace_bytes(_type(t), n, k, batch))
+
+
+def gemv(t, w: torch.Tensor, n: int, k: int, x: torch.Tensor, out=None, ws=None, stream=None):
+    """y[b][r] = sum_c W[r][c] x[b][c] for x of shape [batch, k] (or [k]); fp32.
+
+    ws: workspace tensor (default: the shared per-device buffer); pass False for none.
+    """
+    x2 = x.reshape(-1, k)
+    batch = x2.shape[0]
+    if out is None:
+        out = torch.empty((batch, n), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = workspace(gemv_workspace_bytes(t, n, k, batch), x.device)
+    wsp, wsn = (None, 0) if ws is False else (ws.data_ptr(), ws.numel() * ws.element_size())
+    _check(lib().tq_gemv(_type(t), _ptr(w), n, k, _ptr(x2), batch, _ptr(out), wsp, wsn,
+                         _stream(stream)))
+    return out
+
+
+def swiglu(g: torch.Tensor, u: torch.Tensor, out=None, stream=None):
+    if out is None:
+        out = torch.empty_like(g)
+    _check(lib().tq_swiglu(_ptr(g), _ptr(u), g.numel(), _ptr(out), _stream(stream)))
+    return out

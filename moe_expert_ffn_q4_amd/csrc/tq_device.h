@@ -1,0 +1,49 @@
+// tq_device.h -- small device helpers shared by the libtq kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+// Four dwords, 16-byte aligned.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// Four dwords loaded with only 4-byte alignment guaranteed (rows of Q6_K / Q8_0 blobs).
+typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+// IEEE binary16 bits (low 16 bits of `bits`) -> fp32. Exact; subnormals are kept because HIP
+// kernels run with fp16 denormals enabled.
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFFFu));
+}
+
+// Byte e (0..3) of w as an fp32 integer value (compiles to v_cvt_f32_ubyteN).
+__device__ __forceinline__ float byte_to_float(uint32_t w, int e) {
+  return (float)((w >> (8 * e)) & 0xFFu);
+}
+
+// w with what the compiler knows about its bits forgotten. After masking a dword down to four
+// nibbles, this keeps the four byte conversions as one v_cvt_f32_ubyteN each; otherwise the
+// compiler re-derives each nibble with its own shift/mask before converting.
+__device__ __forceinline__ uint32_t opaque(uint32_t w) {
+  asm("" : "+v"(w));
+  return w;
+}
+
+// The dword that starts two bytes into the 8-byte pair (hi:lo).
+__device__ __forceinline__ uint32_t shift2(uint32_t lo, uint32_t hi) {
+  return __builtin_amdgcn_alignbyte(hi, lo, 2);
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint16_t float_to_bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  uint32_t lsb = (u >> 16) & 1u;
+  return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+}  // namespace tq

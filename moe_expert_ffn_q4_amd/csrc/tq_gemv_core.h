@@ -1,0 +1,414 @@
+// tq_gemv_core.h -- the streaming core shared by the dense GEMV and the grouped expert GEMV.
+//
+// Mapping (gfx950, wave64): one lane owns one output row; a wave owns 64 consecutive rows and
+// walks a contiguous range of 256-weight "units" of those rows (one Q4_K or Q6_K block, or
+// eight Q8_0 blocks). Every lane streams its own row with 16-byte loads while the activation
+// values are the same for all 64 lanes, so they come through scalar loads and feed the FMAs as
+// SGPR operands: no LDS traffic and no VGPRs for activations in the inner loop. Per weight the
+// inner loop costs one byte->float convert and one FMA per token, plus a mask per 4 weights.
+//
+// The affine block terms are factored out of the inner loop:
+//   sum_i w_i x_i = sum_j d*sc_j * sum_{i in j} q_i x_i  -  sum_j dmin*m_j * S_j     (Q4_K)
+//   sum_i w_i x_i = sum_s d*sc_s * (sum_{i in s} q_i x_i - 32 * S_s)                (Q6_K)
+//   sum_i w_i x_i = sum_b d_b * (sum_{i in b} (q_i + 128) x_i - 128 * S_b)          (Q8_0)
+// where S is the sum of x over the 32- (or 16-) weight group. The group sums of the tile's
+// tokens are computed once per workgroup into LDS and read with wave-uniform addresses.
+#pragma once
+
+#include "tq_device.h"
+
+namespace tq {
+
+enum { FMT_Q4_K = 1, FMT_Q6_K = 2, FMT_Q8_0 = 3 };
+
+template <int FMT>
+struct Fmt;
+template <>
+struct Fmt<FMT_Q4_K> {
+  static constexpr int unit_bytes = 144;  // one block
+  static constexpr int group = 32;        // x-sum group (sub-block)
+};
+template <>
+struct Fmt<FMT_Q6_K> {
+  static constexpr int unit_bytes = 210;  // one block
+  static constexpr int group = 16;        // one int8 scale per 16 weights
+};
+template <>
+struct Fmt<FMT_Q8_0> {
+  static constexpr int unit_bytes = 272;  // eight 34-byte blocks
+  static constexpr int group = 32;        // one block
+};
+
+// Raw bytes of one unit of one row, as loaded.
+template <int FMT>
+struct Unit;
+template <>
+struct Unit<FMT_Q4_K> {
+  u32x4 v[9];
+};
+template <>
+struct Unit<FMT_Q6_K> {
+  uint32_t v[53];  // v[0..51]: block bytes 0..207 (after realignment); v[52]: d in low half
+};
+template <>
+struct Unit<FMT_Q8_0> {
+  uint32_t v[68];
+};
+
+// ---- loads ---------------------------------------------------------------------------------
+
+// Q4_K: the block starts at a multiple of 144 bytes from a 16-byte aligned row start.
+__device__ __forceinline__ void load_unit(Unit<FMT_Q4_K> &u, const uint8_t *row, int idx) {
+  const u32x4 *p = reinterpret_cast<const u32x4 *>(row + (size_t)idx * 144);
+#pragma unroll
+  for (int i = 0; i < 9; ++i) u.v[i] = *(p + i);
+}
+
+// Q6_K: row start is 4-byte aligned; block idx starts at 210*idx, i.e. two bytes past a dword
+// boundary for odd idx. The 208 bytes before the fp16 d are loaded as 52 dwords from the dword
+// boundary at or below the block start (never before the row start, never past the block end)
+// and shifted down by two bytes when needed; d itself is loaded as a 16-bit value.
+__device__ __forceinline__ void load_unit(Unit<FMT_Q6_K> &u, const uint8_t *row, int idx) {
+  const int off = idx * 210;
+  const uint8_t *base = row + (off & ~3);
+  const u32x4a4 *p = reinterpret_cast<const u32x4a4 *>(base);
+  uint32_t r[53];
+#pragma unroll
+  for (int i = 0; i < 13; ++i) {
+    u32x4a4 t = *(p + i);
+    r[4 * i + 0] = t.x;
+    r[4 * i + 1] = t.y;
+    r[4 * i + 2] = t.z;
+    r[4 * i + 3] = t.w;
+  }
+  const uint32_t dbits = *reinterpret_cast<const uint16_t *>(row + off + 208);
+  if (off & 2) {  // wave-uniform: every lane is at the same block index
+    r[52] = *reinterpret_cast<const uint32_t *>(base + 208);
+#pragma unroll
+    for (int i = 0; i < 52; ++i) u.v[i] = shift2(r[i], r[i + 1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 52; ++i) u.v[i] = r[i];
+  }
+  u.v[52] = dbits;
+}
+
+// Q8_0: eight blocks (272 bytes) starting at a multiple of 272 from a 16-byte aligned row
+// start (k is a multiple of 256).
+__device__ __forceinline__ void load_unit(Unit<FMT_Q8_0> &u, const uint8_t *row, int idx) {
+  const u32x4 *p = reinterpret_cast<const u32x4 *>(row + (size_t)idx * 272);
+#pragma unroll
+  for (int i = 0; i < 17; ++i) {
+    u32x4 t = *(p + i);
+    u.v[4 * i + 0] = t.x;
+    u.v[4 * i + 1] = t.y;
+    u.v[4 * i + 2] = t.z;
+    u.v[4 * i + 3] = t.w;
+  }
+}
+
+// ---- per-unit arithmetic -------------------------------------------------------------------
+
+// `off`, but only known to the compiler once `dep` has been computed: the scalar activation
+// loads addressed with it cannot be hoisted far ahead of their use (which would need more
+// scalar registers than a wave has).
+__device__ __forceinline__ int after(int off, float dep) {
+  asm volatile("" : "+s"(off) : "v"(dep));
+  return off;
+}
+
+__device__ __forceinline__ uint32_t dword_of(const u32x4 &v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// sum_e f[e] * x[e] over 16 / 32 values; x is wave-uniform (scalar loads). Two chains.
+__device__ __forceinline__ float dot16(const float (&f)[16], const float *x) {
+  float a = 0.f, b = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; e += 2) {
+    a = __builtin_fmaf(f[e], x[e], a);
+    b = __builtin_fmaf(f[e + 1], x[e + 1], b);
+  }
+  return a + b;
+}
+__device__ __forceinline__ float dot32(const float (&f)[32], const float *x) {
+  float a = 0.f, b = 0.f;
+#pragma unroll
+  for (int e = 0; e < 32; e += 2) {
+    a = __builtin_fmaf(f[e], x[e], a);
+    b = __builtin_fmaf(f[e + 1], x[e + 1], b);
+  }
+  return a + b;
+}
+
+// Q6_K: the 6-bit quants of weights l..l+3 of the four 32-weight groups of one half block, from
+// the low-bit dwords A (groups 0, 2), B (groups 1, 3) and the high-bit dword QH, one per byte.
+__device__ __forceinline__ void q6k_quads(uint32_t A, uint32_t B, uint32_t QH, uint32_t (&q)[4]) {
+  q[0] = opaque((A & 0x0F0F0F0Fu) | ((QH << 4) & 0x30303030u));
+  q[1] = opaque((B & 0x0F0F0F0Fu) | ((QH << 2) & 0x30303030u));
+  q[2] = opaque(((A >> 4) & 0x0F0F0F0Fu) | (QH & 0x30303030u));
+  q[3] = opaque(((B >> 4) & 0x0F0F0F0Fu) | ((QH >> 2) & 0x30303030u));
+}
+
+// xp[t]: wave-uniform pointer to token t's activations at the unit's first weight.
+// gs[t]: wave-uniform LDS pointer to token t's group sums at the unit's first group.
+
+template <int NT>
+__device__ __forceinline__ void unit_dot(const Unit<FMT_Q4_K> &u, const float *const (&xp)[NT],
+                                         const float *const (&gs)[NT], float (&acc)[NT]) {
+  const uint32_t h0 = u.v[0].x, s0 = u.v[0].y, s1 = u.v[0].z, s2 = u.v[0].w;
+  const float d = half_bits_to_float(h0), dmin = half_bits_to_float(h0 >> 16);
+  float sc[8], mn[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    sc[j] = (float)((s0 >> (8 * j)) & 63u);
+    mn[j] = (float)((s1 >> (8 * j)) & 63u);
+    sc[4 + j] = (float)(((s2 >> (8 * j)) & 15u) | (((s0 >> (8 * j + 6)) & 3u) << 4));
+    mn[4 + j] = (float)(((s2 >> (8 * j + 4)) & 15u) | (((s1 >> (8 * j + 6)) & 3u) << 4));
+  }
+  float bs[NT], ms[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    bs[t] = 0.f;
+    ms[t] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ms[t] = __builtin_fmaf(mn[j], gs[t][j], ms[t]);
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    // quant bytes 32c..32c+31: low nibbles are sub-block 2c (weights 64c + 0..31), high
+    // nibbles are sub-block 2c+1 (weights 64c + 32..63), read as 16*q.
+    static_assert(NT == 1, "multi-token Q4_K streams 64-weight groups (stream_q4k_groups)");
+    {
+      float dl = 0.f, dh = 0.f;
+#pragma unroll
+      for (int dw = 0; dw < 8; ++dw) {
+        const uint32_t w = dword_of(u.v[1 + 2 * c + (dw >> 2)], dw & 3);
+        const uint32_t lo = opaque(w & 0x0F0F0F0Fu), hi = opaque(w & 0xF0F0F0F0u);
+        const int i = 64 * c + 4 * dw;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dl = __builtin_fmaf(byte_to_float(lo, e), xp[0][i + e], dl);
+          dh = __builtin_fmaf(byte_to_float(hi, e), xp[0][i + 32 + e], dh);
+        }
+      }
+      bs[0] = __builtin_fmaf(sc[2 * c], dl, bs[0]);
+      bs[0] = __builtin_fmaf(sc[2 * c + 1] * 0.0625f, dh, bs[0]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = __builtin_fmaf(d, bs[t], __builtin_fmaf(-dmin, ms[t], acc[t]));
+}
+
+template <int NT>
+__device__ __forceinline__ void unit_dot(const Unit<FMT_Q6_K> &u, const float *const (&xp)[NT],
+                                         const float *const (&gs)[NT], float (&acc)[NT]) {
+  const float d = half_bits_to_float(u.v[52]);
+  float bs[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) bs[t] = 0.f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int lh = 0; lh < 2; ++lh) {
+      float dot[4][NT];
+      if constexpr (NT == 1) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) dot[g][0] = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = 4 * lh + jj;  // weights l = 4j..4j+3 of each 32-weight group of half h
+          uint32_t q[4];
+          q6k_quads(u.v[16 * h + j], u.v[16 * h + 8 + j], u.v[32 + 8 * h + j], q);
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              dot[g][0] = __builtin_fmaf(byte_to_float(q[g], e), xp[0][128 * h + 32 * g + 4 * j + e],
+                                         dot[g][0]);
+        }
+      } else {
+        float f[4][16];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          uint32_t q[4];
+          const int j = 4 * lh + jj;
+          q6k_quads(u.v[16 * h + j], u.v[16 * h + 8 + j], u.v[32 + 8 * h + j], q);
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f[g][4 * jj + e] = byte_to_float(q[g], e);
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            dot[g][t] = dot16(f[g], xp[t] + 128 * h + 32 * g + 16 * lh);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int s = 8 * h + 2 * g + lh;  // int8 scale index of these 16 weights
+        const uint32_t sw = u.v[48 + (s >> 2)];
+        const float scf = (float)(int32_t)(int8_t)(uint8_t)(sw >> (8 * (s & 3)));
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          bs[t] = __builtin_fmaf(scf, __builtin_fmaf(-32.f, gs[t][s], dot[g][t]), bs[t]);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = __builtin_fmaf(d, bs[t], acc[t]);
+}
+
+template <int NT>
+__device__ __forceinline__ void unit_dot(const Unit<FMT_Q8_0> &u, const float *const (&xp)[NT],
+                                         const float *const (&gs)[NT], float (&acc)[NT]) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+#pragma unroll
+    for (int odd = 0; odd < 2; ++odd) {
+      const int bb = 2 * p + odd;  // block within the unit, bytes 34*bb .. 34*bb+33
+      float d;
+      uint32_t q[8];
+      if (!odd) {  // starts on a dword boundary: d = low half, quants start two bytes in
+        d = half_bits_to_float(u.v[17 * p]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = shift2(u.v[17 * p + i], u.v[17 * p + i + 1]);
+      } else {  // starts two bytes into a dword: d = high half, quants dword-aligned
+        d = half_bits_to_float(u.v[17 * p + 8] >> 16);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = u.v[17 * p + 9 + i];
+      }
+      float dot[NT];
+      if constexpr (NT == 1) {
+        dot[0] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t biased = opaque(q[i] ^ 0x80808080u);  // int8 q -> q + 128 as unsigned bytes
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            dot[0] = __builtin_fmaf(byte_to_float(biased, e), xp[0][32 * bb + 4 * i + e], dot[0]);
+        }
+      } else {
+        float f[32];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t biased = opaque(q[i] ^ 0x80808080u);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f[4 * i + e] = byte_to_float(biased, e);
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          dot[t] = dot32(f, xp[t] + 32 * bb);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        acc[t] = __builtin_fmaf(d, __builtin_fmaf(-128.f, gs[t][bb], dot[t]), acc[t]);
+    }
+  }
+}
+
+// Q4_K with several tokens: stream 64-weight groups (header + 32 quant bytes each) in a loop
+// that is not unrolled, so the compiler keeps only one group's converted quants and one token's
+// activations live at a time. The next group's three 16-byte loads are issued before this
+// group's math; the 16-byte header is re-read for each of the four groups of a block (an L1 hit).
+template <int NT>
+__device__ __forceinline__ void stream_q4k_groups(const uint8_t *row, int u0, int u1,
+                                                  const float *const (&x)[NT],
+                                                  const float *const (&gsum)[NT], float (&acc)[NT]) {
+  if (u0 >= u1) return;
+  const int it1 = 4 * u1;
+  auto load = [&](int it, u32x4 (&v)[3]) {
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(row + (size_t)(it >> 2) * 144);
+    v[0] = *(p);
+    v[1] = *(p + 1 + 2 * (it & 3));
+    v[2] = *(p + 2 + 2 * (it & 3));
+  };
+  u32x4 cur[3], nxt[3];
+  load(4 * u0, cur);
+#pragma unroll 1
+  for (int it = 4 * u0; it < it1; ++it) {
+    if (it + 1 < it1) load(it + 1, nxt);
+    const int u = it >> 2, c = it & 3;
+    const uint32_t h0 = cur[0].x, s0 = cur[0].y, s1 = cur[0].z, s2 = cur[0].w;
+    const float d = half_bits_to_float(h0), dmin = half_bits_to_float(h0 >> 16);
+    // scale and min of sub-blocks j0 = 2c (low nibbles) and j1 = 2c + 1 (high nibbles)
+    const int j0 = 2 * c, j1 = 2 * c + 1;
+    uint32_t sc0, m0, sc1, m1;
+    if (c < 2) {
+      sc0 = (s0 >> (8 * j0)) & 63u;
+      m0 = (s1 >> (8 * j0)) & 63u;
+      sc1 = (s0 >> (8 * j1)) & 63u;
+      m1 = (s1 >> (8 * j1)) & 63u;
+    } else {
+      const int a = j0 - 4, b = j1 - 4;
+      sc0 = ((s2 >> (8 * a)) & 15u) | (((s0 >> (8 * a + 6)) & 3u) << 4);
+      m0 = ((s2 >> (8 * a + 4)) & 15u) | (((s1 >> (8 * a + 6)) & 3u) << 4);
+      sc1 = ((s2 >> (8 * b)) & 15u) | (((s0 >> (8 * b + 6)) & 3u) << 4);
+      m1 = ((s2 >> (8 * b + 4)) & 15u) | (((s1 >> (8 * b + 6)) & 3u) << 4);
+    }
+    const float dsc0 = d * (float)sc0, dsc1 = d * (float)sc1 * 0.0625f;
+    const float dm0 = dmin * (float)m0, dm1 = dmin * (float)m1;
+    float fl[32], fh[32];
+#pragma unroll
+    for (int dw = 0; dw < 8; ++dw) {
+      const uint32_t w = dword_of(cur[1 + (dw >> 2)], dw & 3);
+      const uint32_t lo = opaque(w & 0x0F0F0F0Fu), hi = opaque(w & 0xF0F0F0F0u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        fl[4 * dw + e] = byte_to_float(lo, e);
+        fh[4 * dw + e] = byte_to_float(hi, e);
+      }
+    }
+    float prev = fl[0], prev2 = fh[0];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float *xg = x[t] + 256 * u + 64 * c;
+      const float dl = dot32(fl, xg + after(0, prev2));
+      const float dh = dot32(fh, xg + after(32, prev));
+      prev2 = dl;
+      prev = dh;
+      const float *g = gsum[t] + 8 * u + j0;
+      float a = __builtin_fmaf(dsc0, dl, acc[t]);
+      a = __builtin_fmaf(dsc1, dh, a);
+      a = __builtin_fmaf(-dm0, g[0], a);
+      acc[t] = __builtin_fmaf(-dm1, g[1], a);
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i) cur[i] = nxt[i];
+  }
+}
+
+// Stream units [u0, u1) of this lane's row, next unit's loads issued before this one's math.
+template <int FMT, int NT>
+__device__ __forceinline__ void stream_units(const uint8_t *row, int u0, int u1,
+                                             const float *const (&x)[NT],
+                                             const float *const (&gsum)[NT], float (&acc)[NT]) {
+  constexpr int G = Fmt<FMT>::group;
+  if constexpr (FMT == FMT_Q4_K && NT > 1) {
+    stream_q4k_groups<NT>(row, u0, u1, x, gsum, acc);
+  } else {
+    if (u0 >= u1) return;
+    Unit<FMT> cur, nxt;
+    load_unit(cur, row, u0);
+    for (int u = u0; u < u1; ++u) {
+      if (u + 1 < u1) load_unit(nxt, row, u + 1);
+      const float *xp[NT];
+      const float *gs[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        xp[t] = x[t] + 256 * u;
+        gs[t] = gsum[t] + (256 / G) * u;
+      }
+      unit_dot<NT>(cur, xp, gs, acc);
+      cur = nxt;
+    }
+  }
+}
+
+}  // namespace tq

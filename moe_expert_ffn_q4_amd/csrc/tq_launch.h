@@ -1,0 +1,22 @@
+// tq_launch.h -- host-side launchers behind the C ABI (internal to libtq).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+inline int64_t fmt_block_weights(int fmt) { return fmt == 1 ? 256 : fmt == 2 ? 256 : fmt == 3 ? 32 : 0; }
+inline int64_t fmt_block_bytes(int fmt) { return fmt == 1 ? 144 : fmt == 2 ? 210 : fmt == 3 ? 34 : 0; }
+
+// Each returns 0 when everything was enqueued, -1 on a HIP launch error, -2 when the shape needs
+// more LDS than one workgroup may use.
+int launch_dequant(int fmt, const void *w, int64_t n, int64_t k, int out_type, void *out,
+                   hipStream_t s);
+bool gemv_fast_shape(int fmt, int64_t k);
+size_t gemv_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t batch);
+int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, int64_t batch,
+                float *y, void *ws, size_t ws_bytes, hipStream_t s);
+int launch_swiglu(const float *g, const float *u, int64_t count, float *h, hipStream_t s);
+
+}  // namespace tq

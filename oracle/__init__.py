@@ -39,6 +39,8 @@ _i64 = C.c_int64
 
 
 def _declare(L: C.CDLL) -> None:
+    L.orc_num_threads.argtypes = []
+    L.orc_num_threads.restype = C.c_int
     L.orc_block_weights.argtypes = [C.c_int]
     L.orc_block_weights.restype = _i64
     L.orc_block_bytes.argtypes = [C.c_int]
@@ -88,6 +90,10 @@ def _type(t) -> int:
 def _check(rc: int, what: str) -> None:
     if rc != 0:
         raise ValueError(f"oracle {what} rejected its arguments (rc={rc})")
+
+
+def num_threads() -> int:
+    return int(lib().orc_num_threads())
 
 
 def block_weights(t) -> int:

@@ -33,6 +33,9 @@
 extern "C" {
 #endif
 
+/* Threads the oracle's parallel loops use (OpenMP). */
+int orc_num_threads(void);
+
 /* Block format codes used by the oracle. */
 enum { ORC_Q4_K = 1, ORC_Q6_K = 2, ORC_Q8_0 = 3 };
 

@@ -1,0 +1,72 @@
+"""The C ABI on the host (no GPU needed): symbols, size helpers, and argument checks.
+
+Every call here fails validation, which happens before any HIP call, so nothing is launched.
+"""
+import os
+import re
+
+import pytest
+
+import moe_expert_ffn_q4_amd as tq
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "tq.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(tq_[a-z_0-9]+)\s*\(",
+                                 src, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"tq_dequant", "tq_gemv", "tq_gemv_workspace_bytes", "tq_swiglu", "tq_last_error"} <= set(names)
+    L = tq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_size_helpers():
+    L = tq.lib()
+    assert [L.tq_block_weights(t) for t in (1, 2, 3)] == [256, 256, 32]
+    assert [L.tq_block_bytes(t) for t in (1, 2, 3)] == [144, 210, 34]
+    assert L.tq_block_weights(9) == 0
+    assert L.tq_row_bytes(1, 4096) == 2304 and L.tq_row_bytes(2, 8192) == 6720
+    assert L.tq_row_bytes(3, 28672) == 30464 and L.tq_row_bytes(3, 33) == -1
+
+
+@pytest.mark.parametrize("args,code", [
+    ((7, 16, 4, 256, 16, 1, 16), 1),      # unknown type
+    ((1, 0, 4, 256, 16, 1, 16), 1),       # null w
+    ((1, 16, 4, 256, 0, 1, 16), 1),       # null x
+    ((1, 16, 4, 100, 16, 1, 16), 2),      # k not a block multiple
+    ((3, 16, 4, 16, 16, 1, 16), 2),       # k below the block size
+    ((1, 16, 0, 256, 16, 1, 16), 2),      # n = 0
+    ((1, 16, 4, 256, 16, 0, 16), 2),      # batch = 0
+    ((1, 16, 4, 256, 16, 5000, 16), 2),   # batch too large
+    ((1, 8, 4, 256, 16, 1, 16), 3),       # w not 16-byte aligned
+    ((1, 16, 4, 256, 18, 1, 16), 3),      # x not 4-byte aligned
+])
+def test_gemv_rejects(args, code):
+    L = tq.lib()
+    t, w, n, k, x, b, y = args
+    assert L.tq_gemv(t, w or None, n, k, x or None, b, y or None, None, 0, None) == code
+    assert L.tq_last_error()
+
+
+def test_gemv_rejects_misaligned_workspace():
+    L = tq.lib()
+    assert L.tq_gemv(1, 16, 4, 256, 16, 1, 16, 128, 4096, None) == 3
+
+
+def test_dequant_and_swiglu_reject():
+    L = tq.lib()
+    assert L.tq_dequant(1, 16, 4, 100, 0, 16, None) == 2
+    assert L.tq_dequant(1, 16, 4, 256, 7, 16, None) == 1
+    assert L.tq_dequant(1, 8, 4, 256, 0, 16, None) == 3
+    assert L.tq_dequant(1, None, 0, 256, 0, None, None) == 0  # empty: nothing to do
+    assert L.tq_swiglu(16, 16, -1, 16, None) == 2
+    assert L.tq_swiglu(None, 16, 4, 16, None) == 1
+    assert L.tq_swiglu(16, 16, 0, 16, None) == 0

@@ -1,0 +1,167 @@
+"""GPU parity of tq_dequant, tq_gemv and tq_swiglu against the CPU oracle.
+
+Bars: dequantized weights and all-integer-lattice products bitwise; other products within
+|err| <= 1e-3 * sum|w x| + 1e-5 per output; SwiGLU on identical inputs within 1e-5 |h| + 1e-5.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.golden_io import load_blocks
+from tests.gpu_util import assert_product_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+tq = pytest.importorskip("moe_expert_ffn_q4_amd")
+
+
+def _print_case(*a):
+    print("case:", *a, flush=True)
+
+
+@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q8_0"])
+@pytest.mark.parametrize("n,k", [(1, 256), (67, 1024), (130, 4608), (3, 768)])
+def test_dequant_bitwise(t, n, k):
+    _print_case("dequant", t, n, k)
+    g = synth.rng(101, "dq", t, n, k)
+    w = synth.blob(t, g, n, k)
+    wd = dev(w)
+    f32 = host(tq.dequant(t, wd, n, k, "f32"))
+    assert np.array_equal(f32.view(np.uint32), oracle.dequant(t, w, n, k, "f32").view(np.uint32))
+    bf = host(tq.dequant(t, wd, n, k, "bf16")).view(np.uint16)
+    assert np.array_equal(bf, oracle.dequant(t, w, n, k, "bf16"))
+
+
+def test_dequant_golden_blocks_bitwise():
+    for fx in load_blocks():
+        t, blk = fx["type"], fx["block"]
+        k = synth.BLOCK_WEIGHTS[t]
+        _print_case("golden", fx["name"])
+        got = host(tq.dequant(t, dev(blk), 1, k, "f32"))[0]
+        assert np.array_equal(got.astype(np.float64), fx["expect"]), fx["name"]
+        assert np.array_equal(np.signbit(got), np.signbit(fx["expect"])), fx["name"]
+
+
+# shapes span several 64-row groups with a ragged last group, several waves along k with an
+# uneven split, and (q6_k k=768, q8_0 k=96/800) the shapes whose rows are not dword aligned
+GEMV_CASES = [
+    ("q4_k", 200, 2304), ("q4_k", 64, 256), ("q4_k", 1, 4096), ("q4_k", 333, 9216),
+    ("q6_k", 150, 3072), ("q6_k", 70, 768), ("q6_k", 64, 512),
+    ("q8_0", 190, 2560), ("q8_0", 65, 96), ("q8_0", 33, 800),
+]
+
+
+@pytest.mark.parametrize("t,n,k", GEMV_CASES)
+@pytest.mark.parametrize("batch", [1, 2, 3, 8, 9, 16])
+def test_gemv_parity(t, n, k, batch):
+    _print_case("gemv", t, n, k, batch)
+    g = synth.rng(102, "gemv", t, n, k, batch)
+    w = synth.blob(t, g, n, k)
+    x = synth.normal_f32(g, (batch, k))
+    y = host(tq.gemv(t, dev(w), n, k, dev(x)))
+    ref, mag = oracle.gemv(t, w, n, k, x)
+    assert_product_close(y, ref, mag, what=f"{t} {n}x{k} b{batch}")
+
+
+@pytest.mark.parametrize("t,n,k", [("q4_k", 300, 4096), ("q6_k", 200, 3584 * 2), ("q8_0", 129, 2048),
+                                   ("q6_k", 64, 1280), ("q8_0", 64, 352)])
+@pytest.mark.parametrize("batch", [1, 5, 8])
+def test_gemv_integer_lattice_bitwise(t, n, k, batch):
+    """Scales 2^-8 and x in {-1,0,1}: every partial sum is exact in fp32, so any summation order
+    gives the exact result and the GPU must match the oracle bit for bit."""
+    _print_case("lattice", t, n, k, batch)
+    g = synth.rng(103, "lattice", t, n, k)
+    kw = dict(d_value=2.0 ** -8, dmin_value=2.0 ** -8) if t == "q4_k" else dict(d_value=2.0 ** -8)
+    w = synth.blob(t, g, n, k, **kw)
+    if t == "q6_k":  # keep |sc*(q-32)| <= 256 so sums stay below 2^16 in units of 2^-8
+        blk = w.reshape(-1, 210)
+        blk[:, 192:208] = (blk[:, 192:208].view(np.int8) // 16).view(np.uint8)
+    x = synth.ternary_f32(g, (batch, k))
+    y = host(tq.gemv(t, dev(w), n, k, dev(x)))
+    ref, _ = oracle.gemv(t, w, n, k, x)
+    assert np.array_equal(y.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("t,n,k", [("q4_k", 200, 4096), ("q6_k", 130, 3072), ("q8_0", 70, 2048)])
+@pytest.mark.parametrize("batch", [1, 7])
+def test_gemv_without_workspace(t, n, k, batch):
+    """No workspace: every row group in one workgroup; and an explicit workspace."""
+    _print_case("no-ws", t, n, k, batch)
+    g = synth.rng(107, "nows", t, n, k, batch)
+    w = synth.blob(t, g, n, k)
+    x = synth.normal_f32(g, (batch, k))
+    wd, xd = dev(w), dev(x)
+    y0 = host(tq.gemv(t, wd, n, k, xd, ws=False))
+    ref, mag = oracle.gemv(t, w, n, k, x)
+    assert_product_close(y0, ref, mag, what="no workspace")
+    nbytes = tq.gemv_workspace_bytes(t, n, k, batch)
+    ws = torch.full((max(nbytes, 256),), 0x7F, dtype=torch.uint8, device="cuda:0")
+    y1 = host(tq.gemv(t, wd, n, k, xd, ws=ws))
+    assert_product_close(y1, ref, mag, what="own workspace")
+
+
+def test_gemv_unit_vector_picks_dequantized_column():
+    t, n, k = "q4_k", 130, 1024
+    g = synth.rng(104, "ej")
+    w = synth.blob(t, g, n, k)
+    x = np.zeros((3, k), np.float32)
+    x[0, 0] = x[1, 511] = x[2, 1023] = 1.0
+    y = host(tq.gemv(t, dev(w), n, k, dev(x)))
+    dense = oracle.dequant(t, w, n, k, "f32")
+    assert np.array_equal(y[0], dense[:, 0]) and np.array_equal(y[1], dense[:, 511])
+    assert np.array_equal(y[2], dense[:, 1023])
+
+
+def test_gemv_deterministic_across_interleaved_shapes():
+    """Same inputs give the same bits, also when other shapes use the shared workspace between."""
+    t, n, k = "q4_k", 4096, 4096
+    g = synth.rng(105, "det")
+    wd, xd = dev(synth.blob(t, g, n, k)), dev(synth.normal_f32(g, (8, k)))
+    n2, k2 = 28672, 8192
+    w2, x2 = dev(synth.blob("q6_k", g, n2, k2)), dev(synth.normal_f32(g, (3, k2)))
+    a = host(tq.gemv(t, wd, n, k, xd[:1]))
+    c = host(tq.gemv(t, wd, n, k, xd))
+    e = host(tq.gemv("q6_k", w2, n2, k2, x2))
+    b = host(tq.gemv(t, wd, n, k, xd[:1]))
+    f = host(tq.gemv("q6_k", w2, n2, k2, x2))
+    d = host(tq.gemv(t, wd, n, k, xd))
+    assert np.array_equal(a, b) and np.array_equal(c, d) and np.array_equal(e, f)
+
+
+def test_gemv_full_4096x4096_all_rows():
+    """The 4096 x 4096 batch-1 Q4_K case, every output row against the oracle."""
+    t, n, k = "q4_k", 4096, 4096
+    g = synth.rng(synth.DEFAULT_SEED, "c1")
+    w = synth.blob(t, g, n, k)
+    x = synth.normal_f32(g, (1, k))
+    y = host(tq.gemv(t, dev(w), n, k, dev(x)))
+    ref, mag = oracle.gemv(t, w, n, k, x)
+    assert_product_close(y, ref, mag, what="4096x4096")
+
+
+@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q8_0"])
+@pytest.mark.parametrize("name,n,k", [("gate", 28672, 8192), ("down", 8192, 28672), ("k", 1024, 8192)])
+@pytest.mark.parametrize("batch", [1, 4, 16])
+def test_gemv_70b_shapes_sampled_rows(t, name, n, k, batch):
+    """Full 70B-layer projection shapes, sampled output rows checked one by one."""
+    _print_case("70b", t, name, batch)
+    g = synth.rng(synth.DEFAULT_SEED, "70b", t, name)
+    w = synth.blob(t, g, n, k)
+    x = synth.normal_f32(synth.rng(synth.DEFAULT_SEED, "70b-x", batch), (batch, k))
+    y = host(tq.gemv(t, dev(w), n, k, dev(x)))
+    rows = np.unique(np.concatenate([[0, 63, 64, n - 1], g.integers(0, n, 60)]))
+    ref, mag = oracle.gemv(t, w, n, k, x, rows=rows)
+    assert_product_close(y[:, rows], ref, mag, what=f"{t} {name} b{batch}")
+
+
+def test_swiglu_on_identical_inputs():
+    g = synth.rng(106, "swiglu")
+    a = synth.normal_f32(g, 100003, 3.0)
+    b = synth.normal_f32(g, 100003)
+    a[:4] = [0.0, -100.0, 100.0, -800.0]
+    h = host(tq.swiglu(dev(a), dev(b)))
+    ref = oracle.swiglu(a, b)
+    err = np.abs(h.astype(np.float64) - ref)
+    assert np.all(err <= 1e-5 * np.abs(ref) + 1e-5)
