@@ -31,6 +31,10 @@ def _args():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--batch", type=int, default=1, help="tokens per decode step (1 or 8)")
+    p.add_argument("--workload", default="llama8b",
+                   choices=["llama8b", "mixtral", "deepseek"],
+                   help="llama8b: 32-layer dense decode step (default); mixtral / deepseek: one "
+                        "MoE layer at --batch tokens")
     p.add_argument("--seed", type=int, default=42)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -54,6 +58,8 @@ def build_dense_model(tq, synth, torch, batch, seed):
 
 
 def make_step(tq, torch, layers, batch, events=None):
+    """One decode step through the C ABI: per layer q, k, v (input x), o (input: the attention
+    stand-in a), gate and up (input x), SwiGLU, down (input: the SwiGLU output)."""
     H = 4096
     F = 14336
     dev = "cuda"
@@ -61,17 +67,24 @@ def make_step(tq, torch, layers, batch, events=None):
                 v=torch.empty(batch, 1024, device=dev), o=torch.empty(batch, H, device=dev),
                 gate=torch.empty(batch, F, device=dev), up=torch.empty(batch, F, device=dev),
                 h=torch.empty(batch, F, device=dev), down=torch.empty(batch, H, device=dev))
+    L = tq.lib()
+    ws_bytes = max(tq.gemv_workspace_bytes("q4_k", n, k, batch)
+                   for n, k in ((4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)))
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
 
     def gemv(name, projs, x):
         w, n, k = projs[name]
+        stream = torch.cuda.current_stream().cuda_stream
         if events is not None:
             s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             s.record()
-            tq.gemv("q4_k", w, n, k, x, out=bufs[name])
+        rc = L.tq_gemv(tq.Q4_K, w.data_ptr(), n, k, x.data_ptr(), batch, bufs[name].data_ptr(),
+                       ws.data_ptr(), ws.numel(), stream)
+        if rc:
+            raise tq.TQError(rc, L.tq_last_error().decode())
+        if events is not None:
             e.record()
             events.append((s, e, w.numel() + 4 * batch * (n + k)))
-        else:
-            tq.gemv("q4_k", w, n, k, x, out=bufs[name])
 
     def step():
         for projs, x, a in layers:
@@ -122,6 +135,60 @@ def cpu_baseline(synth, batch, seed, budget_s):
                       f"at batch {batch} ({elapsed:.1f} s), scaled linearly to 32 layers"}
 
 
+def moe_bench(args, torch, tq, synth):
+    """One MoE layer (Mixtral- or DeepSeek-shaped, Q4_K experts) at --batch tokens, graph-captured.
+    Roofline: the grouped expert GEMV, algorithmic bytes = blobs of the experts the routing
+    actually selected (plus the shared expert) read once, plus activations."""
+    import numpy as np
+
+    shape = synth.MIXTRAL if args.workload == "mixtral" else synth.DEEPSEEK
+    k = shape["top_k"]
+    T = args.batch
+    layer = synth.moe_layer(shape, "q4_k", seed=args.seed, tag=args.workload)
+    experts = [tuple(torch.from_numpy(b).cuda() for b in e) for e in layer["experts"]]
+    shared = tuple(torch.from_numpy(b).cuda() for b in layer["shared"]) if layer["shared"] else None
+    del layer["experts"]
+    moe = tq.MoeLayer("q4_k", shape["hidden"], shape["ffn"], torch.from_numpy(layer["router"]).cuda(),
+                      experts, shared, top_k=k)
+    x = torch.from_numpy(synth.normal_f32(synth.rng(args.seed, "bench-x", T), (T, shape["hidden"]))).cuda()
+    y = torch.empty_like(x)
+    ws = torch.empty(moe.workspace_bytes(T), dtype=torch.uint8, device="cuda")
+    E = shape["n_experts"]
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        moe(x, out=y, ws=ws, routing=dict(counts=counts))
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            moe(x, out=y, ws=ws)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    c = counts.cpu().numpy()
+    eb = sum(b.numel() for b in experts[0])
+    active = int((c > 0).sum()) + (1 if shared else 0)
+    alg_bytes = active * eb + 4 * T * shape["hidden"] * 2 + moe.router_w.numel() * 4
+    ms = elapsed * 1000 / args.steps
+    return {
+        "metric": METRIC, "value": round(T * args.steps / elapsed, 2), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "q4_k weights, f32 activations and accumulation",
+        "data": "synthetic (seeded random Q4_K experts, N(0,1) activations and router)",
+        "config": {"workload": f"{args.workload}-shaped MoE layer, top-{k} of {E}"
+                               f"{' + shared expert' if shared else ''}, {T} tokens",
+                   "global_batch": T, "seq_len": 1, "parallelism": "none (1 GPU)"},
+        "layer_gbs": round(alg_bytes / (ms / 1000) / 1e9, 1),
+        "active_experts": active,
+    }
+
+
 def main():
     args = _args()
     if args.gpus != 1:
@@ -134,29 +201,44 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
+    if args.workload != "llama8b":
+        print(json.dumps(moe_bench(args, torch, tq, synth)), flush=True)
+        return
     layers = build_dense_model(tq, synth, torch, args.batch, args.seed)
-    step = make_step(tq, torch, layers, args.batch)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        step = make_step(tq, torch, layers, args.batch)
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        # the whole decode step as one HIP graph, replayed once per step
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1000 / args.steps
     tokens_s = args.batch * args.steps / elapsed
 
-    # Roofline of the Q4_K GEMV: the same steps again, each GEMV launch bracketed by events
+    # Roofline of the Q4_K GEMV: the same step again, eager, each tq_gemv bracketed by events on
+    # the launch stream; a GPU-side sleep first lets the host queue the whole step ahead of the
+    # GPU, so the events time the kernels and not the launch latency.
     events = []
-    istep = make_step(tq, torch, layers, args.batch, events=events)
-    for _ in range(min(args.steps, 5)):
+    with torch.cuda.stream(stream):
+        istep = make_step(tq, torch, layers, args.batch, events=events)
+        torch.cuda._sleep(200_000_000)
         istep()
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
     kernel_s = sum(s.elapsed_time(e) for s, e, _ in events) / 1000
     kernel_bytes = sum(b for _, _, b in events)
     achieved = kernel_bytes / kernel_s / 1e9
-    step_bytes = sum(b for _, _, b in events) / min(args.steps, 5)
+    step_bytes = kernel_bytes
 
     out = {
         "metric": METRIC,
@@ -177,7 +259,8 @@ def main():
         "step_gbs": round(step_bytes / (ms_per_step / 1000) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "tq::k_gemv<Q4_K>", "avg_launch_us": round(kernel_s * 1e6 / len(events), 3)},
+                     "kernel": "tq_gemv Q4_K (k_gemv + k_gemv_reduce)",
+                     "avg_launch_us": round(kernel_s * 1e6 / len(events), 3)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(synth, args.batch, args.seed, args.cpu_seconds)

@@ -93,6 +93,67 @@ int tq_gemv(int type, const void *w, int64_t n, int64_t k, const float *x, int64
  */
 int tq_swiglu(const float *g, const float *u, int64_t count, float *h, void *stream);
 
+/* ---- top-k routed MoE expert FFN ------------------------------------------------------------
+ * The layer the pages describe for mixture-of-experts models: a router scores every expert per
+ * token, only the top k experts run (e.g. 2 of 8, so three quarters of the expert weights are not
+ * touched: "Titan Engine" page, "MoE expert streaming"), each expert is a SwiGLU FFN over
+ * block-quantized weights, and an always-on shared expert may be added (DeepSeek-V3-shaped
+ * layers; KTransformers page, MoE on the 671B model).
+ *
+ *   logits[t][e] = sum_h x[t][h] * router_w[e][h]                                  (fp32)
+ *   ids[t][0..k-1]  = the k largest logits, ties to the lower expert index; slot j holds the j-th
+ *   w[t][j]         = exp(l_j - l_0) / sum_{i < k} exp(l_i - l_0)       (renormalize = 1), or
+ *                     exp(l_j - l_0) / sum_{e < E} exp(l_e - l_0)       (renormalize = 0)
+ *   y[t] = sum_j w[t][j] * down_e . silu(gate_e . x_t) * (up_e . x_t)   (e = ids[t][j], j in order)
+ *        + down_s . silu(gate_s . x_t) * (up_s . x_t)                   (shared expert, if any)
+ * silu(z) = z / (1 + exp(-z)). Expert matrices: gate, up [ffn][hidden]; down [hidden][ffn].
+ */
+typedef struct {
+  const void *gate, *up, *down; /* blobs of one expert, 16-byte aligned */
+} tq_expert;
+
+typedef struct {
+  int type;                      /* block format of every expert matrix */
+  int64_t hidden, ffn;           /* multiples of 256 */
+  int64_t n_experts, top_k;      /* 1 <= top_k <= min(n_experts, 32), n_experts <= 1024 */
+  const float *router_w;         /* device [n_experts][hidden] fp32, 16-byte aligned */
+  const tq_expert *experts;      /* device array [n_experts] of device blob pointers */
+  const tq_expert *experts_host; /* host array [n_experts] of pinned host blob pointers; used
+                                    instead of `experts` when experts_on_host is set */
+  tq_expert shared;              /* device blobs of the shared expert; gate == NULL: none */
+  int renormalize;               /* 1: weights renormalised over the selected experts */
+  int experts_on_host;           /* 1: routed experts live in pinned host memory and are copied
+                                    to the workspace on every call (see tq_moe_ffn) */
+  void *copy_stream;             /* hipStream_t for those copies (experts_on_host only) */
+  int path;                      /* TQ_PATH_AUTO / TQ_PATH_F32 / TQ_PATH_BF16_MFMA */
+} tq_moe_desc;
+
+typedef struct {                 /* optional copies of the routing, device pointers or NULL */
+  int32_t *topk_ids;             /* [T][k] */
+  float *topk_w;                 /* [T][k] */
+  float *logits;                 /* [T][n_experts], the fp32 values the selection used */
+  int32_t *counts;               /* [n_experts] tokens routed to each expert */
+  int32_t *offsets;              /* [n_experts + 1] exclusive prefix sum of counts */
+  int32_t *pairs;                /* [T*k] t*k + j, sorted by (expert, t) */
+} tq_moe_routing;
+
+/* Workspace bytes tq_moe_ffn needs for `tokens` tokens (0 if the descriptor is invalid). */
+size_t tq_moe_workspace_bytes(const tq_moe_desc *desc, int64_t tokens);
+
+/*
+ * tq_moe_ffn -- y = MoE(x) as above for x [tokens][hidden] fp32 (device, 16-byte aligned), y
+ * [tokens][hidden] fp32 (device). workspace: device scratch of at least
+ * tq_moe_workspace_bytes(desc, tokens) bytes, 256-byte aligned, contents irrelevant; one call at a
+ * time per workspace. routing_out: NULL or copies of the routing (each field may be NULL).
+ * 1 <= tokens <= 8192. Everything is enqueued on `stream` without host synchronisation, except
+ * with experts_on_host: the selected expert ids are then copied to the host (one synchronisation
+ * of `stream`) and each selected expert is copied from pinned host memory to the workspace with
+ * hipMemcpyAsync on copy_stream, the expert kernels waiting on an event per copy.
+ * Deterministic: the same inputs give bitwise-identical outputs and routing.
+ */
+int tq_moe_ffn(const tq_moe_desc *desc, const float *x, int64_t tokens, float *y,
+               void *workspace, size_t ws_bytes, tq_moe_routing *routing_out, void *stream);
+
 /* Text of the last non-TQ_OK status returned on this thread ("" if none). */
 const char *tq_last_error(void);
 

@@ -53,9 +53,9 @@ class Expert(C.Structure):
 
 class MoeDesc(C.Structure):
     _fields_ = [("type", _int), ("hidden", _i64), ("ffn", _i64), ("n_experts", _i64),
-                ("top_k", _i64), ("router_w", _vp), ("experts", C.POINTER(Expert)),
-                ("shared", C.POINTER(Expert)), ("renormalize", _int),
-                ("experts_on_host", _int), ("copy_stream", _vp), ("path", _int)]
+                ("top_k", _i64), ("router_w", _vp), ("experts", _vp), ("experts_host", _vp),
+                ("shared", Expert), ("renormalize", _int), ("experts_on_host", _int),
+                ("copy_stream", _vp), ("path", _int)]
 
 
 class MoeRouting(C.Structure):
@@ -163,3 +163,52 @@ def swiglu(g: torch.Tensor, u: torch.Tensor, out=None, stream=None):
         out = torch.empty_like(g)
     _check(lib().tq_swiglu(_ptr(g), _ptr(u), g.numel(), _ptr(out), _stream(stream)))
     return out
+
+
+class MoeLayer:
+    """Device-resident MoE layer for tq_moe_ffn: router weights, the device table of expert blob
+    pointers, and an optional shared expert. Blobs are torch uint8 tensors (kept alive here)."""
+
+    def __init__(self, t, hidden: int, ffn: int, router_w: torch.Tensor, experts, shared=None,
+                 top_k: int = 2, renormalize: bool = True, path: int = PATH_AUTO):
+        self.blobs = [b for e in experts for b in e] + (list(shared) if shared else [])
+        self.router_w = router_w
+        E = len(experts)
+        table = torch.tensor([[b.data_ptr() for b in e] for e in experts], dtype=torch.int64)
+        self.table = table.to(router_w.device)
+        self.desc = MoeDesc()
+        self.desc.type = _type(t)
+        self.desc.hidden, self.desc.ffn = hidden, ffn
+        self.desc.n_experts, self.desc.top_k = E, top_k
+        self.desc.router_w = router_w.data_ptr()
+        self.desc.experts = self.table.data_ptr()
+        self.desc.experts_host = None
+        if shared:
+            self.desc.shared = Expert(*[b.data_ptr() for b in shared])
+        self.desc.renormalize = int(renormalize)
+        self.desc.experts_on_host = 0
+        self.desc.copy_stream = None
+        self.desc.path = path
+
+    def workspace_bytes(self, tokens: int) -> int:
+        """Bytes of workspace tq_moe_ffn needs (0 when the descriptor is invalid)."""
+        return int(lib().tq_moe_workspace_bytes(C.byref(self.desc), tokens))
+
+    def __call__(self, x: torch.Tensor, out=None, ws=None, routing: dict | None = None,
+                 stream=None):
+        """y = MoE(x) for x [T, hidden] fp32. routing: dict of preallocated device tensors
+        (topk_ids, topk_w, logits, counts, offsets, pairs) to receive the routing."""
+        T = x.shape[0]
+        if out is None:
+            out = torch.empty_like(x)
+        if ws is None:
+            need = self.workspace_bytes(T)
+            ws = workspace(need, x.device) if need else None
+        r = None
+        if routing is not None:
+            r = MoeRouting(*[(routing[f].data_ptr() if routing.get(f) is not None else None)
+                             for f, _ in MoeRouting._fields_])
+        _check(lib().tq_moe_ffn(C.byref(self.desc), x.data_ptr(), T, out.data_ptr(),
+                                _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                C.byref(r) if r is not None else None, _stream(stream)))
+        return out

@@ -4,6 +4,7 @@
 
 #include "../../include/tq.h"
 #include "tq_launch.h"
+#include "tq_moe.h"
 
 namespace {
 
@@ -85,6 +86,79 @@ int tq_swiglu(const float *g, const float *u, int64_t count, float *h, void *str
   if (!aligned(g, 4) || !aligned(u, 4) || !aligned(h, 4))
     return fail(TQ_EALIGN, "tq_swiglu: pointers must be 4-byte aligned");
   return launched(tq::launch_swiglu(g, u, count, h, (hipStream_t)stream), "tq_swiglu");
+}
+
+static int moe_check(const tq_moe_desc *d, int64_t tokens, tq::MoeShape *out) {
+  if (!d) return fail(TQ_EINVAL, "tq_moe_ffn: null descriptor");
+  if (!known_type(d->type)) return fail(TQ_EINVAL, "tq_moe_ffn: unknown block type %d", d->type);
+  if (d->hidden < 256 || d->ffn < 256 || d->hidden % 256 || d->ffn % 256)
+    return fail(TQ_ESHAPE, "tq_moe_ffn: hidden and ffn must be positive multiples of 256");
+  if (!tq::gemv_fast_shape(d->type, d->hidden) || !tq::gemv_fast_shape(d->type, d->ffn))
+    return fail(TQ_EUNSUPPORTED, "tq_moe_ffn: this block type needs hidden and ffn to be multiples of 512");
+  if (d->n_experts < 1 || d->n_experts > 1024 || d->top_k < 1 || d->top_k > 32 || d->top_k > d->n_experts)
+    return fail(TQ_ESHAPE, "tq_moe_ffn: n_experts=%lld top_k=%lld out of range",
+                (long long)d->n_experts, (long long)d->top_k);
+  if (tokens < 1 || tokens > 8192) return fail(TQ_ESHAPE, "tq_moe_ffn: tokens=%lld not in 1..8192", (long long)tokens);
+  if (tq::group_lds_bytes(tokens, d->n_experts) > 65536)
+    return fail(TQ_EUNSUPPORTED, "tq_moe_ffn: tokens x experts too large for the grouping kernel");
+  if (!d->router_w || !aligned(d->router_w, 16)) return fail(TQ_EINVAL, "tq_moe_ffn: router_w null or not 16-byte aligned");
+  if (d->experts_on_host ? !d->experts_host : !d->experts)
+    return fail(TQ_EINVAL, "tq_moe_ffn: missing expert table");
+  if (d->shared.gate && (!d->shared.up || !d->shared.down))
+    return fail(TQ_EINVAL, "tq_moe_ffn: shared expert needs gate, up and down");
+  if (d->path != TQ_PATH_AUTO && d->path != TQ_PATH_F32 && d->path != TQ_PATH_BF16_MFMA)
+    return fail(TQ_EINVAL, "tq_moe_ffn: unknown path %d", d->path);
+  tq::MoeShape s{};
+  s.type = d->type;
+  s.hidden = d->hidden;
+  s.ffn = d->ffn;
+  s.n_experts = d->n_experts;
+  s.top_k = d->top_k;
+  s.tokens = tokens;
+  s.has_shared = d->shared.gate != nullptr;
+  s.renormalize = d->renormalize != 0;
+  s.experts_on_host = d->experts_on_host != 0;
+  s.gate_bytes = d->ffn * tq_row_bytes(d->type, d->hidden);
+  s.expert_bytes = 2 * s.gate_bytes + d->hidden * tq_row_bytes(d->type, d->ffn);
+  *out = s;
+  return TQ_OK;
+}
+
+size_t tq_moe_workspace_bytes(const tq_moe_desc *desc, int64_t tokens) {
+  tq::MoeShape s;
+  if (moe_check(desc, tokens, &s) != TQ_OK) return 0;
+  return (size_t)tq::plan_moe(s).bytes;
+}
+
+int tq_moe_ffn(const tq_moe_desc *d, const float *x, int64_t tokens, float *y, void *workspace,
+               size_t ws_bytes, tq_moe_routing *routing_out, void *stream) {
+  tq::MoeShape s;
+  int rc = moe_check(d, tokens, &s);
+  if (rc != TQ_OK) return rc;
+  if (!x || !y || !workspace) return fail(TQ_EINVAL, "tq_moe_ffn: null x, y or workspace");
+  if (!aligned(x, 16) || !aligned(y, 4) || !aligned(workspace, 256))
+    return fail(TQ_EALIGN, "tq_moe_ffn: x 16-byte, y 4-byte, workspace 256-byte alignment needed");
+  const tq::MoePlan p = tq::plan_moe(s);
+  if (ws_bytes < (size_t)p.bytes)
+    return fail(TQ_ENOSPC, "tq_moe_ffn: workspace of %zu bytes, %lld needed", ws_bytes, (long long)p.bytes);
+  if (s.experts_on_host) return fail(TQ_EUNSUPPORTED, "tq_moe_ffn: host-resident experts not built yet");
+  hipStream_t st = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  if (tq::launch_moe_routing(p, d->router_w, x, ws, st)) return launched(-1, "tq_moe_ffn routing");
+  if (routing_out) {
+    const int64_t T = tokens, E = s.n_experts, k = s.top_k;
+    struct { void *dst; int64_t off, bytes; } cp[] = {
+        {routing_out->topk_ids, p.off_ids, T * k * 4}, {routing_out->topk_w, p.off_wts, T * k * 4},
+        {routing_out->logits, p.off_logits, T * E * 4}, {routing_out->counts, p.off_counts, E * 4},
+        {routing_out->offsets, p.off_offsets, (E + 1) * 4}, {routing_out->pairs, p.off_pairs, T * k * 4}};
+    for (auto &c : cp)
+      if (c.dst && hipMemcpyAsync(c.dst, ws + c.off, (size_t)c.bytes, hipMemcpyDeviceToDevice, st) != hipSuccess)
+        return fail(TQ_EDEVICE, "tq_moe_ffn: routing copy failed");
+  }
+  tq::MoeExpertPtrs shared{{d->shared.gate, d->shared.up, d->shared.down}};
+  rc = tq::launch_moe_experts(p, reinterpret_cast<const tq::MoeExpertPtrs *>(d->experts), shared,
+                              nullptr, x, y, ws, st);
+  return launched(rc, "tq_moe_ffn experts");
 }
 
 }  // extern "C"

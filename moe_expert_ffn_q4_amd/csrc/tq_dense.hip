@@ -159,60 +159,21 @@ __global__ __launch_bounds__(512) void k_gemv(const uint8_t *__restrict__ w, int
                                               float *__restrict__ y, int64_t ldy,
                                               float *__restrict__ partial) {
   extern __shared__ float lds[];
-  constexpr int G = Fmt<FMT>::group;
-  constexpr int GPU_ = 256 / G;  // groups per unit
-  const int nw = blockDim.x >> 6;
-  const int wave = wave_index();
-  const int lane = threadIdx.x & 63;
   const int rg = blockIdx.x / ksplit, ks = blockIdx.x - rg * ksplit;
   const int row0 = rg * 64;
   const int ku0 = ks * upk, ku1 = min(ku0 + upk, units);
-  const int ngl = (ku1 - ku0) * GPU_;
-
-  // group sums of this slice of x, for every token of the tile
-  for (int i = threadIdx.x; i < NT * ngl; i += blockDim.x) {
-    const int t = i / ngl, gi = i - t * ngl;
-    const float *p = x + t * ldx + (int64_t)(ku0 * GPU_ + gi) * G;
-    float s = 0.f;
-#pragma unroll
-    for (int e = 0; e < G; ++e) s += p[e];
-    lds[i] = s;
-  }
-  __syncthreads();
-
   const float *xr[NT];
-  const float *gs[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    xr[t] = x + t * ldx;
-    gs[t] = lds + t * ngl - ku0 * GPU_;  // indexed with absolute group numbers
-  }
-  float acc[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = 0.f;
-  const int row = min(row0 + lane, n - 1);  // rows past n repeat the last row; not stored
-  const int u0 = ku0 + wave * upw, u1 = min(u0 + upw, ku1);
-  stream_units<FMT, NT>(w + (int64_t)row * row_bytes, u0, u1, xr, gs, acc);
-
-  __syncthreads();  // every wave is done with the group sums
-#pragma unroll
-  for (int t = 0; t < NT; ++t) lds[(wave * NT + t) * 64 + lane] = acc[t];
-  __syncthreads();
+  for (int t = 0; t < NT; ++t) xr[t] = x + t * ldx;
+  gemv_tile<FMT, NT>(w, row_bytes, n, row0, ku0, ku1, upw, xr, lds);
   if (ksplit == 1) {
     for (int i = threadIdx.x; i < NT * 64; i += blockDim.x) {
       const int t = i >> 6, l = i & 63;
-      float s = 0.f;
-      for (int v = 0; v < nw; ++v) s += lds[(v * NT + t) * 64 + l];
-      if (row0 + l < n) y[t * ldy + row0 + l] = s;
+      if (row0 + l < n) y[t * ldy + row0 + l] = lds[i];
     }
-    return;
-  }
-  float *mine = partial + ((int64_t)rg * ksplit + ks) * NT * 64;
-  for (int i = threadIdx.x; i < NT * 64; i += blockDim.x) {
-    const int t = i >> 6, l = i & 63;
-    float s = 0.f;
-    for (int v = 0; v < nw; ++v) s += lds[(v * NT + t) * 64 + l];
-    mine[i] = s;
+  } else {
+    float *mine = partial + ((int64_t)rg * ksplit + ks) * NT * 64;
+    for (int i = threadIdx.x; i < NT * 64; i += blockDim.x) mine[i] = lds[i];
   }
 }
 
@@ -257,19 +218,16 @@ static void launch_gemv_nt(const uint8_t *w, int64_t rb, int n, int units, const
 template <int FMT>
 static int launch_gemv_fmt(const uint8_t *w, int64_t rb, int n, int64_t k, const float *x,
                            int batch, float *y, void *ws, size_t ws_bytes, hipStream_t s) {
-  constexpr int G = Fmt<FMT>::group;
   const int units = (int)(k / 256);
   const bool split = ws != nullptr && ws_bytes >= gemv_workspace_bytes(FMT, n, k, batch);
   const GemvPlan p = plan_gemv(n, k, split);
   float *partial = p.ksplit > 1 ? static_cast<float *>(ws) : nullptr;
-  const int ngl = p.upk * (256 / G);
-  const int per_tok = ngl > p.waves * 64 ? ngl : p.waves * 64;  // LDS floats per token
   const int max_floats = 65536 / 4;
   for (int t0 = 0; t0 < batch;) {
     int nt = batch - t0 < 8 ? batch - t0 : 8;
-    while (nt > 1 && nt * per_tok > max_floats) --nt;
-    if (nt * per_tok > max_floats) return -2;
-    const size_t lds = (size_t)4 * nt * per_tok;
+    while (nt > 1 && gemv_tile_lds_floats<FMT>(nt, p.upk, p.waves) > max_floats) --nt;
+    if (gemv_tile_lds_floats<FMT>(nt, p.upk, p.waves) > max_floats) return -2;
+    const size_t lds = (size_t)4 * gemv_tile_lds_floats<FMT>(nt, p.upk, p.waves);
     const float *xt = x + (int64_t)t0 * k;
     float *yt = y + (int64_t)t0 * n;
     switch (nt) {

@@ -22,6 +22,21 @@ __device__ __forceinline__ float byte_to_float(uint32_t w, int e) {
   return (float)((w >> (8 * e)) & 0xFFu);
 }
 
+// Bytes 2h and 2h+1 of w, each holding a value 0..15, converted to fp32 by the fp8 (e4m3)
+// conversion unit: a byte b < 16 is either the subnormal b * 2^-9 (exponent field 0) or the normal
+// (1 + (b-8)/8) * 2^-6 = b * 2^-9 (exponent field 1), so the result is exactly b times a power of
+// two, two values per instruction. nibble_fp8_unit() is that power of two (read back from the
+// hardware so that either fp8 exponent bias works).
+template <bool HIGH_HALF>
+__device__ __forceinline__ void nibbles_to_float(uint32_t w, float &a, float &b) {
+  const auto v = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HIGH_HALF);
+  a = v[0];
+  b = v[1];
+}
+__device__ __forceinline__ float nibble_fp8_unit() {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(1, false)[0];
+}
+
 // w with what the compiler knows about its bits forgotten. After masking a dword down to four
 // nibbles, this keeps the four byte conversions as one v_cvt_f32_ubyteN each; otherwise the
 // compiler re-derives each nibble with its own shift/mask before converting.

@@ -5,7 +5,9 @@
 // eight Q8_0 blocks). Every lane streams its own row with 16-byte loads while the activation
 // values are the same for all 64 lanes, so they come through scalar loads and feed the FMAs as
 // SGPR operands: no LDS traffic and no VGPRs for activations in the inner loop. Per weight the
-// inner loop costs one byte->float convert and one FMA per token, plus a mask per 4 weights.
+// inner loop costs one FMA per token plus the conversion of the quant to fp32 (one
+// v_cvt_f32_ubyte per weight, or for 4-bit quants half a packed fp8 conversion), and a mask per
+// 4 weights.
 //
 // The affine block terms are factored out of the inner loop:
 //   sum_i w_i x_i = sum_j d*sc_j * sum_{i in j} q_i x_i  -  sum_j dmin*m_j * S_j     (Q4_K)
@@ -113,7 +115,7 @@ __device__ __forceinline__ void load_unit(Unit<FMT_Q8_0> &u, const uint8_t *row,
 // loads addressed with it cannot be hoisted far ahead of their use (which would need more
 // scalar registers than a wave has).
 __device__ __forceinline__ int after(int off, float dep) {
-  asm volatile("" : "+s"(off) : "v"(dep));
+  asm("" : "+s"(off) : "v"(dep));
   return off;
 }
 
@@ -177,28 +179,34 @@ __device__ __forceinline__ void unit_dot(const Unit<FMT_Q4_K> &u, const float *c
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     // quant bytes 32c..32c+31: low nibbles are sub-block 2c (weights 64c + 0..31), high
-    // nibbles are sub-block 2c+1 (weights 64c + 32..63), read as 16*q.
+    // nibbles are sub-block 2c+1 (weights 64c + 32..63).
     static_assert(NT == 1, "multi-token Q4_K streams 64-weight groups (stream_q4k_groups)");
     {
+      // quants come out of the fp8 converter as q * unit; 1/unit is folded into the scales
       float dl = 0.f, dh = 0.f;
 #pragma unroll
       for (int dw = 0; dw < 8; ++dw) {
         const uint32_t w = dword_of(u.v[1 + 2 * c + (dw >> 2)], dw & 3);
-        const uint32_t lo = opaque(w & 0x0F0F0F0Fu), hi = opaque(w & 0xF0F0F0F0u);
+        const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
         const int i = 64 * c + 4 * dw;
+        float f[4];
+        nibbles_to_float<false>(lo, f[0], f[1]);
+        nibbles_to_float<true>(lo, f[2], f[3]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          dl = __builtin_fmaf(byte_to_float(lo, e), xp[0][i + e], dl);
-          dh = __builtin_fmaf(byte_to_float(hi, e), xp[0][i + 32 + e], dh);
-        }
+        for (int e = 0; e < 4; ++e) dl = __builtin_fmaf(f[e], xp[0][i + e], dl);
+        nibbles_to_float<false>(hi, f[0], f[1]);
+        nibbles_to_float<true>(hi, f[2], f[3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dh = __builtin_fmaf(f[e], xp[0][i + 32 + e], dh);
       }
       bs[0] = __builtin_fmaf(sc[2 * c], dl, bs[0]);
-      bs[0] = __builtin_fmaf(sc[2 * c + 1] * 0.0625f, dh, bs[0]);
+      bs[0] = __builtin_fmaf(sc[2 * c + 1], dh, bs[0]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  const float dq = d / nibble_fp8_unit();  // exact: a power-of-two rescale
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = __builtin_fmaf(d, bs[t], __builtin_fmaf(-dmin, ms[t], acc[t]));
+  for (int t = 0; t < NT; ++t) acc[t] = __builtin_fmaf(dq, bs[t], __builtin_fmaf(-dmin, ms[t], acc[t]));
 }
 
 template <int NT>
@@ -352,18 +360,18 @@ __device__ __forceinline__ void stream_q4k_groups(const uint8_t *row, int u0, in
       sc1 = ((s2 >> (8 * b)) & 15u) | (((s0 >> (8 * b + 6)) & 3u) << 4);
       m1 = ((s2 >> (8 * b + 4)) & 15u) | (((s1 >> (8 * b + 6)) & 3u) << 4);
     }
-    const float dsc0 = d * (float)sc0, dsc1 = d * (float)sc1 * 0.0625f;
+    const float dq = d / nibble_fp8_unit();
+    const float dsc0 = dq * (float)sc0, dsc1 = dq * (float)sc1;
     const float dm0 = dmin * (float)m0, dm1 = dmin * (float)m1;
     float fl[32], fh[32];
 #pragma unroll
     for (int dw = 0; dw < 8; ++dw) {
       const uint32_t w = dword_of(cur[1 + (dw >> 2)], dw & 3);
-      const uint32_t lo = opaque(w & 0x0F0F0F0Fu), hi = opaque(w & 0xF0F0F0F0u);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        fl[4 * dw + e] = byte_to_float(lo, e);
-        fh[4 * dw + e] = byte_to_float(hi, e);
-      }
+      const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+      nibbles_to_float<false>(lo, fl[4 * dw], fl[4 * dw + 1]);
+      nibbles_to_float<true>(lo, fl[4 * dw + 2], fl[4 * dw + 3]);
+      nibbles_to_float<false>(hi, fh[4 * dw], fh[4 * dw + 1]);
+      nibbles_to_float<true>(hi, fh[4 * dw + 2], fh[4 * dw + 3]);
     }
     float prev = fl[0], prev2 = fh[0];
 #pragma unroll
@@ -409,6 +417,61 @@ __device__ __forceinline__ void stream_units(const uint8_t *row, int u0, int u1,
       cur = nxt;
     }
   }
+}
+
+// One workgroup's share of a GEMV tile: rows [row0, row0+64) (one per lane, clamped to n-1),
+// units [ku0, ku1) split over the waves (upw units each), NT tokens whose activation rows are
+// xr[t]. Leaves sum over this workgroup's units of w[row][:] . x[t][:] in lds_out[t*64 + lane]
+// (the first NT*64 floats of `lds`), summed over waves in wave order. `lds` must hold
+// max(NT * groups of the slice, waves * NT * 64) floats. Ends with a barrier.
+template <int FMT, int NT>
+__device__ __forceinline__ void gemv_tile(const uint8_t *__restrict__ w, int64_t row_bytes, int n,
+                                          int row0, int ku0, int ku1, int upw,
+                                          const float *const (&xr)[NT], float *lds) {
+  constexpr int G = Fmt<FMT>::group;
+  constexpr int GPU_ = 256 / G;  // groups per unit
+  const int nw = blockDim.x >> 6;
+  const int wave = wave_index();
+  const int lane = threadIdx.x & 63;
+  const int ngl = (ku1 - ku0) * GPU_;
+  // group sums of this slice of x, for every token of the tile
+  for (int i = threadIdx.x; i < NT * ngl; i += blockDim.x) {
+    const int t = i / ngl, gi = i - t * ngl;
+    const float *p = xr[t] + (int64_t)(ku0 * GPU_ + gi) * G;
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < G; ++e) s += p[e];
+    lds[i] = s;
+  }
+  __syncthreads();
+  const float *gs[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) gs[t] = lds + t * ngl - ku0 * GPU_;  // absolute group numbers
+  float acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = 0.f;
+  const int row = min(row0 + lane, n - 1);  // rows past n repeat the last row; never stored
+  const int u0 = ku0 + wave * upw, u1 = min(u0 + upw, ku1);
+  stream_units<FMT, NT>(w + (int64_t)row * row_bytes, u0, u1, xr, gs, acc);
+  __syncthreads();  // every wave is done with the group sums
+#pragma unroll
+  for (int t = 0; t < NT; ++t) lds[NT * 64 + (wave * NT + t) * 64 + lane] = acc[t];
+  __syncthreads();
+  for (int i = threadIdx.x; i < NT * 64; i += blockDim.x) {
+    const int t = i >> 6, l = i & 63;
+    float s = 0.f;
+    for (int v = 0; v < nw; ++v) s += lds[NT * 64 + (v * NT + t) * 64 + l];
+    lds[i] = s;
+  }
+  __syncthreads();
+}
+
+// LDS floats gemv_tile needs for NT tokens, `upk` units per slice and `waves` waves.
+template <int FMT>
+__host__ __device__ inline int gemv_tile_lds_floats(int nt, int upk, int waves) {
+  const int g = nt * upk * (256 / Fmt<FMT>::group);
+  const int r = nt * 64 + waves * nt * 64;
+  return g > r ? g : r;
 }
 
 }  // namespace tq

@@ -1,0 +1,42 @@
+// tq_moe.h -- host-side plan of one MoE layer call (internal to libtq).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+struct MoeExpertPtrs {
+  const void *m[3];  // gate [ffn][hidden], up [ffn][hidden], down [hidden][ffn] blobs
+};
+
+struct MoeShape {
+  int type;
+  int64_t hidden, ffn, n_experts, top_k, tokens;
+  int has_shared, renormalize, experts_on_host;
+  int64_t gate_bytes;    // bytes of one gate (= up) blob
+  int64_t expert_bytes;  // gate + up + down
+};
+
+struct MoePlan {
+  MoeShape s;
+  int64_t P;       // positions: T*k routed pairs, then T shared-expert rows
+  int max_active;  // upper bound of active experts (including the shared one)
+  int rtiles, hsplit, hpk;
+  int gu_rg, gu_ks, gu_upk, gu_waves, gu_upw;
+  int d_rg, d_ks, d_upk, d_waves, d_upw;
+  int64_t off_rpart, off_logits, off_ids, off_wts, off_counts, off_offsets, off_pairs, off_inv,
+      off_act, off_nact, off_gu, off_h, off_o, off_stage;
+  int64_t stage_stride;
+  int64_t bytes;
+};
+
+MoePlan plan_moe(const MoeShape &s);
+size_t group_lds_bytes(int64_t T, int64_t E);
+int launch_moe_routing(const MoePlan &p, const float *router_w, const float *x, char *ws,
+                       hipStream_t st);
+int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
+                       const MoeExpertPtrs &shared, const uint8_t *staging, const float *x,
+                       float *y, char *ws, hipStream_t st);
+
+}  // namespace tq

@@ -1,0 +1,541 @@
+// tq_moe.hip -- top-k routed MoE expert FFN: router logits, top-k, expert grouping, grouped
+// expert GEMV over the selected experts, SwiGLU, and the weighted combine.
+//
+// Decode path, all on one stream and without host synchronisation:
+//   k_router        logits partial sums (fp32), lane per expert row, tokens through scalar loads
+//   k_topk          one wave per token: logits = sum of the partials, k largest (ties to the lower
+//                   expert index), softmax weights renormalised over the selected experts
+//   k_group         one workgroup: per-expert counts, exclusive offsets and a stable scatter of the
+//                   (token, slot) pairs sorted by (expert, token); the list of active experts
+//   k_moe_gemv      grouped GEMV over (active expert, matrix, row group, k slice) work items;
+//                   empty items (experts beyond the active count) return at once
+//   k_moe_swiglu    h = silu(gate) * up from the gate/up slices
+//   k_moe_combine   y[t] = sum_j w[t][j] * o[pair (t, j)] + o_shared[t], slots in order
+// No atomic operation decides any order, so every output is deterministic.
+#include "tq_gemv_core.h"
+#include "tq_launch.h"
+#include "tq_moe.h"
+
+namespace tq {
+
+// ---- router logits ------------------------------------------------------------------------------
+// Grid: x = (expert row group, h slice), y = token tile of 8. partial layout [tile][hs][8][E].
+__global__ __launch_bounds__(256) void k_router(const float *__restrict__ wr, int E, int H,
+                                                const float *__restrict__ x, int T, int hsplit,
+                                                int hpk, float *__restrict__ part) {
+  __shared__ float red[4][8][64];
+  const int rgs = blockIdx.x / hsplit, hs = blockIdx.x - rgs * hsplit;
+  const int tile = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = wave_index(), nw = blockDim.x >> 6;
+  const int e = min(rgs * 64 + lane, E - 1);
+  const int h0 = hs * hpk, h1 = min(h0 + hpk, H);
+  const int per_wave = ((h1 - h0 + nw - 1) / nw + 3) & ~3;
+  const int a0 = h0 + wave * per_wave, a1 = min(a0 + per_wave, h1);
+  const float *xr[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) xr[t] = x + (int64_t)min(tile * 8 + t, T - 1) * H;
+  float acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = 0.f;
+  const float *wrow = wr + (int64_t)e * H;
+  for (int h = a0; h < a1; h += 4) {
+    const float4 wv = *reinterpret_cast<const float4 *>(wrow + h);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      acc[t] = __builtin_fmaf(wv.x, xr[t][h], acc[t]);
+      acc[t] = __builtin_fmaf(wv.y, xr[t][h + 1], acc[t]);
+      acc[t] = __builtin_fmaf(wv.z, xr[t][h + 2], acc[t]);
+      acc[t] = __builtin_fmaf(wv.w, xr[t][h + 3], acc[t]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) red[wave][t][lane] = acc[t];
+  __syncthreads();
+  for (int i = threadIdx.x; i < 8 * 64; i += blockDim.x) {
+    const int t = i >> 6, l = i & 63;
+    float s = 0.f;
+    for (int v = 0; v < nw; ++v) s += red[v][t][l];
+    const int ee = rgs * 64 + l;
+    if (ee < E) part[(((int64_t)tile * hsplit + hs) * 8 + t) * E + ee] = s;
+  }
+}
+
+// ---- top-k and softmax weights -----------------------------------------------------------------
+// One wave per token. Each lane holds the logits of experts lane, lane+64, ...
+
+__device__ __forceinline__ bool better(float va, int ea, float vb, int eb) {
+  return va > vb || (va == vb && ea < eb);
+}
+
+__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, int T, int E,
+                                              int hsplit, int topk, int renormalize,
+                                              float *__restrict__ logits, int *__restrict__ ids,
+                                              float *__restrict__ wts) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (blockDim.x >> 6) + (int)(threadIdx.x >> 6);
+  if (t >= T) return;  // whole wave
+  constexpr int MAXV = 16;  // E <= 1024
+  float v[MAXV];
+  const int nv = (E + 63) >> 6;
+  const int tile = t >> 3, tt = t & 7;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    v[i] = -INFINITY;
+    const int e = lane + 64 * i;
+    if (i < nv && e < E) {
+      float s = 0.f;
+      for (int hs = 0; hs < hsplit; ++hs) s += part[(((int64_t)tile * hsplit + hs) * 8 + tt) * E + e];
+      v[i] = s;
+      logits[(int64_t)t * E + e] = s;
+    }
+  }
+  unsigned taken = 0;  // bit i: expert lane + 64 i already selected
+  float sel0 = 0.f, denom = 0.f;
+  float selv[32];
+  int sele[32];
+  for (int j = 0; j < topk; ++j) {
+    float bv = -INFINITY;
+    int be = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      const int e = lane + 64 * i;
+      if (i < nv && e < E && !(taken >> i & 1u) && better(v[i], e, bv, be)) {
+        bv = v[i];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oe = __shfl_xor(be, off);
+      if (better(ov, oe, bv, be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    selv[j] = bv;
+    sele[j] = be;
+  }
+  sel0 = selv[0];
+  if (renormalize) {
+    for (int j = 0; j < topk; ++j) denom += expf(selv[j] - sel0);
+  } else {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      const int e = lane + 64 * i;
+      if (i < nv && e < E) s += expf(v[i] - sel0);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    denom = s;
+  }
+  if (lane == 0) {
+    for (int j = 0; j < topk; ++j) {
+      ids[(int64_t)t * topk + j] = sele[j];
+      wts[(int64_t)t * topk + j] = expf(selv[j] - sel0) / denom;
+    }
+  }
+}
+
+// ---- grouping --------------------------------------------------------------------------------------
+// One workgroup of 8 waves. Tokens are taken in chunks of 64, one per lane of a wave; a token
+// picks k distinct experts, so for one expert every lane of a chunk appears at most once.
+//   mask[e]    (per wave) the lanes of the current chunk routed to e, built with LDS atomic ORs,
+//              which commute, so the mask does not depend on the order of the updates.
+//   tab[c][e]  first the number of pairs of chunk c routed to e (popcount of the mask), then
+//              in place the number routed to e by the chunks before c.
+//   pairs[offsets[e] + tab[c][e] + r] = t*k + j, r = lanes of chunk c routed to e below t's lane.
+// act: [0, E+1) expert id, [E+1, 2E+2) first position, [2E+2, 3E+3) count, for the active experts
+// in ascending expert order and the shared expert (id E, positions T*k .. T*k+T-1) last.
+__global__ __launch_bounds__(512) void k_group(const int *__restrict__ ids, int T, int topk, int E,
+                                               int has_shared, int *__restrict__ counts,
+                                               int *__restrict__ offsets, int *__restrict__ pairs,
+                                               int *__restrict__ inv, int *__restrict__ act,
+                                               int *__restrict__ n_active) {
+  extern __shared__ unsigned long long smem64[];
+  const int nchunks = (T + 63) >> 6;
+  unsigned long long *masks = smem64;                                   // [8][E]
+  int *off = reinterpret_cast<int *>(masks + 8 * E);                    // [E]
+  unsigned short *tab = reinterpret_cast<unsigned short *>(off + E);    // [nchunks][E]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  unsigned long long *mymask = masks + wave * E;
+  for (int i = threadIdx.x; i < 8 * E; i += blockDim.x) masks[i] = 0ull;
+  for (int i = threadIdx.x; i < nchunks * E; i += blockDim.x) tab[i] = 0;
+  __syncthreads();
+  // per-chunk counts
+  for (int c = wave; c < nchunks; c += nw) {
+    const int t = c * 64 + lane;
+    const bool live = t < T;
+    if (live)
+      for (int j = 0; j < topk; ++j) atomicOr(&mymask[ids[t * topk + j]], 1ull << lane);
+    __builtin_amdgcn_wave_barrier();
+    if (live)
+      for (int j = 0; j < topk; ++j) {
+        const int e = ids[t * topk + j];
+        tab[c * E + e] = (unsigned short)__popcll(mymask[e]);
+      }
+    __builtin_amdgcn_wave_barrier();
+    if (live)
+      for (int j = 0; j < topk; ++j) mymask[ids[t * topk + j]] = 0ull;
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    unsigned run = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      const unsigned v = tab[c * E + e];
+      tab[c * E + e] = (unsigned short)run;
+      run += v;
+    }
+    off[e] = (int)run;  // the count, for now
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0, na = 0;
+    for (int e = 0; e < E; ++e) {
+      const int cnt = off[e];
+      counts[e] = cnt;
+      offsets[e] = run;
+      if (cnt > 0) {
+        act[na] = e;
+        act[(E + 1) + na] = run;
+        act[2 * (E + 1) + na] = cnt;
+        ++na;
+      }
+      off[e] = run;
+      run += cnt;
+    }
+    offsets[E] = run;
+    if (has_shared) {
+      act[na] = E;
+      act[(E + 1) + na] = run;
+      act[2 * (E + 1) + na] = T;
+      ++na;
+    }
+    *n_active = na;
+  }
+  __syncthreads();
+  // stable scatter
+  for (int c = wave; c < nchunks; c += nw) {
+    const int t = c * 64 + lane;
+    const bool live = t < T;
+    if (live)
+      for (int j = 0; j < topk; ++j) atomicOr(&mymask[ids[t * topk + j]], 1ull << lane);
+    __builtin_amdgcn_wave_barrier();
+    if (live) {
+      const unsigned long long below = (1ull << lane) - 1ull;
+      for (int j = 0; j < topk; ++j) {
+        const int e = ids[t * topk + j];
+        const int pos = off[e] + (int)tab[c * E + e] + __popcll(mymask[e] & below);
+        pairs[pos] = t * topk + j;
+        inv[t * topk + j] = pos;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (live)
+      for (int j = 0; j < topk; ++j) mymask[ids[t * topk + j]] = 0ull;
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+size_t group_lds_bytes(int64_t T, int64_t E) {
+  const int64_t nchunks = (T + 63) / 64;
+  return (size_t)(8 * E * 8 + E * 4 + ((nchunks * E * 2 + 7) & ~(int64_t)7));
+}
+
+// ---- grouped expert GEMV -----------------------------------------------------------------------
+// Work item = ((active slot a, matrix m), row group, k slice); the grid covers the largest
+// possible number of active experts and items past the actual count return at once. The token
+// rows of an expert are processed in tiles of up to 8.
+
+struct MoeGemvArgs {
+  const MoeExpertPtrs *experts;  // device table [E]
+  MoeExpertPtrs shared;          // by value (id E)
+  const uint8_t *staging;        // non-null: routed expert a's blobs at staging + a * stage_stride
+  int64_t stage_stride;
+  int64_t stage_off[3];          // offsets of gate / up / down inside one staged expert
+  const int *act;
+  const int *n_active;
+  const int *pairs;
+  int E, topk, Tk;
+  int mat0, nmat;                // matrices m = mat0 .. mat0 + nmat - 1 (0 gate, 1 up, 2 down)
+  int n_rows, units;             // rows of each matrix, units of 256 weights along k
+  int64_t row_bytes;
+  int rowgroups, ksplit, upk, upw;
+  const float *xsrc;             // activation rows: by token (gate/up) or by position (down)
+  int64_t ldx;
+  int x_by_token;
+  float *out;                    // [nmat][ksplit][P][n_rows]
+  int64_t P;
+};
+
+template <int FMT, int NT>
+__device__ __forceinline__ void moe_tile(const MoeGemvArgs &a, const uint8_t *w, int m, int rg,
+                                         int ks, int p0, float *lds) {
+  const int row0 = rg * 64;
+  const int ku0 = ks * a.upk, ku1 = min(ku0 + a.upk, a.units);
+  const float *xr[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int p = p0 + t;
+    int64_t r = p;
+    if (a.x_by_token) r = p >= a.Tk ? p - a.Tk : a.pairs[p] / a.topk;
+    xr[t] = a.xsrc + r * a.ldx;
+  }
+  gemv_tile<FMT, NT>(w, a.row_bytes, a.n_rows, row0, ku0, ku1, a.upw, xr, lds);
+  float *o = a.out + ((int64_t)(m - a.mat0) * a.ksplit + ks) * a.P * a.n_rows;
+  for (int i = threadIdx.x; i < NT * 64; i += blockDim.x) {
+    const int t = i >> 6, l = i & 63;
+    if (row0 + l < a.n_rows) o[(int64_t)(p0 + t) * a.n_rows + row0 + l] = lds[i];
+  }
+  __syncthreads();  // lds is reused by the next tile
+}
+
+template <int FMT>
+__global__ __launch_bounds__(512) void k_moe_gemv(MoeGemvArgs a) {
+  extern __shared__ float lds[];
+  const int per_slot = a.nmat * a.rowgroups * a.ksplit;
+  const int slot = blockIdx.x / per_slot;
+  if (slot >= *a.n_active) return;
+  int r = blockIdx.x - slot * per_slot;
+  const int mi = r / (a.rowgroups * a.ksplit);
+  r -= mi * a.rowgroups * a.ksplit;
+  const int rg = r / a.ksplit, ks = r - rg * a.ksplit;
+  const int m = a.mat0 + mi;
+  const int e = a.act[slot], p0 = a.act[(a.E + 1) + slot], cnt = a.act[2 * (a.E + 1) + slot];
+  const uint8_t *w;
+  if (e == a.E) {
+    w = (const uint8_t *)a.shared.m[m];
+  } else if (a.staging != nullptr) {
+    w = a.staging + (int64_t)slot * a.stage_stride + a.stage_off[m];
+  } else {
+    w = (const uint8_t *)a.experts[e].m[m];
+  }
+  for (int t0 = 0; t0 < cnt; t0 += 8) {
+    const int nt = min(8, cnt - t0);
+    switch (nt) {
+      case 1: moe_tile<FMT, 1>(a, w, m, rg, ks, p0 + t0, lds); break;
+      case 2: moe_tile<FMT, 2>(a, w, m, rg, ks, p0 + t0, lds); break;
+      case 3: moe_tile<FMT, 3>(a, w, m, rg, ks, p0 + t0, lds); break;
+      case 4: moe_tile<FMT, 4>(a, w, m, rg, ks, p0 + t0, lds); break;
+      case 5: moe_tile<FMT, 5>(a, w, m, rg, ks, p0 + t0, lds); break;
+      case 6: moe_tile<FMT, 6>(a, w, m, rg, ks, p0 + t0, lds); break;
+      case 7: moe_tile<FMT, 7>(a, w, m, rg, ks, p0 + t0, lds); break;
+      default: moe_tile<FMT, 8>(a, w, m, rg, ks, p0 + t0, lds); break;
+    }
+  }
+}
+
+// ---- SwiGLU over the gate/up slices and the combine ---------------------------------------------
+
+__global__ __launch_bounds__(256) void k_moe_swiglu(const float *__restrict__ gu, int ksplit,
+                                                    int64_t P, int F, float *__restrict__ h) {
+  const int64_t total = P * F, stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t slice = P * F;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    float g = 0.f, u = 0.f;
+    for (int q = 0; q < ksplit; ++q) {
+      g += gu[(int64_t)q * slice + i];
+      u += gu[((int64_t)ksplit + q) * slice + i];
+    }
+    h[i] = g * u / (1.f + expf(-g));
+  }
+}
+
+__global__ __launch_bounds__(256) void k_moe_combine(const float *__restrict__ o, int ksplit,
+                                                     int64_t P, int H, const int *__restrict__ inv,
+                                                     const float *__restrict__ wts, int T,
+                                                     int topk, int has_shared,
+                                                     float *__restrict__ y) {
+  const int64_t total = (int64_t)T * H, stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t slice = P * H;
+  const int Tk = T * topk;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int t = (int)(i / H), c = (int)(i - (int64_t)t * H);
+    float acc = 0.f;
+    for (int j = 0; j < topk; ++j) {
+      const int64_t pos = inv[t * topk + j];
+      float s = 0.f;
+      for (int q = 0; q < ksplit; ++q) s += o[q * slice + pos * H + c];
+      acc = __builtin_fmaf(wts[t * topk + j], s, acc);
+    }
+    if (has_shared) {
+      float s = 0.f;
+      for (int q = 0; q < ksplit; ++q) s += o[q * slice + (int64_t)(Tk + t) * H + c];
+      acc += s;
+    }
+    y[i] = acc;
+  }
+}
+
+// ---- host side ---------------------------------------------------------------------------------
+
+static int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
+
+static int clampi(int v, int lo, int hi) { return v < lo ? lo : v > hi ? hi : v; }
+
+MoePlan plan_moe(const MoeShape &s) {
+  MoePlan p;
+  p.s = s;
+  const int64_t T = s.tokens, E = s.n_experts, k = s.top_k;
+  p.P = T * k + (s.has_shared ? T : 0);
+  p.max_active = (int)((E < T * k ? E : T * k) + (s.has_shared ? 1 : 0));
+  // router: 64 expert rows per workgroup, token tiles of 8, h split to fill the chip
+  p.rtiles = (int)((T + 7) / 8);
+  const int rrg = (int)((E + 63) / 64);
+  int hs = (512 + rrg * p.rtiles - 1) / (rrg * p.rtiles);
+  hs = clampi(hs, 1, (int)(s.hidden / 256));
+  p.hpk = (int)(((s.hidden + hs - 1) / hs + 3) & ~3);
+  p.hsplit = (int)((s.hidden + p.hpk - 1) / p.hpk);
+  // gate/up: F rows over k = hidden; down: hidden rows over k = F
+  auto split = [&](int64_t rows, int64_t kdim, int nmat, int &rowgroups, int &ks, int &upk,
+                   int &waves, int &upw) {
+    const int units = (int)(kdim / 256);
+    rowgroups = (int)((rows + 63) / 64);
+    const int64_t items = (int64_t)p.max_active * nmat * rowgroups;
+    int want = (int)((1024 + items - 1) / items);
+    want = clampi(want, 1, units);
+    upk = (units + want - 1) / want;
+    ks = (units + upk - 1) / upk;
+    int w = clampi(upk, 1, 4);
+    upw = (upk + w - 1) / w;
+    waves = (upk + upw - 1) / upw;
+  };
+  split(s.ffn, s.hidden, 2, p.gu_rg, p.gu_ks, p.gu_upk, p.gu_waves, p.gu_upw);
+  split(s.hidden, s.ffn, 1, p.d_rg, p.d_ks, p.d_upk, p.d_waves, p.d_upw);
+  // workspace carve-up
+  int64_t o = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  p.off_rpart = take((int64_t)p.rtiles * p.hsplit * 8 * E * 4);
+  p.off_logits = take(T * E * 4);
+  p.off_ids = take(T * k * 4);
+  p.off_wts = take(T * k * 4);
+  p.off_counts = take(E * 4);
+  p.off_offsets = take((E + 1) * 4);
+  p.off_pairs = take(T * k * 4);
+  p.off_inv = take(T * k * 4);
+  p.off_act = take(3 * (E + 1) * 4);
+  p.off_nact = take(4);
+  p.off_gu = take((int64_t)2 * p.gu_ks * p.P * s.ffn * 4);
+  p.off_h = take(p.P * s.ffn * 4);
+  p.off_o = take((int64_t)p.d_ks * p.P * s.hidden * 4);
+  p.stage_stride = align256(s.expert_bytes);
+  p.off_stage = take(s.experts_on_host ? (int64_t)(p.max_active) * p.stage_stride : 0);
+  p.bytes = o;
+  return p;
+}
+
+template <int FMT>
+static int moe_gemv_launch(MoeGemvArgs a, int max_active, int waves, hipStream_t st) {
+  const int grid = max_active * a.nmat * a.rowgroups * a.ksplit;
+  const size_t lds = (size_t)4 * gemv_tile_lds_floats<FMT>(8, a.upk, waves);
+  if (lds > 65536) return -2;
+  hipLaunchKernelGGL(k_moe_gemv<FMT>, dim3((unsigned)grid), dim3(64 * waves), lds, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+static int moe_gemv_dispatch(int fmt, const MoeGemvArgs &a, int max_active, int waves,
+                             hipStream_t st) {
+  switch (fmt) {
+    case FMT_Q4_K: return moe_gemv_launch<FMT_Q4_K>(a, max_active, waves, st);
+    case FMT_Q6_K: return moe_gemv_launch<FMT_Q6_K>(a, max_active, waves, st);
+    default: return moe_gemv_launch<FMT_Q8_0>(a, max_active, waves, st);
+  }
+}
+
+int launch_moe_routing(const MoePlan &p, const float *router_w, const float *x, char *ws,
+                       hipStream_t st) {
+  const MoeShape &s = p.s;
+  const int E = (int)s.n_experts, H = (int)s.hidden, T = (int)s.tokens, k = (int)s.top_k;
+  float *rpart = (float *)(ws + p.off_rpart);
+  const dim3 rgrid((unsigned)(((E + 63) / 64) * p.hsplit), (unsigned)p.rtiles);
+  hipLaunchKernelGGL(k_router, rgrid, dim3(256), 0, st, router_w, E, H, x, T, p.hsplit, p.hpk, rpart);
+  hipLaunchKernelGGL(k_topk, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, rpart, T, E, p.hsplit,
+                     k, s.renormalize, (float *)(ws + p.off_logits), (int *)(ws + p.off_ids),
+                     (float *)(ws + p.off_wts));
+  const size_t glds = group_lds_bytes(s.tokens, s.n_experts);
+  hipLaunchKernelGGL(k_group, dim3(1), dim3(512), glds, st, (const int *)(ws + p.off_ids), T, k, E,
+                     s.has_shared, (int *)(ws + p.off_counts), (int *)(ws + p.off_offsets),
+                     (int *)(ws + p.off_pairs), (int *)(ws + p.off_inv), (int *)(ws + p.off_act),
+                     (int *)(ws + p.off_nact));
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
+                       const MoeExpertPtrs &shared, const uint8_t *staging, const float *x,
+                       float *y, char *ws, hipStream_t st) {
+  const MoeShape &s = p.s;
+  const int E = (int)s.n_experts, T = (int)s.tokens, k = (int)s.top_k;
+  MoeGemvArgs a{};
+  a.experts = experts_dev;
+  a.shared = shared;
+  a.staging = staging;
+  a.stage_stride = p.stage_stride;
+  a.stage_off[0] = 0;
+  a.stage_off[1] = s.gate_bytes;
+  a.stage_off[2] = 2 * s.gate_bytes;
+  a.act = (const int *)(ws + p.off_act);
+  a.n_active = (const int *)(ws + p.off_nact);
+  a.pairs = (const int *)(ws + p.off_pairs);
+  a.E = E;
+  a.topk = k;
+  a.Tk = T * k;
+  a.P = p.P;
+  // gate and up
+  a.mat0 = 0;
+  a.nmat = 2;
+  a.n_rows = (int)s.ffn;
+  a.units = (int)(s.hidden / 256);
+  a.row_bytes = s.hidden / fmt_block_weights(s.type) * fmt_block_bytes(s.type);
+  a.rowgroups = p.gu_rg;
+  a.ksplit = p.gu_ks;
+  a.upk = p.gu_upk;
+  a.upw = p.gu_upw;
+  a.xsrc = x;
+  a.ldx = s.hidden;
+  a.x_by_token = 1;
+  a.out = (float *)(ws + p.off_gu);
+  int rc = moe_gemv_dispatch(s.type, a, p.max_active, p.gu_waves, st);
+  if (rc) return rc;
+  float *h = (float *)(ws + p.off_h);
+  {
+    const int64_t total = p.P * s.ffn;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 16384) blocks = 16384;
+    hipLaunchKernelGGL(k_moe_swiglu, dim3((unsigned)blocks), dim3(256), 0, st, (const float *)a.out,
+                       p.gu_ks, p.P, (int)s.ffn, h);
+  }
+  // down
+  a.mat0 = 2;
+  a.nmat = 1;
+  a.n_rows = (int)s.hidden;
+  a.units = (int)(s.ffn / 256);
+  a.row_bytes = s.ffn / fmt_block_weights(s.type) * fmt_block_bytes(s.type);
+  a.rowgroups = p.d_rg;
+  a.ksplit = p.d_ks;
+  a.upk = p.d_upk;
+  a.upw = p.d_upw;
+  a.xsrc = h;
+  a.ldx = s.ffn;
+  a.x_by_token = 0;
+  a.out = (float *)(ws + p.off_o);
+  rc = moe_gemv_dispatch(s.type, a, p.max_active, p.d_waves, st);
+  if (rc) return rc;
+  {
+    const int64_t total = (int64_t)T * s.hidden;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 16384) blocks = 16384;
+    hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)blocks), dim3(256), 0, st, (const float *)a.out,
+                       p.d_ks, p.P, (int)s.hidden, (const int *)(ws + p.off_inv),
+                       (const float *)(ws + p.off_wts), T, k, s.has_shared, y);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace tq

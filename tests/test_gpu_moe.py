@@ -1,0 +1,185 @@
+"""GPU parity of tq_moe_ffn (router, top-k, grouping, grouped expert FFN, combine) vs the oracle.
+
+Contract checked here:
+  * router logits within 1e-3 * sum|x w| + 1e-5 of the oracle's fp64 logits;
+  * selection: the oracle's top-k re-run on the GPU's fp32 logits gives the same ids, bitwise;
+    weights within 1e-5 * w + 1e-7; with the oracle's own fp64 logits only near ties may differ;
+  * grouping (counts, offsets, pairs) bitwise equal to the oracle's grouping of the GPU ids;
+  * y within 1e-3 * sum|products| + 1e-5 of the oracle MoE evaluated with that routing;
+  * bitwise determinism across calls.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_util import assert_product_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+tq = pytest.importorskip("moe_expert_ffn_q4_amd")
+
+
+def _case(*a):
+    print("case:", *a, flush=True)
+
+
+def _layer_to_device(t, shape, layer, top_k, renormalize=True):
+    experts = [tuple(dev(b) for b in e) for e in layer["experts"]]
+    shared = tuple(dev(b) for b in layer["shared"]) if layer["shared"] is not None else None
+    moe = tq.MoeLayer(t, shape["hidden"], shape["ffn"], dev(layer["router"]), experts, shared,
+                      top_k=top_k, renormalize=renormalize)
+    return moe
+
+
+def _run(moe, x, E, k):
+    T = x.shape[0]
+    r = dict(topk_ids=torch.empty((T, k), dtype=torch.int32, device="cuda:0"),
+             topk_w=torch.empty((T, k), dtype=torch.float32, device="cuda:0"),
+             logits=torch.empty((T, E), dtype=torch.float32, device="cuda:0"),
+             counts=torch.empty(E, dtype=torch.int32, device="cuda:0"),
+             offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda:0"),
+             pairs=torch.empty(T * k, dtype=torch.int32, device="cuda:0"))
+    y = moe(dev(x), routing=r)
+    return host(y), {f: host(v) for f, v in r.items()}
+
+
+def check_moe(t, shape, layer, x, k, tokens=None, renormalize=True, moe=None):
+    E = len(layer["experts"])
+    moe = moe or _layer_to_device(t, shape, layer, k, renormalize)
+    y, r = _run(moe, x, E, k)
+    T = x.shape[0]
+    # logits
+    ref_lg = oracle.router_logits(x, layer["router"])
+    mag_lg = np.abs(x.astype(np.float64)) @ np.abs(layer["router"].astype(np.float64)).T
+    assert_product_close(r["logits"], ref_lg, mag_lg, what="router logits")
+    # selection on the GPU's fp32 logits: bitwise
+    ids, wts = oracle.topk(r["logits"], k, renormalize)
+    assert np.array_equal(r["topk_ids"], ids), "top-k ids"
+    assert np.all(np.abs(r["topk_w"] - wts) <= 1e-5 * wts + 1e-7), "routing weights"
+    # selection on the oracle's own logits: differences only at near ties
+    own, _ = oracle.topk(ref_lg, k, renormalize)
+    diff = np.any(np.sort(own, 1) != np.sort(ids, 1), axis=1)
+    if diff.any() and k < E:
+        srt = np.sort(ref_lg, 1)[:, ::-1]
+        gap = srt[:, k - 1] - srt[:, k]
+        scale = np.max(mag_lg, axis=1)
+        assert np.all(gap[diff] < 1e-4 * scale[diff]), "selection differs beyond a near tie"
+    # grouping: bitwise
+    counts, offsets, pairs = oracle.group(ids, E)
+    assert np.array_equal(r["counts"], counts) and np.array_equal(r["offsets"], offsets)
+    assert np.array_equal(r["pairs"], pairs)
+    # output, with the GPU's routing and oracle weights from the GPU's logits
+    toks = np.arange(T) if tokens is None else np.asarray(tokens)
+    ref, mag = oracle.moe(t, shape["hidden"], shape["ffn"], layer["experts"], layer["shared"], x,
+                          ids, wts, tokens=toks)
+    assert_product_close(y[toks], ref, mag, what=f"moe {t} T={T}")
+    return moe, y
+
+
+SMALL = [
+    ("q4_k", dict(hidden=512, ffn=1024, n_experts=8, shared=False), 2, [1, 5, 64, 130]),
+    ("q4_k", dict(hidden=768, ffn=512, n_experts=16, shared=True), 4, [1, 33]),
+    ("q8_0", dict(hidden=512, ffn=768, n_experts=6, shared=True), 2, [3, 70]),
+    ("q6_k", dict(hidden=1024, ffn=512, n_experts=5, shared=False), 3, [2, 65]),
+]
+
+
+@pytest.mark.parametrize("t,shape,k,Ts", SMALL, ids=lambda v: str(v)[:24])
+def test_moe_small_shapes(t, shape, k, Ts):
+    layer = synth.moe_layer(shape, t, seed=201, tag=f"small-{t}")
+    moe = None
+    for T in Ts:
+        _case("moe-small", t, shape, k, T)
+        x = synth.normal_f32(synth.rng(201, "x", t, T), (T, shape["hidden"]))
+        moe, y = check_moe(t, shape, layer, x, k, moe=moe)
+        y2, _ = _run(moe, x, shape["n_experts"], k)
+        assert np.array_equal(y, y2), "not deterministic"
+
+
+def test_moe_not_renormalized():
+    t, shape, k = "q4_k", dict(hidden=512, ffn=512, n_experts=8, shared=False), 2
+    layer = synth.moe_layer(shape, t, seed=202, tag="norenorm")
+    x = synth.normal_f32(synth.rng(202, "x"), (9, 512))
+    check_moe(t, shape, layer, x, k, renormalize=False)
+
+
+def test_moe_equal_logits_all_tokens_on_first_experts():
+    """A zero router: every logit ties, so every token picks experts 0..k-1 with weight 1/k."""
+    t, shape, k = "q4_k", dict(hidden=512, ffn=512, n_experts=8, shared=True), 2
+    layer = synth.moe_layer(shape, t, seed=203, tag="ties")
+    layer["router"] = np.zeros_like(layer["router"])
+    x = synth.normal_f32(synth.rng(203, "x"), (70, 512))
+    moe, _ = check_moe(t, shape, layer, x, k)
+    _, r = _run(moe, x, 8, k)
+    assert np.all(r["topk_ids"] == np.arange(k)) and np.allclose(r["topk_w"], 0.5)
+    assert list(r["counts"]) == [70, 70, 0, 0, 0, 0, 0, 0]
+
+
+def test_moe_single_expert_equals_dense_ffn():
+    """E = 1, k = 1: the layer is one SwiGLU FFN; compare with tq_gemv + tq_swiglu + tq_gemv."""
+    t, shape = "q4_k", dict(hidden=512, ffn=1024, n_experts=1, shared=False)
+    layer = synth.moe_layer(shape, t, seed=204, tag="one")
+    x = synth.normal_f32(synth.rng(204, "x"), (5, 512))
+    _, y = check_moe(t, shape, layer, x, 1)
+    g, u, d = (dev(b) for b in layer["experts"][0])
+    xd = dev(x)
+    hg = tq.gemv(t, g, 1024, 512, xd)
+    hu = tq.gemv(t, u, 1024, 512, xd)
+    yd = host(tq.gemv(t, d, 512, 1024, tq.swiglu(hg, hu)))
+    ref, mag = oracle.moe(t, 512, 1024, layer["experts"], None, x, np.zeros((5, 1), np.int32),
+                          np.ones((5, 1)))
+    assert_product_close(yd, ref, mag, what="chained dense")
+    assert_product_close(y, ref, mag, what="moe E=1")
+
+
+def test_moe_top_k_equals_n_experts():
+    t, shape = "q4_k", dict(hidden=512, ffn=512, n_experts=4, shared=False)
+    layer = synth.moe_layer(shape, t, seed=205, tag="dense-mix")
+    x = synth.normal_f32(synth.rng(205, "x"), (17, 512))
+    check_moe(t, shape, layer, x, 4)
+
+
+def test_moe_rejects_bad_arguments():
+    t, shape = "q4_k", dict(hidden=512, ffn=512, n_experts=4, shared=False)
+    layer = synth.moe_layer(shape, t, seed=206, tag="bad")
+    moe = _layer_to_device(t, shape, layer, 2)
+    x = dev(synth.normal_f32(synth.rng(206, "x"), (3, 512)))
+    small = torch.empty(256, dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(tq.TQError) as e:
+        moe(x, ws=small)
+    assert e.value.status == 4
+    moe.desc.top_k = 5
+    with pytest.raises(tq.TQError) as e:
+        moe(x)
+    assert e.value.status == 2
+
+
+# ---- full-size layers, sampled tokens --------------------------------------------------------
+
+
+@pytest.fixture(scope="module")
+def mixtral():
+    return synth.moe_layer(synth.MIXTRAL, "q4_k", tag="mixtral")
+
+
+@pytest.mark.parametrize("T", [1, 16, 64])
+def test_moe_mixtral_shape_sampled_tokens(mixtral, T):
+    _case("mixtral", T)
+    x = synth.normal_f32(synth.rng(synth.DEFAULT_SEED, "mixtral-x", T), (T, 4096))
+    toks = [0] if T == 1 else [0, T // 2, T - 1]
+    check_moe("q4_k", synth.MIXTRAL, mixtral, x, 2, tokens=toks)
+
+
+@pytest.fixture(scope="module")
+def deepseek():
+    return synth.moe_layer(synth.DEEPSEEK, "q4_k", tag="deepseek")
+
+
+@pytest.mark.parametrize("T", [1, 256])
+def test_moe_deepseek_shape_sampled_tokens(deepseek, T):
+    _case("deepseek", T)
+    x = synth.normal_f32(synth.rng(synth.DEFAULT_SEED, "deepseek-x", T), (T, 7168))
+    toks = [0] if T == 1 else [0, 255]
+    check_moe("q4_k", synth.DEEPSEEK, deepseek, x, 8, tokens=toks)
