@@ -37,8 +37,11 @@ def _args():
                         "MoE layer at --batch tokens")
     p.add_argument("--seed", type=int, default=42)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=15.0,
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget of the oracle sample")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run one plain 1 GiB device copy (the known-size reference for the "
+                        "FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
 
 
@@ -70,7 +73,7 @@ def make_step(tq, torch, layers, batch, events=None):
     L = tq.lib()
     ws_bytes = max(tq.gemv_workspace_bytes("q4_k", n, k, batch)
                    for n, k in ((4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)))
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
 
     def gemv(name, projs, x):
         w, n, k = projs[name]
@@ -101,10 +104,9 @@ def make_step(tq, torch, layers, batch, events=None):
 
 
 def cpu_baseline(synth, batch, seed, budget_s):
-    """The oracle (as it is) on a bounded sample of the same step: a growing subset of the
-    output rows of layer 0's seven projections, scaled to a full 32-layer step."""
-    import numpy as np
-
+    """The oracle (as it is) on a bounded sample of the same step: whole layers (layer 0's seven
+    Q4_K projections at the bench's batch), repeated until about budget_s of CPU time has been
+    spent, scaled to a 32-layer step."""
     import oracle
 
     shape = synth.LLAMA8B
@@ -112,27 +114,21 @@ def cpu_baseline(synth, batch, seed, budget_s):
     for name, n, k in synth.dense_projections(shape):
         w = synth.blob("q4_k", synth.rng(seed, "8b", 0, name), n, k)
         x = synth.normal_f32(synth.rng(seed, "cpu-x", name, batch), (batch, k))
-        projs.append((name, w, n, k, x))
-    total_rows = sum(n for _, _, n, _, _ in projs)
-    frac = 1.0 / 64
-    elapsed = 0.0
+        projs.append((w, n, k, x))
+    layers = 0
+    t0 = time.perf_counter()
     while True:
-        t0 = time.perf_counter()
-        rows_done = 0
-        for name, w, n, k, x in projs:
-            r = max(1, int(n * frac))
-            oracle.gemv("q4_k", w, n, k, x, rows=np.arange(r))
-            rows_done += r
+        for w, n, k, x in projs:
+            oracle.gemv("q4_k", w, n, k, x)
+        layers += 1
         elapsed = time.perf_counter() - t0
-        if elapsed * 2 > budget_s or frac >= 1.0:
+        if elapsed >= budget_s or layers >= 4 * shape["layers"]:
             break
-        frac = min(1.0, frac * 2)
-    layer_s = elapsed * total_rows / rows_done
-    step_s = layer_s * shape["layers"]
+    step_s = elapsed / layers * shape["layers"]
     return {"value": batch / step_s, "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{rows_done} of {total_rows} output rows of one layer's 7 Q4_K projections "
-                      f"at batch {batch} ({elapsed:.1f} s), scaled linearly to 32 layers"}
+            "sample": f"{layers} full layers (7 Q4_K projections each, batch {batch}) in "
+                      f"{elapsed:.1f} s, scaled to a 32-layer step"}
 
 
 def moe_bench(args, torch, tq, synth):
@@ -259,9 +255,15 @@ def main():
         "step_gbs": round(step_bytes / (ms_per_step / 1000) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "tq_gemv Q4_K (k_gemv + k_gemv_reduce)",
+                     "kernel": "tq_gemv Q4_K batch 1 (tq::k_gemv_kl)" if args.batch == 1
+                               else "tq_gemv Q4_K (tq::k_gemv)",
                      "avg_launch_us": round(kernel_s * 1e6 / len(events), 3)},
     }
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(synth, args.batch, args.seed, args.cpu_seconds)
     print(json.dumps(out), flush=True)

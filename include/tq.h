@@ -75,10 +75,11 @@ int tq_dequant(int type, const void *w, int64_t n, int64_t k, int out_type, void
  *   x          [batch][k] fp32, 4-byte aligned; y [batch][n] fp32, 4-byte aligned; y must not
  *              overlap w or x.
  *   workspace  device scratch of at least tq_gemv_workspace_bytes(type, n, k, batch) bytes,
- *              256-byte aligned, contents irrelevant; it lets the k dimension be split across
- *              workgroups (partial sums are added by a second kernel in a fixed order, so results
- *              stay deterministic). NULL or too small: no split (slower when n is small).
- *              Calls that run concurrently must not share a workspace.
+ *              256-byte aligned, zero-filled before its first use; every call leaves its first
+ *              64 KiB (completion counters) zeroed again. It lets the k dimension be split across
+ *              workgroups; the partial sums are added in a fixed order, so results stay
+ *              deterministic. NULL or too small: no split (slower when n is small). Calls that
+ *              run concurrently must not share a workspace.
  *   n >= 1, k >= block size with k % block == 0, 1 <= batch <= 4096. Weights are streamed once
  *   per group of up to 8 tokens.
  */

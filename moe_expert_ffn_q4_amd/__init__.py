@@ -123,13 +123,14 @@ def dequant(t, w: torch.Tensor, n: int, k: int, out_dtype: str = "f32", out=None
 _workspaces: dict = {}
 
 
-def workspace(nbytes: int, device=None) -> torch.Tensor:
-    """A zero-filled device scratch buffer of at least nbytes, reused across calls (one per
-    device; calls on one stream may share it)."""
+def workspace(nbytes: int, device=None, purpose: str = "gemv") -> torch.Tensor:
+    """A zero-filled device scratch buffer of at least nbytes, reused across calls on one stream.
+    One buffer per (device, purpose): tq_gemv keeps completion counters at the start of its
+    workspace (zero between calls), so it must not share a buffer with tq_moe_ffn."""
     dev = torch.device(device if device is not None else "cuda")
     if dev.index is None:
         dev = torch.device(dev.type, torch.cuda.current_device())
-    key = (dev.type, dev.index)
+    key = (dev.type, dev.index, purpose)
     buf = _workspaces.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
@@ -203,7 +204,7 @@ class MoeLayer:
             out = torch.empty_like(x)
         if ws is None:
             need = self.workspace_bytes(T)
-            ws = workspace(need, x.device) if need else None
+            ws = workspace(need, x.device, "moe") if need else None
         r = None
         if routing is not None:
             r = MoeRouting(*[(routing[f].data_ptr() if routing.get(f) is not None else None)

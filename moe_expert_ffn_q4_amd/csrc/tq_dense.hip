@@ -113,9 +113,11 @@ int launch_dequant(int fmt, const void *w, int64_t n, int64_t k, int out_type, v
 // Work decomposition: the rows are cut into groups of 64 (one lane per row) and the k range into
 // `ksplit` slices of `upk` units; one workgroup per (row group, slice). Inside a workgroup the
 // waves split the slice further and combine their partial sums through LDS in wave order. When
-// ksplit > 1 each workgroup stores its partial sums to the workspace and a second kernel adds the
-// slices in slice order, so the result is deterministic (no atomics, nothing to reset between
-// calls).
+// ksplit > 1 each workgroup stores its partial sums to the workspace; the last workgroup of a row
+// group to arrive (counted with a device-scope atomic) adds the slices in slice order. Which
+// workgroup does the adding does not change the order of the additions, so the result is
+// deterministic. The counters live in the first kCounterBytes of the workspace, apart from the
+// partial sums; they start at zero and every call leaves them at zero.
 
 struct GemvPlan {
   int rowgroups, ksplit, upk, waves, upw;
@@ -143,13 +145,15 @@ GemvPlan plan_gemv(int64_t n, int64_t k, bool split_allowed) {
   return p;
 }
 
+static constexpr size_t kCounterBytes = 65536;  // one counter per row group: n <= 1M rows
+
 size_t gemv_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t batch) {
   (void)batch;
   if (!gemv_fast_shape(fmt, k)) return 0;
   const GemvPlan p = plan_gemv(n, k, true);
-  if (p.ksplit == 1) return 0;
-  // partial sums for up to 8 tokens
-  return (size_t)p.rowgroups * p.ksplit * 8 * 64 * 4;
+  if (p.ksplit == 1 || (size_t)p.rowgroups * 4 > kCounterBytes) return 0;
+  // counters, then partial sums for up to 8 tokens
+  return kCounterBytes + (size_t)p.rowgroups * p.ksplit * 8 * 64 * 4;
 }
 
 template <int FMT, int NT>
@@ -157,8 +161,10 @@ __global__ __launch_bounds__(512) void k_gemv(const uint8_t *__restrict__ w, int
                                               int n, int units, int ksplit, int upk, int upw,
                                               const float *__restrict__ x, int64_t ldx,
                                               float *__restrict__ y, int64_t ldy,
-                                              float *__restrict__ partial) {
+                                              float *__restrict__ partial,
+                                              unsigned *__restrict__ counters) {
   extern __shared__ float lds[];
+  __shared__ int is_last;
   const int rg = blockIdx.x / ksplit, ks = blockIdx.x - rg * ksplit;
   const int row0 = rg * 64;
   const int ku0 = ks * upk, ku1 = min(ku0 + upk, units);
@@ -171,24 +177,124 @@ __global__ __launch_bounds__(512) void k_gemv(const uint8_t *__restrict__ w, int
       const int t = i >> 6, l = i & 63;
       if (row0 + l < n) y[t * ldy + row0 + l] = lds[i];
     }
-  } else {
-    float *mine = partial + ((int64_t)rg * ksplit + ks) * NT * 64;
-    for (int i = threadIdx.x; i < NT * 64; i += blockDim.x) mine[i] = lds[i];
+    return;
   }
+  // k split: store this slice's sums; the last workgroup of the row group to finish adds all
+  // slices in slice order and resets the row group's counter for the next call. The partial sums
+  // are written and read with device-coherent (sc1) accesses, and every store has completed
+  // (s_waitcnt vmcnt(0)) before the workgroup's arrival is counted, so the last workgroup sees all
+  // of them; no cache writeback or invalidation is needed.
+  float *mine = partial + ((int64_t)rg * ksplit + ks) * NT * 64;
+  for (int i = threadIdx.x; i < NT * 64; i += blockDim.x)
+    __hip_atomic_store(mine + i, lds[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0)
+    is_last = __hip_atomic_fetch_add(&counters[rg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              (unsigned)(ksplit - 1);
+  __syncthreads();
+  if (!is_last) return;
+  const float *base = partial + (int64_t)rg * ksplit * NT * 64;
+  for (int i = threadIdx.x; i < NT * 64; i += blockDim.x) {
+    const int t = i >> 6, l = i & 63;
+    float s = 0.f;
+    for (int q0 = 0; q0 < ksplit; q0 += 8) {  // up to 8 loads in flight, added in slice order
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        v[j] = q0 + j < ksplit ? __hip_atomic_load(base + (q0 + j) * NT * 64 + i, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)
+                               : 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (q0 + j < ksplit) s += v[j];
+    }
+    if (row0 + l < n) y[t * ldy + row0 + l] = s;
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&counters[rg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Adds the k slices of every row group in slice order: y[t][r] = sum_q partial[rg][q][t][r%64].
-__global__ __launch_bounds__(256) void k_gemv_reduce(const float *__restrict__ partial, int n,
-                                                     int ksplit, int nt, float *__restrict__ y,
-                                                     int64_t ldy) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)nt * n) return;
-  const int t = (int)(gid / n), r = (int)(gid - (int64_t)t * n);
-  const int rg = r >> 6, l = r & 63;
-  const float *p = partial + (int64_t)rg * ksplit * nt * 64 + t * 64 + l;
-  float s = 0.f;
-  for (int q = 0; q < ksplit; ++q) s += p[(int64_t)q * nt * 64];
-  y[t * ldy + r] = s;
+// Batch-1 Q4_K GEMV, lanes along k (see tq_gemv_core.h). Workgroup = ceil(nblk / 16) waves
+// covering all of k; it computes rows [blockIdx.x * rows_per_wg, ...) R at a time, loading the
+// next R rows while it computes the current ones.
+template <int R>
+__global__ __launch_bounds__(512) void k_gemv_kl(const uint8_t *__restrict__ w, int64_t row_bytes,
+                                                 int n, int nblk, int rows_per_wg,
+                                                 const float *__restrict__ x,
+                                                 float *__restrict__ y) {
+  __shared__ float red[8][R];
+  const int lane = threadIdx.x & 63, wave = wave_index(), nw = blockDim.x >> 6;
+  const int b = 16 * wave + (lane >> 2), c = lane & 3;
+  const bool valid = b < nblk;
+  const int bb = valid ? b : nblk - 1;
+  const int boff = bb * 144;
+  float xv[64];
+  {
+    const float4 *xp = reinterpret_cast<const float4 *>(x + 256 * bb + 64 * c);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float4 t = valid ? xp[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      xv[4 * i] = t.x;
+      xv[4 * i + 1] = t.y;
+      xv[4 * i + 2] = t.z;
+      xv[4 * i + 3] = t.w;
+    }
+  }
+  float sx_lo = 0.f, sx_hi = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    sx_lo += xv[i];
+    sx_hi += xv[32 + i];
+  }
+  const float unit_inv = 1.f / nibble_fp8_unit();
+  const int rb = blockIdx.x * rows_per_wg, re = min(rb + rows_per_wg, n);
+  u32x4 cur[R][3], nxt[R][3];
+  if (rb < re) kl_load_rows<R>(w, row_bytes, n, rb, boff, c, cur);
+  for (int r0 = rb; r0 < re; r0 += R) {
+    if (r0 + R < re) kl_load_rows<R>(w, row_bytes, n, r0 + R, boff, c, nxt);
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = kl_group_dot(cur[r], xv, sx_lo, sx_hi, c, unit_inv);
+    // across the 64 lanes: each step halves the rows a lane keeps and adds its partner's half
+    int cnt = R;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      if (cnt > 1) {
+        const bool upper = (lane & d) != 0;
+        const int h = cnt >> 1;
+#pragma unroll
+        for (int i = 0; i < R / 2; ++i)
+          if (i < h) {
+            const float send = upper ? acc[i] : acc[i + h];
+            const float keep = upper ? acc[i + h] : acc[i];
+            acc[i] = keep + __shfl_xor(send, d);
+          }
+        cnt = h;
+      } else {
+        acc[0] += __shfl_xor(acc[0], d);
+      }
+    }
+    // lane l now holds row sum_s bit(l, 5-s) * R / 2^(s+1); lanes with zero low bits store it
+    if ((lane & (64 / R - 1)) == 0) {
+      int row = 0;
+#pragma unroll
+      for (int sidx = 0, half = R >> 1; half >= 1; ++sidx, half >>= 1)
+        if (lane & (32 >> sidx)) row += half;
+      red[wave][row] = acc[0];
+    }
+    __syncthreads();
+    if (threadIdx.x < R && r0 + (int)threadIdx.x < re) {
+      float s = 0.f;
+      for (int v = 0; v < nw; ++v) s += red[v][threadIdx.x];
+      y[r0 + threadIdx.x] = s;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int i = 0; i < 3; ++i) cur[r][i] = nxt[r][i];
+  }
 }
 
 // Fallback for shapes whose rows are not dword aligned (Q6_K with k % 512 != 0, Q8_0 with
@@ -210,18 +316,22 @@ __global__ __launch_bounds__(256) void k_gemv_generic(int fmt, const uint8_t *__
 template <int FMT, int NT>
 static void launch_gemv_nt(const uint8_t *w, int64_t rb, int n, int units, const GemvPlan &p,
                            const float *x, int64_t ldx, float *y, int64_t ldy, float *partial,
-                           size_t lds, hipStream_t s) {
+                           unsigned *counters, size_t lds, hipStream_t s) {
   hipLaunchKernelGGL((k_gemv<FMT, NT>), dim3((unsigned)(p.rowgroups * p.ksplit)), dim3(64 * p.waves),
-                     lds, s, w, rb, n, units, p.ksplit, p.upk, p.upw, x, ldx, y, ldy, partial);
+                     lds, s, w, rb, n, units, p.ksplit, p.upk, p.upw, x, ldx, y, ldy, partial,
+                     counters);
 }
 
 template <int FMT>
 static int launch_gemv_fmt(const uint8_t *w, int64_t rb, int n, int64_t k, const float *x,
                            int batch, float *y, void *ws, size_t ws_bytes, hipStream_t s) {
   const int units = (int)(k / 256);
-  const bool split = ws != nullptr && ws_bytes >= gemv_workspace_bytes(FMT, n, k, batch);
+  const size_t need = gemv_workspace_bytes(FMT, n, k, batch);
+  const bool split = ws != nullptr && need > 0 && ws_bytes >= need;
   const GemvPlan p = plan_gemv(n, k, split);
-  float *partial = p.ksplit > 1 ? static_cast<float *>(ws) : nullptr;
+  unsigned *counters = p.ksplit > 1 ? static_cast<unsigned *>(ws) : nullptr;
+  float *partial =
+      p.ksplit > 1 ? reinterpret_cast<float *>(static_cast<char *>(ws) + kCounterBytes) : nullptr;
   const int max_floats = 65536 / 4;
   for (int t0 = 0; t0 < batch;) {
     int nt = batch - t0 < 8 ? batch - t0 : 8;
@@ -232,14 +342,9 @@ static int launch_gemv_fmt(const uint8_t *w, int64_t rb, int n, int64_t k, const
     float *yt = y + (int64_t)t0 * n;
     switch (nt) {
 #define TQ_CASE(NTV) \
-  case NTV: launch_gemv_nt<FMT, NTV>(w, rb, n, units, p, xt, k, yt, n, partial, lds, s); break;
+  case NTV: launch_gemv_nt<FMT, NTV>(w, rb, n, units, p, xt, k, yt, n, partial, counters, lds, s); break;
       TQ_CASE(1) TQ_CASE(2) TQ_CASE(3) TQ_CASE(4) TQ_CASE(5) TQ_CASE(6) TQ_CASE(7) TQ_CASE(8)
 #undef TQ_CASE
-    }
-    if (p.ksplit > 1) {
-      const int64_t threads = (int64_t)nt * n;
-      hipLaunchKernelGGL(k_gemv_reduce, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                         partial, n, p.ksplit, nt, yt, (int64_t)n);
     }
     if (hipGetLastError() != hipSuccess) return -1;
     t0 += nt;
@@ -261,6 +366,20 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, in
     const int64_t threads = n * batch;
     hipLaunchKernelGGL(k_gemv_generic, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
                        fmt, wb, rb, (int)n, k, x, (int)batch, y);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
+  static const int kl_mode = env_int("TQ_GEMV_KLANE", 1);
+  if (fmt == FMT_Q4_K && batch == 1 && kl_mode && ((uintptr_t)x & 15) == 0 && k <= 8 * 4096) {
+    const int nblk = (int)(k / 256);
+    const int waves = (nblk + 15) / 16;
+    constexpr int R = 4;
+    static const int target = env_int("TQ_KL_TARGET_WAVES", 2048);
+    int chunks = (int)((n * waves + (int64_t)R * target - 1) / ((int64_t)R * target));
+    chunks = chunks < 1 ? 1 : chunks;
+    const int rows_per_wg = R * chunks;
+    const int grid = (int)((n + rows_per_wg - 1) / rows_per_wg);
+    hipLaunchKernelGGL(k_gemv_kl<R>, dim3((unsigned)grid), dim3(64 * waves), 0, s, wb, rb, (int)n, nblk,
+                       rows_per_wg, x, y);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
   switch (fmt) {

@@ -321,24 +321,28 @@ __device__ __forceinline__ void unit_dot(const Unit<FMT_Q8_0> &u, const float *c
   }
 }
 
+// Header and the 32 quant bytes of 64-weight group `it` (= 4 * unit + group) of a Q4_K row.
+__device__ __forceinline__ void q4k_group_load(const uint8_t *row, int it, u32x4 (&v)[3]) {
+  const u32x4 *p = reinterpret_cast<const u32x4 *>(row + (size_t)(it >> 2) * 144);
+  v[0] = *(p);
+  v[1] = *(p + 1 + 2 * (it & 3));
+  v[2] = *(p + 2 + 2 * (it & 3));
+}
+
 // Q4_K with several tokens: stream 64-weight groups (header + 32 quant bytes each) in a loop
 // that is not unrolled, so the compiler keeps only one group's converted quants and one token's
 // activations live at a time. The next group's three 16-byte loads are issued before this
 // group's math; the 16-byte header is re-read for each of the four groups of a block (an L1 hit).
 template <int NT>
 __device__ __forceinline__ void stream_q4k_groups(const uint8_t *row, int u0, int u1,
+                                                  const u32x4 (&first)[3],
                                                   const float *const (&x)[NT],
                                                   const float *const (&gsum)[NT], float (&acc)[NT]) {
-  if (u0 >= u1) return;
   const int it1 = 4 * u1;
-  auto load = [&](int it, u32x4 (&v)[3]) {
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(row + (size_t)(it >> 2) * 144);
-    v[0] = *(p);
-    v[1] = *(p + 1 + 2 * (it & 3));
-    v[2] = *(p + 2 + 2 * (it & 3));
-  };
+  auto load = [&](int it, u32x4 (&v)[3]) { q4k_group_load(row, it, v); };
   u32x4 cur[3], nxt[3];
-  load(4 * u0, cur);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) cur[i] = first[i];
 #pragma unroll 1
   for (int it = 4 * u0; it < it1; ++it) {
     if (it + 1 < it1) load(it + 1, nxt);
@@ -393,29 +397,26 @@ __device__ __forceinline__ void stream_q4k_groups(const uint8_t *row, int u0, in
 }
 
 // Stream units [u0, u1) of this lane's row, next unit's loads issued before this one's math.
+// Stream units [u0, u1) of this lane's row; `cur` already holds unit u0 (loaded by the caller
+// so that its latency overlaps other work). The next unit's loads are issued before this unit's
+// math.
 template <int FMT, int NT>
-__device__ __forceinline__ void stream_units(const uint8_t *row, int u0, int u1,
+__device__ __forceinline__ void stream_units(const uint8_t *row, int u0, int u1, Unit<FMT> &cur,
                                              const float *const (&x)[NT],
                                              const float *const (&gsum)[NT], float (&acc)[NT]) {
   constexpr int G = Fmt<FMT>::group;
-  if constexpr (FMT == FMT_Q4_K && NT > 1) {
-    stream_q4k_groups<NT>(row, u0, u1, x, gsum, acc);
-  } else {
-    if (u0 >= u1) return;
-    Unit<FMT> cur, nxt;
-    load_unit(cur, row, u0);
-    for (int u = u0; u < u1; ++u) {
-      if (u + 1 < u1) load_unit(nxt, row, u + 1);
-      const float *xp[NT];
-      const float *gs[NT];
+  Unit<FMT> nxt;
+  for (int u = u0; u < u1; ++u) {
+    if (u + 1 < u1) load_unit(nxt, row, u + 1);
+    const float *xp[NT];
+    const float *gs[NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        xp[t] = x[t] + 256 * u;
-        gs[t] = gsum[t] + (256 / G) * u;
-      }
-      unit_dot<NT>(cur, xp, gs, acc);
-      cur = nxt;
+    for (int t = 0; t < NT; ++t) {
+      xp[t] = x[t] + 256 * u;
+      gs[t] = gsum[t] + (256 / G) * u;
     }
+    unit_dot<NT>(cur, xp, gs, acc);
+    cur = nxt;
   }
 }
 
@@ -434,6 +435,18 @@ __device__ __forceinline__ void gemv_tile(const uint8_t *__restrict__ w, int64_t
   const int wave = wave_index();
   const int lane = threadIdx.x & 63;
   const int ngl = (ku1 - ku0) * GPU_;
+  const int row = min(row0 + lane, n - 1);  // rows past n repeat the last row; never stored
+  const int u0 = ku0 + wave * upw, u1 = min(u0 + upw, ku1);
+  const uint8_t *wrow = w + (int64_t)row * row_bytes;
+  // the first weights of this wave are requested before the group sums are formed
+  constexpr bool kGroups = FMT == FMT_Q4_K && NT > 1;
+  Unit<FMT> first;
+  u32x4 gfirst[3];
+  if constexpr (kGroups) {
+    if (u0 < u1) q4k_group_load(wrow, 4 * u0, gfirst);
+  } else {
+    if (u0 < u1) load_unit(first, wrow, u0);
+  }
   // group sums of this slice of x, for every token of the tile
   for (int i = threadIdx.x; i < NT * ngl; i += blockDim.x) {
     const int t = i / ngl, gi = i - t * ngl;
@@ -450,9 +463,11 @@ __device__ __forceinline__ void gemv_tile(const uint8_t *__restrict__ w, int64_t
   float acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = 0.f;
-  const int row = min(row0 + lane, n - 1);  // rows past n repeat the last row; never stored
-  const int u0 = ku0 + wave * upw, u1 = min(u0 + upw, ku1);
-  stream_units<FMT, NT>(w + (int64_t)row * row_bytes, u0, u1, xr, gs, acc);
+  if constexpr (kGroups) {
+    if (u0 < u1) stream_q4k_groups<NT>(wrow, u0, u1, gfirst, xr, gs, acc);
+  } else {
+    if (u0 < u1) stream_units<FMT, NT>(wrow, u0, u1, first, xr, gs, acc);
+  }
   __syncthreads();  // every wave is done with the group sums
 #pragma unroll
   for (int t = 0; t < NT; ++t) lds[NT * 64 + (wave * NT + t) * 64 + lane] = acc[t];
@@ -472,6 +487,70 @@ __host__ __device__ inline int gemv_tile_lds_floats(int nt, int upk, int waves) 
   const int g = nt * upk * (256 / Fmt<FMT>::group);
   const int r = nt * 64 + waves * nt * 64;
   return g > r ? g : r;
+}
+
+}  // namespace tq
+
+namespace tq {
+
+// ---- batch-1 Q4_K GEMV with lanes along k ---------------------------------------------------------
+// A wave covers 16 blocks (4096 weights) of k: lane l owns the 64-weight group c = l % 4 of block
+// 16w + l / 4, i.e. quant bytes 32c..32c+31 (sub-blocks 2c and 2c+1). Its 64 activations stay in
+// VGPRs for all rows, with their two 32-element sums. For each row the lane loads the block
+// header and its 32 quant bytes (three 16-byte loads; consecutive lanes read consecutive bytes of
+// the row), forms its partial dot product, and partial sums are added across lanes every R rows
+// (a butterfly that halves the rows at each step) and across the waves of the workgroup in LDS.
+// Nothing is split across workgroups, so there is no cross-workgroup reduction.
+
+// Scale and min of sub-block j (0..7) from header dwords s0 = S[0..3], s1 = S[4..7], s2 = S[8..11];
+// branch-free, as j differs between lanes.
+__device__ __forceinline__ void q4k_scale_min_of(uint32_t s0, uint32_t s1, uint32_t s2, int j,
+                                                 float &sc, float &m) {
+  const int a = 8 * (j & 3);
+  const uint32_t sa = s0 >> a, sb = s2 >> a, ma = s1 >> a;
+  const bool high = j >= 4;
+  sc = (float)(high ? ((sb & 15u) | (((sa >> 6) & 3u) << 4)) : (sa & 63u));
+  m = (float)(high ? (((sb >> 4) & 15u) | (((ma >> 6) & 3u) << 4)) : (ma & 63u));
+}
+
+template <int R>
+__device__ __forceinline__ void kl_load_rows(const uint8_t *w, int64_t row_bytes, int n, int r0,
+                                             int boff, int c, u32x4 (&v)[R][3]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = min(r0 + r, n - 1);
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(w + (int64_t)row * row_bytes + boff);
+    v[r][0] = p[0];
+    v[r][1] = p[1 + 2 * c];
+    v[r][2] = p[2 + 2 * c];
+  }
+}
+
+// Partial dot product of one row's 64-weight group with this lane's activations.
+__device__ __forceinline__ float kl_group_dot(const u32x4 (&v)[3], const float (&xv)[64],
+                                              float sx_lo, float sx_hi, int c, float unit_inv) {
+  const uint32_t h0 = v[0].x, s0 = v[0].y, s1 = v[0].z, s2 = v[0].w;
+  const float d = half_bits_to_float(h0) * unit_inv, dmin = half_bits_to_float(h0 >> 16);
+  float sc_lo, m_lo, sc_hi, m_hi;
+  q4k_scale_min_of(s0, s1, s2, 2 * c, sc_lo, m_lo);
+  q4k_scale_min_of(s0, s1, s2, 2 * c + 1, sc_hi, m_hi);
+  float dl = 0.f, dh = 0.f;
+#pragma unroll
+  for (int dw = 0; dw < 8; ++dw) {
+    const uint32_t wq = dword_of(v[1 + (dw >> 2)], dw & 3);
+    const uint32_t lo = wq & 0x0F0F0F0Fu, hi = (wq >> 4) & 0x0F0F0F0Fu;
+    float f[4];
+    nibbles_to_float<false>(lo, f[0], f[1]);
+    nibbles_to_float<true>(lo, f[2], f[3]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dl = __builtin_fmaf(f[e], xv[4 * dw + e], dl);
+    nibbles_to_float<false>(hi, f[0], f[1]);
+    nibbles_to_float<true>(hi, f[2], f[3]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dh = __builtin_fmaf(f[e], xv[32 + 4 * dw + e], dh);
+  }
+  const float pos = __builtin_fmaf(sc_lo, dl, sc_hi * dh) * d;
+  return __builtin_fmaf(-dmin, __builtin_fmaf(m_lo, sx_lo, m_hi * sx_hi), pos);
 }
 
 }  // namespace tq

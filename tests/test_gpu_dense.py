@@ -87,7 +87,8 @@ def test_gemv_integer_lattice_bitwise(t, n, k, batch):
 @pytest.mark.parametrize("t,n,k", [("q4_k", 200, 4096), ("q6_k", 130, 3072), ("q8_0", 70, 2048)])
 @pytest.mark.parametrize("batch", [1, 7])
 def test_gemv_without_workspace(t, n, k, batch):
-    """No workspace: every row group in one workgroup; and an explicit workspace."""
+    """No workspace: every row group in one workgroup; and an explicit workspace, whose
+    completion counters the split path must leave at zero."""
     _print_case("no-ws", t, n, k, batch)
     g = synth.rng(107, "nows", t, n, k, batch)
     w = synth.blob(t, g, n, k)
@@ -97,9 +98,10 @@ def test_gemv_without_workspace(t, n, k, batch):
     ref, mag = oracle.gemv(t, w, n, k, x)
     assert_product_close(y0, ref, mag, what="no workspace")
     nbytes = tq.gemv_workspace_bytes(t, n, k, batch)
-    ws = torch.full((max(nbytes, 256),), 0x7F, dtype=torch.uint8, device="cuda:0")
+    ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device="cuda:0")
     y1 = host(tq.gemv(t, wd, n, k, xd, ws=ws))
     assert_product_close(y1, ref, mag, what="own workspace")
+    assert int(host(ws[:65536]).view(np.uint32).max()) == 0, "completion counters not reset"
 
 
 def test_gemv_unit_vector_picks_dequantized_column():
