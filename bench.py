@@ -60,7 +60,7 @@ def build_dense_model(tq, synth, torch, batch, seed):
     return layers
 
 
-def make_step(tq, torch, layers, batch, events=None):
+def make_step(tq, torch, layers, batch, events=None, gemv_only=False):
     """One decode step through the C ABI: per layer q, k, v (input x), o (input: the attention
     stand-in a), gate and up (input x), SwiGLU, down (input: the SwiGLU output)."""
     H = 4096
@@ -78,16 +78,12 @@ def make_step(tq, torch, layers, batch, events=None):
     def gemv(name, projs, x):
         w, n, k = projs[name]
         stream = torch.cuda.current_stream().cuda_stream
-        if events is not None:
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record()
         rc = L.tq_gemv(tq.Q4_K, w.data_ptr(), n, k, x.data_ptr(), batch, bufs[name].data_ptr(),
                        ws.data_ptr(), ws.numel(), stream)
         if rc:
             raise tq.TQError(rc, L.tq_last_error().decode())
-        if events is not None:
-            e.record()
-            events.append((s, e, w.numel() + 4 * batch * (n + k)))
+        if events is not None:  # algorithmic bytes of this launch
+            events.append(w.numel() + 4 * batch * (n + k))
 
     def step():
         for projs, x, a in layers:
@@ -97,7 +93,8 @@ def make_step(tq, torch, layers, batch, events=None):
             gemv("o", projs, a)
             gemv("gate", projs, x)
             gemv("up", projs, x)
-            tq.swiglu(bufs["gate"], bufs["up"], out=bufs["h"])
+            if not gemv_only:
+                tq.swiglu(bufs["gate"], bufs["up"], out=bufs["h"])
             gemv("down", projs, bufs["h"])
 
     return step
@@ -222,18 +219,29 @@ def main():
     ms_per_step = elapsed * 1000 / args.steps
     tokens_s = args.batch * args.steps / elapsed
 
-    # Roofline of the Q4_K GEMV: the same step again, eager, each tq_gemv bracketed by events on
-    # the launch stream; a GPU-side sleep first lets the host queue the whole step ahead of the
-    # GPU, so the events time the kernels and not the launch latency.
+    # Roofline of the Q4_K GEMV: the step's GEMV launches alone (no SwiGLU), captured as their
+    # own graph on the same stream and replayed back to back between two events on that stream;
+    # the average launch duration is the elapsed time over the number of launches.
     events = []
     with torch.cuda.stream(stream):
-        istep = make_step(tq, torch, layers, args.batch, events=events)
-        torch.cuda._sleep(200_000_000)
-        istep()
+        gstep = make_step(tq, torch, layers, args.batch, events=events, gemv_only=True)
+        gstep()
         torch.cuda.synchronize()
-    kernel_s = sum(s.elapsed_time(e) for s, e, _ in events) / 1000
-    kernel_bytes = sum(b for _, _, b in events)
-    achieved = kernel_bytes / kernel_s / 1e9
+        ggraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(ggraph, stream=stream):
+            gstep()
+        ggraph.replay()
+        reps = 5
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(reps):
+            ggraph.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+    launches = len(events) // 2  # the eager call and the captured one each appended
+    kernel_bytes = sum(events[:launches])
+    avg_launch_s = ev0.elapsed_time(ev1) / 1000 / (reps * launches)
+    achieved = kernel_bytes / launches / avg_launch_s / 1e9
     step_bytes = kernel_bytes
 
     out = {
@@ -257,7 +265,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "tq_gemv Q4_K batch 1 (tq::k_gemv_kl)" if args.batch == 1
                                else "tq_gemv Q4_K (tq::k_gemv)",
-                     "avg_launch_us": round(kernel_s * 1e6 / len(events), 3)},
+                     "avg_launch_us": round(avg_launch_s * 1e6, 3)},
     }
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")

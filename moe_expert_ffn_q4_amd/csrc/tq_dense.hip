@@ -219,26 +219,78 @@ __global__ __launch_bounds__(512) void k_gemv(const uint8_t *__restrict__ w, int
 // covering all of k; it computes rows [blockIdx.x * rows_per_wg, ...) R at a time, loading the
 // next R rows while it computes the current ones.
 template <int R>
+__device__ __forceinline__ void kl_rows(const u32x4 (&v)[R][3], const float (&xv)[64], float sx_lo,
+                                        float sx_hi, const Q4kField &f0, const Q4kField &f1,
+                                        float unit_inv, int r0, int re, float (*red)[R],
+                                        float *__restrict__ y) {
+  const int lane = threadIdx.x & 63, wave = wave_index(), nw = blockDim.x >> 6;
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = kl_group_dot(v[r], xv, sx_lo, sx_hi, f0, f1, unit_inv);
+  // across the 64 lanes: each step halves the rows a lane keeps and adds its partner's half
+  int cnt = R;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    if (cnt > 1) {
+      const bool upper = (lane & d) != 0;
+      const int h = cnt >> 1;
+#pragma unroll
+      for (int i = 0; i < R / 2; ++i)
+        if (i < h) {
+          const float send = upper ? acc[i] : acc[i + h];
+          const float keep = upper ? acc[i + h] : acc[i];
+          acc[i] = keep + __shfl_xor(send, d);
+        }
+      cnt = h;
+    } else {
+      acc[0] += __shfl_xor(acc[0], d);
+    }
+  }
+  // lane l now holds row sum_s bit(l, 5-s) * R / 2^(s+1); lanes with zero low bits store it
+  if ((lane & (64 / R - 1)) == 0) {
+    int row = 0;
+#pragma unroll
+    for (int sidx = 0, half = R >> 1; half >= 1; ++sidx, half >>= 1)
+      if (lane & (32 >> sidx)) row += half;
+    red[wave][row] = acc[0];
+  }
+  __syncthreads();
+  if (threadIdx.x < R && r0 + (int)threadIdx.x < re) {
+    float s = 0.f;
+    for (int q = 0; q < nw; ++q) s += red[q][threadIdx.x];
+    y[r0 + threadIdx.x] = s;
+  }
+  __syncthreads();
+}
+
+// Batch-1 Q4_K GEMV, lanes along k (see tq_gemv_core.h). Workgroup = ceil(nblk / 16) waves
+// covering all of k; it computes rows [blockIdx.x * rows_per_wg, ...) R at a time, loading the
+// next R rows while it computes the current ones (two register buffers used in turn).
+template <int R>
 __global__ __launch_bounds__(512) void k_gemv_kl(const uint8_t *__restrict__ w, int64_t row_bytes,
                                                  int n, int nblk, int rows_per_wg,
                                                  const float *__restrict__ x,
                                                  float *__restrict__ y) {
   __shared__ float red[8][R];
-  const int lane = threadIdx.x & 63, wave = wave_index(), nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_index();
   const int b = 16 * wave + (lane >> 2), c = lane & 3;
   const bool valid = b < nblk;
   const int bb = valid ? b : nblk - 1;
   const int boff = bb * 144;
+  const int rb = blockIdx.x * rows_per_wg, re = min(rb + rows_per_wg, n);
+  u32x4 va[R][3], vb[R][3];
+  // the first rows' weights are requested before the activations
+  if (rb < re) kl_load_rows<R>(w, row_bytes, n, rb, boff, c, va);
   float xv[64];
   {
     const float4 *xp = reinterpret_cast<const float4 *>(x + 256 * bb + 64 * c);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float4 t = valid ? xp[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-      xv[4 * i] = t.x;
-      xv[4 * i + 1] = t.y;
-      xv[4 * i + 2] = t.z;
-      xv[4 * i + 3] = t.w;
+      const float4 t = xp[i];
+      xv[4 * i] = valid ? t.x : 0.f;
+      xv[4 * i + 1] = valid ? t.y : 0.f;
+      xv[4 * i + 2] = valid ? t.z : 0.f;
+      xv[4 * i + 3] = valid ? t.w : 0.f;
     }
   }
   float sx_lo = 0.f, sx_hi = 0.f;
@@ -248,52 +300,13 @@ __global__ __launch_bounds__(512) void k_gemv_kl(const uint8_t *__restrict__ w, 
     sx_hi += xv[32 + i];
   }
   const float unit_inv = 1.f / nibble_fp8_unit();
-  const int rb = blockIdx.x * rows_per_wg, re = min(rb + rows_per_wg, n);
-  u32x4 cur[R][3], nxt[R][3];
-  if (rb < re) kl_load_rows<R>(w, row_bytes, n, rb, boff, c, cur);
-  for (int r0 = rb; r0 < re; r0 += R) {
-    if (r0 + R < re) kl_load_rows<R>(w, row_bytes, n, r0 + R, boff, c, nxt);
-    float acc[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = kl_group_dot(cur[r], xv, sx_lo, sx_hi, c, unit_inv);
-    // across the 64 lanes: each step halves the rows a lane keeps and adds its partner's half
-    int cnt = R;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      if (cnt > 1) {
-        const bool upper = (lane & d) != 0;
-        const int h = cnt >> 1;
-#pragma unroll
-        for (int i = 0; i < R / 2; ++i)
-          if (i < h) {
-            const float send = upper ? acc[i] : acc[i + h];
-            const float keep = upper ? acc[i + h] : acc[i];
-            acc[i] = keep + __shfl_xor(send, d);
-          }
-        cnt = h;
-      } else {
-        acc[0] += __shfl_xor(acc[0], d);
-      }
-    }
-    // lane l now holds row sum_s bit(l, 5-s) * R / 2^(s+1); lanes with zero low bits store it
-    if ((lane & (64 / R - 1)) == 0) {
-      int row = 0;
-#pragma unroll
-      for (int sidx = 0, half = R >> 1; half >= 1; ++sidx, half >>= 1)
-        if (lane & (32 >> sidx)) row += half;
-      red[wave][row] = acc[0];
-    }
-    __syncthreads();
-    if (threadIdx.x < R && r0 + (int)threadIdx.x < re) {
-      float s = 0.f;
-      for (int v = 0; v < nw; ++v) s += red[v][threadIdx.x];
-      y[r0 + threadIdx.x] = s;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int i = 0; i < 3; ++i) cur[r][i] = nxt[r][i];
+  const Q4kField f0 = q4k_field(2 * c), f1 = q4k_field(2 * c + 1);
+  for (int r0 = rb; r0 < re; r0 += 2 * R) {
+    if (r0 + R < re) kl_load_rows<R>(w, row_bytes, n, r0 + R, boff, c, vb);
+    kl_rows<R>(va, xv, sx_lo, sx_hi, f0, f1, unit_inv, r0, re, red, y);
+    if (r0 + R >= re) break;
+    if (r0 + 2 * R < re) kl_load_rows<R>(w, row_bytes, n, r0 + 2 * R, boff, c, va);
+    kl_rows<R>(vb, xv, sx_lo, sx_hi, f0, f1, unit_inv, r0 + R, re, red, y);
   }
 }
 
@@ -372,14 +385,22 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, in
   if (fmt == FMT_Q4_K && batch == 1 && kl_mode && ((uintptr_t)x & 15) == 0 && k <= 8 * 4096) {
     const int nblk = (int)(k / 256);
     const int waves = (nblk + 15) / 16;
-    constexpr int R = 4;
+    static const int kl_rows_env = env_int("TQ_KL_ROWS", 4);
     static const int target = env_int("TQ_KL_TARGET_WAVES", 2048);
+    const int R = kl_rows_env == 2 ? 2 : kl_rows_env == 8 ? 8 : 4;
     int chunks = (int)((n * waves + (int64_t)R * target - 1) / ((int64_t)R * target));
     chunks = chunks < 1 ? 1 : chunks;
     const int rows_per_wg = R * chunks;
     const int grid = (int)((n + rows_per_wg - 1) / rows_per_wg);
-    hipLaunchKernelGGL(k_gemv_kl<R>, dim3((unsigned)grid), dim3(64 * waves), 0, s, wb, rb, (int)n, nblk,
-                       rows_per_wg, x, y);
+    if (R == 2)
+      hipLaunchKernelGGL(k_gemv_kl<2>, dim3((unsigned)grid), dim3(64 * waves), 0, s, wb, rb, (int)n,
+                         nblk, rows_per_wg, x, y);
+    else if (R == 8)
+      hipLaunchKernelGGL(k_gemv_kl<8>, dim3((unsigned)grid), dim3(64 * waves), 0, s, wb, rb, (int)n,
+                         nblk, rows_per_wg, x, y);
+    else
+      hipLaunchKernelGGL(k_gemv_kl<4>, dim3((unsigned)grid), dim3(64 * waves), 0, s, wb, rb, (int)n,
+                         nblk, rows_per_wg, x, y);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
   switch (fmt) {

@@ -502,15 +502,34 @@ namespace tq {
 // (a butterfly that halves the rows at each step) and across the waves of the workgroup in LDS.
 // Nothing is split across workgroups, so there is no cross-workgroup reduction.
 
-// Scale and min of sub-block j (0..7) from header dwords s0 = S[0..3], s1 = S[4..7], s2 = S[8..11];
-// branch-free, as j differs between lanes.
-__device__ __forceinline__ void q4k_scale_min_of(uint32_t s0, uint32_t s1, uint32_t s2, int j,
-                                                 float &sc, float &m) {
-  const int a = 8 * (j & 3);
-  const uint32_t sa = s0 >> a, sb = s2 >> a, ma = s1 >> a;
-  const bool high = j >= 4;
-  sc = (float)(high ? ((sb & 15u) | (((sa >> 6) & 3u) << 4)) : (sa & 63u));
-  m = (float)(high ? (((sb >> 4) & 15u) | (((ma >> 6) & 3u) << 4)) : (ma & 63u));
+// Field positions of the 6-bit scale and min of sub-block j inside the 12 packed bytes, as bit
+// offsets / widths used with v_bfe (a field of width 0 reads as 0), so that lanes with j < 4 and
+// j >= 4 run the same instructions:
+//   sc = bfe(j < 4 ? S0..3 : S8..11, lo_off, lo_w) | bfe(S0..3, hi_off, hi_w) << 4
+//   m  = bfe(j < 4 ? S4..7 : S8..11, lo_off + mo, lo_w) | bfe(S4..7, hi_off, hi_w) << 4
+struct Q4kField {
+  uint32_t lo_off, lo_w, hi_off, hi_w, m_off;
+  bool from_s2;
+};
+__device__ __forceinline__ Q4kField q4k_field(int j) {
+  Q4kField f;
+  const uint32_t a = 8u * (uint32_t)(j & 3);
+  f.from_s2 = j >= 4;
+  f.lo_off = a;
+  f.lo_w = f.from_s2 ? 4u : 6u;
+  f.hi_off = a + 6u;
+  f.hi_w = f.from_s2 ? 2u : 0u;
+  f.m_off = f.from_s2 ? a + 4u : a;
+  return f;
+}
+__device__ __forceinline__ uint32_t bfe(uint32_t v, uint32_t off, uint32_t w) {
+  return __builtin_amdgcn_ubfe(v, off, w);
+}
+__device__ __forceinline__ void q4k_scale_min_at(uint32_t s0, uint32_t s1, uint32_t s2,
+                                                 const Q4kField &f, float &sc, float &m) {
+  const uint32_t lsc = f.from_s2 ? s2 : s0, lm = f.from_s2 ? s2 : s1;
+  sc = (float)(bfe(lsc, f.lo_off, f.lo_w) | (bfe(s0, f.hi_off, f.hi_w) << 4));
+  m = (float)(bfe(lm, f.m_off, f.lo_w) | (bfe(s1, f.hi_off, f.hi_w) << 4));
 }
 
 template <int R>
@@ -526,14 +545,16 @@ __device__ __forceinline__ void kl_load_rows(const uint8_t *w, int64_t row_bytes
   }
 }
 
-// Partial dot product of one row's 64-weight group with this lane's activations.
+// Partial dot product of one row's 64-weight group with this lane's activations; f0 / f1 locate
+// the scale and min of the group's two sub-blocks.
 __device__ __forceinline__ float kl_group_dot(const u32x4 (&v)[3], const float (&xv)[64],
-                                              float sx_lo, float sx_hi, int c, float unit_inv) {
+                                              float sx_lo, float sx_hi, const Q4kField &f0,
+                                              const Q4kField &f1, float unit_inv) {
   const uint32_t h0 = v[0].x, s0 = v[0].y, s1 = v[0].z, s2 = v[0].w;
   const float d = half_bits_to_float(h0) * unit_inv, dmin = half_bits_to_float(h0 >> 16);
   float sc_lo, m_lo, sc_hi, m_hi;
-  q4k_scale_min_of(s0, s1, s2, 2 * c, sc_lo, m_lo);
-  q4k_scale_min_of(s0, s1, s2, 2 * c + 1, sc_hi, m_hi);
+  q4k_scale_min_at(s0, s1, s2, f0, sc_lo, m_lo);
+  q4k_scale_min_at(s0, s1, s2, f1, sc_hi, m_hi);
   float dl = 0.f, dh = 0.f;
 #pragma unroll
   for (int dw = 0; dw < 8; ++dw) {
