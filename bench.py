@@ -22,6 +22,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# Sources of the batch-1 Q4_K GEMV; the committed counter summary records their hash, and its
+# HBM traffic is reported only while the kernel is unchanged since the counters were taken.
+GEMV_SOURCES = ("moe_expert_ffn_q4_amd/csrc/tq_dense.hip", "moe_expert_ffn_q4_amd/csrc/tq_gemv_core.h",
+                "moe_expert_ffn_q4_amd/csrc/tq_device.h")
+GEMV_COUNTERS = "profiles/k_gemv_kl_llama8b_b1_hbm_counters.txt"
 METRIC = "Q4_K GEMV HBM GB/s (% of peak); decode tokens/s for 8B-shaped and MoE layers"
 
 
@@ -42,7 +47,104 @@ def _args():
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain 1 GiB device copy (the known-size reference for the "
                         "FETCH_SIZE / WRITE_SIZE counters)")
+    p.add_argument("--summarize", nargs=3, metavar=("KERNEL_STATS", "FETCH_CSV", "WRITE_CSV"),
+                   help="no GPU: print a text summary of a rocprofv3 kernel-stats CSV and two "
+                        "counter-collection CSVs (FETCH_SIZE, WRITE_SIZE) of the llama8b batch-1 "
+                        "step, with per-launch HBM traffic of the Q4_K GEMV")
     return p.parse_args()
+
+
+def source_hash(paths=GEMV_SOURCES):
+    import hashlib
+
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def llama8b_bytes_per_launch(synth, batch=1):
+    """Algorithmic bytes of the average GEMV launch of the dense step: weight blob plus fp32 x
+    and y, over the seven projections of a layer."""
+    tot = 0
+    for _, n, k in synth.dense_projections(synth.LLAMA8B):
+        tot += n * (k // 256) * 144 + 4 * batch * (n + k)
+    return tot / 7
+
+
+def summarize(kt_csv, fetch_csv, write_csv):
+    """Text summary of the profiler's CSVs for the GEMV of the llama8b batch-1 step. FETCH_SIZE
+    and WRITE_SIZE are scaled by what they read for the 1 GiB copy (--calibrate-copy)."""
+    import csv
+    from collections import defaultdict
+
+    import synth
+
+    lines = []
+    lines.append("# per-kernel statistics (rocprofv3 --kernel-trace --stats)")
+    lines.append(f"{'kernel':<64s} {'calls':>6s} {'avg_us':>9s} {'min_us':>8s} {'max_us':>8s} {'pct':>6s}")
+    for r in csv.DictReader(open(kt_csv)):
+        lines.append(f"{r['Name'][:64]:<64s} {int(r['Calls']):6d} {float(r['AverageNs'])/1e3:9.3f} "
+                     f"{float(r['MinNs'])/1e3:8.3f} {float(r['MaxNs'])/1e3:8.3f} "
+                     f"{float(r['Percentage']):6.2f}")
+
+    def load(p):
+        d = defaultdict(list)
+        for r in csv.DictReader(open(p)):
+            key = (r["Kernel_Name"], int(r["Grid_Size"]), int(r["Workgroup_Size"]))
+            d[key].append(float(r["Counter_Value"]))
+        return d
+
+    fetch, write = load(fetch_csv), load(write_csv)
+    copy = [k for k in fetch if "copyBuffer" in k[0] and sum(fetch[k]) / len(fetch[k]) > 1e5]
+    if len(copy) != 1:
+        raise SystemExit("expected exactly one 1 GiB copy launch (run the bench with "
+                         "--calibrate-copy)")
+    gib_kib = float(1 << 20)
+    f_factor = gib_kib / fetch[copy[0]][0]
+    w_factor = gib_kib / write[copy[0]][0]
+    lines.append("")
+    lines.append("# HBM counters (rocprofv3 --pmc, one counter per run), KiB per dispatch")
+    lines.append(f"1 GiB copy: FETCH_SIZE {fetch[copy[0]][0]:.1f} KiB -> factor {f_factor:.4f}; "
+                 f"WRITE_SIZE {write[copy[0]][0]:.1f} KiB -> factor {w_factor:.4f}")
+    lines.append(f"{'kernel':<40s} {'grid':>8s} {'wg':>4s} {'n':>6s} {'FETCH_KiB':>11s} "
+                 f"{'WRITE_KiB':>10s} {'bytes/launch (scaled)':>22s}")
+    tot_bytes, tot_n = 0.0, 0
+    for key in sorted(fetch, key=lambda k: -sum(fetch[k])):
+        if "k_gemv_kl" not in key[0]:
+            continue
+        fv, wv = fetch[key], write.get(key, [0.0])
+        fk, wk = sum(fv) / len(fv), sum(wv) / len(wv)
+        b = (fk * f_factor + wk * w_factor) * 1024
+        tot_bytes += b * len(fv)
+        tot_n += len(fv)
+        lines.append(f"{key[0][:40]:<40s} {key[1]:8d} {key[2]:4d} {len(fv):6d} {fk:11.1f} "
+                     f"{wk:10.1f} {b:22.0f}")
+    algo = llama8b_bytes_per_launch(synth)
+    traffic = tot_bytes / tot_n
+    lines.append("")
+    lines.append(f"algorithmic_bytes_per_launch: {algo:.0f}")
+    lines.append(f"traffic_bytes_per_launch: {traffic:.0f}")
+    lines.append(f"traffic_over_algorithmic: {traffic / algo:.4f}")
+    lines.append(f"kernel_source_sha256: {source_hash()}")
+    return "\n".join(lines)
+
+
+def recorded_traffic():
+    """HBM bytes per GEMV launch from the committed counter summary, or None when the kernel's
+    sources have changed since the counters were taken (or there is no summary)."""
+    path = os.path.join(ROOT, GEMV_COUNTERS)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != source_hash():
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def build_dense_model(tq, synth, torch, batch, seed):
@@ -184,6 +286,9 @@ def moe_bench(args, torch, tq, synth):
 
 def main():
     args = _args()
+    if args.summarize:
+        print(summarize(*args.summarize))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(no multi-GPU path in this build)", file=sys.stderr)
@@ -243,6 +348,7 @@ def main():
     avg_launch_s = ev0.elapsed_time(ev1) / 1000 / (reps * launches)
     achieved = kernel_bytes / launches / avg_launch_s / 1e9
     step_bytes = kernel_bytes
+    traffic = recorded_traffic() if args.batch == 1 else None
 
     out = {
         "metric": METRIC,
@@ -262,7 +368,8 @@ def main():
                    "global_batch": args.batch, "seq_len": 1, "parallelism": "none (1 GPU)"},
         "step_gbs": round(step_bytes / (ms_per_step / 1000) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
                      "kernel": "tq_gemv Q4_K batch 1 (tq::k_gemv_kl)" if args.batch == 1
                                else "tq_gemv Q4_K (tq::k_gemv)",
                      "avg_launch_us": round(avg_launch_s * 1e6, 3)},
