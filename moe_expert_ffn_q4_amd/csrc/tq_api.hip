@@ -88,6 +88,9 @@ int tq_swiglu(const float *g, const float *u, int64_t count, float *h, void *str
   return launched(tq::launch_swiglu(g, u, count, h, (hipStream_t)stream), "tq_swiglu");
 }
 
+// Average routed tokens per expert from which TQ_PATH_AUTO takes the matrix-core path.
+constexpr int64_t kMfmaTokens = 64;
+
 static int moe_check(const tq_moe_desc *d, int64_t tokens, tq::MoeShape *out) {
   if (!d) return fail(TQ_EINVAL, "tq_moe_ffn: null descriptor");
   if (!known_type(d->type)) return fail(TQ_EINVAL, "tq_moe_ffn: unknown block type %d", d->type);
@@ -120,6 +123,14 @@ static int moe_check(const tq_moe_desc *d, int64_t tokens, tq::MoeShape *out) {
   s.experts_on_host = d->experts_on_host != 0;
   s.gate_bytes = d->ffn * tq_row_bytes(d->type, d->hidden);
   s.expert_bytes = 2 * s.gate_bytes + d->hidden * tq_row_bytes(d->type, d->ffn);
+  // matrix cores once the experts average kMfmaTokens routed tokens or more
+  if (d->path == TQ_PATH_BF16_MFMA) {
+    if (d->type != TQ_Q4_K)
+      return fail(TQ_EUNSUPPORTED, "tq_moe_ffn: the bf16 matrix-core path takes Q4_K experts only");
+    s.mfma = 1;
+  } else if (d->path == TQ_PATH_AUTO) {
+    s.mfma = d->type == TQ_Q4_K && tokens * d->top_k >= kMfmaTokens * d->n_experts;
+  }
   *out = s;
   return TQ_OK;
 }

@@ -14,6 +14,7 @@ struct MoeShape {
   int type;
   int64_t hidden, ffn, n_experts, top_k, tokens;
   int has_shared, renormalize, experts_on_host;
+  int mfma;              // expert products on the bf16 matrix cores (Q4_K only)
   int64_t gate_bytes;    // bytes of one gate (= up) blob
   int64_t expert_bytes;  // gate + up + down
 };
@@ -27,6 +28,8 @@ struct MoePlan {
   int d_rg, d_ks, d_upk, d_waves, d_upw;
   int64_t off_rpart, off_logits, off_ids, off_wts, off_counts, off_offsets, off_pairs, off_inv,
       off_act, off_nact, off_gu, off_h, off_o, off_stage;
+  int64_t off_xb, off_hb, off_chunks, off_nchunks;  // matrix-core path only
+  int max_chunks;
   int64_t stage_stride;
   int64_t bytes;
 };

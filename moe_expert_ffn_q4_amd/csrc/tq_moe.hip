@@ -15,6 +15,7 @@
 #include "tq_gemv_core.h"
 #include "tq_launch.h"
 #include "tq_moe.h"
+#include "tq_prefill.h"
 
 namespace tq {
 
@@ -422,8 +423,17 @@ MoePlan plan_moe(const MoeShape &s) {
   p.off_inv = take(T * k * 4);
   p.off_act = take(3 * (E + 1) * 4);
   p.off_nact = take(4);
-  p.off_gu = take((int64_t)2 * p.gu_ks * p.P * s.ffn * 4);
-  p.off_h = take(p.P * s.ffn * 4);
+  if (s.mfma) {
+    p.d_ks = 1;
+    p.max_chunks = prefill_max_chunks(p.P, p.max_active);
+    p.off_xb = take(T * s.hidden * 2);
+    p.off_hb = take(p.P * s.ffn * 2);
+    p.off_chunks = take((int64_t)3 * p.max_chunks * 4);
+    p.off_nchunks = take(4);
+  } else {
+    p.off_gu = take((int64_t)2 * p.gu_ks * p.P * s.ffn * 4);
+    p.off_h = take(p.P * s.ffn * 4);
+  }
   p.off_o = take((int64_t)p.d_ks * p.P * s.hidden * 4);
   p.stage_stride = align256(s.expert_bytes);
   p.off_stage = take(s.experts_on_host ? (int64_t)(p.max_active) * p.stage_stride : 0);
@@ -467,6 +477,19 @@ int launch_moe_routing(const MoePlan &p, const float *router_w, const float *x, 
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+static int launch_combine(const MoePlan &p, char *ws, float *y, hipStream_t st) {
+  const MoeShape &s = p.s;
+  const int T = (int)s.tokens, k = (int)s.top_k;
+  const int64_t total = (int64_t)T * s.hidden;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)blocks), dim3(256), 0, st,
+                     (const float *)(ws + p.off_o), p.d_ks, p.P, (int)s.hidden,
+                     (const int *)(ws + p.off_inv), (const float *)(ws + p.off_wts), T, k,
+                     s.has_shared, y);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
                        const MoeExpertPtrs &shared, const uint8_t *staging, const float *x,
                        float *y, char *ws, hipStream_t st) {
@@ -487,6 +510,23 @@ int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
   a.topk = k;
   a.Tk = T * k;
   a.P = p.P;
+  if (s.mfma) {
+    PrefillArgs b{};
+    b.experts = experts_dev;
+    b.shared = shared;
+    b.act = a.act;
+    b.n_active = a.n_active;
+    b.chunks = (const int *)(ws + p.off_chunks);
+    b.n_chunks = (const int *)(ws + p.off_nchunks);
+    b.pairs = a.pairs;
+    b.E = E;
+    b.topk = k;
+    b.Tk = T * k;
+    int rc = launch_prefill(p.max_chunks, b, x, T, s.hidden, s.ffn, (uint16_t *)(ws + p.off_xb),
+                            (uint16_t *)(ws + p.off_hb), (float *)(ws + p.off_o), st);
+    if (rc) return rc;
+    return launch_combine(p, ws, y, st);
+  }
   // gate and up
   a.mat0 = 0;
   a.nmat = 2;
@@ -527,15 +567,7 @@ int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
   a.out = (float *)(ws + p.off_o);
   rc = moe_gemv_dispatch(s.type, a, p.max_active, p.d_waves, st);
   if (rc) return rc;
-  {
-    const int64_t total = (int64_t)T * s.hidden;
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > 16384) blocks = 16384;
-    hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)blocks), dim3(256), 0, st, (const float *)a.out,
-                       p.d_ks, p.P, (int)s.hidden, (const int *)(ws + p.off_inv),
-                       (const float *)(ws + p.off_wts), T, k, s.has_shared, y);
-  }
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  return launch_combine(p, ws, y, st);
 }
 
 }  // namespace tq

@@ -396,9 +396,71 @@ static void expert_ffn(int type, int64_t hidden, int64_t ffn, const orc_expert *
   free(h);
 }
 
-int orc_moe(int type, int64_t hidden, int64_t ffn, const orc_expert *experts, int64_t n_experts,
-            const orc_expert *shared, const float *x, int64_t T, int64_t k, const int32_t *ids,
-            const double *weights, const int64_t *tokens, int64_t n_tok, double *y, double *mag) {
+/* The bf16 value of a bf16 bit pattern, widened exactly. */
+static double bf16_value(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* v rounded to fp32 and then to bf16 (each to nearest even). */
+static double round_bf16(double v) { return bf16_value(orc_f32_to_bf16((float)v)); }
+
+/* y[i] = sum_c bf16(w[i][c]) * xb[c] for the n rows of a blob, where bf16(w) is the bf16 rounding
+ * of the fp32 weight and xb holds values already rounded to bf16; fp64, ascending c. */
+static int gemv_bf16(int type, const uint8_t *w, int64_t n, int64_t k, const double *xb,
+                     double *y, double *mag) {
+  const int64_t rb = k / orc_block_weights(type) * orc_block_bytes(type);
+  int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+  for (int64_t i = 0; i < n; ++i) {
+    uint16_t *wb = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)k);
+    if (!wb || orc_dequant_bf16(type, w + i * rb, 1, k, wb) != 0) {
+      bad = 1;
+    } else {
+      double s = 0.0, m = 0.0;
+      for (int64_t c = 0; c < k; ++c) {
+        double p = bf16_value(wb[c]) * xb[c];
+        s += p;
+        m += fabs(p);
+      }
+      y[i] = s;
+      if (mag) mag[i] = m;
+    }
+    free(wb);
+  }
+  return bad ? -1 : 0;
+}
+
+/* The expert FFN with bf16 operands: x, every weight and h rounded to bf16, products summed in
+ * fp64. */
+static void expert_ffn_bf16(int type, int64_t hidden, int64_t ffn, const orc_expert *ex,
+                            const float *x, double *o, double *omag) {
+  double *xb = (double *)malloc(sizeof(double) * (size_t)hidden);
+  double *g = (double *)malloc(sizeof(double) * (size_t)ffn);
+  double *u = (double *)malloc(sizeof(double) * (size_t)ffn);
+  double *h = (double *)malloc(sizeof(double) * (size_t)ffn);
+  for (int64_t c = 0; c < hidden; ++c) xb[c] = round_bf16((double)x[c]);
+  gemv_bf16(type, ex->gate, ffn, hidden, xb, g, NULL);
+  gemv_bf16(type, ex->up, ffn, hidden, xb, u, NULL);
+  orc_swiglu_f64(g, u, ffn, h);
+  for (int64_t f = 0; f < ffn; ++f) h[f] = round_bf16(h[f]);
+  gemv_bf16(type, ex->down, hidden, ffn, h, o, omag);
+  free(xb);
+  free(g);
+  free(u);
+  free(h);
+}
+
+typedef void (*expert_fn)(int, int64_t, int64_t, const orc_expert *, const float *, double *,
+                          double *);
+
+static int moe_body(expert_fn ffn_of, int type, int64_t hidden, int64_t ffn,
+                    const orc_expert *experts, int64_t n_experts, const orc_expert *shared,
+                    const float *x, int64_t T, int64_t k, const int32_t *ids,
+                    const double *weights, const int64_t *tokens, int64_t n_tok, double *y,
+                    double *mag) {
   int64_t bw = orc_block_weights(type);
   if (bw == 0 || hidden % bw || ffn % bw || k < 1) return -1;
   int64_t nt = tokens ? n_tok : T;
@@ -425,14 +487,14 @@ int orc_moe(int type, int64_t hidden, int64_t ffn, const orc_expert *experts, in
         return -1;
       }
       double wt = weights[t * k + j];
-      expert_ffn(type, hidden, ffn, &experts[e], x + t * hidden, o, om);
+      ffn_of(type, hidden, ffn, &experts[e], x + t * hidden, o, om);
       for (int64_t i = 0; i < hidden; ++i) {
         yt[i] += wt * o[i];
         if (mt) mt[i] += fabs(wt) * om[i];
       }
     }
     if (shared) {
-      expert_ffn(type, hidden, ffn, shared, x + t * hidden, o, om);
+      ffn_of(type, hidden, ffn, shared, x + t * hidden, o, om);
       for (int64_t i = 0; i < hidden; ++i) {
         yt[i] += o[i];
         if (mt) mt[i] += om[i];
@@ -442,6 +504,21 @@ int orc_moe(int type, int64_t hidden, int64_t ffn, const orc_expert *experts, in
   free(o);
   free(om);
   return 0;
+}
+
+int orc_moe(int type, int64_t hidden, int64_t ffn, const orc_expert *experts, int64_t n_experts,
+            const orc_expert *shared, const float *x, int64_t T, int64_t k, const int32_t *ids,
+            const double *weights, const int64_t *tokens, int64_t n_tok, double *y, double *mag) {
+  return moe_body(expert_ffn, type, hidden, ffn, experts, n_experts, shared, x, T, k, ids,
+                  weights, tokens, n_tok, y, mag);
+}
+
+int orc_moe_bf16(int type, int64_t hidden, int64_t ffn, const orc_expert *experts,
+                 int64_t n_experts, const orc_expert *shared, const float *x, int64_t T,
+                 int64_t k, const int32_t *ids, const double *weights, const int64_t *tokens,
+                 int64_t n_tok, double *y, double *mag) {
+  return moe_body(expert_ffn_bf16, type, hidden, ffn, experts, n_experts, shared, x, T, k, ids,
+                  weights, tokens, n_tok, y, mag);
 }
 
 /* ---- reference quantizers (round-trip tests only) ---- */

@@ -25,11 +25,11 @@ def _case(*a):
     print("case:", *a, flush=True)
 
 
-def _layer_to_device(t, shape, layer, top_k, renormalize=True):
+def _layer_to_device(t, shape, layer, top_k, renormalize=True, path=0):
     experts = [tuple(dev(b) for b in e) for e in layer["experts"]]
     shared = tuple(dev(b) for b in layer["shared"]) if layer["shared"] is not None else None
     moe = tq.MoeLayer(t, shape["hidden"], shape["ffn"], dev(layer["router"]), experts, shared,
-                      top_k=top_k, renormalize=renormalize)
+                      top_k=top_k, renormalize=renormalize, path=path)
     return moe
 
 
@@ -45,9 +45,13 @@ def _run(moe, x, E, k):
     return host(y), {f: host(v) for f, v in r.items()}
 
 
-def check_moe(t, shape, layer, x, k, tokens=None, renormalize=True, moe=None):
+def check_moe(t, shape, layer, x, k, tokens=None, renormalize=True, moe=None, rel=1e-3, path=0,
+              bf16=False):
+    """Routing bitwise, y within rel * mag + 1e-5 of the oracle (its bf16-operand variant when
+    bf16 is set); returns (layer, y, stats) where stats = (largest err / bound, relative L2 error
+    of the checked rows)."""
     E = len(layer["experts"])
-    moe = moe or _layer_to_device(t, shape, layer, k, renormalize)
+    moe = moe or _layer_to_device(t, shape, layer, k, renormalize, path)
     y, r = _run(moe, x, E, k)
     T = x.shape[0]
     # logits
@@ -73,9 +77,10 @@ def check_moe(t, shape, layer, x, k, tokens=None, renormalize=True, moe=None):
     # output, with the GPU's routing and oracle weights from the GPU's logits
     toks = np.arange(T) if tokens is None else np.asarray(tokens)
     ref, mag = oracle.moe(t, shape["hidden"], shape["ffn"], layer["experts"], layer["shared"], x,
-                          ids, wts, tokens=toks)
-    assert_product_close(y[toks], ref, mag, what=f"moe {t} T={T}")
-    return moe, y
+                          ids, wts, tokens=toks, bf16=bf16)
+    worst = assert_product_close(y[toks], ref, mag, rel=rel, what=f"moe {t} T={T}")
+    l2 = float(np.linalg.norm(y[toks] - ref) / max(np.linalg.norm(ref), 1e-30))
+    return moe, y, (worst, l2)
 
 
 SMALL = [
@@ -93,7 +98,7 @@ def test_moe_small_shapes(t, shape, k, Ts):
     for T in Ts:
         _case("moe-small", t, shape, k, T)
         x = synth.normal_f32(synth.rng(201, "x", t, T), (T, shape["hidden"]))
-        moe, y = check_moe(t, shape, layer, x, k, moe=moe)
+        moe, y, _ = check_moe(t, shape, layer, x, k, moe=moe)
         y2, _ = _run(moe, x, shape["n_experts"], k)
         assert np.array_equal(y, y2), "not deterministic"
 
@@ -111,7 +116,7 @@ def test_moe_equal_logits_all_tokens_on_first_experts():
     layer = synth.moe_layer(shape, t, seed=203, tag="ties")
     layer["router"] = np.zeros_like(layer["router"])
     x = synth.normal_f32(synth.rng(203, "x"), (70, 512))
-    moe, _ = check_moe(t, shape, layer, x, k)
+    moe, _, _ = check_moe(t, shape, layer, x, k)
     _, r = _run(moe, x, 8, k)
     assert np.all(r["topk_ids"] == np.arange(k)) and np.allclose(r["topk_w"], 0.5)
     assert list(r["counts"]) == [70, 70, 0, 0, 0, 0, 0, 0]
@@ -122,7 +127,7 @@ def test_moe_single_expert_equals_dense_ffn():
     t, shape = "q4_k", dict(hidden=512, ffn=1024, n_experts=1, shared=False)
     layer = synth.moe_layer(shape, t, seed=204, tag="one")
     x = synth.normal_f32(synth.rng(204, "x"), (5, 512))
-    _, y = check_moe(t, shape, layer, x, 1)
+    _, y, _ = check_moe(t, shape, layer, x, 1)
     g, u, d = (dev(b) for b in layer["experts"][0])
     xd = dev(x)
     hg = tq.gemv(t, g, 1024, 512, xd)

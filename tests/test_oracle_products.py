@@ -219,3 +219,67 @@ def test_moe_relabelling_experts_leaves_output_unchanged():
         experts2[perm[e]] = layer["experts"][e]
     y2, _ = oracle.moe("q4_k", H, F, experts2, None, x, perm[ids].astype(np.int32), wts)
     assert np.array_equal(y, y2)
+
+
+# ---- the bf16-operand MoE (arithmetic of the matrix-core path) -------------------------------
+
+def _bf16(a):
+    """Round to fp32, then to bf16 (nearest even), widened back to fp64 -- torch's conversion."""
+    import torch
+
+    return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_identity_blob_is_identity():
+    from tests import blobs
+
+    for n in (256, 512):
+        assert np.array_equal(oracle.dequant("q4_k", blobs.identity(n), n, n), np.eye(n))
+
+
+def test_moe_bf16_unit_vectors_reduce_to_elementwise_rounding():
+    """E = 1, k = 1, down = identity, x_t = s_t e_{c_t}: every product has a single term, so
+    y_t[i] = bf16(silu(g) u) with g = bf16(w_gate[i][c]) bf16(s), u likewise."""
+    from tests import blobs
+
+    H = F = 256
+    g = synth.rng(40, "unit")
+    gate, up = synth.blob("q4_k", g, F, H), synth.blob("q4_k", g, F, H)
+    T = 6
+    cols = np.array([0, 1, 63, 64, 200, 255])
+    s = np.array([1.2345678, -3.1415927, 0.1, 7.77, -0.333, 1e-3], np.float32)
+    x = np.zeros((T, H), np.float32)
+    x[np.arange(T), cols] = s
+    ids, wts = np.zeros((T, 1), np.int32), np.ones((T, 1))
+    experts = [(gate, up, blobs.identity(H))]
+    y, _ = oracle.moe("q4_k", H, F, experts, None, x, ids, wts, bf16=True)
+    wg = oracle.dequant("q4_k", gate, F, H)
+    wu = oracle.dequant("q4_k", up, F, H)
+    for t in range(T):
+        gg = _bf16(wg[:, cols[t]]) * _bf16(s[t])
+        uu = _bf16(wu[:, cols[t]]) * _bf16(s[t])
+        ref = _bf16(gg * expit(gg) * uu)
+        assert np.array_equal(y[t], ref), t
+    yx, _ = oracle.moe("q4_k", H, F, experts, None, x, ids, wts)
+    assert not np.array_equal(y, yx)
+
+
+def test_moe_bf16_lattice_only_h_is_rounded():
+    """Weights 0..15 and x in {-1, 0, 1} are exact in bf16, so the bf16 MoE differs from the fp64
+    one only by the rounding of h: |diff| <= (2^-9 + 2^-24) * mag, and it is not zero."""
+    from tests import blobs
+
+    H, F, E, k, T = 256, 512, 3, 2, 5
+    g = synth.rng(41, "lattice")
+    experts = [(blobs.lattice(g, F, H), blobs.lattice(g, F, H), blobs.lattice(g, H, F))
+               for _ in range(E)]
+    shared = (blobs.lattice(g, F, H), blobs.lattice(g, F, H), blobs.lattice(g, H, F))
+    x = synth.ternary_f32(synth.rng(41, "x"), (T, H))
+    ids = np.array([[0, 1], [2, 0], [1, 2], [0, 2], [1, 0]], np.int32)
+    wts = np.full((T, k), 0.5)
+    y, mag = oracle.moe("q4_k", H, F, experts, shared, x, ids, wts)
+    yb, magb = oracle.moe("q4_k", H, F, experts, shared, x, ids, wts, bf16=True)
+    diff = np.abs(yb - y)
+    assert np.all(diff <= (2.0**-9 + 2.0**-24) * mag)
+    assert diff.max() > 0
+    np.testing.assert_allclose(magb, mag, rtol=2.0**-8)
