@@ -22,6 +22,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of the MI355X
 # Sources of the batch-1 Q4_K GEMV; the committed counter summary records their hash, and its
 # HBM traffic is reported only while the kernel is unchanged since the counters were taken.
 GEMV_SOURCES = ("moe_expert_ffn_q4_amd/csrc/tq_dense.hip", "moe_expert_ffn_q4_amd/csrc/tq_gemv_core.h",
@@ -37,9 +38,11 @@ def _args():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--batch", type=int, default=1, help="tokens per decode step (1 or 8)")
     p.add_argument("--workload", default="llama8b",
-                   choices=["llama8b", "mixtral", "deepseek"],
+                   choices=["llama8b", "mixtral", "deepseek", "deepseek-prefill"],
                    help="llama8b: 32-layer dense decode step (default); mixtral / deepseek: one "
-                        "MoE layer at --batch tokens")
+                        "MoE layer at --batch tokens; deepseek-prefill: one DeepSeek-shaped MoE "
+                        "layer over --tokens (default 4096) on the bf16 matrix-core path")
+    p.add_argument("--tokens", type=int, default=4096, help="tokens of the prefill workload")
     p.add_argument("--seed", type=int, default=42)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -230,22 +233,52 @@ def cpu_baseline(synth, batch, seed, budget_s):
                       f"{elapsed:.1f} s, scaled to a 32-layer step"}
 
 
+def moe_cpu_baseline(synth, shape, layer, x, budget_s):
+    """The oracle (as it is) on a bounded sample of the same layer: routing of the sampled tokens
+    and their MoE output, one token at a time until about budget_s of CPU time."""
+    import oracle
+
+    k = shape["top_k"]
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        xt = x[done:done + 1]
+        ids, wts = oracle.topk(oracle.router_logits(xt, layer["router"]), k)
+        oracle.moe("q4_k", shape["hidden"], shape["ffn"], layer["experts"], layer["shared"], xt,
+                   ids, wts)
+        done += 1
+        elapsed = time.perf_counter() - t0
+        if elapsed >= budget_s or done >= x.shape[0]:
+            break
+    return {"value": done / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{done} tokens of the same layer (routing + fp64 MoE output) in "
+                      f"{elapsed:.1f} s"}
+
+
 def moe_bench(args, torch, tq, synth):
-    """One MoE layer (Mixtral- or DeepSeek-shaped, Q4_K experts) at --batch tokens, graph-captured.
-    Roofline: the grouped expert GEMV, algorithmic bytes = blobs of the experts the routing
-    actually selected (plus the shared expert) read once, plus activations."""
+    """One MoE layer (Mixtral- or DeepSeek-shaped, Q4_K experts), graph-captured: decode batches
+    on the fp32 GEMV path, or the 4096-token prefill on the bf16 matrix-core path.
+
+    Roofline of the expert products (the stage that holds the dominant kernels), replayed alone
+    as a graph between two events on its stream: decode -> HBM bytes (blobs of the experts the
+    routing selected plus the shared expert, each read once, and the activations); prefill ->
+    FFN flops (2 * 3 * hidden * ffn per routed pair and per token for the shared expert)."""
     import numpy as np
 
+    prefill = args.workload == "deepseek-prefill"
     shape = synth.MIXTRAL if args.workload == "mixtral" else synth.DEEPSEEK
     k = shape["top_k"]
-    T = args.batch
-    layer = synth.moe_layer(shape, "q4_k", seed=args.seed, tag=args.workload)
+    T = args.tokens if prefill else args.batch
+    tag = "deepseek" if prefill else args.workload
+    layer = synth.moe_layer(shape, "q4_k", seed=args.seed, tag=tag)
     experts = [tuple(torch.from_numpy(b).cuda() for b in e) for e in layer["experts"]]
     shared = tuple(torch.from_numpy(b).cuda() for b in layer["shared"]) if layer["shared"] else None
-    del layer["experts"]
+    path = tq.PATH_BF16_MFMA if prefill else tq.PATH_F32
     moe = tq.MoeLayer("q4_k", shape["hidden"], shape["ffn"], torch.from_numpy(layer["router"]).cuda(),
-                      experts, shared, top_k=k)
-    x = torch.from_numpy(synth.normal_f32(synth.rng(args.seed, "bench-x", T), (T, shape["hidden"]))).cuda()
+                      experts, shared, top_k=k, path=path)
+    xh = synth.normal_f32(synth.rng(args.seed, "bench-x", T), (T, shape["hidden"]))
+    x = torch.from_numpy(xh).cuda()
     y = torch.empty_like(x)
     ws = torch.empty(moe.workspace_bytes(T), dtype=torch.uint8, device="cuda")
     E = shape["n_experts"]
@@ -265,23 +298,57 @@ def moe_bench(args, torch, tq, synth):
             graph.replay()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
+        # the expert-product stage alone (routing already in the workspace)
+        egraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(egraph, stream=stream):
+            moe(x, ws=ws, stages=tq.MOE_EXPERTS)
+        egraph.replay()
+        reps = max(3, args.steps)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(reps):
+            egraph.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+    stage_s = ev0.elapsed_time(ev1) / 1000 / reps
     c = counts.cpu().numpy()
+    H, F = shape["hidden"], shape["ffn"]
     eb = sum(b.numel() for b in experts[0])
     active = int((c > 0).sum()) + (1 if shared else 0)
-    alg_bytes = active * eb + 4 * T * shape["hidden"] * 2 + moe.router_w.numel() * 4
     ms = elapsed * 1000 / args.steps
-    return {
+    if prefill:
+        rows = T * k + (T if shared else 0)
+        flops = 2 * 3 * H * F * rows
+        achieved = flops / stage_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "tq_moe_ffn expert stage: k_prefill gate/up+SwiGLU and down "
+                          "(with x->bf16 and the chunk table)",
+                "avg_launch_us": round(stage_s * 1e6, 1)}
+        dtype = "q4_k weights, bf16 MFMA operands, fp32 accumulation"
+    else:
+        stage_bytes = active * eb + 4 * T * H * 2
+        achieved = stage_bytes / stage_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "tq_moe_ffn expert stage: k_moe_gemv gate/up, SwiGLU, down",
+                "avg_launch_us": round(stage_s * 1e6, 1)}
+        dtype = "q4_k weights, f32 activations and accumulation"
+    out = {
         "metric": METRIC, "value": round(T * args.steps / elapsed, 2), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "q4_k weights, f32 activations and accumulation",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
         "data": "synthetic (seeded random Q4_K experts, N(0,1) activations and router)",
-        "config": {"workload": f"{args.workload}-shaped MoE layer, top-{k} of {E}"
-                               f"{' + shared expert' if shared else ''}, {T} tokens",
-                   "global_batch": T, "seq_len": 1, "parallelism": "none (1 GPU)"},
-        "layer_gbs": round(alg_bytes / (ms / 1000) / 1e9, 1),
+        "config": {"workload": f"{tag}-shaped MoE layer{' prefill' if prefill else ''}, top-{k} "
+                               f"of {E}{' + shared expert' if shared else ''}, {T} tokens",
+                   "global_batch": T, "seq_len": T if prefill else 1,
+                   "parallelism": "none (1 GPU)"},
         "active_experts": active,
+        "roofline": roof,
     }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = moe_cpu_baseline(synth, shape, layer, xh, args.cpu_seconds)
+    return out
 
 
 def main():

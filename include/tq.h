@@ -155,6 +155,27 @@ size_t tq_moe_workspace_bytes(const tq_moe_desc *desc, int64_t tokens);
 int tq_moe_ffn(const tq_moe_desc *desc, const float *x, int64_t tokens, float *y,
                void *workspace, size_t ws_bytes, tq_moe_routing *routing_out, void *stream);
 
+/* Stages of tq_moe_ffn, for tq_moe_ffn_stages. */
+enum { TQ_MOE_ROUTE = 1, TQ_MOE_EXPERTS = 2, TQ_MOE_COMBINE = 4, TQ_MOE_ALL = 7 };
+
+/*
+ * tq_moe_ffn_stages -- the stages of tq_moe_ffn selected by the bit mask `stages`, enqueued in
+ * the order route, experts, combine:
+ *   TQ_MOE_ROUTE    logits, top-k selection and the grouping of the (token, slot) pairs per
+ *                   expert (the selection step of the MoE layer above); fills routing_out;
+ *   TQ_MOE_EXPERTS  every selected expert's SwiGLU FFN on its grouped tokens, and the shared
+ *                   expert's on all tokens, into per-pair outputs kept in the workspace;
+ *   TQ_MOE_COMBINE  y[t] = the routing-weighted sum of token t's pair outputs (slot order),
+ *                   plus the shared expert's.
+ * Arguments as for tq_moe_ffn (y may be NULL without TQ_MOE_COMBINE). The workspace carries the
+ * state between stages: a call without TQ_MOE_ROUTE relies on an earlier call, on the same
+ * stream, with the same desc, tokens, x and workspace, that ran the stages before it. The result
+ * equals tq_moe_ffn's. Lets a caller time the stages or place work between them.
+ */
+int tq_moe_ffn_stages(const tq_moe_desc *desc, const float *x, int64_t tokens, float *y,
+                      void *workspace, size_t ws_bytes, tq_moe_routing *routing_out, int stages,
+                      void *stream);
+
 /* Text of the last non-TQ_OK status returned on this thread ("" if none). */
 const char *tq_last_error(void);
 

@@ -19,6 +19,7 @@ Q4_K, Q6_K, Q8_0 = 1, 2, 3
 TYPES = {"q4_k": Q4_K, "q6_k": Q6_K, "q8_0": Q8_0}
 F32, BF16 = 0, 1
 PATH_AUTO, PATH_F32, PATH_BF16_MFMA = 0, 1, 2
+MOE_ROUTE, MOE_EXPERTS, MOE_COMBINE, MOE_ALL = 1, 2, 4, 7
 STATUS = {0: "TQ_OK", 1: "TQ_EINVAL", 2: "TQ_ESHAPE", 3: "TQ_EALIGN", 4: "TQ_ENOSPC",
           5: "TQ_EUNSUPPORTED", 6: "TQ_EDEVICE"}
 
@@ -86,6 +87,9 @@ def _declare(L: C.CDLL) -> None:
         L.tq_moe_ffn.argtypes = [C.POINTER(MoeDesc), _vp, _i64, _vp, _vp, C.c_size_t,
                                  C.POINTER(MoeRouting), _vp]
         L.tq_moe_ffn.restype = _int
+        L.tq_moe_ffn_stages.argtypes = [C.POINTER(MoeDesc), _vp, _i64, _vp, _vp, C.c_size_t,
+                                        C.POINTER(MoeRouting), _int, _vp]
+        L.tq_moe_ffn_stages.restype = _int
 
 
 def _check(rc: int) -> None:
@@ -196,11 +200,13 @@ class MoeLayer:
         return int(lib().tq_moe_workspace_bytes(C.byref(self.desc), tokens))
 
     def __call__(self, x: torch.Tensor, out=None, ws=None, routing: dict | None = None,
-                 stream=None):
+                 stream=None, stages: int = MOE_ALL):
         """y = MoE(x) for x [T, hidden] fp32. routing: dict of preallocated device tensors
-        (topk_ids, topk_w, logits, counts, offsets, pairs) to receive the routing."""
+        (topk_ids, topk_w, logits, counts, offsets, pairs) to receive the routing. stages: a
+        subset of MOE_ROUTE | MOE_EXPERTS | MOE_COMBINE (tq_moe_ffn_stages); the same ws must
+        then be passed to the calls that run the later stages."""
         T = x.shape[0]
-        if out is None:
+        if out is None and stages & MOE_COMBINE:
             out = torch.empty_like(x)
         if ws is None:
             need = self.workspace_bytes(T)
@@ -209,7 +215,12 @@ class MoeLayer:
         if routing is not None:
             r = MoeRouting(*[(routing[f].data_ptr() if routing.get(f) is not None else None)
                              for f, _ in MoeRouting._fields_])
-        _check(lib().tq_moe_ffn(C.byref(self.desc), x.data_ptr(), T, out.data_ptr(),
-                                _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
-                                C.byref(r) if r is not None else None, _stream(stream)))
+        nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+        rr = C.byref(r) if r is not None else None
+        if stages == MOE_ALL:
+            _check(lib().tq_moe_ffn(C.byref(self.desc), x.data_ptr(), T, out.data_ptr(),
+                                    _ptr(ws), nbytes, rr, _stream(stream)))
+        else:
+            _check(lib().tq_moe_ffn_stages(C.byref(self.desc), x.data_ptr(), T, _ptr(out),
+                                           _ptr(ws), nbytes, rr, stages, _stream(stream)))
         return out

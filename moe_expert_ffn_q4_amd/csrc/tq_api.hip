@@ -141,12 +141,16 @@ size_t tq_moe_workspace_bytes(const tq_moe_desc *desc, int64_t tokens) {
   return (size_t)tq::plan_moe(s).bytes;
 }
 
-int tq_moe_ffn(const tq_moe_desc *d, const float *x, int64_t tokens, float *y, void *workspace,
-               size_t ws_bytes, tq_moe_routing *routing_out, void *stream) {
+int tq_moe_ffn_stages(const tq_moe_desc *d, const float *x, int64_t tokens, float *y,
+                      void *workspace, size_t ws_bytes, tq_moe_routing *routing_out, int stages,
+                      void *stream) {
   tq::MoeShape s;
   int rc = moe_check(d, tokens, &s);
   if (rc != TQ_OK) return rc;
-  if (!x || !y || !workspace) return fail(TQ_EINVAL, "tq_moe_ffn: null x, y or workspace");
+  if (stages <= 0 || (stages & ~TQ_MOE_ALL))
+    return fail(TQ_EINVAL, "tq_moe_ffn: stage mask %d not a non-empty subset of TQ_MOE_ALL", stages);
+  if (!x || !workspace || ((stages & TQ_MOE_COMBINE) && !y))
+    return fail(TQ_EINVAL, "tq_moe_ffn: null x, y or workspace");
   if (!aligned(x, 16) || !aligned(y, 4) || !aligned(workspace, 256))
     return fail(TQ_EALIGN, "tq_moe_ffn: x 16-byte, y 4-byte, workspace 256-byte alignment needed");
   const tq::MoePlan p = tq::plan_moe(s);
@@ -155,21 +159,35 @@ int tq_moe_ffn(const tq_moe_desc *d, const float *x, int64_t tokens, float *y, v
   if (s.experts_on_host) return fail(TQ_EUNSUPPORTED, "tq_moe_ffn: host-resident experts not built yet");
   hipStream_t st = (hipStream_t)stream;
   char *ws = (char *)workspace;
-  if (tq::launch_moe_routing(p, d->router_w, x, ws, st)) return launched(-1, "tq_moe_ffn routing");
-  if (routing_out) {
-    const int64_t T = tokens, E = s.n_experts, k = s.top_k;
-    struct { void *dst; int64_t off, bytes; } cp[] = {
-        {routing_out->topk_ids, p.off_ids, T * k * 4}, {routing_out->topk_w, p.off_wts, T * k * 4},
-        {routing_out->logits, p.off_logits, T * E * 4}, {routing_out->counts, p.off_counts, E * 4},
-        {routing_out->offsets, p.off_offsets, (E + 1) * 4}, {routing_out->pairs, p.off_pairs, T * k * 4}};
-    for (auto &c : cp)
-      if (c.dst && hipMemcpyAsync(c.dst, ws + c.off, (size_t)c.bytes, hipMemcpyDeviceToDevice, st) != hipSuccess)
-        return fail(TQ_EDEVICE, "tq_moe_ffn: routing copy failed");
+  if (stages & TQ_MOE_ROUTE) {
+    if (tq::launch_moe_routing(p, d->router_w, x, ws, st)) return launched(-1, "tq_moe_ffn routing");
+    if (routing_out) {
+      const int64_t T = tokens, E = s.n_experts, k = s.top_k;
+      struct { void *dst; int64_t off, bytes; } cp[] = {
+          {routing_out->topk_ids, p.off_ids, T * k * 4}, {routing_out->topk_w, p.off_wts, T * k * 4},
+          {routing_out->logits, p.off_logits, T * E * 4}, {routing_out->counts, p.off_counts, E * 4},
+          {routing_out->offsets, p.off_offsets, (E + 1) * 4}, {routing_out->pairs, p.off_pairs, T * k * 4}};
+      for (auto &c : cp)
+        if (c.dst && hipMemcpyAsync(c.dst, ws + c.off, (size_t)c.bytes, hipMemcpyDeviceToDevice, st) != hipSuccess)
+          return fail(TQ_EDEVICE, "tq_moe_ffn: routing copy failed");
+    }
   }
-  tq::MoeExpertPtrs shared{{d->shared.gate, d->shared.up, d->shared.down}};
-  rc = tq::launch_moe_experts(p, reinterpret_cast<const tq::MoeExpertPtrs *>(d->experts), shared,
-                              nullptr, x, y, ws, st);
-  return launched(rc, "tq_moe_ffn experts");
+  if (stages & TQ_MOE_EXPERTS) {
+    tq::MoeExpertPtrs shared{{d->shared.gate, d->shared.up, d->shared.down}};
+    rc = tq::launch_moe_experts(p, reinterpret_cast<const tq::MoeExpertPtrs *>(d->experts), shared,
+                                nullptr, x, ws, st);
+    if (rc) return launched(rc, "tq_moe_ffn experts");
+  }
+  if (stages & TQ_MOE_COMBINE) {
+    if (tq::launch_moe_combine(p, ws, y, st)) return launched(-1, "tq_moe_ffn combine");
+  }
+  return TQ_OK;
+}
+
+int tq_moe_ffn(const tq_moe_desc *d, const float *x, int64_t tokens, float *y, void *workspace,
+               size_t ws_bytes, tq_moe_routing *routing_out, void *stream) {
+  if (!y) return fail(TQ_EINVAL, "tq_moe_ffn: null x, y or workspace");
+  return tq_moe_ffn_stages(d, x, tokens, y, workspace, ws_bytes, routing_out, TQ_MOE_ALL, stream);
 }
 
 }  // extern "C"

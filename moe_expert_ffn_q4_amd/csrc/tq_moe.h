@@ -38,8 +38,11 @@ MoePlan plan_moe(const MoeShape &s);
 size_t group_lds_bytes(int64_t T, int64_t E);
 int launch_moe_routing(const MoePlan &p, const float *router_w, const float *x, char *ws,
                        hipStream_t st);
+// Expert products of the routed pairs into the per-position outputs in the workspace.
 int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
                        const MoeExpertPtrs &shared, const uint8_t *staging, const float *x,
-                       float *y, char *ws, hipStream_t st);
+                       char *ws, hipStream_t st);
+// y[t] = the routing-weighted sum of the per-position outputs (plus the shared expert's).
+int launch_moe_combine(const MoePlan &p, char *ws, float *y, hipStream_t st);
 
 }  // namespace tq

@@ -477,7 +477,7 @@ int launch_moe_routing(const MoePlan &p, const float *router_w, const float *x, 
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-static int launch_combine(const MoePlan &p, char *ws, float *y, hipStream_t st) {
+int launch_moe_combine(const MoePlan &p, char *ws, float *y, hipStream_t st) {
   const MoeShape &s = p.s;
   const int T = (int)s.tokens, k = (int)s.top_k;
   const int64_t total = (int64_t)T * s.hidden;
@@ -492,7 +492,7 @@ static int launch_combine(const MoePlan &p, char *ws, float *y, hipStream_t st) 
 
 int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
                        const MoeExpertPtrs &shared, const uint8_t *staging, const float *x,
-                       float *y, char *ws, hipStream_t st) {
+                       char *ws, hipStream_t st) {
   const MoeShape &s = p.s;
   const int E = (int)s.n_experts, T = (int)s.tokens, k = (int)s.top_k;
   MoeGemvArgs a{};
@@ -522,10 +522,8 @@ int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
     b.E = E;
     b.topk = k;
     b.Tk = T * k;
-    int rc = launch_prefill(p.max_chunks, b, x, T, s.hidden, s.ffn, (uint16_t *)(ws + p.off_xb),
-                            (uint16_t *)(ws + p.off_hb), (float *)(ws + p.off_o), st);
-    if (rc) return rc;
-    return launch_combine(p, ws, y, st);
+    return launch_prefill(p.max_chunks, b, x, T, s.hidden, s.ffn, (uint16_t *)(ws + p.off_xb),
+                          (uint16_t *)(ws + p.off_hb), (float *)(ws + p.off_o), st);
   }
   // gate and up
   a.mat0 = 0;
@@ -565,9 +563,7 @@ int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
   a.ldx = s.ffn;
   a.x_by_token = 0;
   a.out = (float *)(ws + p.off_o);
-  rc = moe_gemv_dispatch(s.type, a, p.max_active, p.d_waves, st);
-  if (rc) return rc;
-  return launch_combine(p, ws, y, st);
+  return moe_gemv_dispatch(s.type, a, p.max_active, p.d_waves, st);
 }
 
 }  // namespace tq

@@ -35,7 +35,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kChunk = 160;           // token rows per chunk (5 tiles of 32)
-constexpr int kTiles = kChunk / 32;
 constexpr int kRowStride = 272;       // LDS bytes per token row: 128 bf16 + 16 bytes of padding
 constexpr int kBufBytes = kChunk * kRowStride;
 
@@ -54,31 +53,57 @@ __global__ __launch_bounds__(256) void k_to_bf16(const float *__restrict__ x, in
 
 // ---- chunk table --------------------------------------------------------------------------------
 // chunks[3c .. 3c+2] = (active slot, first position, rows); an expert with cnt rows is cut into
-// ceil(cnt / kChunk) chunks of near-equal size. One thread: at most a few hundred experts.
-__global__ void k_chunk_table(const int *__restrict__ act, const int *__restrict__ n_active,
-                              int E, int max_chunks, int *__restrict__ chunks,
-                              int *__restrict__ n_chunks) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+// ceil(cnt / kChunk) chunks of near-equal size, chunks in slot order. One workgroup of 256
+// threads, a thread per slot, an LDS prefix sum over each batch of 256 slots.
+__global__ __launch_bounds__(256) void k_chunk_table(const int *__restrict__ act,
+                                                     const int *__restrict__ n_active, int E,
+                                                     int max_chunks, int *__restrict__ chunks,
+                                                     int *__restrict__ n_chunks) {
+  __shared__ int scan[256];
   const int na = *n_active;
-  int nc = 0;
-  for (int s = 0; s < na; ++s) {
-    const int p0 = act[(E + 1) + s], cnt = act[2 * (E + 1) + s];
-    const int parts = (cnt + kChunk - 1) / kChunk;
-    const int base = cnt / parts, extra = cnt - base * parts;
-    int p = p0;
-    for (int q = 0; q < parts && nc < max_chunks; ++q) {
-      const int rows = base + (q < extra ? 1 : 0);
-      chunks[3 * nc] = s;
-      chunks[3 * nc + 1] = p;
-      chunks[3 * nc + 2] = rows;
-      p += rows;
-      ++nc;
+  int base = 0;  // chunks of the earlier batches
+  for (int s0 = 0; s0 < na; s0 += 256) {
+    const int s = s0 + (int)threadIdx.x;
+    int cnt = 0, p0 = 0, parts = 0;
+    if (s < na) {
+      p0 = act[(E + 1) + s];
+      cnt = act[2 * (E + 1) + s];
+      parts = (cnt + kChunk - 1) / kChunk;
     }
+    scan[threadIdx.x] = parts;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {  // inclusive scan
+      const int v = threadIdx.x >= (unsigned)d ? scan[threadIdx.x - d] : 0;
+      __syncthreads();
+      scan[threadIdx.x] += v;
+      __syncthreads();
+    }
+    int nc = base + scan[threadIdx.x] - parts;
+    if (parts) {
+      const int rows0 = cnt / parts, extra = cnt - rows0 * parts;
+      int p = p0;
+      for (int q = 0; q < parts && nc < max_chunks; ++q) {
+        const int rows = rows0 + (q < extra ? 1 : 0);
+        chunks[3 * nc] = s;
+        chunks[3 * nc + 1] = p;
+        chunks[3 * nc + 2] = rows;
+        p += rows;
+        ++nc;
+      }
+    }
+    base += scan[255];
+    __syncthreads();
   }
-  *n_chunks = nc;
+  if (threadIdx.x == 0) *n_chunks = base < max_chunks ? base : max_chunks;
 }
 
 // ---- the grouped product ------------------------------------------------------------------------
+
+// Loads through the global address space (the blob pointers come from a device table, so the
+// compiler would otherwise issue generic loads, which it cannot count precisely).
+typedef const u32x4 __attribute__((address_space(1))) *gu32x4;
+
+__device__ __forceinline__ u32x4 gload(const void *p) { return *(gu32x4)p; }
 
 // Raw bytes of one Q4_K row for one step: the block header (d, dmin, 12 scale bytes) and the
 // lane's 32 quant bytes.
@@ -87,10 +112,10 @@ struct RawRow {
 };
 
 __device__ __forceinline__ void load_raw(const uint8_t *row, int kb, int c, RawRow &r) {
-  const u32x4 *b = reinterpret_cast<const u32x4 *>(row + (int64_t)kb * 144);
-  r.head = b[0];
-  r.q0 = b[1 + 2 * c];
-  r.q1 = b[2 + 2 * c];
+  const uint8_t *b = row + (int64_t)kb * 144;
+  r.head = gload(b);
+  r.q0 = gload(b + 16 + 32 * c);
+  r.q1 = gload(b + 32 + 32 * c);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -136,39 +161,141 @@ __device__ __forceinline__ bf16x8 dequant_step(const RawRow &r, const GroupScale
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Token rows of step st (k = 128*st .. +127) of the chunk: thread task q covers row q/16, bytes
-// 16*(q%16) of that k range (8 bf16), loaded into registers first and written to LDS later.
-constexpr int kTokTasks = kChunk * 16 / 256;
+__device__ __forceinline__ float silu_mul(float g, float u) { return g * u / (1.f + expf(-g)); }
 
-__device__ __forceinline__ void load_tokens(const uint16_t *xsrc, const int64_t *rowoff, int rows,
-                                            int st, u32x4 (&v)[kTokTasks]) {
+// Token staging. Thread tid copies the 16 bytes at k offset 8*(tid % 16) of the step's 128 k
+// for rows tid/16 + 16 i (i < 2 NT), clamped to the chunk's last row: rows past the chunk only
+// feed token columns that are never stored. In LDS the 8 k of that piece go to two entries:
+// k-half kg = pc/8, steps s and s+1 (s = 2 (pc % 4)), low-nibble half (bytes 0..7 of the
+// 16-byte entry) for pc % 8 < 4, else the high half.
+template <bool GU, int NT>
+__device__ __forceinline__ void prefill_tiles(const PrefillArgs &a, uint8_t (*tok)[kBufBytes],
+                                              const int64_t *rowoff, int rows, int p0,
+                                              const uint8_t *const (&wrow)[2], int col0) {
+  const int lane = threadIdx.x & 63;
+  const int lrow = lane & 31, kg = lane >> 5;
+  const int pc = threadIdx.x & 15, trow = threadIdx.x >> 4;
+  const uint16_t *src[2 * NT];
 #pragma unroll
-  for (int i = 0; i < kTokTasks; ++i) {
-    const int q = (int)threadIdx.x + 256 * i;
-    const int t = q >> 4, pc = q & 15;
-    if (t < rows)
-      v[i] = *reinterpret_cast<const u32x4 *>(xsrc + rowoff[t] + 128 * st + 8 * pc);
+  for (int i = 0; i < 2 * NT; ++i)
+    src[i] = a.xsrc + rowoff[min(trow + 16 * i, rows - 1)] + 8 * pc;
+  const int dst = (trow * kRowStride) + ((pc >> 3) * 8 + 2 * (pc & 3)) * 16 + 8 * ((pc >> 2) & 1);
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+  const float unit_inv = 1.f / nibble_fp8_unit();
+  f32x16 acc[NT][2];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[t][r][j] = 0.f;
+
+  const int steps = 2 * a.kblocks;
+  RawRow raw[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) load_raw(wrow[r], 0, kg, raw[r]);
+  u32x4 tv[2 * NT];
+#pragma unroll
+  for (int i = 0; i < 2 * NT; ++i) tv[i] = gload(src[i]);
+#pragma unroll
+  for (int i = 0; i < 2 * NT; ++i) {
+    uint8_t *d = tok[0] + dst + 16 * i * kRowStride;
+    *reinterpret_cast<u32x2 *>(d) = (u32x2){tv[i].x, tv[i].y};
+    *reinterpret_cast<u32x2 *>(d + 16) = (u32x2){tv[i].z, tv[i].w};
   }
-}
+  __syncthreads();
 
-__device__ __forceinline__ void store_tokens(uint8_t *buf, int rows, const u32x4 (&v)[kTokTasks]) {
+  for (int st = 0; st < steps; ++st) {
+    const int c = 2 * (st & 1) + kg;  // the lane's group in block st/2
+    const RawRow cur[2] = {raw[0], raw[1]};
+    const bool more = st + 1 < steps;
+    if (more) {
+      const int nst = st + 1;
 #pragma unroll
-  for (int i = 0; i < kTokTasks; ++i) {
-    const int q = (int)threadIdx.x + 256 * i;
-    const int t = q >> 4, pc = q & 15;
-    if (t < rows) {
-      // 8 consecutive k of piece pc: k-half kg = pc/8, steps s and s+1 (s = 2*(pc%4)),
-      // low-nibble half (bytes 0..7 of a 16-byte entry) for pc%8 < 4, else the high half.
-      const int kg = pc >> 3, s = 2 * (pc & 3), hi = (pc >> 2) & 1;
-      uint8_t *dst = buf + t * kRowStride + (kg * 8 + s) * 16 + 8 * hi;
-      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      *reinterpret_cast<u32x2 *>(dst) = (u32x2){v[i].x, v[i].y};
-      *reinterpret_cast<u32x2 *>(dst + 16) = (u32x2){v[i].z, v[i].w};
+      for (int r = 0; r < 2; ++r) load_raw(wrow[r], nst >> 1, 2 * (nst & 1) + kg, raw[r]);
+#pragma unroll
+      for (int i = 0; i < 2 * NT; ++i) tv[i] = gload(src[i] + 128 * nst);
+    }
+    const GroupScale gs[2] = {group_scale(cur[0], c, unit_inv), group_scale(cur[1], c, unit_inv)};
+    const uint8_t *buf = tok[st & 1] + lrow * kRowStride + kg * 128;
+    // Software pipeline over the 8 k steps: while the matrix cores work on step s, the lanes
+    // dequantize the A operands of step s+1 and read its B operands from LDS.
+    bf16x8 a0 = dequant_step(cur[0], gs[0], 0), a1 = dequant_step(cur[1], gs[1], 0);
+    bf16x8 bv[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      bv[t] = *reinterpret_cast<const bf16x8 *>(buf + 32 * t * kRowStride);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      bf16x8 n0, n1, nb[NT];
+      if (s < 7) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          nb[t] = *reinterpret_cast<const bf16x8 *>(buf + 32 * t * kRowStride + 16 * (s + 1));
+        n0 = dequant_step(cur[0], gs[0], s + 1);
+        n1 = dequant_step(cur[1], gs[1], s + 1);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        acc[t][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bv[t], acc[t][0], 0, 0, 0);
+        acc[t][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bv[t], acc[t][1], 0, 0, 0);
+      }
+      if (s < 7) {
+        // issue order: the LDS reads, then each MFMA followed by a share of the VALU work
+        __builtin_amdgcn_sched_group_barrier(0x100, NT, 0);
+#pragma unroll
+        for (int t = 0; t < 2 * NT; ++t) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 40 / (2 * NT) + 1, 0);
+        }
+        a0 = n0;
+        a1 = n1;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) bv[t] = nb[t];
+      }
+    }
+    if (more) {
+      uint8_t *nb = tok[(st + 1) & 1] + dst;
+#pragma unroll
+      for (int i = 0; i < 2 * NT; ++i) {
+        uint8_t *d = nb + 16 * i * kRowStride;
+        *reinterpret_cast<u32x2 *>(d) = (u32x2){tv[i].x, tv[i].y};
+        *reinterpret_cast<u32x2 *>(d + 16) = (u32x2){tv[i].z, tv[i].w};
+      }
+    }
+    __syncthreads();
+  }
+
+  // epilogue: lane holds rows 8*(i/4) + 4*kg + i%4 of token column lrow of each tile
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int tr = 32 * t + lrow;
+    if (tr < rows) {
+      const int64_t p = p0 + tr;
+      if (GU) {
+        uint16_t *h = (uint16_t *)a.out + p * a.ldo + col0;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float hv[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) hv[q] = silu_mul(acc[t][0][4 * g + q], acc[t][1][4 * g + q]);
+          *reinterpret_cast<u32x2 *>(h + 8 * g + 4 * kg) =
+              (u32x2){pack_bf16(hv[0], hv[1]), pack_bf16(hv[2], hv[3])};
+        }
+      } else {
+        float *o = (float *)a.out + p * a.ldo + col0;
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<float4 *>(o + 32 * r + 8 * g + 4 * kg) =
+                make_float4(acc[t][r][4 * g], acc[t][r][4 * g + 1], acc[t][r][4 * g + 2],
+                            acc[t][r][4 * g + 3]);
+      }
     }
   }
 }
-
-__device__ __forceinline__ float silu_mul(float g, float u) { return g * u / (1.f + expf(-g)); }
 
 template <bool GU>
 __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
@@ -192,8 +319,7 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
     rowoff[t] = r * a.ldx;
   }
 
-  const int lane = threadIdx.x & 63, wave = wave_index();
-  const int lrow = lane & 31, kg = lane >> 5;
+  const int lrow = threadIdx.x & 31, wave = wave_index();
   // the lane's two weight rows (row-block 0 and 1)
   const uint8_t *wrow[2];
   int col0;  // GU: first ffn column of the wave; down: first hidden row of the wave
@@ -206,84 +332,13 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
     wrow[0] = (const uint8_t *)ex.m[2] + (int64_t)(col0 + lrow) * a.row_bytes;
     wrow[1] = (const uint8_t *)ex.m[2] + (int64_t)(col0 + 32 + lrow) * a.row_bytes;
   }
-  const int ntt = (rows + 31) >> 5;
-  const float unit_inv = 1.f / nibble_fp8_unit();
-
-  f32x16 acc[kTiles][2];
-#pragma unroll
-  for (int t = 0; t < kTiles; ++t)
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[t][r][j] = 0.f;
-
   __syncthreads();  // rowoff
-  const int steps = 2 * a.kblocks;
-  u32x4 tv[kTokTasks];
-  load_tokens(a.xsrc, rowoff, rows, 0, tv);
-  RawRow raw[2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) load_raw(wrow[r], 0, kg, raw[r]);
-  store_tokens(tok[0], rows, tv);
-  __syncthreads();
-
-  for (int st = 0; st < steps; ++st) {
-    const int c = 2 * (st & 1) + kg;  // the lane's group in block st/2
-    const RawRow cur[2] = {raw[0], raw[1]};
-    const GroupScale gs[2] = {group_scale(cur[0], c, unit_inv), group_scale(cur[1], c, unit_inv)};
-    const bool more = st + 1 < steps;
-    if (more) {
-      load_tokens(a.xsrc, rowoff, rows, st + 1, tv);
-      const int nst = st + 1, nc = 2 * (nst & 1) + kg;
-#pragma unroll
-      for (int r = 0; r < 2; ++r) load_raw(wrow[r], nst >> 1, nc, raw[r]);
-    }
-    const uint8_t *buf = tok[st & 1];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const bf16x8 av0 = dequant_step(cur[0], gs[0], s), av1 = dequant_step(cur[1], gs[1], s);
-#pragma unroll
-      for (int t = 0; t < kTiles; ++t) {
-        if (t < ntt) {
-          const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(
-              buf + (32 * t + lrow) * kRowStride + (kg * 8 + s) * 16);
-          acc[t][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av0, bv, acc[t][0], 0, 0, 0);
-          acc[t][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av1, bv, acc[t][1], 0, 0, 0);
-        }
-      }
-    }
-    if (more) store_tokens(tok[(st + 1) & 1], rows, tv);
-    __syncthreads();
-  }
-
-  // epilogue: lane holds rows 8*(i/4) + 4*kg + i%4 of token column lrow of each tile
-#pragma unroll
-  for (int t = 0; t < kTiles; ++t) {
-    const int tr = 32 * t + lrow;
-    if (t < ntt && tr < rows) {
-      const int64_t p = p0 + tr;
-      if (GU) {
-        uint16_t *h = (uint16_t *)a.out + p * a.ldo + col0;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-          float hv[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) hv[q] = silu_mul(acc[t][0][4 * g + q], acc[t][1][4 * g + q]);
-          *reinterpret_cast<u32x2 *>(h + 8 * g + 4 * kg) =
-              (u32x2){pack_bf16(hv[0], hv[1]), pack_bf16(hv[2], hv[3])};
-        }
-      } else {
-        float *o = (float *)a.out + p * a.ldo + col0;
-#pragma unroll
-        for (int r = 0; r < 2; ++r)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            *reinterpret_cast<float4 *>(o + 32 * r + 8 * g + 4 * kg) =
-                make_float4(acc[t][r][4 * g], acc[t][r][4 * g + 1], acc[t][r][4 * g + 2],
-                            acc[t][r][4 * g + 3]);
-      }
-    }
+  switch ((rows + 31) >> 5) {
+    case 1: prefill_tiles<GU, 1>(a, tok, rowoff, rows, p0, wrow, col0); break;
+    case 2: prefill_tiles<GU, 2>(a, tok, rowoff, rows, p0, wrow, col0); break;
+    case 3: prefill_tiles<GU, 3>(a, tok, rowoff, rows, p0, wrow, col0); break;
+    case 4: prefill_tiles<GU, 4>(a, tok, rowoff, rows, p0, wrow, col0); break;
+    default: prefill_tiles<GU, 5>(a, tok, rowoff, rows, p0, wrow, col0); break;
   }
 }
 
@@ -301,7 +356,7 @@ int launch_prefill(int max_chunks, PrefillArgs a, const float *x, int64_t tokens
     if (blocks > 8192) blocks = 8192;
     hipLaunchKernelGGL(k_to_bf16, dim3((unsigned)blocks), dim3(256), 0, st, x, n, (uint32_t *)xb);
   }
-  hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(64), 0, st, a.act, a.n_active, a.E,
+  hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(256), 0, st, a.act, a.n_active, a.E,
                      max_chunks, (int *)a.chunks, (int *)a.n_chunks);
   const int groups = (max_chunks + 7) / 8;
   // gate / up

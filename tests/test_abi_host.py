@@ -70,3 +70,40 @@ def test_dequant_and_swiglu_reject():
     assert L.tq_swiglu(16, 16, -1, 16, None) == 2
     assert L.tq_swiglu(None, 16, 4, 16, None) == 1
     assert L.tq_swiglu(16, 16, 0, 16, None) == 0
+
+
+def _moe_desc(t=1, hidden=7168, ffn=2048, E=256, k=8, path=0):
+    d = tq.MoeDesc()
+    d.type, d.hidden, d.ffn, d.n_experts, d.top_k = t, hidden, ffn, E, k
+    d.router_w = 0x10000  # never dereferenced: every call below fails validation first
+    d.experts = 0x20000
+    d.path = path
+    return d
+
+
+def test_moe_workspace_sizes_follow_the_path():
+    import ctypes as C
+
+    L = tq.lib()
+    f32 = L.tq_moe_workspace_bytes(C.byref(_moe_desc(path=tq.PATH_F32)), 4096)
+    mf = L.tq_moe_workspace_bytes(C.byref(_moe_desc(path=tq.PATH_BF16_MFMA)), 4096)
+    auto = L.tq_moe_workspace_bytes(C.byref(_moe_desc(path=tq.PATH_AUTO)), 4096)
+    P = 4096 * 8
+    assert mf == auto  # 128 routed tokens per expert: AUTO takes the matrix cores
+    assert mf >= P * 7168 * 4 + P * 2048 * 2 + 4096 * 7168 * 2 and f32 >= P * 2048 * 4
+    assert L.tq_moe_workspace_bytes(C.byref(_moe_desc(t=2, path=tq.PATH_BF16_MFMA)), 4096) == 0
+
+
+def test_moe_stages_and_path_rejected_before_any_launch():
+    import ctypes as C
+
+    L = tq.lib()
+    d = _moe_desc(hidden=512, ffn=512, E=8, k=2)
+    for stages in (0, 8, -1):
+        assert L.tq_moe_ffn_stages(C.byref(d), 0x30000, 4, 0x40000, 0x50000, 1 << 30, None,
+                                   stages, None) == 1
+    assert L.tq_moe_ffn_stages(C.byref(d), 0x30000, 4, 0x40000, 0x50000, 256, None,
+                               tq.MOE_ALL, None) == 4  # workspace too small
+    d6 = _moe_desc(t=2, hidden=512, ffn=512, E=8, k=2, path=tq.PATH_BF16_MFMA)
+    assert L.tq_moe_ffn(C.byref(d6), 0x30000, 4, 0x40000, 0x50000, 1 << 30, None, None) == 5
+    assert "Q4_K" in L.tq_last_error().decode()

@@ -188,3 +188,23 @@ def test_moe_deepseek_shape_sampled_tokens(deepseek, T):
     x = synth.normal_f32(synth.rng(synth.DEFAULT_SEED, "deepseek-x", T), (T, 7168))
     toks = [0] if T == 1 else [0, 255]
     check_moe("q4_k", synth.DEEPSEEK, deepseek, x, 8, tokens=toks)
+
+
+@pytest.mark.parametrize("path", [0, 2], ids=["auto-f32", "bf16-mfma"])
+def test_moe_stages_equal_one_call(path):
+    """tq_moe_ffn_stages: route, experts and combine as three calls on one workspace give the
+    one-call result bitwise."""
+    t, shape, k, T = "q4_k", dict(hidden=512, ffn=512, n_experts=8, shared=True), 2, 300
+    layer = synth.moe_layer(shape, t, seed=207, tag="stages")
+    moe = _layer_to_device(t, shape, layer, k, path=path)
+    x = dev(synth.normal_f32(synth.rng(207, "x"), (T, 512)))
+    y_all = host(moe(x))
+    ws = torch.zeros(moe.workspace_bytes(T), dtype=torch.uint8, device="cuda:0")
+    moe(x, ws=ws, stages=tq.MOE_ROUTE)
+    moe(x, ws=ws, stages=tq.MOE_EXPERTS)
+    y = torch.full_like(x, float("nan"))
+    moe(x, out=y, ws=ws, stages=tq.MOE_COMBINE)
+    assert np.array_equal(host(y), y_all)
+    moe(x, out=y, ws=ws, stages=tq.MOE_ROUTE | tq.MOE_EXPERTS)
+    y2 = moe(x, ws=ws, stages=tq.MOE_COMBINE)
+    assert np.array_equal(host(y2), y_all)
