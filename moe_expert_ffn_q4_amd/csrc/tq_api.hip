@@ -2,7 +2,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
-#include "../../include/tq.h"
+#include "tq.h"
 #include "tq_launch.h"
 #include "tq_moe.h"
 

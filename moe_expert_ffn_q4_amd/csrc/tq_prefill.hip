@@ -15,14 +15,16 @@
 //
 // Q4_K block -> k order. One workgroup step covers 128 weights of every row (half a 256-weight
 // block); lane kg of that step owns the 64 weights of group c = 2*half + kg (bytes
-// qs[32c .. 32c+31]: low nibbles are sub-block 2c, high nibbles sub-block 2c+1). Its 16-wide k
-// step s (0..7) uses the dword qs[32c + 4s ..]: the four low-nibble weights first, then the four
-// high-nibble ones. The token tile in LDS is stored in the same order, so a product over a step
-// is a plain dot product over one permutation of k.
+// qs[32c .. 32c+31]: low nibbles are sub-block 2c, high nibbles sub-block 2c+1), and its 16-wide
+// k step s (0..7) holds the 8 consecutive weights 64c + 8s .. 64c + 8s + 7 (in k order, so the
+// token operand is 8 consecutive activations).
 //
 // Each weight is dequantized once per chunk (fp32 fma of d*sc and -dmin*m, then bf16), directly
-// into the lane's A registers; the chunk's token rows are staged through LDS, double-buffered.
+// into the lane's A registers; the chunk's token rows stream into a 3-deep LDS ring with direct
+// global-to-LDS loads, two steps ahead of the matrix cores.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "tq_device.h"
 #include "tq_gemv_core.h"
@@ -35,7 +37,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kChunk = 160;           // token rows per chunk (5 tiles of 32)
-constexpr int kRowStride = 272;       // LDS bytes per token row: 128 bf16 + 16 bytes of padding
+constexpr int kRowStride = 256;       // LDS bytes per token row: 128 bf16 of one step
 constexpr int kBufBytes = kChunk * kRowStride;
 
 // ---- x -> bf16 ----------------------------------------------------------------------------------
@@ -139,20 +141,27 @@ __device__ __forceinline__ GroupScale group_scale(const RawRow &r, int c, float 
   return GroupScale{d * sc_lo, -(dmin * m_lo), d * sc_hi, -(dmin * m_hi)};
 }
 
-// The 8 weights of k step s (quant dword s of the lane's group) as one bf16x8 A operand.
-__device__ __forceinline__ bf16x8 dequant_step(const RawRow &r, const GroupScale &g, int s) {
-  const uint32_t wq = dword_of(s < 4 ? r.q0 : r.q1, s & 3);
-  const uint32_t lo = wq & 0x0F0F0F0Fu, hi = (wq >> 4) & 0x0F0F0F0Fu;
-  float f[8];
-  nibbles_to_float<false>(lo, f[0], f[1]);
-  nibbles_to_float<true>(lo, f[2], f[3]);
-  nibbles_to_float<false>(hi, f[4], f[5]);
-  nibbles_to_float<true>(hi, f[6], f[7]);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    f[e] = __builtin_fmaf(g.al, f[e], g.bl);
-    f[4 + e] = __builtin_fmaf(g.ah, f[4 + e], g.bh);
+// The 8 weights of k step s as one bf16x8 A operand: k = 64c + 8s + 0..7 of the lane's group c,
+// the low nibbles of quant bytes 8s .. 8s+7 for s < 4 (sub-block 2c), the high nibbles of
+// bytes 8(s-4) .. for s >= 4 (sub-block 2c+1).
+template <int S>
+__device__ __forceinline__ bf16x8 dequant_step(const RawRow &r, const GroupScale &g) {
+  const u32x4 &q = (S & 3) < 2 ? r.q0 : r.q1;
+  uint32_t w0 = dword_of(q, (2 * S) & 3), w1 = dword_of(q, (2 * S + 1) & 3);
+  if (S >= 4) {
+    w0 >>= 4;
+    w1 >>= 4;
   }
+  w0 &= 0x0F0F0F0Fu;
+  w1 &= 0x0F0F0F0Fu;
+  float f[8];
+  nibbles_to_float<false>(w0, f[0], f[1]);
+  nibbles_to_float<true>(w0, f[2], f[3]);
+  nibbles_to_float<false>(w1, f[4], f[5]);
+  nibbles_to_float<true>(w1, f[6], f[7]);
+  const float a = S < 4 ? g.al : g.ah, b = S < 4 ? g.bl : g.bh;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = __builtin_fmaf(a, f[e], b);
   u32x4 v;
   v.x = pack_bf16(f[0], f[1]);
   v.y = pack_bf16(f[2], f[3]);
@@ -161,26 +170,70 @@ __device__ __forceinline__ bf16x8 dequant_step(const RawRow &r, const GroupScale
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// s_waitcnt that waits until at most n vector-memory operations of this wave are outstanding
+// (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Byte address of a __shared__ location in the LDS aperture.
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// 16 bytes from global memory straight into LDS: lane l's bytes land at lds_base + 16 l
+// (lds_base must be the same for the whole wave).
+__device__ __forceinline__ void load_lds16(const void *g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// Workgroup barrier once at most N vector-memory operations and no LDS operation of this wave
+// are outstanding. Written as one asm statement with a memory clobber: the compiler keeps memory
+// accesses on their side of it and adds no waits of its own.
+template <int N>
+__device__ __forceinline__ void barrier_after_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "i"(N) : "memory");
+}
+
 __device__ __forceinline__ float silu_mul(float g, float u) { return g * u / (1.f + expf(-g)); }
 
-// Token staging. Thread tid copies the 16 bytes at k offset 8*(tid % 16) of the step's 128 k
-// for rows tid/16 + 16 i (i < 2 NT), clamped to the chunk's last row: rows past the chunk only
-// feed token columns that are never stored. In LDS the 8 k of that piece go to two entries:
-// k-half kg = pc/8, steps s and s+1 (s = 2 (pc % 4)), low-nibble half (bytes 0..7 of the
-// 16-byte entry) for pc % 8 < 4, else the high half.
+// Token staging. A step's token tile (rows of 128 bf16: 16 pieces of 8 k) goes straight from
+// global memory to LDS (global_load_lds, 16 bytes per lane: lane l of a wave instruction writes
+// bytes 16 l of a 1 KB run = 4 rows). Piece pc of row t is stored at position pc ^ (t % 16) of the
+// row, so the 32 lanes of a B-operand read (32 rows, one piece) spread over all banks. Wave w's
+// instruction i fills rows 16 i + 4 w .. +3; rows past the chunk are filled from its last row and
+// only feed token columns that are never stored.
 template <bool GU, int NT>
-__device__ __forceinline__ void prefill_tiles(const PrefillArgs &a, uint8_t (*tok)[kBufBytes],
-                                              const int64_t *rowoff, int rows, int p0,
-                                              const uint8_t *const (&wrow)[2], int col0) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void prefill_tiles(const PrefillArgs &a, uint8_t *__restrict__ tok0,
+                                              uint8_t *__restrict__ tok1,
+                                              uint8_t *__restrict__ tok2, const int64_t *rowoff,
+                                              int rows, int p0, const uint8_t *const (&wrow)[2],
+                                              int col0) {
+  const int lane = threadIdx.x & 63, wave = wave_index();
   const int lrow = lane & 31, kg = lane >> 5;
-  const int pc = threadIdx.x & 15, trow = threadIdx.x >> 4;
   const uint16_t *src[2 * NT];
 #pragma unroll
-  for (int i = 0; i < 2 * NT; ++i)
-    src[i] = a.xsrc + rowoff[min(trow + 16 * i, rows - 1)] + 8 * pc;
-  const int dst = (trow * kRowStride) + ((pc >> 3) * 8 + 2 * (pc & 3)) * 16 + 8 * ((pc >> 2) & 1);
-  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  for (int i = 0; i < 2 * NT; ++i) {
+    const int t = 16 * i + 4 * wave + (lane >> 4);
+    const int pc = (lane & 15) ^ (t & 15);
+    src[i] = a.xsrc + rowoff[min(t, rows - 1)] + 8 * pc;
+  }
+  // enqueue the token tile of step st into tok. The loads are written as asm so that the
+  // compiler does not track them: it cannot tell the three token buffers apart and would
+  // otherwise wait for these loads before every LDS read. Their completion is awaited
+  // explicitly (barrier_after_vmem) before the step that reads them.
+  auto stage = [&](uint8_t *tok, int st) {
+    const uint32_t b = __builtin_amdgcn_readfirstlane(lds_address(tok + 4 * wave * kRowStride));
+#pragma unroll
+    for (int i = 0; i < 2 * NT; ++i)
+      load_lds16(src[i] + 128 * st, b + 16 * i * kRowStride);
+  };
 
   const float unit_inv = 1.f / nibble_fp8_unit();
   f32x16 acc[NT][2];
@@ -192,56 +245,66 @@ __device__ __forceinline__ void prefill_tiles(const PrefillArgs &a, uint8_t (*to
       for (int j = 0; j < 16; ++j) acc[t][r][j] = 0.f;
 
   const int steps = 2 * a.kblocks;
-  RawRow raw[2];
+  // Weights and tokens both run two steps ahead: raw[j] holds the weights of the steps st with
+  // st % 3 == j, tok_j their tokens.
+  RawRow raw[3][2];
+  auto load_w = [&](RawRow (&r)[2], int st) {
 #pragma unroll
-  for (int r = 0; r < 2; ++r) load_raw(wrow[r], 0, kg, raw[r]);
-  u32x4 tv[2 * NT];
-#pragma unroll
-  for (int i = 0; i < 2 * NT; ++i) tv[i] = gload(src[i]);
-#pragma unroll
-  for (int i = 0; i < 2 * NT; ++i) {
-    uint8_t *d = tok[0] + dst + 16 * i * kRowStride;
-    *reinterpret_cast<u32x2 *>(d) = (u32x2){tv[i].x, tv[i].y};
-    *reinterpret_cast<u32x2 *>(d + 16) = (u32x2){tv[i].z, tv[i].w};
-  }
-  __syncthreads();
+    for (int q = 0; q < 2; ++q) load_raw(wrow[q], st >> 1, 2 * (st & 1) + kg, r[q]);
+  };
+  load_w(raw[0], 0);
+  stage(tok0, 0);
+  load_w(raw[1], min(1, steps - 1));
+  stage(tok1, min(1, steps - 1));
+  // B-operand read of tile t, step s: row 32 t + lrow, piece 8 kg + s
+  const int rd = lrow * kRowStride;
+  const int sw = lrow & 15;
 
-  for (int st = 0; st < steps; ++st) {
+  // one step: weights of st in `rc`, tokens in `cur_buf`; those of st+2 go to `rf` and `fill`
+  auto step = [&](int st, const uint8_t *cur_buf, uint8_t *fill, const RawRow (&rc)[2],
+                  RawRow (&rf)[2]) {
+    // Outstanding, oldest first: weights and tokens of st, then of st+1. Every step issues the
+    // same loads (past the last step they repeat the last block / tile into registers and a
+    // buffer nobody reads), so this count is exact on every path.
+    // Then a plain barrier (__syncthreads would add a release fence, i.e. a wait for every load
+    // in flight, the two steps ahead included): after it every wave's tokens of step st are in
+    // LDS and every wave has finished reading `fill` (its tiles of step st-1).
+    barrier_after_vmem<6 + 2 * NT>();
     const int c = 2 * (st & 1) + kg;  // the lane's group in block st/2
-    const RawRow cur[2] = {raw[0], raw[1]};
-    const bool more = st + 1 < steps;
-    if (more) {
-      const int nst = st + 1;
-#pragma unroll
-      for (int r = 0; r < 2; ++r) load_raw(wrow[r], nst >> 1, 2 * (nst & 1) + kg, raw[r]);
-#pragma unroll
-      for (int i = 0; i < 2 * NT; ++i) tv[i] = gload(src[i] + 128 * nst);
-    }
+    const RawRow (&cur)[2] = rc;
     const GroupScale gs[2] = {group_scale(cur[0], c, unit_inv), group_scale(cur[1], c, unit_inv)};
-    const uint8_t *buf = tok[st & 1] + lrow * kRowStride + kg * 128;
+    const uint8_t *buf = cur_buf + rd;
     // Software pipeline over the 8 k steps: while the matrix cores work on step s, the lanes
     // dequantize the A operands of step s+1 and read its B operands from LDS.
-    bf16x8 a0 = dequant_step(cur[0], gs[0], 0), a1 = dequant_step(cur[1], gs[1], 0);
     bf16x8 bv[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
-      bv[t] = *reinterpret_cast<const bf16x8 *>(buf + 32 * t * kRowStride);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
+      bv[t] = *reinterpret_cast<const bf16x8 *>(buf + 32 * t * kRowStride + 16 * ((8 * kg) ^ sw));
+    __builtin_amdgcn_sched_barrier(0);
+    // The loads of step st+2, issued after the first LDS reads of this step: where the compiler
+    // cannot tell the token buffers apart it waits for all earlier loads before those reads,
+    // and this way that wait never covers the loads just issued.
+    load_w(rf, min(st + 2, steps - 1));
+    stage(fill, min(st + 2, steps - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 a0 = dequant_step<0>(cur[0], gs[0]), a1 = dequant_step<0>(cur[1], gs[1]);
+    auto kstep = [&](auto S_) {
+      constexpr int S = decltype(S_)::value;
       bf16x8 n0, n1, nb[NT];
-      if (s < 7) {
+      if constexpr (S < 7) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-          nb[t] = *reinterpret_cast<const bf16x8 *>(buf + 32 * t * kRowStride + 16 * (s + 1));
-        n0 = dequant_step(cur[0], gs[0], s + 1);
-        n1 = dequant_step(cur[1], gs[1], s + 1);
+          nb[t] = *reinterpret_cast<const bf16x8 *>(buf + 32 * t * kRowStride +
+                                                    16 * ((8 * kg + S + 1) ^ sw));
+        n0 = dequant_step<S + 1>(cur[0], gs[0]);
+        n1 = dequant_step<S + 1>(cur[1], gs[1]);
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         acc[t][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bv[t], acc[t][0], 0, 0, 0);
         acc[t][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bv[t], acc[t][1], 0, 0, 0);
       }
-      if (s < 7) {
+      if constexpr (S < 7) {
         // issue order: the LDS reads, then each MFMA followed by a share of the VALU work
         __builtin_amdgcn_sched_group_barrier(0x100, NT, 0);
 #pragma unroll
@@ -254,20 +317,32 @@ __device__ __forceinline__ void prefill_tiles(const PrefillArgs &a, uint8_t (*to
 #pragma unroll
         for (int t = 0; t < NT; ++t) bv[t] = nb[t];
       }
-    }
-    if (more) {
-      uint8_t *nb = tok[(st + 1) & 1] + dst;
-#pragma unroll
-      for (int i = 0; i < 2 * NT; ++i) {
-        uint8_t *d = nb + 16 * i * kRowStride;
-        *reinterpret_cast<u32x2 *>(d) = (u32x2){tv[i].x, tv[i].y};
-        *reinterpret_cast<u32x2 *>(d + 16) = (u32x2){tv[i].z, tv[i].w};
-      }
-    }
-    __syncthreads();
+    };
+    kstep(std::integral_constant<int, 0>{});
+    kstep(std::integral_constant<int, 1>{});
+    kstep(std::integral_constant<int, 2>{});
+    kstep(std::integral_constant<int, 3>{});
+    kstep(std::integral_constant<int, 4>{});
+    kstep(std::integral_constant<int, 5>{});
+    kstep(std::integral_constant<int, 6>{});
+    kstep(std::integral_constant<int, 7>{});
+  };
+  // three steps per trip so that each step's buffers are distinct LDS objects: the compiler then
+  // knows the reads of step st do not touch the tiles still landing for st+1 and st+2
+  // (whole trips in the loop, the 0..2 remaining steps after it: every path into a step then
+  // has the same loads in flight, which keeps the compiler's own wait counts exact)
+  int st = 0;
+  for (; st + 3 <= steps; st += 3) {
+    step(st, tok0, tok2, raw[0], raw[2]);
+    step(st + 1, tok1, tok0, raw[1], raw[0]);
+    step(st + 2, tok2, tok1, raw[2], raw[1]);
   }
+  if (st < steps) step(st, tok0, tok2, raw[0], raw[2]);
+  if (st + 1 < steps) step(st + 1, tok1, tok0, raw[1], raw[0]);
+  wait_vmem<0>();  // the surplus loads of the last steps land before the workgroup ends
 
   // epilogue: lane holds rows 8*(i/4) + 4*kg + i%4 of token column lrow of each tile
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int tr = 32 * t + lrow;
@@ -299,7 +374,9 @@ __device__ __forceinline__ void prefill_tiles(const PrefillArgs &a, uint8_t (*to
 
 template <bool GU>
 __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t tok[2][kBufBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t tok0[kBufBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t tok1[kBufBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t tok2[kBufBytes];
   __shared__ int64_t rowoff[kChunk];
 
   // blockIdx -> (chunk, tile): workgroups are dealt to the 8 XCDs round-robin; XCD x takes the
@@ -334,11 +411,11 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
   }
   __syncthreads();  // rowoff
   switch ((rows + 31) >> 5) {
-    case 1: prefill_tiles<GU, 1>(a, tok, rowoff, rows, p0, wrow, col0); break;
-    case 2: prefill_tiles<GU, 2>(a, tok, rowoff, rows, p0, wrow, col0); break;
-    case 3: prefill_tiles<GU, 3>(a, tok, rowoff, rows, p0, wrow, col0); break;
-    case 4: prefill_tiles<GU, 4>(a, tok, rowoff, rows, p0, wrow, col0); break;
-    default: prefill_tiles<GU, 5>(a, tok, rowoff, rows, p0, wrow, col0); break;
+    case 1: prefill_tiles<GU, 1>(a, tok0, tok1, tok2, rowoff, rows, p0, wrow, col0); break;
+    case 2: prefill_tiles<GU, 2>(a, tok0, tok1, tok2, rowoff, rows, p0, wrow, col0); break;
+    case 3: prefill_tiles<GU, 3>(a, tok0, tok1, tok2, rowoff, rows, p0, wrow, col0); break;
+    case 4: prefill_tiles<GU, 4>(a, tok0, tok1, tok2, rowoff, rows, p0, wrow, col0); break;
+    default: prefill_tiles<GU, 5>(a, tok0, tok1, tok2, rowoff, rows, p0, wrow, col0); break;
   }
 }
 
