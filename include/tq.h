@@ -120,7 +120,8 @@ typedef struct {
   const float *router_w;         /* device [n_experts][hidden] fp32, 16-byte aligned */
   const tq_expert *experts;      /* device array [n_experts] of device blob pointers */
   const tq_expert *experts_host; /* host array [n_experts] of pinned host blob pointers; used
-                                    instead of `experts` when experts_on_host is set */
+                                    instead of `experts` (which may then be NULL) when
+                                    experts_on_host is set */
   tq_expert shared;              /* device blobs of the shared expert; gate == NULL: none */
   int renormalize;               /* 1: weights renormalised over the selected experts */
   int experts_on_host;           /* 1: routed experts live in pinned host memory and are copied
@@ -147,9 +148,15 @@ size_t tq_moe_workspace_bytes(const tq_moe_desc *desc, int64_t tokens);
  * tq_moe_workspace_bytes(desc, tokens) bytes, 256-byte aligned, contents irrelevant; one call at a
  * time per workspace. routing_out: NULL or copies of the routing (each field may be NULL).
  * 1 <= tokens <= 8192. Everything is enqueued on `stream` without host synchronisation, except
- * with experts_on_host: the selected expert ids are then copied to the host (one synchronisation
- * of `stream`) and each selected expert is copied from pinned host memory to the workspace with
- * hipMemcpyAsync on copy_stream, the expert kernels waiting on an event per copy.
+ * with experts_on_host (routed experts kept in host memory, the pages' offload setting): the
+ * active-expert list is then copied to the host (one synchronisation of `stream`, so such calls
+ * cannot be captured into a graph) and each selected expert is copied from pinned host memory
+ * into the workspace with hipMemcpyAsync on copy_stream (NULL: on `stream`), each followed by an
+ * event. The shared expert (always on the device) runs first; on the fp32 path each routed
+ * expert's kernels wait only for their own copy, on the matrix-core path one grouped launch
+ * waits for all copies. Host blobs must stay valid until the call's work has completed; they
+ * must be pinned (hipHostMalloc) for the copies to be asynchronous. The output is bitwise
+ * identical to the device-resident call's.
  * Deterministic: the same inputs give bitwise-identical outputs and routing.
  */
 int tq_moe_ffn(const tq_moe_desc *desc, const float *x, int64_t tokens, float *y,

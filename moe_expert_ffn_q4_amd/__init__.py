@@ -171,28 +171,41 @@ def swiglu(g: torch.Tensor, u: torch.Tensor, out=None, stream=None):
 
 
 class MoeLayer:
-    """Device-resident MoE layer for tq_moe_ffn: router weights, the device table of expert blob
-    pointers, and an optional shared expert. Blobs are torch uint8 tensors (kept alive here)."""
+    """MoE layer for tq_moe_ffn: router weights, the expert blobs and an optional shared expert.
+    Blobs are torch uint8 tensors (kept alive here). Routed experts on the device (a device
+    table of blob pointers), or, when they are CPU tensors, in pinned host memory (the
+    host-resident variant: the selected experts are copied per call on `copy_stream`, a
+    torch.cuda.Stream, or on the call's stream when None). The shared expert is always on the
+    device."""
 
     def __init__(self, t, hidden: int, ffn: int, router_w: torch.Tensor, experts, shared=None,
-                 top_k: int = 2, renormalize: bool = True, path: int = PATH_AUTO):
+                 top_k: int = 2, renormalize: bool = True, path: int = PATH_AUTO,
+                 copy_stream=None):
         self.blobs = [b for e in experts for b in e] + (list(shared) if shared else [])
         self.router_w = router_w
         E = len(experts)
-        table = torch.tensor([[b.data_ptr() for b in e] for e in experts], dtype=torch.int64)
-        self.table = table.to(router_w.device)
+        on_host = experts[0][0].device.type == "cpu"
+        if on_host and not all(b.is_pinned() for e in experts for b in e):
+            raise ValueError("host-resident expert blobs must be pinned (pin_memory=True)")
+        self.copy_stream = copy_stream
+        if on_host:
+            self.host_table = (Expert * E)(*[Expert(*[b.data_ptr() for b in e]) for e in experts])
+            self.table = None
+        else:
+            table = torch.tensor([[b.data_ptr() for b in e] for e in experts], dtype=torch.int64)
+            self.table = table.to(router_w.device)
         self.desc = MoeDesc()
         self.desc.type = _type(t)
         self.desc.hidden, self.desc.ffn = hidden, ffn
         self.desc.n_experts, self.desc.top_k = E, top_k
         self.desc.router_w = router_w.data_ptr()
-        self.desc.experts = self.table.data_ptr()
-        self.desc.experts_host = None
+        self.desc.experts = None if on_host else self.table.data_ptr()
+        self.desc.experts_host = C.addressof(self.host_table) if on_host else None
         if shared:
             self.desc.shared = Expert(*[b.data_ptr() for b in shared])
         self.desc.renormalize = int(renormalize)
-        self.desc.experts_on_host = 0
-        self.desc.copy_stream = None
+        self.desc.experts_on_host = int(on_host)
+        self.desc.copy_stream = copy_stream.cuda_stream if copy_stream is not None else None
         self.desc.path = path
 
     def workspace_bytes(self, tokens: int) -> int:

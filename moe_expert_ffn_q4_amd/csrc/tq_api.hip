@@ -2,6 +2,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <vector>
+
 #include "tq.h"
 #include "tq_launch.h"
 #include "tq_moe.h"
@@ -141,6 +143,127 @@ size_t tq_moe_workspace_bytes(const tq_moe_desc *desc, int64_t tokens) {
   return (size_t)tq::plan_moe(s).bytes;
 }
 
+static bool host_experts_ok(const tq_moe_desc *d) {
+  for (int64_t e = 0; e < d->n_experts; ++e) {
+    const tq_expert &x = d->experts_host[e];
+    if (!x.gate || !x.up || !x.down) return false;
+  }
+  return true;
+}
+
+// Per-thread resources of the host-resident path: a pinned buffer for the active-expert list and
+// events (one per staged expert, one for "the compute stream is done with the staging area").
+struct HostPathState {
+  int device = -1;
+  int *list = nullptr;
+  size_t list_ints = 0;
+  std::vector<hipEvent_t> copied;
+  hipEvent_t ready = nullptr;
+};
+
+static int host_path_state(int64_t list_ints, int n_events, HostPathState *&out) {
+  static thread_local HostPathState hs;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(TQ_EDEVICE, "tq_moe_ffn: no current device");
+  if (hs.device != dev) {  // resources belong to one device; start over on another
+    for (hipEvent_t e : hs.copied) (void)hipEventDestroy(e);
+    hs.copied.clear();
+    if (hs.ready) (void)hipEventDestroy(hs.ready);
+    hs.ready = nullptr;
+    if (hs.list) (void)hipHostFree(hs.list);
+    hs.list = nullptr;
+    hs.list_ints = 0;
+    hs.device = dev;
+  }
+  if (hs.list_ints < (size_t)list_ints) {
+    if (hs.list) (void)hipHostFree(hs.list);
+    hs.list = nullptr;
+    hs.list_ints = 0;
+    if (hipHostMalloc((void **)&hs.list, (size_t)list_ints * 4, hipHostMallocDefault) != hipSuccess)
+      return fail(TQ_EDEVICE, "tq_moe_ffn: pinned host allocation failed");
+    hs.list_ints = (size_t)list_ints;
+  }
+  if (!hs.ready && hipEventCreateWithFlags(&hs.ready, hipEventDisableTiming) != hipSuccess)
+    return fail(TQ_EDEVICE, "tq_moe_ffn: event creation failed");
+  while ((int)hs.copied.size() < n_events) {
+    hipEvent_t e;
+    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
+      return fail(TQ_EDEVICE, "tq_moe_ffn: event creation failed");
+    hs.copied.push_back(e);
+  }
+  out = &hs;
+  return TQ_OK;
+}
+
+// Expert products with the routed experts in pinned host memory. The active-expert list is read
+// back (one synchronisation of `st`); each selected expert is then copied into its staging slot
+// on the copy stream, followed by an event. On the fp32 path the shared expert (resident) runs
+// first and every routed expert's kernels wait only for their own copy, so copies and compute
+// overlap; the matrix-core path waits for all copies and runs one grouped launch.
+static int host_resident_experts(const tq_moe_desc *d, const tq::MoePlan &p,
+                                 const tq::MoeExpertPtrs &shared, const float *x, char *ws,
+                                 hipStream_t st) {
+  const tq::MoeShape &s = p.s;
+  const int E = (int)s.n_experts;
+  const int64_t list_ints = 3 * (E + 1) + 1;
+  HostPathState *hs = nullptr;
+  int rc = host_path_state(list_ints, p.max_active, hs);
+  if (rc != TQ_OK) return rc;
+  int *act = hs->list, *n_active = hs->list + 3 * (E + 1);
+  if (hipMemcpyAsync(act, ws + p.off_act, (size_t)(3 * (E + 1)) * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipMemcpyAsync(n_active, ws + p.off_nact, 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return fail(TQ_EDEVICE, "tq_moe_ffn: reading the active-expert list back failed");
+  const int na = *n_active;
+  if (na < 0 || na > p.max_active) return fail(TQ_EDEVICE, "tq_moe_ffn: corrupt active-expert list");
+  hipStream_t cs = d->copy_stream ? (hipStream_t)d->copy_stream : st;
+  uint8_t *staging = (uint8_t *)(ws + p.off_stage);
+  // the staging area is free once the compute stream's earlier work (a previous call) is done
+  if (hipEventRecord(hs->ready, st) != hipSuccess || hipStreamWaitEvent(cs, hs->ready, 0) != hipSuccess)
+    return fail(TQ_EDEVICE, "tq_moe_ffn: event record / wait failed");
+  const int64_t bytes[3] = {s.gate_bytes, s.gate_bytes, s.expert_bytes - 2 * s.gate_bytes};
+  const int64_t off[3] = {0, s.gate_bytes, 2 * s.gate_bytes};
+  int last_copied = -1;
+  for (int a = 0; a < na; ++a) {
+    const int e = act[a];
+    if (e == E) continue;  // the shared expert stays on the device
+    const tq_expert &hx = d->experts_host[e];
+    const void *src[3] = {hx.gate, hx.up, hx.down};
+    for (int m = 0; m < 3; ++m)
+      if (hipMemcpyAsync(staging + (int64_t)a * p.stage_stride + off[m], src[m], (size_t)bytes[m],
+                         hipMemcpyHostToDevice, cs) != hipSuccess)
+        return fail(TQ_EDEVICE, "tq_moe_ffn: expert copy failed");
+    if (hipEventRecord(hs->copied[a], cs) != hipSuccess)
+      return fail(TQ_EDEVICE, "tq_moe_ffn: event record failed");
+    last_copied = a;
+  }
+  const auto *dev_table = reinterpret_cast<const tq::MoeExpertPtrs *>(d->experts);
+  if (s.mfma) {
+    if (last_copied >= 0 && hipStreamWaitEvent(st, hs->copied[last_copied], 0) != hipSuccess)
+      return fail(TQ_EDEVICE, "tq_moe_ffn: event wait failed");
+    return launched(tq::launch_moe_experts(p, dev_table, shared, staging, x, ws, st),
+                    "tq_moe_ffn experts");
+  }
+  auto slot_range = [&](int a) {
+    return tq::SlotRange{a, 1, act[(E + 1) + a], act[2 * (E + 1) + a]};
+  };
+  for (int a = 0; a < na; ++a)  // the shared expert first: it needs no copy
+    if (act[a] == E) {
+      const tq::SlotRange r = slot_range(a);
+      rc = tq::launch_moe_experts(p, dev_table, shared, staging, x, ws, st, &r);
+      if (rc) return launched(rc, "tq_moe_ffn experts");
+    }
+  for (int a = 0; a < na; ++a) {
+    if (act[a] == E) continue;
+    if (hipStreamWaitEvent(st, hs->copied[a], 0) != hipSuccess)
+      return fail(TQ_EDEVICE, "tq_moe_ffn: event wait failed");
+    const tq::SlotRange r = slot_range(a);
+    rc = tq::launch_moe_experts(p, dev_table, shared, staging, x, ws, st, &r);
+    if (rc) return launched(rc, "tq_moe_ffn experts");
+  }
+  return TQ_OK;
+}
+
 int tq_moe_ffn_stages(const tq_moe_desc *d, const float *x, int64_t tokens, float *y,
                       void *workspace, size_t ws_bytes, tq_moe_routing *routing_out, int stages,
                       void *stream) {
@@ -156,7 +279,8 @@ int tq_moe_ffn_stages(const tq_moe_desc *d, const float *x, int64_t tokens, floa
   const tq::MoePlan p = tq::plan_moe(s);
   if (ws_bytes < (size_t)p.bytes)
     return fail(TQ_ENOSPC, "tq_moe_ffn: workspace of %zu bytes, %lld needed", ws_bytes, (long long)p.bytes);
-  if (s.experts_on_host) return fail(TQ_EUNSUPPORTED, "tq_moe_ffn: host-resident experts not built yet");
+  if (s.experts_on_host && (stages & TQ_MOE_EXPERTS) && !host_experts_ok(d))
+    return fail(TQ_EINVAL, "tq_moe_ffn: experts_host entries must all be non-null");
   hipStream_t st = (hipStream_t)stream;
   char *ws = (char *)workspace;
   if (stages & TQ_MOE_ROUTE) {
@@ -174,9 +298,14 @@ int tq_moe_ffn_stages(const tq_moe_desc *d, const float *x, int64_t tokens, floa
   }
   if (stages & TQ_MOE_EXPERTS) {
     tq::MoeExpertPtrs shared{{d->shared.gate, d->shared.up, d->shared.down}};
-    rc = tq::launch_moe_experts(p, reinterpret_cast<const tq::MoeExpertPtrs *>(d->experts), shared,
-                                nullptr, x, ws, st);
-    if (rc) return launched(rc, "tq_moe_ffn experts");
+    if (s.experts_on_host) {
+      rc = host_resident_experts(d, p, shared, x, ws, st);
+      if (rc != TQ_OK) return rc;
+    } else {
+      rc = tq::launch_moe_experts(p, reinterpret_cast<const tq::MoeExpertPtrs *>(d->experts),
+                                  shared, nullptr, x, ws, st);
+      if (rc) return launched(rc, "tq_moe_ffn experts");
+    }
   }
   if (stages & TQ_MOE_COMBINE) {
     if (tq::launch_moe_combine(p, ws, y, st)) return launched(-1, "tq_moe_ffn combine");

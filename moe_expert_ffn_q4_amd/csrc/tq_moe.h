@@ -38,10 +38,19 @@ MoePlan plan_moe(const MoeShape &s);
 size_t group_lds_bytes(int64_t T, int64_t E);
 int launch_moe_routing(const MoePlan &p, const float *router_w, const float *x, char *ws,
                        hipStream_t st);
-// Expert products of the routed pairs into the per-position outputs in the workspace.
+// A subset of the active-expert list: slots slot0 .. slot0+nslots-1, whose pairs occupy positions
+// pos0 .. pos0+npos-1 (the host knows both once it has read the list back).
+struct SlotRange {
+  int slot0, nslots;
+  int64_t pos0, npos;
+};
+
+// Expert products of the routed pairs into the per-position outputs in the workspace: every
+// active expert (range == nullptr) or the slots of `range`. staging != nullptr: routed expert
+// blobs are read from the workspace's staging area, slot a at staging + a * stage_stride.
 int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
                        const MoeExpertPtrs &shared, const uint8_t *staging, const float *x,
-                       char *ws, hipStream_t st);
+                       char *ws, hipStream_t st, const SlotRange *range = nullptr);
 // y[t] = the routing-weighted sum of the per-position outputs (plus the shared expert's).
 int launch_moe_combine(const MoePlan &p, char *ws, float *y, hipStream_t st);
 

@@ -260,6 +260,7 @@ struct MoeGemvArgs {
   const int *act;
   const int *n_active;
   const int *pairs;
+  int slot0;                     // first active slot of this launch
   int E, topk, Tk;
   int mat0, nmat;                // matrices m = mat0 .. mat0 + nmat - 1 (0 gate, 1 up, 2 down)
   int n_rows, units;             // rows of each matrix, units of 256 weights along k
@@ -298,9 +299,9 @@ template <int FMT>
 __global__ __launch_bounds__(512) void k_moe_gemv(MoeGemvArgs a) {
   extern __shared__ float lds[];
   const int per_slot = a.nmat * a.rowgroups * a.ksplit;
-  const int slot = blockIdx.x / per_slot;
+  const int slot = a.slot0 + (int)blockIdx.x / per_slot;
   if (slot >= *a.n_active) return;
-  int r = blockIdx.x - slot * per_slot;
+  int r = (int)blockIdx.x - (slot - a.slot0) * per_slot;
   const int mi = r / (a.rowgroups * a.ksplit);
   r -= mi * a.rowgroups * a.ksplit;
   const int rg = r / a.ksplit, ks = r - rg * a.ksplit;
@@ -332,10 +333,11 @@ __global__ __launch_bounds__(512) void k_moe_gemv(MoeGemvArgs a) {
 // ---- SwiGLU over the gate/up slices and the combine ---------------------------------------------
 
 __global__ __launch_bounds__(256) void k_moe_swiglu(const float *__restrict__ gu, int ksplit,
-                                                    int64_t P, int F, float *__restrict__ h) {
-  const int64_t total = P * F, stride = (int64_t)gridDim.x * blockDim.x;
+                                                    int64_t P, int F, int64_t pos0, int64_t npos,
+                                                    float *__restrict__ h) {
+  const int64_t end = (pos0 + npos) * F, stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t slice = P * F;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+  for (int64_t i = pos0 * F + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < end; i += stride) {
     float g = 0.f, u = 0.f;
     for (int q = 0; q < ksplit; ++q) {
       g += gu[(int64_t)q * slice + i];
@@ -442,20 +444,20 @@ MoePlan plan_moe(const MoeShape &s) {
 }
 
 template <int FMT>
-static int moe_gemv_launch(MoeGemvArgs a, int max_active, int waves, hipStream_t st) {
-  const int grid = max_active * a.nmat * a.rowgroups * a.ksplit;
+static int moe_gemv_launch(MoeGemvArgs a, int nslots, int waves, hipStream_t st) {
+  const int grid = nslots * a.nmat * a.rowgroups * a.ksplit;
   const size_t lds = (size_t)4 * gemv_tile_lds_floats<FMT>(8, a.upk, waves);
   if (lds > 65536) return -2;
   hipLaunchKernelGGL(k_moe_gemv<FMT>, dim3((unsigned)grid), dim3(64 * waves), lds, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-static int moe_gemv_dispatch(int fmt, const MoeGemvArgs &a, int max_active, int waves,
+static int moe_gemv_dispatch(int fmt, const MoeGemvArgs &a, int nslots, int waves,
                              hipStream_t st) {
   switch (fmt) {
-    case FMT_Q4_K: return moe_gemv_launch<FMT_Q4_K>(a, max_active, waves, st);
-    case FMT_Q6_K: return moe_gemv_launch<FMT_Q6_K>(a, max_active, waves, st);
-    default: return moe_gemv_launch<FMT_Q8_0>(a, max_active, waves, st);
+    case FMT_Q4_K: return moe_gemv_launch<FMT_Q4_K>(a, nslots, waves, st);
+    case FMT_Q6_K: return moe_gemv_launch<FMT_Q6_K>(a, nslots, waves, st);
+    default: return moe_gemv_launch<FMT_Q8_0>(a, nslots, waves, st);
   }
 }
 
@@ -492,7 +494,7 @@ int launch_moe_combine(const MoePlan &p, char *ws, float *y, hipStream_t st) {
 
 int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
                        const MoeExpertPtrs &shared, const uint8_t *staging, const float *x,
-                       char *ws, hipStream_t st) {
+                       char *ws, hipStream_t st, const SlotRange *range) {
   const MoeShape &s = p.s;
   const int E = (int)s.n_experts, T = (int)s.tokens, k = (int)s.top_k;
   MoeGemvArgs a{};
@@ -506,6 +508,9 @@ int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
   a.act = (const int *)(ws + p.off_act);
   a.n_active = (const int *)(ws + p.off_nact);
   a.pairs = (const int *)(ws + p.off_pairs);
+  a.slot0 = range ? range->slot0 : 0;
+  const int nslots = range ? range->nslots : p.max_active;
+  const int64_t pos0 = range ? range->pos0 : 0, npos = range ? range->npos : p.P;
   a.E = E;
   a.topk = k;
   a.Tk = T * k;
@@ -522,6 +527,9 @@ int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
     b.E = E;
     b.topk = k;
     b.Tk = T * k;
+    b.staging = staging;
+    b.stage_stride = p.stage_stride;
+    for (int m = 0; m < 3; ++m) b.stage_off[m] = a.stage_off[m];
     return launch_prefill(p.max_chunks, b, x, T, s.hidden, s.ffn, (uint16_t *)(ws + p.off_xb),
                           (uint16_t *)(ws + p.off_hb), (float *)(ws + p.off_o), st);
   }
@@ -539,15 +547,16 @@ int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
   a.ldx = s.hidden;
   a.x_by_token = 1;
   a.out = (float *)(ws + p.off_gu);
-  int rc = moe_gemv_dispatch(s.type, a, p.max_active, p.gu_waves, st);
+  int rc = moe_gemv_dispatch(s.type, a, nslots, p.gu_waves, st);
   if (rc) return rc;
   float *h = (float *)(ws + p.off_h);
   {
-    const int64_t total = p.P * s.ffn;
+    const int64_t total = npos * s.ffn;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 16384) blocks = 16384;
+    if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL(k_moe_swiglu, dim3((unsigned)blocks), dim3(256), 0, st, (const float *)a.out,
-                       p.gu_ks, p.P, (int)s.ffn, h);
+                       p.gu_ks, p.P, (int)s.ffn, pos0, npos, h);
   }
   // down
   a.mat0 = 2;
@@ -563,7 +572,7 @@ int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
   a.ldx = s.ffn;
   a.x_by_token = 0;
   a.out = (float *)(ws + p.off_o);
-  return moe_gemv_dispatch(s.type, a, p.max_active, p.d_waves, st);
+  return moe_gemv_dispatch(s.type, a, nslots, p.d_waves, st);
 }
 
 }  // namespace tq

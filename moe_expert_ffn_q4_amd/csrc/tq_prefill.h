@@ -11,6 +11,9 @@ namespace tq {
 struct PrefillArgs {
   const MoeExpertPtrs *experts;  // device table [E]
   MoeExpertPtrs shared;          // by value (id E)
+  const uint8_t *staging;        // non-null: routed expert of slot a at staging + a * stage_stride
+  int64_t stage_stride;
+  int64_t stage_off[3];          // offsets of gate / up / down inside one staged expert
   const int *act, *n_active;     // active expert list of the grouping kernel
   const int *chunks, *n_chunks;  // chunk table (slot, first position, rows)
   const int *pairs;

@@ -387,7 +387,17 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
   if (chunk >= *a.n_chunks) return;
   const int slot = a.chunks[3 * chunk], p0 = a.chunks[3 * chunk + 1], rows = a.chunks[3 * chunk + 2];
   const int e = a.act[slot];
-  const MoeExpertPtrs &ex = e == a.E ? a.shared : a.experts[e];
+  const uint8_t *mat[3];
+  if (e == a.E) {
+#pragma unroll
+    for (int m = 0; m < 3; ++m) mat[m] = (const uint8_t *)a.shared.m[m];
+  } else if (a.staging != nullptr) {
+#pragma unroll
+    for (int m = 0; m < 3; ++m) mat[m] = a.staging + (int64_t)slot * a.stage_stride + a.stage_off[m];
+  } else {
+#pragma unroll
+    for (int m = 0; m < 3; ++m) mat[m] = (const uint8_t *)a.experts[e].m[m];
+  }
 
   for (int t = threadIdx.x; t < rows; t += 256) {
     const int p = p0 + t;
@@ -402,12 +412,12 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
   int col0;  // GU: first ffn column of the wave; down: first hidden row of the wave
   if (GU) {
     col0 = tile * 128 + wave * 32;
-    wrow[0] = (const uint8_t *)ex.m[0] + (int64_t)(col0 + lrow) * a.row_bytes;
-    wrow[1] = (const uint8_t *)ex.m[1] + (int64_t)(col0 + lrow) * a.row_bytes;
+    wrow[0] = mat[0] + (int64_t)(col0 + lrow) * a.row_bytes;
+    wrow[1] = mat[1] + (int64_t)(col0 + lrow) * a.row_bytes;
   } else {
     col0 = tile * 256 + wave * 64;
-    wrow[0] = (const uint8_t *)ex.m[2] + (int64_t)(col0 + lrow) * a.row_bytes;
-    wrow[1] = (const uint8_t *)ex.m[2] + (int64_t)(col0 + 32 + lrow) * a.row_bytes;
+    wrow[0] = mat[2] + (int64_t)(col0 + lrow) * a.row_bytes;
+    wrow[1] = mat[2] + (int64_t)(col0 + 32 + lrow) * a.row_bytes;
   }
   __syncthreads();  // rowoff
   switch ((rows + 31) >> 5) {

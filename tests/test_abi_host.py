@@ -107,3 +107,16 @@ def test_moe_stages_and_path_rejected_before_any_launch():
     d6 = _moe_desc(t=2, hidden=512, ffn=512, E=8, k=2, path=tq.PATH_BF16_MFMA)
     assert L.tq_moe_ffn(C.byref(d6), 0x30000, 4, 0x40000, 0x50000, 1 << 30, None, None) == 5
     assert "Q4_K" in L.tq_last_error().decode()
+
+
+def test_moe_host_resident_rejects_null_host_blob():
+    import ctypes as C
+
+    L = tq.lib()
+    d = _moe_desc(hidden=512, ffn=512, E=2, k=1)
+    table = (tq.Expert * 2)(tq.Expert(0x100000, 0x200000, 0x300000), tq.Expert(0x400000, None, 0x500000))
+    d.experts = None
+    d.experts_host = C.addressof(table)
+    d.experts_on_host = 1
+    assert L.tq_moe_ffn(C.byref(d), 0x30000, 4, 0x40000, 0x50000, 1 << 34, None, None) == 1
+    assert "experts_host" in L.tq_last_error().decode()
