@@ -38,10 +38,12 @@ def _args():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--batch", type=int, default=1, help="tokens per decode step (1 or 8)")
     p.add_argument("--workload", default="llama8b",
-                   choices=["llama8b", "mixtral", "deepseek", "deepseek-prefill"],
+                   choices=["llama8b", "mixtral", "deepseek", "deepseek-prefill", "deepseek-host"],
                    help="llama8b: 32-layer dense decode step (default); mixtral / deepseek: one "
                         "MoE layer at --batch tokens; deepseek-prefill: one DeepSeek-shaped MoE "
-                        "layer over --tokens (default 4096) on the bf16 matrix-core path")
+                        "layer over --tokens (default 4096) on the bf16 matrix-core path; "
+                        "deepseek-host: the DeepSeek decode layer at --batch tokens with the routed "
+                        "experts in pinned host memory, copied per step")
     p.add_argument("--tokens", type=int, default=4096, help="tokens of the prefill workload")
     p.add_argument("--seed", type=int, default=42)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -351,6 +353,68 @@ def moe_bench(args, torch, tq, synth):
     return out
 
 
+def host_bench(args, torch, tq, synth):
+    """DeepSeek-shaped decode layer with the routed experts in pinned host memory: every step
+    reads the selected experts' blobs over PCIe (a host sync on the routing, then per-expert
+    copies on a side stream overlapped with the kernels). Not graph-capturable (host sync), so
+    steps are timed eagerly. Reports the layer rate, the achieved host-to-device rate of the
+    expert copies and that of one plain pinned copy of the same size on the same box."""
+    shape = synth.DEEPSEEK
+    k, T = shape["top_k"], args.batch
+    layer = synth.moe_layer(shape, "q4_k", seed=args.seed, tag="deepseek")
+    pinned = [tuple(torch.from_numpy(b).pin_memory() for b in e) for e in layer["experts"]]
+    shared = tuple(torch.from_numpy(b).cuda() for b in layer["shared"])
+    copy_stream = torch.cuda.Stream()
+    moe = tq.MoeLayer("q4_k", shape["hidden"], shape["ffn"], torch.from_numpy(layer["router"]).cuda(),
+                      pinned, shared, top_k=k, copy_stream=copy_stream)
+    x = torch.from_numpy(synth.normal_f32(synth.rng(args.seed, "bench-x", T), (T, shape["hidden"]))).cuda()
+    y = torch.empty_like(x)
+    ws = torch.empty(moe.workspace_bytes(T), dtype=torch.uint8, device="cuda")
+    counts = torch.empty(shape["n_experts"], dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        moe(x, out=y, ws=ws, routing=dict(counts=counts))
+        for _ in range(args.warmup):
+            moe(x, out=y, ws=ws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            moe(x, out=y, ws=ws)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    c = counts.cpu().numpy()
+    eb = sum(b.numel() for b in pinned[0])
+    routed = int((c > 0).sum())
+    h2d_bytes = routed * eb
+    # one plain pinned host-to-device copy of the same number of bytes
+    src = torch.empty(h2d_bytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(h2d_bytes, dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    plain = h2d_bytes * args.steps / (time.perf_counter() - t1) / 1e9
+    ms = elapsed * 1000 / args.steps
+    achieved = h2d_bytes / (ms / 1000) / 1e9
+    return {
+        "metric": METRIC, "value": round(T * args.steps / elapsed, 2), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "q4_k weights, f32 activations and accumulation",
+        "data": "synthetic (seeded random Q4_K experts in pinned host memory, N(0,1) activations)",
+        "config": {"workload": f"deepseek-shaped MoE layer, top-{k} of {shape['n_experts']} routed "
+                               f"experts in pinned host memory + device-resident shared expert, "
+                               f"{T} tokens", "global_batch": T, "seq_len": 1,
+                   "parallelism": "none (1 GPU)"},
+        "routed_experts_copied": routed,
+        "h2d": {"bytes_per_step": h2d_bytes, "achieved": round(achieved, 2),
+                "plain_pinned_copy": round(plain, 2), "unit": "GB/s",
+                "frac": round(achieved / plain, 4)},
+    }
+
+
 def main():
     args = _args()
     if args.summarize:
@@ -366,6 +430,9 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
+    if args.workload == "deepseek-host":
+        print(json.dumps(host_bench(args, torch, tq, synth)), flush=True)
+        return
     if args.workload != "llama8b":
         print(json.dumps(moe_bench(args, torch, tq, synth)), flush=True)
         return
