@@ -3,7 +3,8 @@
 Default workload: a Llama-3-8B-shaped decode step over 32 layers of Q4_K projections at batch 1
 (per layer q 4096->4096, k/v 4096->1024, o 4096->4096, gate/up 4096->14336, SwiGLU,
 down 14336->4096), seeded synthetic weights and N(0,1) activations resident in HBM.
-One step = every projection of every layer plus the SwiGLU, through the C ABI.
+One step = every projection of every layer plus the SwiGLU, through the C ABI: per layer four
+launches (q|k|v sharing x, o, gate|up with the SwiGLU fused, down).
 
 Prints one JSON line: tokens/s for the whole step, the roofline of the dominant kernel (the
 Q4_K GEMV; achieved = algorithmic bytes / its average launch time measured with HIP events on
@@ -168,8 +169,13 @@ def build_dense_model(tq, synth, torch, batch, seed):
 
 
 def make_step(tq, torch, layers, batch, events=None, gemv_only=False):
-    """One decode step through the C ABI: per layer q, k, v (input x), o (input: the attention
-    stand-in a), gate and up (input x), SwiGLU, down (input: the SwiGLU output)."""
+    """One decode step through the C ABI. Per layer: q, k and v (input x) in one tq_gemv_multi
+    launch, o (input: the attention stand-in a), gate and up (input x) with the SwiGLU between
+    them in one tq_gemv_swiglu launch, down (input: the SwiGLU output). gemv_only: the same
+    products without the SwiGLU (gate and up as a two-matrix tq_gemv_multi), for timing the
+    GEMV kernel alone."""
+    import ctypes as C
+
     H = 4096
     F = 14336
     dev = "cuda"
@@ -178,31 +184,46 @@ def make_step(tq, torch, layers, batch, events=None, gemv_only=False):
                 gate=torch.empty(batch, F, device=dev), up=torch.empty(batch, F, device=dev),
                 h=torch.empty(batch, F, device=dev), down=torch.empty(batch, H, device=dev))
     L = tq.lib()
-    ws_bytes = max(tq.gemv_workspace_bytes("q4_k", n, k, batch)
-                   for n, k in ((4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)))
+    shapes = ((4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336))
+    ws_bytes = max([tq.gemv_workspace_bytes("q4_k", n, k, batch) for n, k in shapes] +
+                   [int(L.tq_gemv_swiglu_workspace_bytes(tq.Q4_K, F, H, batch)),
+                    tq.gemv_workspace_bytes("q4_k", F, H, batch)])
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
 
-    def gemv(name, projs, x):
-        w, n, k = projs[name]
-        stream = torch.cuda.current_stream().cuda_stream
-        rc = L.tq_gemv(tq.Q4_K, w.data_ptr(), n, k, x.data_ptr(), batch, bufs[name].data_ptr(),
-                       ws.data_ptr(), ws.numel(), stream)
+    def check(rc):
         if rc:
             raise tq.TQError(rc, L.tq_last_error().decode())
+
+    def nbytes(names, projs):
+        return sum(projs[m][0].numel() for m in names)
+
+    def multi(names, projs, x):
+        P = len(names)
+        w = (C.c_void_p * P)(*[projs[m][0].data_ptr() for m in names])
+        n = (C.c_int64 * P)(*[projs[m][1] for m in names])
+        y = (C.c_void_p * P)(*[bufs[m].data_ptr() for m in names])
+        k = projs[names[0]][2]
+        stream = torch.cuda.current_stream().cuda_stream
+        check(L.tq_gemv_multi(tq.Q4_K, P, w, n, y, k, x.data_ptr(), batch, ws.data_ptr(),
+                              ws.numel(), stream))
         if events is not None:  # algorithmic bytes of this launch
-            events.append(w.numel() + 4 * batch * (n + k))
+            events.append(nbytes(names, projs) + 4 * batch * (sum(projs[m][1] for m in names) + k))
+
+    def swiglu(projs, x):
+        stream = torch.cuda.current_stream().cuda_stream
+        check(L.tq_gemv_swiglu(tq.Q4_K, projs["gate"][0].data_ptr(), projs["up"][0].data_ptr(), F,
+                               H, x.data_ptr(), batch, bufs["h"].data_ptr(), ws.data_ptr(),
+                               ws.numel(), stream))
 
     def step():
         for projs, x, a in layers:
-            gemv("q", projs, x)
-            gemv("k", projs, x)
-            gemv("v", projs, x)
-            gemv("o", projs, a)
-            gemv("gate", projs, x)
-            gemv("up", projs, x)
-            if not gemv_only:
-                tq.swiglu(bufs["gate"], bufs["up"], out=bufs["h"])
-            gemv("down", projs, bufs["h"])
+            multi(("q", "k", "v"), projs, x)
+            multi(("o",), projs, a)
+            if gemv_only:
+                multi(("gate", "up"), projs, x)
+            else:
+                swiglu(projs, x)
+            multi(("down",), projs, bufs["h"])
 
     return step
 

@@ -88,6 +88,37 @@ int tq_gemv(int type, const void *w, int64_t n, int64_t k, const float *x, int64
             float *y, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * tq_gemv_multi -- y_p = W_p x for nparts (1..4) matrices of one block type and the same k that
+ * share the activations x (the q, k and v projections of a decode step read the same x), in one
+ * launch where the lanes-along-k kernel applies (Q4_K, batch 1), else one launch per matrix.
+ *   w, n, y   host arrays of nparts entries: device blob w[p] ([n[p]][k], 16-byte aligned),
+ *             rows n[p], device output y[p] ([batch][n[p]] fp32)
+ *   x         device [batch][k] fp32, 16-byte aligned
+ *   workspace as for tq_gemv, at least tq_gemv_multi_workspace_bytes(...) bytes.
+ * Each y[p] is bitwise what tq_gemv(type, w[p], n[p], k, x, ...) gives.
+ */
+size_t tq_gemv_multi_workspace_bytes(int type, int nparts, const int64_t *n, int64_t k,
+                                     int64_t batch);
+int tq_gemv_multi(int type, int nparts, const void *const *w, const int64_t *n, float *const *y,
+                  int64_t k, const float *x, int64_t batch, void *workspace, size_t ws_bytes,
+                  void *stream);
+
+/*
+ * tq_gemv_swiglu -- h[t][r] = silu(g) * u with g = (W_gate x_t)[r], u = (W_up x_t)[r] and
+ * silu(z) = z / (1 + exp(-z)): the gate and up projections of a SwiGLU FFN and the gating
+ * between them (the Llama-family feed-forward; the pages name the models, not the formula), in
+ * one launch for Q4_K at batch 1 (gate and up rows interleaved inside the kernel); otherwise two
+ * tq_gemv launches and
+ * tq_swiglu through the workspace. w_gate, w_up [n][k]; x [batch][k] (16-byte aligned); h
+ * [batch][n] fp32. workspace: tq_gemv_swiglu_workspace_bytes(type, n, k, batch) bytes (0 on the
+ * one-launch path), 256-byte aligned. Bitwise equal to tq_gemv + tq_gemv + tq_swiglu.
+ */
+size_t tq_gemv_swiglu_workspace_bytes(int type, int64_t n, int64_t k, int64_t batch);
+int tq_gemv_swiglu(int type, const void *w_gate, const void *w_up, int64_t n, int64_t k,
+                   const float *x, int64_t batch, float *h, void *workspace, size_t ws_bytes,
+                   void *stream);
+
+/*
  * tq_swiglu -- h[i] = silu(g[i]) * u[i], silu(z) = z / (1 + exp(-z)), for i < count (the
  * gated activation between a SwiGLU FFN's gate/up and down projections). fp32, 4-byte
  * aligned; h may alias g or u. count >= 0.

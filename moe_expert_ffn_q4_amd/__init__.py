@@ -81,6 +81,15 @@ def _declare(L: C.CDLL) -> None:
     L.tq_gemv.restype = _int
     L.tq_swiglu.argtypes = [_vp, _vp, _i64, _vp, _vp]
     L.tq_swiglu.restype = _int
+    L.tq_gemv_multi_workspace_bytes.argtypes = [_int, _int, C.POINTER(_i64), _i64, _i64]
+    L.tq_gemv_multi_workspace_bytes.restype = C.c_size_t
+    L.tq_gemv_multi.argtypes = [_int, _int, C.POINTER(_vp), C.POINTER(_i64), C.POINTER(_vp), _i64,
+                                _vp, _i64, _vp, C.c_size_t, _vp]
+    L.tq_gemv_multi.restype = _int
+    L.tq_gemv_swiglu_workspace_bytes.argtypes = [_int, _i64, _i64, _i64]
+    L.tq_gemv_swiglu_workspace_bytes.restype = C.c_size_t
+    L.tq_gemv_swiglu.argtypes = [_int, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _vp, C.c_size_t, _vp]
+    L.tq_gemv_swiglu.restype = _int
     if hasattr(L, "tq_moe_ffn"):
         L.tq_moe_workspace_bytes.argtypes = [C.POINTER(MoeDesc), _i64]
         L.tq_moe_workspace_bytes.restype = C.c_size_t
@@ -160,6 +169,38 @@ def gemv(t, w: torch.Tensor, n: int, k: int, x: torch.Tensor, out=None, ws=None,
     wsp, wsn = (None, 0) if ws is False else (ws.data_ptr(), ws.numel() * ws.element_size())
     _check(lib().tq_gemv(_type(t), _ptr(w), n, k, _ptr(x2), batch, _ptr(out), wsp, wsn,
                          _stream(stream)))
+    return out
+
+
+def gemv_multi(t, ws_: list, ns: list, k: int, x: torch.Tensor, outs=None, ws=None, stream=None):
+    """[W_p x for each p] in one call (matrices ws_[p] of ns[p] rows sharing x [batch, k])."""
+    x2 = x.reshape(-1, k)
+    batch, P = x2.shape[0], len(ns)
+    if outs is None:
+        outs = [torch.empty((batch, n), dtype=torch.float32, device=x.device) for n in ns]
+    narr = (_i64 * P)(*ns)
+    if ws is None:
+        ws = workspace(int(lib().tq_gemv_multi_workspace_bytes(_type(t), P, narr, k, batch)),
+                       x.device)
+    _check(lib().tq_gemv_multi(_type(t), P, (_vp * P)(*[w.data_ptr() for w in ws_]), narr,
+                               (_vp * P)(*[o.data_ptr() for o in outs]), k, x2.data_ptr(), batch,
+                               ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
+    return outs
+
+
+def gemv_swiglu(t, w_gate: torch.Tensor, w_up: torch.Tensor, n: int, k: int, x: torch.Tensor,
+                out=None, ws=None, stream=None):
+    """h = silu(W_gate x) * (W_up x), fp32 [batch, n]."""
+    x2 = x.reshape(-1, k)
+    batch = x2.shape[0]
+    if out is None:
+        out = torch.empty((batch, n), dtype=torch.float32, device=x.device)
+    if ws is None:
+        need = int(lib().tq_gemv_swiglu_workspace_bytes(_type(t), n, k, batch))
+        ws = workspace(need, x.device, "swiglu")
+    _check(lib().tq_gemv_swiglu(_type(t), w_gate.data_ptr(), w_up.data_ptr(), n, k, x2.data_ptr(),
+                                batch, out.data_ptr(), ws.data_ptr(),
+                                ws.numel() * ws.element_size(), _stream(stream)))
     return out
 
 

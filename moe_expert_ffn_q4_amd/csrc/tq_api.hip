@@ -81,6 +81,73 @@ int tq_gemv(int type, const void *w, int64_t n, int64_t k, const float *x, int64
                   "tq_gemv");
 }
 
+size_t tq_gemv_multi_workspace_bytes(int type, int nparts, const int64_t *n, int64_t k,
+                                     int64_t batch) {
+  if (!known_type(type) || nparts < 1 || nparts > 4 || !n || k < 1 ||
+      k % tq::fmt_block_weights(type) || batch < 1)
+    return 0;
+  for (int p = 0; p < nparts; ++p)
+    if (n[p] < 1) return 0;
+  return tq::gemv_multi_workspace_bytes(type, nparts, n, k, batch);
+}
+
+int tq_gemv_multi(int type, int nparts, const void *const *w, const int64_t *n, float *const *y,
+                  int64_t k, const float *x, int64_t batch, void *workspace, size_t ws_bytes,
+                  void *stream) {
+  if (!known_type(type)) return fail(TQ_EINVAL, "tq_gemv_multi: unknown block type %d", type);
+  if (nparts < 1 || nparts > 4 || !w || !n || !y)
+    return fail(TQ_EINVAL, "tq_gemv_multi: need 1..4 parts and the w, n, y arrays");
+  if (!x) return fail(TQ_EINVAL, "tq_gemv_multi: null x");
+  const int64_t bw = tq::fmt_block_weights(type);
+  if (k < bw || k % bw || k > (1 << 24) || batch < 1 || batch > 4096)
+    return fail(TQ_ESHAPE, "tq_gemv_multi: k=%lld batch=%lld", (long long)k, (long long)batch);
+  int64_t total = 0;
+  for (int p = 0; p < nparts; ++p) {
+    if (!w[p] || !y[p]) return fail(TQ_EINVAL, "tq_gemv_multi: null w or y of part %d", p);
+    if (n[p] < 1 || n[p] > (1 << 28))
+      return fail(TQ_ESHAPE, "tq_gemv_multi: n of part %d is %lld", p, (long long)n[p]);
+    if (!aligned(w[p], 16) || !aligned(y[p], 4))
+      return fail(TQ_EALIGN, "tq_gemv_multi: w 16-byte, y 4-byte alignment needed");
+    total += n[p];
+  }
+  if (!aligned(x, 16) || !aligned(workspace, 256))
+    return fail(TQ_EALIGN, "tq_gemv_multi: x 16-byte, workspace 256-byte alignment needed");
+  if (ws_bytes < tq::gemv_multi_workspace_bytes(type, nparts, n, k, batch))
+    return fail(TQ_ENOSPC, "tq_gemv_multi: workspace of %zu bytes too small", ws_bytes);
+  return launched(tq::launch_gemv_multi(type, nparts, w, n, y, k, x, batch, workspace, ws_bytes,
+                                        (hipStream_t)stream),
+                  "tq_gemv_multi");
+}
+
+size_t tq_gemv_swiglu_workspace_bytes(int type, int64_t n, int64_t k, int64_t batch) {
+  if (!known_type(type) || n < 1 || k < 1 || k % tq::fmt_block_weights(type) || batch < 1) return 0;
+  static const float probe[4] __attribute__((aligned(16))) = {0, 0, 0, 0};
+  return tq::gemv_swiglu_workspace_bytes(type, n, k, batch,
+                                         tq::gemv_swiglu_fused(type, k, probe, batch));
+}
+
+int tq_gemv_swiglu(int type, const void *w_gate, const void *w_up, int64_t n, int64_t k,
+                   const float *x, int64_t batch, float *h, void *workspace, size_t ws_bytes,
+                   void *stream) {
+  if (!known_type(type)) return fail(TQ_EINVAL, "tq_gemv_swiglu: unknown block type %d", type);
+  if (!w_gate || !w_up || !x || !h) return fail(TQ_EINVAL, "tq_gemv_swiglu: null pointer");
+  const int64_t bw = tq::fmt_block_weights(type);
+  if (n < 1 || n > (1 << 28) || k < bw || k % bw || k > (1 << 24) || batch < 1 || batch > 4096)
+    return fail(TQ_ESHAPE, "tq_gemv_swiglu: n=%lld k=%lld batch=%lld", (long long)n, (long long)k,
+                (long long)batch);
+  if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(x, 16) || !aligned(h, 4) ||
+      !aligned(workspace, 256))
+    return fail(TQ_EALIGN, "tq_gemv_swiglu: w and x 16-byte, h 4-byte, workspace 256-byte "
+                           "alignment needed");
+  const bool fused = tq::gemv_swiglu_fused(type, k, x, batch);
+  if (ws_bytes < tq::gemv_swiglu_workspace_bytes(type, n, k, batch, fused) ||
+      (!fused && !workspace))
+    return fail(TQ_ENOSPC, "tq_gemv_swiglu: workspace of %zu bytes too small", ws_bytes);
+  return launched(tq::launch_gemv_swiglu(type, w_gate, w_up, n, k, x, batch, h, workspace,
+                                         ws_bytes, (hipStream_t)stream),
+                  "tq_gemv_swiglu");
+}
+
 int tq_swiglu(const float *g, const float *u, int64_t count, float *h, void *stream) {
   if (count < 0) return fail(TQ_ESHAPE, "tq_swiglu: negative count");
   if (count == 0) return TQ_OK;

@@ -218,11 +218,13 @@ __global__ __launch_bounds__(512) void k_gemv(const uint8_t *__restrict__ w, int
 // Batch-1 Q4_K GEMV, lanes along k (see tq_gemv_core.h). Workgroup = ceil(nblk / 16) waves
 // covering all of k; it computes rows [blockIdx.x * rows_per_wg, ...) R at a time, loading the
 // next R rows while it computes the current ones.
+__device__ __forceinline__ float silu_mul(float g, float u) { return g * u / (1.f + expf(-g)); }
+
 template <int R>
 __device__ __forceinline__ void kl_rows(const u32x4 (&v)[R][3], const float (&xv)[64], float sx_lo,
                                         float sx_hi, const Q4kField &f0, const Q4kField &f1,
                                         float unit_inv, int r0, int re, float (*red)[R],
-                                        float *__restrict__ y) {
+                                        const KlMap &m) {
   const int lane = threadIdx.x & 63, wave = wave_index(), nw = blockDim.x >> 6;
   float acc[R];
 #pragma unroll
@@ -255,10 +257,20 @@ __device__ __forceinline__ void kl_rows(const u32x4 (&v)[R][3], const float (&xv
     red[wave][row] = acc[0];
   }
   __syncthreads();
-  if (threadIdx.x < R && r0 + (int)threadIdx.x < re) {
+  if (m.swiglu) {  // rows (gate r, up r) pairs; r0 and re are even
+    const int i = 2 * (int)threadIdx.x;
+    if (i < R && r0 + i < re) {
+      float g = 0.f, u = 0.f;
+      for (int q = 0; q < nw; ++q) {
+        g += red[q][i];
+        u += red[q][i + 1];
+      }
+      m.y[0][(r0 + i) >> 1] = silu_mul(g, u);
+    }
+  } else if (threadIdx.x < R && r0 + (int)threadIdx.x < re) {
     float s = 0.f;
     for (int q = 0; q < nw; ++q) s += red[q][threadIdx.x];
-    y[r0 + threadIdx.x] = s;
+    *m.out(r0 + threadIdx.x) = s;
   }
   __syncthreads();
 }
@@ -267,20 +279,18 @@ __device__ __forceinline__ void kl_rows(const u32x4 (&v)[R][3], const float (&xv
 // covering all of k; it computes rows [blockIdx.x * rows_per_wg, ...) R at a time, loading the
 // next R rows while it computes the current ones (two register buffers used in turn).
 template <int R>
-__global__ __launch_bounds__(512) void k_gemv_kl(const uint8_t *__restrict__ w, int64_t row_bytes,
-                                                 int n, int nblk, int rows_per_wg,
-                                                 const float *__restrict__ x,
-                                                 float *__restrict__ y) {
+__global__ __launch_bounds__(512) void k_gemv_kl(KlMap m, int nblk, int rows_per_wg,
+                                                 const float *__restrict__ x) {
   __shared__ float red[8][R];
   const int lane = threadIdx.x & 63, wave = wave_index();
   const int b = 16 * wave + (lane >> 2), c = lane & 3;
   const bool valid = b < nblk;
   const int bb = valid ? b : nblk - 1;
   const int boff = bb * 144;
-  const int rb = blockIdx.x * rows_per_wg, re = min(rb + rows_per_wg, n);
+  const int rb = blockIdx.x * rows_per_wg, re = min(rb + rows_per_wg, m.total);
   u32x4 va[R][3], vb[R][3];
   // the first rows' weights are requested before the activations
-  if (rb < re) kl_load_rows<R>(w, row_bytes, n, rb, boff, c, va);
+  if (rb < re) kl_load_rows<R>(m, rb, boff, c, va);
   float xv[64];
   {
     const float4 *xp = reinterpret_cast<const float4 *>(x + 256 * bb + 64 * c);
@@ -302,11 +312,11 @@ __global__ __launch_bounds__(512) void k_gemv_kl(const uint8_t *__restrict__ w, 
   const float unit_inv = 1.f / nibble_fp8_unit();
   const Q4kField f0 = q4k_field(2 * c), f1 = q4k_field(2 * c + 1);
   for (int r0 = rb; r0 < re; r0 += 2 * R) {
-    if (r0 + R < re) kl_load_rows<R>(w, row_bytes, n, r0 + R, boff, c, vb);
-    kl_rows<R>(va, xv, sx_lo, sx_hi, f0, f1, unit_inv, r0, re, red, y);
+    if (r0 + R < re) kl_load_rows<R>(m, r0 + R, boff, c, vb);
+    kl_rows<R>(va, xv, sx_lo, sx_hi, f0, f1, unit_inv, r0, re, red, m);
     if (r0 + R >= re) break;
-    if (r0 + 2 * R < re) kl_load_rows<R>(w, row_bytes, n, r0 + 2 * R, boff, c, va);
-    kl_rows<R>(vb, xv, sx_lo, sx_hi, f0, f1, unit_inv, r0 + R, re, red, y);
+    if (r0 + 2 * R < re) kl_load_rows<R>(m, r0 + 2 * R, boff, c, va);
+    kl_rows<R>(vb, xv, sx_lo, sx_hi, f0, f1, unit_inv, r0 + R, re, red, m);
   }
 }
 
@@ -365,6 +375,35 @@ static int launch_gemv_fmt(const uint8_t *w, int64_t rb, int n, int64_t k, const
   return 0;
 }
 
+// Batch-1 Q4_K shapes that the lanes-along-k kernel takes.
+static bool klane_ok(int fmt, int64_t k, const float *x, int64_t batch) {
+  static const int kl_mode = env_int("TQ_GEMV_KLANE", 1);
+  return fmt == FMT_Q4_K && batch == 1 && kl_mode && ((uintptr_t)x & 15) == 0 && k % 256 == 0 &&
+         k <= 8 * 4096;
+}
+
+static int launch_kl(const KlMap &m, int64_t k, const float *x, hipStream_t s) {
+  const int nblk = (int)(k / 256);
+  const int waves = (nblk + 15) / 16;
+  static const int kl_rows_env = env_int("TQ_KL_ROWS", 4);
+  static const int target = env_int("TQ_KL_TARGET_WAVES", 2048);
+  const int R = kl_rows_env == 2 ? 2 : kl_rows_env == 8 ? 8 : 4;
+  int chunks = (int)(((int64_t)m.total * waves + (int64_t)R * target - 1) / ((int64_t)R * target));
+  chunks = chunks < 1 ? 1 : chunks;
+  const int rows_per_wg = R * chunks;  // even: SwiGLU pairs never straddle two workgroups
+  const int grid = (m.total + rows_per_wg - 1) / rows_per_wg;
+  if (R == 2)
+    hipLaunchKernelGGL(k_gemv_kl<2>, dim3((unsigned)grid), dim3(64 * waves), 0, s, m, nblk,
+                       rows_per_wg, x);
+  else if (R == 8)
+    hipLaunchKernelGGL(k_gemv_kl<8>, dim3((unsigned)grid), dim3(64 * waves), 0, s, m, nblk,
+                       rows_per_wg, x);
+  else
+    hipLaunchKernelGGL(k_gemv_kl<4>, dim3((unsigned)grid), dim3(64 * waves), 0, s, m, nblk,
+                       rows_per_wg, x);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 bool gemv_fast_shape(int fmt, int64_t k) {
   if (fmt == FMT_Q4_K) return k % 256 == 0;
   if (fmt == FMT_Q6_K) return k % 512 == 0;  // 210 * (k/256) bytes per row is dword aligned
@@ -381,27 +420,15 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, in
                        fmt, wb, rb, (int)n, k, x, (int)batch, y);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
-  static const int kl_mode = env_int("TQ_GEMV_KLANE", 1);
-  if (fmt == FMT_Q4_K && batch == 1 && kl_mode && ((uintptr_t)x & 15) == 0 && k <= 8 * 4096) {
-    const int nblk = (int)(k / 256);
-    const int waves = (nblk + 15) / 16;
-    static const int kl_rows_env = env_int("TQ_KL_ROWS", 4);
-    static const int target = env_int("TQ_KL_TARGET_WAVES", 2048);
-    const int R = kl_rows_env == 2 ? 2 : kl_rows_env == 8 ? 8 : 4;
-    int chunks = (int)((n * waves + (int64_t)R * target - 1) / ((int64_t)R * target));
-    chunks = chunks < 1 ? 1 : chunks;
-    const int rows_per_wg = R * chunks;
-    const int grid = (int)((n + rows_per_wg - 1) / rows_per_wg);
-    if (R == 2)
-      hipLaunchKernelGGL(k_gemv_kl<2>, dim3((unsigned)grid), dim3(64 * waves), 0, s, wb, rb, (int)n,
-                         nblk, rows_per_wg, x, y);
-    else if (R == 8)
-      hipLaunchKernelGGL(k_gemv_kl<8>, dim3((unsigned)grid), dim3(64 * waves), 0, s, wb, rb, (int)n,
-                         nblk, rows_per_wg, x, y);
-    else
-      hipLaunchKernelGGL(k_gemv_kl<4>, dim3((unsigned)grid), dim3(64 * waves), 0, s, wb, rb, (int)n,
-                         nblk, rows_per_wg, x, y);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
+  if (klane_ok(fmt, k, x, batch)) {
+    KlMap m{};
+    m.w[0] = wb;
+    m.y[0] = y;
+    m.cum[1] = (int)n;
+    m.nparts = 1;
+    m.total = (int)n;
+    m.row_bytes = rb;
+    return launch_kl(m, k, x, s);
   }
   switch (fmt) {
     case FMT_Q4_K: return launch_gemv_fmt<FMT_Q4_K>(wb, rb, (int)n, k, x, (int)batch, y, ws, ws_bytes, s);
@@ -410,9 +437,81 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, in
   }
 }
 
-// ---- SwiGLU ------------------------------------------------------------------------------------
+size_t gemv_multi_workspace_bytes(int fmt, int nparts, const int64_t *n, int64_t k,
+                                  int64_t batch) {
+  size_t b = 0;
+  for (int p = 0; p < nparts; ++p) {
+    const size_t q = gemv_workspace_bytes(fmt, n[p], k, batch);
+    b = q > b ? q : b;
+  }
+  return b;
+}
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g * u / (1.f + expf(-g)); }
+int launch_gemv_multi(int fmt, int nparts, const void *const *w, const int64_t *n, float *const *y,
+                      int64_t k, const float *x, int64_t batch, void *ws, size_t ws_bytes,
+                      hipStream_t s) {
+  int64_t total = 0;
+  for (int p = 0; p < nparts; ++p) total += n[p];
+  if (klane_ok(fmt, k, x, batch) && nparts <= 4 && total < (1ll << 30)) {
+    KlMap m{};
+    for (int p = 0; p < nparts; ++p) {
+      m.w[p] = (const uint8_t *)w[p];
+      m.y[p] = y[p];
+      m.cum[p + 1] = m.cum[p] + (int)n[p];
+    }
+    m.nparts = nparts;
+    m.total = (int)total;
+    m.row_bytes = k / fmt_block_weights(fmt) * fmt_block_bytes(fmt);
+    return launch_kl(m, k, x, s);
+  }
+  for (int p = 0; p < nparts; ++p) {  // one launch per matrix, in order on the stream
+    const int rc = launch_gemv(fmt, w[p], n[p], k, x, batch, y[p], ws, ws_bytes, s);
+    if (rc) return rc;
+  }
+  return 0;
+}
+
+// Workspace of tq_gemv_swiglu: none on the fused path; otherwise that of one GEMV followed by the
+// gate and up outputs [batch][n] each.
+static int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+size_t gemv_swiglu_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t batch, bool fused) {
+  if (fused) return 0;
+  return (size_t)align_up((int64_t)gemv_workspace_bytes(fmt, n, k, batch), 256) +
+         (size_t)align_up(4 * batch * n, 256) * 2;
+}
+
+int launch_gemv_swiglu(int fmt, const void *wg, const void *wu, int64_t n, int64_t k,
+                       const float *x, int64_t batch, float *h, void *ws, size_t ws_bytes,
+                       hipStream_t s) {
+  const int64_t rb = k / fmt_block_weights(fmt) * fmt_block_bytes(fmt);
+  if (klane_ok(fmt, k, x, batch) && n < (1ll << 29)) {
+    KlMap m{};
+    m.w[0] = (const uint8_t *)wg;
+    m.w[1] = (const uint8_t *)wu;
+    m.y[0] = h;
+    m.nparts = 1;
+    m.swiglu = 1;
+    m.total = (int)(2 * n);
+    m.cum[1] = m.total;
+    m.row_bytes = rb;
+    return launch_kl(m, k, x, s);
+  }
+  const size_t gws = (size_t)align_up((int64_t)gemv_workspace_bytes(fmt, n, k, batch), 256);
+  float *g = (float *)((char *)ws + gws);
+  float *u = (float *)((char *)g + align_up(4 * batch * n, 256));
+  int rc = launch_gemv(fmt, wg, n, k, x, batch, g, ws, ws_bytes, s);
+  if (rc) return rc;
+  rc = launch_gemv(fmt, wu, n, k, x, batch, u, ws, ws_bytes, s);
+  if (rc) return rc;
+  return launch_swiglu(g, u, batch * n, h, s);
+}
+
+bool gemv_swiglu_fused(int fmt, int64_t k, const float *x, int64_t batch) {
+  return klane_ok(fmt, k, x, batch);
+}
+
+// ---- SwiGLU ------------------------------------------------------------------------------------
 
 __global__ __launch_bounds__(256) void k_swiglu(const float *g, const float *u, int64_t count,
                                                 float *h) {

@@ -532,13 +532,40 @@ __device__ __forceinline__ void q4k_scale_min_at(uint32_t s0, uint32_t s1, uint3
   m = (float)(bfe(lm, f.m_off, f.lo_w) | (bfe(s1, f.hi_off, f.hi_w) << 4));
 }
 
+// The rows of one batch-1 launch: up to four matrices that share the activations, their rows
+// taken one after another (multi), or a gate and an up matrix taken alternately, row r of gate
+// then row r of up (swiglu: the pair is combined into h[r] = silu(gate) * up).
+struct KlMap {
+  const uint8_t *w[4];
+  float *y[4];
+  int cum[5];  // multi: cum[p] = first virtual row of matrix p, cum[nparts] = all rows
+  int nparts;
+  int swiglu;  // 1: w[0] gate, w[1] up, y[0] = h; 2 * n virtual rows
+  int total;   // virtual rows
+  int64_t row_bytes;
+
+  __device__ __forceinline__ const uint8_t *row(int v) const {
+    if (swiglu) return w[v & 1] + (int64_t)(v >> 1) * row_bytes;
+    int p = 0;
+#pragma unroll
+    for (int i = 1; i < 4; ++i) p += (i < nparts && v >= cum[i]) ? 1 : 0;
+    return w[p] + (int64_t)(v - cum[p]) * row_bytes;
+  }
+  __device__ __forceinline__ float *out(int v) const {
+    int p = 0;
+#pragma unroll
+    for (int i = 1; i < 4; ++i) p += (i < nparts && v >= cum[i]) ? 1 : 0;
+    return y[p] + (v - cum[p]);
+  }
+};
+
 template <int R>
-__device__ __forceinline__ void kl_load_rows(const uint8_t *w, int64_t row_bytes, int n, int r0,
-                                             int boff, int c, u32x4 (&v)[R][3]) {
+__device__ __forceinline__ void kl_load_rows(const KlMap &m, int r0, int boff, int c,
+                                             u32x4 (&v)[R][3]) {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int row = min(r0 + r, n - 1);
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(w + (int64_t)row * row_bytes + boff);
+    const int row = min(r0 + r, m.total - 1);
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(m.row(row) + boff);
     v[r][0] = p[0];
     v[r][1] = p[1 + 2 * c];
     v[r][2] = p[2 + 2 * c];

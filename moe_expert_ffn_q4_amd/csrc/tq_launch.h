@@ -18,5 +18,14 @@ size_t gemv_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t batch);
 int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, int64_t batch,
                 float *y, void *ws, size_t ws_bytes, hipStream_t s);
 int launch_swiglu(const float *g, const float *u, int64_t count, float *h, hipStream_t s);
+size_t gemv_multi_workspace_bytes(int fmt, int nparts, const int64_t *n, int64_t k, int64_t batch);
+int launch_gemv_multi(int fmt, int nparts, const void *const *w, const int64_t *n, float *const *y,
+                      int64_t k, const float *x, int64_t batch, void *ws, size_t ws_bytes,
+                      hipStream_t s);
+bool gemv_swiglu_fused(int fmt, int64_t k, const float *x, int64_t batch);
+size_t gemv_swiglu_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t batch, bool fused);
+int launch_gemv_swiglu(int fmt, const void *wg, const void *wu, int64_t n, int64_t k,
+                       const float *x, int64_t batch, float *h, void *ws, size_t ws_bytes,
+                       hipStream_t s);
 
 }  // namespace tq

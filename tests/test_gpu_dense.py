@@ -167,3 +167,36 @@ def test_swiglu_on_identical_inputs():
     ref = oracle.swiglu(a, b)
     err = np.abs(h.astype(np.float64) - ref)
     assert np.all(err <= 1e-5 * np.abs(ref) + 1e-5)
+
+
+@pytest.mark.parametrize("t,ns,k,batch", [
+    ("q4_k", [4096, 1024, 1024], 4096, 1),   # q, k, v of the 8B shape: one launch
+    ("q4_k", [37, 5, 100, 3], 1024, 1),      # parts straddle the kernel's row groups
+    ("q4_k", [300, 77], 2048, 3),            # batch > 1: one launch per part
+    ("q6_k", [130, 64], 3072, 1),
+    ("q8_0", [70, 33], 2048, 2),
+])
+def test_gemv_multi_equals_separate_gemvs(t, ns, k, batch):
+    _print_case("gemv_multi", t, ns, k, batch)
+    blobs = [synth.blob(t, synth.rng(51, t, i, n, k), n, k) for i, n in enumerate(ns)]
+    x = dev(synth.normal_f32(synth.rng(51, "x", k, batch), (batch, k)))
+    ws_ = [dev(b) for b in blobs]
+    outs = tq.gemv_multi(t, ws_, ns, k, x)
+    for w, n, o, b in zip(ws_, ns, outs, blobs):
+        ref = host(tq.gemv(t, w, n, k, x))
+        assert np.array_equal(host(o), ref)
+    # one part against the oracle as well
+    y, mag = oracle.gemv(t, blobs[0], ns[0], k, host(x))
+    assert_product_close(host(outs[0]), y, mag, what="gemv_multi part 0")
+
+
+@pytest.mark.parametrize("t,n,k,batch", [("q4_k", 14336, 4096, 1), ("q4_k", 1001, 2048, 1),
+                                         ("q4_k", 500, 4096, 2), ("q8_0", 300, 2048, 1)])
+def test_gemv_swiglu_equals_gemv_gemv_swiglu(t, n, k, batch):
+    _print_case("gemv_swiglu", t, n, k, batch)
+    g = dev(synth.blob(t, synth.rng(52, "g", n, k), n, k))
+    u = dev(synth.blob(t, synth.rng(52, "u", n, k), n, k))
+    x = dev(synth.normal_f32(synth.rng(52, "x", k, batch), (batch, k)))
+    h = host(tq.gemv_swiglu(t, g, u, n, k, x))
+    ref = host(tq.swiglu(tq.gemv(t, g, n, k, x), tq.gemv(t, u, n, k, x)))
+    assert np.array_equal(h, ref)
