@@ -272,12 +272,13 @@ static int host_resident_experts(const tq_moe_desc *d, const tq::MoePlan &p,
                                  hipStream_t st) {
   const tq::MoeShape &s = p.s;
   const int E = (int)s.n_experts;
-  const int64_t list_ints = 3 * (E + 1) + 1;
+  const int S = p.act_stride;
+  const int64_t list_ints = 3 * (int64_t)S + 1;
   HostPathState *hs = nullptr;
   int rc = host_path_state(list_ints, p.max_active, hs);
   if (rc != TQ_OK) return rc;
-  int *act = hs->list, *n_active = hs->list + 3 * (E + 1);
-  if (hipMemcpyAsync(act, ws + p.off_act, (size_t)(3 * (E + 1)) * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+  int *act = hs->list, *n_active = hs->list + 3 * S;
+  if (hipMemcpyAsync(act, ws + p.off_act, (size_t)(3 * S) * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
       hipMemcpyAsync(n_active, ws + p.off_nact, 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
       hipStreamSynchronize(st) != hipSuccess)
     return fail(TQ_EDEVICE, "tq_moe_ffn: reading the active-expert list back failed");
@@ -312,7 +313,7 @@ static int host_resident_experts(const tq_moe_desc *d, const tq::MoePlan &p,
                     "tq_moe_ffn experts");
   }
   auto slot_range = [&](int a) {
-    return tq::SlotRange{a, 1, act[(E + 1) + a], act[2 * (E + 1) + a]};
+    return tq::SlotRange{a, 1, act[S + a], act[2 * S + a]};
   };
   for (int a = 0; a < na; ++a)  // the shared expert first: it needs no copy
     if (act[a] == E) {

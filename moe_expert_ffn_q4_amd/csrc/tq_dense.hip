@@ -1,6 +1,7 @@
 // tq_dense.hip -- dequantization, dense GEMV and SwiGLU kernels with their host launchers.
 #include "tq_gemv_core.h"
 #include "tq_launch.h"
+#include "tq_moe.h"
 
 #include <stdlib.h>
 
@@ -279,15 +280,13 @@ __device__ __forceinline__ void kl_rows(const u32x4 (&v)[R][3], const float (&xv
 // covering all of k; it computes rows [blockIdx.x * rows_per_wg, ...) R at a time, loading the
 // next R rows while it computes the current ones (two register buffers used in turn).
 template <int R>
-__global__ __launch_bounds__(512) void k_gemv_kl(KlMap m, int nblk, int rows_per_wg,
-                                                 const float *__restrict__ x) {
-  __shared__ float red[8][R];
+__device__ __forceinline__ void kl_body(const KlMap &m, int nblk, int rb, int re,
+                                        const float *__restrict__ x, float (*red)[R]) {
   const int lane = threadIdx.x & 63, wave = wave_index();
   const int b = 16 * wave + (lane >> 2), c = lane & 3;
   const bool valid = b < nblk;
   const int bb = valid ? b : nblk - 1;
   const int boff = bb * 144;
-  const int rb = blockIdx.x * rows_per_wg, re = min(rb + rows_per_wg, m.total);
   u32x4 va[R][3], vb[R][3];
   // the first rows' weights are requested before the activations
   if (rb < re) kl_load_rows<R>(m, rb, boff, c, va);
@@ -318,6 +317,55 @@ __global__ __launch_bounds__(512) void k_gemv_kl(KlMap m, int nblk, int rows_per
     if (r0 + 2 * R < re) kl_load_rows<R>(m, r0 + 2 * R, boff, c, va);
     kl_rows<R>(vb, xv, sx_lo, sx_hi, f0, f1, unit_inv, r0 + R, re, red, m);
   }
+}
+
+// Batch-1 Q4_K GEMV, lanes along k (see tq_gemv_core.h). Workgroup = ceil(nblk / 16) waves
+// covering all of k; it computes rows [blockIdx.x * rows_per_wg, ...) R at a time, loading the
+// next R rows while it computes the current ones (two register buffers used in turn).
+template <int R>
+__global__ __launch_bounds__(512) void k_gemv_kl(KlMap m, int nblk, int rows_per_wg,
+                                                 const float *__restrict__ x) {
+  __shared__ float red[8][R];
+  const int rb = blockIdx.x * rows_per_wg, re = min(rb + rows_per_wg, m.total);
+  kl_body<R>(m, nblk, rb, re, x, red);
+}
+
+// The same kernel over the experts of a one-token MoE step: workgroup b works on active slot
+// slot0 + b / wgs_per_slot (every active expert has that one token). gate/up: the expert's
+// gate and up rows interleaved with the SwiGLU in the epilogue, x = the token's activations,
+// h[position][ffn] out; down: x = h[position], o[position][hidden] out.
+template <int R>
+__global__ __launch_bounds__(512) void k_moe_kl(MoeKlArgs a, int nblk, int rows_per_wg,
+                                                int wgs_per_slot) {
+  __shared__ float red[8][R];
+  const int slot = a.slot0 + (int)blockIdx.x / wgs_per_slot;
+  if (slot >= *a.n_active) return;
+  const int e = a.act[slot], p = a.act[a.act_stride + slot];
+  const uint8_t *w[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int mat = a.gate_up ? q : 2;
+    if (e == a.E)
+      w[q] = (const uint8_t *)a.shared.m[mat];
+    else if (a.staging != nullptr)
+      w[q] = a.staging + (int64_t)slot * a.stage_stride + a.stage_off[mat];
+    else
+      w[q] = (const uint8_t *)a.experts[e].m[mat];
+  }
+  KlMap m{};
+  m.w[0] = w[0];
+  m.w[1] = w[1];
+  m.y[0] = a.out + (int64_t)p * a.ldo;
+  m.nparts = 1;
+  m.swiglu = a.gate_up;
+  m.total = a.rows;
+  m.cum[1] = a.rows;
+  m.row_bytes = a.row_bytes;
+  int64_t xrow = p;
+  if (a.gate_up) xrow = p >= a.Tk ? p - a.Tk : a.pairs[p] / a.topk;
+  const int rb = ((int)blockIdx.x % wgs_per_slot) * rows_per_wg;
+  const int re = min(rb + rows_per_wg, a.rows);
+  kl_body<R>(m, nblk, rb, re, a.x + xrow * a.ldx, red);
 }
 
 // Fallback for shapes whose rows are not dword aligned (Q6_K with k % 512 != 0, Q8_0 with
@@ -401,6 +449,27 @@ static int launch_kl(const KlMap &m, int64_t k, const float *x, hipStream_t s) {
   else
     hipLaunchKernelGGL(k_gemv_kl<4>, dim3((unsigned)grid), dim3(64 * waves), 0, s, m, nblk,
                        rows_per_wg, x);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+bool moe_klane_ok(int fmt, int64_t hidden, int64_t ffn, int64_t tokens) {
+  static const int kl_mode = env_int("TQ_GEMV_KLANE", 1);
+  return fmt == FMT_Q4_K && tokens == 1 && kl_mode && hidden % 256 == 0 && ffn % 256 == 0 &&
+         hidden <= 8 * 4096 && ffn <= 8 * 4096;
+}
+
+int launch_moe_kl(const MoeKlArgs &a, int64_t k, int nslots, hipStream_t s) {
+  const int nblk = (int)(k / 256);
+  const int waves = (nblk + 15) / 16;
+  static const int target = env_int("TQ_KL_TARGET_WAVES", 2048);
+  const int R = 4;
+  int chunks = (int)(((int64_t)a.rows * nslots * waves + (int64_t)R * target - 1) /
+                     ((int64_t)R * target));
+  chunks = chunks < 1 ? 1 : chunks;
+  const int rows_per_wg = R * chunks;  // even: SwiGLU pairs stay in one workgroup
+  const int wgs_per_slot = (a.rows + rows_per_wg - 1) / rows_per_wg;
+  hipLaunchKernelGGL(k_moe_kl<4>, dim3((unsigned)(nslots * wgs_per_slot)), dim3(64 * waves), 0, s,
+                     a, nblk, rows_per_wg, wgs_per_slot);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -23,6 +23,10 @@ struct MoePlan {
   MoeShape s;
   int64_t P;       // positions: T*k routed pairs, then T shared-expert rows
   int max_active;  // upper bound of active experts (including the shared one)
+  int nt;          // token rows per tile of the grouped fp32 GEMV (1, 2, 4 or 8)
+  int klane;       // one-token Q4_K step: the lanes-along-k kernels (SwiGLU fused)
+  int shared_piece;  // positions per active-list entry of the shared expert
+  int act_stride;    // stride of the three arrays of the active-expert list
   int rtiles, hsplit, hpk;
   int gu_rg, gu_ks, gu_upk, gu_waves, gu_upw;
   int d_rg, d_ks, d_upk, d_waves, d_upw;
@@ -38,6 +42,26 @@ MoePlan plan_moe(const MoeShape &s);
 size_t group_lds_bytes(int64_t T, int64_t E);
 int launch_moe_routing(const MoePlan &p, const float *router_w, const float *x, char *ws,
                        hipStream_t st);
+// Arguments of the lanes-along-k kernel over the experts of a one-token step (Q4_K).
+struct MoeKlArgs {
+  const MoeExpertPtrs *experts;
+  MoeExpertPtrs shared;
+  const uint8_t *staging;
+  int64_t stage_stride;
+  int64_t stage_off[3];
+  const int *act, *n_active, *pairs;
+  int slot0, act_stride, E, topk, Tk;
+  int gate_up;        // 1: gate/up rows interleaved, SwiGLU epilogue; 0: down
+  int rows;           // virtual rows per slot: 2 * ffn (gate/up) or hidden (down)
+  int64_t row_bytes;
+  const float *x;     // token rows (gate/up) or h rows by position (down)
+  int64_t ldx;
+  float *out;         // h [P][ffn] or o [P][hidden]
+  int64_t ldo;
+};
+bool moe_klane_ok(int fmt, int64_t hidden, int64_t ffn, int64_t tokens);
+int launch_moe_kl(const MoeKlArgs &a, int64_t k, int nslots, hipStream_t s);
+
 // A subset of the active-expert list: slots slot0 .. slot0+nslots-1, whose pairs occupy positions
 // pos0 .. pos0+npos-1 (the host knows both once it has read the list back).
 struct SlotRange {

@@ -12,6 +12,8 @@
 //   k_moe_swiglu    h = silu(gate) * up from the gate/up slices
 //   k_moe_combine   y[t] = sum_j w[t][j] * o[pair (t, j)] + o_shared[t], slots in order
 // No atomic operation decides any order, so every output is deterministic.
+#include <stdlib.h>
+
 #include "tq_gemv_core.h"
 #include "tq_launch.h"
 #include "tq_moe.h"
@@ -148,10 +150,13 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, in
 //   tab[c][e]  first the number of pairs of chunk c routed to e (popcount of the mask), then
 //              in place the number routed to e by the chunks before c.
 //   pairs[offsets[e] + tab[c][e] + r] = t*k + j, r = lanes of chunk c routed to e below t's lane.
-// act: [0, E+1) expert id, [E+1, 2E+2) first position, [2E+2, 3E+3) count, for the active experts
-// in ascending expert order and the shared expert (id E, positions T*k .. T*k+T-1) last.
+// act (stride S = act_stride): [0, S) expert id, [S, 2S) first position, [2S, 3S) count, for the
+// active experts in ascending expert order, then the shared expert (id E, positions T*k ..
+// T*k+T-1) as entries of at most shared_piece consecutive positions each, so that no single
+// entry carries all T tokens.
 __global__ __launch_bounds__(512) void k_group(const int *__restrict__ ids, int T, int topk, int E,
-                                               int has_shared, int *__restrict__ counts,
+                                               int has_shared, int act_stride, int shared_piece,
+                                               int *__restrict__ counts,
                                                int *__restrict__ offsets, int *__restrict__ pairs,
                                                int *__restrict__ inv, int *__restrict__ act,
                                                int *__restrict__ n_active) {
@@ -201,20 +206,21 @@ __global__ __launch_bounds__(512) void k_group(const int *__restrict__ ids, int 
       offsets[e] = run;
       if (cnt > 0) {
         act[na] = e;
-        act[(E + 1) + na] = run;
-        act[2 * (E + 1) + na] = cnt;
+        act[act_stride + na] = run;
+        act[2 * act_stride + na] = cnt;
         ++na;
       }
       off[e] = run;
       run += cnt;
     }
     offsets[E] = run;
-    if (has_shared) {
-      act[na] = E;
-      act[(E + 1) + na] = run;
-      act[2 * (E + 1) + na] = T;
-      ++na;
-    }
+    if (has_shared)
+      for (int t0 = 0; t0 < T; t0 += shared_piece) {
+        act[na] = E;
+        act[act_stride + na] = run + t0;
+        act[2 * act_stride + na] = min(shared_piece, T - t0);
+        ++na;
+      }
     *n_active = na;
   }
   __syncthreads();
@@ -261,6 +267,7 @@ struct MoeGemvArgs {
   const int *n_active;
   const int *pairs;
   int slot0;                     // first active slot of this launch
+  int act_stride;
   int E, topk, Tk;
   int mat0, nmat;                // matrices m = mat0 .. mat0 + nmat - 1 (0 gate, 1 up, 2 down)
   int n_rows, units;             // rows of each matrix, units of 256 weights along k
@@ -273,29 +280,33 @@ struct MoeGemvArgs {
   int64_t P;
 };
 
+// One tile of up to NT token rows (nt valid ones; the rest repeat the last valid row and their
+// results are dropped).
 template <int FMT, int NT>
 __device__ __forceinline__ void moe_tile(const MoeGemvArgs &a, const uint8_t *w, int m, int rg,
-                                         int ks, int p0, float *lds) {
+                                         int ks, int p0, int nt, float *lds) {
   const int row0 = rg * 64;
   const int ku0 = ks * a.upk, ku1 = min(ku0 + a.upk, a.units);
   const float *xr[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const int p = p0 + t;
+    const int p = p0 + min(t, nt - 1);
     int64_t r = p;
     if (a.x_by_token) r = p >= a.Tk ? p - a.Tk : a.pairs[p] / a.topk;
     xr[t] = a.xsrc + r * a.ldx;
   }
   gemv_tile<FMT, NT>(w, a.row_bytes, a.n_rows, row0, ku0, ku1, a.upw, xr, lds);
   float *o = a.out + ((int64_t)(m - a.mat0) * a.ksplit + ks) * a.P * a.n_rows;
-  for (int i = threadIdx.x; i < NT * 64; i += blockDim.x) {
+  for (int i = threadIdx.x; i < nt * 64; i += blockDim.x) {
     const int t = i >> 6, l = i & 63;
     if (row0 + l < a.n_rows) o[(int64_t)(p0 + t) * a.n_rows + row0 + l] = lds[i];
   }
   __syncthreads();  // lds is reused by the next tile
 }
 
-template <int FMT>
+// Tiles of NT tokens (a compile-time size per launch: one body, no per-tile dispatch, so the
+// kernel keeps the registers of a single tile shape).
+template <int FMT, int NT>
 __global__ __launch_bounds__(512) void k_moe_gemv(MoeGemvArgs a) {
   extern __shared__ float lds[];
   const int per_slot = a.nmat * a.rowgroups * a.ksplit;
@@ -306,7 +317,7 @@ __global__ __launch_bounds__(512) void k_moe_gemv(MoeGemvArgs a) {
   r -= mi * a.rowgroups * a.ksplit;
   const int rg = r / a.ksplit, ks = r - rg * a.ksplit;
   const int m = a.mat0 + mi;
-  const int e = a.act[slot], p0 = a.act[(a.E + 1) + slot], cnt = a.act[2 * (a.E + 1) + slot];
+  const int e = a.act[slot], p0 = a.act[a.act_stride + slot], cnt = a.act[2 * a.act_stride + slot];
   const uint8_t *w;
   if (e == a.E) {
     w = (const uint8_t *)a.shared.m[m];
@@ -315,19 +326,7 @@ __global__ __launch_bounds__(512) void k_moe_gemv(MoeGemvArgs a) {
   } else {
     w = (const uint8_t *)a.experts[e].m[m];
   }
-  for (int t0 = 0; t0 < cnt; t0 += 8) {
-    const int nt = min(8, cnt - t0);
-    switch (nt) {
-      case 1: moe_tile<FMT, 1>(a, w, m, rg, ks, p0 + t0, lds); break;
-      case 2: moe_tile<FMT, 2>(a, w, m, rg, ks, p0 + t0, lds); break;
-      case 3: moe_tile<FMT, 3>(a, w, m, rg, ks, p0 + t0, lds); break;
-      case 4: moe_tile<FMT, 4>(a, w, m, rg, ks, p0 + t0, lds); break;
-      case 5: moe_tile<FMT, 5>(a, w, m, rg, ks, p0 + t0, lds); break;
-      case 6: moe_tile<FMT, 6>(a, w, m, rg, ks, p0 + t0, lds); break;
-      case 7: moe_tile<FMT, 7>(a, w, m, rg, ks, p0 + t0, lds); break;
-      default: moe_tile<FMT, 8>(a, w, m, rg, ks, p0 + t0, lds); break;
-    }
-  }
+  for (int t0 = 0; t0 < cnt; t0 += NT) moe_tile<FMT, NT>(a, w, m, rg, ks, p0 + t0, min(NT, cnt - t0), lds);
 }
 
 // ---- SwiGLU over the gate/up slices and the combine ---------------------------------------------
@@ -384,7 +383,20 @@ MoePlan plan_moe(const MoeShape &s) {
   p.s = s;
   const int64_t T = s.tokens, E = s.n_experts, k = s.top_k;
   p.P = T * k + (s.has_shared ? T : 0);
-  p.max_active = (int)((E < T * k ? E : T * k) + (s.has_shared ? 1 : 0));
+  // the shared expert's T positions as entries of at most shared_piece: 16 on the fp32 grouped
+  // path (two tiles of 8), all T elsewhere (one token, or the matrix-core chunk table)
+  p.shared_piece = (int)(!s.mfma && T > 16 ? 16 : T);
+  const int nsh = s.has_shared ? (int)((T + p.shared_piece - 1) / p.shared_piece) : 0;
+  p.max_active = (int)((E < T * k ? E : T * k) + nsh);
+  p.act_stride = (int)E + (nsh > 1 ? nsh : 1);
+  // token rows per tile of the grouped GEMV: one at T = 1, else about the mean per expert
+  const int64_t mean = (T * k + E - 1) / E;
+  p.nt = T == 1 ? 1 : mean >= 12 ? 8 : mean >= 2 ? 4 : 2;  // measured: Mixtral T=16, 64; DeepSeek T=256
+  if (const char *v = getenv("TQ_MOE_NT")) {  // tuning override: 1, 2, 4 or 8
+    const int n = atoi(v);
+    if (n == 1 || n == 2 || n == 4 || n == 8) p.nt = n;
+  }
+  p.klane = !s.mfma && moe_klane_ok(s.type, s.hidden, s.ffn, s.tokens);
   // router: 64 expert rows per workgroup, token tiles of 8, h split to fill the chip
   p.rtiles = (int)((T + 7) / 8);
   const int rrg = (int)((E + 63) / 64);
@@ -408,6 +420,7 @@ MoePlan plan_moe(const MoeShape &s) {
   };
   split(s.ffn, s.hidden, 2, p.gu_rg, p.gu_ks, p.gu_upk, p.gu_waves, p.gu_upw);
   split(s.hidden, s.ffn, 1, p.d_rg, p.d_ks, p.d_upk, p.d_waves, p.d_upw);
+  if (p.klane) p.d_ks = 1;  // the lanes-along-k kernel writes whole sums
   // workspace carve-up
   int64_t o = 0;
   auto take = [&](int64_t bytes) {
@@ -423,7 +436,7 @@ MoePlan plan_moe(const MoeShape &s) {
   p.off_offsets = take((E + 1) * 4);
   p.off_pairs = take(T * k * 4);
   p.off_inv = take(T * k * 4);
-  p.off_act = take(3 * (E + 1) * 4);
+  p.off_act = take((int64_t)3 * p.act_stride * 4);
   p.off_nact = take(4);
   if (s.mfma) {
     p.d_ks = 1;
@@ -443,21 +456,31 @@ MoePlan plan_moe(const MoeShape &s) {
   return p;
 }
 
-template <int FMT>
+template <int FMT, int NT>
 static int moe_gemv_launch(MoeGemvArgs a, int nslots, int waves, hipStream_t st) {
   const int grid = nslots * a.nmat * a.rowgroups * a.ksplit;
-  const size_t lds = (size_t)4 * gemv_tile_lds_floats<FMT>(8, a.upk, waves);
+  const size_t lds = (size_t)4 * gemv_tile_lds_floats<FMT>(NT, a.upk, waves);
   if (lds > 65536) return -2;
-  hipLaunchKernelGGL(k_moe_gemv<FMT>, dim3((unsigned)grid), dim3(64 * waves), lds, st, a);
+  hipLaunchKernelGGL((k_moe_gemv<FMT, NT>), dim3((unsigned)grid), dim3(64 * waves), lds, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-static int moe_gemv_dispatch(int fmt, const MoeGemvArgs &a, int nslots, int waves,
+template <int FMT>
+static int moe_gemv_nt(const MoeGemvArgs &a, int nt, int nslots, int waves, hipStream_t st) {
+  switch (nt) {
+    case 1: return moe_gemv_launch<FMT, 1>(a, nslots, waves, st);
+    case 2: return moe_gemv_launch<FMT, 2>(a, nslots, waves, st);
+    case 4: return moe_gemv_launch<FMT, 4>(a, nslots, waves, st);
+    default: return moe_gemv_launch<FMT, 8>(a, nslots, waves, st);
+  }
+}
+
+static int moe_gemv_dispatch(int fmt, const MoeGemvArgs &a, int nt, int nslots, int waves,
                              hipStream_t st) {
   switch (fmt) {
-    case FMT_Q4_K: return moe_gemv_launch<FMT_Q4_K>(a, nslots, waves, st);
-    case FMT_Q6_K: return moe_gemv_launch<FMT_Q6_K>(a, nslots, waves, st);
-    default: return moe_gemv_launch<FMT_Q8_0>(a, nslots, waves, st);
+    case FMT_Q4_K: return moe_gemv_nt<FMT_Q4_K>(a, nt, nslots, waves, st);
+    case FMT_Q6_K: return moe_gemv_nt<FMT_Q6_K>(a, nt, nslots, waves, st);
+    default: return moe_gemv_nt<FMT_Q8_0>(a, nt, nslots, waves, st);
   }
 }
 
@@ -473,7 +496,7 @@ int launch_moe_routing(const MoePlan &p, const float *router_w, const float *x, 
                      (float *)(ws + p.off_wts));
   const size_t glds = group_lds_bytes(s.tokens, s.n_experts);
   hipLaunchKernelGGL(k_group, dim3(1), dim3(512), glds, st, (const int *)(ws + p.off_ids), T, k, E,
-                     s.has_shared, (int *)(ws + p.off_counts), (int *)(ws + p.off_offsets),
+                     s.has_shared, p.act_stride, p.shared_piece, (int *)(ws + p.off_counts), (int *)(ws + p.off_offsets),
                      (int *)(ws + p.off_pairs), (int *)(ws + p.off_inv), (int *)(ws + p.off_act),
                      (int *)(ws + p.off_nact));
   return hipGetLastError() == hipSuccess ? 0 : -1;
@@ -509,6 +532,7 @@ int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
   a.n_active = (const int *)(ws + p.off_nact);
   a.pairs = (const int *)(ws + p.off_pairs);
   a.slot0 = range ? range->slot0 : 0;
+  a.act_stride = p.act_stride;
   const int nslots = range ? range->nslots : p.max_active;
   const int64_t pos0 = range ? range->pos0 : 0, npos = range ? range->npos : p.P;
   a.E = E;
@@ -521,6 +545,7 @@ int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
     b.shared = shared;
     b.act = a.act;
     b.n_active = a.n_active;
+    b.act_stride = p.act_stride;
     b.chunks = (const int *)(ws + p.off_chunks);
     b.n_chunks = (const int *)(ws + p.off_nchunks);
     b.pairs = a.pairs;
@@ -532,6 +557,40 @@ int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
     for (int m = 0; m < 3; ++m) b.stage_off[m] = a.stage_off[m];
     return launch_prefill(p.max_chunks, b, x, T, s.hidden, s.ffn, (uint16_t *)(ws + p.off_xb),
                           (uint16_t *)(ws + p.off_hb), (float *)(ws + p.off_o), st);
+  }
+  if (p.klane) {
+    MoeKlArgs g{};
+    g.experts = experts_dev;
+    g.shared = shared;
+    g.staging = staging;
+    g.stage_stride = p.stage_stride;
+    for (int m = 0; m < 3; ++m) g.stage_off[m] = a.stage_off[m];
+    g.act = a.act;
+    g.n_active = a.n_active;
+    g.pairs = a.pairs;
+    g.slot0 = a.slot0;
+    g.act_stride = p.act_stride;
+    g.E = E;
+    g.topk = k;
+    g.Tk = T * k;
+    MoeKlArgs d = g;
+    g.gate_up = 1;
+    g.rows = (int)(2 * s.ffn);
+    g.row_bytes = s.hidden / 256 * 144;
+    g.x = x;
+    g.ldx = s.hidden;
+    g.out = (float *)(ws + p.off_h);
+    g.ldo = s.ffn;
+    int rc = launch_moe_kl(g, s.hidden, nslots, st);
+    if (rc) return rc;
+    d.gate_up = 0;
+    d.rows = (int)s.hidden;
+    d.row_bytes = s.ffn / 256 * 144;
+    d.x = (const float *)(ws + p.off_h);
+    d.ldx = s.ffn;
+    d.out = (float *)(ws + p.off_o);
+    d.ldo = s.hidden;
+    return launch_moe_kl(d, s.ffn, nslots, st);
   }
   // gate and up
   a.mat0 = 0;
@@ -547,7 +606,7 @@ int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
   a.ldx = s.hidden;
   a.x_by_token = 1;
   a.out = (float *)(ws + p.off_gu);
-  int rc = moe_gemv_dispatch(s.type, a, nslots, p.gu_waves, st);
+  int rc = moe_gemv_dispatch(s.type, a, p.nt, nslots, p.gu_waves, st);
   if (rc) return rc;
   float *h = (float *)(ws + p.off_h);
   {
@@ -572,7 +631,7 @@ int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
   a.ldx = s.ffn;
   a.x_by_token = 0;
   a.out = (float *)(ws + p.off_o);
-  return moe_gemv_dispatch(s.type, a, nslots, p.d_waves, st);
+  return moe_gemv_dispatch(s.type, a, p.nt, nslots, p.d_waves, st);
 }
 
 }  // namespace tq

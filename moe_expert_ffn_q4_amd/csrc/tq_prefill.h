@@ -15,6 +15,7 @@ struct PrefillArgs {
   int64_t stage_stride;
   int64_t stage_off[3];          // offsets of gate / up / down inside one staged expert
   const int *act, *n_active;     // active expert list of the grouping kernel
+  int act_stride;
   const int *chunks, *n_chunks;  // chunk table (slot, first position, rows)
   const int *pairs;
   int E, topk, Tk;

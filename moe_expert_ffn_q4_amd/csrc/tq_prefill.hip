@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void k_to_bf16(const float *__restrict__ x, in
 // ceil(cnt / kChunk) chunks of near-equal size, chunks in slot order. One workgroup of 256
 // threads, a thread per slot, an LDS prefix sum over each batch of 256 slots.
 __global__ __launch_bounds__(256) void k_chunk_table(const int *__restrict__ act,
-                                                     const int *__restrict__ n_active, int E,
+                                                     const int *__restrict__ n_active, int act_stride,
                                                      int max_chunks, int *__restrict__ chunks,
                                                      int *__restrict__ n_chunks) {
   __shared__ int scan[256];
@@ -68,8 +68,8 @@ __global__ __launch_bounds__(256) void k_chunk_table(const int *__restrict__ act
     const int s = s0 + (int)threadIdx.x;
     int cnt = 0, p0 = 0, parts = 0;
     if (s < na) {
-      p0 = act[(E + 1) + s];
-      cnt = act[2 * (E + 1) + s];
+      p0 = act[act_stride + s];
+      cnt = act[2 * act_stride + s];
       parts = (cnt + kChunk - 1) / kChunk;
     }
     scan[threadIdx.x] = parts;
@@ -443,7 +443,7 @@ int launch_prefill(int max_chunks, PrefillArgs a, const float *x, int64_t tokens
     if (blocks > 8192) blocks = 8192;
     hipLaunchKernelGGL(k_to_bf16, dim3((unsigned)blocks), dim3(256), 0, st, x, n, (uint32_t *)xb);
   }
-  hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(256), 0, st, a.act, a.n_active, a.E,
+  hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(256), 0, st, a.act, a.n_active, a.act_stride,
                      max_chunks, (int *)a.chunks, (int *)a.n_chunks);
   const int groups = (max_chunks + 7) / 8;
   // gate / up
