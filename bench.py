@@ -53,6 +53,9 @@ def _args():
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain 1 GiB device copy (the known-size reference for the "
                         "FETCH_SIZE / WRITE_SIZE counters)")
+    p.add_argument("--kernel-summary", nargs="+", metavar="CSV",
+                   help="no GPU: print the kernel statistics of a rocprofv3 kernel-stats CSV and "
+                        "the per-kernel averages of any counter-collection CSVs that follow")
     p.add_argument("--summarize", nargs=3, metavar=("KERNEL_STATS", "FETCH_CSV", "WRITE_CSV"),
                    help="no GPU: print a text summary of a rocprofv3 kernel-stats CSV and two "
                         "counter-collection CSVs (FETCH_SIZE, WRITE_SIZE) of the llama8b batch-1 "
@@ -71,12 +74,16 @@ def source_hash(paths=GEMV_SOURCES):
 
 
 def llama8b_bytes_per_launch(synth, batch=1):
-    """Algorithmic bytes of the average GEMV launch of the dense step: weight blob plus fp32 x
-    and y, over the seven projections of a layer."""
+    """Algorithmic bytes of the average GEMV launch of the dense step's GEMV pass: per layer the
+    launches q|k|v, o, gate|up and down, each reading its weight blobs once plus fp32 x and y."""
+    shapes = {name: (n, k) for name, n, k in synth.dense_projections(synth.LLAMA8B)}
+    launches = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
     tot = 0
-    for _, n, k in synth.dense_projections(synth.LLAMA8B):
-        tot += n * (k // 256) * 144 + 4 * batch * (n + k)
-    return tot / 7
+    for names in launches:
+        k = shapes[names[0]][1]
+        rows = sum(shapes[m][0] for m in names)
+        tot += rows * (k // 256) * 144 + 4 * batch * (rows + k)
+    return tot / len(launches)
 
 
 def summarize(kt_csv, fetch_csv, write_csv):
@@ -134,6 +141,30 @@ def summarize(kt_csv, fetch_csv, write_csv):
     lines.append(f"traffic_bytes_per_launch: {traffic:.0f}")
     lines.append(f"traffic_over_algorithmic: {traffic / algo:.4f}")
     lines.append(f"kernel_source_sha256: {source_hash()}")
+    return "\n".join(lines)
+
+
+def kernel_summary(stats_csv, *counter_csvs):
+    """Kernel statistics table plus per-(kernel, grid) averages of the collected counters."""
+    import csv
+    from collections import defaultdict
+
+    lines = [f"{'kernel':<72s} {'calls':>6s} {'avg_us':>10s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}"]
+    for r in csv.DictReader(open(stats_csv)):
+        lines.append(f"{r['Name'][:72]:<72s} {int(r['Calls']):6d} {float(r['AverageNs'])/1e3:10.3f} "
+                     f"{float(r['MinNs'])/1e3:9.3f} {float(r['MaxNs'])/1e3:9.3f} "
+                     f"{float(r['Percentage']):6.2f}")
+    for path in counter_csvs:
+        agg = defaultdict(lambda: defaultdict(list))
+        for r in csv.DictReader(open(path)):
+            key = (r["Kernel_Name"][:60], int(r["Grid_Size"]), int(r["Workgroup_Size"]))
+            agg[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        lines.append("")
+        lines.append(f"# counters per dispatch (mean over dispatches) from {os.path.basename(os.path.dirname(path))}")
+        for key in sorted(agg, key=lambda k: -max(sum(v) for v in agg[k].values())):
+            vals = " ".join(f"{c}={sum(v) / len(v):.4g}" for c, v in sorted(agg[key].items()))
+            n = max(len(v) for v in agg[key].values())
+            lines.append(f"{key[0]:<60s} grid={key[1]} wg={key[2]} n={n} {vals}")
     return "\n".join(lines)
 
 
@@ -440,6 +471,9 @@ def main():
     args = _args()
     if args.summarize:
         print(summarize(*args.summarize))
+        return
+    if args.kernel_summary:
+        print(kernel_summary(*args.kernel_summary))
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "

@@ -171,7 +171,7 @@ static int moe_check(const tq_moe_desc *d, int64_t tokens, tq::MoeShape *out) {
     return fail(TQ_ESHAPE, "tq_moe_ffn: n_experts=%lld top_k=%lld out of range",
                 (long long)d->n_experts, (long long)d->top_k);
   if (tokens < 1 || tokens > 8192) return fail(TQ_ESHAPE, "tq_moe_ffn: tokens=%lld not in 1..8192", (long long)tokens);
-  if (tq::group_lds_bytes(tokens, d->n_experts) > 65536)
+  if (tq::group_lds_bytes(tokens, d->n_experts) > 160 * 1024)
     return fail(TQ_EUNSUPPORTED, "tq_moe_ffn: tokens x experts too large for the grouping kernel");
   if (!d->router_w || !aligned(d->router_w, 16)) return fail(TQ_EINVAL, "tq_moe_ffn: router_w null or not 16-byte aligned");
   if (d->experts_on_host ? !d->experts_host : !d->experts)

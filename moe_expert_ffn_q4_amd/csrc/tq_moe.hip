@@ -87,7 +87,9 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, in
     const int e = lane + 64 * i;
     if (i < nv && e < E) {
       float s = 0.f;
-      for (int hs = 0; hs < hsplit; ++hs) s += part[(((int64_t)tile * hsplit + hs) * 8 + tt) * E + e];
+      const float *pp = part + ((int64_t)tile * hsplit * 8 + tt) * E + e;
+#pragma unroll 8
+      for (int hs = 0; hs < hsplit; ++hs) s += pp[(int64_t)hs * 8 * E];  // loads in flight together
       v[i] = s;
       logits[(int64_t)t * E + e] = s;
     }
@@ -198,30 +200,61 @@ __global__ __launch_bounds__(512) void k_group(const int *__restrict__ ids, int 
     off[e] = (int)run;  // the count, for now
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0, na = 0;
-    for (int e = 0; e < E; ++e) {
-      const int cnt = off[e];
-      counts[e] = cnt;
-      offsets[e] = run;
-      if (cnt > 0) {
-        act[na] = e;
-        act[act_stride + na] = run;
-        act[2 * act_stride + na] = cnt;
-        ++na;
-      }
-      off[e] = run;
-      run += cnt;
+  // counts -> exclusive offsets, and the active-list index of every expert with a non-zero count:
+  // two exclusive scans over the experts, each thread owning two consecutive experts
+  int *scan = off + E + ((nchunks * E + 1) >> 1);  // [2][blockDim]: position and active counts
+  {
+    const int e0 = 2 * (int)threadIdx.x, e1 = e0 + 1;
+    const int c0 = e0 < E ? off[e0] : 0, c1 = e1 < E ? off[e1] : 0;
+    const int nt = blockDim.x;
+    int sp = c0 + c1, sa = (c0 > 0) + (c1 > 0);
+    scan[threadIdx.x] = sp;
+    scan[nt + threadIdx.x] = sa;
+    __syncthreads();
+    for (int d = 1; d < nt; d <<= 1) {  // inclusive scans of the per-thread totals
+      const int vp = threadIdx.x >= (unsigned)d ? scan[threadIdx.x - d] : 0;
+      const int va = threadIdx.x >= (unsigned)d ? scan[nt + threadIdx.x - d] : 0;
+      __syncthreads();
+      scan[threadIdx.x] += vp;
+      scan[nt + threadIdx.x] += va;
+      __syncthreads();
     }
-    offsets[E] = run;
-    if (has_shared)
-      for (int t0 = 0; t0 < T; t0 += shared_piece) {
-        act[na] = E;
-        act[act_stride + na] = run + t0;
-        act[2 * act_stride + na] = min(shared_piece, T - t0);
-        ++na;
+    const int pos0 = scan[threadIdx.x] - sp, act0 = scan[nt + threadIdx.x] - sa;
+    const int total = scan[nt - 1], nact = scan[2 * nt - 1];
+    __syncthreads();  // every thread has read the scans (off is rewritten below)
+    if (e0 < E) {
+      counts[e0] = c0;
+      offsets[e0] = pos0;
+      off[e0] = pos0;
+      if (c0 > 0) {
+        act[act0] = e0;
+        act[act_stride + act0] = pos0;
+        act[2 * act_stride + act0] = c0;
       }
-    *n_active = na;
+    }
+    if (e1 < E) {
+      const int a1 = act0 + (c0 > 0);
+      counts[e1] = c1;
+      offsets[e1] = pos0 + c0;
+      off[e1] = pos0 + c0;
+      if (c1 > 0) {
+        act[a1] = e1;
+        act[act_stride + a1] = pos0 + c0;
+        act[2 * act_stride + a1] = c1;
+      }
+    }
+    if (threadIdx.x == 0) {
+      int na = nact;
+      offsets[E] = total;
+      if (has_shared)
+        for (int t0 = 0; t0 < T; t0 += shared_piece) {
+          act[na] = E;
+          act[act_stride + na] = total + t0;
+          act[2 * act_stride + na] = min(shared_piece, T - t0);
+          ++na;
+        }
+      *n_active = na;
+    }
   }
   __syncthreads();
   // stable scatter
@@ -249,7 +282,8 @@ __global__ __launch_bounds__(512) void k_group(const int *__restrict__ ids, int 
 
 size_t group_lds_bytes(int64_t T, int64_t E) {
   const int64_t nchunks = (T + 63) / 64;
-  return (size_t)(8 * E * 8 + E * 4 + ((nchunks * E * 2 + 7) & ~(int64_t)7));
+  // masks [8][E] u64, off [E] int, tab [nchunks][E] u16 (padded to ints), scan [2][512] int
+  return (size_t)(8 * E * 8 + E * 4 + ((nchunks * E + 1) / 2) * 4 + 2 * 512 * 4);
 }
 
 // ---- grouped expert GEMV -----------------------------------------------------------------------
@@ -495,6 +529,10 @@ int launch_moe_routing(const MoePlan &p, const float *router_w, const float *x, 
                      k, s.renormalize, (float *)(ws + p.off_logits), (int *)(ws + p.off_ids),
                      (float *)(ws + p.off_wts));
   const size_t glds = group_lds_bytes(s.tokens, s.n_experts);
+  if (glds > 65536 &&
+      hipFuncSetAttribute((const void *)k_group, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)glds) != hipSuccess)
+    return -2;
   hipLaunchKernelGGL(k_group, dim3(1), dim3(512), glds, st, (const int *)(ws + p.off_ids), T, k, E,
                      s.has_shared, p.act_stride, p.shared_piece, (int *)(ws + p.off_counts), (int *)(ws + p.off_offsets),
                      (int *)(ws + p.off_pairs), (int *)(ws + p.off_inv), (int *)(ws + p.off_act),

@@ -208,3 +208,12 @@ def test_moe_stages_equal_one_call(path):
     moe(x, out=y, ws=ws, stages=tq.MOE_ROUTE | tq.MOE_EXPERTS)
     y2 = moe(x, ws=ws, stages=tq.MOE_COMBINE)
     assert np.array_equal(host(y2), y_all)
+
+
+def test_moe_grouping_many_tokens_many_experts():
+    """T = 8192 tokens, E = 256, k = 8: 65536 pairs through the grouping kernel (its LDS tables
+    exceed 64 KB here), routing checked bitwise, output on sampled tokens (fp32 path)."""
+    shape = dict(hidden=256, ffn=256, n_experts=256, shared=True)
+    layer = synth.moe_layer(shape, "q4_k", seed=208, tag="many")
+    x = synth.normal_f32(synth.rng(208, "x"), (8192, 256))
+    check_moe("q4_k", shape, layer, x, 8, tokens=[0, 4095, 8191], path=tq.PATH_F32)
