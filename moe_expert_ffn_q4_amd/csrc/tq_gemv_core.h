@@ -577,27 +577,38 @@ __device__ __forceinline__ void kl_load_rows(const KlMap &m, int r0, int boff, i
 __device__ __forceinline__ float kl_group_dot(const u32x4 (&v)[3], const float (&xv)[64],
                                               float sx_lo, float sx_hi, const Q4kField &f0,
                                               const Q4kField &f1, float unit_inv) {
+  (void)sx_lo;
+  (void)sx_hi;
+  (void)unit_inv;
   const uint32_t h0 = v[0].x, s0 = v[0].y, s1 = v[0].z, s2 = v[0].w;
-  const float d = half_bits_to_float(h0) * unit_inv, dmin = half_bits_to_float(h0 >> 16);
+  // quants as fp16 subnormals: the nibble of bits 0-3 (16-19) of a word read as binary16 is
+  // exactly q * 2^-24, that of bits 4-7 (20-23) exactly 16 q * 2^-24; the FMAs take the halves
+  // as fp16 operands (v_fma_mix_f32), so a word yields two weights for one AND
+  const float d = half_bits_to_float(h0) * 0x1p24f, dmin = half_bits_to_float(h0 >> 16);
   float sc_lo, m_lo, sc_hi, m_hi;
   q4k_scale_min_at(s0, s1, s2, f0, sc_lo, m_lo);
   q4k_scale_min_at(s0, s1, s2, f1, sc_hi, m_hi);
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   float dl = 0.f, dh = 0.f;
 #pragma unroll
   for (int dw = 0; dw < 8; ++dw) {
     const uint32_t wq = dword_of(v[1 + (dw >> 2)], dw & 3);
-    const uint32_t lo = wq & 0x0F0F0F0Fu, hi = (wq >> 4) & 0x0F0F0F0Fu;
-    float f[4];
-    nibbles_to_float<false>(lo, f[0], f[1]);
-    nibbles_to_float<true>(lo, f[2], f[3]);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) dl = __builtin_fmaf(f[e], xv[4 * dw + e], dl);
-    nibbles_to_float<false>(hi, f[0], f[1]);
-    nibbles_to_float<true>(hi, f[2], f[3]);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) dh = __builtin_fmaf(f[e], xv[32 + 4 * dw + e], dh);
+    const uint32_t w8 = wq >> 8;
+    const h2 l02 = __builtin_bit_cast(h2, opaque(wq & 0x000F000Fu));
+    const h2 l13 = __builtin_bit_cast(h2, opaque(w8 & 0x000F000Fu));
+    const h2 u02 = __builtin_bit_cast(h2, opaque(wq & 0x00F000F0u));
+    const h2 u13 = __builtin_bit_cast(h2, opaque(w8 & 0x00F000F0u));
+    const float *xl = xv + 4 * dw, *xh = xv + 32 + 4 * dw;
+    dl = __builtin_fmaf((float)l02[0], xl[0], dl);
+    dl = __builtin_fmaf((float)l13[0], xl[1], dl);
+    dl = __builtin_fmaf((float)l02[1], xl[2], dl);
+    dl = __builtin_fmaf((float)l13[1], xl[3], dl);
+    dh = __builtin_fmaf((float)u02[0], xh[0], dh);
+    dh = __builtin_fmaf((float)u13[0], xh[1], dh);
+    dh = __builtin_fmaf((float)u02[1], xh[2], dh);
+    dh = __builtin_fmaf((float)u13[1], xh[3], dh);
   }
-  const float pos = __builtin_fmaf(sc_lo, dl, sc_hi * dh) * d;
+  const float pos = __builtin_fmaf(sc_lo, dl, sc_hi * dh * 0.0625f) * d;
   return __builtin_fmaf(-dmin, __builtin_fmaf(m_lo, sx_lo, m_hi * sx_hi), pos);
 }
 
