@@ -329,27 +329,30 @@ __device__ __forceinline__ void q4k_group_load(const uint8_t *row, int it, u32x4
   v[2] = *(p + 2 + 2 * (it & 3));
 }
 
-// Q4_K with several tokens: stream 64-weight groups (header + 32 quant bytes each) in a loop
-// that is not unrolled, so the compiler keeps only one group's converted quants and one token's
-// activations live at a time. The next group's three 16-byte loads are issued before this
-// group's math; the 16-byte header is re-read for each of the four groups of a block (an L1 hit).
-template <int NT>
-__device__ __forceinline__ void stream_q4k_groups(const uint8_t *row, int u0, int u1,
-                                                  const u32x4 (&first)[3],
-                                                  const float *const (&x)[NT],
-                                                  const float *const (&gsum)[NT], float (&acc)[NT]) {
-  const int it1 = 4 * u1;
-  auto load = [&](int it, u32x4 (&v)[3]) { q4k_group_load(row, it, v); };
-  u32x4 cur[3], nxt[3];
+// Q4_K with several tokens: the lane loads its row's whole 144-byte block at once (nine 16-byte
+// loads, the next block's issued before this block's math), so every cache line of the block is
+// used while it is in flight; rows of one wave lie far apart, and loading a block in pieces over
+// time would let the lines leave L2 between the pieces. The block's four 64-weight groups are
+// then processed one after another (a scheduling barrier between them keeps only one group's
+// converted quants live).
+struct Q4kBlock {
+  u32x4 v[9];  // header, then 128 quant bytes
+};
+
+__device__ __forceinline__ void q4k_block_load(const uint8_t *row, int u, Q4kBlock &b) {
+  const u32x4 *p = reinterpret_cast<const u32x4 *>(row + (size_t)u * 144);
 #pragma unroll
-  for (int i = 0; i < 3; ++i) cur[i] = first[i];
-#pragma unroll 1
-  for (int it = 4 * u0; it < it1; ++it) {
-    if (it + 1 < it1) load(it + 1, nxt);
-    const int u = it >> 2, c = it & 3;
-    const uint32_t h0 = cur[0].x, s0 = cur[0].y, s1 = cur[0].z, s2 = cur[0].w;
-    const float d = half_bits_to_float(h0), dmin = half_bits_to_float(h0 >> 16);
-    // scale and min of sub-blocks j0 = 2c (low nibbles) and j1 = 2c + 1 (high nibbles)
+  for (int i = 0; i < 9; ++i) b.v[i] = p[i];
+}
+
+template <int NT>
+__device__ __forceinline__ void q4k_block_dot(const Q4kBlock &b, int u,
+                                              const float *const (&x)[NT],
+                                              const float *const (&gsum)[NT], float (&acc)[NT]) {
+  const uint32_t h0 = b.v[0].x, s0 = b.v[0].y, s1 = b.v[0].z, s2 = b.v[0].w;
+  const float dq = half_bits_to_float(h0) / nibble_fp8_unit(), dmin = half_bits_to_float(h0 >> 16);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
     const int j0 = 2 * c, j1 = 2 * c + 1;
     uint32_t sc0, m0, sc1, m1;
     if (c < 2) {
@@ -358,19 +361,18 @@ __device__ __forceinline__ void stream_q4k_groups(const uint8_t *row, int u0, in
       sc1 = (s0 >> (8 * j1)) & 63u;
       m1 = (s1 >> (8 * j1)) & 63u;
     } else {
-      const int a = j0 - 4, b = j1 - 4;
+      const int a = j0 - 4, bb = j1 - 4;
       sc0 = ((s2 >> (8 * a)) & 15u) | (((s0 >> (8 * a + 6)) & 3u) << 4);
       m0 = ((s2 >> (8 * a + 4)) & 15u) | (((s1 >> (8 * a + 6)) & 3u) << 4);
-      sc1 = ((s2 >> (8 * b)) & 15u) | (((s0 >> (8 * b + 6)) & 3u) << 4);
-      m1 = ((s2 >> (8 * b + 4)) & 15u) | (((s1 >> (8 * b + 6)) & 3u) << 4);
+      sc1 = ((s2 >> (8 * bb)) & 15u) | (((s0 >> (8 * bb + 6)) & 3u) << 4);
+      m1 = ((s2 >> (8 * bb + 4)) & 15u) | (((s1 >> (8 * bb + 6)) & 3u) << 4);
     }
-    const float dq = d / nibble_fp8_unit();
     const float dsc0 = dq * (float)sc0, dsc1 = dq * (float)sc1;
     const float dm0 = dmin * (float)m0, dm1 = dmin * (float)m1;
     float fl[32], fh[32];
 #pragma unroll
     for (int dw = 0; dw < 8; ++dw) {
-      const uint32_t w = dword_of(cur[1 + (dw >> 2)], dw & 3);
+      const uint32_t w = dword_of(b.v[1 + 2 * c + (dw >> 2)], dw & 3);
       const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
       nibbles_to_float<false>(lo, fl[4 * dw], fl[4 * dw + 1]);
       nibbles_to_float<true>(lo, fl[4 * dw + 2], fl[4 * dw + 3]);
@@ -391,8 +393,21 @@ __device__ __forceinline__ void stream_q4k_groups(const uint8_t *row, int u0, in
       a = __builtin_fmaf(-dm0, g[0], a);
       acc[t] = __builtin_fmaf(-dm1, g[1], a);
     }
-#pragma unroll
-    for (int i = 0; i < 3; ++i) cur[i] = nxt[i];
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void stream_q4k_groups(const uint8_t *row, int u0, int u1,
+                                                  const Q4kBlock &first,
+                                                  const float *const (&x)[NT],
+                                                  const float *const (&gsum)[NT], float (&acc)[NT]) {
+  Q4kBlock cur = first, nxt;
+#pragma unroll 1
+  for (int u = u0; u < u1; ++u) {
+    if (u + 1 < u1) q4k_block_load(row, u + 1, nxt);
+    q4k_block_dot<NT>(cur, u, x, gsum, acc);
+    cur = nxt;
   }
 }
 
@@ -441,9 +456,9 @@ __device__ __forceinline__ void gemv_tile(const uint8_t *__restrict__ w, int64_t
   // the first weights of this wave are requested before the group sums are formed
   constexpr bool kGroups = FMT == FMT_Q4_K && NT > 1;
   Unit<FMT> first;
-  u32x4 gfirst[3];
+  Q4kBlock gfirst;
   if constexpr (kGroups) {
-    if (u0 < u1) q4k_group_load(wrow, 4 * u0, gfirst);
+    if (u0 < u1) q4k_block_load(wrow, u0, gfirst);
   } else {
     if (u0 < u1) load_unit(first, wrow, u0);
   }
