@@ -383,10 +383,16 @@ def moe_bench(args, torch, tq, synth):
     else:
         stage_bytes = active * eb + 4 * T * H * 2
         achieved = stage_bytes / stage_s / 1e9
+        if T > 1 and os.environ.get("TQ_MOE_QMM", "1") != "0":
+            kern = ("tq_moe_ffn expert stage: k_qmm gate/up+SwiGLU and down on the fp16 matrix "
+                    "cores, fp32-accurate (with the row splits and the chunk table)")
+        elif T == 1:
+            kern = "tq_moe_ffn expert stage: k_moe_kl gate/up+SwiGLU and down"
+        else:
+            kern = "tq_moe_ffn expert stage: k_moe_gemv gate/up, SwiGLU, down"
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "tq_moe_ffn expert stage: k_moe_gemv gate/up, SwiGLU, down",
-                "avg_launch_us": round(stage_s * 1e6, 1)}
+                "kernel": kern, "avg_launch_us": round(stage_s * 1e6, 1)}
         dtype = "q4_k weights, f32 activations and accumulation"
     out = {
         "metric": METRIC, "value": round(T * args.steps / elapsed, 2), "unit": "tokens/s",

@@ -219,7 +219,6 @@ __global__ __launch_bounds__(512) void k_gemv(const uint8_t *__restrict__ w, int
 // Batch-1 Q4_K GEMV, lanes along k (see tq_gemv_core.h). Workgroup = ceil(nblk / 16) waves
 // covering all of k; it computes rows [blockIdx.x * rows_per_wg, ...) R at a time, loading the
 // next R rows while it computes the current ones.
-__device__ __forceinline__ float silu_mul(float g, float u) { return g * u / (1.f + expf(-g)); }
 
 template <int R>
 __device__ __forceinline__ void kl_rows(const u32x4 (&v)[R][3], const float (&xv)[64], float sx_lo,

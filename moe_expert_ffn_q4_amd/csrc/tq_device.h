@@ -57,6 +57,9 @@ __device__ __forceinline__ uint16_t float_to_bf16_rne(float f) {
   return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
 }
 
+// SwiGLU of one gate/up pair: silu(g) * u = g * u / (1 + e^-g).
+__device__ __forceinline__ float silu_mul(float g, float u) { return g * u / (1.f + expf(-g)); }
+
 __device__ __forceinline__ int wave_index() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }

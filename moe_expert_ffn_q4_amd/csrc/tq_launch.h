@@ -6,6 +6,7 @@
 
 namespace tq {
 
+inline int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
 inline int64_t fmt_block_weights(int fmt) { return fmt == 1 ? 256 : fmt == 2 ? 256 : fmt == 3 ? 32 : 0; }
 inline int64_t fmt_block_bytes(int fmt) { return fmt == 1 ? 144 : fmt == 2 ? 210 : fmt == 3 ? 34 : 0; }
 

@@ -25,6 +25,8 @@ struct MoePlan {
   int max_active;  // upper bound of active experts (including the shared one)
   int nt;          // token rows per tile of the grouped fp32 GEMV (1, 2, 4 or 8)
   int klane;       // one-token Q4_K step: the lanes-along-k kernels (SwiGLU fused)
+  int qmm;         // Q4_K, 2+ tokens: the fp32-accurate fp16 matrix-core kernels
+  int qmm_nt;      // their token tiles of 16 per chunk (1 or 2)
   int shared_piece;  // positions per active-list entry of the shared expert
   int act_stride;    // stride of the three arrays of the active-expert list
   int rtiles, hsplit, hpk;
@@ -32,7 +34,8 @@ struct MoePlan {
   int d_rg, d_ks, d_upk, d_waves, d_upw;
   int64_t off_rpart, off_logits, off_ids, off_wts, off_counts, off_offsets, off_pairs, off_inv,
       off_act, off_nact, off_gu, off_h, off_o, off_stage;
-  int64_t off_xb, off_hb, off_chunks, off_nchunks;  // matrix-core path only
+  int64_t off_xb, off_hb, off_chunks, off_nchunks;  // matrix-core paths only
+  int64_t off_xsplit, off_hsplit;                    // fp16 split rows (qmm)
   int max_chunks;
   int64_t stage_stride;
   int64_t bytes;

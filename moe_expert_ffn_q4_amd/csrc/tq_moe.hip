@@ -18,6 +18,7 @@
 #include "tq_launch.h"
 #include "tq_moe.h"
 #include "tq_prefill.h"
+#include "tq_qmm.h"
 
 namespace tq {
 
@@ -408,7 +409,6 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float *__restrict__ o
 
 // ---- host side ---------------------------------------------------------------------------------
 
-static int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
 
 static int clampi(int v, int lo, int hi) { return v < lo ? lo : v > hi ? hi : v; }
 
@@ -419,7 +419,15 @@ MoePlan plan_moe(const MoeShape &s) {
   p.P = T * k + (s.has_shared ? T : 0);
   // the shared expert's T positions as entries of at most shared_piece: 16 on the fp32 grouped
   // path (two tiles of 8), all T elsewhere (one token, or the matrix-core chunk table)
-  p.shared_piece = (int)(!s.mfma && T > 16 ? 16 : T);
+  // Q4_K steps of two or more tokens (routed experts in device memory): the fp32-accurate fp16
+  // matrix-core kernels, which read each active expert's weights once per chunk of 16 or 32
+  // positions instead of running VALU dot products per token
+  p.qmm = !s.mfma && s.type == FMT_Q4_K && T > 1 && !s.experts_on_host &&
+          qmm_shape_ok(s.hidden, s.ffn);
+  if (const char *v = getenv("TQ_MOE_QMM")) p.qmm = p.qmm && atoi(v) != 0;  // 0: grouped GEMV
+  p.qmm_nt = (T * k + E - 1) / E > 12 ? 2 : 1;
+  if (const char *v = getenv("TQ_QMM_NT")) p.qmm_nt = atoi(v) == 2 ? 2 : 1;
+  p.shared_piece = (int)(!s.mfma && !p.qmm && T > 16 ? 16 : T);
   const int nsh = s.has_shared ? (int)((T + p.shared_piece - 1) / p.shared_piece) : 0;
   p.max_active = (int)((E < T * k ? E : T * k) + nsh);
   p.act_stride = (int)E + (nsh > 1 ? nsh : 1);
@@ -477,6 +485,14 @@ MoePlan plan_moe(const MoeShape &s) {
     p.max_chunks = prefill_max_chunks(p.P, p.max_active);
     p.off_xb = take(T * s.hidden * 2);
     p.off_hb = take(p.P * s.ffn * 2);
+    p.off_chunks = take((int64_t)3 * p.max_chunks * 4);
+    p.off_nchunks = take(4);
+  } else if (p.qmm) {
+    p.d_ks = 1;
+    p.max_chunks = max_chunks_for(p.P, p.max_active, qmm_chunk_rows(p.qmm_nt));
+    p.off_xsplit = take((int64_t)split_rows_bytes(T, s.hidden));
+    p.off_hsplit = take((int64_t)split_rows_bytes(p.P, s.ffn));
+    p.off_h = take(p.P * s.ffn * 4);
     p.off_chunks = take((int64_t)3 * p.max_chunks * 4);
     p.off_nchunks = take(4);
   } else {
@@ -595,6 +611,27 @@ int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
     for (int m = 0; m < 3; ++m) b.stage_off[m] = a.stage_off[m];
     return launch_prefill(p.max_chunks, b, x, T, s.hidden, s.ffn, (uint16_t *)(ws + p.off_xb),
                           (uint16_t *)(ws + p.off_hb), (float *)(ws + p.off_o), st);
+  }
+  if (p.qmm) {
+    if (range != nullptr) return -2;  // whole steps only (routed experts in device memory)
+    QmmArgs q{};
+    q.experts = experts_dev;
+    q.shared = shared;
+    q.staging = staging;
+    q.stage_stride = p.stage_stride;
+    for (int m = 0; m < 3; ++m) q.stage_off[m] = a.stage_off[m];
+    q.act = a.act;
+    q.n_active = a.n_active;
+    q.act_stride = p.act_stride;
+    q.chunks = (const int *)(ws + p.off_chunks);
+    q.n_chunks = (const int *)(ws + p.off_nchunks);
+    q.pairs = a.pairs;
+    q.E = E;
+    q.topk = k;
+    q.Tk = T * k;
+    return launch_qmm_moe(q, p.qmm_nt, p.max_chunks, x, T, p.P, s.hidden, s.ffn,
+                          ws + p.off_xsplit, ws + p.off_hsplit, (float *)(ws + p.off_h),
+                          (float *)(ws + p.off_o), st);
   }
   if (p.klane) {
     MoeKlArgs g{};

@@ -29,8 +29,15 @@ struct PrefillArgs {
   int ntiles;                    // workgroup tiles per chunk
 };
 
-// Upper bound of the chunk count for P positions over at most max_active experts.
+// Upper bound of the chunk count for P positions over at most max_active experts, cut into chunks
+// of at most chunk_rows (prefill_max_chunks: the matrix-core prefill's chunk size).
+int max_chunks_for(int64_t positions, int max_active, int chunk_rows);
 int prefill_max_chunks(int64_t positions, int max_active);
+
+// The active experts' position ranges cut into chunks of at most chunk_rows rows, near-equal in
+// size: chunks[3c .. 3c+2] = (active slot, first position, rows), *n_chunks = their count.
+void launch_chunk_table(const int *act, const int *n_active, int act_stride, int chunk_rows,
+                        int max_chunks, int *chunks, int *n_chunks, hipStream_t st);
 
 // x -> bf16, chunk table, gate/up with SwiGLU into h, down into o (P rows each).
 int launch_prefill(int max_chunks, PrefillArgs a, const float *x, int64_t tokens, int64_t hidden,

@@ -28,13 +28,11 @@
 
 #include "tq_device.h"
 #include "tq_gemv_core.h"
+#include "tq_mfma.h"
 #include "tq_moe.h"
 #include "tq_prefill.h"
 
 namespace tq {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kChunk = 160;           // token rows per chunk (5 tiles of 32)
 constexpr int kRowStride = 256;       // LDS bytes per token row: 128 bf16 of one step
@@ -55,11 +53,12 @@ __global__ __launch_bounds__(256) void k_to_bf16(const float *__restrict__ x, in
 
 // ---- chunk table --------------------------------------------------------------------------------
 // chunks[3c .. 3c+2] = (active slot, first position, rows); an expert with cnt rows is cut into
-// ceil(cnt / kChunk) chunks of near-equal size, chunks in slot order. One workgroup of 256
+// ceil(cnt / chunk_rows) chunks of near-equal size, chunks in slot order. One workgroup of 256
 // threads, a thread per slot, an LDS prefix sum over each batch of 256 slots.
 __global__ __launch_bounds__(256) void k_chunk_table(const int *__restrict__ act,
                                                      const int *__restrict__ n_active, int act_stride,
-                                                     int max_chunks, int *__restrict__ chunks,
+                                                     int chunk_rows, int max_chunks,
+                                                     int *__restrict__ chunks,
                                                      int *__restrict__ n_chunks) {
   __shared__ int scan[256];
   const int na = *n_active;
@@ -70,7 +69,7 @@ __global__ __launch_bounds__(256) void k_chunk_table(const int *__restrict__ act
     if (s < na) {
       p0 = act[act_stride + s];
       cnt = act[2 * act_stride + s];
-      parts = (cnt + kChunk - 1) / kChunk;
+      parts = (cnt + chunk_rows - 1) / chunk_rows;
     }
     scan[threadIdx.x] = parts;
     __syncthreads();
@@ -101,12 +100,6 @@ __global__ __launch_bounds__(256) void k_chunk_table(const int *__restrict__ act
 
 // ---- the grouped product ------------------------------------------------------------------------
 
-// Loads through the global address space (the blob pointers come from a device table, so the
-// compiler would otherwise issue generic loads, which it cannot count precisely).
-typedef const u32x4 __attribute__((address_space(1))) *gu32x4;
-
-__device__ __forceinline__ u32x4 gload(const void *p) { return *(gu32x4)p; }
-
 // Raw bytes of one Q4_K row for one step: the block header (d, dmin, 12 scale bytes) and the
 // lane's 32 quant bytes.
 struct RawRow {
@@ -118,12 +111,6 @@ __device__ __forceinline__ void load_raw(const uint8_t *row, int kb, int c, RawR
   r.head = gload(b);
   r.q0 = gload(b + 16 + 32 * c);
   r.q1 = gload(b + 32 + 32 * c);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 v = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Scale and offset of the lane's two sub-blocks (2c: low nibbles, 2c+1: high nibbles) of the
@@ -169,39 +156,6 @@ __device__ __forceinline__ bf16x8 dequant_step(const RawRow &r, const GroupScale
   v.w = pack_bf16(f[6], f[7]);
   return __builtin_bit_cast(bf16x8, v);
 }
-
-// s_waitcnt that waits until at most n vector-memory operations of this wave are outstanding
-// (expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-// Byte address of a __shared__ location in the LDS aperture.
-__device__ __forceinline__ uint32_t lds_address(const void *p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
-
-// 16 bytes from global memory straight into LDS: lane l's bytes land at lds_base + 16 l
-// (lds_base must be the same for the whole wave).
-__device__ __forceinline__ void load_lds16(const void *g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(lds_base)
-               : "memory", "m0");
-}
-
-// Workgroup barrier once at most N vector-memory operations and no LDS operation of this wave
-// are outstanding. Written as one asm statement with a memory clobber: the compiler keeps memory
-// accesses on their side of it and adds no waits of its own.
-template <int N>
-__device__ __forceinline__ void barrier_after_vmem() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "i"(N) : "memory");
-}
-
-__device__ __forceinline__ float silu_mul(float g, float u) { return g * u / (1.f + expf(-g)); }
 
 // Token staging. A step's token tile (rows of 128 bf16: 16 pieces of 8 k) goes straight from
 // global memory to LDS (global_load_lds, 16 bytes per lane: lane l of a wave instruction writes
@@ -339,6 +293,14 @@ __device__ __forceinline__ void prefill_tiles(const PrefillArgs &a, uint8_t *__r
   }
   if (st < steps) step(st, tok0, tok2, raw[0], raw[2]);
   if (st + 1 < steps) step(st + 1, tok1, tok0, raw[1], raw[0]);
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      keep_alive(raw[j][q].head);
+      keep_alive(raw[j][q].q0);
+      keep_alive(raw[j][q].q1);
+    }
   wait_vmem<0>();  // the surplus loads of the last steps land before the workgroup ends
 
   // epilogue: lane holds rows 8*(i/4) + 4*kg + i%4 of token column lrow of each tile
@@ -431,8 +393,18 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
 
 // ---- host side ----------------------------------------------------------------------------------
 
+int max_chunks_for(int64_t positions, int max_active, int chunk_rows) {
+  return (int)((positions + (int64_t)(chunk_rows - 1) * max_active) / chunk_rows + 1);
+}
+
 int prefill_max_chunks(int64_t positions, int max_active) {
-  return (int)((positions + (int64_t)(kChunk - 1) * max_active) / kChunk + 1);
+  return max_chunks_for(positions, max_active, kChunk);
+}
+
+void launch_chunk_table(const int *act, const int *n_active, int act_stride, int chunk_rows,
+                        int max_chunks, int *chunks, int *n_chunks, hipStream_t st) {
+  hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(256), 0, st, act, n_active, act_stride,
+                     chunk_rows, max_chunks, chunks, n_chunks);
 }
 
 int launch_prefill(int max_chunks, PrefillArgs a, const float *x, int64_t tokens, int64_t hidden,
@@ -443,8 +415,8 @@ int launch_prefill(int max_chunks, PrefillArgs a, const float *x, int64_t tokens
     if (blocks > 8192) blocks = 8192;
     hipLaunchKernelGGL(k_to_bf16, dim3((unsigned)blocks), dim3(256), 0, st, x, n, (uint32_t *)xb);
   }
-  hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(256), 0, st, a.act, a.n_active, a.act_stride,
-                     max_chunks, (int *)a.chunks, (int *)a.n_chunks);
+  launch_chunk_table(a.act, a.n_active, a.act_stride, kChunk, max_chunks, (int *)a.chunks,
+                     (int *)a.n_chunks, st);
   const int groups = (max_chunks + 7) / 8;
   // gate / up
   a.kblocks = (int)(hidden / 256);

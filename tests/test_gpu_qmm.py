@@ -1,0 +1,95 @@
+"""GPU parity of the fp32-accurate fp16 matrix-core expert kernels (Q4_K MoE steps of 2 or more
+tokens per call take them by default on the fp32 path).
+
+Bars, as for every fp32-accumulated product: routing and grouping bitwise, y within
+1e-3 * sum|products| + 1e-5 of the fp64 oracle. On top of that, the kernels are checked to be at
+fp32 level -- far inside that bound -- and against the grouped fp32 GEMV they replace.
+"""
+import numpy as np
+import pytest
+
+import synth
+from tests.gpu_util import dev, host
+from tests.test_gpu_moe import _case, _layer_to_device, _run, check_moe
+
+pytestmark = pytest.mark.gpu
+
+tq = pytest.importorskip("moe_expert_ffn_q4_amd")
+
+
+def _tile_env(monkeypatch, nt):
+    monkeypatch.setenv("TQ_QMM_NT", str(nt))
+    monkeypatch.delenv("TQ_MOE_QMM", raising=False)
+
+
+# Few experts and top-1 or top-2, so that per-expert counts land on both sides of the chunk
+# sizes (16 and 32 positions) and chunks split into near-equal parts.
+BOUNDARY = [
+    (dict(hidden=512, ffn=768, n_experts=2, shared=False), 1, [2, 15, 16, 17, 31, 32, 33, 40, 70]),
+    (dict(hidden=768, ffn=512, n_experts=4, shared=True), 2, [3, 16, 33, 64, 97]),
+]
+
+
+@pytest.mark.parametrize("nt", [1, 2])
+@pytest.mark.parametrize("shape,k,Ts", BOUNDARY, ids=["E2k1", "E4k2-shared"])
+def test_qmm_chunk_boundaries(monkeypatch, nt, shape, k, Ts):
+    _tile_env(monkeypatch, nt)
+    layer = synth.moe_layer(shape, "q4_k", seed=401, tag=f"qmm-{shape['n_experts']}")
+    moe = None
+    for T in Ts:
+        _case("qmm-boundary", nt, shape, k, T)
+        x = synth.normal_f32(synth.rng(401, "x", T, nt), (T, shape["hidden"]))
+        moe, y, (worst, l2) = check_moe("q4_k", shape, layer, x, k, moe=moe)
+        # fp32 level: the largest error stays far below the 1e-3 bound
+        assert worst < 0.05, f"T={T}: worst error / bound {worst}"
+        y2, _ = _run(moe, x, shape["n_experts"], k)
+        assert np.array_equal(y, y2), "not deterministic"
+
+
+def test_qmm_agrees_with_grouped_gemv(monkeypatch):
+    """The matrix-core kernels and the grouped fp32 GEMV both meet the bar; their difference is
+    fp32 rounding order only (relative L2 difference at the 1e-6 level)."""
+    shape, k, T = dict(hidden=1024, ffn=1536, n_experts=8, shared=True), 2, 48
+    layer = synth.moe_layer(shape, "q4_k", seed=402, tag="qmm-vs-gemv")
+    x = synth.normal_f32(synth.rng(402, "x"), (T, shape["hidden"]))
+    _tile_env(monkeypatch, 2)
+    _, y_q, (wq, lq) = check_moe("q4_k", shape, layer, x, k)
+    monkeypatch.setenv("TQ_MOE_QMM", "0")
+    _, y_g, (wg, lg) = check_moe("q4_k", shape, layer, x, k)
+    print(f"qmm worst {wq:.3g} l2 {lq:.3g}; grouped GEMV worst {wg:.3g} l2 {lg:.3g}")
+    d = float(np.linalg.norm(y_q - y_g) / np.linalg.norm(y_g))
+    assert d < 1e-5, d
+    assert wq < 0.05 and lq < 1e-5
+
+
+def test_qmm_rows_of_any_scale(monkeypatch):
+    """Each activation row is rescaled by its own power of two: rows of magnitude 1e-12 and 1e12,
+    an all-zero row and a row with one huge element keep fp32 accuracy."""
+    _tile_env(monkeypatch, 1)
+    shape, k, T = dict(hidden=512, ffn=512, n_experts=4, shared=True), 2, 12
+    layer = synth.moe_layer(shape, "q4_k", seed=403, tag="qmm-scale")
+    x = synth.normal_f32(synth.rng(403, "x"), (T, shape["hidden"]))
+    x[1] *= np.float32(1e-12)
+    x[2] *= np.float32(1e12)
+    x[3] = 0.0
+    x[4, 7] = np.float32(3e4)
+    x[5] *= np.float32(2.0 ** -100)
+    _case("qmm-scale", T)
+    _, y, (worst, _) = check_moe("q4_k", shape, layer, x, k)
+    assert worst < 0.05, worst
+    assert np.all(np.isfinite(y))
+
+
+def test_qmm_workspace_sizes_differ_by_tile(monkeypatch):
+    """The chunk table grows when chunks hold 16 rather than 32 positions (fp32 path forced: at
+    100 routed tokens per expert the automatic choice is the bf16 prefill path)."""
+    shape = dict(hidden=512, ffn=512, n_experts=4, shared=False)
+    layer = synth.moe_layer(shape, "q4_k", seed=404, tag="qmm-ws")
+    _tile_env(monkeypatch, 1)
+    moe = _layer_to_device("q4_k", shape, layer, 2, path=tq.PATH_F32)
+    w1 = moe.workspace_bytes(200)
+    _tile_env(monkeypatch, 2)
+    w2 = moe.workspace_bytes(200)
+    assert w1 > w2 > 0
+    y = host(moe(dev(synth.normal_f32(synth.rng(404, "x"), (200, 512)))))
+    assert np.all(np.isfinite(y))
