@@ -199,6 +199,15 @@ def build_dense_model(tq, synth, torch, batch, seed):
     return layers
 
 
+def gemv_kernel_name(batch):
+    """The kernel that tq_gemv runs for this batch (with its workspace)."""
+    if batch != 1:
+        return "tq_gemv Q4_K (tq::k_gemv)"
+    if os.environ.get("TQ_GEMV_I8", "1") != "0":
+        return "tq_gemv Q4_K batch 1 (tq::k_gemv_i8, after tq::k_x_digits)"
+    return "tq_gemv Q4_K batch 1 (tq::k_gemv_kl)"
+
+
 def make_step(tq, torch, layers, batch, events=None, gemv_only=False):
     """One decode step through the C ABI. Per layer: q, k and v (input x) in one tq_gemv_multi
     launch, o (input: the attention stand-in a), gate and up (input x) with the SwiGLU between
@@ -565,8 +574,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "tq_gemv Q4_K batch 1 (tq::k_gemv_kl)" if args.batch == 1
-                               else "tq_gemv Q4_K (tq::k_gemv)",
+                     "kernel": gemv_kernel_name(args.batch),
                      "avg_launch_us": round(avg_launch_s * 1e6, 3)},
     }
     if args.calibrate_copy:

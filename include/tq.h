@@ -77,9 +77,12 @@ int tq_dequant(int type, const void *w, int64_t n, int64_t k, int out_type, void
  *   workspace  device scratch of at least tq_gemv_workspace_bytes(type, n, k, batch) bytes,
  *              256-byte aligned, zero-filled before its first use; every call leaves its first
  *              64 KiB (completion counters) zeroed again. It lets the k dimension be split across
- *              workgroups; the partial sums are added in a fixed order, so results stay
- *              deterministic. NULL or too small: no split (slower when n is small). Calls that
- *              run concurrently must not share a workspace.
+ *              workgroups (the partial sums are added in a fixed order, so results stay
+ *              deterministic), and for Q4_K at batch 1 it holds the activation digits of the
+ *              int8 matrix-core kernel (after the first 64 KiB). NULL or too small: no split and
+ *              no matrix-core kernel (slower; results still within the fp32 bar, though not
+ *              bitwise those of a call with the workspace). Calls that run concurrently must not
+ *              share a workspace.
  *   n >= 1, k >= block size with k % block == 0, 1 <= batch <= 4096. Weights are streamed once
  *   per group of up to 8 tokens.
  */
@@ -94,8 +97,10 @@ int tq_gemv(int type, const void *w, int64_t n, int64_t k, const float *x, int64
  *   w, n, y   host arrays of nparts entries: device blob w[p] ([n[p]][k], 16-byte aligned),
  *             rows n[p], device output y[p] ([batch][n[p]] fp32)
  *   x         device [batch][k] fp32, 16-byte aligned
- *   workspace as for tq_gemv, at least tq_gemv_multi_workspace_bytes(...) bytes.
- * Each y[p] is bitwise what tq_gemv(type, w[p], n[p], k, x, ...) gives.
+ *   workspace as for tq_gemv: tq_gemv_multi_workspace_bytes(...) bytes, or NULL / smaller
+ *             (slower kernels).
+ * Each y[p] is bitwise what tq_gemv(type, w[p], n[p], k, x, ...) gives with a workspace of the
+ * size each call asks for.
  */
 size_t tq_gemv_multi_workspace_bytes(int type, int nparts, const int64_t *n, int64_t k,
                                      int64_t batch);
@@ -110,8 +115,10 @@ int tq_gemv_multi(int type, int nparts, const void *const *w, const int64_t *n, 
  * one launch for Q4_K at batch 1 (gate and up rows interleaved inside the kernel); otherwise two
  * tq_gemv launches and
  * tq_swiglu through the workspace. w_gate, w_up [n][k]; x [batch][k] (16-byte aligned); h
- * [batch][n] fp32. workspace: tq_gemv_swiglu_workspace_bytes(type, n, k, batch) bytes (0 on the
- * one-launch path), 256-byte aligned. Bitwise equal to tq_gemv + tq_gemv + tq_swiglu.
+ * [batch][n] fp32. workspace: tq_gemv_swiglu_workspace_bytes(type, n, k, batch) bytes, 256-byte
+ * aligned; on the one-launch path it holds the activation digits of the int8 matrix-core kernel
+ * and may be NULL or smaller (the lanes-along-k kernel runs instead). Bitwise equal to tq_gemv +
+ * tq_gemv + tq_swiglu when each call gets the workspace it asks for.
  */
 size_t tq_gemv_swiglu_workspace_bytes(int type, int64_t n, int64_t k, int64_t batch);
 int tq_gemv_swiglu(int type, const void *w_gate, const void *w_up, int64_t n, int64_t k,

@@ -112,8 +112,6 @@ int tq_gemv_multi(int type, int nparts, const void *const *w, const int64_t *n, 
   }
   if (!aligned(x, 16) || !aligned(workspace, 256))
     return fail(TQ_EALIGN, "tq_gemv_multi: x 16-byte, workspace 256-byte alignment needed");
-  if (ws_bytes < tq::gemv_multi_workspace_bytes(type, nparts, n, k, batch))
-    return fail(TQ_ENOSPC, "tq_gemv_multi: workspace of %zu bytes too small", ws_bytes);
   return launched(tq::launch_gemv_multi(type, nparts, w, n, y, k, x, batch, workspace, ws_bytes,
                                         (hipStream_t)stream),
                   "tq_gemv_multi");
@@ -139,9 +137,10 @@ int tq_gemv_swiglu(int type, const void *w_gate, const void *w_up, int64_t n, in
       !aligned(workspace, 256))
     return fail(TQ_EALIGN, "tq_gemv_swiglu: w and x 16-byte, h 4-byte, workspace 256-byte "
                            "alignment needed");
+  // the one-launch path runs without a workspace too (the int8 kernel then gives way to the
+  // lanes-along-k one); the two-launch path keeps gate and up in it
   const bool fused = tq::gemv_swiglu_fused(type, k, x, batch);
-  if (ws_bytes < tq::gemv_swiglu_workspace_bytes(type, n, k, batch, fused) ||
-      (!fused && !workspace))
+  if (!fused && (ws_bytes < tq::gemv_swiglu_workspace_bytes(type, n, k, batch, false) || !workspace))
     return fail(TQ_ENOSPC, "tq_gemv_swiglu: workspace of %zu bytes too small", ws_bytes);
   return launched(tq::launch_gemv_swiglu(type, w_gate, w_up, n, k, x, batch, h, workspace,
                                          ws_bytes, (hipStream_t)stream),

@@ -1,5 +1,6 @@
 // tq_dense.hip -- dequantization, dense GEMV and SwiGLU kernels with their host launchers.
 #include "tq_gemv_core.h"
+#include "tq_gemv_i8.h"
 #include "tq_launch.h"
 #include "tq_moe.h"
 
@@ -124,11 +125,6 @@ struct GemvPlan {
   int rowgroups, ksplit, upk, waves, upw;
 };
 
-static int env_int(const char *name, int dflt) {
-  const char *v = getenv(name);
-  return v && *v ? atoi(v) : dflt;
-}
-
 GemvPlan plan_gemv(int64_t n, int64_t k, bool split_allowed) {
   static const int target_wg = env_int("TQ_GEMV_TARGET_WG", 1024);
   static const int max_waves = env_int("TQ_GEMV_MAX_WAVES", 4);
@@ -148,13 +144,26 @@ GemvPlan plan_gemv(int64_t n, int64_t k, bool split_allowed) {
 
 static constexpr size_t kCounterBytes = 65536;  // one counter per row group: n <= 1M rows
 
+// Workspace of the int8 matrix-core path: the activation digits, after the counter area.
+static size_t i8_workspace_bytes(int fmt, int64_t k, int64_t batch) {
+  return i8_gemv_ok(fmt, k, batch) ? kCounterBytes + i8_digits_bytes(1, k) : 0;
+}
+
+// The int8 path runs when its workspace is there and x is 16-byte aligned.
+static bool use_i8(int fmt, int64_t k, const float *x, int64_t batch, const void *ws,
+                   size_t ws_bytes) {
+  const size_t need = i8_workspace_bytes(fmt, k, batch);
+  return need && ws != nullptr && ws_bytes >= need && ((uintptr_t)x & 15) == 0;
+}
+
 size_t gemv_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t batch) {
-  (void)batch;
   if (!gemv_fast_shape(fmt, k)) return 0;
+  const size_t i8 = i8_workspace_bytes(fmt, k, batch);
   const GemvPlan p = plan_gemv(n, k, true);
-  if (p.ksplit == 1 || (size_t)p.rowgroups * 4 > kCounterBytes) return 0;
+  if (p.ksplit == 1 || (size_t)p.rowgroups * 4 > kCounterBytes) return i8;
   // counters, then partial sums for up to 8 tokens
-  return kCounterBytes + (size_t)p.rowgroups * p.ksplit * 8 * 64 * 4;
+  const size_t split = kCounterBytes + (size_t)p.rowgroups * p.ksplit * 8 * 64 * 4;
+  return split > i8 ? split : i8;
 }
 
 template <int FMT, int NT>
@@ -488,7 +497,8 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, in
                        fmt, wb, rb, (int)n, k, x, (int)batch, y);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
-  if (klane_ok(fmt, k, x, batch)) {
+  const bool i8 = use_i8(fmt, k, x, batch, ws, ws_bytes) && n < (1ll << 30);
+  if (i8 || klane_ok(fmt, k, x, batch)) {
     KlMap m{};
     m.w[0] = wb;
     m.y[0] = y;
@@ -496,6 +506,7 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, in
     m.nparts = 1;
     m.total = (int)n;
     m.row_bytes = rb;
+    if (i8) return launch_gemv_i8(m, k, x, (char *)ws + kCounterBytes, s);
     return launch_kl(m, k, x, s);
   }
   switch (fmt) {
@@ -520,7 +531,8 @@ int launch_gemv_multi(int fmt, int nparts, const void *const *w, const int64_t *
                       hipStream_t s) {
   int64_t total = 0;
   for (int p = 0; p < nparts; ++p) total += n[p];
-  if (klane_ok(fmt, k, x, batch) && nparts <= 4 && total < (1ll << 30)) {
+  const bool i8 = use_i8(fmt, k, x, batch, ws, ws_bytes);
+  if ((i8 || klane_ok(fmt, k, x, batch)) && nparts <= 4 && total < (1ll << 30)) {
     KlMap m{};
     for (int p = 0; p < nparts; ++p) {
       m.w[p] = (const uint8_t *)w[p];
@@ -530,6 +542,7 @@ int launch_gemv_multi(int fmt, int nparts, const void *const *w, const int64_t *
     m.nparts = nparts;
     m.total = (int)total;
     m.row_bytes = k / fmt_block_weights(fmt) * fmt_block_bytes(fmt);
+    if (i8) return launch_gemv_i8(m, k, x, (char *)ws + kCounterBytes, s);
     return launch_kl(m, k, x, s);
   }
   for (int p = 0; p < nparts; ++p) {  // one launch per matrix, in order on the stream
@@ -544,7 +557,7 @@ int launch_gemv_multi(int fmt, int nparts, const void *const *w, const int64_t *
 static int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
 size_t gemv_swiglu_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t batch, bool fused) {
-  if (fused) return 0;
+  if (fused) return i8_workspace_bytes(fmt, k, batch);
   return (size_t)align_up((int64_t)gemv_workspace_bytes(fmt, n, k, batch), 256) +
          (size_t)align_up(4 * batch * n, 256) * 2;
 }
@@ -553,7 +566,8 @@ int launch_gemv_swiglu(int fmt, const void *wg, const void *wu, int64_t n, int64
                        const float *x, int64_t batch, float *h, void *ws, size_t ws_bytes,
                        hipStream_t s) {
   const int64_t rb = k / fmt_block_weights(fmt) * fmt_block_bytes(fmt);
-  if (klane_ok(fmt, k, x, batch) && n < (1ll << 29)) {
+  const bool i8 = use_i8(fmt, k, x, batch, ws, ws_bytes);
+  if ((i8 || klane_ok(fmt, k, x, batch)) && n < (1ll << 29)) {
     KlMap m{};
     m.w[0] = (const uint8_t *)wg;
     m.w[1] = (const uint8_t *)wu;
@@ -563,6 +577,7 @@ int launch_gemv_swiglu(int fmt, const void *wg, const void *wu, int64_t n, int64
     m.total = (int)(2 * n);
     m.cum[1] = m.total;
     m.row_bytes = rb;
+    if (i8) return launch_gemv_i8(m, k, x, (char *)ws + kCounterBytes, s);
     return launch_kl(m, k, x, s);
   }
   const size_t gws = (size_t)align_up((int64_t)gemv_workspace_bytes(fmt, n, k, batch), 256);

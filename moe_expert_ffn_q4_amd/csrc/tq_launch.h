@@ -3,9 +3,16 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 namespace tq {
 
+// Integer tuning overrides from the environment (read once by each caller).
+inline int env_int(const char *name, int dflt) {
+  const char *v = getenv(name);
+  return v && *v ? atoi(v) : dflt;
+}
+inline int clampi(int v, int lo, int hi) { return v < lo ? lo : v > hi ? hi : v; }
 inline int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
 inline int64_t fmt_block_weights(int fmt) { return fmt == 1 ? 256 : fmt == 2 ? 256 : fmt == 3 ? 32 : 0; }
 inline int64_t fmt_block_bytes(int fmt) { return fmt == 1 ? 144 : fmt == 2 ? 210 : fmt == 3 ? 34 : 0; }

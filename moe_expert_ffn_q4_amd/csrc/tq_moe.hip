@@ -410,8 +410,6 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float *__restrict__ o
 // ---- host side ---------------------------------------------------------------------------------
 
 
-static int clampi(int v, int lo, int hi) { return v < lo ? lo : v > hi ? hi : v; }
-
 MoePlan plan_moe(const MoeShape &s) {
   MoePlan p;
   p.s = s;
