@@ -84,7 +84,10 @@ int tq_dequant(int type, const void *w, int64_t n, int64_t k, int out_type, void
  *              bitwise those of a call with the workspace). Calls that run concurrently must not
  *              share a workspace.
  *   n >= 1, k >= block size with k % block == 0, 1 <= batch <= 4096. Weights are streamed once
- *   per group of up to 8 tokens.
+ *   per group of up to 8 tokens; for Q4_K with 2..32 tokens (given the workspace) once for all of
+ *   them, on the fp16 matrix cores with exact operands (each activation row scaled by a power of
+ *   two and split into fp16 hi + lo, sc * q and the mins as exact fp16 integers), fp32
+ *   accumulation.
  */
 size_t tq_gemv_workspace_bytes(int type, int64_t n, int64_t k, int64_t batch);
 int tq_gemv(int type, const void *w, int64_t n, int64_t k, const float *x, int64_t batch,
@@ -93,7 +96,8 @@ int tq_gemv(int type, const void *w, int64_t n, int64_t k, const float *x, int64
 /*
  * tq_gemv_multi -- y_p = W_p x for nparts (1..4) matrices of one block type and the same k that
  * share the activations x (the q, k and v projections of a decode step read the same x), in one
- * launch where the lanes-along-k kernel applies (Q4_K, batch 1), else one launch per matrix.
+ * launch for Q4_K at batch 1..32 (given the workspace; at batch 1 also without), else one launch
+ * per matrix.
  *   w, n, y   host arrays of nparts entries: device blob w[p] ([n[p]][k], 16-byte aligned),
  *             rows n[p], device output y[p] ([batch][n[p]] fp32)
  *   x         device [batch][k] fp32, 16-byte aligned
@@ -112,8 +116,8 @@ int tq_gemv_multi(int type, int nparts, const void *const *w, const int64_t *n, 
  * tq_gemv_swiglu -- h[t][r] = silu(g) * u with g = (W_gate x_t)[r], u = (W_up x_t)[r] and
  * silu(z) = z / (1 + exp(-z)): the gate and up projections of a SwiGLU FFN and the gating
  * between them (the Llama-family feed-forward; the pages name the models, not the formula), in
- * one launch for Q4_K at batch 1 (gate and up rows interleaved inside the kernel); otherwise two
- * tq_gemv launches and
+ * one launch for Q4_K at batch 1 (gate and up rows interleaved inside the kernel) and at batch
+ * 2..32 given the workspace (gate and up tiles side by side); otherwise two tq_gemv launches and
  * tq_swiglu through the workspace. w_gate, w_up [n][k]; x [batch][k] (16-byte aligned); h
  * [batch][n] fp32. workspace: tq_gemv_swiglu_workspace_bytes(type, n, k, batch) bytes, 256-byte
  * aligned; on the one-launch path it holds the activation digits of the int8 matrix-core kernel

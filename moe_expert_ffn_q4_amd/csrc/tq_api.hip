@@ -140,7 +140,8 @@ int tq_gemv_swiglu(int type, const void *w_gate, const void *w_up, int64_t n, in
   // the one-launch path runs without a workspace too (the int8 kernel then gives way to the
   // lanes-along-k one); the two-launch path keeps gate and up in it
   const bool fused = tq::gemv_swiglu_fused(type, k, x, batch);
-  if (!fused && (ws_bytes < tq::gemv_swiglu_workspace_bytes(type, n, k, batch, false) || !workspace))
+  if (!fused && (ws_bytes < tq::gemv_swiglu_min_workspace_bytes(type, n, k, batch, false) ||
+                 !workspace))
     return fail(TQ_ENOSPC, "tq_gemv_swiglu: workspace of %zu bytes too small", ws_bytes);
   return launched(tq::launch_gemv_swiglu(type, w_gate, w_up, n, k, x, batch, h, workspace,
                                          ws_bytes, (hipStream_t)stream),

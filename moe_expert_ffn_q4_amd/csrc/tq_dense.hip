@@ -1,6 +1,7 @@
 // tq_dense.hip -- dequantization, dense GEMV and SwiGLU kernels with their host launchers.
 #include "tq_gemv_core.h"
 #include "tq_gemv_i8.h"
+#include "tq_qmm.h"
 #include "tq_launch.h"
 #include "tq_moe.h"
 
@@ -156,14 +157,45 @@ static bool use_i8(int fmt, int64_t k, const float *x, int64_t batch, const void
   return need && ws != nullptr && ws_bytes >= need && ((uintptr_t)x & 15) == 0;
 }
 
-size_t gemv_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t batch) {
+// Workspace of the fp16 matrix-core path for 2..32 tokens: counters, split x, slice sums.
+static size_t qmm_workspace_bytes(int fmt, int64_t rows, int64_t k, int64_t batch, bool swiglu) {
+  return qmm_dense_ok(fmt, k, batch) ? kCounterBytes + qmm_dense_bytes(rows, k, batch, swiglu) : 0;
+}
+
+static bool use_qmm(int fmt, int64_t rows, int64_t k, const float *x, int64_t batch,
+                    const void *ws, size_t ws_bytes, bool swiglu) {
+  const size_t need = qmm_workspace_bytes(fmt, rows, k, batch, swiglu);
+  return need && ws != nullptr && ws_bytes >= need && ((uintptr_t)x & 15) == 0 &&
+         rows < (1ll << 30);
+}
+
+// Counters and partial sums of the split-k GEMV (0 when it does not split).
+static size_t split_workspace_bytes(int fmt, int64_t n, int64_t k) {
   if (!gemv_fast_shape(fmt, k)) return 0;
-  const size_t i8 = i8_workspace_bytes(fmt, k, batch);
   const GemvPlan p = plan_gemv(n, k, true);
-  if (p.ksplit == 1 || (size_t)p.rowgroups * 4 > kCounterBytes) return i8;
+  if (p.ksplit == 1 || (size_t)p.rowgroups * 4 > kCounterBytes) return 0;
   // counters, then partial sums for up to 8 tokens
-  const size_t split = kCounterBytes + (size_t)p.rowgroups * p.ksplit * 8 * 64 * 4;
-  return split > i8 ? split : i8;
+  return kCounterBytes + (size_t)p.rowgroups * p.ksplit * 8 * 64 * 4;
+}
+
+static size_t max3(size_t a, size_t b, size_t c) { return a > b ? (a > c ? a : c) : (b > c ? b : c); }
+
+size_t gemv_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t batch) {
+  return max3(split_workspace_bytes(fmt, n, k), i8_workspace_bytes(fmt, k, batch),
+              qmm_workspace_bytes(fmt, n, k, batch, false));
+}
+
+static QmmDense dense_map(int nparts, const void *const *w, const int64_t *n, float *const *y,
+                          int64_t rb) {
+  QmmDense m{};
+  for (int p = 0; p < nparts; ++p) {
+    m.w[p] = (const uint8_t *)w[p];
+    m.y[p] = y[p];
+    m.cum[p + 1] = m.cum[p] + (int)n[p];
+  }
+  m.nparts = nparts;
+  m.row_bytes = rb;
+  return m;
 }
 
 template <int FMT, int NT>
@@ -405,7 +437,7 @@ template <int FMT>
 static int launch_gemv_fmt(const uint8_t *w, int64_t rb, int n, int64_t k, const float *x,
                            int batch, float *y, void *ws, size_t ws_bytes, hipStream_t s) {
   const int units = (int)(k / 256);
-  const size_t need = gemv_workspace_bytes(FMT, n, k, batch);
+  const size_t need = split_workspace_bytes(FMT, n, k);
   const bool split = ws != nullptr && need > 0 && ws_bytes >= need;
   const GemvPlan p = plan_gemv(n, k, split);
   unsigned *counters = p.ksplit > 1 ? static_cast<unsigned *>(ws) : nullptr;
@@ -497,6 +529,13 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, in
                        fmt, wb, rb, (int)n, k, x, (int)batch, y);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
+  if (use_qmm(fmt, n, k, x, batch, ws, ws_bytes, false)) {
+    const void *wp[1] = {w};
+    float *yp[1] = {y};
+    const QmmDense m = dense_map(1, wp, &n, yp, rb);
+    return launch_qmm_dense(m, k, x, batch, (char *)ws + kCounterBytes, (unsigned *)ws,
+                            (int)(kCounterBytes / 4), s);
+  }
   const bool i8 = use_i8(fmt, k, x, batch, ws, ws_bytes) && n < (1ll << 30);
   if (i8 || klane_ok(fmt, k, x, batch)) {
     KlMap m{};
@@ -519,11 +558,14 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, in
 size_t gemv_multi_workspace_bytes(int fmt, int nparts, const int64_t *n, int64_t k,
                                   int64_t batch) {
   size_t b = 0;
+  int64_t total = 0;
   for (int p = 0; p < nparts; ++p) {
     const size_t q = gemv_workspace_bytes(fmt, n[p], k, batch);
     b = q > b ? q : b;
+    total += n[p];
   }
-  return b;
+  const size_t fused = qmm_workspace_bytes(fmt, total, k, batch, false);
+  return fused > b ? fused : b;
 }
 
 int launch_gemv_multi(int fmt, int nparts, const void *const *w, const int64_t *n, float *const *y,
@@ -531,6 +573,11 @@ int launch_gemv_multi(int fmt, int nparts, const void *const *w, const int64_t *
                       hipStream_t s) {
   int64_t total = 0;
   for (int p = 0; p < nparts; ++p) total += n[p];
+  if (nparts <= 4 && use_qmm(fmt, total, k, x, batch, ws, ws_bytes, false)) {
+    const QmmDense m = dense_map(nparts, w, n, y, k / fmt_block_weights(fmt) * fmt_block_bytes(fmt));
+    return launch_qmm_dense(m, k, x, batch, (char *)ws + kCounterBytes, (unsigned *)ws,
+                            (int)(kCounterBytes / 4), s);
+  }
   const bool i8 = use_i8(fmt, k, x, batch, ws, ws_bytes);
   if ((i8 || klane_ok(fmt, k, x, batch)) && nparts <= 4 && total < (1ll << 30)) {
     KlMap m{};
@@ -556,10 +603,21 @@ int launch_gemv_multi(int fmt, int nparts, const void *const *w, const int64_t *
 // gate and up outputs [batch][n] each.
 static int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
-size_t gemv_swiglu_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t batch, bool fused) {
-  if (fused) return i8_workspace_bytes(fmt, k, batch);
-  return (size_t)align_up((int64_t)gemv_workspace_bytes(fmt, n, k, batch), 256) +
+// Two-launch path: the split-k GEMV's workspace, then the gate and up outputs.
+static size_t swiglu_two_launch_bytes(int fmt, int64_t n, int64_t k, int64_t batch) {
+  return (size_t)align_up((int64_t)split_workspace_bytes(fmt, n, k), 256) +
          (size_t)align_up(4 * batch * n, 256) * 2;
+}
+
+size_t gemv_swiglu_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t batch, bool fused) {
+  const size_t qmm = qmm_workspace_bytes(fmt, n, k, batch, true);
+  if (fused) return i8_workspace_bytes(fmt, k, batch);
+  const size_t two = swiglu_two_launch_bytes(fmt, n, k, batch);
+  return qmm > two ? qmm : two;
+}
+
+size_t gemv_swiglu_min_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t batch, bool fused) {
+  return fused ? 0 : swiglu_two_launch_bytes(fmt, n, k, batch);
 }
 
 int launch_gemv_swiglu(int fmt, const void *wg, const void *wu, int64_t n, int64_t k,
@@ -580,12 +638,25 @@ int launch_gemv_swiglu(int fmt, const void *wg, const void *wu, int64_t n, int64
     if (i8) return launch_gemv_i8(m, k, x, (char *)ws + kCounterBytes, s);
     return launch_kl(m, k, x, s);
   }
-  const size_t gws = (size_t)align_up((int64_t)gemv_workspace_bytes(fmt, n, k, batch), 256);
+  if (use_qmm(fmt, n, k, x, batch, ws, ws_bytes, true)) {
+    QmmDense m{};
+    m.w[0] = (const uint8_t *)wg;
+    m.w[1] = (const uint8_t *)wu;
+    m.y[0] = h;
+    m.cum[1] = (int)n;
+    m.nparts = 1;
+    m.swiglu = 1;
+    m.row_bytes = rb;
+    return launch_qmm_dense(m, k, x, batch, (char *)ws + kCounterBytes, (unsigned *)ws,
+                            (int)(kCounterBytes / 4), s);
+  }
+  // two launches through the workspace: its head is the split GEMV's, then gate and up
+  const size_t gws = (size_t)align_up((int64_t)split_workspace_bytes(fmt, n, k), 256);
   float *g = (float *)((char *)ws + gws);
   float *u = (float *)((char *)g + align_up(4 * batch * n, 256));
-  int rc = launch_gemv(fmt, wg, n, k, x, batch, g, ws, ws_bytes, s);
+  int rc = launch_gemv(fmt, wg, n, k, x, batch, g, ws, gws, s);
   if (rc) return rc;
-  rc = launch_gemv(fmt, wu, n, k, x, batch, u, ws, ws_bytes, s);
+  rc = launch_gemv(fmt, wu, n, k, x, batch, u, ws, gws, s);
   if (rc) return rc;
   return launch_swiglu(g, u, batch * n, h, s);
 }

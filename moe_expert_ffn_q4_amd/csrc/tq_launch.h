@@ -31,6 +31,8 @@ int launch_gemv_multi(int fmt, int nparts, const void *const *w, const int64_t *
                       int64_t k, const float *x, int64_t batch, void *ws, size_t ws_bytes,
                       hipStream_t s);
 bool gemv_swiglu_fused(int fmt, int64_t k, const float *x, int64_t batch);
+// The least workspace the call accepts (the one-launch paths run without one).
+size_t gemv_swiglu_min_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t batch, bool fused);
 size_t gemv_swiglu_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t batch, bool fused);
 int launch_gemv_swiglu(int fmt, const void *wg, const void *wu, int64_t n, int64_t k,
                        const float *x, int64_t batch, float *h, void *ws, size_t ws_bytes,

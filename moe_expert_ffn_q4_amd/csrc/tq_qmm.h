@@ -55,4 +55,23 @@ int launch_qmm_moe(QmmArgs a, int nt_max, int max_chunks, const float *x, int64_
                    int64_t positions, int64_t hidden, int64_t ffn, char *xsplit, char *hsplit,
                    float *h, float *o, hipStream_t st);
 
+// Dense products of 2..32 tokens: the rows of up to four matrices that share x, one after another
+// (multi), or a gate and an up matrix with the SwiGLU applied (swiglu: n = cum[1] columns).
+struct QmmDense {
+  const uint8_t *w[4];
+  float *y[4];  // [batch][n_p]; SwiGLU: y[0] = h [batch][n]
+  int cum[5];
+  int nparts;
+  int swiglu;
+  int64_t row_bytes;
+};
+bool qmm_dense_ok(int fmt, int64_t k, int64_t batch);
+// Workspace after the completion counters: the split activations and the k-slice partial sums.
+size_t qmm_dense_bytes(int64_t rows, int64_t k, int64_t batch, bool swiglu);
+// The k dimension is cut into slices of a fixed number of blocks (a function of k only, so every
+// row is summed in the same order whatever the launch); the last workgroup of a row tile to finish
+// adds the slices in order. counters: one per row tile, zero before and after the call.
+int launch_qmm_dense(const QmmDense &m, int64_t k, const float *x, int64_t batch, char *ws,
+                     unsigned *counters, int max_counters, hipStream_t st);
+
 }  // namespace tq

@@ -51,6 +51,7 @@ typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kXBlockBytes = 1024;  // one row's split block: 256 hi halves, then 256 lo halves
 constexpr int kAuxBytes = 32;       // one row's sub-block sums of a block: 8 hi, 8 lo halves
+constexpr int kMaxSlices = 8;       // k slices of the dense products
 
 // Position i of a run of 8 holds value perm8(i) (an involution: 1 <-> 2, 5 <-> 6).
 __device__ __forceinline__ constexpr int perm8(int i) {
@@ -58,20 +59,33 @@ __device__ __forceinline__ constexpr int perm8(int i) {
 }
 
 // ---- split rows ---------------------------------------------------------------------------------
-// One workgroup per row: the row's largest magnitude, then per run of 8 values (a thread each)
-// the scaled hi/lo halves and, over four neighbouring threads, the sub-block sums.
+// One workgroup per row, each thread holding its runs of 8 values in registers (the row is read
+// once): the row's largest magnitude, then per run the scaled hi/lo halves and, over four
+// neighbouring threads, the sub-block sums. RUNS = runs of 8 per thread (K <= 2048 RUNS).
+template <int RUNS>
 __global__ __launch_bounds__(256) void k_split_rows(const float *__restrict__ src, int64_t ld, int K,
                                                     uint8_t *__restrict__ xs,
                                                     uint8_t *__restrict__ aux,
                                                     float *__restrict__ unscale) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
-  const float *x = src + row * ld;
-  const float4 *x4 = reinterpret_cast<const float4 *>(x);
+  const float4 *x4 = reinterpret_cast<const float4 *>(src + row * ld);
+  const int runs = K / 8;  // a multiple of 32
+  float4 v[RUNS][2];
   float m = 0.f;
-  for (int i = threadIdx.x; i < K / 4; i += 256) {
-    const float4 v = x4[i];
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+#pragma unroll
+  for (int r = 0; r < RUNS; ++r) {
+    const int gi = threadIdx.x + 256 * r;
+    if (gi < runs) {
+      v[r][0] = x4[2 * gi];
+      v[r][1] = x4[2 * gi + 1];
+    } else {
+      v[r][0] = v[r][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v[r][h].x), fabsf(v[r][h].y)),
+                         fmaxf(fabsf(v[r][h].z), fabsf(v[r][h].w))));
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
@@ -91,15 +105,18 @@ __global__ __launch_bounds__(256) void k_split_rows(const float *__restrict__ sr
   const int kblocks = K / 256;
   uint8_t *xrow = xs + row * (int64_t)kblocks * kXBlockBytes;
   uint8_t *arow = aux + row * (int64_t)kblocks * kAuxBytes;
-  for (int gi = threadIdx.x; gi < K / 8; gi += 256) {  // K / 8 is a multiple of 32
-    const float4 a = x4[2 * gi], b = x4[2 * gi + 1];
-    const float v[8] = {a.x * s, a.y * s, a.z * s, a.w * s, b.x * s, b.y * s, b.z * s, b.w * s};
+#pragma unroll
+  for (int r = 0; r < RUNS; ++r) {
+    const int gi = threadIdx.x + 256 * r;
+    if (gi >= runs) break;  // whole groups of 32 runs stay active together
+    const float vv[8] = {v[r][0].x * s, v[r][0].y * s, v[r][0].z * s, v[r][0].w * s,
+                         v[r][1].x * s, v[r][1].y * s, v[r][1].z * s, v[r][1].w * s};
     _Float16 hi[8], lo[8];
     float sum = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      hi[i] = (_Float16)v[i];
-      lo[i] = (_Float16)(v[i] - (float)hi[i]);
+      hi[i] = (_Float16)vv[i];
+      lo[i] = (_Float16)(vv[i] - (float)hi[i]);
       sum += (float)hi[i] + (float)lo[i];
     }
     half8 h8, l8;
@@ -198,35 +215,44 @@ __device__ __forceinline__ half8 qb(const QRow &r, uint32_t sc2) {
 // Token staging: a block of one token row (1 KB of hi/lo halves) is one direct global-to-LDS
 // wave instruction, lane l bringing the row's 16-byte piece l ^ (t % 16) to LDS piece l, so that
 // the 16 token rows of an operand read (same piece, t = 0..15) fall on distinct banks. Wave w's
-// instruction i fills token row 4 i + w. Rows past the chunk repeat its last row; they feed only
-// outputs that are never stored.
-template <bool GU, int NT, int NTMAX>
-__device__ __forceinline__ void qmm_tiles(const QmmArgs &a, uint8_t *__restrict__ xbuf,
-                                          const int *rowidx, int rows, int p0,
-                                          const uint8_t *const (&wrow)[2], int col0) {
+// instruction i fills token row 4 i + w. Rows past the chunk are not loaded: whatever their LDS
+// rows hold reaches only their own accumulator rows, which are never stored (the vmcnt waits
+// count only the newer weight loads, so a varying number of these loads is fine).
+// Blocks kb0 .. kb0 + steps - 1 of the lane's two weight rows (wrow: the rows' first block)
+// against token rows rowidx[0 .. rows-1] of the split activations; epi(acc) receives the
+// accumulators (lane: tokens 16 tt + 4 g + i, weight row t16 of tiles 0 and 1), in units of the
+// scaled activations.
+template <bool GU, int NT, int NTMAX, class Epi>
+__device__ __forceinline__ void qmm_tiles(const SplitRows &x, uint8_t *__restrict__ xbuf,
+                                          const int *rowidx, int rows, int xblocks,
+                                          const uint8_t *const (&wrow)[2], int kb0, int steps,
+                                          const Epi &epi) {
   constexpr int kBuf = 16 * NTMAX * kXBlockBytes;
   const int lane = threadIdx.x & 63, wave = wave_index();
   const int t16 = lane & 15, g = lane >> 4;
-  const int64_t xrow_bytes = (int64_t)a.kblocks * kXBlockBytes;
-  const int64_t arow_bytes = (int64_t)a.kblocks * kAuxBytes;
+  const int64_t xrow_bytes = (int64_t)xblocks * kXBlockBytes;
+  const int64_t arow_bytes = (int64_t)xblocks * kAuxBytes;
   const uint8_t *xsrc[4 * NT];
 #pragma unroll
   for (int i = 0; i < 4 * NT; ++i) {
     const int t = 4 * i + wave;
-    xsrc[i] = a.x.xs + rowidx[min(t, rows - 1)] * xrow_bytes + 16 * (lane ^ (t & 15));
+    xsrc[i] = x.xs + rowidx[min(t, rows - 1)] * xrow_bytes + (int64_t)kb0 * kXBlockBytes +
+              16 * (lane ^ (t & 15));
   }
   const uint8_t *asrc[NT];
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt)
-    asrc[tt] = a.x.aux + rowidx[min(16 * tt + t16, rows - 1)] * arow_bytes + 8 * g;
+    asrc[tt] = x.aux + rowidx[min(16 * tt + t16, rows - 1)] * arow_bytes +
+               (int64_t)kb0 * kAuxBytes + 8 * g;
 
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(xbuf));
   // enqueue block kb of the chunk's token rows into buffer buf (asm loads, awaited explicitly)
   auto stage = [&](int buf, int kb) {
 #pragma unroll
     for (int i = 0; i < 4 * NT; ++i)
-      load_lds16(xsrc[i] + (int64_t)kb * kXBlockBytes,
-                 lds0 + buf * kBuf + (4 * i + wave) * kXBlockBytes);
+      if (4 * i + wave < rows)  // rows past the chunk: their outputs are never stored
+        load_lds16(xsrc[i] + (int64_t)kb * kXBlockBytes,
+                   lds0 + buf * kBuf + (4 * i + wave) * kXBlockBytes);
   };
   auto load_w = [&](QRow (&r)[2], u32x2 (&ax)[NT], int kb) {
     qrow_load(wrow[0], kb, g, r[0]);
@@ -242,7 +268,6 @@ __device__ __forceinline__ void qmm_tiles(const QmmArgs &a, uint8_t *__restrict_
     for (int tt = 0; tt < NT; ++tt) acc[r][tt] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
-  const int steps = a.kblocks;
   // weights and sums run two blocks ahead (set j holds the blocks st with st % 3 == j), token
   // rows one block ahead (buffer st % 2)
   QRow raw[3][2];
@@ -348,25 +373,36 @@ __device__ __forceinline__ void qmm_tiles(const QmmArgs &a, uint8_t *__restrict_
     for (int tt = 0; tt < NT; ++tt) keep_alive(axr[j][tt]);
   }
   wait_vmem<0>();  // the surplus loads of the last steps land before the workgroup ends
+  epi(acc);
+}
 
-  // lane: tokens 16 tt + 4 g + i, weight row t16 of each tile
+// Grouped (MoE) epilogue: unscaled sums of the chunk's positions, SwiGLU'd for gate/up.
+template <bool GU>
+struct MoeEpi {
+  const QmmArgs *a;
+  const int *rowidx;
+  int rows, p0, col0;
+  template <int NT>
+  __device__ __forceinline__ void operator()(const f32x4 (&acc)[2][NT]) const {
+    const int lane = threadIdx.x & 63, t16 = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int tt = 0; tt < NT; ++tt)
+    for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = 16 * tt + 4 * g + i;
-      if (tok < rows) {
-        const float us = a.x.unscale[rowidx[tok]];
-        float *o = a.out + (int64_t)(p0 + tok) * a.ldo + col0 + t16;
-        if (GU) {
-          o[0] = silu_mul(acc[0][tt][i] * us, acc[1][tt][i] * us);
-        } else {
-          o[0] = acc[0][tt][i] * us;
-          o[16] = acc[1][tt][i] * us;
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 16 * tt + 4 * g + i;
+        if (tok < rows) {
+          const float us = a->x.unscale[rowidx[tok]];
+          float *o = a->out + (int64_t)(p0 + tok) * a->ldo + col0 + t16;
+          if (GU) {
+            o[0] = silu_mul(acc[0][tt][i] * us, acc[1][tt][i] * us);
+          } else {
+            o[0] = acc[0][tt][i] * us;
+            o[16] = acc[1][tt][i] * us;
+          }
         }
       }
-    }
-}
+  }
+};
 
 template <bool GU, int NTMAX>
 __global__ __launch_bounds__(256) void k_qmm(QmmArgs a) {
@@ -410,18 +446,163 @@ __global__ __launch_bounds__(256) void k_qmm(QmmArgs a) {
     wrow[1] = mat[2] + (int64_t)(col0 + 16 + t16) * a.row_bytes;
   }
   __syncthreads();  // rowidx
+  const MoeEpi<GU> epi{&a, rowidx, rows, p0, col0};
   if (NTMAX == 1 || rows <= 16)
-    qmm_tiles<GU, 1, NTMAX>(a, xbuf, rowidx, rows, p0, wrow, col0);
+    qmm_tiles<GU, 1, NTMAX>(a.x, xbuf, rowidx, rows, a.kblocks, wrow, 0, a.kblocks, epi);
   else
-    qmm_tiles<GU, (NTMAX > 1 ? 2 : 1), NTMAX>(a, xbuf, rowidx, rows, p0, wrow, col0);
+    qmm_tiles<GU, (NTMAX > 1 ? 2 : 1), NTMAX>(a.x, xbuf, rowidx, rows, a.kblocks, wrow, 0,
+                                              a.kblocks, epi);
+}
+
+// ---- dense products (2..32 tokens) --------------------------------------------------------------
+
+__device__ __forceinline__ const uint8_t *dense_row(const QmmDense &m, int v) {
+  int p = 0;
+#pragma unroll
+  for (int i = 1; i < 4; ++i) p += (i < m.nparts && v >= m.cum[i]) ? 1 : 0;
+  return m.w[p] + (int64_t)(v - m.cum[p]) * m.row_bytes;
+}
+
+// Partial sums of one (row tile, k slice) as [token][128]: GU: gate columns 0..63, up 64..127;
+// otherwise the tile's 128 rows. With one slice the sums are the results.
+template <bool GU>
+struct DenseEpi {
+  const QmmDense *m;
+  const SplitRows *x;
+  int B, tile, ks, ksplit;
+  float *partial;
+  unsigned *counters;
+  int *is_last;  // LDS
+
+  // a final value of row rt of the (non-SwiGLU) tile for token tok
+  __device__ __forceinline__ void store(int tok, int rt, float v) const {
+    const int vrow = tile * 128 + rt;
+    if (vrow < m->cum[m->nparts]) {
+      int p = 0;
+#pragma unroll
+      for (int i = 1; i < 4; ++i) p += (i < m->nparts && vrow >= m->cum[i]) ? 1 : 0;
+      m->y[p][(int64_t)tok * (m->cum[p + 1] - m->cum[p]) + (vrow - m->cum[p])] = v;
+    }
+  }
+
+  template <int NT>
+  __device__ __forceinline__ void operator()(const f32x4 (&acc)[2][NT]) const {
+    const int lane = threadIdx.x & 63, t16 = lane & 15, g = lane >> 4, wave = wave_index();
+    const int n = GU ? m->cum[1] : m->cum[m->nparts];
+    auto row_in_tile = [&](int r) { return GU ? r * 64 + 16 * wave + t16 : 32 * wave + 16 * r + t16; };
+    if (ksplit == 1) {
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = 16 * tt + 4 * g + i;
+          if (tok >= B) continue;
+          const float us = x->unscale[tok];
+          if (GU) {
+            const int col = tile * 64 + 16 * wave + t16;
+            if (col < n)
+              m->y[0][(int64_t)tok * n + col] = silu_mul(acc[0][tt][i] * us, acc[1][tt][i] * us);
+          } else {
+            store(tok, row_in_tile(0), acc[0][tt][i] * us);
+            store(tok, row_in_tile(1), acc[1][tt][i] * us);
+          }
+        }
+      return;
+    }
+    // k split: this slice's sums (device-coherent stores, all completed before the arrival is
+    // counted); the last workgroup of the tile adds the slices in order and resets the counter
+    float *mine = partial + ((int64_t)tile * ksplit + ks) * B * 128;
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 16 * tt + 4 * g + i;
+        if (tok >= B) continue;
+        const float us = x->unscale[tok];
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+          __hip_atomic_store(mine + tok * 128 + row_in_tile(r), acc[r][tt][i] * us,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (threadIdx.x == 0)
+      *is_last = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(ksplit - 1);
+    __syncthreads();
+    if (!*is_last) return;
+    const float *base = partial + (int64_t)tile * ksplit * B * 128;
+    const int per = GU ? 64 : 128;
+    for (int idx = threadIdx.x; idx < B * per; idx += blockDim.x) {
+      const int tok = idx / per, rt = idx - tok * per;
+      float v0[kMaxSlices], v1[kMaxSlices];
+#pragma unroll
+      for (int q = 0; q < kMaxSlices; ++q) {  // every slice's value in flight, then the sums
+        const float *pq = base + (int64_t)q * B * 128 + tok * 128;
+        v0[q] = q < ksplit ? __hip_atomic_load(pq + rt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           : 0.f;
+        v1[q] = GU && q < ksplit
+                    ? __hip_atomic_load(pq + 64 + rt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                    : 0.f;
+      }
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int q = 0; q < kMaxSlices; ++q)
+        if (q < ksplit) {
+          s0 += v0[q];
+          s1 += v1[q];
+        }
+      if (GU) {
+        const int col = tile * 64 + rt;
+        if (col < n) m->y[0][(int64_t)tok * n + col] = silu_mul(s0, s1);
+      } else {
+        store(tok, rt, s0);
+      }
+    }
+    if (threadIdx.x == 0)
+      __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+};
+
+template <bool GU, int NTMAX>
+__global__ __launch_bounds__(256) void k_qmm_dense(QmmDense m, SplitRows x, int B, int kblocks,
+                                                   int ksplit, int upk, float *partial,
+                                                   unsigned *counters) {
+  __shared__ __attribute__((aligned(16))) uint8_t xbuf[2 * 16 * NTMAX * kXBlockBytes];
+  __shared__ int rowidx[16 * NTMAX];
+  __shared__ int is_last;
+  const int tile = blockIdx.x / ksplit, ks = blockIdx.x - tile * ksplit;
+  const int kb0 = ks * upk, steps = min(upk, kblocks - kb0);
+  if ((int)threadIdx.x < 16 * NTMAX) rowidx[threadIdx.x] = min((int)threadIdx.x, B - 1);
+  const int t16 = threadIdx.x & 15, wave = wave_index();
+  const uint8_t *wrow[2];
+  if (GU) {
+    const int c = min(tile * 64 + wave * 16 + t16, m.cum[1] - 1);
+    wrow[0] = m.w[0] + (int64_t)c * m.row_bytes + (int64_t)kb0 * 144;
+    wrow[1] = m.w[1] + (int64_t)c * m.row_bytes + (int64_t)kb0 * 144;
+  } else {
+    const int total = m.cum[m.nparts];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      wrow[r] = dense_row(m, min(tile * 128 + wave * 32 + 16 * r + t16, total - 1)) +
+                (int64_t)kb0 * 144;
+  }
+  __syncthreads();  // rowidx
+  const DenseEpi<GU> epi{&m, &x, B, tile, ks, ksplit, partial, counters, &is_last};
+  if (NTMAX == 1 || B <= 16)
+    qmm_tiles<GU, 1, NTMAX>(x, xbuf, rowidx, B, kblocks, wrow, kb0, steps, epi);
+  else
+    qmm_tiles<GU, (NTMAX > 1 ? 2 : 1), NTMAX>(x, xbuf, rowidx, B, kblocks, wrow, kb0, steps, epi);
 }
 
 // ---- host side ----------------------------------------------------------------------------------
 
 int qmm_chunk_rows(int nt_max) { return 16 * nt_max; }
 
+// The row split keeps a row in registers: k <= 32768.
 bool qmm_shape_ok(int64_t hidden, int64_t ffn) {
-  return hidden % 256 == 0 && ffn % 256 == 0 && hidden >= 256 && ffn >= 256;
+  return hidden % 256 == 0 && ffn % 256 == 0 && hidden >= 256 && ffn >= 256 && hidden <= 32768 &&
+         ffn <= 32768;
 }
 
 size_t split_rows_bytes(int64_t rows, int64_t k) {
@@ -436,11 +617,21 @@ SplitRows split_rows_at(char *base, int64_t rows, int64_t k) {
   return s;
 }
 
+template <int RUNS>
+static void split_rows_launch(const float *src, int64_t ld, int64_t rows, int64_t k,
+                              SplitRows out, hipStream_t st) {
+  hipLaunchKernelGGL(k_split_rows<RUNS>, dim3((unsigned)rows), dim3(256), 0, st, src, ld, (int)k,
+                     out.xs, out.aux, out.unscale);
+}
+
 void launch_split_rows(const float *src, int64_t ld, int64_t rows, int64_t k, SplitRows out,
                        hipStream_t st) {
   if (rows <= 0) return;
-  hipLaunchKernelGGL(k_split_rows, dim3((unsigned)rows), dim3(256), 0, st, src, ld, (int)k, out.xs,
-                     out.aux, out.unscale);
+  const int64_t runs = (k / 8 + 255) / 256;  // runs of 8 per thread
+  if (runs <= 2) split_rows_launch<2>(src, ld, rows, k, out, st);
+  else if (runs <= 4) split_rows_launch<4>(src, ld, rows, k, out, st);
+  else if (runs <= 8) split_rows_launch<8>(src, ld, rows, k, out, st);
+  else split_rows_launch<16>(src, ld, rows, k, out, st);  // k <= 32768
 }
 
 template <int NTMAX>
@@ -482,6 +673,56 @@ int launch_qmm_moe(QmmArgs a, int nt_max, int max_chunks, const float *x, int64_
   a.ntiles = (int)(hidden / 128);
   if (nt_max == 1) qmm_launch<1>(a, max_chunks, false, st);
   else qmm_launch<2>(a, max_chunks, false, st);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// ---- dense host side ----------------------------------------------------------------------------
+
+bool qmm_dense_ok(int fmt, int64_t k, int64_t batch) {
+  const int mode = env_int("TQ_GEMV_QMM", 1);
+  return mode && fmt == FMT_Q4_K && batch >= 2 && batch <= 32 && k % 256 == 0 && k >= 256 &&
+         k <= 32768;
+}
+
+// Blocks per k slice: a function of k only -- at least two, and at most 8 slices (the last
+// workgroup of a tile reads every slice's sums, all at once).
+static int dense_upk(int64_t k) {
+  const int nblk = (int)(k / 256);
+  const int v = env_int("TQ_QMM_UPK", 0);
+  if (v > 0) return clampi(v, 1, nblk);
+  return clampi((nblk + 7) / 8, 2, nblk);
+}
+
+static int64_t dense_tiles(int64_t rows, bool swiglu) { return swiglu ? (rows + 63) / 64 : (rows + 127) / 128; }
+
+size_t qmm_dense_bytes(int64_t rows, int64_t k, int64_t batch, bool swiglu) {
+  const int64_t nblk = k / 256, upk = dense_upk(k), ksplit = (nblk + upk - 1) / upk;
+  const int64_t tiles = dense_tiles(rows, swiglu);
+  return split_rows_bytes(batch, k) + (ksplit > 1 ? (size_t)align256(tiles * ksplit * batch * 128 * 4) : 0);
+}
+
+int launch_qmm_dense(const QmmDense &m, int64_t k, const float *x, int64_t batch, char *ws,
+                     unsigned *counters, int max_counters, hipStream_t st) {
+  const int64_t rows = m.swiglu ? m.cum[1] : m.cum[m.nparts];
+  const int nblk = (int)(k / 256), upk = dense_upk(k), ksplit = (nblk + upk - 1) / upk;
+  const int64_t tiles = dense_tiles(rows, m.swiglu != 0);
+  if ((ksplit > 1 && tiles > max_counters) || ksplit > kMaxSlices) return -2;
+  const SplitRows xr = split_rows_at(ws, batch, k);
+  float *partial = (float *)(ws + split_rows_bytes(batch, k));
+  launch_split_rows(x, k, batch, k, xr, st);
+  const dim3 grid((unsigned)(tiles * ksplit));
+  const int B = (int)batch;
+  if (m.swiglu) {
+    if (B <= 16)
+      hipLaunchKernelGGL((k_qmm_dense<true, 1>), grid, dim3(256), 0, st, m, xr, B, nblk, ksplit, upk, partial, counters);
+    else
+      hipLaunchKernelGGL((k_qmm_dense<true, 2>), grid, dim3(256), 0, st, m, xr, B, nblk, ksplit, upk, partial, counters);
+  } else {
+    if (B <= 16)
+      hipLaunchKernelGGL((k_qmm_dense<false, 1>), grid, dim3(256), 0, st, m, xr, B, nblk, ksplit, upk, partial, counters);
+    else
+      hipLaunchKernelGGL((k_qmm_dense<false, 2>), grid, dim3(256), 0, st, m, xr, B, nblk, ksplit, upk, partial, counters);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -93,3 +93,65 @@ def test_qmm_workspace_sizes_differ_by_tile(monkeypatch):
     assert w1 > w2 > 0
     y = host(moe(dev(synth.normal_f32(synth.rng(404, "x"), (200, 512)))))
     assert np.all(np.isfinite(y))
+
+
+# ---- dense products of 2..32 tokens (tq_gemv / tq_gemv_multi / tq_gemv_swiglu) -------------------
+
+import oracle  # noqa: E402
+from tests.gpu_util import assert_product_close  # noqa: E402
+
+
+@pytest.mark.parametrize("n,k,batch", [(300, 4096, 2), (128, 1024, 4), (1000, 2048, 8), (64, 14336, 8),
+                                       (257, 512, 16), (96, 3072, 17), (130, 4096, 32)])
+def test_qmm_dense_gemv(n, k, batch):
+    _case("qmm-dense", n, k, batch)
+    g = synth.rng(410, "dense", n, k, batch)
+    w = synth.blob("q4_k", g, n, k)
+    x = synth.normal_f32(g, (batch, k))
+    y = host(tq.gemv("q4_k", dev(w), n, k, dev(x)))
+    ref, mag = oracle.gemv("q4_k", w, n, k, x)
+    worst = assert_product_close(y, ref, mag, what=f"dense {n}x{k} b{batch}")
+    assert worst < 0.05, worst
+    y2 = host(tq.gemv("q4_k", dev(w), n, k, dev(x)))
+    assert np.array_equal(y, y2), "not deterministic"
+
+
+def test_qmm_dense_multi_and_swiglu_bitwise():
+    """The fused q/k/v launch and the fused gate/up + SwiGLU launch give bitwise the single-GEMV
+    results (k slices of a fixed size, added in order)."""
+    k, batch = 4096, 8
+    g = synth.rng(411, "dense-multi")
+    ns = [512, 128, 128]
+    ws = [synth.blob("q4_k", g, n, k) for n in ns]
+    x = dev(synth.normal_f32(g, (batch, k)))
+    outs = tq.gemv_multi("q4_k", [dev(w) for w in ws], ns, k, x)
+    for w, n, o in zip(ws, ns, outs):
+        assert np.array_equal(host(o), host(tq.gemv("q4_k", dev(w), n, k, x)))
+    F = 448
+    wg, wu = synth.blob("q4_k", g, F, k), synth.blob("q4_k", g, F, k)
+    h = host(tq.gemv_swiglu("q4_k", dev(wg), dev(wu), F, k, x))
+    gg = tq.gemv("q4_k", dev(wg), F, k, x)
+    uu = tq.gemv("q4_k", dev(wu), F, k, x)
+    assert np.array_equal(h, host(tq.swiglu(gg, uu)))
+
+
+def test_qmm_dense_agrees_with_fp32_gemv(monkeypatch):
+    """Matrix-core path vs the fp32 multi-token GEMV (TQ_GEMV_QMM=0): fp32 rounding apart."""
+    n, k, batch = 512, 8192, 8
+    g = synth.rng(412, "dense-vs")
+    w, x = dev(synth.blob("q4_k", g, n, k)), dev(synth.normal_f32(g, (batch, k)))
+    a = host(tq.gemv("q4_k", w, n, k, x))
+    monkeypatch.setenv("TQ_GEMV_QMM", "0")
+    b = host(tq.gemv("q4_k", w, n, k, x))
+    assert np.linalg.norm(a - b) / np.linalg.norm(b) < 1e-6
+
+
+def test_qmm_dense_without_workspace():
+    """No workspace: the fp32 GEMV runs (still within the bar)."""
+    n, k, batch = 200, 2048, 4
+    g = synth.rng(413, "dense-nows")
+    w = synth.blob("q4_k", g, n, k)
+    x = synth.normal_f32(g, (batch, k))
+    y = host(tq.gemv("q4_k", dev(w), n, k, dev(x), ws=False))
+    ref, mag = oracle.gemv("q4_k", w, n, k, x)
+    assert_product_close(y, ref, mag, what="dense no-ws")
