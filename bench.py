@@ -39,12 +39,15 @@ def _args():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--batch", type=int, default=1, help="tokens per decode step (1 or 8)")
     p.add_argument("--workload", default="llama8b",
-                   choices=["llama8b", "mixtral", "deepseek", "deepseek-prefill", "deepseek-host"],
+                   choices=["llama8b", "llama70b", "mixtral", "deepseek", "deepseek-prefill",
+                            "deepseek-host"],
                    help="llama8b: 32-layer dense decode step (default); mixtral / deepseek: one "
                         "MoE layer at --batch tokens; deepseek-prefill: one DeepSeek-shaped MoE "
                         "layer over --tokens (default 4096) on the bf16 matrix-core path; "
                         "deepseek-host: the DeepSeek decode layer at --batch tokens with the routed "
-                        "experts in pinned host memory, copied per step")
+                        "experts in pinned host memory, copied per step; llama70b: one "
+                        "Llama-3-70B-shaped layer in each of Q4_K, Q6_K and Q8_0 at batch 1, 4 "
+                        "and 16")
     p.add_argument("--tokens", type=int, default=4096, help="tokens of the prefill workload")
     p.add_argument("--seed", type=int, default=42)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -200,12 +203,15 @@ def build_dense_model(tq, synth, torch, batch, seed):
 
 
 def gemv_kernel_name(batch):
-    """The kernel that tq_gemv runs for this batch (with its workspace)."""
-    if batch != 1:
-        return "tq_gemv Q4_K (tq::k_gemv)"
-    if os.environ.get("TQ_GEMV_I8", "1") != "0":
-        return "tq_gemv Q4_K batch 1 (tq::k_gemv_i8, after tq::k_x_digits)"
-    return "tq_gemv Q4_K batch 1 (tq::k_gemv_kl)"
+    """The kernel that tq_gemv runs for the 8B shapes (k = 4096 and 14336) at this batch, given
+    its workspace (the int8 kernel takes k >= 16384 unless TQ_GEMV_I8=2)."""
+    if batch == 1:
+        if os.environ.get("TQ_GEMV_I8", "1") == "2":
+            return "tq_gemv Q4_K batch 1 (tq::k_gemv_i8, after tq::k_x_digits)"
+        return "tq_gemv Q4_K batch 1 (tq::k_gemv_kl)"
+    if batch <= 32 and os.environ.get("TQ_GEMV_QMM", "1") != "0":
+        return f"tq_gemv Q4_K batch {batch} (tq::k_qmm_dense, after tq::k_split_rows)"
+    return f"tq_gemv Q4_K batch {batch} (tq::k_gemv)"
 
 
 def make_step(tq, torch, layers, batch, events=None, gemv_only=False):
@@ -420,6 +426,87 @@ def moe_bench(args, torch, tq, synth):
     return out
 
 
+def llama70b_bench(args, torch, tq, synth):
+    """One Llama-3-70B-shaped layer (q, k, v, o, gate, up, down) in each of Q4_K, Q6_K and Q8_0,
+    at batch 1, 4 and 16: q/k/v as one tq_gemv_multi call, o, gate/up as one tq_gemv_swiglu
+    call, down; the layer captured as a HIP graph and replayed. Reports per (format, batch) the
+    layer time and the blob bytes over that time. value: Q4_K tokens/s of the layer at batch 1."""
+    import ctypes as C
+
+    shape = synth.LLAMA70B
+    H, F = shape["hidden"], shape["ffn"]
+    L = tq.lib()
+    results = {}
+    stream = torch.cuda.Stream()
+    for t in ("q4_k", "q6_k", "q8_0"):
+        T = tq._type(t)
+        projs = {}
+        for name, n, k in synth.dense_projections(shape):
+            w = synth.blob(t, synth.rng(args.seed, "70b", t, name), n, k)
+            projs[name] = (torch.from_numpy(w).to("cuda"), n, k)
+        blob_bytes = sum(w.numel() for w, _, _ in projs.values())
+        for batch in (1, 4, 16):
+            g = synth.rng(args.seed, "70b-act", t, batch)
+            x = torch.from_numpy(synth.normal_f32(g, (batch, H))).cuda()
+            a = torch.from_numpy(synth.normal_f32(g, (batch, H))).cuda()
+            out = {m: torch.empty(batch, n, device="cuda") for m, (_, n, _) in projs.items()}
+            hbuf = torch.empty(batch, F, device="cuda")
+            need = [tq.gemv_workspace_bytes(t, n, k, batch) for _, n, k in projs.values()]
+            narr = (C.c_int64 * 3)(H, shape["kv"], shape["kv"])
+            need.append(int(L.tq_gemv_multi_workspace_bytes(T, 3, narr, H, batch)))
+            need.append(int(L.tq_gemv_swiglu_workspace_bytes(T, F, H, batch)))
+            ws = torch.zeros(max(max(need), 256), dtype=torch.uint8, device="cuda")
+            wsn = ws.numel()
+
+            def step():
+                st = torch.cuda.current_stream().cuda_stream
+                w3 = (C.c_void_p * 3)(*[projs[m][0].data_ptr() for m in ("q", "k", "v")])
+                y3 = (C.c_void_p * 3)(*[out[m].data_ptr() for m in ("q", "k", "v")])
+                rc = L.tq_gemv_multi(T, 3, w3, narr, y3, H, x.data_ptr(), batch, ws.data_ptr(),
+                                     wsn, st)
+                rc = rc or L.tq_gemv(T, projs["o"][0].data_ptr(), H, H, a.data_ptr(), batch,
+                                     out["o"].data_ptr(), ws.data_ptr(), wsn, st)
+                rc = rc or L.tq_gemv_swiglu(T, projs["gate"][0].data_ptr(),
+                                            projs["up"][0].data_ptr(), F, H, x.data_ptr(), batch,
+                                            hbuf.data_ptr(), ws.data_ptr(), wsn, st)
+                rc = rc or L.tq_gemv(T, projs["down"][0].data_ptr(), H, F, hbuf.data_ptr(), batch,
+                                     out["down"].data_ptr(), ws.data_ptr(), wsn, st)
+                if rc:
+                    raise tq.TQError(rc, L.tq_last_error().decode())
+
+            with torch.cuda.stream(stream):
+                step()
+                torch.cuda.synchronize()
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph, stream=stream):
+                    step()
+                for _ in range(args.warmup):
+                    graph.replay()
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(args.steps):
+                    graph.replay()
+                torch.cuda.synchronize()
+                dt = (time.perf_counter() - t0) / args.steps
+            results[f"{t} b{batch}"] = {"ms_per_layer": round(dt * 1000, 4),
+                                        "tokens_s_one_layer": round(batch / dt, 1),
+                                        "blob_gbs": round(blob_bytes / dt / 1e9, 1)}
+        del projs
+        torch.cuda.empty_cache()
+    q = results["q4_k b1"]
+    return {
+        "metric": METRIC, "value": q["tokens_s_one_layer"], "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": q["ms_per_layer"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "q4_k / q6_k / q8_0 weights, f32 activations and accumulation",
+        "data": "synthetic (seeded random blocks, N(0,1) activations)",
+        "config": {"workload": "llama3-70b-shaped layer (hidden 8192, kv 1024, ffn 28672), one "
+                               "layer per format, batch 1 / 4 / 16", "global_batch": 1,
+                   "seq_len": 1, "parallelism": "none (1 GPU)"},
+        "per_format_batch": results,
+    }
+
+
 def host_bench(args, torch, tq, synth):
     """DeepSeek-shaped decode layer with the routed experts in pinned host memory: every step
     reads the selected experts' blobs over PCIe (a host sync on the routing, then per-expert
@@ -502,6 +589,9 @@ def main():
     torch.cuda.set_device(0)
     if args.workload == "deepseek-host":
         print(json.dumps(host_bench(args, torch, tq, synth)), flush=True)
+        return
+    if args.workload == "llama70b":
+        print(json.dumps(llama70b_bench(args, torch, tq, synth)), flush=True)
         return
     if args.workload != "llama8b":
         print(json.dumps(moe_bench(args, torch, tq, synth)), flush=True)
