@@ -194,9 +194,9 @@ size_t tq_moe_workspace_bytes(const tq_moe_desc *desc, int64_t tokens);
  * active-expert list is then copied to the host (one synchronisation of `stream`, so such calls
  * cannot be captured into a graph) and each selected expert is copied from pinned host memory
  * into the workspace with hipMemcpyAsync on copy_stream (NULL: on `stream`), each followed by an
- * event. The shared expert (always on the device) runs first; on the fp32 path each routed
- * expert's kernels wait only for their own copy, on the matrix-core path one grouped launch
- * waits for all copies. Host blobs must stay valid until the call's work has completed; they
+ * event. The shared expert (always on the device) runs first; where each expert has kernels of
+ * its own (one token, or Q6_K / Q8_0) they wait only for their own copy; on the matrix-core paths
+ * (bf16 prefill; Q4_K with 2+ tokens) one grouped launch waits for all copies. Host blobs must stay valid until the call's work has completed; they
  * must be pinned (hipHostMalloc) for the copies to be asynchronous. The output is bitwise
  * identical to the device-resident call's.
  * Deterministic: the same inputs give bitwise-identical outputs and routing.

@@ -306,7 +306,7 @@ static int host_resident_experts(const tq_moe_desc *d, const tq::MoePlan &p,
     last_copied = a;
   }
   const auto *dev_table = reinterpret_cast<const tq::MoeExpertPtrs *>(d->experts);
-  if (s.mfma) {
+  if (s.mfma || p.qmm) {  // one grouped launch once every copy has landed
     if (last_copied >= 0 && hipStreamWaitEvent(st, hs->copied[last_copied], 0) != hipSuccess)
       return fail(TQ_EDEVICE, "tq_moe_ffn: event wait failed");
     return launched(tq::launch_moe_experts(p, dev_table, shared, staging, x, ws, st),

@@ -67,10 +67,15 @@ __global__ __launch_bounds__(256) void k_router(const float *__restrict__ wr, in
 // ---- top-k and softmax weights -----------------------------------------------------------------
 // One wave per token. Each lane holds the logits of experts lane, lane+64, ...
 
+constexpr int kMaxHSplit = 32;  // hidden slices of the router's partial sums
+
 __device__ __forceinline__ bool better(float va, int ea, float vb, int eb) {
   return va > vb || (va == vb && ea < eb);
 }
 
+// NV = expert slots per lane (E <= 64 NV). The code is kept short (rolled loops): one wave runs
+// it cold, so instruction fetch, not arithmetic, sets its time.
+template <int NV>
 __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, int T, int E,
                                               int hsplit, int topk, int renormalize,
                                               float *__restrict__ logits, int *__restrict__ ids,
@@ -78,39 +83,48 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, in
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (blockDim.x >> 6) + (int)(threadIdx.x >> 6);
   if (t >= T) return;  // whole wave
-  constexpr int MAXV = 16;  // E <= 1024
-  float v[MAXV];
-  const int nv = (E + 63) >> 6;
   const int tile = t >> 3, tt = t & 7;
+  const float *pbase = part + ((int64_t)tile * hsplit * 8 + tt) * E;
+  // logits: the hidden slices' partial sums, added in slice order. They were just written by the
+  // router's workgroups on every XCD, so each dependent batch of loads costs a memory round trip:
+  // up to 4 slots per lane every slice's load goes out at once (HB = all 32), beyond 8 at a time.
+  constexpr int HB = NV <= 4 ? kMaxHSplit : 8;
+  float v[NV];
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    v[i] = -INFINITY;
-    const int e = lane + 64 * i;
-    if (i < nv && e < E) {
-      float s = 0.f;
-      const float *pp = part + ((int64_t)tile * hsplit * 8 + tt) * E + e;
-#pragma unroll 8
-      for (int hs = 0; hs < hsplit; ++hs) s += pp[(int64_t)hs * 8 * E];  // loads in flight together
-      v[i] = s;
-      logits[(int64_t)t * E + e] = s;
+  for (int i = 0; i < NV; ++i) v[i] = 0.f;
+  for (int h0 = 0; h0 < hsplit; h0 += HB) {
+    float b[NV][HB];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = min(lane + 64 * i, E - 1);
+#pragma unroll
+      for (int q = 0; q < HB; ++q) b[i][q] = pbase[(int64_t)min(h0 + q, hsplit - 1) * 8 * E + e];
     }
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int q = 0; q < HB; ++q) v[i] += h0 + q < hsplit ? b[i][q] : 0.f;
   }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    if (lane + 64 * i < E) logits[(int64_t)t * E + lane + 64 * i] = v[i];
+    else v[i] = -INFINITY;
+  }
+  // k rounds of a wave arg-max on (value, -index); round j's id and exp(value - first value)
+  // are written at once, the weights divided by their sum afterwards
   unsigned taken = 0;  // bit i: expert lane + 64 i already selected
   float sel0 = 0.f, denom = 0.f;
-  float selv[32];
-  int sele[32];
   for (int j = 0; j < topk; ++j) {
     float bv = -INFINITY;
     int be = 0x7FFFFFFF;
 #pragma unroll
-    for (int i = 0; i < MAXV; ++i) {
+    for (int i = 0; i < NV; ++i) {
       const int e = lane + 64 * i;
-      if (i < nv && e < E && !(taken >> i & 1u) && better(v[i], e, bv, be)) {
+      if (e < E && !(taken >> i & 1u) && better(v[i], e, bv, be)) {
         bv = v[i];
         be = e;
       }
     }
-#pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
       const float ov = __shfl_xor(bv, off);
       const int oe = __shfl_xor(be, off);
@@ -120,29 +134,24 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, in
       }
     }
     if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    selv[j] = bv;
-    sele[j] = be;
+    if (j == 0) sel0 = bv;
+    const float ej = expf(bv - sel0);
+    if (renormalize) denom += ej;
+    if (lane == 0) {
+      ids[(int64_t)t * topk + j] = be;
+      wts[(int64_t)t * topk + j] = ej;
+    }
   }
-  sel0 = selv[0];
-  if (renormalize) {
-    for (int j = 0; j < topk; ++j) denom += expf(selv[j] - sel0);
-  } else {
+  if (!renormalize) {
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < MAXV; ++i) {
-      const int e = lane + 64 * i;
-      if (i < nv && e < E) s += expf(v[i] - sel0);
-    }
-#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (lane + 64 * i < E) s += expf(v[i] - sel0);
     for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
     denom = s;
   }
-  if (lane == 0) {
-    for (int j = 0; j < topk; ++j) {
-      ids[(int64_t)t * topk + j] = sele[j];
-      wts[(int64_t)t * topk + j] = expf(selv[j] - sel0) / denom;
-    }
-  }
+  if (lane == 0)
+    for (int j = 0; j < topk; ++j) wts[(int64_t)t * topk + j] = wts[(int64_t)t * topk + j] / denom;
 }
 
 // ---- grouping --------------------------------------------------------------------------------------
@@ -417,11 +426,10 @@ MoePlan plan_moe(const MoeShape &s) {
   p.P = T * k + (s.has_shared ? T : 0);
   // the shared expert's T positions as entries of at most shared_piece: 16 on the fp32 grouped
   // path (two tiles of 8), all T elsewhere (one token, or the matrix-core chunk table)
-  // Q4_K steps of two or more tokens (routed experts in device memory): the fp32-accurate fp16
-  // matrix-core kernels, which read each active expert's weights once per chunk of 16 or 32
-  // positions instead of running VALU dot products per token
-  p.qmm = !s.mfma && s.type == FMT_Q4_K && T > 1 && !s.experts_on_host &&
-          qmm_shape_ok(s.hidden, s.ffn);
+  // Q4_K steps of two or more tokens: the fp32-accurate fp16 matrix-core kernels, which read each
+  // active expert's weights once per chunk of 16 or 32 positions instead of running VALU dot
+  // products per token (with host-resident experts: one launch once every copy has landed)
+  p.qmm = !s.mfma && s.type == FMT_Q4_K && T > 1 && qmm_shape_ok(s.hidden, s.ffn);
   if (const char *v = getenv("TQ_MOE_QMM")) p.qmm = p.qmm && atoi(v) != 0;  // 0: grouped GEMV
   p.qmm_nt = (T * k + E - 1) / E > 12 ? 2 : 1;
   if (const char *v = getenv("TQ_QMM_NT")) p.qmm_nt = atoi(v) == 2 ? 2 : 1;
@@ -441,7 +449,7 @@ MoePlan plan_moe(const MoeShape &s) {
   p.rtiles = (int)((T + 7) / 8);
   const int rrg = (int)((E + 63) / 64);
   int hs = (512 + rrg * p.rtiles - 1) / (rrg * p.rtiles);
-  hs = clampi(hs, 1, (int)(s.hidden / 256));
+  hs = clampi(hs, 1, (int)(s.hidden / 256 < kMaxHSplit ? s.hidden / 256 : kMaxHSplit));
   p.hpk = (int)(((s.hidden + hs - 1) / hs + 3) & ~3);
   p.hsplit = (int)((s.hidden + p.hpk - 1) / p.hpk);
   // gate/up: F rows over k = hidden; down: hidden rows over k = F
@@ -539,9 +547,17 @@ int launch_moe_routing(const MoePlan &p, const float *router_w, const float *x, 
   float *rpart = (float *)(ws + p.off_rpart);
   const dim3 rgrid((unsigned)(((E + 63) / 64) * p.hsplit), (unsigned)p.rtiles);
   hipLaunchKernelGGL(k_router, rgrid, dim3(256), 0, st, router_w, E, H, x, T, p.hsplit, p.hpk, rpart);
-  hipLaunchKernelGGL(k_topk, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, rpart, T, E, p.hsplit,
-                     k, s.renormalize, (float *)(ws + p.off_logits), (int *)(ws + p.off_ids),
-                     (float *)(ws + p.off_wts));
+  {
+    const dim3 g((unsigned)((T + 3) / 4));
+    float *lg = (float *)(ws + p.off_logits), *wt = (float *)(ws + p.off_wts);
+    int *id = (int *)(ws + p.off_ids);
+    if (E <= 64)
+      hipLaunchKernelGGL(k_topk<1>, g, dim3(256), 0, st, rpart, T, E, p.hsplit, k, s.renormalize, lg, id, wt);
+    else if (E <= 256)
+      hipLaunchKernelGGL(k_topk<4>, g, dim3(256), 0, st, rpart, T, E, p.hsplit, k, s.renormalize, lg, id, wt);
+    else
+      hipLaunchKernelGGL(k_topk<16>, g, dim3(256), 0, st, rpart, T, E, p.hsplit, k, s.renormalize, lg, id, wt);
+  }
   const size_t glds = group_lds_bytes(s.tokens, s.n_experts);
   if (glds > 65536 &&
       hipFuncSetAttribute((const void *)k_group, hipFuncAttributeMaxDynamicSharedMemorySize,
