@@ -78,11 +78,11 @@ int tq_dequant(int type, const void *w, int64_t n, int64_t k, int out_type, void
  *              256-byte aligned, zero-filled before its first use; every call leaves its first
  *              64 KiB (completion counters) zeroed again. It lets the k dimension be split across
  *              workgroups (the partial sums are added in a fixed order, so results stay
- *              deterministic), and for Q4_K at batch 1 it holds the activation digits of the
- *              int8 matrix-core kernel (after the first 64 KiB). NULL or too small: no split and
- *              no matrix-core kernel (slower; results still within the fp32 bar, though not
- *              bitwise those of a call with the workspace). Calls that run concurrently must not
- *              share a workspace.
+ *              deterministic), also for the int8 matrix-core kernel that takes Q4_K at batch 1
+ *              for k >= 16384 (its k-slice sums after the first 64 KiB). NULL or too small: no
+ *              split and no matrix-core kernel (slower; results still within the fp32 bar,
+ *              though not bitwise those of a call with the workspace). Calls that run
+ *              concurrently must not share a workspace.
  *   n >= 1, k >= block size with k % block == 0, 1 <= batch <= 4096. Weights are streamed once
  *   per group of up to 8 tokens; for Q4_K with 2..32 tokens (given the workspace) once for all of
  *   them, on the fp16 matrix cores with exact operands (each activation row scaled by a power of
@@ -120,8 +120,8 @@ int tq_gemv_multi(int type, int nparts, const void *const *w, const int64_t *n, 
  * 2..32 given the workspace (gate and up tiles side by side); otherwise two tq_gemv launches and
  * tq_swiglu through the workspace. w_gate, w_up [n][k]; x [batch][k] (16-byte aligned); h
  * [batch][n] fp32. workspace: tq_gemv_swiglu_workspace_bytes(type, n, k, batch) bytes, 256-byte
- * aligned; on the one-launch path it holds the activation digits of the int8 matrix-core kernel
- * and may be NULL or smaller (the lanes-along-k kernel runs instead). Bitwise equal to tq_gemv +
+ * aligned; on the one-launch path it holds the k-slice sums of the int8 matrix-core kernel
+ * (k >= 16384) and may be NULL or smaller (the lanes-along-k kernel runs instead). Bitwise equal to tq_gemv +
  * tq_gemv + tq_swiglu when each call gets the workspace it asks for.
  */
 size_t tq_gemv_swiglu_workspace_bytes(int type, int64_t n, int64_t k, int64_t batch);

@@ -145,16 +145,22 @@ GemvPlan plan_gemv(int64_t n, int64_t k, bool split_allowed) {
 
 static constexpr size_t kCounterBytes = 65536;  // one counter per row group: n <= 1M rows
 
-// Workspace of the int8 matrix-core path: the activation digits, after the counter area.
-static size_t i8_workspace_bytes(int fmt, int64_t k, int64_t batch) {
-  return i8_gemv_ok(fmt, k, batch) ? kCounterBytes + i8_digits_bytes(1, k) : 0;
+// Workspace of the int8 matrix-core path: counters, then the k slices' partial sums.
+static size_t i8_ws_bytes(int fmt, int64_t rows, int64_t k, int64_t batch) {
+  return i8_gemv_ok(fmt, k, batch) ? kCounterBytes + i8_workspace_bytes(rows, k) : 0;
 }
 
 // The int8 path runs when its workspace is there and x is 16-byte aligned.
-static bool use_i8(int fmt, int64_t k, const float *x, int64_t batch, const void *ws,
-                   size_t ws_bytes) {
-  const size_t need = i8_workspace_bytes(fmt, k, batch);
-  return need && ws != nullptr && ws_bytes >= need && ((uintptr_t)x & 15) == 0;
+static bool use_i8(int fmt, int64_t rows, int64_t k, const float *x, int64_t batch,
+                   const void *ws, size_t ws_bytes) {
+  const size_t need = i8_ws_bytes(fmt, rows, k, batch);
+  return need && ws != nullptr && ws_bytes >= need && ((uintptr_t)x & 15) == 0 &&
+         rows < (1ll << 30);
+}
+
+static int launch_i8(const KlMap &m, int64_t k, const float *x, void *ws, hipStream_t s) {
+  return launch_gemv_i8(m, k, x, (float *)((char *)ws + kCounterBytes), (unsigned *)ws,
+                        (int)(kCounterBytes / 4), s);
 }
 
 // Workspace of the fp16 matrix-core path for 2..32 tokens: counters, split x, slice sums.
@@ -181,7 +187,7 @@ static size_t split_workspace_bytes(int fmt, int64_t n, int64_t k) {
 static size_t max3(size_t a, size_t b, size_t c) { return a > b ? (a > c ? a : c) : (b > c ? b : c); }
 
 size_t gemv_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t batch) {
-  return max3(split_workspace_bytes(fmt, n, k), i8_workspace_bytes(fmt, k, batch),
+  return max3(split_workspace_bytes(fmt, n, k), i8_ws_bytes(fmt, n, k, batch),
               qmm_workspace_bytes(fmt, n, k, batch, false));
 }
 
@@ -536,7 +542,7 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, in
     return launch_qmm_dense(m, k, x, batch, (char *)ws + kCounterBytes, (unsigned *)ws,
                             (int)(kCounterBytes / 4), s);
   }
-  const bool i8 = use_i8(fmt, k, x, batch, ws, ws_bytes) && n < (1ll << 30);
+  const bool i8 = use_i8(fmt, n, k, x, batch, ws, ws_bytes);
   if (i8 || klane_ok(fmt, k, x, batch)) {
     KlMap m{};
     m.w[0] = wb;
@@ -545,7 +551,7 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, in
     m.nparts = 1;
     m.total = (int)n;
     m.row_bytes = rb;
-    if (i8) return launch_gemv_i8(m, k, x, (char *)ws + kCounterBytes, s);
+    if (i8) return launch_i8(m, k, x, ws, s);
     return launch_kl(m, k, x, s);
   }
   switch (fmt) {
@@ -565,7 +571,8 @@ size_t gemv_multi_workspace_bytes(int fmt, int nparts, const int64_t *n, int64_t
     total += n[p];
   }
   const size_t fused = qmm_workspace_bytes(fmt, total, k, batch, false);
-  return fused > b ? fused : b;
+  const size_t i8 = i8_ws_bytes(fmt, total, k, batch);
+  return max3(b, fused, i8);
 }
 
 int launch_gemv_multi(int fmt, int nparts, const void *const *w, const int64_t *n, float *const *y,
@@ -578,7 +585,7 @@ int launch_gemv_multi(int fmt, int nparts, const void *const *w, const int64_t *
     return launch_qmm_dense(m, k, x, batch, (char *)ws + kCounterBytes, (unsigned *)ws,
                             (int)(kCounterBytes / 4), s);
   }
-  const bool i8 = use_i8(fmt, k, x, batch, ws, ws_bytes);
+  const bool i8 = use_i8(fmt, total, k, x, batch, ws, ws_bytes);
   if ((i8 || klane_ok(fmt, k, x, batch)) && nparts <= 4 && total < (1ll << 30)) {
     KlMap m{};
     for (int p = 0; p < nparts; ++p) {
@@ -589,7 +596,7 @@ int launch_gemv_multi(int fmt, int nparts, const void *const *w, const int64_t *
     m.nparts = nparts;
     m.total = (int)total;
     m.row_bytes = k / fmt_block_weights(fmt) * fmt_block_bytes(fmt);
-    if (i8) return launch_gemv_i8(m, k, x, (char *)ws + kCounterBytes, s);
+    if (i8) return launch_i8(m, k, x, ws, s);
     return launch_kl(m, k, x, s);
   }
   for (int p = 0; p < nparts; ++p) {  // one launch per matrix, in order on the stream
@@ -611,7 +618,7 @@ static size_t swiglu_two_launch_bytes(int fmt, int64_t n, int64_t k, int64_t bat
 
 size_t gemv_swiglu_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t batch, bool fused) {
   const size_t qmm = qmm_workspace_bytes(fmt, n, k, batch, true);
-  if (fused) return i8_workspace_bytes(fmt, k, batch);
+  if (fused) return i8_ws_bytes(fmt, 2 * n, k, batch);
   const size_t two = swiglu_two_launch_bytes(fmt, n, k, batch);
   return qmm > two ? qmm : two;
 }
@@ -624,7 +631,7 @@ int launch_gemv_swiglu(int fmt, const void *wg, const void *wu, int64_t n, int64
                        const float *x, int64_t batch, float *h, void *ws, size_t ws_bytes,
                        hipStream_t s) {
   const int64_t rb = k / fmt_block_weights(fmt) * fmt_block_bytes(fmt);
-  const bool i8 = use_i8(fmt, k, x, batch, ws, ws_bytes);
+  const bool i8 = use_i8(fmt, 2 * n, k, x, batch, ws, ws_bytes);
   if ((i8 || klane_ok(fmt, k, x, batch)) && n < (1ll << 29)) {
     KlMap m{};
     m.w[0] = (const uint8_t *)wg;
@@ -635,7 +642,7 @@ int launch_gemv_swiglu(int fmt, const void *wg, const void *wu, int64_t n, int64
     m.total = (int)(2 * n);
     m.cum[1] = m.total;
     m.row_bytes = rb;
-    if (i8) return launch_gemv_i8(m, k, x, (char *)ws + kCounterBytes, s);
+    if (i8) return launch_i8(m, k, x, ws, s);
     return launch_kl(m, k, x, s);
   }
   if (use_qmm(fmt, n, k, x, batch, ws, ws_bytes, true)) {

@@ -8,18 +8,15 @@
 
 namespace tq {
 
-// Activation digits of `tokens` rows of k values (see tq_gemv_i8.hip for the layout).
-struct I8Digits {
-  int8_t *xd;
-  float *S;
-  float *unscale;
-};
-size_t i8_digits_bytes(int64_t tokens, int64_t k);
-I8Digits i8_digits_at(void *base, int64_t tokens, int64_t k);
-
-// Shapes the int8 kernel takes: Q4_K, one token, k a multiple of 256 (by default k >= 16384).
+// Shapes the int8 kernel takes: Q4_K, one token, k a multiple of 256, 16384 <= k <= 32768 (all
+// k <= 32768 with TQ_GEMV_I8=2).
 bool i8_gemv_ok(int fmt, int64_t k, int64_t batch);
-// x [k] -> digits (in `digits`, i8_digits_bytes(1, k) bytes), then the rows of m.
-int launch_gemv_i8(const KlMap &m, int64_t k, const float *x, void *digits, hipStream_t s);
+// Workspace after the completion counters: the k slices' partial sums of `rows` rows (0 when k
+// is one slice).
+size_t i8_workspace_bytes(int64_t rows, int64_t k);
+// The rows of m against x [k] (16-byte aligned). partial: i8_workspace_bytes(m.total, k) bytes;
+// counters: zero, one per row group (max_counters of them), left zero.
+int launch_gemv_i8(const KlMap &m, int64_t k, const float *x, float *partial,
+                   unsigned *counters, int max_counters, hipStream_t s);
 
 }  // namespace tq

@@ -18,9 +18,11 @@
 // -dmin * m_j * S_j, both times the block's 2^-e. Everything before the fold is exact; the fold
 // is fp32.
 //
-// Work split: one workgroup per 32 rows; its waves take the row tile's blocks in turn (the count
-// of waves depends on k only, so a row's sum is formed in the same order whatever the matrix
-// height), then add their partial sums in LDS in wave order.
+// Work split: a workgroup takes one k slice (a number of blocks set by k alone) of 32 W rows, one
+// 32-row tile per wave. It first turns the slice of x into digits in LDS (16 threads per block),
+// then each wave streams its rows' blocks of the slice, the next block's loads in flight. With
+// more than one slice, the last workgroup of a row group to finish adds the slices' sums in slice
+// order. A row's sum is thus formed the same way whatever the matrix height or the launch.
 #include <hip/hip_runtime.h>
 
 #include "tq_device.h"
@@ -34,7 +36,10 @@ namespace tq {
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kDigitBlockBytes = 1024;  // one token's digits of one block: 8 sub-blocks x 4 x 32
+constexpr int kDigitBytes = 1024;  // one block's digits: 8 sub-blocks x 4 digits x 32 int8
+constexpr int kLdsBlock = 1088;    // per block in LDS: digits, S [h][q] (8 fp32), 2^-e (fp32), pad
+constexpr int kMaxSliceBlocks = 16;
+constexpr int kMaxSlices = 8;
 
 // Fractional bits v needs: the least e with v * 2^e an integer.
 __device__ __forceinline__ int frac_bits(float v) {
@@ -47,22 +52,12 @@ __device__ __forceinline__ int frac_bits(float v) {
   return f > 0 ? f : 0;
 }
 
-// ---- activation digits --------------------------------------------------------------------------
-// A thread per 16 values, the 16 threads of a 256-value block together. Layout per token row:
-// xd [kb][j][d][32 bytes] (the 32 digits d of sub-block j of block kb), S [kb][h][q] fp32 = sum
-// of x' over sub-block 2q + h, unscale [kb] = 2^-e of the block.
-__global__ __launch_bounds__(256) void k_x_digits(const float *__restrict__ x, int64_t ldx,
-                                                  int64_t T, int K, int8_t *__restrict__ xd,
-                                                  float *__restrict__ S,
-                                                  float *__restrict__ unscale) {
-  const int per_row = K / 16;  // a multiple of 16: the threads of a block are active together
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= T * per_row) return;
-  const int64_t t = gid / per_row;
-  const int gi = (int)(gid - t * per_row);
-  const int k0 = 16 * gi, kb = k0 >> 8, j = (k0 >> 5) & 7, hh = (k0 >> 4) & 1;
-  const int nblk = K / 256;
-  const float4 *x4 = reinterpret_cast<const float4 *>(x + t * ldx + k0);
+// Digits of values 16 gi .. 16 gi + 15 of one 256-value block of x (xb), written into the block's
+// LDS record (blk): 4 x 16 bytes at [j][d][16 hh], then the sub-block sums and 2^-e. The block's
+// 16 threads (16 consecutive lanes of one wave) call this together.
+__device__ __forceinline__ void make_digits(const float *__restrict__ xb, int gi, uint8_t *blk) {
+  const int j = gi >> 1, hh = gi & 1;  // sub-block j, half hh
+  const float4 *x4 = reinterpret_cast<const float4 *>(xb + 16 * gi);
   float v[16];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -91,8 +86,6 @@ __global__ __launch_bounds__(256) void k_x_digits(const float *__restrict__ x, i
     e = min(min(27 - ex, fb), 126);
   }
   const float s = ldexpf(1.f, e);
-  if ((gi & 15) == 0) unscale[t * nblk + kb] = ldexpf(1.f, -e);
-
   uint32_t dig[4][4];
   long long sum = 0;
 #pragma unroll
@@ -116,177 +109,220 @@ __global__ __launch_bounds__(256) void k_x_digits(const float *__restrict__ x, i
 #pragma unroll
     for (int d = 0; d < 4; ++d) dig[d][q] = b[d];
   }
-  int8_t *dst = xd + (t * nblk + kb) * kDigitBlockBytes + j * 128 + 16 * hh;
 #pragma unroll
   for (int d = 0; d < 4; ++d)
-    *reinterpret_cast<u32x4 *>(dst + 32 * d) = (u32x4){dig[d][0], dig[d][1], dig[d][2], dig[d][3]};
+    *reinterpret_cast<u32x4 *>(blk + j * 128 + 32 * d + 16 * hh) =
+        (u32x4){dig[d][0], dig[d][1], dig[d][2], dig[d][3]};
   // the sub-block's other half is the neighbouring thread's
   const int lo = __shfl_xor((int)(sum & 0xFFFFFFFFll), 1);
   const int hi = __shfl_xor((int)(sum >> 32), 1);
   sum += ((long long)hi << 32) | (unsigned)lo;
-  if (hh == 0) S[(t * nblk + kb) * 8 + (j & 1) * 4 + (j >> 1)] = (float)sum;
+  float *sf = reinterpret_cast<float *>(blk + kDigitBytes);
+  if (hh == 0) sf[(j & 1) * 4 + (j >> 1)] = (float)sum;
+  if (gi == 0) sf[8] = ldexpf(1.f, -e);
 }
 
-// ---- the product --------------------------------------------------------------------------------
+// One block of 32 rows: the lane's row header and quant half-bytes, its digit piece, its
+// sub-blocks' sums and the block's 2^-e -> the block's contribution to the lane's row (lanes l and
+// l + 32 hold the two sub-block parities of row l % 32).
+__device__ __forceinline__ float i8_block(const u32x4 &head, const u32x4 (&q)[4], const u32x4 &xa,
+                                          const u32x4 &S, float us, int my_sub, int h) {
+  const i32x16 zero = {};
+  i32x16 C;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const u32x4 &qw = q[j >> 1];
+    const u32x4 bq = (j & 1) ? ((qw >> 4u) & 0x0F0F0F0Fu) : (qw & 0x0F0F0F0Fu);
+    const u32x4 a = my_sub == j ? xa : (u32x4){0u, 0u, 0u, 0u};
+    C = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
+                                              __builtin_bit_cast(i32x4, bq), j == 0 ? zero : C,
+                                              0, 0, 0);
+  }
+  // the lane's sub-blocks 2q + h: scales and mins (bytes 0 and 2 after a shift by 8h)
+  const uint32_t h0 = head.x, s0 = head.y, s1 = head.z, s2 = head.w;
+  const float d = half_bits_to_float(h0), dmin = half_bits_to_float(h0 >> 16);
+  const uint32_t sh = 8u * (uint32_t)h;
+  const uint32_t sc_lo = (s0 & 0x3F3F3F3Fu) >> sh;
+  const uint32_t sc_hi = ((s2 & 0x0F0F0F0Fu) | ((s0 >> 2) & 0x30303030u)) >> sh;
+  const uint32_t m_lo = (s1 & 0x3F3F3F3Fu) >> sh;
+  const uint32_t m_hi = (((s2 >> 4) & 0x0F0F0F0Fu) | ((s1 >> 2) & 0x30303030u)) >> sh;
+  const float sc[4] = {byte_to_float(sc_lo, 0), byte_to_float(sc_lo, 2), byte_to_float(sc_hi, 0),
+                       byte_to_float(sc_hi, 2)};
+  const float mn[4] = {byte_to_float(m_lo, 0), byte_to_float(m_lo, 2), byte_to_float(m_hi, 0),
+                       byte_to_float(m_hi, 2)};
+  float bs = 0.f;
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    // rows 8 qq + 4h + digit of the accumulator: sub-block 2 qq + h, digits 0..3
+    const int lo3 = C[4 * qq] + (C[4 * qq + 1] << 7) + (C[4 * qq + 2] << 14);
+    const float f = __builtin_fmaf((float)C[4 * qq + 3], 0x1p21f, (float)lo3);
+    bs = __builtin_fmaf(sc[qq], f, bs);
+  }
+  const float sv[4] = {__uint_as_float(S.x), __uint_as_float(S.y), __uint_as_float(S.z),
+                       __uint_as_float(S.w)};
+  float ms = 0.f;
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) ms = __builtin_fmaf(mn[qq], sv[qq], ms);
+  return __builtin_fmaf(d * us, bs, -dmin * us * ms);
+}
 
-template <int NTOK>
-__global__ __launch_bounds__(1024) void k_gemv_i8(KlMap m, int nblk, I8Digits dg, int ldy_rows) {
-  __shared__ float red[16][NTOK][32];
-  const int lane = threadIdx.x & 63, w = wave_index(), W = blockDim.x >> 6;
+// Output of virtual row v (multi: the part it falls in).
+__device__ __forceinline__ void i8_store(const KlMap &m, int v, float s) {
+  int p = 0;
+#pragma unroll
+  for (int k = 1; k < 4; ++k) p += (k < m.nparts && v >= m.cum[k]) ? 1 : 0;
+  m.y[p][v - m.cum[p]] = s;
+}
+
+__global__ __launch_bounds__(256) void k_gemv_i8(KlMap m, const float *__restrict__ x, int nblk,
+                                                 int upk, int ksplit, float *__restrict__ partial,
+                                                 unsigned *__restrict__ counters) {
+  __shared__ __attribute__((aligned(16))) uint8_t xl[kMaxSliceBlocks * kLdsBlock];
+  __shared__ float red[4][32];
+  __shared__ int is_last;
+  const int W = blockDim.x >> 6;  // row tiles of this workgroup
+  const int grp = blockIdx.x / ksplit, ks = blockIdx.x - grp * ksplit;
+  const int kb0 = ks * upk, nb = min(upk, nblk - kb0);
+  const int lane = threadIdx.x & 63, w = wave_index();
   const int n = lane & 31, h = lane >> 5;
-  const int r0 = blockIdx.x * 32;
-  const uint8_t *row = m.row(min(r0 + n, m.total - 1));
-  const int my_sub = n >> 2;  // the sub-block whose digit row this lane supplies
-
+  const int r0 = grp * 32 * W + 32 * w;
+  const uint8_t *row = m.row(min(r0 + n, m.total - 1)) + (int64_t)kb0 * 144;
   struct Blk {
     u32x4 head, q[4];
-    u32x4 xa[NTOK];
-    u32x4 S[NTOK];  // fp32 bits
-    uint32_t us[NTOK];  // the block's 2^-e, fp32 bits
   };
   auto load = [&](Blk &b, int kb) {
     const uint8_t *p = row + (int64_t)kb * 144;
     b.head = gload(p);
 #pragma unroll
     for (int c = 0; c < 4; ++c) b.q[c] = gload(p + 16 + 32 * c + 16 * h);
-#pragma unroll
-    for (int t = 0; t < NTOK; ++t) {
-      const int64_t blk = (int64_t)t * nblk + kb;
-      b.xa[t] = gload(dg.xd + blk * kDigitBlockBytes + n * 32 + 16 * h);
-      b.S[t] = gload(dg.S + blk * 8 + 4 * h);
-      b.us[t] = *(const uint32_t __attribute__((address_space(1))) *)(dg.unscale + blk);
-    }
   };
-  float acc[NTOK];
-#pragma unroll
-  for (int t = 0; t < NTOK; ++t) acc[t] = 0.f;
-  const i32x16 zero = {};
-
-  auto compute = [&](const Blk &b) {
-    i32x16 C[NTOK];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const u32x4 &qw = b.q[j >> 1];
-      const u32x4 bq = (j & 1) ? ((qw >> 4u) & 0x0F0F0F0Fu) : (qw & 0x0F0F0F0Fu);
-      const bool mine = my_sub == j;
-#pragma unroll
-      for (int t = 0; t < NTOK; ++t) {
-        const u32x4 a = mine ? b.xa[t] : (u32x4){0u, 0u, 0u, 0u};
-        C[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
-                                                     __builtin_bit_cast(i32x4, bq),
-                                                     j == 0 ? zero : C[t], 0, 0, 0);
-      }
-    }
-    // the lane's sub-blocks 2q + h: scales and mins (bytes 0 and 2 after a shift by 8h)
-    const uint32_t h0 = b.head.x, s0 = b.head.y, s1 = b.head.z, s2 = b.head.w;
-    const float d = half_bits_to_float(h0), dmin = half_bits_to_float(h0 >> 16);
-    const uint32_t sh = 8u * (uint32_t)h;
-    const uint32_t sc_lo = (s0 & 0x3F3F3F3Fu) >> sh;
-    const uint32_t sc_hi = ((s2 & 0x0F0F0F0Fu) | ((s0 >> 2) & 0x30303030u)) >> sh;
-    const uint32_t m_lo = (s1 & 0x3F3F3F3Fu) >> sh;
-    const uint32_t m_hi = (((s2 >> 4) & 0x0F0F0F0Fu) | ((s1 >> 2) & 0x30303030u)) >> sh;
-    const float sc[4] = {byte_to_float(sc_lo, 0), byte_to_float(sc_lo, 2), byte_to_float(sc_hi, 0),
-                         byte_to_float(sc_hi, 2)};
-    const float mn[4] = {byte_to_float(m_lo, 0), byte_to_float(m_lo, 2), byte_to_float(m_hi, 0),
-                         byte_to_float(m_hi, 2)};
-#pragma unroll
-    for (int t = 0; t < NTOK; ++t) {
-      float bs = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        // rows 8q + 4h + digit of the accumulator: sub-block 2q + h, digits 0..3
-        const int lo3 = C[t][4 * q] + (C[t][4 * q + 1] << 7) + (C[t][4 * q + 2] << 14);
-        const float f = __builtin_fmaf((float)C[t][4 * q + 3], 0x1p21f, (float)lo3);
-        bs = __builtin_fmaf(sc[q], f, bs);
-      }
-      const float sv[4] = {__uint_as_float(b.S[t].x), __uint_as_float(b.S[t].y),
-                           __uint_as_float(b.S[t].z), __uint_as_float(b.S[t].w)};
-      float ms = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) ms = __builtin_fmaf(mn[q], sv[q], ms);
-      const float us = __uint_as_float(b.us[t]);
-      acc[t] = __builtin_fmaf(d * us, bs, __builtin_fmaf(-dmin * us, ms, acc[t]));
-    }
+  auto compute = [&](const Blk &b, int kb) {
+    const uint8_t *l = xl + kb * kLdsBlock;
+    const u32x4 xa = *reinterpret_cast<const u32x4 *>(l + n * 32 + 16 * h);
+    const u32x4 S = *reinterpret_cast<const u32x4 *>(l + kDigitBytes + 16 * h);
+    const float us = *reinterpret_cast<const float *>(l + kDigitBytes + 32);
+    return i8_block(b.head, b.q, xa, S, us, n >> 2, h);
   };
-
-  // the wave's blocks w, w + W, ..., one block ahead in registers
+  // the first two blocks' weights are requested before the digits are made, so both latencies
+  // overlap; then two blocks stay in flight ahead of the one being computed
   Blk b0, b1;
-  int kb = w;
-  if (kb < nblk) load(b0, kb);
-  while (kb < nblk) {
-    if (kb + W < nblk) load(b1, kb + W);
-    compute(b0);
-    kb += W;
-    if (kb >= nblk) break;
-    if (kb + W < nblk) load(b0, kb + W);
-    compute(b1);
-    kb += W;
+  load(b0, 0);
+  if (nb > 1) load(b1, 1);
+  // the slice of x as digits (16 threads per block; groups of 16 stay active together)
+  for (int i = threadIdx.x; i < 16 * nb; i += blockDim.x)
+    make_digits(x + (int64_t)(kb0 + (i >> 4)) * 256, i & 15, xl + (i >> 4) * kLdsBlock);
+  __syncthreads();
+  float acc = 0.f;
+  for (int kb = 0;;) {
+    acc += compute(b0, kb);
+    if (++kb >= nb) break;
+    if (kb + 1 < nb) load(b0, kb + 1);
+    acc += compute(b1, kb);
+    if (++kb >= nb) break;
+    if (kb + 1 < nb) load(b1, kb + 1);
   }
+  acc += __shfl_xor(acc, 32);  // the two sub-block parities of the row
 
-  // rows: the two parities, then the waves in order
+  if (ksplit == 1) {
+    const float u = __shfl_down(acc, 1);
+    const int v = r0 + n;
+    if (h == 0) {
+      if (m.swiglu) {
+        if ((n & 1) == 0 && v + 1 < m.total) m.y[0][v >> 1] = silu_mul(acc, u);
+      } else if (v < m.total) {
+        i8_store(m, v, acc);
+      }
+    }
+    return;
+  }
+  // k slices: this slice's sums (device-coherent stores, completed before the arrival is
+  // counted); the last workgroup of the row group adds them in slice order, resets the counter
+  const int rows = 32 * W;
+  float *mine = partial + ((int64_t)grp * ksplit + ks) * rows;
+  if (h == 0)
+    __hip_atomic_store(mine + 32 * w + n, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  if (threadIdx.x == 0)
+    is_last = __hip_atomic_fetch_add(&counters[grp], 1u, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(ksplit - 1);
+  __syncthreads();
+  if (!is_last) return;
+  const float *base = partial + (int64_t)grp * ksplit * rows;
+  for (int i = threadIdx.x; i < rows; i += blockDim.x) {
+    float vals[kMaxSlices];
 #pragma unroll
-  for (int t = 0; t < NTOK; ++t) {
-    acc[t] += __shfl_xor(acc[t], 32);
-    if (h == 0) red[w][t][n] = acc[t];
+    for (int q = 0; q < kMaxSlices; ++q)  // every slice's value in flight, then the sum
+      vals[q] = q < ksplit ? __hip_atomic_load(base + (int64_t)q * rows + i, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT)
+                           : 0.f;
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < kMaxSlices; ++q)
+      if (q < ksplit) s += vals[q];
+    red[i >> 5][i & 31] = s;
   }
   __syncthreads();
-  if ((int)threadIdx.x < 32 * NTOK) {
-    const int t = threadIdx.x >> 5, i = threadIdx.x & 31;
-    float s = 0.f;
-    for (int q = 0; q < W; ++q) s += red[q][t][i];
-    const int v = r0 + i;
+  for (int i = threadIdx.x; i < rows; i += blockDim.x) {
+    const int v = grp * rows + i;
+    const float s = red[i >> 5][i & 31];
     if (m.swiglu) {
-      // virtual rows alternate gate, up; the even lane combines its pair
-      const float u = __shfl_down(s, 1);
-      if ((i & 1) == 0 && v + 1 < m.total) m.y[0][(int64_t)t * ldy_rows + (v >> 1)] = silu_mul(s, u);
+      if ((i & 1) == 0 && v + 1 < m.total) m.y[0][v >> 1] = silu_mul(s, red[i >> 5][(i & 31) + 1]);
     } else if (v < m.total) {
-      int p = 0;
-#pragma unroll
-      for (int k = 1; k < 4; ++k) p += (k < m.nparts && v >= m.cum[k]) ? 1 : 0;
-      m.y[p][(int64_t)t * (m.cum[p + 1] - m.cum[p]) + (v - m.cum[p])] = s;
+      i8_store(m, v, s);
     }
   }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&counters[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---- host side ----------------------------------------------------------------------------------
 
-size_t i8_digits_bytes(int64_t tokens, int64_t k) {
-  return (size_t)(align256(tokens * 4 * k) + align256(tokens * (k / 8)) +
-                  align256(tokens * (k / 64)));
-}
-
-I8Digits i8_digits_at(void *base, int64_t tokens, int64_t k) {
-  char *p = (char *)base;
-  I8Digits d;
-  d.xd = (int8_t *)p;
-  d.S = (float *)(p + align256(tokens * 4 * k));
-  d.unscale = (float *)(p + align256(tokens * 4 * k) + align256(tokens * (k / 8)));
-  return d;
-}
-
-// Taken from k = 16384 on: below that the lanes-along-k kernel, which reads x as it is, is as fast
-// once the digits pass (a launch of its own) is counted; above it that kernel's per-weight VALU
-// work and its workgroups of k / 4096 waves hold it to about half the rate of this one.
-// TQ_GEMV_I8: 0 never, 2 for every Q4_K batch-1 shape (tests and tuning), else the rule above.
+// Q4_K, one token, k a multiple of 256 up to 32768; by default from k = 16384 on. Below that the
+// lanes-along-k kernel is as fast on the measured shapes (inside a graph, the 8B-shaped step
+// 1.60 ms against 1.86 ms with this kernel everywhere), above it this one is about twice as fast
+// (8192 x 28672: 26 us against 58 us) -- that kernel's workgroups of k / 4096 waves and its VALU
+// work per weight hold it back there. TQ_GEMV_I8: 0 never, 2 every such shape (tests, tuning).
 bool i8_gemv_ok(int fmt, int64_t k, int64_t batch) {
   const int mode = env_int("TQ_GEMV_I8", 1);
-  if (mode == 0 || fmt != FMT_Q4_K || batch != 1 || k % 256 != 0 || k < 256) return false;
+  if (mode == 0 || fmt != FMT_Q4_K || batch != 1 || k % 256 != 0 || k < 256 ||
+      k > 256 * kMaxSliceBlocks * kMaxSlices)
+    return false;
   return mode == 2 || k >= 16384;
 }
 
-// Waves per workgroup: about two blocks each, at most 16 (a function of k only).
-static int i8_waves(int nblk) { return clampi(nblk / 2, 1, 16); }
-
-int launch_gemv_i8(const KlMap &m, int64_t k, const float *x, void *digits, hipStream_t s) {
+// Blocks per k slice, a function of k only: at least four, at most 8 slices.
+static int i8_upk(int64_t k) {
   const int nblk = (int)(k / 256);
-  const I8Digits dg = i8_digits_at(digits, 1, k);
-  const int64_t threads = k / 16;
-  hipLaunchKernelGGL(k_x_digits, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, x, k,
-                     (int64_t)1, (int)k, dg.xd, dg.S, dg.unscale);
-  const int W = i8_waves(nblk);
-  const int grid = (m.total + 31) / 32;
-  int ldy = m.swiglu ? m.total / 2 : 0;
-  hipLaunchKernelGGL(k_gemv_i8<1>, dim3((unsigned)grid), dim3(64 * W), 0, s, m, nblk, dg, ldy);
+  const int least = (nblk + kMaxSlices - 1) / kMaxSlices;
+  const int v = env_int("TQ_I8_UPK", 4);
+  return clampi(v > least ? v : least, 1, nblk);
+}
+
+// Row tiles per workgroup: 4 (128 rows) while that gives 512 workgroups, else fewer.
+static int i8_tiles_per_wg(int64_t rows, int ksplit) {
+  for (int W = 4; W > 1; W >>= 1)
+    if (((rows + 32 * W - 1) / (32 * W)) * ksplit >= 512) return W;
+  return 1;
+}
+
+size_t i8_workspace_bytes(int64_t rows, int64_t k) {
+  const int nblk = (int)(k / 256), upk = i8_upk(k), ksplit = (nblk + upk - 1) / upk;
+  if (ksplit == 1) return 0;
+  const int W = i8_tiles_per_wg(rows, ksplit);
+  const int64_t groups = (rows + 32 * W - 1) / (32 * W);
+  return (size_t)align256(groups * ksplit * 32 * W * 4);
+}
+
+int launch_gemv_i8(const KlMap &m, int64_t k, const float *x, float *partial,
+                   unsigned *counters, int max_counters, hipStream_t s) {
+  const int nblk = (int)(k / 256), upk = i8_upk(k), ksplit = (nblk + upk - 1) / upk;
+  if (upk > kMaxSliceBlocks || ksplit > kMaxSlices) return -2;
+  const int W = i8_tiles_per_wg(m.total, ksplit);
+  const int groups = (m.total + 32 * W - 1) / (32 * W);
+  if (ksplit > 1 && groups > max_counters) return -2;
+  hipLaunchKernelGGL(k_gemv_i8, dim3((unsigned)(groups * ksplit)), dim3(64 * W), 0, s, m, x, nblk,
+                     upk, ksplit, partial, counters);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
