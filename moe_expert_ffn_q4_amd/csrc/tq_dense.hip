@@ -263,23 +263,25 @@ __global__ __launch_bounds__(512) void k_gemv(const uint8_t *__restrict__ w, int
     __hip_atomic_store(&counters[rg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Batch-1 Q4_K GEMV, lanes along k (see tq_gemv_core.h). Workgroup = ceil(nblk / 16) waves
-// covering all of k; it computes rows [blockIdx.x * rows_per_wg, ...) R at a time, loading the
-// next R rows while it computes the current ones.
+// Batch-1 Q4_K GEMV, lanes along k (see tq_gemv_core.h). A lane group of 64 / G lanes covers all
+// of k (G > 1 only when k fits in 16 / G blocks, so that short rows leave no lane idle); group g of
+// a pass over rows r0.. computes rows r0 + g R .. r0 + g R + R - 1.
 
-template <int R>
+template <int R, int G>
 __device__ __forceinline__ void kl_rows(const u32x4 (&v)[R][3], const float (&xv)[64], float sx_lo,
                                         float sx_hi, const Q4kField &f0, const Q4kField &f1,
-                                        float unit_inv, int r0, int re, float (*red)[R],
+                                        float unit_inv, int r0, int re, float (*red)[G * R],
                                         const KlMap &m) {
+  constexpr int L = 64 / G;  // lanes per group
+  static_assert(L >= R, "a group needs at least one lane per row");
   const int lane = threadIdx.x & 63, wave = wave_index(), nw = blockDim.x >> 6;
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = kl_group_dot(v[r], xv, sx_lo, sx_hi, f0, f1, unit_inv);
-  // across the 64 lanes: each step halves the rows a lane keeps and adds its partner's half
+  // across the group's lanes: each step halves the rows a lane keeps and adds its partner's half
   int cnt = R;
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
+  for (int d = L / 2; d >= 1; d >>= 1) {
     if (cnt > 1) {
       const bool upper = (lane & d) != 0;
       const int h = cnt >> 1;
@@ -295,18 +297,19 @@ __device__ __forceinline__ void kl_rows(const u32x4 (&v)[R][3], const float (&xv
       acc[0] += __shfl_xor(acc[0], d);
     }
   }
-  // lane l now holds row sum_s bit(l, 5-s) * R / 2^(s+1); lanes with zero low bits store it
-  if ((lane & (64 / R - 1)) == 0) {
-    int row = 0;
+  // lane l of group g now holds row g R + sum_s bit(l, log2(L) - 1 - s) * R / 2^(s+1); lanes with
+  // zero low bits store it
+  if ((lane & (L / R - 1)) == 0) {
+    int row = (lane / L) * R;
 #pragma unroll
     for (int sidx = 0, half = R >> 1; half >= 1; ++sidx, half >>= 1)
-      if (lane & (32 >> sidx)) row += half;
+      if (lane & ((L / 2) >> sidx)) row += half;
     red[wave][row] = acc[0];
   }
   __syncthreads();
   if (m.swiglu) {  // rows (gate r, up r) pairs; r0 and re are even
     const int i = 2 * (int)threadIdx.x;
-    if (i < R && r0 + i < re) {
+    if (i < G * R && r0 + i < re) {
       float g = 0.f, u = 0.f;
       for (int q = 0; q < nw; ++q) {
         g += red[q][i];
@@ -314,7 +317,7 @@ __device__ __forceinline__ void kl_rows(const u32x4 (&v)[R][3], const float (&xv
       }
       m.y[0][(r0 + i) >> 1] = silu_mul(g, u);
     }
-  } else if (threadIdx.x < R && r0 + (int)threadIdx.x < re) {
+  } else if (threadIdx.x < G * R && r0 + (int)threadIdx.x < re) {
     float s = 0.f;
     for (int q = 0; q < nw; ++q) s += red[q][threadIdx.x];
     *m.out(r0 + threadIdx.x) = s;
@@ -322,20 +325,20 @@ __device__ __forceinline__ void kl_rows(const u32x4 (&v)[R][3], const float (&xv
   __syncthreads();
 }
 
-// Batch-1 Q4_K GEMV, lanes along k (see tq_gemv_core.h). Workgroup = ceil(nblk / 16) waves
-// covering all of k; it computes rows [blockIdx.x * rows_per_wg, ...) R at a time, loading the
-// next R rows while it computes the current ones (two register buffers used in turn).
-template <int R>
+// Rows [rb, re) of the workgroup, G R per pass, loading the next pass's rows while it computes the
+// current ones (two register buffers used in turn).
+template <int R, int G>
 __device__ __forceinline__ void kl_body(const KlMap &m, int nblk, int rb, int re,
-                                        const float *__restrict__ x, float (*red)[R]) {
+                                        const float *__restrict__ x, float (*red)[G * R]) {
+  constexpr int L = 64 / G, P = G * R;
   const int lane = threadIdx.x & 63, wave = wave_index();
-  const int b = 16 * wave + (lane >> 2), c = lane & 3;
+  const int b = (L / 4) * wave + ((lane & (L - 1)) >> 2), c = lane & 3, g = lane / L;
   const bool valid = b < nblk;
   const int bb = valid ? b : nblk - 1;
   const int boff = bb * 144;
   u32x4 va[R][3], vb[R][3];
   // the first rows' weights are requested before the activations
-  if (rb < re) kl_load_rows<R>(m, rb, boff, c, va);
+  if (rb < re) kl_load_rows<R>(m, rb + g * R, boff, c, va);
   float xv[64];
   {
     const float4 *xp = reinterpret_cast<const float4 *>(x + 256 * bb + 64 * c);
@@ -356,34 +359,34 @@ __device__ __forceinline__ void kl_body(const KlMap &m, int nblk, int rb, int re
   }
   const float unit_inv = 1.f / nibble_fp8_unit();
   const Q4kField f0 = q4k_field(2 * c), f1 = q4k_field(2 * c + 1);
-  for (int r0 = rb; r0 < re; r0 += 2 * R) {
-    if (r0 + R < re) kl_load_rows<R>(m, r0 + R, boff, c, vb);
-    kl_rows<R>(va, xv, sx_lo, sx_hi, f0, f1, unit_inv, r0, re, red, m);
-    if (r0 + R >= re) break;
-    if (r0 + 2 * R < re) kl_load_rows<R>(m, r0 + 2 * R, boff, c, va);
-    kl_rows<R>(vb, xv, sx_lo, sx_hi, f0, f1, unit_inv, r0 + R, re, red, m);
+  for (int r0 = rb; r0 < re; r0 += 2 * P) {
+    if (r0 + P < re) kl_load_rows<R>(m, r0 + P + g * R, boff, c, vb);
+    kl_rows<R, G>(va, xv, sx_lo, sx_hi, f0, f1, unit_inv, r0, re, red, m);
+    if (r0 + P >= re) break;
+    if (r0 + 2 * P < re) kl_load_rows<R>(m, r0 + 2 * P + g * R, boff, c, va);
+    kl_rows<R, G>(vb, xv, sx_lo, sx_hi, f0, f1, unit_inv, r0 + P, re, red, m);
   }
 }
 
 // Batch-1 Q4_K GEMV, lanes along k (see tq_gemv_core.h). Workgroup = ceil(nblk / 16) waves
 // covering all of k; it computes rows [blockIdx.x * rows_per_wg, ...) R at a time, loading the
 // next R rows while it computes the current ones (two register buffers used in turn).
-template <int R>
+template <int R, int G>
 __global__ __launch_bounds__(512) void k_gemv_kl(KlMap m, int nblk, int rows_per_wg,
                                                  const float *__restrict__ x) {
-  __shared__ float red[8][R];
+  __shared__ float red[8][G * R];
   const int rb = blockIdx.x * rows_per_wg, re = min(rb + rows_per_wg, m.total);
-  kl_body<R>(m, nblk, rb, re, x, red);
+  kl_body<R, G>(m, nblk, rb, re, x, red);
 }
 
 // The same kernel over the experts of a one-token MoE step: workgroup b works on active slot
 // slot0 + b / wgs_per_slot (every active expert has that one token). gate/up: the expert's
 // gate and up rows interleaved with the SwiGLU in the epilogue, x = the token's activations,
 // h[position][ffn] out; down: x = h[position], o[position][hidden] out.
-template <int R>
+template <int R, int G>
 __global__ __launch_bounds__(512) void k_moe_kl(MoeKlArgs a, int nblk, int rows_per_wg,
                                                 int wgs_per_slot) {
-  __shared__ float red[8][R];
+  __shared__ float red[8][G * R];
   const int slot = a.slot0 + (int)blockIdx.x / wgs_per_slot;
   if (slot >= *a.n_active) return;
   const int e = a.act[slot], p = a.act[a.act_stride + slot];
@@ -411,7 +414,7 @@ __global__ __launch_bounds__(512) void k_moe_kl(MoeKlArgs a, int nblk, int rows_
   if (a.gate_up) xrow = p >= a.Tk ? p - a.Tk : a.pairs[p] / a.topk;
   const int rb = ((int)blockIdx.x % wgs_per_slot) * rows_per_wg;
   const int re = min(rb + rows_per_wg, a.rows);
-  kl_body<R>(m, nblk, rb, re, a.x + xrow * a.ldx, red);
+  kl_body<R, G>(m, nblk, rb, re, a.x + xrow * a.ldx, red);
 }
 
 // Fallback for shapes whose rows are not dword aligned (Q6_K with k % 512 != 0, Q8_0 with
@@ -476,25 +479,44 @@ static bool klane_ok(int fmt, int64_t k, const float *x, int64_t batch) {
          k <= 8 * 4096;
 }
 
+// Lane groups per wave: 4 for k <= 1024, 2 for k <= 2048, else 1 (TQ_KL_GROUPS=1 turns them off).
+static int kl_groups(int nblk) {
+  const int allow = env_int("TQ_KL_GROUPS", 4);
+  const int g = nblk <= 4 ? 4 : nblk <= 8 ? 2 : 1;
+  return g < allow ? g : allow >= 4 ? 4 : allow >= 2 ? 2 : 1;
+}
+
+// Workgroup rows: whole passes of G R rows, as many as bring the launch near `target` waves.
+static int kl_rows_per_wg(int64_t rows, int waves, int pass, int target) {
+  int64_t chunks = (rows * waves + (int64_t)pass * target - 1) / ((int64_t)pass * target);
+  return pass * (int)(chunks < 1 ? 1 : chunks);  // even: SwiGLU pairs never straddle two workgroups
+}
+
+template <int R, int G>
+static void launch_kl_rg(const KlMap &m, int nblk, int waves, int target, const float *x,
+                         hipStream_t s) {
+  const int rows_per_wg = kl_rows_per_wg(m.total, waves, G * R, target);
+  const int grid = (m.total + rows_per_wg - 1) / rows_per_wg;
+  hipLaunchKernelGGL((k_gemv_kl<R, G>), dim3((unsigned)grid), dim3(64 * waves), 0, s, m, nblk,
+                     rows_per_wg, x);
+}
+
 static int launch_kl(const KlMap &m, int64_t k, const float *x, hipStream_t s) {
   const int nblk = (int)(k / 256);
   const int waves = (nblk + 15) / 16;
   static const int kl_rows_env = env_int("TQ_KL_ROWS", 4);
   static const int target = env_int("TQ_KL_TARGET_WAVES", 2048);
-  const int R = kl_rows_env == 2 ? 2 : kl_rows_env == 8 ? 8 : 4;
-  int chunks = (int)(((int64_t)m.total * waves + (int64_t)R * target - 1) / ((int64_t)R * target));
-  chunks = chunks < 1 ? 1 : chunks;
-  const int rows_per_wg = R * chunks;  // even: SwiGLU pairs never straddle two workgroups
-  const int grid = (m.total + rows_per_wg - 1) / rows_per_wg;
-  if (R == 2)
-    hipLaunchKernelGGL(k_gemv_kl<2>, dim3((unsigned)grid), dim3(64 * waves), 0, s, m, nblk,
-                       rows_per_wg, x);
-  else if (R == 8)
-    hipLaunchKernelGGL(k_gemv_kl<8>, dim3((unsigned)grid), dim3(64 * waves), 0, s, m, nblk,
-                       rows_per_wg, x);
+  const int G = kl_groups(nblk);
+  if (kl_rows_env == 2)
+    launch_kl_rg<2, 1>(m, nblk, waves, target, x, s);
+  else if (kl_rows_env == 8)
+    launch_kl_rg<8, 1>(m, nblk, waves, target, x, s);
+  else if (G == 4)
+    launch_kl_rg<4, 4>(m, nblk, waves, target, x, s);
+  else if (G == 2)
+    launch_kl_rg<4, 2>(m, nblk, waves, target, x, s);
   else
-    hipLaunchKernelGGL(k_gemv_kl<4>, dim3((unsigned)grid), dim3(64 * waves), 0, s, m, nblk,
-                       rows_per_wg, x);
+    launch_kl_rg<4, 1>(m, nblk, waves, target, x, s);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -504,18 +526,26 @@ bool moe_klane_ok(int fmt, int64_t hidden, int64_t ffn, int64_t tokens) {
          hidden <= 8 * 4096 && ffn <= 8 * 4096;
 }
 
+template <int G>
+static void launch_moe_kl_g(const MoeKlArgs &a, int nblk, int waves, int nslots, int target,
+                            hipStream_t s) {
+  const int rows_per_wg = kl_rows_per_wg((int64_t)a.rows * nslots, waves, G * 4, target);
+  const int wgs_per_slot = (a.rows + rows_per_wg - 1) / rows_per_wg;
+  hipLaunchKernelGGL((k_moe_kl<4, G>), dim3((unsigned)(nslots * wgs_per_slot)), dim3(64 * waves), 0,
+                     s, a, nblk, rows_per_wg, wgs_per_slot);
+}
+
 int launch_moe_kl(const MoeKlArgs &a, int64_t k, int nslots, hipStream_t s) {
   const int nblk = (int)(k / 256);
   const int waves = (nblk + 15) / 16;
   static const int target = env_int("TQ_KL_TARGET_WAVES", 2048);
-  const int R = 4;
-  int chunks = (int)(((int64_t)a.rows * nslots * waves + (int64_t)R * target - 1) /
-                     ((int64_t)R * target));
-  chunks = chunks < 1 ? 1 : chunks;
-  const int rows_per_wg = R * chunks;  // even: SwiGLU pairs stay in one workgroup
-  const int wgs_per_slot = (a.rows + rows_per_wg - 1) / rows_per_wg;
-  hipLaunchKernelGGL(k_moe_kl<4>, dim3((unsigned)(nslots * wgs_per_slot)), dim3(64 * waves), 0, s,
-                     a, nblk, rows_per_wg, wgs_per_slot);
+  const int G = kl_groups(nblk);
+  if (G == 4)
+    launch_moe_kl_g<4>(a, nblk, waves, nslots, target, s);
+  else if (G == 2)
+    launch_moe_kl_g<2>(a, nblk, waves, nslots, target, s);
+  else
+    launch_moe_kl_g<1>(a, nblk, waves, nslots, target, s);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

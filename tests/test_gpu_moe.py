@@ -217,3 +217,16 @@ def test_moe_grouping_many_tokens_many_experts():
     layer = synth.moe_layer(shape, "q4_k", seed=208, tag="many")
     x = synth.normal_f32(synth.rng(208, "x"), (8192, 256))
     check_moe("q4_k", shape, layer, x, 8, tokens=[0, 4095, 8191], path=tq.PATH_F32)
+
+
+def test_moe_one_token_lane_groups_bitwise(monkeypatch):
+    """One-token Q4_K steps with k <= 2048 per product (hidden 2048: gate/up in 2 lane groups per
+    wave; ffn 1024: down in 4) give bitwise the whole-wave results (TQ_KL_GROUPS=1)."""
+    t, shape, k = "q4_k", dict(hidden=2048, ffn=1024, n_experts=8, shared=True), 2
+    layer = synth.moe_layer(shape, t, seed=215, tag="kl-groups")
+    x = synth.normal_f32(synth.rng(215, "x"), (1, shape["hidden"]))
+    _case("moe-kl-groups", shape, k)
+    moe, y, _ = check_moe(t, shape, layer, x, k)
+    monkeypatch.setenv("TQ_KL_GROUPS", "1")
+    y1, _ = _run(moe, x, shape["n_experts"], k)
+    assert np.array_equal(y, y1)
