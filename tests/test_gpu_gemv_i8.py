@@ -22,6 +22,7 @@ tq = pytest.importorskip("moe_expert_ffn_q4_amd")
 @pytest.fixture
 def i8(monkeypatch):
     monkeypatch.setenv("TQ_GEMV_I8", "2")
+    monkeypatch.setenv("TQ_GEMV_I8S", "0")  # the k-sliced kernel, not the streaming one
 
 
 def _case(*a):
@@ -42,8 +43,8 @@ def test_i8_gemv_random(i8, n, k):
 
 
 def test_i8_gemv_default_threshold():
-    """Without the override the kernel takes k >= 16384 (and agrees with the oracle there)."""
-    n, k = 40, 16384
+    """Without the override the kernel takes k > 16384 (and agrees with the oracle there)."""
+    n, k = 40, 20480
     g = synth.rng(502, "i8-default")
     w = synth.blob("q4_k", g, n, k)
     x = synth.normal_f32(g, (1, k))
@@ -119,6 +120,7 @@ def test_i8_agrees_with_lanes_along_k(monkeypatch):
     g = synth.rng(507, "i8-vs-kl")
     w, x = dev(synth.blob("q4_k", g, n, k)), dev(synth.normal_f32(g, (1, k)))
     monkeypatch.setenv("TQ_GEMV_I8", "2")
+    monkeypatch.setenv("TQ_GEMV_I8S", "0")
     a = host(tq.gemv("q4_k", w, n, k, x))
     monkeypatch.setenv("TQ_GEMV_I8", "0")
     b = host(tq.gemv("q4_k", w, n, k, x))
