@@ -1,5 +1,6 @@
 // tq_dense.hip -- dequantization, dense GEMV and SwiGLU kernels with their host launchers.
 #include "tq_gemv_core.h"
+#include "tq_gemm_f32m.h"
 #include "tq_gemv_i8.h"
 #include "tq_qmm.h"
 #include "tq_launch.h"
@@ -158,6 +159,26 @@ static bool use_i8(int fmt, int64_t rows, int64_t k, const float *x, int64_t bat
          rows < (1ll << 30);
 }
 
+// Q6_K / Q8_0 batches on the fp32 matrix cores: workspace (counters, slice sums) when k is sliced.
+static size_t f32m_ws_bytes(int fmt, int64_t rows, int64_t k, int64_t batch) {
+  if (!f32m_ok(fmt, k, batch)) return 0;
+  const size_t p = f32m_workspace_bytes(rows, k);
+  return p ? kCounterBytes + p : 0;
+}
+
+static bool use_f32m(int fmt, int64_t rows, int64_t k, const float *x, int64_t batch,
+                     const void *ws, size_t ws_bytes) {
+  if (!f32m_ok(fmt, k, batch) || ((uintptr_t)x & 15) != 0 || rows >= (1ll << 30)) return false;
+  const size_t need = f32m_ws_bytes(fmt, rows, k, batch);
+  return need == 0 || (ws != nullptr && ws_bytes >= need);
+}
+
+static int launch_f32m(int fmt, const KlMap &m, int64_t k, const float *x, int64_t batch,
+                       void *ws, hipStream_t s) {
+  return launch_gemm_f32m(fmt, m, k, x, batch, ws ? (float *)((char *)ws + kCounterBytes) : nullptr,
+                          (unsigned *)ws, (int)(kCounterBytes / 4), s);
+}
+
 // The streaming int8 path needs no workspace, only a 16-byte aligned x.
 static bool use_i8s(int fmt, int64_t rows, int64_t k, const float *x, int64_t batch) {
   return i8s_gemv_ok(fmt, k, batch) && ((uintptr_t)x & 15) == 0 && rows < (1ll << 30);
@@ -192,8 +213,10 @@ static size_t split_workspace_bytes(int fmt, int64_t n, int64_t k) {
 static size_t max3(size_t a, size_t b, size_t c) { return a > b ? (a > c ? a : c) : (b > c ? b : c); }
 
 size_t gemv_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t batch) {
-  return max3(split_workspace_bytes(fmt, n, k), i8_ws_bytes(fmt, n, k, batch),
-              qmm_workspace_bytes(fmt, n, k, batch, false));
+  const size_t a = max3(split_workspace_bytes(fmt, n, k), i8_ws_bytes(fmt, n, k, batch),
+                        qmm_workspace_bytes(fmt, n, k, batch, false));
+  const size_t b = f32m_ws_bytes(fmt, n, k, batch);
+  return a > b ? a : b;
 }
 
 static QmmDense dense_map(int nparts, const void *const *w, const int64_t *n, float *const *y,
@@ -577,6 +600,16 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, in
     return launch_qmm_dense(m, k, x, batch, (char *)ws + kCounterBytes, (unsigned *)ws,
                             (int)(kCounterBytes / 4), s);
   }
+  if (use_f32m(fmt, n, k, x, batch, ws, ws_bytes)) {
+    KlMap m{};
+    m.w[0] = wb;
+    m.y[0] = y;
+    m.cum[1] = (int)n;
+    m.nparts = 1;
+    m.total = (int)n;
+    m.row_bytes = rb;
+    return launch_f32m(fmt, m, k, x, batch, ws, s);
+  }
   const bool i8s = use_i8s(fmt, n, k, x, batch);
   const bool i8 = !i8s && use_i8(fmt, n, k, x, batch, ws, ws_bytes);
   if (i8s || i8 || klane_ok(fmt, k, x, batch)) {
@@ -609,7 +642,9 @@ size_t gemv_multi_workspace_bytes(int fmt, int nparts, const int64_t *n, int64_t
   }
   const size_t fused = qmm_workspace_bytes(fmt, total, k, batch, false);
   const size_t i8 = i8_ws_bytes(fmt, total, k, batch);
-  return max3(b, fused, i8);
+  const size_t f32m = f32m_ws_bytes(fmt, total, k, batch);
+  const size_t r = max3(b, fused, i8);
+  return r > f32m ? r : f32m;
 }
 
 int launch_gemv_multi(int fmt, int nparts, const void *const *w, const int64_t *n, float *const *y,
@@ -622,9 +657,10 @@ int launch_gemv_multi(int fmt, int nparts, const void *const *w, const int64_t *
     return launch_qmm_dense(m, k, x, batch, (char *)ws + kCounterBytes, (unsigned *)ws,
                             (int)(kCounterBytes / 4), s);
   }
-  const bool i8s = use_i8s(fmt, total, k, x, batch);
-  const bool i8 = !i8s && use_i8(fmt, total, k, x, batch, ws, ws_bytes);
-  if ((i8s || i8 || klane_ok(fmt, k, x, batch)) && nparts <= 4 && total < (1ll << 30)) {
+  const bool f32m = use_f32m(fmt, total, k, x, batch, ws, ws_bytes);
+  const bool i8s = !f32m && use_i8s(fmt, total, k, x, batch);
+  const bool i8 = !f32m && !i8s && use_i8(fmt, total, k, x, batch, ws, ws_bytes);
+  if ((f32m || i8s || i8 || klane_ok(fmt, k, x, batch)) && nparts <= 4 && total < (1ll << 30)) {
     KlMap m{};
     for (int p = 0; p < nparts; ++p) {
       m.w[p] = (const uint8_t *)w[p];
@@ -634,6 +670,7 @@ int launch_gemv_multi(int fmt, int nparts, const void *const *w, const int64_t *
     m.nparts = nparts;
     m.total = (int)total;
     m.row_bytes = k / fmt_block_weights(fmt) * fmt_block_bytes(fmt);
+    if (f32m) return launch_f32m(fmt, m, k, x, batch, ws, s);
     if (i8s) return launch_gemv_i8s(m, k, x, s);
     if (i8) return launch_i8(m, k, x, ws, s);
     return launch_kl(m, k, x, s);
@@ -659,7 +696,8 @@ size_t gemv_swiglu_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t batch,
   const size_t qmm = qmm_workspace_bytes(fmt, n, k, batch, true);
   if (fused) return i8_ws_bytes(fmt, 2 * n, k, batch);
   const size_t two = swiglu_two_launch_bytes(fmt, n, k, batch);
-  return qmm > two ? qmm : two;
+  const size_t f32m = f32m_ws_bytes(fmt, 2 * n, k, batch);
+  return max3(qmm, two, f32m);
 }
 
 size_t gemv_swiglu_min_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t batch, bool fused) {
@@ -670,6 +708,18 @@ int launch_gemv_swiglu(int fmt, const void *wg, const void *wu, int64_t n, int64
                        const float *x, int64_t batch, float *h, void *ws, size_t ws_bytes,
                        hipStream_t s) {
   const int64_t rb = k / fmt_block_weights(fmt) * fmt_block_bytes(fmt);
+  if (use_f32m(fmt, 2 * n, k, x, batch, ws, ws_bytes) && n < (1ll << 29)) {
+    KlMap m{};
+    m.w[0] = (const uint8_t *)wg;
+    m.w[1] = (const uint8_t *)wu;
+    m.y[0] = h;
+    m.nparts = 1;
+    m.swiglu = 1;
+    m.total = (int)(2 * n);
+    m.cum[1] = m.total;
+    m.row_bytes = rb;
+    return launch_f32m(fmt, m, k, x, batch, ws, s);
+  }
   const bool i8s = use_i8s(fmt, 2 * n, k, x, batch);
   const bool i8 = !i8s && use_i8(fmt, 2 * n, k, x, batch, ws, ws_bytes);
   if ((i8s || i8 || klane_ok(fmt, k, x, batch)) && n < (1ll << 29)) {
