@@ -46,9 +46,10 @@ struct F32mRaw<FMT_Q8_0> {
 // Q6_K: of block kb, the 64 low-bit bytes of half h = g / 2, its 32 high-bit bytes, the four int8
 // scales of the quarter and d, as loaded: dword runs from the dword boundary at or below each run
 // (blocks start 2 bytes past one for odd kb; rows are dword aligned), one dword longer than the
-// run. The bytes are realigned only when the block is computed, so the loads stay in flight while
-// the previous block is computed. Every dword read lies inside the block: the extra dword of the
-// scale run is read only for odd kb (for even kb it would pass the block's end).
+// run. Each dword is realigned (v_alignbyte) where it is used, so the loads stay in flight while
+// the previous block is computed and no realigned copy is kept. Every dword read lies inside the
+// block: the extra dword of the scale run is read only for odd kb (for even kb it would pass the
+// block's end).
 template <>
 struct F32mRaw<FMT_Q6_K> {
   uint32_t ql[17], qh[9], sc[2];
@@ -68,23 +69,21 @@ struct F32mRaw<FMT_Q6_K> {
   }
 };
 
-// The realigned runs of a Q6_K quarter.
-struct Q6Quarter {
-  uint32_t ql[16], qh[8], sc;
-};
-__device__ __forceinline__ Q6Quarter q6_realign(const F32mRaw<FMT_Q6_K> &r) {
-  Q6Quarter q;
+// The lane's 16 activations of steps 16 j .. 16 j + 15 (its token row's piece in LDS).
+__device__ __forceinline__ void f32m_x16(const float *xs, int j, float (&xv)[16]) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) q.ql[i] = __builtin_amdgcn_alignbyte(r.ql[i + 1], r.ql[i], r.shift);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) q.qh[i] = __builtin_amdgcn_alignbyte(r.qh[i + 1], r.qh[i], r.shift);
-  q.sc = __builtin_amdgcn_alignbyte(r.sc[1], r.sc[0], r.shift);
-  return q;
+  for (int i = 0; i < 4; ++i) {
+    const f32x4m v = *reinterpret_cast<const f32x4m *>(xs + 16 * j + 4 * i);
+    xv[4 * i] = v[0];
+    xv[4 * i + 1] = v[1];
+    xv[4 * i + 2] = v[2];
+    xv[4 * i + 3] = v[3];
+  }
 }
 
 // The tile's contribution of one block: 64 steps of the matrix cores; Q6_K folds d at the end.
 template <int FMT>
-__device__ __forceinline__ void f32m_block(const F32mRaw<FMT> (&raw)[kF32mRT], const float (&xv)[64],
+__device__ __forceinline__ void f32m_block(const F32mRaw<FMT> (&raw)[kF32mRT], const float *xs,
                                            int g, f32x4m (&acc)[kF32mRT]) {
   const f32x4m zero = {0.f, 0.f, 0.f, 0.f};
   if constexpr (FMT == FMT_Q8_0) {
@@ -95,45 +94,69 @@ __device__ __forceinline__ void f32m_block(const F32mRaw<FMT> (&raw)[kF32mRT], c
       for (int r = 0; r < kF32mRT; ++r)
         d[r] = half_bits_to_float(half ? raw[r].v[8] >> 16 : raw[r].v[0] & 0xFFFFu);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int o = 34 * half + 2 + i;  // byte of quant i of this half
+      for (int j = 0; j < 2; ++j) {
+        float xv[16];
+        f32m_x16(xs, 2 * half + j, xv);
 #pragma unroll
-        for (int r = 0; r < kF32mRT; ++r) {
-          const int q = __builtin_amdgcn_sbfe(raw[r].v[o >> 2], 8 * (o & 3), 8);
-          acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[32 * half + i], d[r] * (float)q,
-                                                        acc[r], 0, 0, 0);
+        for (int e = 0; e < 16; ++e) {
+          const int o = 34 * half + 2 + 16 * j + e;  // byte of quant 16 j + e of this half
+#pragma unroll
+          for (int r = 0; r < kF32mRT; ++r) {
+            const int q = __builtin_amdgcn_sbfe(raw[r].v[o >> 2], 8 * (o & 3), 8);
+            acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[e], d[r] * (float)q, acc[r], 0, 0, 0);
+          }
         }
       }
     }
   } else {
     // the quarter's nibbles: low ones for even g, high ones for odd g; its two high bits: bits
-    // 4 (g & 1) + 2 (s / 32) of the high-bit byte
+    // 4 (g & 1) + 2 (s / 32) of the high-bit byte. Four consecutive steps take bytes l..l+3 of
+    // one low-bit and one high-bit dword, so their 6-bit quants are assembled as the four bytes of
+    // one dword (five integer operations), then each is one byte conversion and one FMA:
+    // sc * q - 32 sc, an integer below 2^13 in magnitude, exact in fp32.
     const uint32_t sh = 4u * (uint32_t)(g & 1);
-    Q6Quarter qq[kF32mRT];
+    uint32_t scw[kF32mRT];
 #pragma unroll
-    for (int r = 0; r < kF32mRT; ++r) qq[r] = q6_realign(raw[r]);
+    for (int r = 0; r < kF32mRT; ++r)
+      scw[r] = __builtin_amdgcn_alignbyte(raw[r].sc[1], raw[r].sc[0], raw[r].shift);
     f32x4m D[kF32mRT];
 #pragma unroll
     for (int r = 0; r < kF32mRT; ++r) D[r] = zero;
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {  // 16 weights per int8 scale
-      int scv[kF32mRT], nsc[kF32mRT];
+      float xv[16];
+      f32m_x16(xs, grp, xv);
+      float scf[kF32mRT], nscf[kF32mRT];
 #pragma unroll
       for (int r = 0; r < kF32mRT; ++r) {
-        scv[r] = __builtin_amdgcn_sbfe(qq[r].sc, 8 * grp, 8);
-        nsc[r] = -32 * scv[r];
+        // the signed byte goes through a full register before its conversion: folded into one
+        // SDWA conversion, the extract came out as an unsigned conversion of the sign-extended
+        // byte (negative scales turned into values near 2^32)
+        scf[r] = (float)(int)opaque((uint32_t)__builtin_amdgcn_sbfe(scw[r], 8 * grp, 8));
+        nscf[r] = -32.f * scf[r];
       }
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int s = 16 * grp + e, l = s & 31, hi = s >> 5;
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int s0 = 16 * grp + 4 * e4, l = s0 & 31, hi = s0 >> 5;
         const int qb = l + 32 * hi;  // low-bit byte within the half's 64
+        uint32_t q4[kF32mRT];
 #pragma unroll
         for (int r = 0; r < kF32mRT; ++r) {
-          const uint32_t lo4 = (qq[r].ql[qb >> 2] >> (8 * (qb & 3) + sh)) & 15u;
-          const uint32_t hi2 = (qq[r].qh[l >> 2] >> (8 * (l & 3) + sh + 2 * hi)) & 3u;
-          const int q = (int)(lo4 | (hi2 << 4));
-          const int v = q * scv[r] + nsc[r];  // sc * (q - 32), exact
-          D[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[s], (float)v, D[r], 0, 0, 0);
+          const uint32_t qlw = __builtin_amdgcn_alignbyte(raw[r].ql[(qb >> 2) + 1],
+                                                          raw[r].ql[qb >> 2], raw[r].shift);
+          const uint32_t qhw = __builtin_amdgcn_alignbyte(raw[r].qh[(l >> 2) + 1],
+                                                          raw[r].qh[l >> 2], raw[r].shift);
+          const uint32_t lo = (qlw >> sh) & 0x0F0F0F0Fu;
+          const uint32_t h2 = (qhw >> (sh + 2 * hi)) & 0x03030303u;
+          q4[r] = opaque(lo | (h2 << 4));
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+#pragma unroll
+          for (int r = 0; r < kF32mRT; ++r) {
+            const float v = __builtin_fmaf(byte_to_float(q4[r], e), scf[r], nscf[r]);
+            D[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[4 * e4 + e], v, D[r], 0, 0, 0);
+          }
         }
       }
     }
@@ -175,12 +198,12 @@ __device__ __forceinline__ void f32m_store(const KlMap &m, int B, int rb, int t,
 constexpr int kF32mXRow = 260;  // LDS floats per token row of a block (+4: rows on distinct banks)
 
 template <int FMT>
-__global__ __launch_bounds__(256) void k_gemm_f32m(KlMap m, const float *__restrict__ x, int B,
-                                                   int kblocks, int ksplit, int upk,
-                                                   float *__restrict__ partial,
-                                                   unsigned *__restrict__ counters) {
-  __shared__ __attribute__((aligned(16))) float xsh[2][16 * kF32mXRow];
-  __shared__ int is_last;
+__device__ __forceinline__ void f32m_body(const KlMap &m, const float *__restrict__ x, int B,
+                                          int kblocks, int ksplit, int upk,
+                                          float *__restrict__ partial,
+                                          unsigned *__restrict__ counters,
+                                          float (*xsh)[16 * kF32mXRow], int *is_last_p) {
+  int &is_last = *is_last_p;
   constexpr int RT = kF32mRT;
   const int lane = threadIdx.x & 63, w = wave_index();
   const int t = lane & 15, g = lane >> 4;
@@ -194,19 +217,21 @@ __global__ __launch_bounds__(256) void k_gemm_f32m(KlMap m, const float *__restr
   // token rows of a block: 16 rows x 64 float4, four per thread (rows past the batch repeat the
   // last token; their outputs are never stored)
   const int64_t xld = (int64_t)kblocks * 64;  // float4 per token row
-  float4 xn[4];
+  // (a native vector type: HIP's float4 struct kept this array in scratch memory, and every
+  // fetch waited for its loads to store them there)
+  f32x4m xn[4];
   auto fetch_x = [&](int kb) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int idx = (int)threadIdx.x + 256 * j, tok = idx >> 6, c4 = idx & 63;
-      xn[j] = reinterpret_cast<const float4 *>(x)[(int64_t)min(tok, B - 1) * xld + kb * 64 + c4];
+      xn[j] = reinterpret_cast<const f32x4m *>(x)[(int64_t)min(tok, B - 1) * xld + kb * 64 + c4];
     }
   };
   auto put_x = [&](int b) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int idx = (int)threadIdx.x + 256 * j, tok = idx >> 6, c4 = idx & 63;
-      *reinterpret_cast<float4 *>(&xsh[b][tok * kF32mXRow + 4 * c4]) = xn[j];
+      *reinterpret_cast<f32x4m *>(&xsh[b][tok * kF32mXRow + 4 * c4]) = xn[j];
     }
   };
 
@@ -219,17 +244,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32m(KlMap m, const float *__restr
     for (int r = 0; r < RT; ++r) raw[r].load(wrow[r], kb, g);
   };
   auto compute = [&](const F32mRaw<FMT>(&raw)[RT], int b) {
-    float xv[64];
-    const float *xs = &xsh[b][t * kF32mXRow + 64 * g];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float4 v = *reinterpret_cast<const float4 *>(xs + 4 * i);
-      xv[4 * i] = v.x;
-      xv[4 * i + 1] = v.y;
-      xv[4 * i + 2] = v.z;
-      xv[4 * i + 3] = v.w;
-    }
-    f32m_block<FMT>(raw, xv, g, acc);
+    f32m_block<FMT>(raw, &xsh[b][t * kF32mXRow + 64 * g], g, acc);
   };
   // Weights one block ahead in two register sets used in turn; token rows one block ahead in
   // registers, then in the other LDS buffer. The barrier at the end of block i makes block i+1's
@@ -293,18 +308,36 @@ __global__ __launch_bounds__(256) void k_gemm_f32m(KlMap m, const float *__restr
     __hip_atomic_store(&counters[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Q8_0 fits three waves per SIMD (the compiler then reaches four); Q6_K keeps two (at three its
+// two register sets of raw runs spill).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_gemm_f32m_q8(
+    KlMap m, const float *__restrict__ x, int B, int kblocks, int ksplit, int upk,
+    float *__restrict__ partial, unsigned *__restrict__ counters) {
+  __shared__ __attribute__((aligned(16))) float xsh[2][16 * kF32mXRow];
+  __shared__ int is_last;
+  f32m_body<FMT_Q8_0>(m, x, B, kblocks, ksplit, upk, partial, counters, xsh, &is_last);
+}
+
+__global__ __launch_bounds__(256) void k_gemm_f32m_q6(KlMap m, const float *__restrict__ x, int B,
+                                                      int kblocks, int ksplit, int upk,
+                                                      float *__restrict__ partial,
+                                                      unsigned *__restrict__ counters) {
+  __shared__ __attribute__((aligned(16))) float xsh[2][16 * kF32mXRow];
+  __shared__ int is_last;
+  f32m_body<FMT_Q6_K>(m, x, B, kblocks, ksplit, upk, partial, counters, xsh, &is_last);
+}
+
 // ---- host side ----------------------------------------------------------------------------------
 
-// Q8_0 at 2..16 tokens, Q6_K (dword-aligned rows: k a multiple of 512) at 5..16 tokens, k up to
-// 65536. At 4 tokens and fewer the fp32 vector GEMV is as fast or faster for Q6_K (measured on
-// the 70B-shaped layer at batch 4: 0.60 against 0.68 ms; its dequantization costs about nine
-// VALU instructions per matrix-core step, against three for Q8_0). TQ_GEMM_F32M=0 turns the
-// path off, =2 takes every batch of 2..16 (tests).
+// Q8_0 at 2..16 tokens, Q6_K (dword-aligned rows: k a multiple of 512) at 4..16 tokens, k up to
+// 65536 (on the 70B-shaped layer at batch 4 Q6_K takes 0.51 ms here against 0.60 ms on the fp32
+// vector GEMV; fewer tokens stay there). TQ_GEMM_F32M=0 turns the path off, =2 takes every batch
+// of 2..16 (tests).
 bool f32m_ok(int fmt, int64_t k, int64_t batch) {
   const int mode = env_int("TQ_GEMM_F32M", 1);
   if (mode == 0) return false;
   if (batch < 2 || batch > 16 || k <= 0 || k > 65536) return false;
-  if (fmt == FMT_Q6_K) return k % 512 == 0 && (batch >= 5 || mode == 2);
+  if (fmt == FMT_Q6_K) return k % 512 == 0 && (batch >= 4 || mode == 2);
   return fmt == FMT_Q8_0 && k % 256 == 0;
 }
 
@@ -332,11 +365,11 @@ int launch_gemm_f32m(int fmt, const KlMap &m, int64_t k, const float *x, int64_t
   if (ksplit > 1 && groups > max_counters) return -2;
   const dim3 grid((unsigned)(groups * ksplit));
   if (fmt == FMT_Q6_K)
-    hipLaunchKernelGGL(k_gemm_f32m<FMT_Q6_K>, grid, dim3(256), 0, s, m, x, (int)batch, nblk,
-                       ksplit, upk, partial, counters);
+    hipLaunchKernelGGL(k_gemm_f32m_q6, grid, dim3(256), 0, s, m, x, (int)batch, nblk, ksplit, upk,
+                       partial, counters);
   else
-    hipLaunchKernelGGL(k_gemm_f32m<FMT_Q8_0>, grid, dim3(256), 0, s, m, x, (int)batch, nblk,
-                       ksplit, upk, partial, counters);
+    hipLaunchKernelGGL(k_gemm_f32m_q8, grid, dim3(256), 0, s, m, x, (int)batch, nblk, ksplit, upk,
+                       partial, counters);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -24,7 +24,7 @@ tq = pytest.importorskip("moe_expert_ffn_q4_amd")
 
 @pytest.fixture(autouse=True)
 def every_batch(monkeypatch):
-    """Every batch of 2..16 on the matrix-core path (by default Q6_K takes it from 5 tokens)."""
+    """Every batch of 2..16 on the matrix-core path (by default Q6_K takes it from 4 tokens)."""
     monkeypatch.setenv("TQ_GEMM_F32M", "2")
 
 
