@@ -295,11 +295,11 @@ __global__ __launch_bounds__(512) void k_gemv(const uint8_t *__restrict__ w, int
 // of k (G > 1 only when k fits in 16 / G blocks, so that short rows leave no lane idle); group g of
 // a pass over rows r0.. computes rows r0 + g R .. r0 + g R + R - 1.
 
-template <int R, int G>
+template <int R, int G, class Map>
 __device__ __forceinline__ void kl_rows(const u32x4 (&v)[R][3], const float (&xv)[64], float sx_lo,
                                         float sx_hi, const Q4kField &f0, const Q4kField &f1,
                                         float unit_inv, int r0, int re, float (*red)[G * R],
-                                        const KlMap &m) {
+                                        const Map &m) {
   constexpr int L = 64 / G;  // lanes per group
   static_assert(L >= R, "a group needs at least one lane per row");
   const int lane = threadIdx.x & 63, wave = wave_index(), nw = blockDim.x >> 6;
@@ -343,7 +343,7 @@ __device__ __forceinline__ void kl_rows(const u32x4 (&v)[R][3], const float (&xv
         g += red[q][i];
         u += red[q][i + 1];
       }
-      m.y[0][(r0 + i) >> 1] = silu_mul(g, u);
+      *m.swiglu_out((r0 + i) >> 1) = silu_mul(g, u);
     }
   } else if (threadIdx.x < G * R && r0 + (int)threadIdx.x < re) {
     float s = 0.f;
@@ -355,8 +355,8 @@ __device__ __forceinline__ void kl_rows(const u32x4 (&v)[R][3], const float (&xv
 
 // Rows [rb, re) of the workgroup, G R per pass, loading the next pass's rows while it computes the
 // current ones (two register buffers used in turn).
-template <int R, int G>
-__device__ __forceinline__ void kl_body(const KlMap &m, int nblk, int rb, int re,
+template <int R, int G, class Map>
+__device__ __forceinline__ void kl_body(const Map &m, int nblk, int rb, int re,
                                         const float *__restrict__ x, float (*red)[G * R]) {
   constexpr int L = 64 / G, P = G * R;
   const int lane = threadIdx.x & 63, wave = wave_index();
@@ -366,7 +366,7 @@ __device__ __forceinline__ void kl_body(const KlMap &m, int nblk, int rb, int re
   const int boff = bb * 144;
   u32x4 va[R][3], vb[R][3];
   // the first rows' weights are requested before the activations
-  if (rb < re) kl_load_rows<R>(m, rb + g * R, boff, c, va);
+  if (rb < re) kl_load_rows<R, Map>(m, rb + g * R, boff, c, va);
   float xv[64];
   {
     const float4 *xp = reinterpret_cast<const float4 *>(x + 256 * bb + 64 * c);
@@ -388,11 +388,11 @@ __device__ __forceinline__ void kl_body(const KlMap &m, int nblk, int rb, int re
   const float unit_inv = 1.f / nibble_fp8_unit();
   const Q4kField f0 = q4k_field(2 * c), f1 = q4k_field(2 * c + 1);
   for (int r0 = rb; r0 < re; r0 += 2 * P) {
-    if (r0 + P < re) kl_load_rows<R>(m, r0 + P + g * R, boff, c, vb);
-    kl_rows<R, G>(va, xv, sx_lo, sx_hi, f0, f1, unit_inv, r0, re, red, m);
+    if (r0 + P < re) kl_load_rows<R, Map>(m, r0 + P + g * R, boff, c, vb);
+    kl_rows<R, G, Map>(va, xv, sx_lo, sx_hi, f0, f1, unit_inv, r0, re, red, m);
     if (r0 + P >= re) break;
-    if (r0 + 2 * P < re) kl_load_rows<R>(m, r0 + 2 * P + g * R, boff, c, va);
-    kl_rows<R, G>(vb, xv, sx_lo, sx_hi, f0, f1, unit_inv, r0 + P, re, red, m);
+    if (r0 + 2 * P < re) kl_load_rows<R, Map>(m, r0 + 2 * P + g * R, boff, c, va);
+    kl_rows<R, G, Map>(vb, xv, sx_lo, sx_hi, f0, f1, unit_inv, r0 + P, re, red, m);
   }
 }
 
@@ -404,8 +404,23 @@ __global__ __launch_bounds__(512) void k_gemv_kl(KlMap m, int nblk, int rows_per
                                                  const float *__restrict__ x) {
   __shared__ float red[8][G * R];
   const int rb = blockIdx.x * rows_per_wg, re = min(rb + rows_per_wg, m.total);
-  kl_body<R, G>(m, nblk, rb, re, x, red);
+  kl_body<R, G, KlMap>(m, nblk, rb, re, x, red);
 }
+
+// Rows of one expert's matrices for the one-token MoE kernel: two pointers and no arrays (a
+// general row map built inside a kernel and indexed at run time is kept in scratch memory).
+struct MoeRowMap {
+  const uint8_t *w0, *w1;  // gate, up (gate_up) or down, unused
+  float *y;
+  int swiglu, total;
+  int64_t row_bytes;
+  __device__ __forceinline__ const uint8_t *row(int v) const {
+    return swiglu ? ((v & 1) ? w1 : w0) + (int64_t)(v >> 1) * row_bytes
+                  : w0 + (int64_t)v * row_bytes;
+  }
+  __device__ __forceinline__ float *swiglu_out(int j) const { return y + j; }
+  __device__ __forceinline__ float *out(int v) const { return y + v; }
+};
 
 // The same kernel over the experts of a one-token MoE step: workgroup b works on active slot
 // slot0 + b / wgs_per_slot (every active expert has that one token). gate/up: the expert's
@@ -429,20 +444,12 @@ __global__ __launch_bounds__(512) void k_moe_kl(MoeKlArgs a, int nblk, int rows_
     else
       w[q] = (const uint8_t *)a.experts[e].m[mat];
   }
-  KlMap m{};
-  m.w[0] = w[0];
-  m.w[1] = w[1];
-  m.y[0] = a.out + (int64_t)p * a.ldo;
-  m.nparts = 1;
-  m.swiglu = a.gate_up;
-  m.total = a.rows;
-  m.cum[1] = a.rows;
-  m.row_bytes = a.row_bytes;
+  const MoeRowMap m{w[0], w[1], a.out + (int64_t)p * a.ldo, a.gate_up, a.rows, a.row_bytes};
   int64_t xrow = p;
   if (a.gate_up) xrow = p >= a.Tk ? p - a.Tk : a.pairs[p] / a.topk;
   const int rb = ((int)blockIdx.x % wgs_per_slot) * rows_per_wg;
   const int re = min(rb + rows_per_wg, a.rows);
-  kl_body<R, G>(m, nblk, rb, re, a.x + xrow * a.ldx, red);
+  kl_body<R, G, MoeRowMap>(m, nblk, rb, re, a.x + xrow * a.ldx, red);
 }
 
 // Fallback for shapes whose rows are not dword aligned (Q6_K with k % 512 != 0, Q8_0 with

@@ -566,6 +566,8 @@ struct KlMap {
     for (int i = 1; i < 4; ++i) p += (i < nparts && v >= cum[i]) ? 1 : 0;
     return w[p] + (int64_t)(v - cum[p]) * row_bytes;
   }
+  // SwiGLU output j (rows 2j, 2j+1)
+  __device__ __forceinline__ float *swiglu_out(int j) const { return y[0] + j; }
   __device__ __forceinline__ float *out(int v) const {
     int p = 0;
 #pragma unroll
@@ -574,8 +576,8 @@ struct KlMap {
   }
 };
 
-template <int R>
-__device__ __forceinline__ void kl_load_rows(const KlMap &m, int r0, int boff, int c,
+template <int R, class Map>
+__device__ __forceinline__ void kl_load_rows(const Map &m, int r0, int boff, int c,
                                              u32x4 (&v)[R][3]) {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
