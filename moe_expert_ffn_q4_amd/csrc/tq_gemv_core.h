@@ -559,20 +559,30 @@ struct KlMap {
   int total;   // virtual rows
   int64_t row_bytes;
 
+  // Row v's bytes and output. The part is picked with selects among the four pointers held in
+  // scalar registers (opaque to the compiler): indexing the argument's arrays with a per-lane part
+  // number compiles to a vector load from the argument segment and a wait on every outstanding
+  // load, the next rows' prefetch included.
   __device__ __forceinline__ const uint8_t *row(int v) const {
-    if (swiglu) return w[v & 1] + (int64_t)(v >> 1) * row_bytes;
-    int p = 0;
-#pragma unroll
-    for (int i = 1; i < 4; ++i) p += (i < nparts && v >= cum[i]) ? 1 : 0;
-    return w[p] + (int64_t)(v - cum[p]) * row_bytes;
+    const uint8_t *p0 = w[0], *p1 = w[1], *p2 = w[2], *p3 = w[3];
+    asm("" : "+s"(p0), "+s"(p1), "+s"(p2), "+s"(p3));
+    if (swiglu) return ((v & 1) ? p1 : p0) + (int64_t)(v >> 1) * row_bytes;
+    const int c1 = nparts > 1 ? cum[1] : 1 << 30, c2 = nparts > 2 ? cum[2] : 1 << 30,
+              c3 = nparts > 3 ? cum[3] : 1 << 30;
+    const uint8_t *b = v >= c3 ? p3 : v >= c2 ? p2 : v >= c1 ? p1 : p0;
+    const int first = v >= c3 ? c3 : v >= c2 ? c2 : v >= c1 ? c1 : 0;
+    return b + (int64_t)(v - first) * row_bytes;
   }
   // SwiGLU output j (rows 2j, 2j+1)
   __device__ __forceinline__ float *swiglu_out(int j) const { return y[0] + j; }
   __device__ __forceinline__ float *out(int v) const {
-    int p = 0;
-#pragma unroll
-    for (int i = 1; i < 4; ++i) p += (i < nparts && v >= cum[i]) ? 1 : 0;
-    return y[p] + (v - cum[p]);
+    float *p0 = y[0], *p1 = y[1], *p2 = y[2], *p3 = y[3];
+    asm("" : "+s"(p0), "+s"(p1), "+s"(p2), "+s"(p3));
+    const int c1 = nparts > 1 ? cum[1] : 1 << 30, c2 = nparts > 2 ? cum[2] : 1 << 30,
+              c3 = nparts > 3 ? cum[3] : 1 << 30;
+    float *b = v >= c3 ? p3 : v >= c2 ? p2 : v >= c1 ? p1 : p0;
+    const int first = v >= c3 ? c3 : v >= c2 ? c2 : v >= c1 ? c1 : 0;
+    return b + (v - first);
   }
 };
 

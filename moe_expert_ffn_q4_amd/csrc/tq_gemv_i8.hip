@@ -167,12 +167,7 @@ __device__ __forceinline__ float i8_block(const u32x4 &head, const u32x4 (&q)[4]
 }
 
 // Output of virtual row v (multi: the part it falls in).
-__device__ __forceinline__ void i8_store(const KlMap &m, int v, float s) {
-  int p = 0;
-#pragma unroll
-  for (int k = 1; k < 4; ++k) p += (k < m.nparts && v >= m.cum[k]) ? 1 : 0;
-  m.y[p][v - m.cum[p]] = s;
-}
+__device__ __forceinline__ void i8_store(const KlMap &m, int v, float s) { *m.out(v) = s; }
 
 __global__ __launch_bounds__(256) void k_gemv_i8(KlMap m, const float *__restrict__ x, int nblk,
                                                  int upk, int ksplit, float *__restrict__ partial,
