@@ -456,11 +456,31 @@ __global__ __launch_bounds__(256) void k_qmm(QmmArgs a) {
 
 // ---- dense products (2..32 tokens) --------------------------------------------------------------
 
+// Part of virtual row v: its index among the parts' first rows. The part's pointers are then
+// picked with selects among scalar registers (opaque to the compiler): a per-lane index into the
+// argument's pointer arrays compiles to a vector load of the pointer and a wait on every
+// outstanding load.
+struct DensePart {
+  int p, first, last;
+};
+__device__ __forceinline__ DensePart dense_part(const QmmDense &m, int v) {
+  const int n = m.nparts, total = m.cum[n];
+  const int c1 = n > 1 ? m.cum[1] : total, c2 = n > 2 ? m.cum[2] : total,
+            c3 = n > 3 ? m.cum[3] : total;
+  if (v >= c3) return {3, c3, total};
+  if (v >= c2) return {2, c2, c3};
+  if (v >= c1) return {1, c1, c2};
+  return {0, 0, c1};
+}
+template <class T>
+__device__ __forceinline__ T *pick4(T *p0, T *p1, T *p2, T *p3, int p) {
+  asm("" : "+s"(p0), "+s"(p1), "+s"(p2), "+s"(p3));
+  return p == 3 ? p3 : p == 2 ? p2 : p == 1 ? p1 : p0;
+}
+
 __device__ __forceinline__ const uint8_t *dense_row(const QmmDense &m, int v) {
-  int p = 0;
-#pragma unroll
-  for (int i = 1; i < 4; ++i) p += (i < m.nparts && v >= m.cum[i]) ? 1 : 0;
-  return m.w[p] + (int64_t)(v - m.cum[p]) * m.row_bytes;
+  const DensePart q = dense_part(m, v);
+  return pick4(m.w[0], m.w[1], m.w[2], m.w[3], q.p) + (int64_t)(v - q.first) * m.row_bytes;
 }
 
 // Partial sums of one (row tile, k slice) as [token][128]: GU: gate columns 0..63, up 64..127;
@@ -478,10 +498,9 @@ struct DenseEpi {
   __device__ __forceinline__ void store(int tok, int rt, float v) const {
     const int vrow = tile * 128 + rt;
     if (vrow < m->cum[m->nparts]) {
-      int p = 0;
-#pragma unroll
-      for (int i = 1; i < 4; ++i) p += (i < m->nparts && vrow >= m->cum[i]) ? 1 : 0;
-      m->y[p][(int64_t)tok * (m->cum[p + 1] - m->cum[p]) + (vrow - m->cum[p])] = v;
+      const DensePart q = dense_part(*m, vrow);
+      pick4(m->y[0], m->y[1], m->y[2], m->y[3], q.p)[(int64_t)tok * (q.last - q.first) +
+                                                      (vrow - q.first)] = v;
     }
   }
 
