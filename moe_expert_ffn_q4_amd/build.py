@@ -23,25 +23,61 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, verbose: bool) -> str:
+RESOURCES = os.path.join(OBJ, "kernel_resources.json")
+REMARKS = "-Rpass-analysis=kernel-resource-usage"
+
+
+def parse_resource_remarks(text: str) -> dict:
+    """Per-kernel register, scratch, occupancy and LDS figures from the compiler's
+    kernel-resource-usage remarks: {mangled name: {field: int}}."""
+    import re
+
+    out, cur = {}, None
+    fields = {"VGPRs": "vgprs", "AGPRs": "agprs", "ScratchSize [bytes/lane]": "scratch",
+              "Occupancy [waves/SIMD]": "occupancy", "LDS Size [bytes/block]": "lds"}
+    for line in text.splitlines():
+        if "remark:" not in line:
+            continue
+        body = line.split("remark:", 1)[1].strip()
+        body = re.sub(r"\s*\[-Rpass-analysis=kernel-resource-usage\]$", "", body)
+        if body.startswith("Function Name:"):
+            cur = body.split(":", 1)[1].strip()
+            out[cur] = {}
+            continue
+        if cur is None or ":" not in body:
+            continue
+        key, val = body.rsplit(":", 1)
+        key = key.strip()
+        if key in fields and val.strip().lstrip("-").isdigit():
+            out[cur][fields[key]] = int(val)
+    return out
+
+
+def _compile(src: str, verbose: bool) -> tuple:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, REMARKS, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError(f"hipcc failed on {src}")
-    if verbose and r.stderr.strip():
-        sys.stderr.write(r.stderr)
-    return obj
+    return obj, parse_resource_remarks(r.stderr)
 
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+        results = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    objs = [o for o, _ in results]
+    resources = {}
+    for _, r in results:
+        resources.update(r)
+    import json
+
+    with open(RESOURCES, "w") as f:
+        json.dump(resources, f, indent=1, sort_keys=True)
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
@@ -49,6 +85,33 @@ def build(verbose: bool = False) -> str:
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     return LIB
+
+
+def kernel_resources() -> dict:
+    """The per-kernel figures recorded by the last build (compiling the sources, without linking,
+    when no build has recorded them or a source is newer than the record)."""
+    import json
+
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h")))
+    if os.path.exists(RESOURCES) and all(os.path.getmtime(RESOURCES) >= os.path.getmtime(p)
+                                         for p in srcs):
+        with open(RESOURCES) as f:
+            return json.load(f)
+    os.makedirs(OBJ, exist_ok=True)
+
+    def one(src):
+        cmd = [HIPCC, *FLAGS, REMARKS, "--offload-device-only", "-c", src, "-o", os.devnull]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+        return parse_resource_remarks(r.stderr)
+
+    hips = [p for p in srcs if p.endswith(".hip")]
+    out = {}
+    with ThreadPoolExecutor(max_workers=min(8, len(hips))) as ex:
+        for r in ex.map(one, hips):
+            out.update(r)
+    return out
 
 
 if __name__ == "__main__":

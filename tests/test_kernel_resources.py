@@ -1,0 +1,45 @@
+"""The hot kernels as compiled for gfx950: no scratch memory, and the occupancy they were tuned
+at. Scratch use has twice crept in unnoticed (a pointer map built inside a kernel and indexed at
+run time, a HIP float4 array of prefetched values); each time it put a full wait on the memory
+pipeline into the inner loop. The figures are the compiler's kernel-resource-usage remarks,
+recorded by the build (or compiled here when no build has recorded them)."""
+import re
+
+import pytest
+
+from moe_expert_ffn_q4_amd import build
+
+# (pattern on the mangled name, least occupancy in waves per SIMD)
+HOT = [
+    (r"k_gemv_klILi4E", 2),          # batch-1 Q4_K GEMV, lanes along k
+    (r"k_moe_klILi4E", 2),           # one-token MoE experts
+    (r"k_gemv_i8E", 4),              # batch-1 Q4_K GEMV, int8 matrix cores, sliced k
+    (r"k_gemv_i8sI", 2),             # the streaming form
+    (r"k_gemm_f32m_q8", 4),          # Q8_0 batches, fp32 matrix cores
+    (r"k_gemm_f32m_q6", 2),          # Q6_K batches
+    (r"k_qmm_denseI", 1),            # dense few-token Q4_K products, fp16 matrix cores
+    (r"k_qmmILb", 1),                # MoE few-token products
+    (r"k_prefillI", 1),              # prompt-sized MoE products, bf16 matrix cores
+    (r"k_gemvILi[123]ELi[1248]E", 1),  # fp32 lane-per-row GEMV
+    (r"k_router|k_topk|k_group|k_moe_combine|k_moe_swiglu|k_split_rows|k_dequant", 1),
+]
+
+
+@pytest.fixture(scope="module")
+def resources():
+    return build.kernel_resources()
+
+
+def test_remarks_parsed(resources):
+    assert len(resources) >= 20, sorted(resources)
+    some = next(iter(resources.values()))
+    assert {"vgprs", "scratch", "occupancy"} <= set(some), some
+
+
+@pytest.mark.parametrize("pattern,occ", HOT, ids=[p for p, _ in HOT])
+def test_hot_kernels_use_no_scratch(resources, pattern, occ):
+    hits = {k: v for k, v in resources.items() if re.search(pattern, k)}
+    assert hits, f"no kernel matches {pattern}"
+    for name, r in hits.items():
+        assert r["scratch"] == 0, f"{name}: {r['scratch']} bytes of scratch per lane"
+        assert r["occupancy"] >= occ, f"{name}: occupancy {r['occupancy']} < {occ}"
