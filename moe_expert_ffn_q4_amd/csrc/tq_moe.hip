@@ -3,6 +3,7 @@
 //
 // Decode path, all on one stream and without host synchronisation:
 //   k_router        logits partial sums (fp32), lane per expert row, tokens through scalar loads
+//   k_router_kl     the same for T <= 8, lanes along the hidden dimension (coalesced rows)
 //   k_topk          one wave per token: logits = sum of the partials, k largest (ties to the lower
 //                   expert index), softmax weights renormalised over the selected experts
 //   k_group         one workgroup: per-expert counts, exclusive offsets and a stable scatter of the
@@ -75,6 +76,60 @@ __device__ __forceinline__ bool better(float va, int ea, float vb, int eb) {
 
 // NV = expert slots per lane (E <= 64 NV). The code is kept short (rolled loops): one wave runs
 // it cold, so instruction fetch, not arithmetic, sets its time.
+// Router for decode-sized batches (T <= 8): lanes along the hidden dimension, so a wave's loads
+// of its expert rows are coalesced 1 KB runs, all of a slice's loads in flight at once. Workgroup
+// = 4 waves x 4 expert rows, one hidden slice of hpk values (a multiple of 256); each lane adds
+// its 4 values per 256-value step, then a halving butterfly over the wave leaves row r's slice sum
+// in lane 16 r. Output layout as k_router's (tile 0): part[(hs * 8 + t) * E + e].
+__global__ __launch_bounds__(256) void k_router_kl(const float *__restrict__ wr, int E, int H,
+                                                   const float *__restrict__ x, int T, int hsplit,
+                                                   int hpk, float *__restrict__ part) {
+  constexpr int RW = 4, NT = 8;
+  const int rg = blockIdx.x / hsplit, hs = blockIdx.x - rg * hsplit;
+  const int lane = threadIdx.x & 63, wave = wave_index();
+  const int e0 = rg * 16 + wave * RW;
+  const int h0 = hs * hpk, h1 = min(h0 + hpk, H);
+  const float *wrow[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) wrow[r] = wr + (int64_t)min(e0 + r, E - 1) * H;
+  float acc[RW][NT];
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[r][t] = 0.f;
+  for (int h = h0 + 4 * lane; h < h1; h += 256) {
+    float4 wv[RW], xv[NT];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) wv[r] = *reinterpret_cast<const float4 *>(wrow[r] + h);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      xv[t] = *reinterpret_cast<const float4 *>(x + (int64_t)min(t, T - 1) * H + h);
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        float a = acc[r][t];
+        a = __builtin_fmaf(wv[r].x, xv[t].x, a);
+        a = __builtin_fmaf(wv[r].y, xv[t].y, a);
+        a = __builtin_fmaf(wv[r].z, xv[t].z, a);
+        a = __builtin_fmaf(wv[r].w, xv[t].w, a);
+        acc[r][t] = a;
+      }
+  }
+  // per token: 4 rows -> 2 (lanes 32 apart), -> 1 (16 apart), then plain sums over 8, 4, 2, 1
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const bool up32 = (lane & 32) != 0, up16 = (lane & 16) != 0;
+    float a0 = (up32 ? acc[2][t] : acc[0][t]) + __shfl_xor(up32 ? acc[0][t] : acc[2][t], 32);
+    float a1 = (up32 ? acc[3][t] : acc[1][t]) + __shfl_xor(up32 ? acc[1][t] : acc[3][t], 32);
+    float b = (up16 ? a1 : a0) + __shfl_xor(up16 ? a0 : a1, 16);
+#pragma unroll
+    for (int d = 8; d >= 1; d >>= 1) b += __shfl_xor(b, d);
+    const int e = e0 + (up32 ? 2 : 0) + (up16 ? 1 : 0);
+    if ((lane & 15) == 0 && t < T && e < E) part[((int64_t)hs * 8 + t) * E + e] = b;
+  }
+}
+
 template <int NV>
 __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, int T, int E,
                                               int hsplit, int topk, int renormalize,
@@ -452,6 +507,15 @@ MoePlan plan_moe(const MoeShape &s) {
   hs = clampi(hs, 1, (int)(s.hidden / 256 < kMaxHSplit ? s.hidden / 256 : kMaxHSplit));
   p.hpk = (int)(((s.hidden + hs - 1) / hs + 3) & ~3);
   p.hsplit = (int)((s.hidden + p.hpk - 1) / p.hpk);
+  // decode-sized batches: the lanes-along-hidden router, slices of whole 256-value steps, as many
+  // as the partial-sum table allows
+  p.router_kl = T <= 8 && s.hidden % 256 == 0 && env_int("TQ_ROUTER_KL", 1) != 0;
+  if (p.router_kl) {
+    const int steps = (int)(s.hidden / 256);
+    const int hsk = steps < kMaxHSplit ? steps : kMaxHSplit;
+    p.hpk = (int)(((steps + hsk - 1) / hsk) * 256);
+    p.hsplit = (int)((s.hidden + p.hpk - 1) / p.hpk);
+  }
   // gate/up: F rows over k = hidden; down: hidden rows over k = F
   auto split = [&](int64_t rows, int64_t kdim, int nmat, int &rowgroups, int &ks, int &upk,
                    int &waves, int &upw) {
@@ -545,8 +609,14 @@ int launch_moe_routing(const MoePlan &p, const float *router_w, const float *x, 
   const MoeShape &s = p.s;
   const int E = (int)s.n_experts, H = (int)s.hidden, T = (int)s.tokens, k = (int)s.top_k;
   float *rpart = (float *)(ws + p.off_rpart);
-  const dim3 rgrid((unsigned)(((E + 63) / 64) * p.hsplit), (unsigned)p.rtiles);
-  hipLaunchKernelGGL(k_router, rgrid, dim3(256), 0, st, router_w, E, H, x, T, p.hsplit, p.hpk, rpart);
+  if (p.router_kl && ((uintptr_t)x & 15) == 0 && ((uintptr_t)router_w & 15) == 0) {
+    hipLaunchKernelGGL(k_router_kl, dim3((unsigned)(((E + 15) / 16) * p.hsplit)), dim3(256), 0, st,
+                       router_w, E, H, x, T, p.hsplit, p.hpk, rpart);
+  } else {
+    const dim3 rgrid((unsigned)(((E + 63) / 64) * p.hsplit), (unsigned)p.rtiles);
+    hipLaunchKernelGGL(k_router, rgrid, dim3(256), 0, st, router_w, E, H, x, T, p.hsplit, p.hpk,
+                       rpart);
+  }
   {
     const dim3 g((unsigned)((T + 3) / 4));
     float *lg = (float *)(ws + p.off_logits), *wt = (float *)(ws + p.off_wts);
