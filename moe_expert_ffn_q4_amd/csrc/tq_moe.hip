@@ -74,6 +74,43 @@ __device__ __forceinline__ bool better(float va, int ea, float vb, int eb) {
   return va > vb || (va == vb && ea < eb);
 }
 
+// Keep the better of (v, e) and the pair DPP control CTRL brings from another lane of the row.
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(float &v, int &e) {
+  const float ov = __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+  const int oe = __builtin_amdgcn_update_dpp(0, e, CTRL, 0xF, 0xF, false);
+  if (better(ov, oe, v, e)) {
+    v = ov;
+    e = oe;
+  }
+}
+
+// The wave's best (value, index) pair, in every lane. (value, index) with distinct indices is a
+// total order, so the result does not depend on the order of the comparisons. Within each row of
+// 16 lanes by DPP (swaps within quads, then the half-row and row mirrors), then the four rows'
+// results through readlane.
+__device__ __forceinline__ void wave_argmax(float &v, int &e) {
+  argmax_dpp<0xB1>(v, e);   // quad_perm [1, 0, 3, 2]
+  argmax_dpp<0x4E>(v, e);   // quad_perm [2, 3, 0, 1]
+  argmax_dpp<0x141>(v, e);  // row_half_mirror: lane i <-> 7 - i within 8
+  argmax_dpp<0x140>(v, e);  // row_mirror: lane i <-> 15 - i within 16
+  float bv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  int be = __builtin_amdgcn_readlane(e, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const float rv =
+        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16 * r));
+    const int re = __builtin_amdgcn_readlane(e, 16 * r);
+    if (better(rv, re, bv, be)) {
+      bv = rv;
+      be = re;
+    }
+  }
+  v = bv;
+  e = be;
+}
+
 // NV = expert slots per lane (E <= 64 NV). The code is kept short (rolled loops): one wave runs
 // it cold, so instruction fetch, not arithmetic, sets its time.
 // Router for decode-sized batches (T <= 8): lanes along the hidden dimension, so a wave's loads
@@ -180,14 +217,7 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, in
         be = e;
       }
     }
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oe = __shfl_xor(be, off);
-      if (better(ov, oe, bv, be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
+    wave_argmax(bv, be);
     if ((be & 63) == lane) taken |= 1u << (be >> 6);
     if (j == 0) sel0 = bv;
     const float ej = expf(bv - sel0);
