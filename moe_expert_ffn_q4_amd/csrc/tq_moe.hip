@@ -167,11 +167,19 @@ __global__ __launch_bounds__(256) void k_router_kl(const float *__restrict__ wr,
   }
 }
 
+// Grouping of a one-token batch, written by the top-k wave itself (no grouping launch): the same
+// outputs as k_group, whose stable scatter reduces for T = 1 to the rank of each chosen expert
+// among the chosen ones.
+struct Group1Out {
+  int *counts, *offsets, *pairs, *inv, *act, *n_active;
+  int act_stride, has_shared;
+};
+
 template <int NV>
 __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, int T, int E,
                                               int hsplit, int topk, int renormalize,
                                               float *__restrict__ logits, int *__restrict__ ids,
-                                              float *__restrict__ wts) {
+                                              float *__restrict__ wts, Group1Out g1) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (blockDim.x >> 6) + (int)(threadIdx.x >> 6);
   if (t >= T) return;  // whole wave
@@ -206,6 +214,7 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, in
   // are written at once, the weights divided by their sum afterwards
   unsigned taken = 0;  // bit i: expert lane + 64 i already selected
   float sel0 = 0.f, denom = 0.f;
+  int my_id = 0x7FFFFFFF;  // lane j < topk: the id chosen in round j
   for (int j = 0; j < topk; ++j) {
     float bv = -INFINITY;
     int be = 0x7FFFFFFF;
@@ -219,6 +228,7 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, in
     }
     wave_argmax(bv, be);
     if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    if (lane == j) my_id = be;
     if (j == 0) sel0 = bv;
     const float ej = expf(bv - sel0);
     if (renormalize) denom += ej;
@@ -237,6 +247,39 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, in
   }
   if (lane == 0)
     for (int j = 0; j < topk; ++j) wts[(int64_t)t * topk + j] = wts[(int64_t)t * topk + j] / denom;
+  if (g1.counts != nullptr) {  // T = 1 (the launch has a single wave at work)
+    // rank of lane j's expert among the chosen ones: its position in expert order
+    int rank = 0;
+    for (int q = 0; q < topk; ++q) rank += __builtin_amdgcn_readlane(my_id, q) < my_id ? 1 : 0;
+    if (lane < topk) {
+      g1.pairs[rank] = lane;
+      g1.inv[lane] = rank;
+      g1.act[rank] = my_id;
+      g1.act[g1.act_stride + rank] = rank;
+      g1.act[2 * g1.act_stride + rank] = 1;
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E) {
+        int below = 0;
+        for (int q = 0; q < topk; ++q) below += __builtin_amdgcn_readlane(my_id, q) < e ? 1 : 0;
+        g1.counts[e] = (int)(taken >> i & 1u);
+        g1.offsets[e] = below;
+      }
+    }
+    if (lane == 0) {
+      g1.offsets[E] = topk;
+      int na = topk;
+      if (g1.has_shared) {  // the shared expert's one position, after the routed pairs
+        g1.act[na] = E;
+        g1.act[g1.act_stride + na] = topk;
+        g1.act[2 * g1.act_stride + na] = 1;
+        ++na;
+      }
+      *g1.n_active = na;
+    }
+  }
 }
 
 // ---- grouping --------------------------------------------------------------------------------------
@@ -651,12 +694,24 @@ int launch_moe_routing(const MoePlan &p, const float *router_w, const float *x, 
     const dim3 g((unsigned)((T + 3) / 4));
     float *lg = (float *)(ws + p.off_logits), *wt = (float *)(ws + p.off_wts);
     int *id = (int *)(ws + p.off_ids);
+    Group1Out g1{};
+    if (T == 1 && env_int("TQ_GROUP1", 1) != 0) {
+      g1.counts = (int *)(ws + p.off_counts);
+      g1.offsets = (int *)(ws + p.off_offsets);
+      g1.pairs = (int *)(ws + p.off_pairs);
+      g1.inv = (int *)(ws + p.off_inv);
+      g1.act = (int *)(ws + p.off_act);
+      g1.n_active = (int *)(ws + p.off_nact);
+      g1.act_stride = p.act_stride;
+      g1.has_shared = s.has_shared ? 1 : 0;
+    }
     if (E <= 64)
-      hipLaunchKernelGGL(k_topk<1>, g, dim3(256), 0, st, rpart, T, E, p.hsplit, k, s.renormalize, lg, id, wt);
+      hipLaunchKernelGGL(k_topk<1>, g, dim3(256), 0, st, rpart, T, E, p.hsplit, k, s.renormalize, lg, id, wt, g1);
     else if (E <= 256)
-      hipLaunchKernelGGL(k_topk<4>, g, dim3(256), 0, st, rpart, T, E, p.hsplit, k, s.renormalize, lg, id, wt);
+      hipLaunchKernelGGL(k_topk<4>, g, dim3(256), 0, st, rpart, T, E, p.hsplit, k, s.renormalize, lg, id, wt, g1);
     else
-      hipLaunchKernelGGL(k_topk<16>, g, dim3(256), 0, st, rpart, T, E, p.hsplit, k, s.renormalize, lg, id, wt);
+      hipLaunchKernelGGL(k_topk<16>, g, dim3(256), 0, st, rpart, T, E, p.hsplit, k, s.renormalize, lg, id, wt, g1);
+    if (g1.counts != nullptr) return hipGetLastError() == hipSuccess ? 0 : -1;
   }
   const size_t glds = group_lds_bytes(s.tokens, s.n_experts);
   if (glds > 65536 &&
