@@ -87,7 +87,9 @@ int tq_dequant(int type, const void *w, int64_t n, int64_t k, int out_type, void
  *   per group of up to 8 tokens; for Q4_K with 2..32 tokens (given the workspace) once for all of
  *   them, on the fp16 matrix cores with exact operands (each activation row scaled by a power of
  *   two and split into fp16 hi + lo, sc * q and the mins as exact fp16 integers), fp32
- *   accumulation.
+ *   accumulation. Q8_0 at 2..16 tokens and Q6_K (k % 512 == 0) at 4..16 tokens stream them once
+ *   on the fp32 matrix cores, with the exactly dequantized weights as operands (x 16-byte
+ *   aligned; the workspace when k spans more than one slice of 8 blocks).
  */
 size_t tq_gemv_workspace_bytes(int type, int64_t n, int64_t k, int64_t batch);
 int tq_gemv(int type, const void *w, int64_t n, int64_t k, const float *x, int64_t batch,
@@ -96,8 +98,8 @@ int tq_gemv(int type, const void *w, int64_t n, int64_t k, const float *x, int64
 /*
  * tq_gemv_multi -- y_p = W_p x for nparts (1..4) matrices of one block type and the same k that
  * share the activations x (the q, k and v projections of a decode step read the same x), in one
- * launch for Q4_K at batch 1..32 (given the workspace; at batch 1 also without), else one launch
- * per matrix.
+ * launch for Q4_K at batch 1..32 (given the workspace; at batch 1 also without) and for the
+ * Q6_K / Q8_0 batches that tq_gemv takes on the fp32 matrix cores, else one launch per matrix.
  *   w, n, y   host arrays of nparts entries: device blob w[p] ([n[p]][k], 16-byte aligned),
  *             rows n[p], device output y[p] ([batch][n[p]] fp32)
  *   x         device [batch][k] fp32, 16-byte aligned
@@ -116,13 +118,14 @@ int tq_gemv_multi(int type, int nparts, const void *const *w, const int64_t *n, 
  * tq_gemv_swiglu -- h[t][r] = silu(g) * u with g = (W_gate x_t)[r], u = (W_up x_t)[r] and
  * silu(z) = z / (1 + exp(-z)): the gate and up projections of a SwiGLU FFN and the gating
  * between them (the Llama-family feed-forward; the pages name the models, not the formula), in
- * one launch for Q4_K at batch 1 (gate and up rows interleaved inside the kernel) and at batch
- * 2..32 given the workspace (gate and up tiles side by side); otherwise two tq_gemv launches and
+ * one launch for Q4_K at batch 1 (gate and up rows interleaved inside the kernel), at batch
+ * 2..32 given the workspace (gate and up tiles side by side), and for the Q6_K / Q8_0 batches
+ * that tq_gemv takes on the fp32 matrix cores (rows interleaved); otherwise two tq_gemv launches and
  * tq_swiglu through the workspace. w_gate, w_up [n][k]; x [batch][k] (16-byte aligned); h
  * [batch][n] fp32. workspace: tq_gemv_swiglu_workspace_bytes(type, n, k, batch) bytes, 256-byte
  * aligned; on the one-launch path it holds the k-slice sums of the int8 matrix-core kernel
- * (k >= 16384) and may be NULL or smaller (the lanes-along-k kernel runs instead). Bitwise equal to tq_gemv +
- * tq_gemv + tq_swiglu when each call gets the workspace it asks for.
+ * (k >= 16384) and may be NULL or smaller (the lanes-along-k kernel runs instead). Bitwise
+ * equal to tq_gemv + tq_gemv + tq_swiglu when each call gets the workspace it asks for.
  */
 size_t tq_gemv_swiglu_workspace_bytes(int type, int64_t n, int64_t k, int64_t batch);
 int tq_gemv_swiglu(int type, const void *w_gate, const void *w_up, int64_t n, int64_t k,
