@@ -438,12 +438,16 @@ def llama70b_bench(args, torch, tq, synth):
     L = tq.lib()
     results = {}
     stream = torch.cuda.Stream()
+    host_q4k = {}  # the Q4_K layer's host blobs, for the oracle's CPU baseline
+    act_bytes = {}
     for t in ("q4_k", "q6_k", "q8_0"):
         T = tq._type(t)
         projs = {}
         for name, n, k in synth.dense_projections(shape):
             w = synth.blob(t, synth.rng(args.seed, "70b", t, name), n, k)
             projs[name] = (torch.from_numpy(w).to("cuda"), n, k)
+            if t == "q4_k":
+                host_q4k[name] = (w, n, k)
         blob_bytes = sum(w.numel() for w, _, _ in projs.values())
         for batch in (1, 4, 16):
             g = synth.rng(args.seed, "70b-act", t, batch)
@@ -488,13 +492,18 @@ def llama70b_bench(args, torch, tq, synth):
                     graph.replay()
                 torch.cuda.synchronize()
                 dt = (time.perf_counter() - t0) / args.steps
+            # algorithmic bytes: every blob once, plus fp32 activations in and out
+            algo = blob_bytes + 4 * batch * sum(n + k for _, n, k in projs.values())
+            act_bytes[f"{t} b{batch}"] = algo
             results[f"{t} b{batch}"] = {"ms_per_layer": round(dt * 1000, 4),
                                         "tokens_s_one_layer": round(batch / dt, 1),
-                                        "blob_gbs": round(blob_bytes / dt / 1e9, 1)}
+                                        "blob_gbs": round(blob_bytes / dt / 1e9, 1),
+                                        "hbm_frac": round(algo / dt / 1e9 / HBM_PEAK_GBS, 4)}
         del projs
         torch.cuda.empty_cache()
     q = results["q4_k b1"]
-    return {
+    achieved = act_bytes["q4_k b1"] / (q["ms_per_layer"] / 1000) / 1e9
+    out = {
         "metric": METRIC, "value": q["tokens_s_one_layer"], "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": q["ms_per_layer"], "higher_is_better": True, "scaling": "weak",
@@ -504,7 +513,37 @@ def llama70b_bench(args, torch, tq, synth):
                                "layer per format, batch 1 / 4 / 16", "global_batch": 1,
                    "seq_len": 1, "parallelism": "none (1 GPU)"},
         "per_format_batch": results,
+        # the layer's four launches (q|k|v, o, gate|up + SwiGLU, down), Q4_K at batch 1: bytes
+        # and time summed over the launches, i.e. per-launch bytes over the average launch time
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "Q4_K batch-1 layer (tq::k_gemv_kl; down on tq::k_gemv_i8)"},
     }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = llama70b_cpu_baseline(host_q4k, args.cpu_seconds)
+    return out
+
+
+def llama70b_cpu_baseline(projs, budget_s):
+    """The oracle (as it is) on the same Q4_K layer at batch 1, whole layers repeated until about
+    budget_s of CPU time has been spent."""
+    import oracle
+    import synth
+
+    xs = {name: synth.normal_f32(synth.rng(7, "70b-cpu-x", name), (1, k))
+          for name, (_, _, k) in projs.items()}
+    layers = 0
+    t0 = time.perf_counter()
+    while True:
+        for name, (w, n, k) in projs.items():
+            oracle.gemv("q4_k", w, n, k, xs[name])
+        layers += 1
+        elapsed = time.perf_counter() - t0
+        if elapsed >= budget_s or layers >= 50:
+            break
+    return {"value": layers / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{layers} full Q4_K layers (7 projections each, batch 1) in {elapsed:.1f} s"}
 
 
 def host_bench(args, torch, tq, synth):
