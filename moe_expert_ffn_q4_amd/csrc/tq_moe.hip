@@ -585,7 +585,8 @@ MoePlan plan_moe(const MoeShape &s) {
   p.router_kl = T <= 8 && s.hidden % 256 == 0 && env_int("TQ_ROUTER_KL", 1) != 0;
   if (p.router_kl) {
     const int steps = (int)(s.hidden / 256);
-    const int hsk = steps < kMaxHSplit ? steps : kMaxHSplit;
+    const int per = clampi(env_int("TQ_ROUTER_STEPS", 1), 1, steps);  // 256-value steps per slice
+    const int hsk = clampi((steps + per - 1) / per, 1, kMaxHSplit);
     p.hpk = (int)(((steps + hsk - 1) / hsk) * 256);
     p.hsplit = (int)((s.hidden + p.hpk - 1) / p.hpk);
   }
