@@ -295,6 +295,30 @@ __global__ __launch_bounds__(512) void k_gemv(const uint8_t *__restrict__ w, int
 // of k (G > 1 only when k fits in 16 / G blocks, so that short rows leave no lane idle); group g of
 // a pass over rows r0.. computes rows r0 + g R .. r0 + g R + R - 1.
 
+// The value of v in lane (lane ^ d), d a power of two fixed at compile time: DPP for 1, 2 and 8
+// (quad permutes, a rotation by 8 within rows of 16), a swizzle for 4 and 16, a lane-half swap for
+// 32 -- register moves instead of LDS permutes on the reduction's dependent chain. The same values
+// as __shfl_xor, so every sum is formed exactly as before.
+__device__ __forceinline__ float xor_recv(float v, int d) {
+  const int iv = __builtin_bit_cast(int, v);
+  int r;
+  if (d == 1) {
+    r = __builtin_amdgcn_update_dpp(0, iv, 0xB1, 0xF, 0xF, false);  // quad_perm [1, 0, 3, 2]
+  } else if (d == 2) {
+    r = __builtin_amdgcn_update_dpp(0, iv, 0x4E, 0xF, 0xF, false);  // quad_perm [2, 3, 0, 1]
+  } else if (d == 8) {
+    r = __builtin_amdgcn_update_dpp(0, iv, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else if (d == 4) {
+    r = __builtin_amdgcn_ds_swizzle(iv, 0x101F);  // bit mode: xor 4 within 32 lanes
+  } else if (d == 16) {
+    r = __builtin_amdgcn_ds_swizzle(iv, 0x401F);  // bit mode: xor 16 within 32 lanes
+  } else {  // 32: lanes 0-31 and 32-63 exchange halves
+    const auto sw = __builtin_amdgcn_permlane32_swap((unsigned)iv, (unsigned)iv, false, false);
+    r = (int)((threadIdx.x & 32) ? sw[0] : sw[1]);
+  }
+  return __builtin_bit_cast(float, r);
+}
+
 template <int R, int G, class Map>
 __device__ __forceinline__ void kl_rows(const u32x4 (&v)[R][3], const float (&xv)[64], float sx_lo,
                                         float sx_hi, const Q4kField &f0, const Q4kField &f1,
@@ -318,11 +342,11 @@ __device__ __forceinline__ void kl_rows(const u32x4 (&v)[R][3], const float (&xv
         if (i < h) {
           const float send = upper ? acc[i] : acc[i + h];
           const float keep = upper ? acc[i + h] : acc[i];
-          acc[i] = keep + __shfl_xor(send, d);
+          acc[i] = keep + xor_recv(send, d);
         }
       cnt = h;
     } else {
-      acc[0] += __shfl_xor(acc[0], d);
+      acc[0] += xor_recv(acc[0], d);
     }
   }
   // lane l of group g now holds row g R + sum_s bit(l, log2(L) - 1 - s) * R / 2^(s+1); lanes with
