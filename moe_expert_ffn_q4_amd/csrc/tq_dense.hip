@@ -351,13 +351,22 @@ __device__ __forceinline__ void kl_rows(const u32x4 (&v)[R][3], const float (&xv
   }
   // lane l of group g now holds row g R + sum_s bit(l, log2(L) - 1 - s) * R / 2^(s+1); lanes with
   // zero low bits store it
-  if ((lane & (L / R - 1)) == 0) {
-    int row = (lane / L) * R;
+  int row = (lane / L) * R;
 #pragma unroll
-    for (int sidx = 0, half = R >> 1; half >= 1; ++sidx, half >>= 1)
-      if (lane & ((L / 2) >> sidx)) row += half;
-    red[wave][row] = acc[0];
+  for (int sidx = 0, half = R >> 1; half >= 1; ++sidx, half >>= 1)
+    if (lane & ((L / 2) >> sidx)) row += half;
+  const bool holder = (lane & (L / R - 1)) == 0;
+  if (nw == 1) {  // one wave: its sums are the rows' totals, stored by the lanes that hold them
+    if (m.swiglu) {  // the up row (row + 1) sits L / R lanes away (the butterfly's last halving)
+      const float u = xor_recv(acc[0], L / R);
+      if (holder && (row & 1) == 0 && r0 + row < re)
+        *m.swiglu_out((r0 + row) >> 1) = silu_mul(acc[0], u);
+    } else if (holder && r0 + row < re) {
+      *m.out(r0 + row) = acc[0];
+    }
+    return;
   }
+  if (holder) red[wave][row] = acc[0];
   __syncthreads();
   if (m.swiglu) {  // rows (gate r, up r) pairs; r0 and re are even
     const int i = 2 * (int)threadIdx.x;
