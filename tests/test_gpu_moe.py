@@ -230,3 +230,45 @@ def test_moe_one_token_lane_groups_bitwise(monkeypatch):
     monkeypatch.setenv("TQ_KL_GROUPS", "1")
     y1, _ = _run(moe, x, shape["n_experts"], k)
     assert np.array_equal(y, y1)
+
+
+@pytest.mark.parametrize("shape,k", [(dict(hidden=768, ffn=512, n_experts=16, shared=True), 4),
+                                     (dict(hidden=512, ffn=1024, n_experts=8, shared=False), 2),
+                                     (dict(hidden=1024, ffn=512, n_experts=300, shared=True), 8)])
+def test_moe_one_token_grouping_in_topk_equals_group_kernel(monkeypatch, shape, k):
+    """For one token the top-k wave writes the grouping itself; it must equal the grouping
+    kernel's (TQ_GROUP1=0) bit for bit, and so must the layer output."""
+    _case("group1", shape, k)
+    t = "q4_k"
+    layer = synth.moe_layer(shape, t, seed=231, tag="group1")
+    x = synth.normal_f32(synth.rng(231, "x", shape["n_experts"]), (1, shape["hidden"]))
+    moe = _layer_to_device(t, shape, layer, k)
+    E = shape["n_experts"]
+    y1, r1 = _run(moe, x, E, k)
+    monkeypatch.setenv("TQ_GROUP1", "0")
+    y0, r0 = _run(moe, x, E, k)
+    for f in ("topk_ids", "counts", "offsets", "pairs"):
+        assert np.array_equal(r1[f], r0[f]), f
+    assert np.array_equal(y1, y0)
+    monkeypatch.delenv("TQ_GROUP1")
+    check_moe(t, shape, layer, x, k, moe=moe)
+
+
+def test_moe_router_weights_not_16_byte_aligned():
+    """Router weights must be 16-byte aligned (the decode-sized router reads them 16 bytes at a
+    time): tq_moe_ffn rejects others with TQ_EINVAL before launching anything."""
+    t, shape, k = "q4_k", dict(hidden=512, ffn=512, n_experts=8, shared=False), 2
+    layer = synth.moe_layer(shape, t, seed=232, tag="misaligned")
+    E, H = shape["n_experts"], shape["hidden"]
+    buf = torch.zeros(E * H + 1, dtype=torch.float32, device="cuda:0")
+    buf[1:] = dev(layer["router"]).reshape(-1)
+    router = buf[1:].view(E, H)  # 4 bytes past a 256-byte boundary
+    assert router.data_ptr() % 16 == 4
+    experts = [tuple(dev(b) for b in e) for e in layer["experts"]]
+    moe = tq.MoeLayer(t, H, shape["ffn"], router, experts, None, top_k=k)
+    x = dev(synth.normal_f32(synth.rng(232, "x"), (3, H)))
+    y = torch.full((3, H), 7.0, device="cuda:0")
+    with pytest.raises(tq.TQError) as err:
+        moe(x, out=y)
+    assert "router_w" in str(err.value)
+    assert bool(torch.all(y == 7.0))  # nothing was launched
