@@ -608,6 +608,15 @@ def host_bench(args, torch, tq, synth):
     }
 
 
+def calibrate_copy(torch):
+    """One plain 1 GiB device-to-device copy: the reading that the HBM counters of the same run
+    are scaled by (bytes copied / counter value)."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 def main():
     args = _args()
     if args.summarize:
@@ -626,14 +635,14 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
-    if args.workload == "deepseek-host":
-        print(json.dumps(host_bench(args, torch, tq, synth)), flush=True)
-        return
-    if args.workload == "llama70b":
-        print(json.dumps(llama70b_bench(args, torch, tq, synth)), flush=True)
-        return
-    if args.workload != "llama8b":
-        print(json.dumps(moe_bench(args, torch, tq, synth)), flush=True)
+    other = {"deepseek-host": host_bench, "llama70b": llama70b_bench}.get(args.workload)
+    if other is None and args.workload != "llama8b":
+        other = moe_bench
+    if other is not None:
+        out = other(args, torch, tq, synth)
+        if args.calibrate_copy:
+            calibrate_copy(torch)
+        print(json.dumps(out), flush=True)
         return
     layers = build_dense_model(tq, synth, torch, args.batch, args.seed)
     stream = torch.cuda.Stream()
@@ -707,10 +716,7 @@ def main():
                      "avg_launch_us": round(avg_launch_s * 1e6, 3)},
     }
     if args.calibrate_copy:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
+        calibrate_copy(torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(synth, args.batch, args.seed, args.cpu_seconds)
     print(json.dumps(out), flush=True)
