@@ -31,6 +31,7 @@ struct MoePlan {
   int act_stride;    // stride of the three arrays of the active-expert list
   int rtiles, hsplit, hpk;
   int router_kl;   // T <= 8: the lanes-along-hidden router (slices of whole 256-value steps)
+  int router_mf;   // T > 8, E >= 64: the fp32 matrix-core router (slices of 16-value steps)
   int gu_rg, gu_ks, gu_upk, gu_waves, gu_upw;
   int d_rg, d_ks, d_upk, d_waves, d_upw;
   int64_t off_rpart, off_logits, off_ids, off_wts, off_counts, off_offsets, off_pairs, off_inv,

@@ -4,6 +4,7 @@
 // Decode path, all on one stream and without host synchronisation:
 //   k_router        logits partial sums (fp32), lane per expert row, tokens through scalar loads
 //   k_router_kl     the same for T <= 8, lanes along the hidden dimension (coalesced rows)
+//   k_router_mf     the same for T > 8 and E >= 64 on the fp32 matrix cores
 //   k_topk          one wave per token: logits = sum of the partials, k largest (ties to the lower
 //                   expert index), softmax weights renormalised over the selected experts
 //   k_group         one workgroup: per-expert counts, exclusive offsets and a stable scatter of the
@@ -12,6 +13,7 @@
 //                   empty items (experts beyond the active count) return at once
 //   k_moe_swiglu    h = silu(gate) * up from the gate/up slices
 //   k_moe_combine   y[t] = sum_j w[t][j] * o[pair (t, j)] + o_shared[t], slots in order
+//   k_moe_combine4  the same sums, a workgroup per token and 16-byte column runs
 // No atomic operation decides any order, so every output is deterministic.
 #include <stdlib.h>
 
@@ -165,6 +167,87 @@ __global__ __launch_bounds__(256) void k_router_kl(const float *__restrict__ wr,
     const int e = e0 + (up32 ? 2 : 0) + (up16 ? 1 : 0);
     if ((lane & 15) == 0 && t < T && e < E) part[((int64_t)hs * 8 + t) * E + e] = b;
   }
+}
+
+// Router for many tokens and experts (T > 8, E >= 64) on the fp32 matrix cores: the logits are
+// the dense product x[T][H] . wr[E][H]^T, fp32 products and sums as in the vector routers, in
+// another order. One wave per (64-token tile, 64-expert tile, hidden slice of hpk values, a
+// multiple of 16); v_mfma_f32_16x16x4_f32 with A = 16 token rows x 4 k, B = 4 k x 16 expert
+// rows, 4 x 4 such blocks per wave. Lane l = 16 g + t loads, per 16-value step of the slice, the
+// 4 values at h + 4 g of token rows 16 i + t and expert rows 16 j + t (one 16-byte load each), so
+// the 4 components of a load feed 4 consecutive MFMAs: every value of the step meets its partner
+// once. The lane receives D[token 4 g + c][expert t]. The next step's 8 loads are issued before
+// the current step's 64 MFMAs (two register sets in turn). Rows beyond T or E are clamped on load
+// and not stored. The 4 expert tiles of one (token tile, slice) are dealt to one XCD in a row, so
+// they share its L2 for the token rows. Output layout as k_router's:
+// part[((tok / 8 * hsplit + hs) * 8 + tok % 8) * E + e].
+typedef float f32x4r __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(64) void k_router_mf(const float *__restrict__ wr, int E, int H,
+                                                  const float *__restrict__ x, int T, int hsplit,
+                                                  int hpk, float *__restrict__ part) {
+  const int nte = (E + 63) >> 6, ntt = (T + 63) >> 6;
+  const int b = blockIdx.x, grp = (b >> 3) / nte * 8 + (b & 7), te = (b >> 3) % nte;
+  if (grp >= ntt * hsplit) return;
+  const int tt = grp / hsplit, hs = grp - tt * hsplit;
+  const int lane = threadIdx.x, g = lane >> 4, t = lane & 15;
+  const int h0 = hs * hpk, h1 = min(h0 + hpk, H);
+  const float *xp[4], *wp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    xp[i] = x + (int64_t)min(tt * 64 + 16 * i + t, T - 1) * H + 4 * g;
+    wp[i] = wr + (int64_t)min(te * 64 + 16 * i + t, E - 1) * H + 4 * g;
+  }
+  f32x4r acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4r{0.f, 0.f, 0.f, 0.f};
+  // two register sets in turn; the scheduling barriers keep each set's loads ahead of the
+  // other set's MFMAs (left to itself the compiler sinks them to the end of the step)
+  f32x4r xa[4], wa[4], xb[4], wb[4];
+  const int n = (h1 - h0) >> 4;
+  auto load = [&](f32x4r *xv, f32x4r *wv, int step) {
+    const int h = h0 + 16 * min(step, n - 1);  // past the end: reload the last step
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xv[i] = *reinterpret_cast<const f32x4r *>(xp[i] + h);
+      wv[i] = *reinterpret_cast<const f32x4r *>(wp[i] + h);
+    }
+  };
+  auto mma = [&](const f32x4r *xv, const f32x4r *wv) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[i][c], wv[j][c], acc[i][j], 0, 0, 0);
+  };
+  load(xa, wa, 0);
+  for (int st = 0; st + 1 < n; st += 2) {
+    load(xb, wb, st + 1);
+    mma(xa, wa);
+    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);   // the 8 loads first
+    __builtin_amdgcn_sched_group_barrier(0x008, 64, 0);  // then the 64 MFMAs
+    load(xa, wa, st + 2);
+    mma(xb, wb);
+    __builtin_amdgcn_sched_group_barrier(0x020, 8, 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 64, 1);
+  }
+  if (n & 1) mma(xa, wa);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = te * 64 + 16 * j + t;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int tok = tt * 64 + 16 * i + 4 * g + c;
+        if (tok < T && e < E)
+          part[(((int64_t)(tok >> 3) * hsplit + hs) * 8 + (tok & 7)) * E + e] = acc[i][j][c];
+      }
+    }
 }
 
 // Grouping of a one-token batch, written by the top-k wave itself (no grouping launch): the same
@@ -544,6 +627,52 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float *__restrict__ o
   }
 }
 
+// The same sums with one workgroup per (token, run of 4 x 256 columns): the token's pair
+// positions and weights are uniform (scalar loads) and each thread adds 4 adjacent columns with
+// 16-byte loads, up to 8 slots' loads in flight at once; slots, and k slices within a slot, are
+// added in the same order as k_moe_combine, so the results are bitwise the same. y 16-byte
+// aligned.
+__global__ __launch_bounds__(256) void k_moe_combine4(const float *__restrict__ o, int ksplit,
+                                                      int64_t P, int H,
+                                                      const int *__restrict__ inv,
+                                                      const float *__restrict__ wts, int T,
+                                                      int topk, int has_shared,
+                                                      float *__restrict__ y) {
+  const int t = blockIdx.y;
+  const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (c >= H) return;
+  const int64_t slice = P * H;
+  const int *ip = inv + (int64_t)t * topk;
+  const float *wp = wts + (int64_t)t * topk;
+  auto ld = [&](int64_t pos, int q) {
+    return *reinterpret_cast<const f32x4r *>(o + q * slice + pos * H + c);
+  };
+  f32x4r acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < topk; j0 += 8) {
+    f32x4r s[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s[j] = ld(ip[min(j0 + j, topk - 1)], 0);
+    for (int q = 1; q < ksplit; ++q)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s[j] += ld(ip[min(j0 + j, topk - 1)], q);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j0 + j < topk) {
+        const float w = wp[j0 + j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, 0.f + s[j][e], acc[e]);
+      }
+  }
+  if (has_shared) {
+    const int64_t pos = (int64_t)T * topk + t;
+    f32x4r s = ld(pos, 0);
+    for (int q = 1; q < ksplit; ++q) s += ld(pos, q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += 0.f + s[e];
+  }
+  *reinterpret_cast<f32x4r *>(y + (int64_t)t * H + c) = acc;
+}
+
 // ---- host side ---------------------------------------------------------------------------------
 
 
@@ -588,6 +717,16 @@ MoePlan plan_moe(const MoeShape &s) {
     const int per = clampi(env_int("TQ_ROUTER_STEPS", 1), 1, steps);  // 256-value steps per slice
     const int hsk = clampi((steps + per - 1) / per, 1, kMaxHSplit);
     p.hpk = (int)(((steps + hsk - 1) / hsk) * 256);
+    p.hsplit = (int)((s.hidden + p.hpk - 1) / p.hpk);
+  }
+  // many tokens and 64 or more experts: the matrix-core router, hidden slices (multiples of 16)
+  // so that about 2048 waves run
+  p.router_mf = !p.router_kl && T > 8 && E >= 64 && env_int("TQ_ROUTER_MF", 1) != 0;
+  if (p.router_mf) {
+    const int64_t tiles = ((T + 63) / 64) * ((E + 63) / 64);
+    int hsm = (int)((2048 + tiles - 1) / tiles);
+    hsm = clampi(hsm, 1, (int)(s.hidden / 256 < kMaxHSplit ? s.hidden / 256 : kMaxHSplit));
+    p.hpk = (int)(((s.hidden + hsm - 1) / hsm + 15) & ~15);
     p.hsplit = (int)((s.hidden + p.hpk - 1) / p.hpk);
   }
   // gate/up: F rows over k = hidden; down: hidden rows over k = F
@@ -686,6 +825,11 @@ int launch_moe_routing(const MoePlan &p, const float *router_w, const float *x, 
   if (p.router_kl && ((uintptr_t)x & 15) == 0 && ((uintptr_t)router_w & 15) == 0) {
     hipLaunchKernelGGL(k_router_kl, dim3((unsigned)(((E + 15) / 16) * p.hsplit)), dim3(256), 0, st,
                        router_w, E, H, x, T, p.hsplit, p.hpk, rpart);
+  } else if (p.router_mf && ((uintptr_t)x & 15) == 0 && ((uintptr_t)router_w & 15) == 0) {
+    const int64_t groups = ((T + 63) / 64) * (int64_t)p.hsplit;
+    const int64_t blocks = (groups + 7) / 8 * 8 * ((E + 63) / 64);
+    hipLaunchKernelGGL(k_router_mf, dim3((unsigned)blocks), dim3(64), 0, st, router_w, E, H, x, T,
+                       p.hsplit, p.hpk, rpart);
   } else {
     const dim3 rgrid((unsigned)(((E + 63) / 64) * p.hsplit), (unsigned)p.rtiles);
     hipLaunchKernelGGL(k_router, rgrid, dim3(256), 0, st, router_w, E, H, x, T, p.hsplit, p.hpk,
@@ -729,6 +873,14 @@ int launch_moe_routing(const MoePlan &p, const float *router_w, const float *x, 
 int launch_moe_combine(const MoePlan &p, char *ws, float *y, hipStream_t st) {
   const MoeShape &s = p.s;
   const int T = (int)s.tokens, k = (int)s.top_k;
+  if (((uintptr_t)y & 15) == 0 && env_int("TQ_COMBINE4", 1) != 0) {
+    const int quads = (int)(s.hidden / 4), threads = T >= 64 ? 256 : 64;
+    hipLaunchKernelGGL(k_moe_combine4, dim3((unsigned)((quads + threads - 1) / threads), T),
+                       dim3(threads), 0, st, (const float *)(ws + p.off_o), p.d_ks, p.P,
+                       (int)s.hidden, (const int *)(ws + p.off_inv),
+                       (const float *)(ws + p.off_wts), T, k, s.has_shared, y);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   const int64_t total = (int64_t)T * s.hidden;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 16384) blocks = 16384;

@@ -272,3 +272,52 @@ def test_moe_router_weights_not_16_byte_aligned():
         moe(x, out=y)
     assert "router_w" in str(err.value)
     assert bool(torch.all(y == 7.0))  # nothing was launched
+
+
+@pytest.mark.parametrize("mf", ["1", "0"], ids=["matrix-cores", "vector"])
+def test_moe_router_many_tokens_ragged_tiles(monkeypatch, mf):
+    """T = 130 tokens and E = 300 experts: neither fills whole 64 x 64 tiles of the matrix-core
+    router (rows clamped on load, not stored); its logits and the vector router's both meet the
+    oracle's bar, and routing and grouping follow bitwise."""
+    monkeypatch.setenv("TQ_ROUTER_MF", mf)
+    t, shape, k = "q4_k", dict(hidden=1024, ffn=256, n_experts=300, shared=True), 8
+    _case("router-ragged", mf, shape, k)
+    layer = synth.moe_layer(shape, t, seed=233, tag="router-ragged")
+    x = synth.normal_f32(synth.rng(233, "x"), (130, shape["hidden"]))
+    check_moe(t, shape, layer, x, k, tokens=[0, 63, 64, 127, 128, 129])
+
+
+def test_moe_router_hidden_slices_not_whole_blocks():
+    """T = 8192, E = 320, hidden 1280: the matrix-core router runs 640 tiles in 4 hidden slices
+    of 320 values (20 steps of 16, not whole 256-value blocks)."""
+    t, shape, k = "q4_k", dict(hidden=1280, ffn=256, n_experts=320, shared=False), 2
+    _case("router-slices", shape, k)
+    layer = synth.moe_layer(shape, t, seed=234, tag="router-slices")
+    x = synth.normal_f32(synth.rng(234, "x"), (8192, shape["hidden"]))
+    check_moe(t, shape, layer, x, k, tokens=[0, 4097, 8191], path=tq.PATH_F32)
+
+
+@pytest.mark.parametrize("T,path", [(1, 0), (33, 0), (33, 1), (300, 2)],
+                         ids=["T1", "T33-auto", "T33-f32", "T300-bf16"])
+def test_moe_combine_column_runs_bitwise(monkeypatch, T, path):
+    """The combine with a workgroup per token and 16-byte column runs gives bitwise the
+    element-wise combine's output (TQ_COMBINE4=0); an output 4 bytes off 16-byte alignment takes
+    the element-wise combine and gives the same bits."""
+    t, shape, k = "q4_k", dict(hidden=768, ffn=512, n_experts=16, shared=True), 4
+    _case("combine4", T, path)
+    layer = synth.moe_layer(shape, t, seed=235, tag="combine4")
+    x = synth.normal_f32(synth.rng(235, "x", T), (T, shape["hidden"]))
+    moe = _layer_to_device(t, shape, layer, k, path=path)
+    xd = dev(x)
+    y4 = host(moe(xd))
+    monkeypatch.setenv("TQ_COMBINE4", "0")
+    y1 = host(moe(xd))
+    monkeypatch.delenv("TQ_COMBINE4")
+    assert np.array_equal(y4, y1)
+    buf = torch.empty(T * shape["hidden"] + 1, dtype=torch.float32, device="cuda:0")
+    out = buf[1:].view(T, shape["hidden"])
+    assert out.data_ptr() % 16 == 4
+    moe(xd, out=out)
+    assert np.array_equal(host(out), y4)
+    if path != 2:  # the bf16 path's parity is covered by the prefill tests
+        check_moe(t, shape, layer, x, k, moe=moe, tokens=[0, T - 1])
