@@ -364,6 +364,8 @@ int tq_moe_ffn_stages(const tq_moe_desc *d, const float *x, int64_t tokens, floa
           return fail(TQ_EDEVICE, "tq_moe_ffn: routing copy failed");
     }
   }
+  // one token, every stage in this call: the combine runs inside the down launch
+  const bool fuse = stages == TQ_MOE_ALL && !s.experts_on_host && tq::moe_fuse_combine_ok(p);
   if (stages & TQ_MOE_EXPERTS) {
     tq::MoeExpertPtrs shared{{d->shared.gate, d->shared.up, d->shared.down}};
     if (s.experts_on_host) {
@@ -371,11 +373,11 @@ int tq_moe_ffn_stages(const tq_moe_desc *d, const float *x, int64_t tokens, floa
       if (rc != TQ_OK) return rc;
     } else {
       rc = tq::launch_moe_experts(p, reinterpret_cast<const tq::MoeExpertPtrs *>(d->experts),
-                                  shared, nullptr, x, ws, st);
+                                  shared, nullptr, x, ws, st, nullptr, fuse ? y : nullptr);
       if (rc) return launched(rc, "tq_moe_ffn experts");
     }
   }
-  if (stages & TQ_MOE_COMBINE) {
+  if ((stages & TQ_MOE_COMBINE) && !fuse) {
     if (tq::launch_moe_combine(p, ws, y, st)) return launched(-1, "tq_moe_ffn combine");
   }
   return TQ_OK;

@@ -362,7 +362,7 @@ __device__ __forceinline__ void kl_rows(const u32x4 (&v)[R][3], const float (&xv
       if (holder && (row & 1) == 0 && r0 + row < re)
         *m.swiglu_out((r0 + row) >> 1) = silu_mul(acc[0], u);
     } else if (holder && r0 + row < re) {
-      *m.out(r0 + row) = acc[0];
+      m.put(r0 + row, acc[0]);
     }
     return;
   }
@@ -381,7 +381,7 @@ __device__ __forceinline__ void kl_rows(const u32x4 (&v)[R][3], const float (&xv
   } else if (threadIdx.x < G * R && r0 + (int)threadIdx.x < re) {
     float s = 0.f;
     for (int q = 0; q < nw; ++q) s += red[q][threadIdx.x];
-    *m.out(r0 + threadIdx.x) = s;
+    m.put(r0 + threadIdx.x, s);
   }
   __syncthreads();
 }
@@ -442,18 +442,66 @@ __global__ __launch_bounds__(512) void k_gemv_kl(KlMap m, int nblk, int rows_per
 
 // Rows of one expert's matrices for the one-token MoE kernel: two pointers and no arrays (a
 // general row map built inside a kernel and indexed at run time is kept in scratch memory).
+// A pointer that is the same in every lane, moved to scalar registers.
+__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
+  const uint64_t u = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u),
+                 hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const uint8_t *)(((uint64_t)hi << 32) | lo);
+}
+
 struct MoeRowMap {
   const uint8_t *w0, *w1;  // gate, up (gate_up) or down, unused
   float *y;
   int swiglu, total;
   int64_t row_bytes;
+  int coherent;  // sums stored at device scope (read back in the same launch)
+  // The gate / up pick is a select between two scalar registers (opaque to the compiler): left
+  // to itself it makes a two-entry table of the pointers per lane in LDS and reads it back before
+  // every pass's loads.
   __device__ __forceinline__ const uint8_t *row(int v) const {
-    return swiglu ? ((v & 1) ? w1 : w0) + (int64_t)(v >> 1) * row_bytes
-                  : w0 + (int64_t)v * row_bytes;
+    const uint8_t *p0 = uniform_ptr(w0), *p1 = uniform_ptr(w1);
+    asm("" : "+s"(p0), "+s"(p1));
+    return swiglu ? ((v & 1) ? p1 : p0) + (int64_t)(v >> 1) * row_bytes
+                  : p0 + (int64_t)v * row_bytes;
   }
   __device__ __forceinline__ float *swiglu_out(int j) const { return y + j; }
   __device__ __forceinline__ float *out(int v) const { return y + v; }
+  __device__ __forceinline__ void put(int v, float s) const {
+    if (coherent)
+      __hip_atomic_store(y + v, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      y[v] = s;
+  }
 };
+
+// The combine of a one-token layer inside the down launch: each workgroup counts itself on its
+// row range's counter once its sums are stored (device-scope stores, awaited before counting);
+// the last of the active slots to arrive adds, for each of the range's rows, the slots in order
+// and then the shared expert, exactly as the combine kernel does. Counters start at zero (the
+// gate/up launch of the same call clears them); nothing waits on another workgroup.
+__device__ __forceinline__ void moe_kl_combine(const MoeKlArgs &a, int rb, int re, int rr) {
+  __shared__ int last;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this workgroup's sums are stored
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(&a.ctr[rr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           (unsigned)(*a.n_active - 1);
+  __syncthreads();
+  if (!last) return;
+  for (int c = rb + (int)threadIdx.x; c < re; c += blockDim.x) {
+    float acc = 0.f;
+    for (int j = 0; j < a.topk; ++j) {
+      const float v = __hip_atomic_load(a.out + (int64_t)a.inv[j] * a.ldo + c, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+      acc = __builtin_fmaf(a.wts[j], 0.f + v, acc);
+    }
+    if (a.has_shared)
+      acc += 0.f + __hip_atomic_load(a.out + (int64_t)a.Tk * a.ldo + c, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+    a.fuse_y[c] = acc;
+  }
+}
 
 // The same kernel over the experts of a one-token MoE step: workgroup b works on active slot
 // slot0 + b / wgs_per_slot (every active expert has that one token). gate/up: the expert's
@@ -463,6 +511,9 @@ template <int R, int G>
 __global__ __launch_bounds__(512) void k_moe_kl(MoeKlArgs a, int nblk, int rows_per_wg,
                                                 int wgs_per_slot) {
   __shared__ float red[8][G * R];
+  if (a.nctr > 0 && blockIdx.x == 0)  // gate/up of a fused one-token call: clear the counters
+    for (int i = (int)threadIdx.x; i < a.nctr; i += blockDim.x)
+      __hip_atomic_store(a.ctr + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int slot = a.slot0 + (int)blockIdx.x / wgs_per_slot;
   if (slot >= *a.n_active) return;
   const int e = a.act[slot], p = a.act[a.act_stride + slot];
@@ -477,12 +528,14 @@ __global__ __launch_bounds__(512) void k_moe_kl(MoeKlArgs a, int nblk, int rows_
     else
       w[q] = (const uint8_t *)a.experts[e].m[mat];
   }
-  const MoeRowMap m{w[0], w[1], a.out + (int64_t)p * a.ldo, a.gate_up, a.rows, a.row_bytes};
+  const MoeRowMap m{w[0], w[1], a.out + (int64_t)p * a.ldo, a.gate_up, a.rows, a.row_bytes,
+                    a.fuse_y != nullptr};
   int64_t xrow = p;
   if (a.gate_up) xrow = p >= a.Tk ? p - a.Tk : a.pairs[p] / a.topk;
   const int rb = ((int)blockIdx.x % wgs_per_slot) * rows_per_wg;
   const int re = min(rb + rows_per_wg, a.rows);
   kl_body<R, G, MoeRowMap>(m, nblk, rb, re, a.x + xrow * a.ldx, red);
+  if (a.fuse_y != nullptr) moe_kl_combine(a, rb, re, (int)blockIdx.x % wgs_per_slot);
 }
 
 // Fallback for shapes whose rows are not dword aligned (Q6_K with k % 512 != 0, Q8_0 with

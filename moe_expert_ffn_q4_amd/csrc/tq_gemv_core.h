@@ -575,6 +575,7 @@ struct KlMap {
   }
   // SwiGLU output j (rows 2j, 2j+1)
   __device__ __forceinline__ float *swiglu_out(int j) const { return y[0] + j; }
+  __device__ __forceinline__ void put(int v, float s) const { *out(v) = s; }
   __device__ __forceinline__ float *out(int v) const {
     float *p0 = y[0], *p1 = y[1], *p2 = y[2], *p3 = y[3];
     asm("" : "+s"(p0), "+s"(p1), "+s"(p2), "+s"(p3));

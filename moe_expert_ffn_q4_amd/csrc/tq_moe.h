@@ -32,10 +32,11 @@ struct MoePlan {
   int rtiles, hsplit, hpk;
   int router_kl;   // T <= 8: the lanes-along-hidden router (slices of whole 256-value steps)
   int router_mf;   // T > 8, E >= 64: the fp32 matrix-core router (slices of 16-value steps)
+  int nctr;        // T = 1: arrival counters of the fused combine (0: none)
   int gu_rg, gu_ks, gu_upk, gu_waves, gu_upw;
   int d_rg, d_ks, d_upk, d_waves, d_upw;
   int64_t off_rpart, off_logits, off_ids, off_wts, off_counts, off_offsets, off_pairs, off_inv,
-      off_act, off_nact, off_gu, off_h, off_o, off_stage;
+      off_act, off_nact, off_gu, off_h, off_o, off_stage, off_ctr;
   int64_t off_xb, off_hb, off_chunks, off_nchunks;  // matrix-core paths only
   int64_t off_xsplit, off_hsplit;                    // fp16 split rows (qmm)
   int max_chunks;
@@ -63,6 +64,13 @@ struct MoeKlArgs {
   int64_t ldx;
   float *out;         // h [P][ffn] or o [P][hidden]
   int64_t ldo;
+  // One token with the combine fused into the down launch (all null / 0 otherwise):
+  unsigned *ctr;      // arrival counters, one per row range of the down launch
+  int nctr;           // gate/up: its first workgroup zeroes ctr[0 .. nctr)
+  float *fuse_y;      // down: y [hidden], written by the last workgroup of each row range
+  const float *wts;   // the token's routing weights [topk]
+  const int *inv;     // the positions of the token's slots [topk]
+  int has_shared;     // the shared expert's output sits at position Tk
 };
 bool moe_klane_ok(int fmt, int64_t hidden, int64_t ffn, int64_t tokens);
 int launch_moe_kl(const MoeKlArgs &a, int64_t k, int nslots, hipStream_t s);
@@ -79,7 +87,11 @@ struct SlotRange {
 // blobs are read from the workspace's staging area, slot a at staging + a * stage_stride.
 int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
                        const MoeExpertPtrs &shared, const uint8_t *staging, const float *x,
-                       char *ws, hipStream_t st, const SlotRange *range = nullptr);
+                       char *ws, hipStream_t st, const SlotRange *range = nullptr,
+                       float *fuse_y = nullptr);
+// One-token layers on the lanes-along-k kernels: the combine can run inside the down launch
+// (launch_moe_experts with fuse_y = y; then no launch_moe_combine).
+bool moe_fuse_combine_ok(const MoePlan &p);
 // y[t] = the routing-weighted sum of the per-position outputs (plus the shared expert's).
 int launch_moe_combine(const MoePlan &p, char *ws, float *y, hipStream_t st);
 

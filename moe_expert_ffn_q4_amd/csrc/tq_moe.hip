@@ -783,6 +783,10 @@ MoePlan plan_moe(const MoeShape &s) {
     p.off_h = take(p.P * s.ffn * 4);
   }
   p.off_o = take((int64_t)p.d_ks * p.P * s.hidden * 4);
+  // one token: arrival counters for the combine fused into the down launch, one per row range
+  // (a range holds at least 4 rows, so hidden / 4 + 1 always suffice)
+  p.nctr = T == 1 && p.klane ? (int)(s.hidden / 4 + 1) : 0;
+  p.off_ctr = take((int64_t)p.nctr * 4);
   p.stage_stride = align256(s.expert_bytes);
   p.off_stage = take(s.experts_on_host ? (int64_t)(p.max_active) * p.stage_stride : 0);
   p.bytes = o;
@@ -891,9 +895,14 @@ int launch_moe_combine(const MoePlan &p, char *ws, float *y, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+bool moe_fuse_combine_ok(const MoePlan &p) {
+  return p.nctr > 0 && p.klane && p.s.tokens == 1 && p.d_ks == 1 &&
+         env_int("TQ_FUSE_COMBINE", 1) != 0;
+}
+
 int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
                        const MoeExpertPtrs &shared, const uint8_t *staging, const float *x,
-                       char *ws, hipStream_t st, const SlotRange *range) {
+                       char *ws, hipStream_t st, const SlotRange *range, float *fuse_y) {
   const MoeShape &s = p.s;
   const int E = (int)s.n_experts, T = (int)s.tokens, k = (int)s.top_k;
   MoeGemvArgs a{};
@@ -978,6 +987,15 @@ int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
     g.ldx = s.hidden;
     g.out = (float *)(ws + p.off_h);
     g.ldo = s.ffn;
+    if (fuse_y != nullptr) {
+      if (!moe_fuse_combine_ok(p) || range != nullptr) return -2;
+      g.ctr = d.ctr = (unsigned *)(ws + p.off_ctr);
+      g.nctr = p.nctr;  // d.nctr stays 0: only the gate/up launch clears them
+      d.fuse_y = fuse_y;
+      d.wts = (const float *)(ws + p.off_wts);
+      d.inv = (const int *)(ws + p.off_inv);
+      d.has_shared = s.has_shared ? 1 : 0;
+    }
     int rc = launch_moe_kl(g, s.hidden, nslots, st);
     if (rc) return rc;
     d.gate_up = 0;

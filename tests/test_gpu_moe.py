@@ -321,3 +321,33 @@ def test_moe_combine_column_runs_bitwise(monkeypatch, T, path):
     assert np.array_equal(host(out), y4)
     if path != 2:  # the bf16 path's parity is covered by the prefill tests
         check_moe(t, shape, layer, x, k, moe=moe, tokens=[0, T - 1])
+
+
+@pytest.mark.parametrize("shape,k", [(dict(hidden=768, ffn=512, n_experts=16, shared=True), 4),
+                                     (dict(hidden=2048, ffn=1024, n_experts=8, shared=False), 2),
+                                     (dict(hidden=1024, ffn=512, n_experts=300, shared=True), 8)])
+def test_moe_one_token_combine_in_down_launch_bitwise(monkeypatch, shape, k):
+    """One token, every stage in one call: the last down workgroup of each row range adds the
+    slots (counters cleared by the gate/up launch of the same call). Bitwise equal to the separate
+    combine (TQ_FUSE_COMBINE=0) and to a call split into stages, on three calls in a row with
+    different tokens, and within the oracle's bar."""
+    t = "q4_k"
+    _case("fused-combine", shape, k)
+    layer = synth.moe_layer(shape, t, seed=236, tag="fused-combine")
+    moe = _layer_to_device(t, shape, layer, k)
+    E = shape["n_experts"]
+    ws = torch.empty(moe.workspace_bytes(1), dtype=torch.uint8, device="cuda:0")
+    for i in range(3):
+        x = synth.normal_f32(synth.rng(236, "x", i), (1, shape["hidden"]))
+        xd = dev(x)
+        y_f = host(moe(xd, ws=ws))
+        monkeypatch.setenv("TQ_FUSE_COMBINE", "0")
+        y_s = host(moe(xd, ws=ws))
+        monkeypatch.delenv("TQ_FUSE_COMBINE")
+        assert np.array_equal(y_f, y_s), f"call {i}"
+        y_st = torch.full_like(xd, float("nan"))
+        moe(xd, out=y_st, ws=ws, stages=tq.MOE_ROUTE)
+        moe(xd, out=y_st, ws=ws, stages=tq.MOE_EXPERTS | tq.MOE_COMBINE)
+        assert np.array_equal(host(y_st), y_f), f"stages, call {i}"
+        if i == 2:
+            check_moe(t, shape, layer, x, k, moe=moe)
