@@ -293,10 +293,10 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, in
     if (lane + 64 * i < E) logits[(int64_t)t * E + lane + 64 * i] = v[i];
     else v[i] = -INFINITY;
   }
-  // k rounds of a wave arg-max on (value, -index); round j's id and exp(value - first value)
-  // are written at once, the weights divided by their sum afterwards
+  // k rounds of a wave arg-max on (value, -index); round j's id is written at once, its
+  // exp(value - first value) kept by lane j and divided by the sum at the end (no read-back)
   unsigned taken = 0;  // bit i: expert lane + 64 i already selected
-  float sel0 = 0.f, denom = 0.f;
+  float sel0 = 0.f, denom = 0.f, my_w = 0.f;
   int my_id = 0x7FFFFFFF;  // lane j < topk: the id chosen in round j
   for (int j = 0; j < topk; ++j) {
     float bv = -INFINITY;
@@ -311,14 +311,14 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, in
     }
     wave_argmax(bv, be);
     if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == j) my_id = be;
     if (j == 0) sel0 = bv;
     const float ej = expf(bv - sel0);
-    if (renormalize) denom += ej;
-    if (lane == 0) {
-      ids[(int64_t)t * topk + j] = be;
-      wts[(int64_t)t * topk + j] = ej;
+    if (lane == j) {
+      my_id = be;
+      my_w = ej;
     }
+    if (renormalize) denom += ej;
+    if (lane == 0) ids[(int64_t)t * topk + j] = be;
   }
   if (!renormalize) {
     float s = 0.f;
@@ -328,8 +328,7 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, in
     for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
     denom = s;
   }
-  if (lane == 0)
-    for (int j = 0; j < topk; ++j) wts[(int64_t)t * topk + j] = wts[(int64_t)t * topk + j] / denom;
+  if (lane < topk) wts[(int64_t)t * topk + lane] = my_w / denom;
   if (g1.counts != nullptr) {  // T = 1 (the launch has a single wave at work)
     // rank of lane j's expert among the chosen ones: its position in expert order
     int rank = 0;

@@ -43,3 +43,18 @@ def test_hot_kernels_use_no_scratch(resources, pattern, occ):
     for name, r in hits.items():
         assert r["scratch"] == 0, f"{name}: {r['scratch']} bytes of scratch per lane"
         assert r["occupancy"] >= occ, f"{name}: occupancy {r['occupancy']} < {occ}"
+
+
+# (pattern, largest LDS bytes per workgroup): the lanes-along-k kernels keep only their reduction
+# table in LDS. The one-token MoE kernel once carried 20 KB more: the compiler had turned the
+# pick between the gate and up pointers into a per-lane table in LDS, sized for the 512-thread
+# bound and read back before every pass's loads.
+SMALL_LDS = [(r"k_gemv_klILi", 1024), (r"k_moe_klILi", 1024), (r"k_router_mf|k_router_kl", 0)]
+
+
+@pytest.mark.parametrize("pattern,most", SMALL_LDS, ids=[p for p, _ in SMALL_LDS])
+def test_lanes_along_k_kernels_keep_lds_small(resources, pattern, most):
+    hits = {k: v for k, v in resources.items() if re.search(pattern, k)}
+    assert hits, f"no kernel matches {pattern}"
+    for name, r in hits.items():
+        assert r["lds"] <= most, f"{name}: {r['lds']} bytes of LDS"
