@@ -265,9 +265,6 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, in
                                               float *__restrict__ wts, Group1Out g1) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (blockDim.x >> 6) + (int)(threadIdx.x >> 6);
-  if (t >= T) return;  // whole wave
-  const int tile = t >> 3, tt = t & 7;
-  const float *pbase = part + ((int64_t)tile * hsplit * 8 + tt) * E;
   // logits: the hidden slices' partial sums, added in slice order. They were just written by the
   // router's workgroups on every XCD, so each dependent batch of loads costs a memory round trip:
   // up to 4 slots per lane every slice's load goes out at once (HB = all 32), beyond 8 at a time.
@@ -275,18 +272,40 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, in
   float v[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) v[i] = 0.f;
-  for (int h0 = 0; h0 < hsplit; h0 += HB) {
-    float b[NV][HB];
+  if (NV > 1 && NV <= 4 && T == 1) {
+    // One token: the workgroup's 4 waves share the sums (wave w: experts 64 w .. 64 w + 63, the
+    // same additions in the same order as below, the padded slices' +0 included), so each lane
+    // issues hsplit loads instead of NV hsplit; then wave 0 goes on alone.
+    __shared__ float lg[4 * 64];
+    const int w = (int)(threadIdx.x >> 6), e = min(lane + 64 * w, E - 1);
+    float sum = 0.f;
+    float b[HB];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = min(lane + 64 * i, E - 1);
+    for (int q = 0; q < HB; ++q) b[q] = part[(int64_t)min(q, hsplit - 1) * 8 * E + e];
 #pragma unroll
-      for (int q = 0; q < HB; ++q) b[i][q] = pbase[(int64_t)min(h0 + q, hsplit - 1) * 8 * E + e];
+    for (int q = 0; q < HB; ++q) sum += q < hsplit ? b[q] : 0.f;
+    lg[64 * w + lane] = sum;
+    __syncthreads();
+    if (t != 0) return;  // waves 1..3
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = lg[64 * i + lane];
+  } else {
+    if (t >= T) return;  // whole wave
+    const int tile = t >> 3, tt = t & 7;
+    const float *pbase = part + ((int64_t)tile * hsplit * 8 + tt) * E;
+    for (int h0 = 0; h0 < hsplit; h0 += HB) {
+      float b[NV][HB];
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int e = min(lane + 64 * i, E - 1);
+#pragma unroll
+        for (int q = 0; q < HB; ++q) b[i][q] = pbase[(int64_t)min(h0 + q, hsplit - 1) * 8 * E + e];
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int q = 0; q < HB; ++q) v[i] += h0 + q < hsplit ? b[i][q] : 0.f;
     }
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-#pragma unroll
-      for (int q = 0; q < HB; ++q) v[i] += h0 + q < hsplit ? b[i][q] : 0.f;
   }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
