@@ -199,9 +199,12 @@ size_t tq_moe_workspace_bytes(const tq_moe_desc *desc, int64_t tokens);
  * into the workspace with hipMemcpyAsync on copy_stream (NULL: on `stream`), each followed by an
  * event. The shared expert (always on the device) runs first; where each expert has kernels of
  * its own (one token, or Q6_K / Q8_0) they wait only for their own copy; on the matrix-core paths
- * (bf16 prefill; Q4_K with 2+ tokens) one grouped launch waits for all copies. Host blobs must stay valid until the call's work has completed; they
- * must be pinned (hipHostMalloc) for the copies to be asynchronous. The output is bitwise
- * identical to the device-resident call's.
+ * (bf16 prefill; Q4_K with 2+ tokens) one grouped launch waits for all copies. Host blobs must
+ * stay valid until the call's work has completed; they must be pinned (hipHostMalloc) for the
+ * copies to be asynchronous. The output is bitwise identical to the device-resident call's.
+ * A one-token Q4_K call with the experts on the device adds the slots inside its down launch
+ * (the last workgroup of each row range, counted on counters the same call clears first); the
+ * output is bitwise what the separate combine stage gives.
  * Deterministic: the same inputs give bitwise-identical outputs and routing.
  */
 int tq_moe_ffn(const tq_moe_desc *desc, const float *x, int64_t tokens, float *y,
