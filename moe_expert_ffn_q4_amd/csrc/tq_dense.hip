@@ -360,7 +360,7 @@ __device__ __forceinline__ void kl_rows(const u32x4 (&v)[R][3], const float (&xv
     if (m.swiglu) {  // the up row (row + 1) sits L / R lanes away (the butterfly's last halving)
       const float u = xor_recv(acc[0], L / R);
       if (holder && (row & 1) == 0 && r0 + row < re)
-        *m.swiglu_out((r0 + row) >> 1) = silu_mul(acc[0], u);
+        gstore(m.swiglu_out((r0 + row) >> 1), silu_mul(acc[0], u));
     } else if (holder && r0 + row < re) {
       m.put(r0 + row, acc[0]);
     }
@@ -376,7 +376,7 @@ __device__ __forceinline__ void kl_rows(const u32x4 (&v)[R][3], const float (&xv
         g += red[q][i];
         u += red[q][i + 1];
       }
-      *m.swiglu_out((r0 + i) >> 1) = silu_mul(g, u);
+      gstore(m.swiglu_out((r0 + i) >> 1), silu_mul(g, u));
     }
   } else if (threadIdx.x < G * R && r0 + (int)threadIdx.x < re) {
     float s = 0.f;
@@ -471,7 +471,7 @@ struct MoeRowMap {
     if (coherent)
       __hip_atomic_store(y + v, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else
-      y[v] = s;
+      gstore(y + v, s);
   }
 };
 

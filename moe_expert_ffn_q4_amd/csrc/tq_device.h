@@ -11,6 +11,17 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // Four dwords loaded with only 4-byte alignment guaranteed (rows of Q6_K / Q8_0 blobs).
 typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
 
+// Loads and stores through the global address space. Pointers read from a device table, or
+// passed through an asm statement (the scalar-register selects of the row maps), are generic to
+// the compiler, and generic (flat) accesses count against lgkmcnt as well as vmcnt: every wait
+// for a scalar load or an LDS access would then also wait for the weight prefetch in flight.
+typedef const u32x4 __attribute__((address_space(1))) *gu32x4;
+
+__device__ __forceinline__ u32x4 gload(const void *p) { return *(gu32x4)p; }
+__device__ __forceinline__ void gstore(float *p, float v) {
+  *(__attribute__((address_space(1))) float *)p = v;
+}
+
 // IEEE binary16 bits (low 16 bits of `bits`) -> fp32. Exact; subnormals are kept because HIP
 // kernels run with fp16 denormals enabled.
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits) {

@@ -29,6 +29,9 @@ typedef float f32x4m __attribute__((ext_vector_type(4)));
 constexpr int kF32mRT = 2;         // 16-row tiles per wave
 constexpr int kF32mMaxSlices = 8;  // k slices
 
+// Dwords read through the global address space (row pointers from the row map are generic).
+typedef const __attribute__((address_space(1))) uint32_t gu32;
+
 template <int FMT>
 struct F32mRaw;
 
@@ -37,7 +40,7 @@ template <>
 struct F32mRaw<FMT_Q8_0> {
   uint32_t v[17];
   __device__ __forceinline__ void load(const uint8_t *row, int kb, int g) {
-    const uint32_t *p = reinterpret_cast<const uint32_t *>(row + (int64_t)kb * 272 + 68 * g);
+    const gu32 *p = (const gu32 *)(row + (int64_t)kb * 272 + 68 * g);
 #pragma unroll
     for (int i = 0; i < 17; ++i) v[i] = p[i];
   }
@@ -57,9 +60,9 @@ struct F32mRaw<FMT_Q6_K> {
   uint32_t shift;  // 2 for odd kb, else 0 (wave-uniform)
   __device__ __forceinline__ void load(const uint8_t *row, int kb, int g) {
     const int off = kb * 210, h = g >> 1;
-    const uint32_t *base = reinterpret_cast<const uint32_t *>(row + (off & ~3));
+    const gu32 *base = (const gu32 *)(row + (off & ~3));
     shift = (uint32_t)(off & 2);
-    dbits = *reinterpret_cast<const uint16_t *>(row + off + 208);
+    dbits = *(const __attribute__((address_space(1))) uint16_t *)(row + off + 208);
 #pragma unroll
     for (int i = 0; i < 17; ++i) ql[i] = base[16 * h + i];
 #pragma unroll

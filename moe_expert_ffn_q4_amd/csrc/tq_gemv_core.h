@@ -575,7 +575,7 @@ struct KlMap {
   }
   // SwiGLU output j (rows 2j, 2j+1)
   __device__ __forceinline__ float *swiglu_out(int j) const { return y[0] + j; }
-  __device__ __forceinline__ void put(int v, float s) const { *out(v) = s; }
+  __device__ __forceinline__ void put(int v, float s) const { gstore(out(v), s); }
   __device__ __forceinline__ float *out(int v) const {
     float *p0 = y[0], *p1 = y[1], *p2 = y[2], *p3 = y[3];
     asm("" : "+s"(p0), "+s"(p1), "+s"(p2), "+s"(p3));
@@ -593,10 +593,10 @@ __device__ __forceinline__ void kl_load_rows(const Map &m, int r0, int boff, int
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int row = min(r0 + r, m.total - 1);
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(m.row(row) + boff);
-    v[r][0] = p[0];
-    v[r][1] = p[1 + 2 * c];
-    v[r][2] = p[2 + 2 * c];
+    const uint8_t *p = m.row(row) + boff;
+    v[r][0] = gload(p);
+    v[r][1] = gload(p + 16 * (1 + 2 * c));
+    v[r][2] = gload(p + 16 * (2 + 2 * c));
   }
 }
 

@@ -11,11 +11,6 @@ namespace tq {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Loads through the global address space (the blob pointers come from a device table, so the
-// compiler would otherwise issue generic loads, which it cannot count precisely).
-typedef const u32x4 __attribute__((address_space(1))) *gu32x4;
-
-__device__ __forceinline__ u32x4 gload(const void *p) { return *(gu32x4)p; }
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
