@@ -16,6 +16,7 @@ typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
 // the compiler, and generic (flat) accesses count against lgkmcnt as well as vmcnt: every wait
 // for a scalar load or an LDS access would then also wait for the weight prefetch in flight.
 typedef const u32x4 __attribute__((address_space(1))) *gu32x4;
+typedef const u32x4a4 __attribute__((address_space(1))) *gu32x4a4;
 
 __device__ __forceinline__ u32x4 gload(const void *p) { return *(gu32x4)p; }
 __device__ __forceinline__ void gstore(float *p, float v) {

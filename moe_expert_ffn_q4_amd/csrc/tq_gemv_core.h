@@ -61,7 +61,7 @@ struct Unit<FMT_Q8_0> {
 
 // Q4_K: the block starts at a multiple of 144 bytes from a 16-byte aligned row start.
 __device__ __forceinline__ void load_unit(Unit<FMT_Q4_K> &u, const uint8_t *row, int idx) {
-  const u32x4 *p = reinterpret_cast<const u32x4 *>(row + (size_t)idx * 144);
+  const gu32x4 p = (gu32x4)(row + (size_t)idx * 144);
 #pragma unroll
   for (int i = 0; i < 9; ++i) u.v[i] = *(p + i);
 }
@@ -73,7 +73,7 @@ __device__ __forceinline__ void load_unit(Unit<FMT_Q4_K> &u, const uint8_t *row,
 __device__ __forceinline__ void load_unit(Unit<FMT_Q6_K> &u, const uint8_t *row, int idx) {
   const int off = idx * 210;
   const uint8_t *base = row + (off & ~3);
-  const u32x4a4 *p = reinterpret_cast<const u32x4a4 *>(base);
+  const gu32x4a4 p = (gu32x4a4)base;
   uint32_t r[53];
 #pragma unroll
   for (int i = 0; i < 13; ++i) {
@@ -83,9 +83,9 @@ __device__ __forceinline__ void load_unit(Unit<FMT_Q6_K> &u, const uint8_t *row,
     r[4 * i + 2] = t.z;
     r[4 * i + 3] = t.w;
   }
-  const uint32_t dbits = *reinterpret_cast<const uint16_t *>(row + off + 208);
+  const uint32_t dbits = *(const __attribute__((address_space(1))) uint16_t *)(row + off + 208);
   if (off & 2) {  // wave-uniform: every lane is at the same block index
-    r[52] = *reinterpret_cast<const uint32_t *>(base + 208);
+    r[52] = *(const __attribute__((address_space(1))) uint32_t *)(base + 208);
 #pragma unroll
     for (int i = 0; i < 52; ++i) u.v[i] = shift2(r[i], r[i + 1]);
   } else {
@@ -98,7 +98,7 @@ __device__ __forceinline__ void load_unit(Unit<FMT_Q6_K> &u, const uint8_t *row,
 // Q8_0: eight blocks (272 bytes) starting at a multiple of 272 from a 16-byte aligned row
 // start (k is a multiple of 256).
 __device__ __forceinline__ void load_unit(Unit<FMT_Q8_0> &u, const uint8_t *row, int idx) {
-  const u32x4 *p = reinterpret_cast<const u32x4 *>(row + (size_t)idx * 272);
+  const gu32x4 p = (gu32x4)(row + (size_t)idx * 272);
 #pragma unroll
   for (int i = 0; i < 17; ++i) {
     u32x4 t = *(p + i);
@@ -323,7 +323,7 @@ __device__ __forceinline__ void unit_dot(const Unit<FMT_Q8_0> &u, const float *c
 
 // Header and the 32 quant bytes of 64-weight group `it` (= 4 * unit + group) of a Q4_K row.
 __device__ __forceinline__ void q4k_group_load(const uint8_t *row, int it, u32x4 (&v)[3]) {
-  const u32x4 *p = reinterpret_cast<const u32x4 *>(row + (size_t)(it >> 2) * 144);
+  const gu32x4 p = (gu32x4)(row + (size_t)(it >> 2) * 144);
   v[0] = *(p);
   v[1] = *(p + 1 + 2 * (it & 3));
   v[2] = *(p + 2 + 2 * (it & 3));
@@ -340,7 +340,7 @@ struct Q4kBlock {
 };
 
 __device__ __forceinline__ void q4k_block_load(const uint8_t *row, int u, Q4kBlock &b) {
-  const u32x4 *p = reinterpret_cast<const u32x4 *>(row + (size_t)u * 144);
+  const gu32x4 p = (gu32x4)(row + (size_t)u * 144);
 #pragma unroll
   for (int i = 0; i < 9; ++i) b.v[i] = p[i];
 }
