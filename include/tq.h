@@ -231,6 +231,61 @@ int tq_moe_ffn_stages(const tq_moe_desc *desc, const float *x, int64_t tokens, f
                       void *workspace, size_t ws_bytes, tq_moe_routing *routing_out, int stages,
                       void *stream);
 
+/* ---- a decode step as one launch ------------------------------------------------------------
+ * A decode step is a chain of products in which every product's input derives from the output of
+ * the product before it: q|k|v, then (attention) o, then (residual and norm) gate|up with the
+ * SwiGLU, then down, then (residual and norm) the next layer. KTransformers replays each decode
+ * step as one CUDA graph (KTransformers page (news.fishai.com.cn), "KTransformers 的技术原理",
+ * "CUDA Graph 优化"); here the whole chain of batch-1 Q4_K products runs as one persistent
+ * launch that fetches every product's weights before the product's input is ready.
+ *
+ * Each op is a tq_gemv_multi (nparts matrices sharing x, batch 1) or, with swiglu set, a
+ * tq_gemv_swiglu (w[0] gate, w[1] up, h in y[0]), and each output is bitwise what that call gives.
+ * Op i reads its x only after op i-1 has stored all of its outputs, so an op may read (or
+ * overwrite) any buffer that an earlier op wrote or read. Weights must not be written by the chain.
+ */
+typedef struct {
+  int nparts;          /* 1..4 matrices sharing x, rows taken one after another (2 with swiglu) */
+  int swiglu;          /* 0, or 1: y[0][r] = silu((w[0] x)[r]) * (w[1] x)[r], n[0] == n[1] */
+  const void *w[4];    /* device Q4_K blobs [n[p]][k], 16-byte aligned (entries past nparts unused) */
+  int64_t n[4];        /* rows of each matrix, >= 1 */
+  float *y[4];         /* device outputs [n[p]] fp32, 4-byte aligned (swiglu: y[0] only, [n[0]]) */
+  int64_t k;           /* a multiple of 256, 256 <= k <= 16384 */
+  const float *x;      /* device [k] fp32, 16-byte aligned */
+} tq_chain_op;
+
+/* Bytes of the plan of a chain of nops ops (1..4096); 0 if nops is out of range. */
+size_t tq_chain_plan_bytes(int nops);
+
+/*
+ * tq_chain_prepare -- check the ops (type must be TQ_Q4_K) and write the chain's plan into plan
+ * (device memory of tq_chain_plan_bytes(nops) bytes, 256-byte aligned, contents irrelevant).
+ * Synchronous (it copies the plan to the device and waits); the ops array may be freed when it
+ * returns. The plan holds the device pointers of the ops, which must stay valid while it is run.
+ */
+int tq_chain_prepare(int type, const tq_chain_op *ops, int nops, void *plan, size_t plan_bytes);
+
+/*
+ * tq_chain_run -- SWITCHED OFF in this build: returns TQ_EUNSUPPORTED and enqueues nothing (the
+ * persistent kernel's waits need every workgroup of its grid resident at once, which a plain
+ * launch does not guarantee). When enabled it enqueues one run of a prepared chain on `stream`:
+ * a small kernel that clears the
+ * plan's completion counters, then the persistent kernel (its workgroups must all be resident at
+ * once; the grid is sized from the device's occupancy for it). No host synchronisation; the pair
+ * may be captured into a graph and replayed. A plan is one run at a time: runs of the same plan
+ * on different streams race. Every device-side wait is bounded: if the device does not make
+ * progress for about a second (e.g. other work holds the compute units the grid needs), the
+ * waiting workgroups give up, the outputs are undefined and the plan's error word is set, which
+ * tq_chain_status reports; the launch still ends normally.
+ */
+int tq_chain_run(void *plan, void *stream);
+
+/*
+ * tq_chain_status -- wait for `stream`, then TQ_OK if no run of the plan has given up a wait since
+ * the last call, else TQ_EDEVICE (and the error word is cleared).
+ */
+int tq_chain_status(void *plan, void *stream);
+
 /* Text of the last non-TQ_OK status returned on this thread ("" if none). */
 const char *tq_last_error(void);
 

@@ -59,6 +59,11 @@ class MoeDesc(C.Structure):
                 ("copy_stream", _vp), ("path", _int)]
 
 
+class ChainOp(C.Structure):
+    _fields_ = [("nparts", _int), ("swiglu", _int), ("w", _vp * 4), ("n", _i64 * 4),
+                ("y", _vp * 4), ("k", _i64), ("x", _vp)]
+
+
 class MoeRouting(C.Structure):
     _fields_ = [("topk_ids", _vp), ("topk_w", _vp), ("logits", _vp), ("counts", _vp),
                 ("offsets", _vp), ("pairs", _vp)]
@@ -90,6 +95,14 @@ def _declare(L: C.CDLL) -> None:
     L.tq_gemv_swiglu_workspace_bytes.restype = C.c_size_t
     L.tq_gemv_swiglu.argtypes = [_int, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _vp, C.c_size_t, _vp]
     L.tq_gemv_swiglu.restype = _int
+    L.tq_chain_plan_bytes.argtypes = [_int]
+    L.tq_chain_plan_bytes.restype = C.c_size_t
+    L.tq_chain_prepare.argtypes = [_int, C.POINTER(ChainOp), _int, _vp, C.c_size_t]
+    L.tq_chain_prepare.restype = _int
+    L.tq_chain_run.argtypes = [_vp, _vp]
+    L.tq_chain_run.restype = _int
+    L.tq_chain_status.argtypes = [_vp, _vp]
+    L.tq_chain_status.restype = _int
     if hasattr(L, "tq_moe_ffn"):
         L.tq_moe_workspace_bytes.argtypes = [C.POINTER(MoeDesc), _i64]
         L.tq_moe_workspace_bytes.restype = C.c_size_t
@@ -209,6 +222,48 @@ def swiglu(g: torch.Tensor, u: torch.Tensor, out=None, stream=None):
         out = torch.empty_like(g)
     _check(lib().tq_swiglu(_ptr(g), _ptr(u), g.numel(), _ptr(out), _stream(stream)))
     return out
+
+
+class Chain:
+    """A prepared chain of batch-1 Q4_K products (tq_chain_prepare / tq_chain_run), run as one
+    persistent launch. ops: list of dicts with keys w (list of uint8 blobs), n (list of rows),
+    y (list of fp32 output tensors), k, x (fp32 input tensor), and optionally swiglu=True (w =
+    [gate, up], y = [h]). Op i reads its x only after op i-1 has stored all of its outputs. The
+    tensors are kept alive here."""
+
+    def __init__(self, t, ops: list, device=None):
+        self.keep = []
+        arr = (ChainOp * len(ops))()
+        for i, op in enumerate(ops):
+            c = arr[i]
+            sw = bool(op.get("swiglu", False))
+            c.nparts = len(op["w"])
+            c.swiglu = int(sw)
+            for p, w in enumerate(op["w"]):
+                c.w[p] = w.data_ptr()
+                c.n[p] = int(op["n"][p])
+            for p, y in enumerate(op["y"]):
+                c.y[p] = y.data_ptr()
+            c.k = int(op["k"])
+            c.x = op["x"].data_ptr()
+            self.keep += list(op["w"]) + list(op["y"]) + [op["x"]]
+        self.ops = arr
+        nbytes = int(lib().tq_chain_plan_bytes(len(ops)))
+        if nbytes == 0:
+            raise ValueError(f"chain of {len(ops)} ops is out of range")
+        dev = device if device is not None else ops[0]["x"].device
+        self.plan = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        _check(lib().tq_chain_prepare(_type(t), arr, len(ops), self.plan.data_ptr(), nbytes))
+
+    def run(self, stream=None):
+        _check(lib().tq_chain_run(self.plan.data_ptr(), _stream(stream)))
+
+    def status(self, stream=None) -> int:
+        """0 (TQ_OK) or TQ_EDEVICE if a run gave up a wait since the last call (the reason is in
+        last_error())."""
+        rc = int(lib().tq_chain_status(self.plan.data_ptr(), _stream(stream)))
+        self.last_error = lib().tq_last_error().decode() if rc else ""
+        return rc
 
 
 class MoeLayer:

@@ -5,6 +5,7 @@
 #include <vector>
 
 #include "tq.h"
+#include "tq_chain.h"
 #include "tq_launch.h"
 #include "tq_moe.h"
 
@@ -387,6 +388,102 @@ int tq_moe_ffn(const tq_moe_desc *d, const float *x, int64_t tokens, float *y, v
                size_t ws_bytes, tq_moe_routing *routing_out, void *stream) {
   if (!y) return fail(TQ_EINVAL, "tq_moe_ffn: null x, y or workspace");
   return tq_moe_ffn_stages(d, x, tokens, y, workspace, ws_bytes, routing_out, TQ_MOE_ALL, stream);
+}
+
+size_t tq_chain_plan_bytes(int nops) {
+  if (nops < 1 || nops > tq::kChainMaxOps) return 0;
+  return tq::chain_plan_bytes(nops);
+}
+
+int tq_chain_prepare(int type, const tq_chain_op *ops, int nops, void *plan, size_t plan_bytes) {
+  if (type != TQ_Q4_K) {
+    if (!known_type(type)) return fail(TQ_EINVAL, "tq_chain_prepare: unknown block type %d", type);
+    return fail(TQ_EUNSUPPORTED, "tq_chain_prepare: chains take Q4_K products only");
+  }
+  if (!ops || !plan) return fail(TQ_EINVAL, "tq_chain_prepare: null ops or plan");
+  if (nops < 1 || nops > tq::kChainMaxOps)
+    return fail(TQ_ESHAPE, "tq_chain_prepare: nops=%d not in 1..%d", nops, tq::kChainMaxOps);
+  if (plan_bytes < tq::chain_plan_bytes(nops))
+    return fail(TQ_ENOSPC, "tq_chain_prepare: plan has %zu bytes, needs %zu", plan_bytes,
+                tq::chain_plan_bytes(nops));
+  if (!aligned(plan, 256)) return fail(TQ_EALIGN, "tq_chain_prepare: plan must be 256-byte aligned");
+  std::vector<tq::ChainOpDesc> d((size_t)nops);
+  for (int i = 0; i < nops; ++i) {
+    const tq_chain_op &o = ops[i];
+    if (o.swiglu != 0 && o.swiglu != 1)
+      return fail(TQ_EINVAL, "tq_chain_prepare: op %d: swiglu must be 0 or 1", i);
+    const int np = o.swiglu ? 2 : o.nparts;
+    if (np < 1 || np > 4 || (o.swiglu && o.nparts != 2))
+      return fail(TQ_EINVAL, "tq_chain_prepare: op %d: nparts=%d (1..4, 2 with swiglu)", i, o.nparts);
+    if (o.k < 256 || o.k > 16384 || o.k % 256)
+      return fail(TQ_ESHAPE, "tq_chain_prepare: op %d: k=%lld (a multiple of 256 in 256..16384)", i,
+                  (long long)o.k);
+    if (!o.x) return fail(TQ_EINVAL, "tq_chain_prepare: op %d: null x", i);
+    if (!aligned(o.x, 16)) return fail(TQ_EALIGN, "tq_chain_prepare: op %d: x must be 16-byte aligned", i);
+    int64_t rows = 0;
+    for (int p = 0; p < np; ++p) {
+      if (!o.w[p] || (!o.y[p] && !(o.swiglu && p == 1)))
+        return fail(TQ_EINVAL, "tq_chain_prepare: op %d: null w or y of matrix %d", i, p);
+      if (o.n[p] < 1 || o.n[p] > (1 << 26))
+        return fail(TQ_ESHAPE, "tq_chain_prepare: op %d: n[%d]=%lld", i, p, (long long)o.n[p]);
+      if (!aligned(o.w[p], 16) || (o.y[p] && !aligned(o.y[p], 4)))
+        return fail(TQ_EALIGN, "tq_chain_prepare: op %d: w 16-byte, y 4-byte alignment needed", i);
+      rows += o.n[p];
+    }
+    if (o.swiglu && o.n[0] != o.n[1])
+      return fail(TQ_ESHAPE, "tq_chain_prepare: op %d: gate and up rows differ", i);
+    if (rows > (1 << 27)) return fail(TQ_ESHAPE, "tq_chain_prepare: op %d: too many rows", i);
+    d[i].nparts = np;
+    d[i].swiglu = o.swiglu;
+    for (int p = 0; p < 4; ++p) {
+      d[i].w[p] = p < np ? o.w[p] : o.w[0];
+      d[i].n[p] = p < np ? o.n[p] : 0;
+      d[i].y[p] = p < np ? o.y[p] : o.y[0];
+    }
+    d[i].k = o.k;
+    d[i].x = o.x;
+  }
+  std::vector<char> buf;
+  if (tq::chain_build(d.data(), nops, buf)) return fail(TQ_ESHAPE, "tq_chain_prepare: too many items");
+  if (hipMemcpy(plan, buf.data(), buf.size(), hipMemcpyHostToDevice) != hipSuccess)
+    return fail(TQ_EDEVICE, "tq_chain_prepare: copy of the plan failed: %s",
+                hipGetErrorString(hipGetLastError()));
+  return TQ_OK;
+}
+
+int tq_chain_run(void *plan, void *stream) {
+  if (!plan) return fail(TQ_EINVAL, "tq_chain_run: null plan");
+  if (!aligned(plan, 256)) return fail(TQ_EALIGN, "tq_chain_run: plan must be 256-byte aligned");
+  (void)stream;
+  // Switched off: the persistent kernel's device-side waits assume that every workgroup of the
+  // grid is resident at once, which an ordinary launch does not guarantee; one run of it left
+  // the device hung. It stays off until the launch guarantees residency (or the work is dealt
+  // by in-order tickets, which needs no residency) and the waits are bounded in time.
+  return fail(TQ_EUNSUPPORTED, "tq_chain_run: the persistent chain is switched off in this build "
+                               "(its waits need every workgroup resident, which a plain launch "
+                               "does not guarantee)");
+}
+
+int tq_chain_status(void *plan, void *stream) {
+  if (!plan) return fail(TQ_EINVAL, "tq_chain_status: null plan");
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+    return fail(TQ_EDEVICE, "tq_chain_status: stream synchronisation failed: %s",
+                hipGetErrorString(hipGetLastError()));
+  unsigned word = 0;
+  char *err = (char *)plan + tq::kChainErrorOffset;
+  if (hipMemcpy(&word, err, sizeof word, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(TQ_EDEVICE, "tq_chain_status: reading the error word failed");
+  if (word == 0) return TQ_OK;
+  const unsigned zero = 0;
+  if (hipMemcpy(err, &zero, sizeof zero, hipMemcpyHostToDevice) != hipSuccess)
+    return fail(TQ_EDEVICE, "tq_chain_status: clearing the error word failed");
+  static const char *const kinds[] = {"?", "for the op before it to complete",
+                                      "for its input to be staged", "for room in the sums ring",
+                                      "for the slice sums of an item"};
+  const unsigned kind = word >> 24;
+  return fail(TQ_EDEVICE, "tq_chain_status: a run gave up waiting %s at op %u (the chain's "
+                          "workgroups were not all resident, or the device stalled); its outputs "
+                          "are undefined", kinds[kind < 5 ? kind : 0], word & 0xFFFFFFu);
 }
 
 }  // extern "C"

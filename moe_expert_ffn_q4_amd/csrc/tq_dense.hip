@@ -295,41 +295,17 @@ __global__ __launch_bounds__(512) void k_gemv(const uint8_t *__restrict__ w, int
 // of k (G > 1 only when k fits in 16 / G blocks, so that short rows leave no lane idle); group g of
 // a pass over rows r0.. computes rows r0 + g R .. r0 + g R + R - 1.
 
-// The value of v in lane (lane ^ d), d a power of two fixed at compile time: DPP for 1, 2 and 8
-// (quad permutes, a rotation by 8 within rows of 16), a swizzle for 4 and 16, a lane-half swap for
-// 32 -- register moves instead of LDS permutes on the reduction's dependent chain. The same values
-// as __shfl_xor, so every sum is formed exactly as before.
-__device__ __forceinline__ float xor_recv(float v, int d) {
-  const int iv = __builtin_bit_cast(int, v);
-  int r;
-  if (d == 1) {
-    r = __builtin_amdgcn_update_dpp(0, iv, 0xB1, 0xF, 0xF, false);  // quad_perm [1, 0, 3, 2]
-  } else if (d == 2) {
-    r = __builtin_amdgcn_update_dpp(0, iv, 0x4E, 0xF, 0xF, false);  // quad_perm [2, 3, 0, 1]
-  } else if (d == 8) {
-    r = __builtin_amdgcn_update_dpp(0, iv, 0x128, 0xF, 0xF, false);  // row_ror:8
-  } else if (d == 4) {
-    r = __builtin_amdgcn_ds_swizzle(iv, 0x101F);  // bit mode: xor 4 within 32 lanes
-  } else if (d == 16) {
-    r = __builtin_amdgcn_ds_swizzle(iv, 0x401F);  // bit mode: xor 16 within 32 lanes
-  } else {  // 32: lanes 0-31 and 32-63 exchange halves
-    const auto sw = __builtin_amdgcn_permlane32_swap((unsigned)iv, (unsigned)iv, false, false);
-    r = (int)((threadIdx.x & 32) ? sw[0] : sw[1]);
-  }
-  return __builtin_bit_cast(float, r);
-}
-
 template <int R, int G, class Map>
 __device__ __forceinline__ void kl_rows(const u32x4 (&v)[R][3], const float (&xv)[64], float sx_lo,
                                         float sx_hi, const Q4kField &f0, const Q4kField &f1,
-                                        float unit_inv, int r0, int re, float (*red)[G * R],
+                                        int r0, int re, float (*red)[G * R],
                                         const Map &m) {
   constexpr int L = 64 / G;  // lanes per group
   static_assert(L >= R, "a group needs at least one lane per row");
   const int lane = threadIdx.x & 63, wave = wave_index(), nw = blockDim.x >> 6;
   float acc[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = kl_group_dot(v[r], xv, sx_lo, sx_hi, f0, f1, unit_inv);
+  for (int r = 0; r < R; ++r) acc[r] = kl_group_dot(v[r], xv, sx_lo, sx_hi, f0, f1);
   // across the group's lanes: each step halves the rows a lane keeps and adds its partner's half
   int cnt = R;
 #pragma unroll
@@ -418,14 +394,13 @@ __device__ __forceinline__ void kl_body(const Map &m, int nblk, int rb, int re,
     sx_lo += xv[i];
     sx_hi += xv[32 + i];
   }
-  const float unit_inv = 1.f / nibble_fp8_unit();
   const Q4kField f0 = q4k_field(2 * c), f1 = q4k_field(2 * c + 1);
   for (int r0 = rb; r0 < re; r0 += 2 * P) {
     if (r0 + P < re) kl_load_rows<R, Map>(m, r0 + P + g * R, boff, c, vb);
-    kl_rows<R, G, Map>(va, xv, sx_lo, sx_hi, f0, f1, unit_inv, r0, re, red, m);
+    kl_rows<R, G, Map>(va, xv, sx_lo, sx_hi, f0, f1, r0, re, red, m);
     if (r0 + P >= re) break;
     if (r0 + 2 * P < re) kl_load_rows<R, Map>(m, r0 + 2 * P + g * R, boff, c, va);
-    kl_rows<R, G, Map>(vb, xv, sx_lo, sx_hi, f0, f1, unit_inv, r0 + P, re, red, m);
+    kl_rows<R, G, Map>(vb, xv, sx_lo, sx_hi, f0, f1, r0 + P, re, red, m);
   }
 }
 

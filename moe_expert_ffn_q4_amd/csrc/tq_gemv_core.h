@@ -600,44 +600,79 @@ __device__ __forceinline__ void kl_load_rows(const Map &m, int r0, int boff, int
   }
 }
 
-// Partial dot product of one row's 64-weight group with this lane's activations; f0 / f1 locate
-// the scale and min of the group's two sub-blocks.
-__device__ __forceinline__ float kl_group_dot(const u32x4 (&v)[3], const float (&xv)[64],
-                                              float sx_lo, float sx_hi, const Q4kField &f0,
-                                              const Q4kField &f1, float unit_inv) {
-  (void)sx_lo;
-  (void)sx_hi;
-  (void)unit_inv;
-  const uint32_t h0 = v[0].x, s0 = v[0].y, s1 = v[0].z, s2 = v[0].w;
-  // quants as fp16 subnormals: the nibble of bits 0-3 (16-19) of a word read as binary16 is
-  // exactly q * 2^-24, that of bits 4-7 (20-23) exactly 16 q * 2^-24; the FMAs take the halves
-  // as fp16 operands (v_fma_mix_f32), so a word yields two weights for one AND
+// The value of v in lane (lane ^ d), d a power of two fixed at compile time: DPP for 1, 2 and 8
+// (quad permutes, a rotation by 8 within rows of 16), a swizzle for 4 and 16, a lane-half swap for
+// 32 -- register moves instead of LDS permutes on the reduction's dependent chain. The same values
+// as __shfl_xor, so every sum is formed exactly as before.
+__device__ __forceinline__ float xor_recv(float v, int d) {
+  const int iv = __builtin_bit_cast(int, v);
+  int r;
+  if (d == 1) {
+    r = __builtin_amdgcn_update_dpp(0, iv, 0xB1, 0xF, 0xF, false);  // quad_perm [1, 0, 3, 2]
+  } else if (d == 2) {
+    r = __builtin_amdgcn_update_dpp(0, iv, 0x4E, 0xF, 0xF, false);  // quad_perm [2, 3, 0, 1]
+  } else if (d == 8) {
+    r = __builtin_amdgcn_update_dpp(0, iv, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else if (d == 4) {
+    r = __builtin_amdgcn_ds_swizzle(iv, 0x101F);  // bit mode: xor 4 within 32 lanes
+  } else if (d == 16) {
+    r = __builtin_amdgcn_ds_swizzle(iv, 0x401F);  // bit mode: xor 16 within 32 lanes
+  } else {  // 32: lanes 0-31 and 32-63 exchange halves
+    const auto sw = __builtin_amdgcn_permlane32_swap((unsigned)iv, (unsigned)iv, false, false);
+    r = (int)((threadIdx.x & 32) ? sw[0] : sw[1]);
+  }
+  return __builtin_bit_cast(float, r);
+}
+
+// The scale and min of the group's two sub-blocks applied to its two partial sums: dl = sum over
+// the low sub-block of q x (quants as fp16 subnormals, i.e. q * 2^-24), dh the same for the high
+// sub-block with the quants scaled by 16 (their nibble sits 4 bits up).
+__device__ __forceinline__ float kl_group_finish(const u32x4 &hdr, float dl, float dh, float sx_lo,
+                                                 float sx_hi, const Q4kField &f0,
+                                                 const Q4kField &f1) {
+  const uint32_t h0 = hdr.x, s0 = hdr.y, s1 = hdr.z, s2 = hdr.w;
   const float d = half_bits_to_float(h0) * 0x1p24f, dmin = half_bits_to_float(h0 >> 16);
   float sc_lo, m_lo, sc_hi, m_hi;
   q4k_scale_min_at(s0, s1, s2, f0, sc_lo, m_lo);
   q4k_scale_min_at(s0, s1, s2, f1, sc_hi, m_hi);
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  float dl = 0.f, dh = 0.f;
-#pragma unroll
-  for (int dw = 0; dw < 8; ++dw) {
-    const uint32_t wq = dword_of(v[1 + (dw >> 2)], dw & 3);
-    const uint32_t w8 = wq >> 8;
-    const h2 l02 = __builtin_bit_cast(h2, opaque(wq & 0x000F000Fu));
-    const h2 l13 = __builtin_bit_cast(h2, opaque(w8 & 0x000F000Fu));
-    const h2 u02 = __builtin_bit_cast(h2, opaque(wq & 0x00F000F0u));
-    const h2 u13 = __builtin_bit_cast(h2, opaque(w8 & 0x00F000F0u));
-    const float *xl = xv + 4 * dw, *xh = xv + 32 + 4 * dw;
-    dl = __builtin_fmaf((float)l02[0], xl[0], dl);
-    dl = __builtin_fmaf((float)l13[0], xl[1], dl);
-    dl = __builtin_fmaf((float)l02[1], xl[2], dl);
-    dl = __builtin_fmaf((float)l13[1], xl[3], dl);
-    dh = __builtin_fmaf((float)u02[0], xh[0], dh);
-    dh = __builtin_fmaf((float)u13[0], xh[1], dh);
-    dh = __builtin_fmaf((float)u02[1], xh[2], dh);
-    dh = __builtin_fmaf((float)u13[1], xh[3], dh);
-  }
   const float pos = __builtin_fmaf(sc_lo, dl, sc_hi * dh * 0.0625f) * d;
   return __builtin_fmaf(-dmin, __builtin_fmaf(m_lo, sx_lo, m_hi * sx_hi), pos);
+}
+
+typedef _Float16 kl_h2 __attribute__((ext_vector_type(2)));
+
+// Quant dword dw (0..7) of a row's 32 group bytes against four activations of each sub-block
+// (xl: weights 4 dw .. 4 dw + 3 of the low sub-block, xh: the same of the high one), added to
+// the running sums in a fixed order. The nibble of bits 0-3 (16-19) of a word read as binary16 is
+// exactly q * 2^-24, that of bits 4-7 (20-23) exactly 16 q * 2^-24; the FMAs take the halves as
+// fp16 operands (v_fma_mix_f32), so a word yields two weights for one AND.
+__device__ __forceinline__ void kl_dword_fma(uint32_t wq, const float *xl, const float *xh,
+                                             float &dl, float &dh) {
+  const uint32_t w8 = wq >> 8;
+  const kl_h2 l02 = __builtin_bit_cast(kl_h2, opaque(wq & 0x000F000Fu));
+  const kl_h2 l13 = __builtin_bit_cast(kl_h2, opaque(w8 & 0x000F000Fu));
+  const kl_h2 u02 = __builtin_bit_cast(kl_h2, opaque(wq & 0x00F000F0u));
+  const kl_h2 u13 = __builtin_bit_cast(kl_h2, opaque(w8 & 0x00F000F0u));
+  dl = __builtin_fmaf((float)l02[0], xl[0], dl);
+  dl = __builtin_fmaf((float)l13[0], xl[1], dl);
+  dl = __builtin_fmaf((float)l02[1], xl[2], dl);
+  dl = __builtin_fmaf((float)l13[1], xl[3], dl);
+  dh = __builtin_fmaf((float)u02[0], xh[0], dh);
+  dh = __builtin_fmaf((float)u13[0], xh[1], dh);
+  dh = __builtin_fmaf((float)u02[1], xh[2], dh);
+  dh = __builtin_fmaf((float)u13[1], xh[3], dh);
+}
+
+// Partial dot product of one row's 64-weight group with this lane's activations; f0 / f1 locate
+// the scale and min of the group's two sub-blocks.
+__device__ __forceinline__ float kl_group_dot(const u32x4 (&v)[3], const float (&xv)[64],
+                                              float sx_lo, float sx_hi, const Q4kField &f0,
+                                              const Q4kField &f1) {
+  float dl = 0.f, dh = 0.f;
+#pragma unroll
+  for (int dw = 0; dw < 8; ++dw)
+    kl_dword_fma(dword_of(v[1 + (dw >> 2)], dw & 3), xv + 4 * dw, xv + 32 + 4 * dw, dl, dh);
+  return kl_group_finish(v[0], dl, dh, sx_lo, sx_hi, f0, f1);
 }
 
 }  // namespace tq

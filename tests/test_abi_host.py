@@ -120,3 +120,51 @@ def test_moe_host_resident_rejects_null_host_blob():
     d.experts_on_host = 1
     assert L.tq_moe_ffn(C.byref(d), 0x30000, 4, 0x40000, 0x50000, 1 << 34, None, None) == 1
     assert "experts_host" in L.tq_last_error().decode()
+
+
+def _chain_op(**kw):
+    op = tq.ChainOp()
+    op.nparts, op.swiglu, op.k = kw.get("nparts", 1), kw.get("swiglu", 0), kw.get("k", 4096)
+    for p in range(4):
+        op.w[p] = kw.get("w", 4096)
+        op.n[p] = kw.get("n", 64)
+        op.y[p] = kw.get("y", 4096)
+    op.x = kw.get("x", 4096)
+    return op
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=100), 2),             # k not a multiple of 256
+    (dict(k=16640), 2),           # k beyond 16384
+    (dict(nparts=0), 1),          # no matrix
+    (dict(nparts=5), 1),          # too many matrices
+    (dict(swiglu=2), 1),          # swiglu flag not 0/1
+    (dict(swiglu=1, nparts=3), 1),
+    (dict(x=0), 1),               # null x
+    (dict(x=4100), 3),            # x not 16-byte aligned
+    (dict(w=4104), 3),            # w not 16-byte aligned
+    (dict(n=0), 2),               # no rows
+])
+def test_chain_prepare_rejects(kw, code):
+    """Every op is checked before anything touches the device."""
+    L = tq.lib()
+    ops = (tq.ChainOp * 2)(_chain_op(), _chain_op(**kw))
+    nbytes = L.tq_chain_plan_bytes(2)
+    assert nbytes > 0
+    assert L.tq_chain_prepare(1, ops, 2, 4096, nbytes) == code
+    assert L.tq_last_error()
+
+
+def test_chain_prepare_and_run_argument_checks():
+    L = tq.lib()
+    ops = (tq.ChainOp * 1)(_chain_op())
+    assert L.tq_chain_plan_bytes(0) == 0 and L.tq_chain_plan_bytes(5000) == 0
+    assert L.tq_chain_prepare(2, ops, 1, 4096, 1 << 20) == 5     # Q6_K: unsupported
+    assert L.tq_chain_prepare(9, ops, 1, 4096, 1 << 20) == 1     # unknown type
+    assert L.tq_chain_prepare(1, ops, 1, 4096, 16) == 4          # plan too small
+    assert L.tq_chain_prepare(1, ops, 1, 4100, 1 << 20) == 3     # plan not 256-byte aligned
+    assert L.tq_chain_run(None, None) == 1
+    assert L.tq_chain_run(4100, None) == 3
+    # the persistent chain is switched off in this build: refused before any launch
+    assert L.tq_chain_run(4096, None) == 5
+    assert "switched off" in L.tq_last_error().decode()
