@@ -296,6 +296,8 @@ static int host_resident_experts(const tq_moe_desc *d, const tq::MoePlan &p,
   for (int a = 0; a < na; ++a) {
     const int e = act[a];
     if (e == E) continue;  // the shared expert stays on the device
+    if (e < 0 || e > E)
+      return fail(TQ_EDEVICE, "tq_moe_ffn: active-expert list holds id %d (of %d experts)", e, E);
     const tq_expert &hx = d->experts_host[e];
     const void *src[3] = {hx.gate, hx.up, hx.down};
     for (int m = 0; m < 3; ++m)

@@ -492,6 +492,7 @@ __global__ __launch_bounds__(512) void k_moe_kl(MoeKlArgs a, int nblk, int rows_
   const int slot = a.slot0 + (int)blockIdx.x / wgs_per_slot;
   if (slot >= *a.n_active) return;
   const int e = a.act[slot], p = a.act[a.act_stride + slot];
+  if ((unsigned)e > (unsigned)a.E) return;  // never past the expert table (id E: shared expert)
   const uint8_t *w[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {

@@ -323,8 +323,11 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, in
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int e = lane + 64 * i;
-      if (e < E && !(taken >> i & 1u) && better(v[i], e, bv, be)) {
-        bv = v[i];
+      // a NaN logit ranks below every number (ties to the lower index as usual), so the chosen
+      // id is always an unchosen expert in [0, E); its weight then comes out NaN
+      const float vi = v[i] == v[i] ? v[i] : -INFINITY;
+      if (e < E && !(taken >> i & 1u) && better(vi, e, bv, be)) {
+        bv = vi;
         be = e;
       }
     }
@@ -384,6 +387,13 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, in
 }
 
 // ---- grouping --------------------------------------------------------------------------------------
+// An expert id read back from the top-k output, kept inside [0, E) so that no table is ever
+// indexed past its end (the top-k kernel only writes ids in range).
+__device__ __forceinline__ int id_at(const int *ids, int i, int E) {
+  const unsigned e = (unsigned)ids[i];
+  return (int)(e < (unsigned)E ? e : (unsigned)(E - 1));
+}
+
 // One workgroup of 8 waves. Tokens are taken in chunks of 64, one per lane of a wave; a token
 // picks k distinct experts, so for one expert every lane of a chunk appears at most once.
 //   mask[e]    (per wave) the lanes of the current chunk routed to e, built with LDS atomic ORs,
@@ -416,16 +426,16 @@ __global__ __launch_bounds__(512) void k_group(const int *__restrict__ ids, int 
     const int t = c * 64 + lane;
     const bool live = t < T;
     if (live)
-      for (int j = 0; j < topk; ++j) atomicOr(&mymask[ids[t * topk + j]], 1ull << lane);
+      for (int j = 0; j < topk; ++j) atomicOr(&mymask[id_at(ids, t * topk + j, E)], 1ull << lane);
     __builtin_amdgcn_wave_barrier();
     if (live)
       for (int j = 0; j < topk; ++j) {
-        const int e = ids[t * topk + j];
+        const int e = id_at(ids, t * topk + j, E);
         tab[c * E + e] = (unsigned short)__popcll(mymask[e]);
       }
     __builtin_amdgcn_wave_barrier();
     if (live)
-      for (int j = 0; j < topk; ++j) mymask[ids[t * topk + j]] = 0ull;
+      for (int j = 0; j < topk; ++j) mymask[id_at(ids, t * topk + j, E)] = 0ull;
     __builtin_amdgcn_wave_barrier();
   }
   __syncthreads();
@@ -501,12 +511,12 @@ __global__ __launch_bounds__(512) void k_group(const int *__restrict__ ids, int 
     const int t = c * 64 + lane;
     const bool live = t < T;
     if (live)
-      for (int j = 0; j < topk; ++j) atomicOr(&mymask[ids[t * topk + j]], 1ull << lane);
+      for (int j = 0; j < topk; ++j) atomicOr(&mymask[id_at(ids, t * topk + j, E)], 1ull << lane);
     __builtin_amdgcn_wave_barrier();
     if (live) {
       const unsigned long long below = (1ull << lane) - 1ull;
       for (int j = 0; j < topk; ++j) {
-        const int e = ids[t * topk + j];
+        const int e = id_at(ids, t * topk + j, E);
         const int pos = off[e] + (int)tab[c * E + e] + __popcll(mymask[e] & below);
         pairs[pos] = t * topk + j;
         inv[t * topk + j] = pos;
@@ -514,7 +524,7 @@ __global__ __launch_bounds__(512) void k_group(const int *__restrict__ ids, int 
     }
     __builtin_amdgcn_wave_barrier();
     if (live)
-      for (int j = 0; j < topk; ++j) mymask[ids[t * topk + j]] = 0ull;
+      for (int j = 0; j < topk; ++j) mymask[id_at(ids, t * topk + j, E)] = 0ull;
     __builtin_amdgcn_wave_barrier();
   }
 }

@@ -161,6 +161,62 @@ def test_moe_rejects_bad_arguments():
     assert e.value.status == 2
 
 
+NAN_CASES = [(dict(hidden=512, ffn=512, n_experts=8, shared=True), 2, T) for T in (1, 5)] + \
+            [(dict(hidden=256, ffn=256, n_experts=256, shared=False), 8, T) for T in (1, 9)]
+
+
+@pytest.mark.parametrize("shape,k,T", NAN_CASES, ids=lambda v: str(v)[:24])
+def test_moe_nan_activation_routes_in_range(shape, k, T):
+    """A NaN in one token's activations makes all its logits NaN. NaN ranks below every number,
+    so that token takes experts 0..k-1 (ties go to the lower id), its weights and output row are
+    NaN, and every other token's routing and output are those of the oracle."""
+    t, E = "q4_k", shape["n_experts"]
+    _case("moe nan activation", E, k, T)
+    layer = synth.moe_layer(shape, t, seed=230, tag=f"nan-{E}")
+    x = synth.normal_f32(synth.rng(230, "x", E, T), (T, shape["hidden"]))
+    bad = T // 2
+    x[bad, 7] = np.nan
+    moe = _layer_to_device(t, shape, layer, k)
+    y, r = _run(moe, x, E, k)
+    ids = r["topk_ids"]
+    assert np.all((ids >= 0) & (ids < E)), "expert id out of range"
+    assert np.array_equal(ids[bad], np.arange(k)), "NaN token's experts"
+    assert np.all(np.isnan(r["topk_w"][bad])) and np.all(np.isnan(y[bad]))
+    counts, offsets, pairs = oracle.group(ids, E)
+    assert np.array_equal(r["counts"], counts) and np.array_equal(r["offsets"], offsets)
+    assert np.array_equal(r["pairs"], pairs)
+    ok = np.array([i for i in range(T) if i != bad], dtype=np.int64)
+    if ok.size:
+        ref_ids, ref_w = oracle.topk(r["logits"][ok], k)
+        assert np.array_equal(ids[ok], ref_ids)
+        assert np.all(np.abs(r["topk_w"][ok] - ref_w) <= 1e-5 * ref_w + 1e-7)
+        wts = np.zeros((T, k))
+        wts[ok] = ref_w
+        ref, mag = oracle.moe(t, shape["hidden"], shape["ffn"], layer["experts"], layer["shared"],
+                              x, ids, wts, tokens=ok)
+        assert_product_close(y[ok], ref, mag, what="tokens without NaN")
+
+
+def test_moe_nan_router_row_never_chosen():
+    """One expert's router row is NaN: its logit is NaN for every token and ranks below every
+    number, so it is never chosen; the routing and output equal the oracle's with that logit
+    taken as -inf."""
+    t, shape, k, E, T = "q4_k", dict(hidden=512, ffn=512, n_experts=8, shared=True), 2, 8, 40
+    layer = synth.moe_layer(shape, t, seed=231, tag="nan-row")
+    layer["router"][3, 100] = np.nan
+    x = synth.normal_f32(synth.rng(231, "x"), (T, 512))
+    moe = _layer_to_device(t, shape, layer, k)
+    y, r = _run(moe, x, E, k)
+    assert np.all(np.isnan(r["logits"][:, 3]))
+    lg = np.where(np.isnan(r["logits"]), -np.inf, r["logits"]).astype(np.float32)
+    ref_ids, ref_w = oracle.topk(lg, k)
+    assert not np.any(ref_ids == 3)
+    assert np.array_equal(r["topk_ids"], ref_ids)
+    assert np.all(np.abs(r["topk_w"] - ref_w) <= 1e-5 * ref_w + 1e-7)
+    ref, mag = oracle.moe(t, 512, 512, layer["experts"], layer["shared"], x, ref_ids, ref_w)
+    assert_product_close(y, ref, mag, what="moe with a NaN router row")
+
+
 # ---- full-size layers, sampled tokens --------------------------------------------------------
 
 
