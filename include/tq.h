@@ -75,8 +75,9 @@ int tq_dequant(int type, const void *w, int64_t n, int64_t k, int out_type, void
  *   x          [batch][k] fp32, 4-byte aligned; y [batch][n] fp32, 4-byte aligned; y must not
  *              overlap w or x.
  *   workspace  device scratch of at least tq_gemv_workspace_bytes(type, n, k, batch) bytes,
- *              256-byte aligned, zero-filled before its first use; every call leaves its first
- *              64 KiB (completion counters) zeroed again. It lets the k dimension be split across
+ *              256-byte aligned, any contents (its completion counters carry a token that
+ *              differs for every call, so bytes left by other work are never taken for a count;
+ *              nothing needs clearing before or after). It lets the k dimension be split across
  *              workgroups (the partial sums are added in a fixed order, so results stay
  *              deterministic), also for the int8 matrix-core kernel that takes Q4_K at batch 1
  *              for k >= 16384 (its k-slice sums after the first 64 KiB). NULL or too small: no

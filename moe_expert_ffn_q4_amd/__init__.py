@@ -150,9 +150,9 @@ _workspaces: dict = {}
 
 
 def workspace(nbytes: int, device=None, purpose: str = "gemv") -> torch.Tensor:
-    """A zero-filled device scratch buffer of at least nbytes, reused across calls on one stream.
-    One buffer per (device, purpose): tq_gemv keeps completion counters at the start of its
-    workspace (zero between calls), so it must not share a buffer with tq_moe_ffn."""
+    """A device scratch buffer of at least nbytes, reused across calls on one stream. The
+    library takes workspaces with any contents; one buffer per (device, purpose) keeps calls
+    that the caller runs on different streams from sharing one."""
     dev = torch.device(device if device is not None else "cuda")
     if dev.index is None:
         dev = torch.device(dev.type, torch.cuda.current_device())

@@ -2,6 +2,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+#include <chrono>
 #include <vector>
 
 #include "tq.h"
@@ -32,6 +34,23 @@ int launched(int rc, const char *what) {
 }
 
 }  // namespace
+
+namespace tq {
+
+unsigned long long call_tag() {
+  // splitmix64 of the load time and an address: where the token sequence starts
+  static std::atomic<unsigned long long> next{[] {
+    unsigned long long z = (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() ^
+                           (unsigned long long)(uintptr_t)&g_err;
+    z += 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+  }()};
+  return (next.fetch_add(1, std::memory_order_relaxed) & 0xFFFFFFFFFFFFull) << 16;
+}
+
+}  // namespace tq
 
 extern "C" {
 

@@ -120,8 +120,9 @@ int launch_dequant(int fmt, const void *w, int64_t n, int64_t k, int out_type, v
 // ksplit > 1 each workgroup stores its partial sums to the workspace; the last workgroup of a row
 // group to arrive (counted with a device-scope atomic) adds the slices in slice order. Which
 // workgroup does the adding does not change the order of the additions, so the result is
-// deterministic. The counters live in the first kCounterBytes of the workspace, apart from the
-// partial sums; they start at zero and every call leaves them at zero.
+// deterministic. The counters (Arrivals: tagged with the launch's token, so the workspace may hold
+// anything beforehand) live in the first kCounterBytes of the workspace, apart from the partial
+// sums.
 
 struct GemvPlan {
   int rowgroups, ksplit, upk, waves, upw;
@@ -144,7 +145,7 @@ GemvPlan plan_gemv(int64_t n, int64_t k, bool split_allowed) {
   return p;
 }
 
-static constexpr size_t kCounterBytes = 65536;  // one counter per row group: n <= 1M rows
+static constexpr size_t kCounterBytes = 65536;  // one 8-byte counter per row group
 
 // Workspace of the int8 matrix-core path: counters, then the k slices' partial sums.
 static size_t i8_ws_bytes(int fmt, int64_t rows, int64_t k, int64_t batch) {
@@ -176,7 +177,7 @@ static bool use_f32m(int fmt, int64_t rows, int64_t k, const float *x, int64_t b
 static int launch_f32m(int fmt, const KlMap &m, int64_t k, const float *x, int64_t batch,
                        void *ws, hipStream_t s) {
   return launch_gemm_f32m(fmt, m, k, x, batch, ws ? (float *)((char *)ws + kCounterBytes) : nullptr,
-                          (unsigned *)ws, (int)(kCounterBytes / 4), s);
+                          (unsigned long long *)ws, (int)(kCounterBytes / 8), s);
 }
 
 // The streaming int8 path needs no workspace, only a 16-byte aligned x.
@@ -185,8 +186,8 @@ static bool use_i8s(int fmt, int64_t rows, int64_t k, const float *x, int64_t ba
 }
 
 static int launch_i8(const KlMap &m, int64_t k, const float *x, void *ws, hipStream_t s) {
-  return launch_gemv_i8(m, k, x, (float *)((char *)ws + kCounterBytes), (unsigned *)ws,
-                        (int)(kCounterBytes / 4), s);
+  return launch_gemv_i8(m, k, x, (float *)((char *)ws + kCounterBytes), (unsigned long long *)ws,
+                        (int)(kCounterBytes / 8), s);
 }
 
 // Workspace of the fp16 matrix-core path for 2..32 tokens: counters, split x, slice sums.
@@ -205,7 +206,7 @@ static bool use_qmm(int fmt, int64_t rows, int64_t k, const float *x, int64_t ba
 static size_t split_workspace_bytes(int fmt, int64_t n, int64_t k) {
   if (!gemv_fast_shape(fmt, k)) return 0;
   const GemvPlan p = plan_gemv(n, k, true);
-  if (p.ksplit == 1 || (size_t)p.rowgroups * 4 > kCounterBytes) return 0;
+  if (p.ksplit == 1 || (size_t)p.rowgroups * 8 > kCounterBytes) return 0;
   // counters, then partial sums for up to 8 tokens
   return kCounterBytes + (size_t)p.rowgroups * p.ksplit * 8 * 64 * 4;
 }
@@ -237,8 +238,7 @@ __global__ __launch_bounds__(512) void k_gemv(const uint8_t *__restrict__ w, int
                                               int n, int units, int ksplit, int upk, int upw,
                                               const float *__restrict__ x, int64_t ldx,
                                               float *__restrict__ y, int64_t ldy,
-                                              float *__restrict__ partial,
-                                              unsigned *__restrict__ counters) {
+                                              float *__restrict__ partial, Arrivals arr) {
   extern __shared__ float lds[];
   __shared__ int is_last;
   const int rg = blockIdx.x / ksplit, ks = blockIdx.x - rg * ksplit;
@@ -256,18 +256,16 @@ __global__ __launch_bounds__(512) void k_gemv(const uint8_t *__restrict__ w, int
     return;
   }
   // k split: store this slice's sums; the last workgroup of the row group to finish adds all
-  // slices in slice order and resets the row group's counter for the next call. The partial sums
-  // are written and read with device-coherent (sc1) accesses, and every store has completed
-  // (s_waitcnt vmcnt(0)) before the workgroup's arrival is counted, so the last workgroup sees all
-  // of them; no cache writeback or invalidation is needed.
+  // slices in slice order. The partial sums are written and read with device-coherent (sc1)
+  // accesses, and every store has completed (s_waitcnt vmcnt(0)) before the workgroup's arrival
+  // is counted, so the last workgroup sees all of them; no cache writeback or invalidation is
+  // needed.
   float *mine = partial + ((int64_t)rg * ksplit + ks) * NT * 64;
   for (int i = threadIdx.x; i < NT * 64; i += blockDim.x)
     __hip_atomic_store(mine + i, lds[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores have completed
   __syncthreads();
-  if (threadIdx.x == 0)
-    is_last = __hip_atomic_fetch_add(&counters[rg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              (unsigned)(ksplit - 1);
+  if (threadIdx.x == 0) is_last = arrive_last(arr, rg, (unsigned)ksplit);
   __syncthreads();
   if (!is_last) return;
   const float *base = partial + (int64_t)rg * ksplit * NT * 64;
@@ -287,8 +285,6 @@ __global__ __launch_bounds__(512) void k_gemv(const uint8_t *__restrict__ w, int
     }
     if (row0 + l < n) y[t * ldy + row0 + l] = s;
   }
-  if (threadIdx.x == 0)
-    __hip_atomic_store(&counters[rg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Batch-1 Q4_K GEMV, lanes along k (see tq_gemv_core.h). A lane group of 64 / G lanes covers all
@@ -533,10 +529,10 @@ __global__ __launch_bounds__(256) void k_gemv_generic(int fmt, const uint8_t *__
 template <int FMT, int NT>
 static void launch_gemv_nt(const uint8_t *w, int64_t rb, int n, int units, const GemvPlan &p,
                            const float *x, int64_t ldx, float *y, int64_t ldy, float *partial,
-                           unsigned *counters, size_t lds, hipStream_t s) {
+                           unsigned long long *counters, size_t lds, hipStream_t s) {
   hipLaunchKernelGGL((k_gemv<FMT, NT>), dim3((unsigned)(p.rowgroups * p.ksplit)), dim3(64 * p.waves),
                      lds, s, w, rb, n, units, p.ksplit, p.upk, p.upw, x, ldx, y, ldy, partial,
-                     counters);
+                     Arrivals{counters, counters ? call_tag() : 0ull});
 }
 
 template <int FMT>
@@ -546,7 +542,7 @@ static int launch_gemv_fmt(const uint8_t *w, int64_t rb, int n, int64_t k, const
   const size_t need = split_workspace_bytes(FMT, n, k);
   const bool split = ws != nullptr && need > 0 && ws_bytes >= need;
   const GemvPlan p = plan_gemv(n, k, split);
-  unsigned *counters = p.ksplit > 1 ? static_cast<unsigned *>(ws) : nullptr;
+  unsigned long long *counters = p.ksplit > 1 ? static_cast<unsigned long long *>(ws) : nullptr;
   float *partial =
       p.ksplit > 1 ? reinterpret_cast<float *>(static_cast<char *>(ws) + kCounterBytes) : nullptr;
   const int max_floats = 65536 / 4;
@@ -666,8 +662,8 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, in
     const void *wp[1] = {w};
     float *yp[1] = {y};
     const QmmDense m = dense_map(1, wp, &n, yp, rb);
-    return launch_qmm_dense(m, k, x, batch, (char *)ws + kCounterBytes, (unsigned *)ws,
-                            (int)(kCounterBytes / 4), s);
+    return launch_qmm_dense(m, k, x, batch, (char *)ws + kCounterBytes,
+                            (unsigned long long *)ws, (int)(kCounterBytes / 8), s);
   }
   if (use_f32m(fmt, n, k, x, batch, ws, ws_bytes)) {
     KlMap m{};
@@ -723,8 +719,8 @@ int launch_gemv_multi(int fmt, int nparts, const void *const *w, const int64_t *
   for (int p = 0; p < nparts; ++p) total += n[p];
   if (nparts <= 4 && use_qmm(fmt, total, k, x, batch, ws, ws_bytes, false)) {
     const QmmDense m = dense_map(nparts, w, n, y, k / fmt_block_weights(fmt) * fmt_block_bytes(fmt));
-    return launch_qmm_dense(m, k, x, batch, (char *)ws + kCounterBytes, (unsigned *)ws,
-                            (int)(kCounterBytes / 4), s);
+    return launch_qmm_dense(m, k, x, batch, (char *)ws + kCounterBytes,
+                            (unsigned long long *)ws, (int)(kCounterBytes / 8), s);
   }
   const bool f32m = use_f32m(fmt, total, k, x, batch, ws, ws_bytes);
   const bool i8s = !f32m && use_i8s(fmt, total, k, x, batch);
@@ -814,8 +810,8 @@ int launch_gemv_swiglu(int fmt, const void *wg, const void *wu, int64_t n, int64
     m.nparts = 1;
     m.swiglu = 1;
     m.row_bytes = rb;
-    return launch_qmm_dense(m, k, x, batch, (char *)ws + kCounterBytes, (unsigned *)ws,
-                            (int)(kCounterBytes / 4), s);
+    return launch_qmm_dense(m, k, x, batch, (char *)ws + kCounterBytes,
+                            (unsigned long long *)ws, (int)(kCounterBytes / 8), s);
   }
   // two launches through the workspace: its head is the split GEMV's, then gate and up
   const size_t gws = (size_t)align_up((int64_t)split_workspace_bytes(fmt, n, k), 256);

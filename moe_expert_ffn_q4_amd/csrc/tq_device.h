@@ -76,4 +76,39 @@ __device__ __forceinline__ int wave_index() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
 
+// Completion counters of the k-sliced products: the workgroup that finishes a row group's last k
+// slice adds the slices' partial sums. A counter word is (tag | arrivals): the tag is the call's
+// token shifted past 16 count bits, and the token differs for every call the process makes
+// (call_tag() on the host), so a word that another call left, or whatever bytes a fresh
+// workspace holds, never passes for this call's. Nothing has to be cleared before or after.
+struct Arrivals {
+  unsigned long long *ctr;  // one 8-byte word per row group
+  unsigned long long tag;   // token << 16
+};
+constexpr unsigned long long kArrivalCountMask = 0xFFFFull;
+
+// Counts the calling workgroup on row group g and returns true for the one that brings the count
+// to `parts` (< 65536). One thread calls it, after the workgroup's partial sums have completed at
+// agent scope. A workgroup whose add lands on another call's word turns it into this call's word
+// with a count of one, or, when another workgroup of this call has done that in the meantime,
+// counts itself again on that word (its add on the old word is dropped with the old word).
+__device__ inline bool arrive_last(const Arrivals &a, int g, unsigned parts) {
+  unsigned long long *p = a.ctr + g;
+  unsigned long long w =
+      __hip_atomic_fetch_add(p, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((w & ~kArrivalCountMask) != a.tag) {
+    w += 1ull;  // what the word holds if nobody else touched it
+    for (;;) {
+      if (__hip_atomic_compare_exchange_strong(p, &w, a.tag | 1ull, __ATOMIC_RELAXED,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+        return parts == 1u;
+      if ((w & ~kArrivalCountMask) == a.tag) {  // claimed by another workgroup of this call
+        w = __hip_atomic_fetch_add(p, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  return (unsigned)(w & kArrivalCountMask) + 1u == parts;
+}
+
 }  // namespace tq

@@ -15,8 +15,9 @@ bool f32m_ok(int fmt, int64_t k, int64_t batch);
 // Partial sums of the k slices after the counters (0 when k is one slice).
 size_t f32m_workspace_bytes(int64_t rows, int64_t k);
 // The rows of m (y[p] is [batch][n_p]; SwiGLU: y[0] = h [batch][total / 2]) against x
-// [batch][k] (16-byte aligned). counters: zero, one per row group, left zero.
+// [batch][k] (16-byte aligned). counters: one 8-byte word per row group (Arrivals), any contents.
 int launch_gemm_f32m(int fmt, const KlMap &m, int64_t k, const float *x, int64_t batch,
-                     float *partial, unsigned *counters, int max_counters, hipStream_t s);
+                     float *partial, unsigned long long *counters, int max_counters,
+                     hipStream_t s);
 
 }  // namespace tq

@@ -203,8 +203,7 @@ constexpr int kF32mXRow = 260;  // LDS floats per token row of a block (+4: rows
 template <int FMT>
 __device__ __forceinline__ void f32m_body(const KlMap &m, const float *__restrict__ x, int B,
                                           int kblocks, int ksplit, int upk,
-                                          float *__restrict__ partial,
-                                          unsigned *__restrict__ counters,
+                                          float *__restrict__ partial, const Arrivals &arr,
                                           float (*xsh)[16 * kF32mXRow], int *is_last_p) {
   int &is_last = *is_last_p;
   constexpr int RT = kF32mRT;
@@ -291,9 +290,7 @@ __device__ __forceinline__ void f32m_body(const KlMap &m, const float *__restric
                          __HIP_MEMORY_SCOPE_AGENT);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the partial sums are stored before counting
   __syncthreads();
-  if (threadIdx.x == 0)
-    is_last = __hip_atomic_fetch_add(&counters[grp], 1u, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(ksplit - 1);
+  if (threadIdx.x == 0) is_last = arrive_last(arr, grp, (unsigned)ksplit);
   __syncthreads();
   if (!is_last) return;
   const float *base = partial + (int64_t)grp * ksplit * tiles * 256;
@@ -307,27 +304,25 @@ __device__ __forceinline__ void f32m_body(const KlMap &m, const float *__restric
                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     f32m_store(m, B, rbase + 16 * r, t, g, s);
   }
-  if (threadIdx.x == 0)
-    __hip_atomic_store(&counters[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Q8_0 fits three waves per SIMD (the compiler then reaches four); Q6_K keeps two (at three its
 // two register sets of raw runs spill).
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_gemm_f32m_q8(
     KlMap m, const float *__restrict__ x, int B, int kblocks, int ksplit, int upk,
-    float *__restrict__ partial, unsigned *__restrict__ counters) {
+    float *__restrict__ partial, Arrivals arr) {
   __shared__ __attribute__((aligned(16))) float xsh[2][16 * kF32mXRow];
   __shared__ int is_last;
-  f32m_body<FMT_Q8_0>(m, x, B, kblocks, ksplit, upk, partial, counters, xsh, &is_last);
+  f32m_body<FMT_Q8_0>(m, x, B, kblocks, ksplit, upk, partial, arr, xsh, &is_last);
 }
 
 __global__ __launch_bounds__(256) void k_gemm_f32m_q6(KlMap m, const float *__restrict__ x, int B,
                                                       int kblocks, int ksplit, int upk,
                                                       float *__restrict__ partial,
-                                                      unsigned *__restrict__ counters) {
+                                                      Arrivals arr) {
   __shared__ __attribute__((aligned(16))) float xsh[2][16 * kF32mXRow];
   __shared__ int is_last;
-  f32m_body<FMT_Q6_K>(m, x, B, kblocks, ksplit, upk, partial, counters, xsh, &is_last);
+  f32m_body<FMT_Q6_K>(m, x, B, kblocks, ksplit, upk, partial, arr, xsh, &is_last);
 }
 
 // ---- host side ----------------------------------------------------------------------------------
@@ -361,18 +356,20 @@ size_t f32m_workspace_bytes(int64_t rows, int64_t k) {
 }
 
 int launch_gemm_f32m(int fmt, const KlMap &m, int64_t k, const float *x, int64_t batch,
-                     float *partial, unsigned *counters, int max_counters, hipStream_t s) {
+                     float *partial, unsigned long long *counters, int max_counters,
+                     hipStream_t s) {
   const int nblk = (int)(k / 256), upk = f32m_upk(k), ksplit = (nblk + upk - 1) / upk;
   if (ksplit > kF32mMaxSlices) return -2;
   const int64_t groups = f32m_groups(m.total);
   if (ksplit > 1 && groups > max_counters) return -2;
   const dim3 grid((unsigned)(groups * ksplit));
+  const Arrivals arr{counters, ksplit > 1 ? call_tag() : 0ull};
   if (fmt == FMT_Q6_K)
     hipLaunchKernelGGL(k_gemm_f32m_q6, grid, dim3(256), 0, s, m, x, (int)batch, nblk, ksplit, upk,
-                       partial, counters);
+                       partial, arr);
   else
     hipLaunchKernelGGL(k_gemm_f32m_q8, grid, dim3(256), 0, s, m, x, (int)batch, nblk, ksplit, upk,
-                       partial, counters);
+                       partial, arr);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -152,9 +152,9 @@ bool i8_gemv_ok(int fmt, int64_t k, int64_t batch);
 // is one slice).
 size_t i8_workspace_bytes(int64_t rows, int64_t k);
 // The rows of m against x [k] (16-byte aligned). partial: i8_workspace_bytes(m.total, k) bytes;
-// counters: zero, one per row group (max_counters of them), left zero.
+// counters: one 8-byte word per row group (Arrivals; max_counters of them), any contents.
 int launch_gemv_i8(const KlMap &m, int64_t k, const float *x, float *partial,
-                   unsigned *counters, int max_counters, hipStream_t s);
+                   unsigned long long *counters, int max_counters, hipStream_t s);
 
 // Streaming form (no workspace; opt-in with TQ_GEMV_I8S=1): Q4_K, one token, k a multiple of 256
 // up to 16384; all of x is made

@@ -38,7 +38,7 @@ __device__ __forceinline__ void i8_store(const KlMap &m, int v, float s) { *m.ou
 
 __global__ __launch_bounds__(256) void k_gemv_i8(KlMap m, const float *__restrict__ x, int nblk,
                                                  int upk, int ksplit, float *__restrict__ partial,
-                                                 unsigned *__restrict__ counters) {
+                                                 Arrivals arr) {
   __shared__ __attribute__((aligned(16))) uint8_t xl[kMaxSliceBlocks * kLdsBlock];
   __shared__ float red[4][32];
   __shared__ int is_last;
@@ -98,16 +98,14 @@ __global__ __launch_bounds__(256) void k_gemv_i8(KlMap m, const float *__restric
     return;
   }
   // k slices: this slice's sums (device-coherent stores, completed before the arrival is
-  // counted); the last workgroup of the row group adds them in slice order, resets the counter
+  // counted); the last workgroup of the row group adds them in slice order
   const int rows = 32 * W;
   float *mine = partial + ((int64_t)grp * ksplit + ks) * rows;
   if (h == 0)
     __hip_atomic_store(mine + 32 * w + n, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
-  if (threadIdx.x == 0)
-    is_last = __hip_atomic_fetch_add(&counters[grp], 1u, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(ksplit - 1);
+  if (threadIdx.x == 0) is_last = arrive_last(arr, grp, (unsigned)ksplit);
   __syncthreads();
   if (!is_last) return;
   const float *base = partial + (int64_t)grp * ksplit * rows;
@@ -134,8 +132,6 @@ __global__ __launch_bounds__(256) void k_gemv_i8(KlMap m, const float *__restric
       i8_store(m, v, s);
     }
   }
-  if (threadIdx.x == 0)
-    __hip_atomic_store(&counters[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Streaming form for k up to 16384 (no cross-workgroup reduction): a workgroup of NW waves turns
@@ -255,14 +251,14 @@ size_t i8_workspace_bytes(int64_t rows, int64_t k) {
 }
 
 int launch_gemv_i8(const KlMap &m, int64_t k, const float *x, float *partial,
-                   unsigned *counters, int max_counters, hipStream_t s) {
+                   unsigned long long *counters, int max_counters, hipStream_t s) {
   const int nblk = (int)(k / 256), upk = i8_upk(k), ksplit = (nblk + upk - 1) / upk;
   if (upk > kMaxSliceBlocks || ksplit > kMaxSlices) return -2;
   const int W = i8_tiles_per_wg(m.total, ksplit);
   const int groups = (m.total + 32 * W - 1) / (32 * W);
   if (ksplit > 1 && groups > max_counters) return -2;
   hipLaunchKernelGGL(k_gemv_i8, dim3((unsigned)(groups * ksplit)), dim3(64 * W), 0, s, m, x, nblk,
-                     upk, ksplit, partial, counters);
+                     upk, ksplit, partial, Arrivals{counters, ksplit > 1 ? call_tag() : 0ull});
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -12,6 +12,10 @@ inline int env_int(const char *name, int dflt) {
   const char *v = getenv(name);
   return v && *v ? atoi(v) : dflt;
 }
+// Tag of one call's completion counters (Arrivals::tag): a 48-bit token, distinct for every call
+// of the process (a counter starting from a value drawn at load time), shifted past 16 count bits.
+unsigned long long call_tag();
+
 inline int clampi(int v, int lo, int hi) { return v < lo ? lo : v > hi ? hi : v; }
 inline int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
 inline int64_t fmt_block_weights(int fmt) { return fmt == 1 ? 256 : fmt == 2 ? 256 : fmt == 3 ? 32 : 0; }

@@ -70,8 +70,8 @@ bool qmm_dense_ok(int fmt, int64_t k, int64_t batch);
 size_t qmm_dense_bytes(int64_t rows, int64_t k, int64_t batch, bool swiglu);
 // The k dimension is cut into slices of a fixed number of blocks (a function of k only, so every
 // row is summed in the same order whatever the launch); the last workgroup of a row tile to finish
-// adds the slices in order. counters: one per row tile, zero before and after the call.
+// adds the slices in order. counters: one 8-byte word per row tile (Arrivals), any contents.
 int launch_qmm_dense(const QmmDense &m, int64_t k, const float *x, int64_t batch, char *ws,
-                     unsigned *counters, int max_counters, hipStream_t st);
+                     unsigned long long *counters, int max_counters, hipStream_t st);
 
 }  // namespace tq

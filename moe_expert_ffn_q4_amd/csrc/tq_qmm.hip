@@ -491,7 +491,7 @@ struct DenseEpi {
   const SplitRows *x;
   int B, tile, ks, ksplit;
   float *partial;
-  unsigned *counters;
+  Arrivals arr;
   int *is_last;  // LDS
 
   // a final value of row rt of the (non-SwiGLU) tile for token tok
@@ -545,9 +545,7 @@ struct DenseEpi {
       }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    if (threadIdx.x == 0)
-      *is_last = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(ksplit - 1);
+    if (threadIdx.x == 0) *is_last = arrive_last(arr, tile, (unsigned)ksplit);
     __syncthreads();
     if (!*is_last) return;
     const float *base = partial + (int64_t)tile * ksplit * B * 128;
@@ -578,15 +576,13 @@ struct DenseEpi {
         store(tok, rt, s0);
       }
     }
-    if (threadIdx.x == 0)
-      __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 };
 
 template <bool GU, int NTMAX>
 __global__ __launch_bounds__(256) void k_qmm_dense(QmmDense m, SplitRows x, int B, int kblocks,
                                                    int ksplit, int upk, float *partial,
-                                                   unsigned *counters) {
+                                                   Arrivals arr) {
   __shared__ __attribute__((aligned(16))) uint8_t xbuf[2 * 16 * NTMAX * kXBlockBytes];
   __shared__ int rowidx[16 * NTMAX];
   __shared__ int is_last;
@@ -607,7 +603,7 @@ __global__ __launch_bounds__(256) void k_qmm_dense(QmmDense m, SplitRows x, int 
                 (int64_t)kb0 * 144;
   }
   __syncthreads();  // rowidx
-  const DenseEpi<GU> epi{&m, &x, B, tile, ks, ksplit, partial, counters, &is_last};
+  const DenseEpi<GU> epi{&m, &x, B, tile, ks, ksplit, partial, arr, &is_last};
   if (NTMAX == 1 || B <= 16)
     qmm_tiles<GU, 1, NTMAX>(x, xbuf, rowidx, B, kblocks, wrow, kb0, steps, epi);
   else
@@ -722,7 +718,7 @@ size_t qmm_dense_bytes(int64_t rows, int64_t k, int64_t batch, bool swiglu) {
 }
 
 int launch_qmm_dense(const QmmDense &m, int64_t k, const float *x, int64_t batch, char *ws,
-                     unsigned *counters, int max_counters, hipStream_t st) {
+                     unsigned long long *counters, int max_counters, hipStream_t st) {
   const int64_t rows = m.swiglu ? m.cum[1] : m.cum[m.nparts];
   const int nblk = (int)(k / 256), upk = dense_upk(k), ksplit = (nblk + upk - 1) / upk;
   const int64_t tiles = dense_tiles(rows, m.swiglu != 0);
@@ -732,16 +728,17 @@ int launch_qmm_dense(const QmmDense &m, int64_t k, const float *x, int64_t batch
   launch_split_rows(x, k, batch, k, xr, st);
   const dim3 grid((unsigned)(tiles * ksplit));
   const int B = (int)batch;
+  const Arrivals counters_arr{counters, ksplit > 1 ? call_tag() : 0ull};
   if (m.swiglu) {
     if (B <= 16)
-      hipLaunchKernelGGL((k_qmm_dense<true, 1>), grid, dim3(256), 0, st, m, xr, B, nblk, ksplit, upk, partial, counters);
+      hipLaunchKernelGGL((k_qmm_dense<true, 1>), grid, dim3(256), 0, st, m, xr, B, nblk, ksplit, upk, partial, counters_arr);
     else
-      hipLaunchKernelGGL((k_qmm_dense<true, 2>), grid, dim3(256), 0, st, m, xr, B, nblk, ksplit, upk, partial, counters);
+      hipLaunchKernelGGL((k_qmm_dense<true, 2>), grid, dim3(256), 0, st, m, xr, B, nblk, ksplit, upk, partial, counters_arr);
   } else {
     if (B <= 16)
-      hipLaunchKernelGGL((k_qmm_dense<false, 1>), grid, dim3(256), 0, st, m, xr, B, nblk, ksplit, upk, partial, counters);
+      hipLaunchKernelGGL((k_qmm_dense<false, 1>), grid, dim3(256), 0, st, m, xr, B, nblk, ksplit, upk, partial, counters_arr);
     else
-      hipLaunchKernelGGL((k_qmm_dense<false, 2>), grid, dim3(256), 0, st, m, xr, B, nblk, ksplit, upk, partial, counters);
+      hipLaunchKernelGGL((k_qmm_dense<false, 2>), grid, dim3(256), 0, st, m, xr, B, nblk, ksplit, upk, partial, counters_arr);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -87,8 +87,7 @@ def test_gemv_integer_lattice_bitwise(t, n, k, batch):
 @pytest.mark.parametrize("t,n,k", [("q4_k", 200, 4096), ("q6_k", 130, 3072), ("q8_0", 70, 2048)])
 @pytest.mark.parametrize("batch", [1, 7])
 def test_gemv_without_workspace(t, n, k, batch):
-    """No workspace: every row group in one workgroup; and an explicit workspace, whose
-    completion counters the split path must leave at zero."""
+    """No workspace: every row group in one workgroup; and an explicit workspace."""
     _print_case("no-ws", t, n, k, batch)
     g = synth.rng(107, "nows", t, n, k, batch)
     w = synth.blob(t, g, n, k)
@@ -101,7 +100,34 @@ def test_gemv_without_workspace(t, n, k, batch):
     ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device="cuda:0")
     y1 = host(tq.gemv(t, wd, n, k, xd, ws=ws))
     assert_product_close(y1, ref, mag, what="own workspace")
-    assert int(host(ws[:65536]).view(np.uint32).max()) == 0, "completion counters not reset"
+
+
+@pytest.mark.parametrize("t,n,k,batch", [("q4_k", 300, 16384, 1), ("q4_k", 200, 4096, 8),
+                                         ("q8_0", 200, 8192, 4), ("q6_k", 300, 4096, 1),
+                                         ("q6_k", 100, 8192, 3)])
+def test_gemv_workspace_any_contents(t, n, k, batch):
+    """The k-split paths (int8 matrix cores, fp16 and fp32 matrix cores, the lane-per-row split)
+    take a workspace with any contents: all-ones bytes, random bytes, or what a call of another
+    shape left give bitwise the result of a zeroed workspace, call after call."""
+    _print_case("ws-contents", t, n, k, batch)
+    g = synth.rng(108, "wsany", t, n, k, batch)
+    w = synth.blob(t, g, n, k)
+    x = synth.normal_f32(g, (batch, k))
+    wd, xd = dev(w), dev(x)
+    nbytes = max(tq.gemv_workspace_bytes(t, n, k, batch), 256)
+    assert nbytes > 65536, "shape must take a k-split path"
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda:0")
+    ref = host(tq.gemv(t, wd, n, k, xd, ws=ws))
+    oref, mag = oracle.gemv(t, w, n, k, x)
+    assert_product_close(ref, oref, mag, what="zeroed workspace")
+    ws.fill_(255)
+    assert np.array_equal(host(tq.gemv(t, wd, n, k, xd, ws=ws)), ref), "all-ones workspace"
+    ws.copy_(torch.from_numpy(g.integers(0, 256, nbytes, dtype=np.uint8)).to("cuda:0"))
+    for i in range(3):
+        assert np.array_equal(host(tq.gemv(t, wd, n, k, xd, ws=ws)), ref), f"random bytes, call {i}"
+    w2 = dev(synth.blob(t, g, 2 * n + 7, k))
+    tq.gemv(t, w2, 2 * n + 7, k, dev(synth.normal_f32(g, (batch, k))), ws=ws)
+    assert np.array_equal(host(tq.gemv(t, wd, n, k, xd, ws=ws)), ref), "after another shape"
 
 
 def test_gemv_unit_vector_picks_dequantized_column():
