@@ -97,6 +97,23 @@ int tq_gemv(int type, const void *w, int64_t n, int64_t k, const float *x, int64
             float *y, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * tq_gemv_noalloc -- tq_gemv for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc). Same arguments and result as
+ * tq_gemv given a workspace of tq_gemv_workspace_bytes(type, n, k, batch) bytes (bitwise), minus
+ * the workspace: it uses a scratch array that the library holds on each device (statically, in
+ * its code object, until the process ends). Allocates nothing, clears nothing (the scratch may
+ * hold anything, as tq_gemv's workspace may).
+ *   Returns TQ_ENOSPC when that workspace size exceeds TQ_GEMV_NOALLOC_MAX_BYTES (16 MiB: every
+ *   8B- and 70B-shaped projection up to batch 16), TQ_EDEVICE when the scratch's device address
+ *   cannot be found.
+ *   All calls on one device share its scratch: calls that can overlap on one device (other
+ *   streams, other threads) race and must be serialized by the caller.
+ */
+#define TQ_GEMV_NOALLOC_MAX_BYTES (16u << 20)
+int tq_gemv_noalloc(int type, const void *w, int64_t n, int64_t k, const float *x, int64_t batch,
+                    float *y, void *stream);
+
+/*
  * tq_gemv_multi -- y_p = W_p x for nparts (1..4) matrices of one block type and the same k that
  * share the activations x (the q, k and v projections of a decode step read the same x), in one
  * launch for Q4_K at batch 1..32 (given the workspace; at batch 1 also without) and for the

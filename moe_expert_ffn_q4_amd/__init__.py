@@ -84,6 +84,8 @@ def _declare(L: C.CDLL) -> None:
     L.tq_gemv_workspace_bytes.restype = C.c_size_t
     L.tq_gemv.argtypes = [_int, _vp, _i64, _i64, _vp, _i64, _vp, _vp, C.c_size_t, _vp]
     L.tq_gemv.restype = _int
+    L.tq_gemv_noalloc.argtypes = [_int, _vp, _i64, _i64, _vp, _i64, _vp, _vp]
+    L.tq_gemv_noalloc.restype = _int
     L.tq_swiglu.argtypes = [_vp, _vp, _i64, _vp, _vp]
     L.tq_swiglu.restype = _int
     L.tq_gemv_multi_workspace_bytes.argtypes = [_int, _int, C.POINTER(_i64), _i64, _i64]
@@ -182,6 +184,19 @@ def gemv(t, w: torch.Tensor, n: int, k: int, x: torch.Tensor, out=None, ws=None,
     wsp, wsn = (None, 0) if ws is False else (ws.data_ptr(), ws.numel() * ws.element_size())
     _check(lib().tq_gemv(_type(t), _ptr(w), n, k, _ptr(x2), batch, _ptr(out), wsp, wsn,
                          _stream(stream)))
+    return out
+
+
+GEMV_NOALLOC_MAX_BYTES = 16 << 20  # TQ_GEMV_NOALLOC_MAX_BYTES
+
+
+def gemv_noalloc(t, w: torch.Tensor, n: int, k: int, x: torch.Tensor, out: torch.Tensor,
+                 stream=None):
+    """tq_gemv_noalloc: y = W x into the preallocated out [batch, n], with the library's own
+    per-device scratch instead of a workspace (nothing is allocated)."""
+    x2 = x.reshape(-1, k)
+    _check(lib().tq_gemv_noalloc(_type(t), _ptr(w), n, k, _ptr(x2), x2.shape[0], _ptr(out),
+                                 _stream(stream)))
     return out
 
 

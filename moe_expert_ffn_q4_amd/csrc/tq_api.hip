@@ -4,6 +4,7 @@
 
 #include <atomic>
 #include <chrono>
+#include <mutex>
 #include <vector>
 
 #include "tq.h"
@@ -99,6 +100,63 @@ int tq_gemv(int type, const void *w, int64_t n, int64_t k, const float *x, int64
                            "workspace 256-byte aligned");
   return launched(tq::launch_gemv(type, w, n, k, x, batch, y, workspace, ws_bytes, (hipStream_t)stream),
                   "tq_gemv");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of tq_gemv_noalloc. Each GPU the library runs on holds its own copy until the process
+// ends; in host code this name is only a stand-in, so every host use goes through the device
+// address that noalloc_scratch() looked up for the current device.
+static __device__ __align__(256) unsigned char scratch[TQ_GEMV_NOALLOC_MAX_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// The current device's address of `scratch`, looked up once per device.
+int noalloc_scratch(void **out) {
+  static std::mutex mu;
+  static void *addr[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(TQ_EDEVICE, "tq_gemv_noalloc: no current HIP device (or more than %d)", kMaxDevices);
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(TQ_EDEVICE, "tq_gemv_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tq_gemv_noalloc(int type, const void *w, int64_t n, int64_t k, const float *x, int64_t batch,
+                    float *y, void *stream) {
+  if (!known_type(type)) return fail(TQ_EINVAL, "tq_gemv_noalloc: unknown block type %d", type);
+  if (!w || !x || !y) return fail(TQ_EINVAL, "tq_gemv_noalloc: null pointer");
+  const int64_t bw = tq::fmt_block_weights(type);
+  if (n < 1 || n > (1 << 30) || k < bw || k % bw || k > (1 << 24) || batch < 1 || batch > 4096)
+    return fail(TQ_ESHAPE, "tq_gemv_noalloc: n=%lld k=%lld batch=%lld out of range",
+                (long long)n, (long long)k, (long long)batch);
+  if (!aligned(w, 16) || !aligned(x, 4) || !aligned(y, 4))
+    return fail(TQ_EALIGN, "tq_gemv_noalloc: w must be 16-byte aligned, x and y 4-byte aligned");
+  const size_t need = tq::gemv_workspace_bytes(type, n, k, batch);
+  if (need > TQ_GEMV_NOALLOC_MAX_BYTES)
+    return fail(TQ_ENOSPC, "tq_gemv_noalloc: n=%lld k=%lld batch=%lld needs %zu bytes of scratch, "
+                "more than the %u this entry point has", (long long)n, (long long)k,
+                (long long)batch, need, (unsigned)TQ_GEMV_NOALLOC_MAX_BYTES);
+  void *ws = nullptr;
+  if (need > 0) {
+    const int rc = noalloc_scratch(&ws);
+    if (rc != TQ_OK) return rc;
+  }
+  return tq_gemv(type, w, n, k, x, batch, y, ws, need, stream);
 }
 
 size_t tq_gemv_multi_workspace_bytes(int type, int nparts, const int64_t *n, int64_t k,

@@ -56,6 +56,30 @@ def test_gemv_rejects(args, code):
     assert L.tq_last_error()
 
 
+@pytest.mark.parametrize("args,code", [
+    ((7, 16, 4, 256, 16, 1, 16), 1),          # unknown type
+    ((1, 16, 4, 256, 16, 1, 0), 1),           # null y
+    ((1, 16, 4, 100, 16, 1, 16), 2),          # k not a block multiple
+    ((1, 16, 4, 256, 16, 5000, 16), 2),       # batch too large
+    ((1, 8, 4, 256, 16, 1, 16), 3),           # w not 16-byte aligned
+    ((1, 16, 4, 256, 16, 1, 18), 3),          # y not 4-byte aligned
+    ((1, 16, 128256, 4096, 16, 32, 16), 4),   # its workspace would exceed the scratch
+])
+def test_gemv_noalloc_rejects(args, code):
+    L = tq.lib()
+    t, w, n, k, x, b, y = args
+    assert L.tq_gemv_noalloc(t, w or None, n, k, x or None, b, y or None, None) == code
+    assert L.tq_last_error()
+    if code == 4:
+        assert L.tq_gemv_workspace_bytes(t, n, k, b) > tq.GEMV_NOALLOC_MAX_BYTES
+
+
+def test_gemv_noalloc_max_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define TQ_GEMV_NOALLOC_MAX_BYTES \((\d+)u << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == tq.GEMV_NOALLOC_MAX_BYTES
+
+
 def test_gemv_rejects_misaligned_workspace():
     L = tq.lib()
     assert L.tq_gemv(1, 16, 4, 256, 16, 1, 16, 128, 4096, None) == 3
