@@ -72,6 +72,8 @@ def _declare(L: C.CDLL) -> None:
     L.orc_moe.restype = C.c_int
     L.orc_moe_bf16.argtypes = L.orc_moe.argtypes
     L.orc_moe_bf16.restype = C.c_int
+    L.orc_moe_grouped.argtypes = L.orc_moe.argtypes
+    L.orc_moe_grouped.restype = C.c_int
     L.orc_requant.argtypes = [C.c_int, _p, _p, _i64, _i64, _p]
     L.orc_requant.restype = C.c_int
     L.orc_quantize.argtypes = [C.c_int, _p, _i64, _i64, _p]
@@ -244,11 +246,14 @@ class _Expert(C.Structure):
 
 
 def moe(t, hidden: int, ffn: int, experts, shared, x: np.ndarray, ids: np.ndarray,
-        weights: np.ndarray, tokens=None, bf16: bool = False):
+        weights: np.ndarray, tokens=None, bf16: bool = False, grouped: bool = True):
     """(y, mag) of the MoE FFN for a given routing, fp64 [n_tok][hidden].
 
     experts: list of (gate, up, down) uint8 blobs; shared: one such tuple or None.
     bf16: x, the weights and h rounded to bf16 first (orc_moe_bf16).
+    grouped (fp32 operands only): orc_moe_grouped, the same bits as orc_moe (token by token)
+    with the tokens of one expert taken together, which is what makes whole large layers
+    affordable.
     """
     t = _type(t)
     keep = []
@@ -269,7 +274,7 @@ def moe(t, hidden: int, ffn: int, experts, shared, x: np.ndarray, ids: np.ndarra
     nt = T if tok is None else tok.size
     y = np.empty((nt, hidden), np.float64)
     mag = np.empty((nt, hidden), np.float64)
-    fn = lib().orc_moe_bf16 if bf16 else lib().orc_moe
+    fn = lib().orc_moe_bf16 if bf16 else lib().orc_moe_grouped if grouped else lib().orc_moe
     rc = fn(t, hidden, ffn, arr, len(experts), sh, _ptr(x), T, k, _ptr(ids),
                        _ptr(weights), _ptr(tok), 0 if tok is None else nt, _ptr(y), _ptr(mag))
     _check(rc, "moe")

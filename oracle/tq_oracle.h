@@ -111,6 +111,13 @@ int orc_moe(int type, int64_t hidden, int64_t ffn, const orc_expert *experts, in
             const orc_expert *shared, const float *x, int64_t T, int64_t k, const int32_t *ids,
             const double *weights, const int64_t *tokens, int64_t n_tok, double *y, double *mag);
 
+/* orc_moe's result, bitwise, with the work grouped by expert (each expert's rows decoded once for
+ * all the tokens routed to it; every output from the same expressions in the same order). */
+int orc_moe_grouped(int type, int64_t hidden, int64_t ffn, const orc_expert *experts,
+                    int64_t n_experts, const orc_expert *shared, const float *x, int64_t T,
+                    int64_t k, const int32_t *ids, const double *weights, const int64_t *tokens,
+                    int64_t n_tok, double *y, double *mag);
+
 /* The same MoE output with bf16 operands, the arithmetic of the matrix-core path: x, every
  * weight (the bf16 rounding of its fp32 value) and h = swiglu(g, u) (rounded to fp32, then to
  * bf16) are rounded to nearest even; products and sums stay fp64; mag from the rounded operands.

@@ -43,6 +43,21 @@ def test_golden_block(fx):
         assert oracle.lib().orc_block_weight(oracle.TYPES[t], fx["block"].ctypes.data, i) == exp[i]
 
 
+@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q8_0"])
+def test_row_decode_equals_per_weight_definition(t):
+    """Rows are decoded a block at a time; every value equals orc_block_weight's, bit for bit."""
+    n, k = 3, 1024
+    blob = synth.blob(t, synth.rng(41, "rowdec", t), n, k)
+    w64 = oracle.dequant(t, blob, n, k, out="f64")
+    bw, bb = synth.BLOCK_WEIGHTS[t], synth.BLOCK_BYTES[t]
+    L, tt = oracle.lib(), oracle.TYPES[t]
+    rows = blob.reshape(n, -1)
+    for r in range(n):
+        for c in range(k):
+            blk = np.ascontiguousarray(rows[r, (c // bw) * bb:(c // bw + 1) * bb])
+            assert L.orc_block_weight(tt, blk.ctypes.data, c % bw) == w64[r, c], (r, c)
+
+
 def test_q4k_fields_of_scale_fixture():
     fx = {f["name"]: f for f in load_blocks()}["q4k_scales_q15"]
     fl = oracle.block_fields("q4_k", fx["block"])

@@ -207,6 +207,29 @@ def test_moe_against_dense_numpy(t):
     np.testing.assert_allclose(y[1] - yn[1], o, rtol=1e-9, atol=1e-9)
 
 
+@pytest.mark.parametrize("t,shape,k,T", [
+    ("q4_k", dict(hidden=256, ffn=512, n_experts=5, shared=True), 2, 7),
+    ("q6_k", dict(hidden=512, ffn=256, n_experts=3, shared=False), 3, 4),
+    ("q8_0", dict(hidden=256, ffn=256, n_experts=8, shared=True), 4, 9),
+])
+def test_moe_grouped_equals_token_by_token(t, shape, k, T):
+    """The expert-grouped MoE gives the token-by-token MoE's bits: all tokens, a token subset in
+    any order (with repeats), and empty experts."""
+    layer = synth.moe_layer(shape, t, seed=33, tag=f"grouped-{t}")
+    H, F = shape["hidden"], shape["ffn"]
+    x = synth.normal_f32(synth.rng(33, "x", t), (T, H))
+    ids, wts = oracle.topk(oracle.router_logits(x, layer["router"]).astype(np.float32), k)
+    for toks in (None, [T - 1, 0, 2, 0]):
+        yg, mg = oracle.moe(t, H, F, layer["experts"], layer["shared"], x, ids, wts, tokens=toks)
+        yt, mt = oracle.moe(t, H, F, layer["experts"], layer["shared"], x, ids, wts, tokens=toks,
+                            grouped=False)
+        assert np.array_equal(yg, yt) and np.array_equal(mg, mt)
+    ids0 = np.zeros_like(ids) + np.arange(k, dtype=np.int32)  # experts k.. stay empty
+    yg, _ = oracle.moe(t, H, F, layer["experts"], layer["shared"], x, ids0, wts)
+    yt, _ = oracle.moe(t, H, F, layer["experts"], layer["shared"], x, ids0, wts, grouped=False)
+    assert np.array_equal(yg, yt)
+
+
 def test_moe_relabelling_experts_leaves_output_unchanged():
     H, F, E, k, T = 256, 256, 4, 2, 4
     layer = synth.moe_layer(dict(hidden=H, ffn=F, n_experts=E), "q4_k", seed=32, tag="perm")
