@@ -48,7 +48,8 @@ unsigned long long call_tag() {
     z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
     return z ^ (z >> 31);
   }()};
-  return (next.fetch_add(1, std::memory_order_relaxed) & 0xFFFFFFFFFFFFull) << 16;
+  // 47 bits of the sequence plus a set top bit: never zero, the value a finished launch leaves
+  return ((next.fetch_add(1, std::memory_order_relaxed) & 0x7FFFFFFFFFFFull) | 0x800000000000ull) << 16;
 }
 
 }  // namespace tq

@@ -256,7 +256,7 @@ __global__ __launch_bounds__(512) void k_gemv(const uint8_t *__restrict__ w, int
     return;
   }
   // k split: store this slice's sums; the last workgroup of the row group to finish adds all
-  // slices in slice order. The partial sums are written and read with device-coherent (sc1)
+  // slices in slice order and zeroes the row group's counter. The partial sums are written and read with device-coherent (sc1)
   // accesses, and every store has completed (s_waitcnt vmcnt(0)) before the workgroup's arrival
   // is counted, so the last workgroup sees all of them; no cache writeback or invalidation is
   // needed.
@@ -285,6 +285,7 @@ __global__ __launch_bounds__(512) void k_gemv(const uint8_t *__restrict__ w, int
     }
     if (row0 + l < n) y[t * ldy + row0 + l] = s;
   }
+  if (threadIdx.x == 0) done_arrivals(arr, rg);
 }
 
 // Batch-1 Q4_K GEMV, lanes along k (see tq_gemv_core.h). A lane group of 64 / G lanes covers all

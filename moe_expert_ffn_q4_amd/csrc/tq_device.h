@@ -77,10 +77,12 @@ __device__ __forceinline__ int wave_index() {
 }
 
 // Completion counters of the k-sliced products: the workgroup that finishes a row group's last k
-// slice adds the slices' partial sums. A counter word is (tag | arrivals): the tag is the call's
-// token shifted past 16 count bits, and the token differs for every call the process makes
-// (call_tag() on the host), so a word that another call left, or whatever bytes a fresh
-// workspace holds, never passes for this call's. Nothing has to be cleared before or after.
+// slice adds the slices' partial sums. A counter word is (tag | arrivals): the tag is the launch's
+// token (never zero) shifted past 16 count bits, and the token differs for every launch the host
+// makes (call_tag()), so whatever bytes a fresh workspace holds never pass for this launch's
+// word. The last workgroup sets its word back to zero (done_arrivals), because a launch recorded
+// in a HIP graph keeps its token on every replay: each replay then starts from zero, which no
+// token matches. Nothing has to be cleared by the caller.
 struct Arrivals {
   unsigned long long *ctr;  // one 8-byte word per row group
   unsigned long long tag;   // token << 16
@@ -109,6 +111,11 @@ __device__ inline bool arrive_last(const Arrivals &a, int g, unsigned parts) {
     }
   }
   return (unsigned)(w & kArrivalCountMask) + 1u == parts;
+}
+
+// The last workgroup of row group g, once done: the word back to zero for the next launch.
+__device__ inline void done_arrivals(const Arrivals &a, int g) {
+  __hip_atomic_store(a.ctr + g, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace tq

@@ -304,6 +304,7 @@ __device__ __forceinline__ void f32m_body(const KlMap &m, const float *__restric
                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     f32m_store(m, B, rbase + 16 * r, t, g, s);
   }
+  if (threadIdx.x == 0) done_arrivals(arr, grp);
 }
 
 // Q8_0 fits three waves per SIMD (the compiler then reaches four); Q6_K keeps two (at three its

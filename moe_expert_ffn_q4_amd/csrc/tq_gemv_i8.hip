@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void k_gemv_i8(KlMap m, const float *__restric
     return;
   }
   // k slices: this slice's sums (device-coherent stores, completed before the arrival is
-  // counted); the last workgroup of the row group adds them in slice order
+  // counted); the last workgroup of the row group adds them in slice order, zeroes the counter
   const int rows = 32 * W;
   float *mine = partial + ((int64_t)grp * ksplit + ks) * rows;
   if (h == 0)
@@ -132,6 +132,7 @@ __global__ __launch_bounds__(256) void k_gemv_i8(KlMap m, const float *__restric
       i8_store(m, v, s);
     }
   }
+  if (threadIdx.x == 0) done_arrivals(arr, grp);
 }
 
 // Streaming form for k up to 16384 (no cross-workgroup reduction): a workgroup of NW waves turns

@@ -12,8 +12,9 @@ inline int env_int(const char *name, int dflt) {
   const char *v = getenv(name);
   return v && *v ? atoi(v) : dflt;
 }
-// Tag of one call's completion counters (Arrivals::tag): a 48-bit token, distinct for every call
-// of the process (a counter starting from a value drawn at load time), shifted past 16 count bits.
+// Tag of one launch's completion counters (Arrivals::tag): a 48-bit token, never zero and distinct
+// for every launch of the process (a counter starting from a value drawn at load time), shifted
+// past 16 count bits.
 unsigned long long call_tag();
 
 inline int clampi(int v, int lo, int hi) { return v < lo ? lo : v > hi ? hi : v; }

@@ -576,6 +576,7 @@ struct DenseEpi {
         store(tok, rt, s0);
       }
     }
+    if (threadIdx.x == 0) done_arrivals(arr, tile);
   }
 };
 

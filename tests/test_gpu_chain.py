@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import synth
-from tests.gpu_util import assert_product_close, dev, host
+from tests.gpu_util import assert_product_close, assert_swiglu_close, dev, host
 
 pytestmark = [
     pytest.mark.gpu,
@@ -35,19 +35,6 @@ def _nan(n):
 
 def _blob(tag, n, k):
     return synth.blob("q4_k", synth.rng(61, "chain", tag, n, k), n, k)
-
-
-def assert_swiglu_close(h, g, mg, u, mu, what=""):
-    """h = silu(g) u with g, u each within the product bar of the oracle's (g, mg, u, mu):
-    |dh| <= |silu'| eg |u| + |silu(g)| eu + 1.1 eg eu with |silu'| <= 1.1, plus the SwiGLU bar on
-    identical inputs (1e-5 |h| + 1e-5) for the fp32 evaluation itself."""
-    eg, eu = 1e-3 * mg + 1e-5, 1e-3 * mu + 1e-5
-    ref = oracle.swiglu(g, u)
-    silu = g / (1.0 + np.exp(-np.clip(g, -700, 700)))
-    bound = 1.1 * eg * np.abs(u) + np.abs(silu) * eu + 1.1 * eg * eu + 1e-5 * np.abs(ref) + 1e-5
-    err = np.abs(np.asarray(h, np.float64) - ref)
-    bad = err > bound
-    assert not bad.any(), f"{what}: {int(bad.sum())} of {err.size} outside the SwiGLU bound"
 
 
 def _check_chain(ops, blobs):

@@ -1,13 +1,16 @@
 """Host-resident routed experts (pinned host memory, copied per call) against the device-resident
-layer: same routing, bitwise-identical output, on the fp32 and the matrix-core paths, with and
-without a separate copy stream."""
+layer and the oracle: the same routing and bitwise the same output as the device-resident layer,
+and the output within the product bar of the oracle (the bf16-operand oracle on the matrix-core
+path), on the fp32 and the matrix-core paths, with and without a separate copy stream. Each layer
+is called again with other activations, which route to other experts, so the staging area is
+reused with different contents."""
 import numpy as np
 import pytest
 import torch
 
 import synth
 from tests.gpu_util import dev, host
-from tests.test_gpu_moe import _run
+from tests.test_gpu_moe import _run, check_moe
 
 pytestmark = pytest.mark.gpu
 
@@ -43,27 +46,30 @@ def test_host_resident_matches_device_resident(t, shape, k, Ts, path, side_strea
     layer = synth.moe_layer(shape, t, seed=401, tag="host")
     cs = torch.cuda.Stream() if side_stream else None
     on_dev, on_host = _layers(t, shape, layer, k, path, cs)
+    bf16 = path == tq.PATH_BF16_MFMA
     for T in Ts:
-        _case("host-resident", t, shape, k, T, path, side_stream)
-        x = synth.normal_f32(synth.rng(401, "x", T), (T, shape["hidden"]))
-        yd, rd = _run(on_dev, x, shape["n_experts"], k)
-        yh, rh = _run(on_host, x, shape["n_experts"], k)
-        for f in rd:
-            assert np.array_equal(rd[f], rh[f]), f
-        assert np.array_equal(yd, yh)
-        # a second call reuses the staging area: still identical
-        yh2, _ = _run(on_host, x, shape["n_experts"], k)
-        assert np.array_equal(yh2, yd)
+        for rep in range(2):
+            _case("host-resident", t, shape, k, T, path, side_stream, rep)
+            x = synth.normal_f32(synth.rng(401, "x", T, rep), (T, shape["hidden"]))
+            yd, rd = _run(on_dev, x, shape["n_experts"], k)
+            yh, rh = _run(on_host, x, shape["n_experts"], k)
+            for f in rd:
+                assert np.array_equal(rd[f], rh[f]), f
+            assert np.array_equal(yd, yh)
+            check_moe(t, shape, layer, x, k, moe=on_host, bf16=bf16,
+                      rel=1e-3 + 2.0**-8 if bf16 else 1e-3)
 
 
 def test_host_resident_deepseek_shape_one_token():
     _case("host-resident deepseek", 1)
     layer = synth.moe_layer(synth.DEEPSEEK, "q4_k", tag="deepseek")
     on_dev, on_host = _layers("q4_k", synth.DEEPSEEK, layer, 8, tq.PATH_AUTO, torch.cuda.Stream())
-    x = synth.normal_f32(synth.rng(synth.DEFAULT_SEED, "deepseek-x", 1), (1, 7168))
-    yd, _ = _run(on_dev, x, 256, 8)
-    yh, _ = _run(on_host, x, 256, 8)
-    assert np.array_equal(yd, yh)
+    for rep in range(2):
+        x = synth.normal_f32(synth.rng(synth.DEFAULT_SEED, "deepseek-x", 1, rep), (1, 7168))
+        yd, _ = _run(on_dev, x, 256, 8)
+        yh, _ = _run(on_host, x, 256, 8)
+        assert np.array_equal(yd, yh)
+        check_moe("q4_k", synth.DEEPSEEK, layer, x, 8, moe=on_host)
 
 
 def test_host_resident_rejects_unpinned_blobs():

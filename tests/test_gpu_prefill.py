@@ -9,9 +9,11 @@ the oracle with the GPU's routing, element by element:
     values -- one bf16 ulp of a term is at most 2^-8 of its magnitude. On top of that at most
     one element in 1000 may exceed 1e-3 * sum|products| + 1e-5, and the relative L2 error must
     stay below 2e-5;
-  * the exact fp64 MoE at the DeepSeek-shaped 4096-token prefill: within 2e-2 * sum|products|
-    + 1e-5. On the small shapes the bf16 roundings of x and of the weights alone move a few
-    elements further than that (the fp64 comparison is printed there, not asserted).
+  * the exact fp64 MoE: at the DeepSeek-shaped 4096-token prefill (67 tokens spread over the
+    whole batch, so over every expert's chunks) within 2e-2 * sum|products| + 1e-5 per element;
+    on the small shapes, where a gate or up sum that cancels can turn the bf16 roundings of x
+    and of the weights into a larger relative change of h, the relative L2 error of y within
+    2e-2 (the per-element figure is printed).
 """
 import numpy as np
 import pytest
@@ -56,7 +58,8 @@ def _check_vs_bf16_oracle(moe, shape, layer, x, k, tokens=None):
 
 
 def _report_fp64(shape, layer, x, k, y, moe, tokens=None):
-    """Largest |err| / mag and relative L2 against the exact fp64 oracle (printed)."""
+    """Relative L2 error against the exact fp64 oracle within 2e-2; the largest |err| / mag
+    is printed."""
     E = shape["n_experts"]
     _, r = _run(moe, x, E, k)
     ids, wts = oracle.topk(r["logits"], k, True)
@@ -64,8 +67,10 @@ def _report_fp64(shape, layer, x, k, y, moe, tokens=None):
     ref, mag = oracle.moe("q4_k", shape["hidden"], shape["ffn"], layer["experts"],
                           layer["shared"], x, ids, wts, tokens=toks)
     e = np.abs(y[toks] - ref)
-    print(f"  vs fp64 oracle: max err/mag {np.max(e / (mag + 1e-30)):.2e}, rel L2 "
-          f"{np.linalg.norm(y[toks] - ref) / np.linalg.norm(ref):.2e}", flush=True)
+    l2 = float(np.linalg.norm(y[toks] - ref) / np.linalg.norm(ref))
+    print(f"  vs fp64 oracle: max err/mag {np.max(e / (mag + 1e-30)):.2e}, rel L2 {l2:.2e}",
+          flush=True)
+    assert l2 <= REL, f"relative L2 {l2:.2e} against the fp64 oracle"
 
 
 def _case(*a):
@@ -162,14 +167,20 @@ def deepseek():
 
 
 def test_prefill_deepseek_4096_sampled_tokens(deepseek):
+    """Routing of all 4096 tokens bitwise; y of 67 tokens spread over the batch (the first two,
+    64 evenly spaced, the last: about 540 routed pairs over the experts' chunks) against the fp64
+    oracle per element; 8 of them against the bf16-operand oracle."""
     T = 4096
     _case("deepseek prefill", T)
     x = synth.normal_f32(synth.rng(synth.DEFAULT_SEED, "deepseek-x", T), (T, 7168))
-    toks = [0, 1, 2048, 4095]
+    toks = sorted(set([0, 1] + list(range(31, T, 64)) + [T - 1]))
+    assert len(toks) >= 64
     moe, y, (worst, l2) = check_moe("q4_k", synth.DEEPSEEK, deepseek, x, 8, tokens=toks, rel=REL,
                                     path=tq.PATH_BF16_MFMA)
-    print(f"  vs fp64 oracle: worst err/bound {worst:.3f}, rel L2 {l2:.2e}", flush=True)
-    # the same tokens against the bf16-operand oracle
+    print(f"  vs fp64 oracle ({len(toks)} tokens): worst err/bound {worst:.3f}, rel L2 {l2:.2e}",
+          flush=True)
+    # some of them against the bf16-operand oracle
+    toks = toks[::9]
     _, r = _run(moe, x, 256, 8)
     ids, wts = oracle.topk(r["logits"], 8, True)
     ref, mag = oracle.moe("q4_k", 7168, 2048, deepseek["experts"], deepseek["shared"], x, ids,
