@@ -29,19 +29,22 @@ BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of the MI355X
 GEMV_SOURCES = ("moe_expert_ffn_q4_amd/csrc/tq_dense.hip", "moe_expert_ffn_q4_amd/csrc/tq_gemv_core.h",
                 "moe_expert_ffn_q4_amd/csrc/tq_device.h")
 GEMV_COUNTERS = "profiles/k_gemv_kl_llama8b_b1_hbm_counters.txt"
+C1_COUNTERS = "profiles/k_gemv_kl_c1_4096x4096_hbm_counters.txt"
 METRIC = "Q4_K GEMV HBM GB/s (% of peak); decode tokens/s for 8B-shaped and MoE layers"
 
 
 def _args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--batch", type=int, default=1, help="tokens per decode step (1 or 8)")
     p.add_argument("--workload", default="llama8b",
-                   choices=["llama8b", "llama70b", "mixtral", "deepseek", "deepseek-prefill",
+                   choices=["llama8b", "c1", "llama70b", "mixtral", "deepseek", "deepseek-prefill",
                             "deepseek-host"],
-                   help="llama8b: 32-layer dense decode step (default); mixtral / deepseek: one "
+                   help="llama8b: 32-layer dense decode step (default); c1: one 4096x4096 Q4_K "
+                        "GEMV at batch 1 over 64 distinct weight copies, next to a plain read of "
+                        "the same bytes; mixtral / deepseek: one "
                         "MoE layer at --batch tokens; deepseek-prefill: one DeepSeek-shaped MoE "
                         "layer over --tokens (default 4096) on the bf16 matrix-core path; "
                         "deepseek-host: the DeepSeek decode layer at --batch tokens with the routed "
@@ -62,7 +65,8 @@ def _args():
     p.add_argument("--summarize", nargs=3, metavar=("KERNEL_STATS", "FETCH_CSV", "WRITE_CSV"),
                    help="no GPU: print a text summary of a rocprofv3 kernel-stats CSV and two "
                         "counter-collection CSVs (FETCH_SIZE, WRITE_SIZE) of the llama8b batch-1 "
-                        "step, with per-launch HBM traffic of the Q4_K GEMV")
+                        "step (or of --workload c1), with per-launch HBM traffic of the Q4_K "
+                        "GEMV")
     return p.parse_args()
 
 
@@ -74,6 +78,79 @@ def source_hash(paths=GEMV_SOURCES):
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def timed_replays(torch, graph, stream, steps):
+    """The timed region: `steps` replays of `graph` back to back on `stream`, bracketed by device
+    synchronizations, with a HIP event recorded on that stream before each replay and after the
+    last. Returns (wall-clock seconds of the region, per-replay milliseconds from the events)."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i].record(stream)
+        graph.replay()
+    evs[steps].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+
+
+def trial_stats(ms, per=1):
+    """Median and 10th / 90th percentiles of per-replay times (divided by `per` launches)."""
+    import numpy as np
+
+    a = np.asarray(ms, np.float64) / per
+    return {"trials": int(a.size), "median_ms": round(float(np.median(a)), 5),
+            "p10_ms": round(float(np.percentile(a, 10)), 5),
+            "p90_ms": round(float(np.percentile(a, 90)), 5)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+def oracle_repeat(fn, budget_s, max_reps):
+    """Calls fn() until about budget_s of wall time or max_reps calls; (calls, seconds)."""
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        elapsed = time.perf_counter() - t0
+        if elapsed >= budget_s or reps >= max_reps:
+            return reps, elapsed
+
+
+def single_thread(fn, budget_s, max_reps):
+    """oracle_repeat with the oracle's loops on one thread (the default restored after)."""
+    import oracle
+
+    n = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        return oracle_repeat(fn, budget_s, max_reps)
+    finally:
+        oracle.set_num_threads(n)
+
+
+def check_against(got, ref, mag):
+    """Every element of a GPU result against the oracle's: the worst |err| / (1e-3 mag + 1e-5)."""
+    import numpy as np
+
+    err = np.abs(np.asarray(got, np.float64) - ref)
+    worst = float(np.max(err / (1e-3 * mag + 1e-5))) if err.size else 0.0
+    return {"elements": int(err.size), "max_err_over_bound": float(f"{worst:.3g}"),
+            "pass": bool(worst <= 1.0)}
 
 
 def llama8b_bytes_per_launch(synth, batch=1):
@@ -89,9 +166,10 @@ def llama8b_bytes_per_launch(synth, batch=1):
     return tot / len(launches)
 
 
-def summarize(kt_csv, fetch_csv, write_csv):
-    """Text summary of the profiler's CSVs for the GEMV of the llama8b batch-1 step. FETCH_SIZE
-    and WRITE_SIZE are scaled by what they read for the 1 GiB copy (--calibrate-copy)."""
+def summarize(kt_csv, fetch_csv, write_csv, workload="llama8b"):
+    """Text summary of the profiler's CSVs for the GEMV of the llama8b batch-1 step (or of the
+    c1 workload). FETCH_SIZE and WRITE_SIZE are scaled by what they read for the 1 GiB copy
+    (--calibrate-copy)."""
     import csv
     from collections import defaultdict
 
@@ -137,7 +215,7 @@ def summarize(kt_csv, fetch_csv, write_csv):
         tot_n += len(fv)
         lines.append(f"{key[0][:40]:<40s} {key[1]:8d} {key[2]:4d} {len(fv):6d} {fk:11.1f} "
                      f"{wk:10.1f} {b:22.0f}")
-    algo = llama8b_bytes_per_launch(synth)
+    algo = C1_BYTES_PER_LAUNCH if workload == "c1" else llama8b_bytes_per_launch(synth)
     traffic = tot_bytes / tot_n
     lines.append("")
     lines.append(f"algorithmic_bytes_per_launch: {algo:.0f}")
@@ -171,10 +249,10 @@ def kernel_summary(stats_csv, *counter_csvs):
     return "\n".join(lines)
 
 
-def recorded_traffic():
-    """HBM bytes per GEMV launch from the committed counter summary, or None when the kernel's
+def recorded_traffic(summary=GEMV_COUNTERS):
+    """HBM bytes per GEMV launch from a committed counter summary, or None when the kernel's
     sources have changed since the counters were taken (or there is no summary)."""
-    path = os.path.join(ROOT, GEMV_COUNTERS)
+    path = os.path.join(ROOT, summary)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -274,10 +352,11 @@ def make_step(tq, torch, layers, batch, events=None, gemv_only=False):
     return step
 
 
-def cpu_baseline(synth, batch, seed, budget_s):
+def cpu_baseline(synth, batch, seed, budget_s, tq, torch):
     """The oracle (as it is) on a bounded sample of the same step: whole layers (layer 0's seven
-    Q4_K projections at the bench's batch), repeated until about budget_s of CPU time has been
-    spent, scaled to a 32-layer step."""
+    Q4_K projections at the bench's batch), on all the host's threads until about budget_s,
+    then on one thread for about a third of that, each scaled to a 32-layer step. The outputs of
+    the all-core run are checked element by element against the GPU's for the same inputs."""
     import oracle
 
     shape = synth.LLAMA8B
@@ -286,43 +365,111 @@ def cpu_baseline(synth, batch, seed, budget_s):
         w = synth.blob("q4_k", synth.rng(seed, "8b", 0, name), n, k)
         x = synth.normal_f32(synth.rng(seed, "cpu-x", name, batch), (batch, k))
         projs.append((w, n, k, x))
-    layers = 0
-    t0 = time.perf_counter()
-    while True:
-        for w, n, k, x in projs:
-            oracle.gemv("q4_k", w, n, k, x)
-        layers += 1
-        elapsed = time.perf_counter() - t0
-        if elapsed >= budget_s or layers >= 4 * shape["layers"]:
-            break
+    refs = []
+
+    def layer():
+        refs[:] = [oracle.gemv("q4_k", w, n, k, x) for w, n, k, x in projs]
+
+    layers, elapsed = oracle_repeat(layer, budget_s, 100 * shape["layers"])
+    cores = oracle.num_threads()
+    # the same products on the GPU, every element against the oracle's
+    checks = []
+    for (w, n, k, x), (ref, mag) in zip(projs, refs):
+        y = tq.gemv("q4_k", torch.from_numpy(w).cuda(), n, k, torch.from_numpy(x).cuda())
+        checks.append(check_against(y.cpu().numpy(), ref, mag))
+    one = lambda: [oracle.gemv("q4_k", w, n, k, x) for w, n, k, x in projs[:4]]
+    reps1, el1 = single_thread(one, budget_s / 3, 10000)
+    frac4 = sum(w.size for w, *_ in projs[:4]) / sum(w.size for w, *_ in projs)
+    step1 = el1 / reps1 / frac4 * shape["layers"]
     step_s = elapsed / layers * shape["layers"]
-    return {"value": batch / step_s, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+    return {"value": round(batch / step_s, 4), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{layers} full layers (7 Q4_K projections each, batch {batch}) in "
-                      f"{elapsed:.1f} s, scaled to a 32-layer step"}
+                      f"{elapsed:.1f} s on {cores} threads, scaled to a 32-layer step",
+            "single_thread": {"value": round(batch / step1, 5), "unit": "tokens/s",
+                              "sample": f"{reps1} x (q, k, v, o) in {el1:.1f} s on 1 thread, "
+                                        f"scaled by blob bytes to a 32-layer step"},
+            "checked_vs_gpu": {"elements": sum(c["elements"] for c in checks),
+                               "max_err_over_bound": max(c["max_err_over_bound"] for c in checks),
+                               "pass": all(c["pass"] for c in checks),
+                               "what": "layer 0's 7 projections, every output element, the "
+                                       "all-core oracle's result against tq_gemv's"}}
 
 
-def moe_cpu_baseline(synth, shape, layer, x, budget_s):
-    """The oracle (as it is) on a bounded sample of the same layer: routing of the sampled tokens
-    and their MoE output, one token at a time until about budget_s of CPU time."""
+def c1_cpu_baseline(w, x, y_gpu, n, k, budget_s):
+    """The oracle on the same 4096x4096 GEMV: all threads, then one thread; GB/s of blob bytes
+    processed. The all-core result is checked element by element against the GPU's."""
+    import oracle
+
+    out = {}
+
+    def gemv():
+        out["ref"] = oracle.gemv("q4_k", w, n, k, x)
+
+    reps, el = oracle_repeat(gemv, budget_s, 100000)
+    cores = oracle.num_threads()
+    ref, mag = out["ref"]
+    reps1, el1 = single_thread(lambda: oracle.gemv("q4_k", w, n, k, x), budget_s / 3, 10000)
+    return {"value": round(w.size * reps / el / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"{reps} GEMVs of the same 4096x4096 Q4_K blob in {el:.1f} s on {cores} "
+                      f"threads",
+            "single_thread": {"value": round(w.size * reps1 / el1 / 1e9, 5), "unit": "GB/s",
+                              "sample": f"{reps1} GEMVs in {el1:.1f} s on 1 thread"},
+            "checked_vs_gpu": dict(check_against(y_gpu, ref, mag),
+                                   what="every output row of the GEMV")}
+
+
+def moe_cpu_baseline(synth, shape, layer, x, y_gpu, ids_gpu, budget_s):
+    """The oracle (as it is) on a bounded sample of the same layer: routing of the tokens and
+    their MoE output, on all the host's threads one token at a time until about budget_s, then
+    on one thread for about a third of that. The all-core outputs are checked element by
+    element against the GPU's y for the tokens whose oracle routing picked the same experts."""
+    import numpy as np
+
     import oracle
 
     k = shape["top_k"]
-    done = 0
-    t0 = time.perf_counter()
-    while True:
-        xt = x[done:done + 1]
+    H, F = shape["hidden"], shape["ffn"]
+    res = []
+
+    def token():
+        xt = x[len(res):len(res) + 1]
         ids, wts = oracle.topk(oracle.router_logits(xt, layer["router"]), k)
-        oracle.moe("q4_k", shape["hidden"], shape["ffn"], layer["experts"], layer["shared"], xt,
-                   ids, wts)
-        done += 1
-        elapsed = time.perf_counter() - t0
-        if elapsed >= budget_s or done >= x.shape[0]:
-            break
-    return {"value": done / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{done} tokens of the same layer (routing + fp64 MoE output) in "
-                      f"{elapsed:.1f} s"}
+        y, mag = oracle.moe("q4_k", H, F, layer["experts"], layer["shared"], xt, ids, wts,
+                            grouped=False)
+        res.append((ids, y, mag))
+
+    done, elapsed = oracle_repeat(token, budget_s, x.shape[0])
+    cores = oracle.num_threads()
+    checks, skipped = [], 0
+    for t, (ids, y, mag) in enumerate(res):
+        if np.array_equal(np.sort(ids[0]), np.sort(ids_gpu[t])):
+            checks.append(check_against(y_gpu[t:t + 1], y, mag))
+        else:  # a near tie the two evaluations of the logits resolved differently
+            skipped += 1
+    checks = checks or [{"elements": 0, "max_err_over_bound": 0.0, "pass": False}]
+    n1 = [0]
+
+    def token1():
+        xt = x[n1[0] % x.shape[0]:n1[0] % x.shape[0] + 1]
+        ids, wts = oracle.topk(oracle.router_logits(xt, layer["router"]), k)
+        oracle.moe("q4_k", H, F, layer["experts"], layer["shared"], xt, ids, wts, grouped=False)
+        n1[0] += 1
+
+    done1, el1 = single_thread(token1, budget_s / 3, x.shape[0])
+    return {"value": round(done / elapsed, 4), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"{done} tokens of the same layer (routing + fp64 MoE output, one token at "
+                      f"a time) in {elapsed:.1f} s on {cores} threads",
+            "single_thread": {"value": round(done1 / el1, 5), "unit": "tokens/s",
+                              "sample": f"{done1} tokens in {el1:.1f} s on 1 thread"},
+            "checked_vs_gpu": {"elements": sum(c["elements"] for c in checks),
+                               "max_err_over_bound": max(c["max_err_over_bound"] for c in checks),
+                               "pass": all(c["pass"] for c in checks),
+                               "tokens_skipped_on_near_ties": skipped,
+                               "what": f"y of the {done} sampled tokens, every element, the "
+                                       f"all-core oracle's (its own routing) against the GPU's"}}
 
 
 def moe_bench(args, torch, tq, synth):
@@ -352,21 +499,17 @@ def moe_bench(args, torch, tq, synth):
     ws = torch.empty(moe.workspace_bytes(T), dtype=torch.uint8, device="cuda")
     E = shape["n_experts"]
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    ids_gpu = torch.empty((T, k), dtype=torch.int32, device="cuda")
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
-        moe(x, out=y, ws=ws, routing=dict(counts=counts))
+        moe(x, out=y, ws=ws, routing=dict(counts=counts, topk_ids=ids_gpu))
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
             moe(x, out=y, ws=ws)
         for _ in range(args.warmup):
             graph.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
+        elapsed, per_step = timed_replays(torch, graph, stream, args.steps)
         # the expert-product stage alone (routing already in the workspace)
         egraph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(egraph, stream=stream):
@@ -419,10 +562,111 @@ def moe_bench(args, torch, tq, synth):
                    "global_batch": T, "seq_len": T if prefill else 1,
                    "parallelism": "none (1 GPU)"},
         "active_experts": active,
+        "step_ms": trial_stats(per_step),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = moe_cpu_baseline(synth, shape, layer, xh, args.cpu_seconds)
+        out["cpu_baseline"] = moe_cpu_baseline(synth, shape, layer, xh, y.cpu().numpy(),
+                                               ids_gpu.cpu().numpy(), args.cpu_seconds)
+    return out
+
+
+C1_COPIES = 64
+C1_BYTES_PER_LAUNCH = 4096 * 16 * 144 + 4 * (4096 + 4096)  # blob + fp32 x and y
+
+
+def c1_bench(args, torch, tq, synth):
+    """One 4096x4096 Q4_K GEMV at batch 1 (fp32 x ~ N(0,1), y = W x). The weights are copied into
+    64 distinct device buffers (604 MB, more than twice the 256 MB last-level cache), and one graph
+    holds 64 launches, launch i reading copy i, so every launch streams its weights from HBM.
+    A step is one replay of that graph; the launch time is the replay time over 64. The same 64
+    buffers are then read by a plain streaming-read kernel (libtq_readref.so) in a graph of 64
+    launches, which gives the read-only time of the same bytes in the same launch setting."""
+    import ctypes as C
+
+    import numpy as np
+
+    n = k = 4096
+    g = synth.rng(args.seed, "c1")
+    wh = synth.blob("q4_k", g, n, k)
+    xh = synth.normal_f32(g, (1, k))
+    copies = [torch.from_numpy(wh).cuda() for _ in range(C1_COPIES)]
+    x = torch.from_numpy(xh).cuda()
+    ys = [torch.empty((1, n), dtype=torch.float32, device="cuda") for _ in range(C1_COPIES)]
+    ws = torch.zeros(max(tq.gemv_workspace_bytes("q4_k", n, k, 1), 256), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.Stream()
+
+    def step():
+        for w, y in zip(copies, ys):
+            tq.gemv("q4_k", w, n, k, x, out=y, ws=ws)
+
+    with torch.cuda.stream(stream):
+        step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        wall, per = timed_replays(torch, graph, stream, args.steps)
+    y0 = ys[0].cpu().numpy()
+    assert all(np.array_equal(y0, y.cpu().numpy()) for y in ys[1:]), "copies disagree"
+    launches = args.steps * C1_COPIES
+    launch_s = wall / launches
+    kernel_s = sum(per) / 1000 / launches
+    algo = wh.size + 4 * (n + k)
+    assert algo == C1_BYTES_PER_LAUNCH
+    achieved = algo / kernel_s / 1e9
+
+    # the plain streaming read of the same 64 buffers
+    R = C.CDLL(os.path.join(ROOT, "moe_expert_ffn_q4_amd", "libtq_readref.so"))
+    R.tq_read_ref.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]
+    R.tq_read_ref.restype = C.c_int
+    R.tq_read_ref_sink_words.argtypes = [C.c_int64]
+    R.tq_read_ref_sink_words.restype = C.c_int64
+    sink = torch.empty(int(R.tq_read_ref_sink_words(wh.size)), dtype=torch.int32, device="cuda")
+
+    def read_step():
+        st = torch.cuda.current_stream().cuda_stream
+        for w in copies:
+            if R.tq_read_ref(w.data_ptr(), wh.size, sink.data_ptr(), st):
+                raise RuntimeError("tq_read_ref failed")
+
+    with torch.cuda.stream(stream):
+        read_step()
+        torch.cuda.synchronize()
+        rgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(rgraph, stream=stream):
+            read_step()
+        for _ in range(args.warmup):
+            rgraph.replay()
+        _, rper = timed_replays(torch, rgraph, stream, args.steps)
+    read_s = sum(rper) / 1000 / launches
+    out = {
+        "metric": METRIC, "value": round(algo / launch_s / 1e9, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1000 / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "q4_k weights, f32 activations and accumulation",
+        "data": "synthetic (seeded random Q4_K blocks, N(0,1) activations)",
+        "config": {"workload": "single Q4_K GEMV at batch 1, W 4096x4096, 64 distinct weight "
+                               "copies cycled (one launch per copy)", "global_batch": 1,
+                   "seq_len": 1, "parallelism": "none (1 GPU)"},
+        "launches_per_step": C1_COPIES,
+        "launch_us": trial_stats([m * 1000 for m in per], C1_COPIES),
+        "plain_read": {"launch_us": round(read_s * 1e6, 3),
+                       "achieved": round(wh.size / read_s / 1e9, 1), "unit": "GB/s",
+                       "gemv_over_read_time": round(kernel_s / read_s, 3),
+                       "what": "tq_read_ref over the same 64 buffers, 64 launches per graph"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(C1_COUNTERS),
+                     "kernel": "tq_gemv Q4_K batch 1 (tq::k_gemv_kl)",
+                     "avg_launch_us": round(kernel_s * 1e6, 3)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = c1_cpu_baseline(wh, xh, y0, n, k, args.cpu_seconds)
     return out
 
 
@@ -486,16 +730,13 @@ def llama70b_bench(args, torch, tq, synth):
                     step()
                 for _ in range(args.warmup):
                     graph.replay()
-                torch.cuda.synchronize()
-                t0 = time.perf_counter()
-                for _ in range(args.steps):
-                    graph.replay()
-                torch.cuda.synchronize()
-                dt = (time.perf_counter() - t0) / args.steps
+                wall, per = timed_replays(torch, graph, stream, args.steps)
+                dt = wall / args.steps
             # algorithmic bytes: every blob once, plus fp32 activations in and out
             algo = blob_bytes + 4 * batch * sum(n + k for _, n, k in projs.values())
             act_bytes[f"{t} b{batch}"] = algo
             results[f"{t} b{batch}"] = {"ms_per_layer": round(dt * 1000, 4),
+                                        "layer_ms": trial_stats(per),
                                         "tokens_s_one_layer": round(batch / dt, 1),
                                         "blob_gbs": round(blob_bytes / dt / 1e9, 1),
                                         "hbm_frac": round(algo / dt / 1e9 / HBM_PEAK_GBS, 4)}
@@ -520,30 +761,47 @@ def llama70b_bench(args, torch, tq, synth):
                      "kernel": "Q4_K batch-1 layer (tq::k_gemv_kl; down on tq::k_gemv_i8)"},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = llama70b_cpu_baseline(host_q4k, args.cpu_seconds)
+        out["cpu_baseline"] = llama70b_cpu_baseline(host_q4k, args.cpu_seconds, tq, torch)
     return out
 
 
-def llama70b_cpu_baseline(projs, budget_s):
-    """The oracle (as it is) on the same Q4_K layer at batch 1, whole layers repeated until about
-    budget_s of CPU time has been spent."""
+def llama70b_cpu_baseline(projs, budget_s, tq, torch):
+    """The oracle (as it is) on the same Q4_K layer at batch 1: whole layers on all the host's
+    threads until about budget_s, then on one thread for about a third of that. The all-core
+    outputs are checked element by element against tq_gemv's for the same inputs."""
     import oracle
     import synth
 
     xs = {name: synth.normal_f32(synth.rng(7, "70b-cpu-x", name), (1, k))
           for name, (_, _, k) in projs.items()}
-    layers = 0
-    t0 = time.perf_counter()
-    while True:
+    refs = {}
+
+    def layer():
         for name, (w, n, k) in projs.items():
-            oracle.gemv("q4_k", w, n, k, xs[name])
-        layers += 1
-        elapsed = time.perf_counter() - t0
-        if elapsed >= budget_s or layers >= 50:
-            break
-    return {"value": layers / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{layers} full Q4_K layers (7 projections each, batch 1) in {elapsed:.1f} s"}
+            refs[name] = oracle.gemv("q4_k", w, n, k, xs[name])
+
+    layers, elapsed = oracle_repeat(layer, budget_s, 1000)
+    cores = oracle.num_threads()
+    checks = []
+    for name, (w, n, k) in projs.items():
+        y = tq.gemv("q4_k", torch.from_numpy(w).cuda(), n, k, torch.from_numpy(xs[name]).cuda())
+        checks.append(check_against(y.cpu().numpy(), *refs[name]))
+    w, n, k = projs["o"]
+    reps1, el1 = single_thread(lambda: oracle.gemv("q4_k", w, n, k, xs["o"]), budget_s / 3,
+                               10000)
+    frac = w.size / sum(p[0].size for p in projs.values())
+    return {"value": round(layers / elapsed, 4), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"{layers} full Q4_K layers (7 projections each, batch 1) in {elapsed:.1f} s "
+                      f"on {cores} threads",
+            "single_thread": {"value": round(frac / (el1 / reps1), 5), "unit": "tokens/s",
+                              "sample": f"{reps1} x the o projection in {el1:.1f} s on 1 thread, "
+                                        f"scaled by blob bytes to the layer"},
+            "checked_vs_gpu": {"elements": sum(c["elements"] for c in checks),
+                               "max_err_over_bound": max(c["max_err_over_bound"] for c in checks),
+                               "pass": all(c["pass"] for c in checks),
+                               "what": "the Q4_K layer's 7 projections at batch 1, every output "
+                                       "element, the all-core oracle's against tq_gemv's"}}
 
 
 def host_bench(args, torch, tq, synth):
@@ -620,7 +878,7 @@ def calibrate_copy(torch):
 def main():
     args = _args()
     if args.summarize:
-        print(summarize(*args.summarize))
+        print(summarize(*args.summarize, workload=args.workload))
         return
     if args.kernel_summary:
         print(kernel_summary(*args.kernel_summary))
@@ -635,7 +893,8 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
-    other = {"deepseek-host": host_bench, "llama70b": llama70b_bench}.get(args.workload)
+    other = {"deepseek-host": host_bench, "llama70b": llama70b_bench,
+             "c1": c1_bench}.get(args.workload)
     if other is None and args.workload != "llama8b":
         other = moe_bench
     if other is not None:
@@ -657,12 +916,7 @@ def main():
             step()
         for _ in range(args.warmup):
             graph.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
+        elapsed, per_step = timed_replays(torch, graph, stream, args.steps)
     ms_per_step = elapsed * 1000 / args.steps
     tokens_s = args.batch * args.steps / elapsed
 
@@ -678,16 +932,10 @@ def main():
         with torch.cuda.graph(ggraph, stream=stream):
             gstep()
         ggraph.replay()
-        reps = 5
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        for _ in range(reps):
-            ggraph.replay()
-        ev1.record(stream)
-        torch.cuda.synchronize()
+        _, gper = timed_replays(torch, ggraph, stream, max(5, args.steps // 4))
     launches = len(events) // 2  # the eager call and the captured one each appended
     kernel_bytes = sum(events[:launches])
-    avg_launch_s = ev0.elapsed_time(ev1) / 1000 / (reps * launches)
+    avg_launch_s = sum(gper) / 1000 / (len(gper) * launches)
     achieved = kernel_bytes / launches / avg_launch_s / 1e9
     step_bytes = kernel_bytes
     traffic = recorded_traffic() if args.batch == 1 else None
@@ -709,6 +957,7 @@ def main():
                                f"SwiGLU, batch {args.batch}",
                    "global_batch": args.batch, "seq_len": 1, "parallelism": "none (1 GPU)"},
         "step_gbs": round(step_bytes / (ms_per_step / 1000) / 1e9, 1),
+        "step_ms": trial_stats(per_step),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
@@ -718,7 +967,8 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(torch)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(synth, args.batch, args.seed, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(synth, args.batch, args.seed, args.cpu_seconds, tq,
+                                           torch)
     print(json.dumps(out), flush=True)
 
 

@@ -84,7 +84,23 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    build_read_ref(verbose)
     return LIB
+
+
+READ_REF = os.path.join(HERE, "libtq_readref.so")
+
+
+def build_read_ref(verbose: bool = False) -> str:
+    """libtq_readref.so: the plain streaming-read kernel the benchmark compares the GEMV with."""
+    src = os.path.join(CSRC, "ref", "tq_read_ref.hip")
+    tmp = READ_REF + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-shared", "-o", tmp, src]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, READ_REF)
+    return READ_REF
 
 
 def kernel_resources() -> dict:

@@ -41,6 +41,8 @@ _i64 = C.c_int64
 def _declare(L: C.CDLL) -> None:
     L.orc_num_threads.argtypes = []
     L.orc_num_threads.restype = C.c_int
+    L.orc_set_num_threads.argtypes = [C.c_int]
+    L.orc_set_num_threads.restype = None
     L.orc_block_weights.argtypes = [C.c_int]
     L.orc_block_weights.restype = _i64
     L.orc_block_bytes.argtypes = [C.c_int]
@@ -98,6 +100,11 @@ def _check(rc: int, what: str) -> None:
 
 def num_threads() -> int:
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops from now on."""
+    lib().orc_set_num_threads(int(n))
 
 
 def block_weights(t) -> int:

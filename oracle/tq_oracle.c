@@ -45,6 +45,14 @@ int orc_num_threads(void) {
 #endif
 }
 
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 int64_t orc_block_weights(int type) {
   switch (type) {
     case ORC_Q4_K: return 256;

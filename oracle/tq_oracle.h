@@ -35,6 +35,8 @@ extern "C" {
 
 /* Threads the oracle's parallel loops use (OpenMP). */
 int orc_num_threads(void);
+/* Threads of the parallel loops from now on (n >= 1; the OpenMP default otherwise). */
+void orc_set_num_threads(int n);
 
 /* Block format codes used by the oracle. */
 enum { ORC_Q4_K = 1, ORC_Q6_K = 2, ORC_Q8_0 = 3 };
