@@ -17,8 +17,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-Q4_K, Q6_K, Q8_0 = 1, 2, 3
-TYPES = {"q4_k": Q4_K, "q6_k": Q6_K, "q8_0": Q8_0}
+Q4_K, Q6_K, Q8_0, Q5_K, Q4_0 = 1, 2, 3, 4, 5
+TYPES = {"q4_k": Q4_K, "q6_k": Q6_K, "q8_0": Q8_0, "q5_k": Q5_K, "q4_0": Q4_0}
 
 _lib = None
 
@@ -134,7 +134,7 @@ def block_fields(t, block: np.ndarray) -> dict:
     _check(lib().orc_block_fields(t, _ptr(block), C.byref(d), C.byref(dmin), _ptr(sc), _ptr(m),
                                   _ptr(q)), "block_fields")
     out = {"d": d.value}
-    if t == Q4_K:
+    if t in (Q4_K, Q5_K):
         out.update(dmin=dmin.value, sc=sc[:8].copy(), m=m.copy(), q=q.copy())
     elif t == Q6_K:
         out.update(sc=sc.copy(), q=q.copy())

@@ -23,10 +23,21 @@
  *     low4 = nibble (low if g < 2, high otherwise) of ql[64h + l + 32*(g%2)], high2 = bits
  *     2g..2g+1 of qh[32h + l], q = low4 + 16*high2 in 0..63. Value: w = d*sc[i/16]*(q - 32).
  *   Q8_0, 32 weights in 34 bytes: [0,2) d fp16, [2,34) int8 q. Value: w = d*q.
+ *   Q5_K, 256 weights in 176 bytes: [0,2) d fp16, [2,4) dmin fp16, [4,16) the twelve scale/min
+ *     bytes S of Q4_K, [16,48) 32 bytes qh of high bits, [48,176) 128 bytes qs of low 4 bits
+ *     laid out as Q4_K's quants. Weight i (sub-block j = i/32, position l = i%32) has low4 from
+ *     qs as in Q4_K and its fifth bit in bit j of qh[l]: q = low4 + 16*((qh[l] >> j) & 1), 0..31.
+ *     Value: w = d*sc_j*q - dmin*m_j.
+ *   Q4_0, 32 weights in 18 bytes: [0,2) d fp16, [2,18) 16 bytes of 4-bit quants; weight i < 16
+ *     is the low nibble of byte 2+i, weight i >= 16 the high nibble of byte 2+i-16. Value:
+ *     w = d*(q - 8).
  *
- * Every product above has at most 23 significant bits and both Q4_K terms are multiples of
- * 2^-24 below 2^27 in magnitude, so the fp64 arithmetic here is exact; orc_dequant_f32 then
- * rounds once.
+ * The pages list these two among the formats of the NTransformer loader ("Show HN" page,
+ * section "Quantization support": Q4_0, Q8_0, Q4_K_M, Q5_K, Q6_K).
+ *
+ * Every product above has at most 23 significant bits and both Q4_K (and Q5_K) terms are
+ * multiples of 2^-24 below 2^28 in magnitude, so the fp64 arithmetic here is exact;
+ * orc_dequant_f32 then rounds once.
  */
 #include "tq_oracle.h"
 
@@ -58,6 +69,8 @@ int64_t orc_block_weights(int type) {
     case ORC_Q4_K: return 256;
     case ORC_Q6_K: return 256;
     case ORC_Q8_0: return 32;
+    case ORC_Q5_K: return 256;
+    case ORC_Q4_0: return 32;
     default: return 0;
   }
 }
@@ -67,6 +80,8 @@ int64_t orc_block_bytes(int type) {
     case ORC_Q4_K: return 144;
     case ORC_Q6_K: return 210;
     case ORC_Q8_0: return 34;
+    case ORC_Q5_K: return 176;
+    case ORC_Q4_0: return 18;
     default: return 0;
   }
 }
@@ -132,6 +147,14 @@ static int q4k_quant(const uint8_t *qs, int i) {
   return r < 32 ? (qs[32 * c + r] & 15) : (qs[32 * c + r - 32] >> 4);
 }
 
+static int q5k_quant(const uint8_t *qh, const uint8_t *qs, int i) {
+  return q4k_quant(qs, i) + 16 * ((qh[i % 32] >> (i / 32)) & 1);
+}
+
+static int q40_quant(const uint8_t *qs, int i) {
+  return i < 16 ? (qs[i] & 15) : (qs[i - 16] >> 4);
+}
+
 static int q6k_quant(const uint8_t *ql, const uint8_t *qh, int i) {
   int h = i / 128, r = i % 128, g = r / 32, l = r % 32;
   uint8_t lb = ql[64 * h + l + 32 * (g % 2)];
@@ -158,6 +181,18 @@ double orc_block_weight(int type, const uint8_t *b, int i) {
   if (type == ORC_Q8_0) {
     double d = orc_half_to_double(rd16(b));
     return d * (int8_t)b[2 + i];
+  }
+  if (type == ORC_Q5_K) {
+    double d = orc_half_to_double(rd16(b));
+    double dmin = orc_half_to_double(rd16(b + 2));
+    int sc, m;
+    q4k_scale_min(b + 4, i / 32, &sc, &m);
+    int q = q5k_quant(b + 16, b + 48, i);
+    return d * sc * q - dmin * m;
+  }
+  if (type == ORC_Q4_0) {
+    double d = orc_half_to_double(rd16(b));
+    return d * (q40_quant(b + 2, i) - 8);
   }
   return NAN;
 }
@@ -191,6 +226,25 @@ int orc_block_fields(int type, const uint8_t *b, double *d, double *dmin, int32_
       for (int i = 0; i < 32; ++i) q[i] = (int8_t)b[2 + i];
     return 0;
   }
+  if (type == ORC_Q5_K) {
+    if (d) *d = orc_half_to_double(rd16(b));
+    if (dmin) *dmin = orc_half_to_double(rd16(b + 2));
+    for (int j = 0; j < 8; ++j) {
+      int s, mm;
+      q4k_scale_min(b + 4, j, &s, &mm);
+      if (sc) sc[j] = s;
+      if (m) m[j] = mm;
+    }
+    if (q)
+      for (int i = 0; i < 256; ++i) q[i] = q5k_quant(b + 16, b + 48, i);
+    return 0;
+  }
+  if (type == ORC_Q4_0) {
+    if (d) *d = orc_half_to_double(rd16(b));
+    if (q)
+      for (int i = 0; i < 32; ++i) q[i] = q40_quant(b + 2, i);
+    return 0;
+  }
   return -1;
 }
 
@@ -220,6 +274,18 @@ static void decode_block(int type, const uint8_t *b, double *out) {
   } else if (type == ORC_Q8_0) {
     double d = orc_half_to_double(rd16(b));
     for (int i = 0; i < 32; ++i) out[i] = d * (int8_t)b[2 + i];
+  } else if (type == ORC_Q5_K) {
+    double d = orc_half_to_double(rd16(b));
+    double dmin = orc_half_to_double(rd16(b + 2));
+    for (int j = 0; j < 8; ++j) {
+      int sc, m;
+      q4k_scale_min(b + 4, j, &sc, &m);
+      for (int i = 32 * j; i < 32 * j + 32; ++i)
+        out[i] = d * sc * q5k_quant(b + 16, b + 48, i) - dmin * m;
+    }
+  } else if (type == ORC_Q4_0) {
+    double d = orc_half_to_double(rd16(b));
+    for (int i = 0; i < 32; ++i) out[i] = d * (q40_quant(b + 2, i) - 8);
   }
 }
 
@@ -686,6 +752,22 @@ static void q4k_put_scales(uint8_t *S, const int *sc, const int *m) {
   }
 }
 
+/* Write quants q[256] (0..31) into a Q5_K block's qh/qs bytes (inverse of q5k_quant). */
+static void q5k_put_quants(uint8_t *qh, uint8_t *qs, const int *q) {
+  int low[256];
+  memset(qh, 0, 32);
+  for (int i = 0; i < 256; ++i) {
+    low[i] = q[i] & 15;
+    qh[i % 32] |= (uint8_t)(((q[i] >> 4) & 1) << (i / 32));
+  }
+  q4k_put_quants(qs, low);
+}
+
+/* Write quants q[32] (0..15) into a Q4_0 block's 16 quant bytes (inverse of q40_quant). */
+static void q40_put_quants(uint8_t *qs, const int *q) {
+  for (int i = 0; i < 16; ++i) qs[i] = (uint8_t)((q[i] & 15) | ((q[i + 16] & 15) << 4));
+}
+
 /* Write quants q[256] (0..63) into a Q6_K block's ql/qh bytes (inverse of q6k_quant). */
 static void q6k_put_quants(uint8_t *ql, uint8_t *qh, const int *q) {
   memset(ql, 0, 128);
@@ -710,15 +792,24 @@ int orc_requant(int type, const uint8_t *w_blob, const double *w, int64_t n, int
     const double *wv = w + blk * bw; /* blocks are contiguous along rows of [n][k] */
     memcpy(ob, b, (size_t)bb);
     int q[256];
-    if (type == ORC_Q4_K) {
+    if (type == ORC_Q4_K || type == ORC_Q5_K) {
       double d, dmin;
       int32_t sc[8], m[8];
+      const int qmax = type == ORC_Q4_K ? 15 : 31;
       orc_block_fields(type, b, &d, &dmin, sc, m, NULL);
       for (int i = 0; i < 256; ++i) {
         double step = d * sc[i / 32];
-        q[i] = step != 0.0 ? clampi(nearbyint((wv[i] + dmin * m[i / 32]) / step), 0, 15) : 0;
+        q[i] = step != 0.0 ? clampi(nearbyint((wv[i] + dmin * m[i / 32]) / step), 0, qmax) : 0;
       }
-      q4k_put_quants(ob + 16, q);
+      if (type == ORC_Q4_K)
+        q4k_put_quants(ob + 16, q);
+      else
+        q5k_put_quants(ob + 16, ob + 48, q);
+    } else if (type == ORC_Q4_0) {
+      double d;
+      orc_block_fields(type, b, &d, NULL, NULL, NULL, NULL);
+      for (int i = 0; i < 32; ++i) q[i] = d != 0.0 ? clampi(nearbyint(wv[i] / d) + 8, 0, 15) : 8;
+      q40_put_quants(ob + 2, q);
     } else if (type == ORC_Q6_K) {
       double d;
       int32_t sc[16];
@@ -749,7 +840,15 @@ int orc_quantize(int type, const float *w, int64_t n, int64_t k, uint8_t *out) {
     uint8_t *ob = out + blk * bb;
     memset(ob, 0, (size_t)bb);
     int q[256];
-    if (type == ORC_Q8_0) {
+    if (type == ORC_Q4_0) {
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs((double)wv[i]));
+      uint16_t dh = double_to_half_rne(amax / 7.0); /* |w| <= 7d: quants 1..15 */
+      double d = orc_half_to_double(dh);
+      wr16(ob, dh);
+      for (int i = 0; i < 32; ++i) q[i] = d != 0.0 ? clampi(nearbyint(wv[i] / d) + 8, 0, 15) : 8;
+      q40_put_quants(ob + 2, q);
+    } else if (type == ORC_Q8_0) {
       double amax = 0.0;
       for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs((double)wv[i]));
       uint16_t dh = double_to_half_rne(amax / 127.0);
@@ -780,7 +879,8 @@ int orc_quantize(int type, const float *w, int64_t n, int64_t k, uint8_t *out) {
         q[i] = step != 0.0 ? clampi(nearbyint(wv[i] / step) + 32, 0, 63) : 32;
       }
       q6k_put_quants(ob, ob + 128, q);
-    } else {
+    } else { /* Q4_K, Q5_K */
+      const int qmax = type == ORC_Q4_K ? 15 : 31;
       double s[8], mn[8], smax = 0.0, mmax = 0.0;
       for (int j = 0; j < 8; ++j) {
         double lo = 0.0, hi = -INFINITY;
@@ -789,8 +889,8 @@ int orc_quantize(int type, const float *w, int64_t n, int64_t k, uint8_t *out) {
           hi = fmax(hi, (double)wv[32 * j + i]);
         }
         if (hi < lo) hi = lo;
-        mn[j] = -lo;             /* min offset, >= 0 */
-        s[j] = (hi - lo) / 15.0; /* step spanning [lo, hi] with 16 levels */
+        mn[j] = -lo;              /* min offset, >= 0 */
+        s[j] = (hi - lo) / qmax;  /* step spanning [lo, hi] with qmax + 1 levels */
         smax = fmax(smax, s[j]);
         mmax = fmax(mmax, mn[j]);
       }
@@ -806,9 +906,12 @@ int orc_quantize(int type, const float *w, int64_t n, int64_t k, uint8_t *out) {
       q4k_put_scales(ob + 4, sc, m);
       for (int i = 0; i < 256; ++i) {
         double step = d * sc[i / 32];
-        q[i] = step != 0.0 ? clampi(nearbyint((wv[i] + dmin * m[i / 32]) / step), 0, 15) : 0;
+        q[i] = step != 0.0 ? clampi(nearbyint((wv[i] + dmin * m[i / 32]) / step), 0, qmax) : 0;
       }
-      q4k_put_quants(ob + 16, q);
+      if (type == ORC_Q4_K)
+        q4k_put_quants(ob + 16, q);
+      else
+        q5k_put_quants(ob + 16, ob + 48, q);
     }
   }
   return 0;

@@ -39,7 +39,7 @@ int orc_num_threads(void);
 void orc_set_num_threads(int n);
 
 /* Block format codes used by the oracle. */
-enum { ORC_Q4_K = 1, ORC_Q6_K = 2, ORC_Q8_0 = 3 };
+enum { ORC_Q4_K = 1, ORC_Q6_K = 2, ORC_Q8_0 = 3, ORC_Q5_K = 4, ORC_Q4_0 = 5 };
 
 /* Weights per block and bytes per block for a format code; 0 for an unknown code. */
 int64_t orc_block_weights(int type);

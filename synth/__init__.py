@@ -10,6 +10,8 @@ are format knowledge here:
   Q4_K (144 B / 256 weights): d at byte 0, dmin at byte 2.
   Q6_K (210 B / 256 weights): d at byte 208.
   Q8_0 (34 B / 32 weights):   d at byte 0; the int8 quants are drawn from U{-127..127}.
+  Q5_K (176 B / 256 weights): d at byte 0, dmin at byte 2 (5-bit quants ~ U{0..31}).
+  Q4_0 (18 B / 32 weights):   d at byte 0 (4-bit quants ~ U{0..15}).
 
 Default distributions follow the workload descriptions: d ~ U(1e-3, 1e-2), dmin ~ U(0, 5e-3),
 6-bit scales and mins ~ U{0..63}, 4-bit quants ~ U{0..15}, Q6_K int8 scales ~ U{-128..127} and
@@ -24,9 +26,9 @@ import hashlib
 
 import numpy as np
 
-Q4_K, Q6_K, Q8_0 = "q4_k", "q6_k", "q8_0"
-BLOCK_WEIGHTS = {Q4_K: 256, Q6_K: 256, Q8_0: 32}
-BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, Q8_0: 34}
+Q4_K, Q6_K, Q8_0, Q5_K, Q4_0 = "q4_k", "q6_k", "q8_0", "q5_k", "q4_0"
+BLOCK_WEIGHTS = {Q4_K: 256, Q6_K: 256, Q8_0: 32, Q5_K: 256, Q4_0: 32}
+BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, Q8_0: 34, Q5_K: 176, Q4_0: 18}
 DEFAULT_SEED = 42
 
 
@@ -60,9 +62,11 @@ def blob(t: str, g: np.random.Generator, n: int, k: int, *, d_range=(1e-3, 1e-2)
         raise ValueError(f"k={k} is not a multiple of {bw}")
     nblk = n * (k // bw)
     raw = np.frombuffer(g.bytes(nblk * bb), np.uint8).copy().reshape(nblk, bb)
-    if t == Q4_K:
+    if t in (Q4_K, Q5_K):
         raw[:, 0:2] = _fp16_field(g, nblk, *d_range, d_value)
         raw[:, 2:4] = _fp16_field(g, nblk, *dmin_range, dmin_value)
+    elif t == Q4_0:
+        raw[:, 0:2] = _fp16_field(g, nblk, *d_range, d_value)
     elif t == Q6_K:
         raw[:, 208:210] = _fp16_field(g, nblk, *d_range, d_value)
     elif t == Q8_0:

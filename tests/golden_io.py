@@ -4,8 +4,8 @@ import os
 import numpy as np
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-BLOCK_BYTES = {"q4_k": 144, "q6_k": 210, "q8_0": 34}
-BLOCK_WEIGHTS = {"q4_k": 256, "q6_k": 256, "q8_0": 32}
+BLOCK_BYTES = {"q4_k": 144, "q6_k": 210, "q8_0": 34, "q5_k": 176, "q4_0": 18}
+BLOCK_WEIGHTS = {"q4_k": 256, "q6_k": 256, "q8_0": 32, "q5_k": 256, "q4_0": 32}
 
 
 def _value(tok: str) -> float:

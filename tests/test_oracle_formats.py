@@ -43,7 +43,7 @@ def test_golden_block(fx):
         assert oracle.lib().orc_block_weight(oracle.TYPES[t], fx["block"].ctypes.data, i) == exp[i]
 
 
-@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q8_0"])
+@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q8_0", "q5_k", "q4_0"])
 def test_row_decode_equals_per_weight_definition(t):
     """Rows are decoded a block at a time; every value equals orc_block_weight's, bit for bit."""
     n, k = 3, 1024
@@ -104,7 +104,7 @@ def test_q6k_nibble_pattern():
     assert np.array_equal(got, exp)
 
 
-@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q8_0"])
+@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q8_0", "q5_k", "q4_0"])
 def test_f32_is_one_rounding_of_exact(t):
     g = synth.rng(7, "f32-rounding", t)
     n, k = 6, 512
@@ -112,8 +112,8 @@ def test_f32_is_one_rounding_of_exact(t):
     w64 = oracle.dequant(t, w, n, k, out="f64")
     w32 = oracle.dequant(t, w, n, k, out="f32")
     assert np.array_equal(w64.astype(np.float32), w32)
-    if t != "q4_k":
-        # d*sc*(q-32) and d*q carry at most 23 significant bits: exact in fp32
+    if t not in ("q4_k", "q5_k"):
+        # d*sc*(q-32), d*q and d*(q-8) carry at most 23 significant bits: exact in fp32
         assert np.array_equal(w32.astype(np.float64), w64)
 
 
@@ -130,7 +130,7 @@ def test_bf16_matches_torch_rne():
     assert np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q8_0"])
+@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q8_0", "q5_k", "q4_0"])
 def test_requant_round_trip(t):
     """Quants re-derived from a blob's own decoded values and scale fields equal the blob's."""
     g = synth.rng(11, "requant", t)
@@ -143,7 +143,7 @@ def test_requant_round_trip(t):
     for blk in range(wb.shape[0]):
         f0 = oracle.block_fields(t, wb[blk])
         f1 = oracle.block_fields(t, bk[blk])
-        if t == "q4_k":
+        if t in ("q4_k", "q5_k"):
             assert np.array_equal(wb[blk, :16], bk[blk, :16])
             live = np.repeat(f0["sc"] != 0, 32) & (f0["d"] != 0)
         elif t == "q6_k":
@@ -159,7 +159,7 @@ def test_requant_round_trip(t):
     assert np.array_equal(back32, back)
 
 
-@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q8_0"])
+@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q8_0", "q5_k", "q4_0"])
 def test_quantizer_error_within_one_step(t):
     g = synth.rng(5, "quantize", t)
     n, k = 16, 512
@@ -171,7 +171,7 @@ def test_quantizer_error_within_one_step(t):
     steps = np.empty((n * k // bw, bw))
     for blk, raw in enumerate(blob.reshape(-1, bb)):
         f = oracle.block_fields(t, raw)
-        if t == "q4_k":
+        if t in ("q4_k", "q5_k"):
             steps[blk] = np.repeat(f["d"] * f["sc"], 32)
         elif t == "q6_k":
             steps[blk] = np.repeat(f["d"] * np.abs(f["sc"]), 16)
@@ -194,3 +194,10 @@ def test_synth_is_deterministic_and_in_range():
     assert np.all((d >= 9.99e-4) & (d <= 1.0001e-2)) and np.all((dmin >= 0) & (dmin <= 5.01e-3))
     q8 = synth.blob("q8_0", synth.rng(1, "y"), 64, 1024).reshape(-1, 34)[:, 2:].view(np.int8)
     assert q8.min() >= -127 and q8.max() <= 127
+    for t, bb, fields in (("q5_k", 176, (0, 2)), ("q4_0", 18, (0,))):
+        blk = synth.blob(t, synth.rng(1, "z", t), 8, 512).reshape(-1, bb)
+        d = blk[:, 0:2].copy().view(np.float16).astype(np.float64).ravel()
+        assert np.all((d >= 9.99e-4) & (d <= 1.0001e-2))
+        if 2 in fields:
+            dmin = blk[:, 2:4].copy().view(np.float16).astype(np.float64).ravel()
+            assert np.all((dmin >= 0) & (dmin <= 5.01e-3))

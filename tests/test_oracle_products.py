@@ -22,7 +22,7 @@ def _dense(t, w, n, k):
     return oracle.dequant(t, w, n, k, out="f64")
 
 
-@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q8_0"])
+@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q8_0", "q5_k", "q4_0"])
 @pytest.mark.parametrize("n,k,b", [(1, 256, 1), (3, 512, 2), (2, 256, 3)])
 def test_gemv_brute_force(t, n, k, b):
     g = synth.rng(21, "gemv-bf", t, n, k, b)
@@ -36,7 +36,7 @@ def test_gemv_brute_force(t, n, k, b):
     np.testing.assert_allclose(mag, refmag, rtol=1e-12)
 
 
-@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q8_0"])
+@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q8_0", "q5_k", "q4_0"])
 def test_gemv_unit_vector_picks_column(t):
     g = synth.rng(22, "gemv-ej", t)
     n, k = 5, 512
@@ -177,7 +177,7 @@ def _dense_ffn(t, ex, H, F, x64):
     return down @ h, np.abs(down) @ np.abs(h)
 
 
-@pytest.mark.parametrize("t", ["q4_k", "q8_0"])
+@pytest.mark.parametrize("t", ["q4_k", "q8_0", "q5_k", "q4_0"])
 def test_moe_against_dense_numpy(t):
     H, F, E, k, T = 256, 512, 4, 2, 3
     shape = dict(hidden=H, ffn=F, n_experts=E, shared=True)
