@@ -14,6 +14,12 @@
  *   TQ_Q6_K  256 weights / 210 bytes: 128 bytes low 4 bits, 64 bytes high 2 bits, 16 int8
  *            scales, d fp16; w = d*sc*(q - 32).
  *   TQ_Q8_0  32 weights / 34 bytes: d fp16, 32 int8 quants; w = d*q.
+ *   TQ_Q5_K  256 weights / 176 bytes: d fp16, dmin fp16, the 12 scale/min bytes of Q4_K, 32 bytes
+ *            of fifth bits (bit j of byte l: position l of sub-block j), 128 bytes of low 4 bits
+ *            laid out as Q4_K's; w = d*sc*q - dmin*m with q in 0..31.
+ *   TQ_Q4_0  32 weights / 18 bytes: d fp16, 16 bytes of nibbles (weight i < 16 the low nibble of
+ *            byte i, weight i >= 16 the high nibble of byte i-16); w = d*(q - 8).
+ *            (Q5_K and Q4_0: the "Show HN" page's "Quantization support" list.)
  * A weight matrix is n rows ("out") by k columns ("in"), stored row-major as n rows of k/B
  * consecutive blocks (B = weights per block), i.e. n * tq_row_bytes(type, k) bytes.
  *
@@ -38,7 +44,7 @@
 extern "C" {
 #endif
 
-enum { TQ_Q4_K = 1, TQ_Q6_K = 2, TQ_Q8_0 = 3 };                 /* block formats */
+enum { TQ_Q4_K = 1, TQ_Q6_K = 2, TQ_Q8_0 = 3, TQ_Q5_K = 4, TQ_Q4_0 = 5 }; /* block formats */
 enum { TQ_F32 = 0, TQ_BF16 = 1 };                                /* dequant output types */
 enum {                                                           /* status codes */
   TQ_OK = 0,
@@ -51,7 +57,8 @@ enum {                                                           /* status codes
 };
 enum { TQ_PATH_AUTO = 0, TQ_PATH_F32 = 1, TQ_PATH_BF16_MFMA = 2 }; /* MoE expert-product path */
 
-/* Weights per block (256, 256, 32) and bytes per block (144, 210, 34); 0 for an unknown type. */
+/* Weights per block (Q4_K, Q6_K, Q8_0, Q5_K, Q4_0: 256, 256, 32, 256, 32) and bytes per block
+ * (144, 210, 34, 176, 18); 0 for an unknown type. */
 int64_t tq_block_weights(int type);
 int64_t tq_block_bytes(int type);
 /* Bytes of one row of k weights; -1 if type is unknown or k is not a multiple of the block. */
@@ -61,7 +68,7 @@ int64_t tq_row_bytes(int type, int64_t k);
  * tq_dequant -- expand a blob to dense values (the block decode of the formats above).
  *   w     [n rows of tq_row_bytes(type,k)] blob, 16-byte aligned.
  *   out   [n][k] of out_type: TQ_F32 holds each weight's exact value rounded once to nearest
- *         even (bitwise equal to the exact value for Q6_K and Q8_0); TQ_BF16 holds the
+ *         even (bitwise equal to the exact value for Q6_K, Q8_0 and Q4_0); TQ_BF16 holds the
  *         nearest-even bf16 rounding of that fp32 value, as uint16 bit patterns. 4-byte aligned.
  *   n >= 0, k >= 0 with k % tq_block_weights(type) == 0; n*k == 0 enqueues nothing.
  */
@@ -90,7 +97,8 @@ int tq_dequant(int type, const void *w, int64_t n, int64_t k, int out_type, void
  *   two and split into fp16 hi + lo, sc * q and the mins as exact fp16 integers), fp32
  *   accumulation. Q8_0 at 2..16 tokens and Q6_K (k % 512 == 0) at 4..16 tokens stream them once
  *   on the fp32 matrix cores, with the exactly dequantized weights as operands (x 16-byte
- *   aligned; the workspace when k spans more than one slice of 8 blocks).
+ *   aligned; the workspace when k spans more than one slice of 8 blocks). Q5_K and Q4_0 take the
+ *   lane-per-row fp32 kernel (k % 256 == 0; other Q4_0 k: a per-weight kernel).
  */
 size_t tq_gemv_workspace_bytes(int type, int64_t n, int64_t k, int64_t batch);
 int tq_gemv(int type, const void *w, int64_t n, int64_t k, const float *x, int64_t batch,
@@ -177,7 +185,8 @@ typedef struct {
 } tq_expert;
 
 typedef struct {
-  int type;                      /* block format of every expert matrix */
+  int type;                      /* block format of every expert matrix (any of the five on the
+                                    fp32 path; Q4_K only on TQ_PATH_BF16_MFMA) */
   int64_t hidden, ffn;           /* multiples of 256 */
   int64_t n_experts, top_k;      /* 1 <= top_k <= min(n_experts, 32), n_experts <= 1024 */
   const float *router_w;         /* device [n_experts][hidden] fp32, 16-byte aligned */

@@ -15,8 +15,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtq.so")
 
-Q4_K, Q6_K, Q8_0 = 1, 2, 3
-TYPES = {"q4_k": Q4_K, "q6_k": Q6_K, "q8_0": Q8_0}
+Q4_K, Q6_K, Q8_0, Q5_K, Q4_0 = 1, 2, 3, 4, 5
+TYPES = {"q4_k": Q4_K, "q6_k": Q6_K, "q8_0": Q8_0, "q5_k": Q5_K, "q4_0": Q4_0}
 F32, BF16 = 0, 1
 PATH_AUTO, PATH_F32, PATH_BF16_MFMA = 0, 1, 2
 MOE_ROUTE, MOE_EXPERTS, MOE_COMBINE, MOE_ALL = 1, 2, 4, 7

@@ -26,7 +26,9 @@ int fail(int code, const char *fmt, ...) {
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-bool known_type(int t) { return t == TQ_Q4_K || t == TQ_Q6_K || t == TQ_Q8_0; }
+bool known_type(int t) {
+  return t == TQ_Q4_K || t == TQ_Q6_K || t == TQ_Q8_0 || t == TQ_Q5_K || t == TQ_Q4_0;
+}
 
 int launched(int rc, const char *what) {
   if (rc == 0) return TQ_OK;

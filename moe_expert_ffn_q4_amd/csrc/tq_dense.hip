@@ -51,6 +51,23 @@ __device__ float weight_at(int fmt, const uint8_t *row, int64_t i) {
     const float sc = (float)(int8_t)b[192 + (r >> 4)];
     return (half_bits_to_float(rd16(b + 208)) * sc) * (float)q;
   }
+  if (fmt == FMT_Q5_K) {
+    const uint8_t *b = row + (i >> 8) * 176;
+    const int r = (int)(i & 255), j = r >> 5, c = r >> 6, o = r & 63, l = r & 31;
+    uint32_t sc, m;
+    q4k_sm(b + 4, j, sc, m);
+    const uint32_t lo = o < 32 ? (b[48 + 32 * c + o] & 15u) : (uint32_t)(b[48 + 32 * c + o - 32] >> 4);
+    const uint32_t q = lo | (((uint32_t)(b[16 + l] >> j) & 1u) << 4);
+    // d*sc*q (<= 17 + 5 bits) and dmin*m are exact in fp32: one rounding, in the subtraction
+    return (half_bits_to_float(rd16(b)) * (float)sc) * (float)q -
+           half_bits_to_float(rd16(b + 2)) * (float)m;
+  }
+  if (fmt == FMT_Q4_0) {
+    const uint8_t *b = row + (i >> 5) * 18;
+    const int r = (int)(i & 31);
+    const uint32_t q = r < 16 ? (b[2 + r] & 15u) : (uint32_t)(b[2 + r - 16] >> 4);
+    return half_bits_to_float(rd16(b)) * (float)((int)q - 8);
+  }
   const uint8_t *b = row + (i >> 5) * 34;
   return half_bits_to_float(rd16(b)) * (float)(int8_t)b[2 + (i & 31)];
 }
@@ -554,11 +571,17 @@ static int launch_gemv_fmt(const uint8_t *w, int64_t rb, int n, int64_t k, const
     const size_t lds = (size_t)4 * gemv_tile_lds_floats<FMT>(nt, p.upk, p.waves);
     const float *xt = x + (int64_t)t0 * k;
     float *yt = y + (int64_t)t0 * n;
-    switch (nt) {
+    if constexpr (FMT == FMT_Q5_K) {  // one token per pass (see unit_dot for Q5_K)
+      nt = 1;
+      launch_gemv_nt<FMT, 1>(w, rb, n, units, p, xt, k, yt, n, partial, counters,
+                             (size_t)4 * gemv_tile_lds_floats<FMT>(1, p.upk, p.waves), s);
+    } else {
+      switch (nt) {
 #define TQ_CASE(NTV) \
   case NTV: launch_gemv_nt<FMT, NTV>(w, rb, n, units, p, xt, k, yt, n, partial, counters, lds, s); break;
-      TQ_CASE(1) TQ_CASE(2) TQ_CASE(3) TQ_CASE(4) TQ_CASE(5) TQ_CASE(6) TQ_CASE(7) TQ_CASE(8)
+        TQ_CASE(1) TQ_CASE(2) TQ_CASE(3) TQ_CASE(4) TQ_CASE(5) TQ_CASE(6) TQ_CASE(7) TQ_CASE(8)
 #undef TQ_CASE
+      }
     }
     if (hipGetLastError() != hipSuccess) return -1;
     t0 += nt;
@@ -644,9 +667,9 @@ int launch_moe_kl(const MoeKlArgs &a, int64_t k, int nslots, hipStream_t s) {
 }
 
 bool gemv_fast_shape(int fmt, int64_t k) {
-  if (fmt == FMT_Q4_K) return k % 256 == 0;
   if (fmt == FMT_Q6_K) return k % 512 == 0;  // 210 * (k/256) bytes per row is dword aligned
-  return k % 256 == 0;                       // Q8_0: whole 8-block units, 16-byte aligned rows
+  // Q4_K, Q5_K: whole blocks; Q8_0, Q4_0: whole 8-block units; rows 16-byte aligned
+  return k % 256 == 0;
 }
 
 int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, int64_t batch,
@@ -693,6 +716,8 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, in
   switch (fmt) {
     case FMT_Q4_K: return launch_gemv_fmt<FMT_Q4_K>(wb, rb, (int)n, k, x, (int)batch, y, ws, ws_bytes, s);
     case FMT_Q6_K: return launch_gemv_fmt<FMT_Q6_K>(wb, rb, (int)n, k, x, (int)batch, y, ws, ws_bytes, s);
+    case FMT_Q5_K: return launch_gemv_fmt<FMT_Q5_K>(wb, rb, (int)n, k, x, (int)batch, y, ws, ws_bytes, s);
+    case FMT_Q4_0: return launch_gemv_fmt<FMT_Q4_0>(wb, rb, (int)n, k, x, (int)batch, y, ws, ws_bytes, s);
     default: return launch_gemv_fmt<FMT_Q8_0>(wb, rb, (int)n, k, x, (int)batch, y, ws, ws_bytes, s);
   }
 }

@@ -13,6 +13,8 @@
 //   sum_i w_i x_i = sum_j d*sc_j * sum_{i in j} q_i x_i  -  sum_j dmin*m_j * S_j     (Q4_K)
 //   sum_i w_i x_i = sum_s d*sc_s * (sum_{i in s} q_i x_i - 32 * S_s)                (Q6_K)
 //   sum_i w_i x_i = sum_b d_b * (sum_{i in b} (q_i + 128) x_i - 128 * S_b)          (Q8_0)
+//   sum_i w_i x_i = sum_j d*sc_j * sum_{i in j} q_i x_i  -  sum_j dmin*m_j * S_j     (Q5_K)
+//   sum_i w_i x_i = sum_b d_b * (sum_{i in b} q_i x_i - 8 * S_b)                    (Q4_0)
 // where S is the sum of x over the 32- (or 16-) weight group. The group sums of the tile's
 // tokens are computed once per workgroup into LDS and read with wave-uniform addresses.
 #pragma once
@@ -21,7 +23,7 @@
 
 namespace tq {
 
-enum { FMT_Q4_K = 1, FMT_Q6_K = 2, FMT_Q8_0 = 3 };
+enum { FMT_Q4_K = 1, FMT_Q6_K = 2, FMT_Q8_0 = 3, FMT_Q5_K = 4, FMT_Q4_0 = 5 };
 
 template <int FMT>
 struct Fmt;
@@ -40,6 +42,16 @@ struct Fmt<FMT_Q8_0> {
   static constexpr int unit_bytes = 272;  // eight 34-byte blocks
   static constexpr int group = 32;        // one block
 };
+template <>
+struct Fmt<FMT_Q5_K> {
+  static constexpr int unit_bytes = 176;  // one block
+  static constexpr int group = 32;        // sub-block
+};
+template <>
+struct Fmt<FMT_Q4_0> {
+  static constexpr int unit_bytes = 144;  // eight 18-byte blocks
+  static constexpr int group = 32;        // one block
+};
 
 // Raw bytes of one unit of one row, as loaded.
 template <int FMT>
@@ -55,6 +67,14 @@ struct Unit<FMT_Q6_K> {
 template <>
 struct Unit<FMT_Q8_0> {
   uint32_t v[68];
+};
+template <>
+struct Unit<FMT_Q5_K> {
+  uint32_t v[44];  // header (4 dwords), 32 high-bit bytes (8), 128 low-nibble bytes (32)
+};
+template <>
+struct Unit<FMT_Q4_0> {
+  uint32_t v[36];
 };
 
 // ---- loads ---------------------------------------------------------------------------------
@@ -101,6 +121,33 @@ __device__ __forceinline__ void load_unit(Unit<FMT_Q8_0> &u, const uint8_t *row,
   const gu32x4 p = (gu32x4)(row + (size_t)idx * 272);
 #pragma unroll
   for (int i = 0; i < 17; ++i) {
+    u32x4 t = *(p + i);
+    u.v[4 * i + 0] = t.x;
+    u.v[4 * i + 1] = t.y;
+    u.v[4 * i + 2] = t.z;
+    u.v[4 * i + 3] = t.w;
+  }
+}
+
+// Q5_K: the block starts at a multiple of 176 bytes from a 16-byte aligned row start.
+__device__ __forceinline__ void load_unit(Unit<FMT_Q5_K> &u, const uint8_t *row, int idx) {
+  const gu32x4 p = (gu32x4)(row + (size_t)idx * 176);
+#pragma unroll
+  for (int i = 0; i < 11; ++i) {
+    u32x4 t = *(p + i);
+    u.v[4 * i + 0] = t.x;
+    u.v[4 * i + 1] = t.y;
+    u.v[4 * i + 2] = t.z;
+    u.v[4 * i + 3] = t.w;
+  }
+}
+
+// Q4_0: eight blocks (144 bytes) starting at a multiple of 144 from a 16-byte aligned row start
+// (k is a multiple of 256).
+__device__ __forceinline__ void load_unit(Unit<FMT_Q4_0> &u, const uint8_t *row, int idx) {
+  const gu32x4 p = (gu32x4)(row + (size_t)idx * 144);
+#pragma unroll
+  for (int i = 0; i < 9; ++i) {
     u32x4 t = *(p + i);
     u.v[4 * i + 0] = t.x;
     u.v[4 * i + 1] = t.y;
@@ -317,6 +364,87 @@ __device__ __forceinline__ void unit_dot(const Unit<FMT_Q8_0> &u, const float *c
 #pragma unroll
       for (int t = 0; t < NT; ++t)
         acc[t] = __builtin_fmaf(d, __builtin_fmaf(-128.f, gs[t][bb], dot[t]), acc[t]);
+    }
+  }
+}
+
+// Q5_K, one token: quants of sub-block j as bytes (low nibble from the Q4_K-style plane, fifth bit
+// from bit j of the high-bit byte of the same position), converted one byte per weight; each
+// sub-block's scale and min unpacked where they are used, the min term added last. Batches run
+// this once per token: the multi-token forms of it spilled registers to scratch memory.
+template <int NT>
+__device__ __forceinline__ void unit_dot(const Unit<FMT_Q5_K> &u, const float *const (&xp)[NT],
+                                         const float *const (&gs)[NT], float (&acc)[NT]) {
+  static_assert(NT == 1, "Q5_K runs one token per pass");
+  const uint32_t h0 = u.v[0], s0 = u.v[1], s1 = u.v[2], s2 = u.v[3];
+  float bs = 0.f, ms = 0.f;
+  float dep = 0.f;  // the previous sub-block's result: its activation loads wait for it
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int c = j >> 1, sh = 8 * (j & 3);
+    const float *xj = xp[0] + after(32 * j, dep);
+    const uint32_t scj = j < 4 ? (s0 >> sh) & 63u : ((s2 >> sh) & 15u) | (((s0 >> (sh + 6)) & 3u) << 4);
+    const uint32_t mj = j < 4 ? (s1 >> sh) & 63u
+                              : ((s2 >> (sh + 4)) & 15u) | (((s1 >> (sh + 6)) & 3u) << 4);
+    float dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t w = u.v[12 + 8 * c + i];
+      const uint32_t hb = u.v[4 + i];
+      const uint32_t nib = (j & 1) ? ((w >> 4) & 0x0F0F0F0Fu) : (w & 0x0F0F0F0Fu);
+      const uint32_t q = opaque(nib | (((hb >> j) & 0x01010101u) << 4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dot = __builtin_fmaf(byte_to_float(q, e), xj[4 * i + e], dot);
+    }
+    bs = __builtin_fmaf((float)scj, dot, bs);
+    ms = __builtin_fmaf((float)mj, gs[0][j], ms);
+    dep = bs;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const float d = half_bits_to_float(h0), dmin = half_bits_to_float(h0 >> 16);
+  acc[0] = __builtin_fmaf(d, bs, __builtin_fmaf(-dmin, ms, acc[0]));
+}
+
+// Q4_0: eight blocks; block 2p starts on a dword boundary (d in the low half, quants two bytes
+// in), block 2p + 1 two bytes past one (d in the high half, quants dword-aligned). Nibbles go
+// through the fp8 converter (q * unit, the unit folded into d).
+template <int NT>
+__device__ __forceinline__ void unit_dot(const Unit<FMT_Q4_0> &u, const float *const (&xp)[NT],
+                                         const float *const (&gs)[NT], float (&acc)[NT]) {
+  const float inv_unit = 1.f / nibble_fp8_unit();  // exact: a power of two
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+#pragma unroll
+    for (int odd = 0; odd < 2; ++odd) {
+      const int bb = 2 * p + odd;
+      float d;
+      uint32_t q[4];
+      if (!odd) {
+        d = half_bits_to_float(u.v[9 * p]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = shift2(u.v[9 * p + i], u.v[9 * p + i + 1]);
+      } else {
+        d = half_bits_to_float(u.v[9 * p + 4] >> 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = u.v[9 * p + 5 + i];
+      }
+      // weights 4i..4i+3 are the low nibbles of quant dword i, weights 16+4i.. the high ones
+      float f[32];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = q[i] & 0x0F0F0F0Fu, hi = (q[i] >> 4) & 0x0F0F0F0Fu;
+        nibbles_to_float<false>(lo, f[4 * i], f[4 * i + 1]);
+        nibbles_to_float<true>(lo, f[4 * i + 2], f[4 * i + 3]);
+        nibbles_to_float<false>(hi, f[16 + 4 * i], f[16 + 4 * i + 1]);
+        nibbles_to_float<true>(hi, f[16 + 4 * i + 2], f[16 + 4 * i + 3]);
+      }
+      const float dq = d * inv_unit;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float dot = dot32(f, xp[t] + 32 * bb);
+        acc[t] = __builtin_fmaf(dq, dot, __builtin_fmaf(-8.f * d, gs[t][bb], acc[t]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }

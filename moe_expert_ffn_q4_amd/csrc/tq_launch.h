@@ -19,8 +19,13 @@ unsigned long long call_tag();
 
 inline int clampi(int v, int lo, int hi) { return v < lo ? lo : v > hi ? hi : v; }
 inline int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
-inline int64_t fmt_block_weights(int fmt) { return fmt == 1 ? 256 : fmt == 2 ? 256 : fmt == 3 ? 32 : 0; }
-inline int64_t fmt_block_bytes(int fmt) { return fmt == 1 ? 144 : fmt == 2 ? 210 : fmt == 3 ? 34 : 0; }
+// Q4_K, Q6_K, Q8_0, Q5_K, Q4_0
+inline int64_t fmt_block_weights(int fmt) {
+  return fmt == 1 || fmt == 2 || fmt == 4 ? 256 : fmt == 3 || fmt == 5 ? 32 : 0;
+}
+inline int64_t fmt_block_bytes(int fmt) {
+  return fmt == 1 ? 144 : fmt == 2 ? 210 : fmt == 3 ? 34 : fmt == 4 ? 176 : fmt == 5 ? 18 : 0;
+}
 
 // Each returns 0 when everything was enqueued, -1 on a HIP launch error, -2 when the shape needs
 // more LDS than one workgroup may use.

@@ -832,11 +832,15 @@ static int moe_gemv_launch(MoeGemvArgs a, int nslots, int waves, hipStream_t st)
 
 template <int FMT>
 static int moe_gemv_nt(const MoeGemvArgs &a, int nt, int nslots, int waves, hipStream_t st) {
-  switch (nt) {
-    case 1: return moe_gemv_launch<FMT, 1>(a, nslots, waves, st);
-    case 2: return moe_gemv_launch<FMT, 2>(a, nslots, waves, st);
-    case 4: return moe_gemv_launch<FMT, 4>(a, nslots, waves, st);
-    default: return moe_gemv_launch<FMT, 8>(a, nslots, waves, st);
+  if constexpr (FMT == FMT_Q5_K) {
+    return moe_gemv_launch<FMT, 1>(a, nslots, waves, st);  // one token per pass
+  } else {
+    switch (nt) {
+      case 1: return moe_gemv_launch<FMT, 1>(a, nslots, waves, st);
+      case 2: return moe_gemv_launch<FMT, 2>(a, nslots, waves, st);
+      case 4: return moe_gemv_launch<FMT, 4>(a, nslots, waves, st);
+      default: return moe_gemv_launch<FMT, 8>(a, nslots, waves, st);
+    }
   }
 }
 
@@ -845,6 +849,8 @@ static int moe_gemv_dispatch(int fmt, const MoeGemvArgs &a, int nt, int nslots, 
   switch (fmt) {
     case FMT_Q4_K: return moe_gemv_nt<FMT_Q4_K>(a, nt, nslots, waves, st);
     case FMT_Q6_K: return moe_gemv_nt<FMT_Q6_K>(a, nt, nslots, waves, st);
+    case FMT_Q5_K: return moe_gemv_nt<FMT_Q5_K>(a, nt, nslots, waves, st);
+    case FMT_Q4_0: return moe_gemv_nt<FMT_Q4_0>(a, nt, nslots, waves, st);
     default: return moe_gemv_nt<FMT_Q8_0>(a, nt, nslots, waves, st);
   }
 }

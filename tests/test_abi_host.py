@@ -30,8 +30,9 @@ def test_exports_every_declared_symbol():
 
 def test_size_helpers():
     L = tq.lib()
-    assert [L.tq_block_weights(t) for t in (1, 2, 3)] == [256, 256, 32]
-    assert [L.tq_block_bytes(t) for t in (1, 2, 3)] == [144, 210, 34]
+    assert [L.tq_block_weights(t) for t in (1, 2, 3, 4, 5)] == [256, 256, 32, 256, 32]
+    assert [L.tq_block_bytes(t) for t in (1, 2, 3, 4, 5)] == [144, 210, 34, 176, 18]
+    assert L.tq_row_bytes(4, 4096) == 2816 and L.tq_row_bytes(5, 96) == 54
     assert L.tq_block_weights(9) == 0
     assert L.tq_row_bytes(1, 4096) == 2304 and L.tq_row_bytes(2, 8192) == 6720
     assert L.tq_row_bytes(3, 28672) == 30464 and L.tq_row_bytes(3, 33) == -1

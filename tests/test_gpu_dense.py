@@ -21,7 +21,7 @@ def _print_case(*a):
     print("case:", *a, flush=True)
 
 
-@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q8_0"])
+@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q8_0", "q5_k", "q4_0"])
 @pytest.mark.parametrize("n,k", [(1, 256), (67, 1024), (130, 4608), (3, 768)])
 def test_dequant_bitwise(t, n, k):
     _print_case("dequant", t, n, k)
@@ -50,6 +50,8 @@ GEMV_CASES = [
     ("q4_k", 200, 2304), ("q4_k", 64, 256), ("q4_k", 1, 4096), ("q4_k", 333, 9216),
     ("q6_k", 150, 3072), ("q6_k", 70, 768), ("q6_k", 64, 512),
     ("q8_0", 190, 2560), ("q8_0", 65, 96), ("q8_0", 33, 800),
+    ("q5_k", 150, 2304), ("q5_k", 64, 256), ("q5_k", 70, 5120),
+    ("q4_0", 190, 2560), ("q4_0", 65, 96), ("q4_0", 33, 800),
 ]
 
 
@@ -66,14 +68,16 @@ def test_gemv_parity(t, n, k, batch):
 
 
 @pytest.mark.parametrize("t,n,k", [("q4_k", 300, 4096), ("q6_k", 200, 3584 * 2), ("q8_0", 129, 2048),
-                                   ("q6_k", 64, 1280), ("q8_0", 64, 352)])
+                                   ("q6_k", 64, 1280), ("q8_0", 64, 352), ("q5_k", 150, 4096),
+                                   ("q4_0", 129, 2048), ("q4_0", 64, 352)])
 @pytest.mark.parametrize("batch", [1, 5, 8])
 def test_gemv_integer_lattice_bitwise(t, n, k, batch):
     """Scales 2^-8 and x in {-1,0,1}: every partial sum is exact in fp32, so any summation order
     gives the exact result and the GPU must match the oracle bit for bit."""
     _print_case("lattice", t, n, k, batch)
     g = synth.rng(103, "lattice", t, n, k)
-    kw = dict(d_value=2.0 ** -8, dmin_value=2.0 ** -8) if t == "q4_k" else dict(d_value=2.0 ** -8)
+    kw = (dict(d_value=2.0 ** -8, dmin_value=2.0 ** -8) if t in ("q4_k", "q5_k")
+          else dict(d_value=2.0 ** -8))
     w = synth.blob(t, g, n, k, **kw)
     if t == "q6_k":  # keep |sc*(q-32)| <= 256 so sums stay below 2^16 in units of 2^-8
         blk = w.reshape(-1, 210)
@@ -84,7 +88,8 @@ def test_gemv_integer_lattice_bitwise(t, n, k, batch):
     assert np.array_equal(y.astype(np.float64), ref)
 
 
-@pytest.mark.parametrize("t,n,k", [("q4_k", 200, 4096), ("q6_k", 130, 3072), ("q8_0", 70, 2048)])
+@pytest.mark.parametrize("t,n,k", [("q4_k", 200, 4096), ("q6_k", 130, 3072), ("q8_0", 70, 2048),
+                                   ("q5_k", 130, 4096), ("q4_0", 70, 2048)])
 @pytest.mark.parametrize("batch", [1, 7])
 def test_gemv_without_workspace(t, n, k, batch):
     """No workspace: every row group in one workgroup; and an explicit workspace."""

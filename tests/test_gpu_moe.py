@@ -88,6 +88,8 @@ SMALL = [
     ("q4_k", dict(hidden=768, ffn=512, n_experts=16, shared=True), 4, [1, 33]),
     ("q8_0", dict(hidden=512, ffn=768, n_experts=6, shared=True), 2, [3, 70]),
     ("q6_k", dict(hidden=1024, ffn=512, n_experts=5, shared=False), 3, [2, 65]),
+    ("q5_k", dict(hidden=512, ffn=768, n_experts=6, shared=True), 2, [1, 3, 40]),
+    ("q4_0", dict(hidden=768, ffn=512, n_experts=8, shared=False), 2, [1, 5, 33]),
 ]
 
 
