@@ -52,6 +52,12 @@ def _args():
                         "Llama-3-70B-shaped layer in each of Q4_K, Q6_K and Q8_0 at batch 1, 4 "
                         "and 16")
     p.add_argument("--tokens", type=int, default=4096, help="tokens of the prefill workload")
+    p.add_argument("--cache-slots", type=int, nargs="*", default=None,
+                   help="deepseek-host: also sweep an expert residency cache of these slot "
+                        "counts over a Zipf-skewed routing trace (0 = no cache)")
+    p.add_argument("--prefetch", type=int, nargs="*", default=[0, 4],
+                   help="deepseek-host cache sweep: experts prefetched per call (each value is "
+                        "swept with every slot count)")
     p.add_argument("--seed", type=int, default=42)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -849,7 +855,7 @@ def host_bench(args, torch, tq, synth):
     plain = h2d_bytes * args.steps / (time.perf_counter() - t1) / 1e9
     ms = elapsed * 1000 / args.steps
     achieved = h2d_bytes / (ms / 1000) / 1e9
-    return {
+    out = {
         "metric": METRIC, "value": round(T * args.steps / elapsed, 2), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -864,6 +870,76 @@ def host_bench(args, torch, tq, synth):
                 "plain_pinned_copy": round(plain, 2), "unit": "GB/s",
                 "frac": round(achieved / plain, 4)},
     }
+    if args.cache_slots:
+        out["cache_sweep"] = {
+            "trace": f"Zipf-skewed routing (synth.zipf_router), one new x per step, {T} token(s) "
+                     f"per step, {args.steps} timed steps after {args.warmup}",
+            "rows": cache_sweep(args, torch, tq, synth)}
+    return out
+
+
+def cache_sweep(args, torch, tq, synth):
+    """The DeepSeek-shaped decode layer (T = --batch) with its routed experts in pinned host
+    memory and a router whose routing favours some experts (synth.zipf_router: the hottest 32 of
+    256 experts take about 3/4 of the selections), one new activation vector per step (x = z + v).
+    For each slot count (0: no cache) the same trace of steps runs after --warmup steps; reported
+    per configuration: time and tokens/s per step, host-to-device bytes per step, and the cache's
+    hit rate and prefetches."""
+    shape = synth.DEEPSEEK
+    k, T, E, H = shape["top_k"], args.batch, shape["n_experts"], shape["hidden"]
+    layer = synth.moe_layer(shape, "q4_k", seed=args.seed, tag="deepseek")
+    wr, v = synth.zipf_router(synth.rng(args.seed, "zipf-router"), E, H)
+    pinned = [tuple(torch.from_numpy(b).pin_memory() for b in e) for e in layer["experts"]]
+    shared = tuple(torch.from_numpy(b).cuda() for b in layer["shared"])
+    expert_bytes = sum(b.numel() for b in pinned[0])
+    g = synth.rng(args.seed, "zipf-trace", T)
+    n = args.warmup + args.steps
+    xs = torch.from_numpy(synth.normal_f32(g, (n, T, H)) + v).cuda()
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    rows = []
+    configs = [(0, 0)] if 0 in args.cache_slots else []
+    configs += [(s, min(p, s)) for s in args.cache_slots if s > 0 for p in args.prefetch]
+    for slots, prefetch in dict.fromkeys(configs):
+        moe = tq.MoeLayer("q4_k", H, shape["ffn"], torch.from_numpy(wr).cuda(), pinned, shared,
+                          top_k=k, copy_stream=torch.cuda.Stream())
+        ws = torch.empty(moe.workspace_bytes(T), dtype=torch.uint8, device="cuda")
+        cache = moe.attach_cache(slots, prefetch) if slots else None
+        stream = torch.cuda.Stream()
+        routed = 0
+        with torch.cuda.stream(stream):
+            for i in range(args.warmup):
+                moe(xs[i], out=y, ws=ws)
+            torch.cuda.synchronize()
+            s0 = cache.stats() if cache else None
+            t0 = time.perf_counter()
+            for i in range(args.warmup, n):
+                moe(xs[i], out=y, ws=ws)
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - t0) / args.steps
+            if not cache:  # the experts each step routes to (all copied without a cache)
+                for i in range(args.warmup, n):
+                    moe(xs[i], out=y, ws=ws, routing=dict(counts=counts))
+                    routed += int((counts > 0).sum().item())
+        row = {"slots": slots, "prefetch": prefetch,
+               "device_gb": round(slots * expert_bytes / 1e9, 2),
+               "ms_per_step": round(dt * 1000, 3), "tokens_s": round(T / dt, 1)}
+        if cache:
+            s1 = cache.stats()
+            d = {f: s1[f] - s0[f] for f in s1}
+            routed = d["hits"] + d["misses"] + d["fallbacks"]
+            row.update(h2d_mb_per_step=round(d["bytes_copied"] / args.steps / 1e6, 1),
+                       hit_rate=round(d["hits"] / max(routed, 1), 4),
+                       prefetched_per_step=round(d["prefetched"] / args.steps, 2),
+                       prefetch_hits_per_step=round(d["prefetch_hits"] / args.steps, 2))
+            moe.detach_cache()
+        else:
+            row.update(h2d_mb_per_step=round(routed * expert_bytes / args.steps / 1e6, 1),
+                       hit_rate=0.0)
+        rows.append(row)
+        del moe, ws
+        torch.cuda.empty_cache()
+    return rows
 
 
 def calibrate_copy(torch):

@@ -25,7 +25,11 @@
  *
  * Conventions for every call below:
  *   - Pointers are device pointers (memory the caller allocated on the current HIP device)
- *     unless stated otherwise. The caller owns every buffer; the library allocates nothing.
+ *     unless stated otherwise. The caller owns every buffer; the library allocates no device
+ *     memory. One exception on the host: the host-resident MoE variant (experts_on_host) keeps,
+ *     per calling thread and device, a small pinned host buffer (the active-expert list and the
+ *     call's expert-pointer table) and HIP events, made on first use and kept until the thread
+ *     ends.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Every call only
  *     enqueues work on it and returns; results are ready when the stream is synchronized.
  *   - Arguments are checked before anything is enqueued. On a non-TQ_OK status nothing was
@@ -200,6 +204,8 @@ typedef struct {
                                     to the workspace on every call (see tq_moe_ffn) */
   void *copy_stream;             /* hipStream_t for those copies (experts_on_host only) */
   int path;                      /* TQ_PATH_AUTO / TQ_PATH_F32 / TQ_PATH_BF16_MFMA */
+  void *expert_cache;            /* NULL, or a residency cache set up by tq_expert_cache_init
+                                    for this descriptor (experts_on_host only) */
 } tq_moe_desc;
 
 typedef struct {                 /* optional copies of the routing, device pointers or NULL */
@@ -210,6 +216,53 @@ typedef struct {                 /* optional copies of the routing, device point
   int32_t *offsets;              /* [n_experts + 1] exclusive prefix sum of counts */
   int32_t *pairs;                /* [T*k] t*k + j, sorted by (expert, t) */
 } tq_moe_routing;
+
+/*
+ * Expert residency cache for the host-resident variant: device slots that keep routed experts
+ * between calls, so that an expert used again is not copied again, plus prefetch of the experts
+ * most likely to be routed next (the pages' expert streaming: "Titan Engine" page, "MoE expert
+ * streaming" -- an LRU expert cache in VRAM, smart prefetch, asynchronous loading; "Show HN" page,
+ * "Technical highlights" -- double-buffered streaming that overlaps transfers with compute).
+ *
+ * The caller owns both pieces of memory: `state` (host, tq_expert_cache_state_bytes) and
+ * `slot_mem` (device, slots * tq_expert_cache_slot_bytes, 256-byte aligned). Setting
+ * desc->expert_cache = state makes every tq_moe_ffn call with experts_on_host use it:
+ *   - a routed expert held by a slot is read there (a hit: no copy);
+ *   - otherwise it is copied into the least recently used slot that this call does not use (a
+ *     miss), or, when every slot is taken by the call, into the workspace's staging area as
+ *     without a cache (a fallback);
+ *   - then up to `prefetch` experts that are not resident are copied, highest score first (every
+ *     call multiplies each expert's score by 7/8 and adds 1 for each expert it routes to), each
+ *     into an empty slot or over the lowest-scored expert in a slot this call does not read, and
+ *     never over an expert with the same or a higher score. Prefetches run on the copy stream
+ *     behind this call's demand copies, so they overlap with this call's compute.
+ * Each slot has an event: the call's kernels wait for the copies of the slots they read, and a
+ * slot is overwritten only after the compute stream has finished the calls before the current
+ * one. Results are bitwise those of the call without a cache. One state per descriptor and per
+ * device; calls that use one state must not overlap (they share its slots and bookkeeping).
+ */
+typedef struct {
+  int64_t calls;         /* tq_moe_ffn calls that used the cache */
+  int64_t hits;          /* routed experts found in a slot */
+  int64_t misses;        /* routed experts copied into a slot when routed */
+  int64_t fallbacks;     /* routed experts staged in the workspace (no free slot this call) */
+  int64_t prefetched;    /* experts copied ahead of their use */
+  int64_t prefetch_hits; /* hits on a prefetched slot before any other use of it */
+  int64_t bytes_copied;  /* host-to-device bytes of all the copies above */
+} tq_expert_cache_stats;
+
+/* Device bytes of one slot (one routed expert's three blobs, 256-byte aligned); 0 if invalid. */
+size_t tq_expert_cache_slot_bytes(const tq_moe_desc *desc);
+/* Host bytes of the cache state for `slots` slots (1..4096); 0 if invalid. */
+size_t tq_expert_cache_state_bytes(const tq_moe_desc *desc, int64_t slots);
+/* Set up `state` (empty slots, zero statistics) on the current device; creates one HIP event per
+ * slot. prefetch: 0..slots experts copied ahead per call. */
+int tq_expert_cache_init(void *state, size_t state_bytes, const tq_moe_desc *desc, int64_t slots,
+                         int64_t prefetch, void *slot_mem, size_t slot_mem_bytes);
+/* Counters since tq_expert_cache_init. */
+int tq_expert_cache_stats_get(const void *state, tq_expert_cache_stats *out);
+/* Releases the state's events (the caller then frees both pieces of memory). */
+int tq_expert_cache_destroy(void *state);
 
 /* Workspace bytes tq_moe_ffn needs for `tokens` tokens (0 if the descriptor is invalid). */
 size_t tq_moe_workspace_bytes(const tq_moe_desc *desc, int64_t tokens);

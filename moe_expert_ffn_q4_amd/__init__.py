@@ -56,7 +56,12 @@ class MoeDesc(C.Structure):
     _fields_ = [("type", _int), ("hidden", _i64), ("ffn", _i64), ("n_experts", _i64),
                 ("top_k", _i64), ("router_w", _vp), ("experts", _vp), ("experts_host", _vp),
                 ("shared", Expert), ("renormalize", _int), ("experts_on_host", _int),
-                ("copy_stream", _vp), ("path", _int)]
+                ("copy_stream", _vp), ("path", _int), ("expert_cache", _vp)]
+
+
+class ExpertCacheStats(C.Structure):
+    _fields_ = [("calls", _i64), ("hits", _i64), ("misses", _i64), ("fallbacks", _i64),
+                ("prefetched", _i64), ("prefetch_hits", _i64), ("bytes_copied", _i64)]
 
 
 class ChainOp(C.Structure):
@@ -114,6 +119,17 @@ def _declare(L: C.CDLL) -> None:
         L.tq_moe_ffn_stages.argtypes = [C.POINTER(MoeDesc), _vp, _i64, _vp, _vp, C.c_size_t,
                                         C.POINTER(MoeRouting), _int, _vp]
         L.tq_moe_ffn_stages.restype = _int
+        L.tq_expert_cache_slot_bytes.argtypes = [C.POINTER(MoeDesc)]
+        L.tq_expert_cache_slot_bytes.restype = C.c_size_t
+        L.tq_expert_cache_state_bytes.argtypes = [C.POINTER(MoeDesc), _i64]
+        L.tq_expert_cache_state_bytes.restype = C.c_size_t
+        L.tq_expert_cache_init.argtypes = [_vp, C.c_size_t, C.POINTER(MoeDesc), _i64, _i64, _vp,
+                                           C.c_size_t]
+        L.tq_expert_cache_init.restype = _int
+        L.tq_expert_cache_stats_get.argtypes = [_vp, C.POINTER(ExpertCacheStats)]
+        L.tq_expert_cache_stats_get.restype = _int
+        L.tq_expert_cache_destroy.argtypes = [_vp]
+        L.tq_expert_cache_destroy.restype = _int
 
 
 def _check(rc: int) -> None:
@@ -319,6 +335,19 @@ class MoeLayer:
         self.desc.copy_stream = copy_stream.cuda_stream if copy_stream is not None else None
         self.desc.path = path
 
+    def attach_cache(self, slots: int, prefetch: int = 0) -> "ExpertCache":
+        """A residency cache of `slots` device slots (host-resident experts only), used by every
+        later call of this layer; returns it (its stats() count hits, misses, prefetches)."""
+        self.cache = ExpertCache(self, slots, prefetch)
+        self.desc.expert_cache = self.cache.state_ptr
+        return self.cache
+
+    def detach_cache(self) -> None:
+        self.desc.expert_cache = None
+        if getattr(self, "cache", None) is not None:
+            self.cache.close()
+            self.cache = None
+
     def workspace_bytes(self, tokens: int) -> int:
         """Bytes of workspace tq_moe_ffn needs (0 when the descriptor is invalid)."""
         return int(lib().tq_moe_workspace_bytes(C.byref(self.desc), tokens))
@@ -348,3 +377,33 @@ class MoeLayer:
             _check(lib().tq_moe_ffn_stages(C.byref(self.desc), x.data_ptr(), T, _ptr(out),
                                            _ptr(ws), nbytes, rr, stages, _stream(stream)))
         return out
+
+
+class ExpertCache:
+    """The device slots and host state of a residency cache (tq_expert_cache_init) for one
+    host-resident MoE layer. Keeps its memory alive; close() releases the state's events."""
+
+    def __init__(self, layer: MoeLayer, slots: int, prefetch: int = 0):
+        L = lib()
+        nstate = int(L.tq_expert_cache_state_bytes(C.byref(layer.desc), slots))
+        nslot = int(L.tq_expert_cache_slot_bytes(C.byref(layer.desc)))
+        if not nstate or not nslot:
+            raise TQError(1, "invalid layer descriptor or slot count for an expert cache")
+        self._state = (C.c_char * (nstate + 64))()  # host memory, 64-byte aligned below
+        base = C.addressof(self._state)
+        self.state_ptr = (base + 63) & ~63
+        self.slots = torch.empty(slots * nslot, dtype=torch.uint8, device=layer.router_w.device)
+        _check(L.tq_expert_cache_init(self.state_ptr, nstate, C.byref(layer.desc), slots, prefetch,
+                                      self.slots.data_ptr(), self.slots.numel()))
+        self.open = True
+
+    def stats(self) -> dict:
+        s = ExpertCacheStats()
+        _check(lib().tq_expert_cache_stats_get(self.state_ptr, C.byref(s)))
+        return {f: getattr(s, f) for f, _ in ExpertCacheStats._fields_}
+
+    def close(self) -> None:
+        if self.open:
+            torch.cuda.synchronize()
+            _check(lib().tq_expert_cache_destroy(self.state_ptr))
+            self.open = False

@@ -2,9 +2,12 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <atomic>
 #include <chrono>
+#include <cstdint>
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "tq.h"
@@ -303,7 +306,7 @@ static bool host_experts_ok(const tq_moe_desc *d) {
 // events (one per staged expert, one for "the compute stream is done with the staging area").
 struct HostPathState {
   int device = -1;
-  int *list = nullptr;
+  int *list = nullptr;  // the active-expert list, then (cache only) the call's expert table
   size_t list_ints = 0;
   std::vector<hipEvent_t> copied;
   hipEvent_t ready = nullptr;
@@ -343,6 +346,71 @@ static int host_path_state(int64_t list_ints, int n_events, HostPathState *&out)
   return TQ_OK;
 }
 
+// ---- expert residency cache (state in caller memory) ----------------------------------------------
+
+constexpr uint64_t kCacheMagic = 0x5451455843414348ull;  // "TQEXCACH"
+
+struct CacheHeader {
+  uint64_t magic;
+  int device, type;
+  int64_t hidden, ffn, n_experts, expert_bytes, gate_bytes;
+  int64_t slots, prefetch, stride;
+  uint8_t *mem;
+  int64_t clock;
+  tq_expert_cache_stats stats;
+};
+
+// The arrays that follow the header, each 64-byte aligned.
+struct CacheView {
+  CacheHeader *h;
+  int32_t *slot_expert;  // [slots] expert held, -1: empty
+  int64_t *slot_used;    // [slots] clock of the last call that read or filled it
+  hipEvent_t *slot_ready;  // [slots] recorded after the slot's latest copy
+  uint8_t *slot_pref;    // [slots] 1: filled by a prefetch and not read since
+  int32_t *expert_slot;  // [n_experts] slot holding the expert, -1: none
+  float *score;          // [n_experts]
+};
+
+static size_t cache_layout(int64_t slots, int64_t E, size_t off[6]) {
+  auto up = [](size_t v) { return (v + 63) & ~(size_t)63; };
+  size_t o = up(sizeof(CacheHeader));
+  off[0] = o; o = up(o + 4 * (size_t)slots);
+  off[1] = o; o = up(o + 8 * (size_t)slots);
+  off[2] = o; o = up(o + sizeof(hipEvent_t) * (size_t)slots);
+  off[3] = o; o = up(o + (size_t)slots);
+  off[4] = o; o = up(o + 4 * (size_t)E);
+  off[5] = o; o = up(o + 4 * (size_t)E);
+  return o;
+}
+
+static CacheView cache_view(void *state) {
+  CacheView v{};
+  v.h = (CacheHeader *)state;
+  size_t off[6];
+  cache_layout(v.h->slots, v.h->n_experts, off);
+  char *b = (char *)state;
+  v.slot_expert = (int32_t *)(b + off[0]);
+  v.slot_used = (int64_t *)(b + off[1]);
+  v.slot_ready = (hipEvent_t *)(b + off[2]);
+  v.slot_pref = (uint8_t *)(b + off[3]);
+  v.expert_slot = (int32_t *)(b + off[4]);
+  v.score = (float *)(b + off[5]);
+  return v;
+}
+
+// The state belongs to this descriptor's expert shape and to the current device.
+static int cache_check(const tq_moe_desc *d, const tq::MoeShape &s, CacheView &v) {
+  const CacheHeader *h = (const CacheHeader *)d->expert_cache;
+  if (h->magic != kCacheMagic) return fail(TQ_EINVAL, "tq_moe_ffn: expert_cache is not an initialized cache state");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(TQ_EDEVICE, "tq_moe_ffn: no current device");
+  if (h->device != dev || h->type != s.type || h->hidden != s.hidden || h->ffn != s.ffn ||
+      h->n_experts != s.n_experts || h->expert_bytes != s.expert_bytes)
+    return fail(TQ_EINVAL, "tq_moe_ffn: expert_cache was set up for another layer shape or device");
+  v = cache_view(d->expert_cache);
+  return TQ_OK;
+}
+
 // Expert products with the routed experts in pinned host memory. The active-expert list is read
 // back (one synchronisation of `st`); each selected expert is then copied into its staging slot
 // on the copy stream, followed by an event. On the fp32 path the shared expert (resident) runs
@@ -354,9 +422,17 @@ static int host_resident_experts(const tq_moe_desc *d, const tq::MoePlan &p,
   const tq::MoeShape &s = p.s;
   const int E = (int)s.n_experts;
   const int S = p.act_stride;
-  const int64_t list_ints = 3 * (int64_t)S + 1;
+  CacheView cv{};
+  const bool cached = d->expert_cache != nullptr;
+  if (cached) {
+    const int rc = cache_check(d, s, cv);
+    if (rc != TQ_OK) return rc;
+  }
+  // pinned host memory: the active-expert list, then (with a cache) the call's expert table
+  const int64_t list_ints = (3 * (int64_t)S + 1 + 1) & ~(int64_t)1;
+  const int64_t table_ints = cached ? E * (int64_t)(sizeof(tq::MoeExpertPtrs) / 4) : 0;
   HostPathState *hs = nullptr;
-  int rc = host_path_state(list_ints, p.max_active, hs);
+  int rc = host_path_state(list_ints + table_ints, p.max_active, hs);
   if (rc != TQ_OK) return rc;
   int *act = hs->list, *n_active = hs->list + 3 * S;
   if (hipMemcpyAsync(act, ws + p.off_act, (size_t)(3 * S) * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
@@ -365,34 +441,151 @@ static int host_resident_experts(const tq_moe_desc *d, const tq::MoePlan &p,
     return fail(TQ_EDEVICE, "tq_moe_ffn: reading the active-expert list back failed");
   const int na = *n_active;
   if (na < 0 || na > p.max_active) return fail(TQ_EDEVICE, "tq_moe_ffn: corrupt active-expert list");
+  for (int a = 0; a < na; ++a)
+    if (act[a] < 0 || act[a] > E)
+      return fail(TQ_EDEVICE, "tq_moe_ffn: active-expert list holds id %d (of %d experts)", act[a], E);
   hipStream_t cs = d->copy_stream ? (hipStream_t)d->copy_stream : st;
   uint8_t *staging = (uint8_t *)(ws + p.off_stage);
-  // the staging area is free once the compute stream's earlier work (a previous call) is done
+  // copies may overwrite the staging area and the cache slots once the compute stream's earlier
+  // work (the calls before this one) is done
   if (hipEventRecord(hs->ready, st) != hipSuccess || hipStreamWaitEvent(cs, hs->ready, 0) != hipSuccess)
     return fail(TQ_EDEVICE, "tq_moe_ffn: event record / wait failed");
   const int64_t bytes[3] = {s.gate_bytes, s.gate_bytes, s.expert_bytes - 2 * s.gate_bytes};
   const int64_t off[3] = {0, s.gate_bytes, 2 * s.gate_bytes};
-  int last_copied = -1;
-  for (int a = 0; a < na; ++a) {
-    const int e = act[a];
-    if (e == E) continue;  // the shared expert stays on the device
-    if (e < 0 || e > E)
-      return fail(TQ_EDEVICE, "tq_moe_ffn: active-expert list holds id %d (of %d experts)", e, E);
+  auto copy_expert = [&](int e, uint8_t *dst, hipEvent_t done) -> int {
     const tq_expert &hx = d->experts_host[e];
     const void *src[3] = {hx.gate, hx.up, hx.down};
     for (int m = 0; m < 3; ++m)
-      if (hipMemcpyAsync(staging + (int64_t)a * p.stage_stride + off[m], src[m], (size_t)bytes[m],
-                         hipMemcpyHostToDevice, cs) != hipSuccess)
+      if (hipMemcpyAsync(dst + off[m], src[m], (size_t)bytes[m], hipMemcpyHostToDevice, cs) != hipSuccess)
         return fail(TQ_EDEVICE, "tq_moe_ffn: expert copy failed");
-    if (hipEventRecord(hs->copied[a], cs) != hipSuccess)
-      return fail(TQ_EDEVICE, "tq_moe_ffn: event record failed");
-    last_copied = a;
+    if (hipEventRecord(done, cs) != hipSuccess) return fail(TQ_EDEVICE, "tq_moe_ffn: event record failed");
+    return TQ_OK;
+  };
+  std::vector<hipEvent_t> wait_ev((size_t)na, nullptr);  // what slot a's kernels wait for
+  const tq::MoeExpertPtrs *dev_table = reinterpret_cast<const tq::MoeExpertPtrs *>(d->experts);
+  const uint8_t *stage_arg = staging;
+  if (!cached) {
+    for (int a = 0; a < na; ++a) {
+      if (act[a] == E) continue;  // the shared expert stays on the device
+      rc = copy_expert(act[a], staging + (int64_t)a * p.stage_stride, hs->copied[a]);
+      if (rc != TQ_OK) return rc;
+      wait_ev[a] = hs->copied[a];
+    }
+  } else {
+    CacheHeader &h = *cv.h;
+    h.clock += 1;
+    h.stats.calls += 1;
+    for (int e = 0; e < E; ++e) cv.score[e] *= 0.875f;
+    for (int a = 0; a < na; ++a)
+      if (act[a] != E) cv.score[act[a]] += 1.f;
+    std::vector<char> used((size_t)h.slots, 0);
+    for (int a = 0; a < na; ++a)  // slots this call reads are not victims
+      if (act[a] != E && cv.expert_slot[act[a]] >= 0) used[cv.expert_slot[act[a]]] = 1;
+    auto *table = reinterpret_cast<tq::MoeExpertPtrs *>(hs->list + list_ints);
+    for (int e = 0; e < E; ++e) table[e] = tq::MoeExpertPtrs{{nullptr, nullptr, nullptr}};
+    for (int a = 0; a < na; ++a) {
+      const int e = act[a];
+      if (e == E) continue;
+      uint8_t *dst;
+      const int sl = cv.expert_slot[e];
+      if (sl >= 0) {  // hit
+        h.stats.hits += 1;
+        if (cv.slot_pref[sl]) {
+          h.stats.prefetch_hits += 1;
+          cv.slot_pref[sl] = 0;
+        }
+        cv.slot_used[sl] = h.clock;
+        dst = h.mem + (int64_t)sl * h.stride;
+        wait_ev[a] = cv.slot_ready[sl];
+      } else {
+        int victim = -1;
+        int64_t oldest = INT64_MAX;
+        for (int64_t q = 0; q < h.slots; ++q) {
+          if (used[q]) continue;
+          if (cv.slot_expert[q] < 0) {
+            victim = (int)q;
+            break;
+          }
+          if (cv.slot_used[q] < oldest) {
+            oldest = cv.slot_used[q];
+            victim = (int)q;
+          }
+        }
+        if (victim < 0) {  // every slot is read by this call: stage it as without a cache
+          dst = staging + (int64_t)a * p.stage_stride;
+          rc = copy_expert(e, dst, hs->copied[a]);
+          wait_ev[a] = hs->copied[a];
+          h.stats.fallbacks += 1;
+        } else {
+          if (cv.slot_expert[victim] >= 0) cv.expert_slot[cv.slot_expert[victim]] = -1;
+          cv.slot_expert[victim] = e;
+          cv.expert_slot[e] = victim;
+          cv.slot_pref[victim] = 0;
+          cv.slot_used[victim] = h.clock;
+          used[victim] = 1;
+          dst = h.mem + (int64_t)victim * h.stride;
+          rc = copy_expert(e, dst, cv.slot_ready[victim]);
+          wait_ev[a] = cv.slot_ready[victim];
+          h.stats.misses += 1;
+        }
+        if (rc != TQ_OK) return rc;
+        h.stats.bytes_copied += s.expert_bytes;
+      }
+      table[e] = tq::MoeExpertPtrs{{dst + off[0], dst + off[1], dst + off[2]}};
+    }
+    // prefetch: the highest-scored experts not resident, into slots this call does not read,
+    // each over the lowest-scored resident expert, never over a higher score
+    if (h.prefetch > 0) {
+      std::vector<std::pair<float, int>> cand;
+      for (int e = 0; e < E; ++e)
+        if (cv.expert_slot[e] < 0 && cv.score[e] > 0.f) cand.push_back({cv.score[e], e});
+      const size_t want = std::min(cand.size(), (size_t)h.prefetch);
+      std::partial_sort(cand.begin(), cand.begin() + want, cand.end(),
+                        [](const std::pair<float, int> &a, const std::pair<float, int> &b) {
+                          return a.first > b.first || (a.first == b.first && a.second < b.second);
+                        });
+      for (size_t i = 0; i < want; ++i) {
+        int victim = -1;
+        float low = 0.f;
+        for (int64_t q = 0; q < h.slots; ++q) {
+          if (used[q]) continue;
+          if (cv.slot_expert[q] < 0) {
+            victim = (int)q;
+            low = -1.f;
+            break;
+          }
+          const float sc = cv.score[cv.slot_expert[q]];
+          if (victim < 0 || sc < low) {
+            victim = (int)q;
+            low = sc;
+          }
+        }
+        if (victim < 0 || low >= cand[i].first) break;
+        const int e = cand[i].second;
+        if (cv.slot_expert[victim] >= 0) cv.expert_slot[cv.slot_expert[victim]] = -1;
+        cv.slot_expert[victim] = e;
+        cv.expert_slot[e] = victim;
+        cv.slot_pref[victim] = 1;
+        cv.slot_used[victim] = h.clock;
+        used[victim] = 1;
+        rc = copy_expert(e, h.mem + (int64_t)victim * h.stride, cv.slot_ready[victim]);
+        if (rc != TQ_OK) return rc;
+        h.stats.prefetched += 1;
+        h.stats.bytes_copied += s.expert_bytes;
+      }
+    }
+    // the call's expert table, on the compute stream ahead of the kernels that read it
+    if (hipMemcpyAsync(ws + p.off_table, table, (size_t)E * sizeof(tq::MoeExpertPtrs),
+                       hipMemcpyHostToDevice, st) != hipSuccess)
+      return fail(TQ_EDEVICE, "tq_moe_ffn: expert table copy failed");
+    dev_table = reinterpret_cast<const tq::MoeExpertPtrs *>(ws + p.off_table);
+    stage_arg = nullptr;
   }
-  const auto *dev_table = reinterpret_cast<const tq::MoeExpertPtrs *>(d->experts);
-  if (s.mfma || p.qmm) {  // one grouped launch once every copy has landed
-    if (last_copied >= 0 && hipStreamWaitEvent(st, hs->copied[last_copied], 0) != hipSuccess)
-      return fail(TQ_EDEVICE, "tq_moe_ffn: event wait failed");
-    return launched(tq::launch_moe_experts(p, dev_table, shared, staging, x, ws, st),
+  if (s.mfma || p.qmm) {  // one grouped launch once every copy it reads has landed
+    for (int a = 0; a < na; ++a)
+      if (wait_ev[a] && hipStreamWaitEvent(st, wait_ev[a], 0) != hipSuccess)
+        return fail(TQ_EDEVICE, "tq_moe_ffn: event wait failed");
+    return launched(tq::launch_moe_experts(p, dev_table, shared, stage_arg, x, ws, st),
                     "tq_moe_ffn experts");
   }
   auto slot_range = [&](int a) {
@@ -401,17 +594,101 @@ static int host_resident_experts(const tq_moe_desc *d, const tq::MoePlan &p,
   for (int a = 0; a < na; ++a)  // the shared expert first: it needs no copy
     if (act[a] == E) {
       const tq::SlotRange r = slot_range(a);
-      rc = tq::launch_moe_experts(p, dev_table, shared, staging, x, ws, st, &r);
+      rc = tq::launch_moe_experts(p, dev_table, shared, stage_arg, x, ws, st, &r);
       if (rc) return launched(rc, "tq_moe_ffn experts");
     }
   for (int a = 0; a < na; ++a) {
     if (act[a] == E) continue;
-    if (hipStreamWaitEvent(st, hs->copied[a], 0) != hipSuccess)
+    if (hipStreamWaitEvent(st, wait_ev[a], 0) != hipSuccess)
       return fail(TQ_EDEVICE, "tq_moe_ffn: event wait failed");
     const tq::SlotRange r = slot_range(a);
-    rc = tq::launch_moe_experts(p, dev_table, shared, staging, x, ws, st, &r);
+    rc = tq::launch_moe_experts(p, dev_table, shared, stage_arg, x, ws, st, &r);
     if (rc) return launched(rc, "tq_moe_ffn experts");
   }
+  return TQ_OK;
+}
+
+size_t tq_expert_cache_slot_bytes(const tq_moe_desc *desc) {
+  tq::MoeShape s;
+  if (moe_check(desc, 1, &s) != TQ_OK) return 0;
+  return (size_t)tq::align256(s.expert_bytes);
+}
+
+size_t tq_expert_cache_state_bytes(const tq_moe_desc *desc, int64_t slots) {
+  tq::MoeShape s;
+  if (slots < 1 || slots > 4096 || moe_check(desc, 1, &s) != TQ_OK) return 0;
+  size_t off[6];
+  return cache_layout(slots, s.n_experts, off);
+}
+
+int tq_expert_cache_init(void *state, size_t state_bytes, const tq_moe_desc *desc, int64_t slots,
+                         int64_t prefetch, void *slot_mem, size_t slot_mem_bytes) {
+  tq::MoeShape s;
+  int rc = moe_check(desc, 1, &s);
+  if (rc != TQ_OK) return rc;
+  if (!state || !slot_mem) return fail(TQ_EINVAL, "tq_expert_cache_init: null state or slot memory");
+  if (slots < 1 || slots > 4096 || prefetch < 0 || prefetch > slots)
+    return fail(TQ_ESHAPE, "tq_expert_cache_init: slots=%lld prefetch=%lld (need 1..4096, 0..slots)",
+                (long long)slots, (long long)prefetch);
+  if (!aligned(state, 64) || !aligned(slot_mem, 256))
+    return fail(TQ_EALIGN, "tq_expert_cache_init: state 64-byte and slot memory 256-byte alignment needed");
+  size_t off[6];
+  if (state_bytes < cache_layout(slots, s.n_experts, off))
+    return fail(TQ_ENOSPC, "tq_expert_cache_init: state of %zu bytes too small", state_bytes);
+  const int64_t stride = tq::align256(s.expert_bytes);
+  if (slot_mem_bytes < (size_t)(slots * stride))
+    return fail(TQ_ENOSPC, "tq_expert_cache_init: slot memory of %zu bytes, %lld needed", slot_mem_bytes,
+                (long long)(slots * stride));
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(TQ_EDEVICE, "tq_expert_cache_init: no current device");
+  CacheHeader *h = (CacheHeader *)state;
+  *h = CacheHeader{};
+  h->device = dev;
+  h->type = (int)s.type;
+  h->hidden = s.hidden;
+  h->ffn = s.ffn;
+  h->n_experts = s.n_experts;
+  h->expert_bytes = s.expert_bytes;
+  h->gate_bytes = s.gate_bytes;
+  h->slots = slots;
+  h->prefetch = prefetch;
+  h->stride = stride;
+  h->mem = (uint8_t *)slot_mem;
+  CacheView v = cache_view(state);
+  for (int64_t q = 0; q < slots; ++q) {
+    v.slot_expert[q] = -1;
+    v.slot_used[q] = 0;
+    v.slot_pref[q] = 0;
+    v.slot_ready[q] = nullptr;
+  }
+  for (int64_t e = 0; e < s.n_experts; ++e) {
+    v.expert_slot[e] = -1;
+    v.score[e] = 0.f;
+  }
+  for (int64_t q = 0; q < slots; ++q)
+    if (hipEventCreateWithFlags(&v.slot_ready[q], hipEventDisableTiming) != hipSuccess) {
+      for (int64_t r = 0; r < q; ++r) (void)hipEventDestroy(v.slot_ready[r]);
+      return fail(TQ_EDEVICE, "tq_expert_cache_init: event creation failed");
+    }
+  h->magic = kCacheMagic;
+  return TQ_OK;
+}
+
+int tq_expert_cache_stats_get(const void *state, tq_expert_cache_stats *out) {
+  if (!state || !out) return fail(TQ_EINVAL, "tq_expert_cache_stats_get: null argument");
+  const CacheHeader *h = (const CacheHeader *)state;
+  if (h->magic != kCacheMagic) return fail(TQ_EINVAL, "tq_expert_cache_stats_get: not a cache state");
+  *out = h->stats;
+  return TQ_OK;
+}
+
+int tq_expert_cache_destroy(void *state) {
+  if (!state) return fail(TQ_EINVAL, "tq_expert_cache_destroy: null state");
+  CacheHeader *h = (CacheHeader *)state;
+  if (h->magic != kCacheMagic) return fail(TQ_EINVAL, "tq_expert_cache_destroy: not a cache state");
+  CacheView v = cache_view(state);
+  for (int64_t q = 0; q < h->slots; ++q) (void)hipEventDestroy(v.slot_ready[q]);
+  h->magic = 0;
   return TQ_OK;
 }
 
@@ -432,6 +709,10 @@ int tq_moe_ffn_stages(const tq_moe_desc *d, const float *x, int64_t tokens, floa
     return fail(TQ_ENOSPC, "tq_moe_ffn: workspace of %zu bytes, %lld needed", ws_bytes, (long long)p.bytes);
   if (s.experts_on_host && (stages & TQ_MOE_EXPERTS) && !host_experts_ok(d))
     return fail(TQ_EINVAL, "tq_moe_ffn: experts_host entries must all be non-null");
+  if (d->expert_cache && !s.experts_on_host)
+    return fail(TQ_EINVAL, "tq_moe_ffn: expert_cache is for host-resident experts only");
+  if (d->expert_cache && ((const CacheHeader *)d->expert_cache)->magic != kCacheMagic)
+    return fail(TQ_EINVAL, "tq_moe_ffn: expert_cache is not an initialized cache state");
   hipStream_t st = (hipStream_t)stream;
   char *ws = (char *)workspace;
   if (stages & TQ_MOE_ROUTE) {

@@ -36,7 +36,7 @@ struct MoePlan {
   int gu_rg, gu_ks, gu_upk, gu_waves, gu_upw;
   int d_rg, d_ks, d_upk, d_waves, d_upw;
   int64_t off_rpart, off_logits, off_ids, off_wts, off_counts, off_offsets, off_pairs, off_inv,
-      off_act, off_nact, off_gu, off_h, off_o, off_stage, off_ctr;
+      off_act, off_nact, off_gu, off_h, off_o, off_stage, off_ctr, off_table;
   int64_t off_xb, off_hb, off_chunks, off_nchunks;  // matrix-core paths only
   int64_t off_xsplit, off_hsplit;                    // fp16 split rows (qmm)
   int max_chunks;

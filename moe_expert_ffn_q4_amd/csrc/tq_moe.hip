@@ -817,6 +817,8 @@ MoePlan plan_moe(const MoeShape &s) {
   p.off_ctr = take((int64_t)p.nctr * 4);
   p.stage_stride = align256(s.expert_bytes);
   p.off_stage = take(s.experts_on_host ? (int64_t)(p.max_active) * p.stage_stride : 0);
+  // host-resident experts with a residency cache: the call's device table of expert pointers
+  p.off_table = take(s.experts_on_host ? E * (int64_t)sizeof(MoeExpertPtrs) : 0);
   p.bytes = o;
   return p;
 }

@@ -91,6 +91,20 @@ def router_weights(g: np.random.Generator, n_experts: int, hidden: int) -> np.nd
     return normal_f32(g, (n_experts, hidden), 1.0 / np.sqrt(hidden))
 
 
+def zipf_router(g: np.random.Generator, n_experts: int, hidden: int, s: float = 1.0,
+                spread: float = 0.5):
+    """(router weights [E][H], offset v [H]) for routing traces with Zipf-like expert popularity.
+    Activations are drawn as x = z + v with z ~ N(0, 1): the logit of expert e is then about
+    N(0, 2) + b_e with b_e = spread * log(1 / rank_e^s), the ranks 1..E in a random order, so the
+    experts are chosen with a popularity that falls off with their rank."""
+    base = router_weights(g, n_experts, hidden).astype(np.float64)
+    v = g.choice(np.array([-1.0, 1.0]), hidden)  # |v|^2 = hidden
+    ranks = g.permutation(n_experts).astype(np.float64) + 1.0
+    b = -spread * s * np.log(ranks)
+    w = base + np.outer(b, v) / hidden
+    return w.astype(np.float32), v.astype(np.float32)
+
+
 # ---------------------------------------------------------------------------------------------
 # Workload shapes (the five configurations; sizes only).
 # ---------------------------------------------------------------------------------------------
