@@ -286,14 +286,14 @@ def build_dense_model(tq, synth, torch, batch, seed):
     return layers
 
 
-def gemv_kernel_name(batch):
+def gemv_kernel_name(tq, batch):
     """The kernel that tq_gemv runs for the 8B shapes (k = 4096 and 14336) at this batch, given
-    its workspace (the int8 kernel takes k >= 16384 unless TQ_GEMV_I8=2)."""
+    its workspace (the int8 kernel takes k >= 16384 unless its knob is set to 2)."""
     if batch == 1:
-        if os.environ.get("TQ_GEMV_I8", "1") == "2":
+        if tq.get_knob("gemv_i8") == 2:
             return "tq_gemv Q4_K batch 1 (tq::k_gemv_i8, after tq::k_x_digits)"
         return "tq_gemv Q4_K batch 1 (tq::k_gemv_kl)"
-    if batch <= 32 and os.environ.get("TQ_GEMV_QMM", "1") != "0":
+    if batch <= 32 and tq.get_knob("gemv_qmm") != 0:
         return f"tq_gemv Q4_K batch {batch} (tq::k_qmm_dense, after tq::k_split_rows)"
     return f"tq_gemv Q4_K batch {batch} (tq::k_gemv)"
 
@@ -547,7 +547,7 @@ def moe_bench(args, torch, tq, synth):
     else:
         stage_bytes = active * eb + 4 * T * H * 2
         achieved = stage_bytes / stage_s / 1e9
-        if T > 1 and os.environ.get("TQ_MOE_QMM", "1") != "0":
+        if T > 1 and tq.get_knob("moe_qmm") != 0:
             kern = ("tq_moe_ffn expert stage: k_qmm gate/up+SwiGLU and down on the fp16 matrix "
                     "cores, fp32-accurate (with the row splits and the chunk table)")
         elif T == 1:
@@ -1037,7 +1037,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": gemv_kernel_name(args.batch),
+                     "kernel": gemv_kernel_name(tq, args.batch),
                      "avg_launch_us": round(avg_launch_s * 1e6, 3)},
     }
     if args.calibrate_copy:

@@ -369,6 +369,47 @@ int tq_chain_status(void *plan, void *stream);
 /* Text of the last non-TQ_OK status returned on this thread ("" if none). */
 const char *tq_last_error(void);
 
+/*
+ * Tuning knobs -- for tests and tuning sweeps only. Every knob's default is the production choice
+ * (the kernel selection and launch shapes measured to be fastest on gfx950); an override changes
+ * which kernel or launch shape a call takes, and so possibly the result bits, never the contract
+ * (every path meets the same error bars). The knobs are process-wide and read on every call;
+ * set them while no call runs. Nothing else (no environment variable) changes what a call does.
+ *   tq_tuning_set(knob, value): value >= 0 overrides, value < 0 restores the default; TQ_EINVAL for
+ *   an unknown knob. tq_tuning_get(knob): the override, or -1 (default in effect or unknown knob).
+ */
+enum {
+  TQ_KNOB_GEMV_TARGET_WG = 0, /* lane-per-row GEMV: workgroups the k split aims for (1024) */
+  TQ_KNOB_GEMV_MAX_WAVES = 1, /* lane-per-row GEMV: most waves per workgroup (4) */
+  TQ_KNOB_GEMV_KLANE = 2, /* batch-1 Q4_K on the lanes-along-k kernel: 1 on (default), 0 off */
+  TQ_KNOB_KL_GROUPS = 3, /* lanes-along-k kernel: most lane groups per wave for short rows (4; 1 turns them off) */
+  TQ_KNOB_KL_ROWS = 4, /* lanes-along-k kernel: rows per pass, 2, 4 (default) or 8 */
+  TQ_KNOB_KL_TARGET_WAVES = 5, /* lanes-along-k kernel: waves the launch aims for (2048) */
+  TQ_KNOB_GEMM_F32M = 6, /* Q6_K / Q8_0 batches on the fp32 matrix cores: 1 default shapes, 0 never, 2 every batch */
+  TQ_KNOB_F32M_UPK = 7, /* fp32 matrix-core kernel: blocks per k slice (8) */
+  TQ_KNOB_GEMV_I8 = 8, /* int8 matrix-core batch-1 Q4_K GEMV: 1 from k = 16384 (default), 0 never, 2 always */
+  TQ_KNOB_I8_UPK = 9, /* int8 matrix-core kernel: blocks per k slice (4) */
+  TQ_KNOB_GEMV_I8S = 10, /* streaming int8 GEMV: 0 off (default), 1 on */
+  TQ_KNOB_I8S_NW = 11, /* streaming int8 GEMV: waves per workgroup (8) */
+  TQ_KNOB_I8S_D = 12, /* streaming int8 GEMV: blocks in flight per wave (4) */
+  TQ_KNOB_I8S_KS = 13, /* streaming int8 GEMV: k parts (0: chosen from k) */
+  TQ_KNOB_I8S_PART = 14, /* streaming int8 GEMV: least blocks per k part (4) */
+  TQ_KNOB_MOE_QMM = 15, /* MoE steps of 2+ tokens on the fp16 matrix cores: 1 on (default), 0 grouped fp32 GEMV */
+  TQ_KNOB_QMM_NT = 16, /* fp16 matrix-core MoE kernel: chunks of 16 (1) or 32 (2) positions (0: chosen from the mean tokens per expert) */
+  TQ_KNOB_MOE_NT = 17, /* grouped fp32 MoE GEMV: token tile 1, 2, 4 or 8 (0: chosen from the mean tokens per expert) */
+  TQ_KNOB_ROUTER_KL = 18, /* router for up to 8 tokens with lanes along the hidden dimension: 1 on (default), 0 off */
+  TQ_KNOB_ROUTER_STEPS = 19, /* that router: 256-value steps per hidden slice (1) */
+  TQ_KNOB_ROUTER_MF = 20, /* router for more than 8 tokens and 64+ experts on the fp32 matrix cores: 1 on (default), 0 off */
+  TQ_KNOB_GROUP1 = 21, /* one token: grouping written by the top-k kernel: 1 on (default), 0 the grouping kernel */
+  TQ_KNOB_COMBINE4 = 22, /* combine by 16-byte column runs: 1 on (default), 0 element-wise */
+  TQ_KNOB_FUSE_COMBINE = 23, /* one token: combine inside the down launch: 1 on (default), 0 a combine launch */
+  TQ_KNOB_GEMV_QMM = 24, /* Q4_K GEMV of 2..32 tokens on the fp16 matrix cores: 1 on (default), 0 off */
+  TQ_KNOB_QMM_UPK = 25, /* fp16 matrix-core dense kernel: blocks per k slice (4) */
+  TQ_KNOB_COUNT = 26
+};
+int tq_tuning_set(int knob, int value);
+int tq_tuning_get(int knob);
+
 #ifdef __cplusplus
 }
 #endif

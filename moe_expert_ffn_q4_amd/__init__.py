@@ -119,6 +119,10 @@ def _declare(L: C.CDLL) -> None:
         L.tq_moe_ffn_stages.argtypes = [C.POINTER(MoeDesc), _vp, _i64, _vp, _vp, C.c_size_t,
                                         C.POINTER(MoeRouting), _int, _vp]
         L.tq_moe_ffn_stages.restype = _int
+        L.tq_tuning_set.argtypes = [_int, _int]
+        L.tq_tuning_set.restype = _int
+        L.tq_tuning_get.argtypes = [_int]
+        L.tq_tuning_get.restype = _int
         L.tq_expert_cache_slot_bytes.argtypes = [C.POINTER(MoeDesc)]
         L.tq_expert_cache_slot_bytes.restype = C.c_size_t
         L.tq_expert_cache_state_bytes.argtypes = [C.POINTER(MoeDesc), _i64]
@@ -407,3 +411,64 @@ class ExpertCache:
             torch.cuda.synchronize()
             _check(lib().tq_expert_cache_destroy(self.state_ptr))
             self.open = False
+
+
+# Tuning knobs (TQ_KNOB_* of tq.h), for tests and tuning sweeps: the defaults are the production
+# choices; an override changes which kernel or launch shape a call takes.
+KNOBS = {
+    "gemv_target_wg": 0,
+    "gemv_max_waves": 1,
+    "gemv_klane": 2,
+    "kl_groups": 3,
+    "kl_rows": 4,
+    "kl_target_waves": 5,
+    "gemm_f32m": 6,
+    "f32m_upk": 7,
+    "gemv_i8": 8,
+    "i8_upk": 9,
+    "gemv_i8s": 10,
+    "i8s_nw": 11,
+    "i8s_d": 12,
+    "i8s_ks": 13,
+    "i8s_part": 14,
+    "moe_qmm": 15,
+    "qmm_nt": 16,
+    "moe_nt": 17,
+    "router_kl": 18,
+    "router_steps": 19,
+    "router_mf": 20,
+    "group1": 21,
+    "combine4": 22,
+    "fuse_combine": 23,
+    "gemv_qmm": 24,
+    "qmm_upk": 25,
+}
+
+
+def set_knob(name: str, value: int) -> None:
+    """Override a tuning knob process-wide (value < 0: back to the default)."""
+    _check(lib().tq_tuning_set(KNOBS[name], int(value)))
+
+
+def get_knob(name: str) -> int:
+    """The knob's override, or -1 while its default is in effect."""
+    return int(lib().tq_tuning_get(KNOBS[name]))
+
+
+class knobs:
+    """Context manager: knobs(gemv_i8=2, gemv_i8s=0) sets overrides and restores the previous
+    values on exit."""
+
+    def __init__(self, **values):
+        self.values = values
+
+    def __enter__(self):
+        self.old = {k: get_knob(k) for k in self.values}
+        for k, v in self.values.items():
+            set_knob(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k, v in self.old.items():
+            set_knob(k, v)
+        return False

@@ -43,6 +43,21 @@ int launched(int rc, const char *what) {
 
 namespace tq {
 
+namespace {
+std::atomic<int> g_knobs[TQ_KNOB_COUNT] = {};  // value + 1: 0 means no override
+}  // namespace
+
+int knob(int id, int dflt) {
+  const int v = g_knobs[id].load(std::memory_order_relaxed);
+  return v > 0 ? v - 1 : dflt;
+}
+
+void g_knobs_store(int id, int value) {
+  g_knobs[id].store(value < 0 ? 0 : value + 1, std::memory_order_relaxed);
+}
+
+int g_knobs_load(int id) { return g_knobs[id].load(std::memory_order_relaxed) - 1; }
+
 unsigned long long call_tag() {
   // splitmix64 of the load time and an address: where the token sequence starts
   static std::atomic<unsigned long long> next{[] {
@@ -60,6 +75,18 @@ unsigned long long call_tag() {
 }  // namespace tq
 
 extern "C" {
+
+int tq_tuning_set(int knob, int value) {
+  if (knob < 0 || knob >= TQ_KNOB_COUNT) return fail(TQ_EINVAL, "tq_tuning_set: unknown knob %d", knob);
+  if (value >= 0x7FFFFFFF) return fail(TQ_EINVAL, "tq_tuning_set: value %d too large", value);
+  tq::g_knobs_store(knob, value);
+  return TQ_OK;
+}
+
+int tq_tuning_get(int knob) {
+  if (knob < 0 || knob >= TQ_KNOB_COUNT) return -1;
+  return tq::g_knobs_load(knob);
+}
 
 int64_t tq_block_weights(int type) { return known_type(type) ? tq::fmt_block_weights(type) : 0; }
 int64_t tq_block_bytes(int type) { return known_type(type) ? tq::fmt_block_bytes(type) : 0; }

@@ -146,8 +146,8 @@ struct GemvPlan {
 };
 
 GemvPlan plan_gemv(int64_t n, int64_t k, bool split_allowed) {
-  static const int target_wg = env_int("TQ_GEMV_TARGET_WG", 1024);
-  static const int max_waves = env_int("TQ_GEMV_MAX_WAVES", 4);
+  const int target_wg = knob(TQ_KNOB_GEMV_TARGET_WG, 1024);
+  const int max_waves = knob(TQ_KNOB_GEMV_MAX_WAVES, 4);
   GemvPlan p;
   const int units = (int)(k / 256);
   p.rowgroups = (int)((n + 63) / 64);
@@ -591,14 +591,14 @@ static int launch_gemv_fmt(const uint8_t *w, int64_t rb, int n, int64_t k, const
 
 // Batch-1 Q4_K shapes that the lanes-along-k kernel takes.
 static bool klane_ok(int fmt, int64_t k, const float *x, int64_t batch) {
-  static const int kl_mode = env_int("TQ_GEMV_KLANE", 1);
+  const int kl_mode = knob(TQ_KNOB_GEMV_KLANE, 1);
   return fmt == FMT_Q4_K && batch == 1 && kl_mode && ((uintptr_t)x & 15) == 0 && k % 256 == 0 &&
          k <= 8 * 4096;
 }
 
-// Lane groups per wave: 4 for k <= 1024, 2 for k <= 2048, else 1 (TQ_KL_GROUPS=1 turns them off).
+// Lane groups per wave: 4 for k <= 1024, 2 for k <= 2048, else 1 (TQ_KNOB_KL_GROUPS = 1 turns them off).
 static int kl_groups(int nblk) {
-  const int allow = env_int("TQ_KL_GROUPS", 4);
+  const int allow = knob(TQ_KNOB_KL_GROUPS, 4);
   const int g = nblk <= 4 ? 4 : nblk <= 8 ? 2 : 1;
   return g < allow ? g : allow >= 4 ? 4 : allow >= 2 ? 2 : 1;
 }
@@ -621,8 +621,8 @@ static void launch_kl_rg(const KlMap &m, int nblk, int waves, int target, const 
 static int launch_kl(const KlMap &m, int64_t k, const float *x, hipStream_t s) {
   const int nblk = (int)(k / 256);
   const int waves = (nblk + 15) / 16;
-  static const int kl_rows_env = env_int("TQ_KL_ROWS", 4);
-  static const int target = env_int("TQ_KL_TARGET_WAVES", 2048);
+  const int kl_rows_env = knob(TQ_KNOB_KL_ROWS, 4);
+  const int target = knob(TQ_KNOB_KL_TARGET_WAVES, 2048);
   const int G = kl_groups(nblk);
   if (kl_rows_env == 2)
     launch_kl_rg<2, 1>(m, nblk, waves, target, x, s);
@@ -638,7 +638,7 @@ static int launch_kl(const KlMap &m, int64_t k, const float *x, hipStream_t s) {
 }
 
 bool moe_klane_ok(int fmt, int64_t hidden, int64_t ffn, int64_t tokens) {
-  static const int kl_mode = env_int("TQ_GEMV_KLANE", 1);
+  const int kl_mode = knob(TQ_KNOB_GEMV_KLANE, 1);
   return fmt == FMT_Q4_K && tokens == 1 && kl_mode && hidden % 256 == 0 && ffn % 256 == 0 &&
          hidden <= 8 * 4096 && ffn <= 8 * 4096;
 }
@@ -655,7 +655,7 @@ static void launch_moe_kl_g(const MoeKlArgs &a, int nblk, int waves, int nslots,
 int launch_moe_kl(const MoeKlArgs &a, int64_t k, int nslots, hipStream_t s) {
   const int nblk = (int)(k / 256);
   const int waves = (nblk + 15) / 16;
-  static const int target = env_int("TQ_KL_TARGET_WAVES", 2048);
+  const int target = knob(TQ_KNOB_KL_TARGET_WAVES, 2048);
   const int G = kl_groups(nblk);
   if (G == 4)
     launch_moe_kl_g<4>(a, nblk, waves, nslots, target, s);

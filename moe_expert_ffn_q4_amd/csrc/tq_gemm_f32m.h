@@ -10,7 +10,7 @@
 namespace tq {
 
 // Q8_0 with k a multiple of 256 and 2 <= batch <= 16; Q6_K with k a multiple of 512 and
-// 4 <= batch <= 16 (2..16 with TQ_GEMM_F32M=2).
+// 4 <= batch <= 16 (2..16 with TQ_KNOB_GEMM_F32M = 2).
 bool f32m_ok(int fmt, int64_t k, int64_t batch);
 // Partial sums of the k slices after the counters (0 when k is one slice).
 size_t f32m_workspace_bytes(int64_t rows, int64_t k);

@@ -330,21 +330,21 @@ __global__ __launch_bounds__(256) void k_gemm_f32m_q6(KlMap m, const float *__re
 
 // Q8_0 at 2..16 tokens, Q6_K (dword-aligned rows: k a multiple of 512) at 4..16 tokens, k up to
 // 65536 (on the 70B-shaped layer at batch 4 Q6_K takes 0.51 ms here against 0.60 ms on the fp32
-// vector GEMV; fewer tokens stay there). TQ_GEMM_F32M=0 turns the path off, =2 takes every batch
+// vector GEMV; fewer tokens stay there). TQ_KNOB_GEMM_F32M = 0 turns the path off, =2 takes every batch
 // of 2..16 (tests).
 bool f32m_ok(int fmt, int64_t k, int64_t batch) {
-  const int mode = env_int("TQ_GEMM_F32M", 1);
+  const int mode = knob(TQ_KNOB_GEMM_F32M, 1);
   if (mode == 0) return false;
   if (batch < 2 || batch > 16 || k <= 0 || k > 65536) return false;
   if (fmt == FMT_Q6_K) return k % 512 == 0 && (batch >= 4 || mode == 2);
   return fmt == FMT_Q8_0 && k % 256 == 0;
 }
 
-// Blocks per k slice, from k alone: at least TQ_F32M_UPK (8), at most 8 slices.
+// Blocks per k slice, from k alone: at least TQ_KNOB_F32M_UPK (8), at most 8 slices.
 static int f32m_upk(int64_t k) {
   const int nblk = (int)(k / 256);
   const int least = (nblk + kF32mMaxSlices - 1) / kF32mMaxSlices;
-  const int v = env_int("TQ_F32M_UPK", 8);
+  const int v = knob(TQ_KNOB_F32M_UPK, 8);
   return clampi(v > least ? v : least, 1, nblk);
 }
 

@@ -219,9 +219,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_i8s(KlMap m, const float *__re
 // lanes-along-k kernel is as fast on the measured shapes (inside a graph, the 8B-shaped step
 // 1.60 ms against 1.86 ms with this kernel everywhere), above it this one is about twice as fast
 // (8192 x 28672: 26 us against 58 us) -- that kernel's workgroups of k / 4096 waves and its VALU
-// work per weight hold it back there. TQ_GEMV_I8: 0 never, 2 every such shape (tests, tuning).
+// work per weight hold it back there. TQ_KNOB_GEMV_I8: 0 never, 2 every such shape (tests, tuning).
 bool i8_gemv_ok(int fmt, int64_t k, int64_t batch) {
-  const int mode = env_int("TQ_GEMV_I8", 1);
+  const int mode = knob(TQ_KNOB_GEMV_I8, 1);
   if (mode == 0 || fmt != FMT_Q4_K || batch != 1 || k % 256 != 0 || k < 256 ||
       k > 256 * kMaxSliceBlocks * kMaxSlices)
     return false;
@@ -232,7 +232,7 @@ bool i8_gemv_ok(int fmt, int64_t k, int64_t batch) {
 static int i8_upk(int64_t k) {
   const int nblk = (int)(k / 256);
   const int least = (nblk + kMaxSlices - 1) / kMaxSlices;
-  const int v = env_int("TQ_I8_UPK", 4);
+  const int v = knob(TQ_KNOB_I8_UPK, 4);
   return clampi(v > least ? v : least, 1, nblk);
 }
 
@@ -265,12 +265,12 @@ int launch_gemv_i8(const KlMap &m, int64_t k, const float *x, float *partial,
 
 // ---- streaming form ----------------------------------------------------------------------------
 
-// Opt-in (TQ_GEMV_I8S=1): on the 8B-shaped projections it is level with the lanes-along-k kernel
+// Opt-in (TQ_KNOB_GEMV_I8S = 1): on the 8B-shaped projections it is level with the lanes-along-k kernel
 // on q|k|v and o, 10% faster on gate|up and 35% slower on down (each workgroup makes the digits of
 // all of k, and 32-row tiles leave few workgroups on short matrices).
 bool i8s_gemv_ok(int fmt, int64_t k, int64_t batch) {
-  const int mode = env_int("TQ_GEMV_I8S", 0);
-  return mode != 0 && env_int("TQ_GEMV_I8", 1) != 0 && fmt == FMT_Q4_K && batch == 1 &&
+  const int mode = knob(TQ_KNOB_GEMV_I8S, 0);
+  return mode != 0 && knob(TQ_KNOB_GEMV_I8, 1) != 0 && fmt == FMT_Q4_K && batch == 1 &&
          k % 256 == 0 && k >= 256 && k <= 16384;
 }
 
@@ -290,13 +290,13 @@ static int launch_i8s_cfg(const KlMap &m, int nb, int ks, const float *x, hipStr
 
 // k parts per 32-row tile, from k alone (so a row's sum is formed the same way whatever the
 // matrix height or the call): the most parts, up to the workgroup's waves, that leave each part at
-// least TQ_I8S_PART (4) blocks. Workgroup waves and blocks in flight: TQ_I8S_NW / TQ_I8S_D.
+// least TQ_KNOB_I8S_PART (4) blocks. Workgroup waves and blocks in flight: TQ_KNOB_I8S_NW / TQ_KNOB_I8S_D.
 int launch_gemv_i8s(const KlMap &m, int64_t k, const float *x, hipStream_t s) {
   const int nb = (int)(k / 256);
-  const int nw_env = env_int("TQ_I8S_NW", 8);
-  const int d_env = env_int("TQ_I8S_D", 4);
-  const int ks_env = env_int("TQ_I8S_KS", 0);
-  const int part_min = clampi(env_int("TQ_I8S_PART", 4), 1, 64);
+  const int nw_env = knob(TQ_KNOB_I8S_NW, 8);
+  const int d_env = knob(TQ_KNOB_I8S_D, 4);
+  const int ks_env = knob(TQ_KNOB_I8S_KS, 0);
+  const int part_min = clampi(knob(TQ_KNOB_I8S_PART, 4), 1, 64);
   const int nw = nw_env == 4 || nw_env == 16 ? nw_env : 8;
   int ks = 1;
   if (ks_env > 0) {

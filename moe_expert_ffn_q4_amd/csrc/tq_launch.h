@@ -5,13 +5,15 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include "tq.h"
+
 namespace tq {
 
-// Integer tuning overrides from the environment (read once by each caller).
-inline int env_int(const char *name, int dflt) {
-  const char *v = getenv(name);
-  return v && *v ? atoi(v) : dflt;
-}
+// The value of tuning knob `id` (TQ_KNOB_*): its override (tq_tuning_set), else `dflt`. Read on
+// every call.
+int knob(int id, int dflt);
+void g_knobs_store(int id, int value);  // value < 0: back to the default
+int g_knobs_load(int id);               // the override, or -1
 // Tag of one launch's completion counters (Arrivals::tag): a 48-bit token, never zero and distinct
 // for every launch of the process (a counter starting from a value drawn at load time), shifted
 // past 16 count bits.

@@ -715,9 +715,9 @@ MoePlan plan_moe(const MoeShape &s) {
   // active expert's weights once per chunk of 16 or 32 positions instead of running VALU dot
   // products per token (with host-resident experts: one launch once every copy has landed)
   p.qmm = !s.mfma && s.type == FMT_Q4_K && T > 1 && qmm_shape_ok(s.hidden, s.ffn);
-  if (const char *v = getenv("TQ_MOE_QMM")) p.qmm = p.qmm && atoi(v) != 0;  // 0: grouped GEMV
+  p.qmm = p.qmm && knob(TQ_KNOB_MOE_QMM, 1) != 0;  // 0: grouped GEMV
   p.qmm_nt = (T * k + E - 1) / E > 12 ? 2 : 1;
-  if (const char *v = getenv("TQ_QMM_NT")) p.qmm_nt = atoi(v) == 2 ? 2 : 1;
+  if (const int v = knob(TQ_KNOB_QMM_NT, 0)) p.qmm_nt = v == 2 ? 2 : 1;
   p.shared_piece = (int)(!s.mfma && !p.qmm && T > 16 ? 16 : T);
   const int nsh = s.has_shared ? (int)((T + p.shared_piece - 1) / p.shared_piece) : 0;
   p.max_active = (int)((E < T * k ? E : T * k) + nsh);
@@ -725,10 +725,8 @@ MoePlan plan_moe(const MoeShape &s) {
   // token rows per tile of the grouped GEMV: one at T = 1, else about the mean per expert
   const int64_t mean = (T * k + E - 1) / E;
   p.nt = T == 1 ? 1 : mean >= 12 ? 8 : mean >= 2 ? 4 : 2;  // measured: Mixtral T=16, 64; DeepSeek T=256
-  if (const char *v = getenv("TQ_MOE_NT")) {  // tuning override: 1, 2, 4 or 8
-    const int n = atoi(v);
+  if (const int n = knob(TQ_KNOB_MOE_NT, 0))  // tuning override: 1, 2, 4 or 8
     if (n == 1 || n == 2 || n == 4 || n == 8) p.nt = n;
-  }
   p.klane = !s.mfma && moe_klane_ok(s.type, s.hidden, s.ffn, s.tokens);
   // router: 64 expert rows per workgroup, token tiles of 8, h split to fill the chip
   p.rtiles = (int)((T + 7) / 8);
@@ -739,17 +737,17 @@ MoePlan plan_moe(const MoeShape &s) {
   p.hsplit = (int)((s.hidden + p.hpk - 1) / p.hpk);
   // decode-sized batches: the lanes-along-hidden router, slices of whole 256-value steps, as many
   // as the partial-sum table allows
-  p.router_kl = T <= 8 && s.hidden % 256 == 0 && env_int("TQ_ROUTER_KL", 1) != 0;
+  p.router_kl = T <= 8 && s.hidden % 256 == 0 && knob(TQ_KNOB_ROUTER_KL, 1) != 0;
   if (p.router_kl) {
     const int steps = (int)(s.hidden / 256);
-    const int per = clampi(env_int("TQ_ROUTER_STEPS", 1), 1, steps);  // 256-value steps per slice
+    const int per = clampi(knob(TQ_KNOB_ROUTER_STEPS, 1), 1, steps);  // 256-value steps per slice
     const int hsk = clampi((steps + per - 1) / per, 1, kMaxHSplit);
     p.hpk = (int)(((steps + hsk - 1) / hsk) * 256);
     p.hsplit = (int)((s.hidden + p.hpk - 1) / p.hpk);
   }
   // many tokens and 64 or more experts: the matrix-core router, hidden slices (multiples of 16)
   // so that about 2048 waves run
-  p.router_mf = !p.router_kl && T > 8 && E >= 64 && env_int("TQ_ROUTER_MF", 1) != 0;
+  p.router_mf = !p.router_kl && T > 8 && E >= 64 && knob(TQ_KNOB_ROUTER_MF, 1) != 0;
   if (p.router_mf) {
     const int64_t tiles = ((T + 63) / 64) * ((E + 63) / 64);
     int hsm = (int)((2048 + tiles - 1) / tiles);
@@ -880,7 +878,7 @@ int launch_moe_routing(const MoePlan &p, const float *router_w, const float *x, 
     float *lg = (float *)(ws + p.off_logits), *wt = (float *)(ws + p.off_wts);
     int *id = (int *)(ws + p.off_ids);
     Group1Out g1{};
-    if (T == 1 && env_int("TQ_GROUP1", 1) != 0) {
+    if (T == 1 && knob(TQ_KNOB_GROUP1, 1) != 0) {
       g1.counts = (int *)(ws + p.off_counts);
       g1.offsets = (int *)(ws + p.off_offsets);
       g1.pairs = (int *)(ws + p.off_pairs);
@@ -913,7 +911,7 @@ int launch_moe_routing(const MoePlan &p, const float *router_w, const float *x, 
 int launch_moe_combine(const MoePlan &p, char *ws, float *y, hipStream_t st) {
   const MoeShape &s = p.s;
   const int T = (int)s.tokens, k = (int)s.top_k;
-  if (((uintptr_t)y & 15) == 0 && env_int("TQ_COMBINE4", 1) != 0) {
+  if (((uintptr_t)y & 15) == 0 && knob(TQ_KNOB_COMBINE4, 1) != 0) {
     const int quads = (int)(s.hidden / 4), threads = T >= 64 ? 256 : 64;
     hipLaunchKernelGGL(k_moe_combine4, dim3((unsigned)((quads + threads - 1) / threads), T),
                        dim3(threads), 0, st, (const float *)(ws + p.off_o), p.d_ks, p.P,
@@ -933,7 +931,7 @@ int launch_moe_combine(const MoePlan &p, char *ws, float *y, hipStream_t st) {
 
 bool moe_fuse_combine_ok(const MoePlan &p) {
   return p.nctr > 0 && p.klane && p.s.tokens == 1 && p.d_ks == 1 &&
-         env_int("TQ_FUSE_COMBINE", 1) != 0;
+         knob(TQ_KNOB_FUSE_COMBINE, 1) != 0;
 }
 
 int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,

@@ -695,7 +695,7 @@ int launch_qmm_moe(QmmArgs a, int nt_max, int max_chunks, const float *x, int64_
 // ---- dense host side ----------------------------------------------------------------------------
 
 bool qmm_dense_ok(int fmt, int64_t k, int64_t batch) {
-  const int mode = env_int("TQ_GEMV_QMM", 1);
+  const int mode = knob(TQ_KNOB_GEMV_QMM, 1);
   return mode && fmt == FMT_Q4_K && batch >= 2 && batch <= 32 && k % 256 == 0 && k >= 256 &&
          k <= 32768;
 }
@@ -705,7 +705,7 @@ bool qmm_dense_ok(int fmt, int64_t k, int64_t batch) {
 // most 8 slices (the last workgroup of a tile reads every slice's sums, all at once).
 static int dense_upk(int64_t k) {
   const int nblk = (int)(k / 256);
-  const int v = env_int("TQ_QMM_UPK", 4);
+  const int v = knob(TQ_KNOB_QMM_UPK, 4);
   const int least = (nblk + kMaxSlices - 1) / kMaxSlices;
   return clampi(v > least ? v : least, 1, nblk);
 }

@@ -193,3 +193,33 @@ def test_chain_prepare_and_run_argument_checks():
     # the persistent chain is switched off in this build: refused before any launch
     assert L.tq_chain_run(4096, None) == 5
     assert "switched off" in L.tq_last_error().decode()
+
+
+def test_tuning_knobs_match_header_and_round_trip():
+    src = open(HEADER).read()
+    declared = {m.group(1).lower(): int(m.group(2))
+                for m in re.finditer(r"TQ_KNOB_([A-Z0-9_]+) = (\d+)", src)}
+    count = declared.pop("count")
+    assert declared == tq.KNOBS and count == len(tq.KNOBS)
+    L = tq.lib()
+    for name, i in tq.KNOBS.items():
+        assert L.tq_tuning_get(i) == -1, name
+    assert L.tq_tuning_set(tq.KNOBS["gemv_i8"], 2) == 0 and L.tq_tuning_get(tq.KNOBS["gemv_i8"]) == 2
+    assert L.tq_tuning_set(tq.KNOBS["gemv_i8"], 0) == 0 and L.tq_tuning_get(tq.KNOBS["gemv_i8"]) == 0
+    assert L.tq_tuning_set(tq.KNOBS["gemv_i8"], -1) == 0 and L.tq_tuning_get(tq.KNOBS["gemv_i8"]) == -1
+    assert L.tq_tuning_set(count, 1) == 1 and L.tq_tuning_set(-1, 1) == 1
+    assert L.tq_tuning_get(count) == -1
+    with tq.knobs(moe_nt=4, kl_rows=8):
+        assert tq.get_knob("moe_nt") == 4 and tq.get_knob("kl_rows") == 8
+    assert tq.get_knob("moe_nt") == -1 and tq.get_knob("kl_rows") == -1
+
+
+def test_library_reads_no_environment():
+    """Kernel selection is set through the tuning knobs only: no source of the library reads the
+    environment."""
+    import glob
+
+    root = os.path.join(os.path.dirname(HEADER), "..", "moe_expert_ffn_q4_amd", "csrc")
+    for path in glob.glob(os.path.join(root, "**", "*.*"), recursive=True):
+        if path.endswith((".hip", ".h", ".cpp")):
+            assert "getenv" not in open(path).read(), path

@@ -234,21 +234,21 @@ def test_gemv_swiglu_equals_gemv_gemv_swiglu(t, n, k, batch):
 
 
 @pytest.mark.parametrize("n,k", [(37, 256), (130, 768), (64, 1024), (301, 1280), (130, 2048)])
-def test_gemv_lane_groups_bitwise(monkeypatch, n, k):
+def test_gemv_lane_groups_bitwise(knobs, n, k):
     """Batch-1 Q4_K rows of k <= 2048 are split over 2 or 4 lane groups per wave; each row's lane
     partials are added in the same tree as with whole-wave rows (whose extra lanes add exact
-    zeros), so the results are bitwise those of TQ_KL_GROUPS=1, and within the bar."""
+    zeros), so the results are bitwise those of TQ_KNOB_KL_GROUPS = 1, and within the bar."""
     _print_case("kl-groups", n, k)
-    monkeypatch.setenv("TQ_GEMV_I8S", "0")  # the lanes-along-k kernel
+    knobs("gemv_i8s", 0)  # the lanes-along-k kernel
     g = synth.rng(120, "kl-groups", n, k)
     w, x = synth.blob("q4_k", g, n, k), synth.normal_f32(g, (1, k))
     a = host(tq.gemv("q4_k", dev(w), n, k, dev(x)))
     ref, mag = oracle.gemv("q4_k", w, n, k, x)
     assert_product_close(a, ref, mag, what=f"kl groups {n}x{k}")
-    monkeypatch.setenv("TQ_KL_GROUPS", "1")
+    knobs("kl_groups", 1)
     b = host(tq.gemv("q4_k", dev(w), n, k, dev(x)))
     assert np.array_equal(a, b)
-    monkeypatch.delenv("TQ_KL_GROUPS")
+    knobs("kl_groups", -1)
     F = n + (n & 1)
     wg, wu = synth.blob("q4_k", g, F, k), synth.blob("q4_k", g, F, k)
     xd = dev(x)

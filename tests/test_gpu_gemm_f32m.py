@@ -23,9 +23,9 @@ tq = pytest.importorskip("moe_expert_ffn_q4_amd")
 
 
 @pytest.fixture(autouse=True)
-def every_batch(monkeypatch):
+def every_batch(knobs):
     """Every batch of 2..16 on the matrix-core path (by default Q6_K takes it from 4 tokens)."""
-    monkeypatch.setenv("TQ_GEMM_F32M", "2")
+    knobs("gemm_f32m", 2)
 
 
 def _case(*a):
@@ -98,12 +98,12 @@ def test_f32m_workspace_any_contents_and_repeatable():
 
 
 @pytest.mark.parametrize("t", ["q6_k", "q8_0"])
-def test_f32m_agrees_with_fp32_gemv(monkeypatch, t):
+def test_f32m_agrees_with_fp32_gemv(knobs, t):
     """The matrix-core path and the fp32 vector GEMV differ by fp32 rounding only."""
     n, k, batch = 200, 4096, 8
     g = synth.rng(705, "f32m-vs", t)
     w, x = dev(synth.blob(t, g, n, k)), dev(synth.normal_f32(g, (batch, k)))
     a = host(tq.gemv(t, w, n, k, x))
-    monkeypatch.setenv("TQ_GEMM_F32M", "0")
+    knobs("gemm_f32m", 0)
     b = host(tq.gemv(t, w, n, k, x))
     assert np.linalg.norm(a - b) / np.linalg.norm(b) < 1e-6

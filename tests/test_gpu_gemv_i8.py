@@ -1,6 +1,6 @@
 """GPU parity of the batch-1 Q4_K GEMV on the int8 matrix cores (activation digits + MFMA).
 
-The kernel runs by default from k = 16384 on; TQ_GEMV_I8=2 sends every Q4_K batch-1 shape to it,
+The kernel runs by default from k = 16384 on; TQ_KNOB_GEMV_I8 = 2 sends every Q4_K batch-1 shape to it,
 which these tests use to cover small and ragged shapes. Bars as for every fp32-accumulated
 product (1e-3 * sum|w x| + 1e-5 against the fp64 oracle), bitwise on the integer lattice (the
 activation digits of integer-valued blocks are exact and every partial sum is an integer below
@@ -20,9 +20,9 @@ tq = pytest.importorskip("moe_expert_ffn_q4_amd")
 
 
 @pytest.fixture
-def i8(monkeypatch):
-    monkeypatch.setenv("TQ_GEMV_I8", "2")
-    monkeypatch.setenv("TQ_GEMV_I8S", "0")  # the k-sliced kernel, not the streaming one
+def i8(knobs):
+    knobs("gemv_i8", 2)
+    knobs("gemv_i8s", 0)  # the k-sliced kernel, not the streaming one
 
 
 def _case(*a):
@@ -114,14 +114,14 @@ def test_i8_multi_and_swiglu_match_single_gemvs(i8):
     assert np.array_equal(h, host(tq.swiglu(gg, uu)))
 
 
-def test_i8_agrees_with_lanes_along_k(monkeypatch):
+def test_i8_agrees_with_lanes_along_k(knobs):
     """The int8 and the lanes-along-k kernels both meet the bar and differ by fp32 rounding."""
     n, k = 128, 8192
     g = synth.rng(507, "i8-vs-kl")
     w, x = dev(synth.blob("q4_k", g, n, k)), dev(synth.normal_f32(g, (1, k)))
-    monkeypatch.setenv("TQ_GEMV_I8", "2")
-    monkeypatch.setenv("TQ_GEMV_I8S", "0")
+    knobs("gemv_i8", 2)
+    knobs("gemv_i8s", 0)
     a = host(tq.gemv("q4_k", w, n, k, x))
-    monkeypatch.setenv("TQ_GEMV_I8", "0")
+    knobs("gemv_i8", 0)
     b = host(tq.gemv("q4_k", w, n, k, x))
     assert np.linalg.norm(a - b) / np.linalg.norm(b) < 1e-6

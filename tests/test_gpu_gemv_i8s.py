@@ -3,7 +3,7 @@
 Each workgroup makes the activation digits for all of k in LDS, each wave streams one 32-row tile
 over one k part with several blocks of loads in flight, and the parts of a tile are added in part
 order inside the workgroup. The launch shape (waves per workgroup, blocks in flight, k parts) is
-forced through TQ_I8S_NW / TQ_I8S_D / TQ_I8S_KS to cover every compiled form, including parts
+forced through TQ_KNOB_I8S_NW / TQ_KNOB_I8S_D / TQ_KNOB_I8S_KS to cover every compiled form, including parts
 left empty when k has fewer blocks than parts. Bars: 1e-3 * sum|w x| + 1e-5 per element against
 the fp64 oracle; bitwise on the integer lattice (every digit and partial sum exact); bitwise
 agreement of the one-launch multi and SwiGLU calls with single GEMVs (the k parts depend on k
@@ -29,21 +29,21 @@ def _case(*a):
     print("case:", *a, flush=True)
 
 
-def _config(monkeypatch, cfg):
-    monkeypatch.setenv("TQ_GEMV_I8S", "1")
+def _config(knobs, cfg):
+    knobs("gemv_i8s", 1)
     if cfg is not None:
         nw, d, ks = cfg
-        monkeypatch.setenv("TQ_I8S_NW", nw)
-        monkeypatch.setenv("TQ_I8S_D", d)
-        monkeypatch.setenv("TQ_I8S_KS", ks)
+        knobs("i8s_nw", int(nw))
+        knobs("i8s_d", int(d))
+        knobs("i8s_ks", int(ks))
 
 
 @pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: "default" if c is None else "-".join(c))
 @pytest.mark.parametrize("n,k", [(1, 256), (31, 512), (33, 1024), (100, 4096), (257, 3072),
                                  (64, 14336), (97, 16384), (1000, 2304)])
-def test_i8s_gemv_random(monkeypatch, cfg, n, k):
+def test_i8s_gemv_random(knobs, cfg, n, k):
     _case("i8s", cfg, n, k)
-    _config(monkeypatch, cfg)
+    _config(knobs, cfg)
     g = synth.rng(601, "i8s", n, k)
     w = synth.blob("q4_k", g, n, k)
     x = synth.normal_f32(g, (1, k))
@@ -56,11 +56,11 @@ def test_i8s_gemv_random(monkeypatch, cfg, n, k):
 @pytest.mark.parametrize("cfg", [None, ("4", "2", "1"), ("16", "2", "16")],
                          ids=lambda c: "default" if c is None else "-".join(c))
 @pytest.mark.parametrize("n,k", [(64, 4096), (50, 16384), (33, 768)])
-def test_i8s_gemv_lattice_bitwise(monkeypatch, cfg, n, k):
+def test_i8s_gemv_lattice_bitwise(knobs, cfg, n, k):
     """Scales 2^-8, x in {-1, 0, 1}: the digits are the integers themselves and every partial sum
     is exact, so the result equals the oracle's bit for bit."""
     _case("i8s-lattice", cfg, n, k)
-    _config(monkeypatch, cfg)
+    _config(knobs, cfg)
     g = synth.rng(602, "i8s-lattice", n, k)
     w = synth.blob("q4_k", g, n, k, d_value=2.0 ** -8, dmin_value=2.0 ** -8)
     x = synth.ternary_f32(g, (1, k))
@@ -69,11 +69,11 @@ def test_i8s_gemv_lattice_bitwise(monkeypatch, cfg, n, k):
     assert np.array_equal(y.astype(np.float64), ref)
 
 
-def test_i8s_identity_and_blocks_of_any_scale(monkeypatch):
+def test_i8s_identity_and_blocks_of_any_scale(knobs):
     """W = I gives x back (exactly for blocks with few significant bits); blocks of x scaled by
     1e-30 and 1e30, a zero block and an outlier keep fp32 accuracy (per-block power-of-two
     digit scales)."""
-    _config(monkeypatch, None)
+    _config(knobs, None)
     n = 1024
     g = synth.rng(603, "i8s-identity")
     x = synth.normal_f32(g, (1, n))
@@ -94,11 +94,11 @@ def test_i8s_identity_and_blocks_of_any_scale(monkeypatch):
 
 
 @pytest.mark.parametrize("k", [2048, 4096, 14336])
-def test_i8s_multi_and_swiglu_match_single_gemvs(monkeypatch, k):
+def test_i8s_multi_and_swiglu_match_single_gemvs(knobs, k):
     """q|k|v in one launch and gate|up with the SwiGLU in one launch give bitwise the results of
     single GEMVs (and of tq_swiglu on them): the k parts are chosen from k alone."""
     _case("i8s-multi", k)
-    _config(monkeypatch, None)
+    _config(knobs, None)
     g = synth.rng(604, "i8s-multi", k)
     ns = [512, 96, 160]
     ws = [synth.blob("q4_k", g, n, k) for n in ns]
@@ -116,10 +116,10 @@ def test_i8s_multi_and_swiglu_match_single_gemvs(monkeypatch, k):
 
 @pytest.mark.parametrize("name,n,k", [("o", 4096, 4096), ("gate", 14336, 4096),
                                       ("down", 4096, 14336)])
-def test_i8s_llama8b_shapes_all_rows(monkeypatch, name, n, k):
+def test_i8s_llama8b_shapes_all_rows(knobs, name, n, k):
     """The 8B-shaped projections at full size, every output row against the oracle."""
     _case("i8s-8b", name, n, k)
-    _config(monkeypatch, None)
+    _config(knobs, None)
     g = synth.rng(605, "i8s-8b", name)
     w = synth.blob("q4_k", g, n, k)
     x = synth.normal_f32(g, (1, k))
@@ -128,18 +128,18 @@ def test_i8s_llama8b_shapes_all_rows(monkeypatch, name, n, k):
     assert assert_product_close(y, ref, mag, what=f"i8s {name}") < 0.05
 
 
-def test_i8s_agrees_with_other_kernels(monkeypatch):
+def test_i8s_agrees_with_other_kernels(knobs):
     """The streaming kernel, the k-sliced int8 kernel and the lanes-along-k kernel all meet the
     bar on the same inputs and differ by fp32 rounding only."""
     n, k = 200, 8192
     g = synth.rng(606, "i8s-vs")
     w, x = dev(synth.blob("q4_k", g, n, k)), dev(synth.normal_f32(g, (1, k)))
-    _config(monkeypatch, None)
+    _config(knobs, None)
     a = host(tq.gemv("q4_k", w, n, k, x))
-    monkeypatch.setenv("TQ_GEMV_I8S", "0")
-    monkeypatch.setenv("TQ_GEMV_I8", "2")
+    knobs("gemv_i8s", 0)
+    knobs("gemv_i8", 2)
     b = host(tq.gemv("q4_k", w, n, k, x))
-    monkeypatch.setenv("TQ_GEMV_I8", "0")
+    knobs("gemv_i8", 0)
     c = host(tq.gemv("q4_k", w, n, k, x))
     assert np.linalg.norm(a - b) / np.linalg.norm(b) < 1e-6
     assert np.linalg.norm(a - c) / np.linalg.norm(c) < 1e-6

@@ -279,15 +279,15 @@ def test_moe_grouping_many_tokens_many_experts():
     check_moe("q4_k", shape, layer, x, 8, tokens=[0, 4095, 8191], path=tq.PATH_F32)
 
 
-def test_moe_one_token_lane_groups_bitwise(monkeypatch):
+def test_moe_one_token_lane_groups_bitwise(knobs):
     """One-token Q4_K steps with k <= 2048 per product (hidden 2048: gate/up in 2 lane groups per
-    wave; ffn 1024: down in 4) give bitwise the whole-wave results (TQ_KL_GROUPS=1)."""
+    wave; ffn 1024: down in 4) give bitwise the whole-wave results (TQ_KNOB_KL_GROUPS = 1)."""
     t, shape, k = "q4_k", dict(hidden=2048, ffn=1024, n_experts=8, shared=True), 2
     layer = synth.moe_layer(shape, t, seed=215, tag="kl-groups")
     x = synth.normal_f32(synth.rng(215, "x"), (1, shape["hidden"]))
     _case("moe-kl-groups", shape, k)
     moe, y, _ = check_moe(t, shape, layer, x, k)
-    monkeypatch.setenv("TQ_KL_GROUPS", "1")
+    knobs("kl_groups", 1)
     y1, _ = _run(moe, x, shape["n_experts"], k)
     assert np.array_equal(y, y1)
 
@@ -295,9 +295,9 @@ def test_moe_one_token_lane_groups_bitwise(monkeypatch):
 @pytest.mark.parametrize("shape,k", [(dict(hidden=768, ffn=512, n_experts=16, shared=True), 4),
                                      (dict(hidden=512, ffn=1024, n_experts=8, shared=False), 2),
                                      (dict(hidden=1024, ffn=512, n_experts=300, shared=True), 8)])
-def test_moe_one_token_grouping_in_topk_equals_group_kernel(monkeypatch, shape, k):
+def test_moe_one_token_grouping_in_topk_equals_group_kernel(knobs, shape, k):
     """For one token the top-k wave writes the grouping itself; it must equal the grouping
-    kernel's (TQ_GROUP1=0) bit for bit, and so must the layer output."""
+    kernel's (TQ_KNOB_GROUP1 = 0) bit for bit, and so must the layer output."""
     _case("group1", shape, k)
     t = "q4_k"
     layer = synth.moe_layer(shape, t, seed=231, tag="group1")
@@ -305,12 +305,12 @@ def test_moe_one_token_grouping_in_topk_equals_group_kernel(monkeypatch, shape, 
     moe = _layer_to_device(t, shape, layer, k)
     E = shape["n_experts"]
     y1, r1 = _run(moe, x, E, k)
-    monkeypatch.setenv("TQ_GROUP1", "0")
+    knobs("group1", 0)
     y0, r0 = _run(moe, x, E, k)
     for f in ("topk_ids", "counts", "offsets", "pairs"):
         assert np.array_equal(r1[f], r0[f]), f
     assert np.array_equal(y1, y0)
-    monkeypatch.delenv("TQ_GROUP1")
+    knobs("group1", -1)
     check_moe(t, shape, layer, x, k, moe=moe)
 
 
@@ -335,11 +335,11 @@ def test_moe_router_weights_not_16_byte_aligned():
 
 
 @pytest.mark.parametrize("mf", ["1", "0"], ids=["matrix-cores", "vector"])
-def test_moe_router_many_tokens_ragged_tiles(monkeypatch, mf):
+def test_moe_router_many_tokens_ragged_tiles(knobs, mf):
     """T = 130 tokens and E = 300 experts: neither fills whole 64 x 64 tiles of the matrix-core
     router (rows clamped on load, not stored); its logits and the vector router's both meet the
     oracle's bar, and routing and grouping follow bitwise."""
-    monkeypatch.setenv("TQ_ROUTER_MF", mf)
+    knobs("router_mf", int(mf))
     t, shape, k = "q4_k", dict(hidden=1024, ffn=256, n_experts=300, shared=True), 8
     _case("router-ragged", mf, shape, k)
     layer = synth.moe_layer(shape, t, seed=233, tag="router-ragged")
@@ -359,9 +359,9 @@ def test_moe_router_hidden_slices_not_whole_blocks():
 
 @pytest.mark.parametrize("T,path", [(1, 0), (33, 0), (33, 1), (300, 2)],
                          ids=["T1", "T33-auto", "T33-f32", "T300-bf16"])
-def test_moe_combine_column_runs_bitwise(monkeypatch, T, path):
+def test_moe_combine_column_runs_bitwise(knobs, T, path):
     """The combine with a workgroup per token and 16-byte column runs gives bitwise the
-    element-wise combine's output (TQ_COMBINE4=0); an output 4 bytes off 16-byte alignment takes
+    element-wise combine's output (TQ_KNOB_COMBINE4 = 0); an output 4 bytes off 16-byte alignment takes
     the element-wise combine and gives the same bits."""
     t, shape, k = "q4_k", dict(hidden=768, ffn=512, n_experts=16, shared=True), 4
     _case("combine4", T, path)
@@ -370,9 +370,9 @@ def test_moe_combine_column_runs_bitwise(monkeypatch, T, path):
     moe = _layer_to_device(t, shape, layer, k, path=path)
     xd = dev(x)
     y4 = host(moe(xd))
-    monkeypatch.setenv("TQ_COMBINE4", "0")
+    knobs("combine4", 0)
     y1 = host(moe(xd))
-    monkeypatch.delenv("TQ_COMBINE4")
+    knobs("combine4", -1)
     assert np.array_equal(y4, y1)
     buf = torch.empty(T * shape["hidden"] + 1, dtype=torch.float32, device="cuda:0")
     out = buf[1:].view(T, shape["hidden"])
@@ -386,10 +386,10 @@ def test_moe_combine_column_runs_bitwise(monkeypatch, T, path):
 @pytest.mark.parametrize("shape,k", [(dict(hidden=768, ffn=512, n_experts=16, shared=True), 4),
                                      (dict(hidden=2048, ffn=1024, n_experts=8, shared=False), 2),
                                      (dict(hidden=1024, ffn=512, n_experts=300, shared=True), 8)])
-def test_moe_one_token_combine_in_down_launch_bitwise(monkeypatch, shape, k):
+def test_moe_one_token_combine_in_down_launch_bitwise(knobs, shape, k):
     """One token, every stage in one call: the last down workgroup of each row range adds the
     slots (counters cleared by the gate/up launch of the same call). Bitwise equal to the separate
-    combine (TQ_FUSE_COMBINE=0) and to a call split into stages, on three calls in a row with
+    combine (TQ_KNOB_FUSE_COMBINE = 0) and to a call split into stages, on three calls in a row with
     different tokens, and within the oracle's bar."""
     t = "q4_k"
     _case("fused-combine", shape, k)
@@ -401,9 +401,9 @@ def test_moe_one_token_combine_in_down_launch_bitwise(monkeypatch, shape, k):
         x = synth.normal_f32(synth.rng(236, "x", i), (1, shape["hidden"]))
         xd = dev(x)
         y_f = host(moe(xd, ws=ws))
-        monkeypatch.setenv("TQ_FUSE_COMBINE", "0")
+        knobs("fuse_combine", 0)
         y_s = host(moe(xd, ws=ws))
-        monkeypatch.delenv("TQ_FUSE_COMBINE")
+        knobs("fuse_combine", -1)
         assert np.array_equal(y_f, y_s), f"call {i}"
         y_st = torch.full_like(xd, float("nan"))
         moe(xd, out=y_st, ws=ws, stages=tq.MOE_ROUTE)

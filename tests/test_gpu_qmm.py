@@ -17,9 +17,9 @@ pytestmark = pytest.mark.gpu
 tq = pytest.importorskip("moe_expert_ffn_q4_amd")
 
 
-def _tile_env(monkeypatch, nt):
-    monkeypatch.setenv("TQ_QMM_NT", str(nt))
-    monkeypatch.delenv("TQ_MOE_QMM", raising=False)
+def _tile_env(knobs, nt):
+    knobs("qmm_nt", nt)
+    knobs("moe_qmm", -1)
 
 
 # Few experts and top-1 or top-2, so that per-expert counts land on both sides of the chunk
@@ -32,8 +32,8 @@ BOUNDARY = [
 
 @pytest.mark.parametrize("nt", [1, 2])
 @pytest.mark.parametrize("shape,k,Ts", BOUNDARY, ids=["E2k1", "E4k2-shared"])
-def test_qmm_chunk_boundaries(monkeypatch, nt, shape, k, Ts):
-    _tile_env(monkeypatch, nt)
+def test_qmm_chunk_boundaries(knobs, nt, shape, k, Ts):
+    _tile_env(knobs, nt)
     layer = synth.moe_layer(shape, "q4_k", seed=401, tag=f"qmm-{shape['n_experts']}")
     moe = None
     for T in Ts:
@@ -46,15 +46,15 @@ def test_qmm_chunk_boundaries(monkeypatch, nt, shape, k, Ts):
         assert np.array_equal(y, y2), "not deterministic"
 
 
-def test_qmm_agrees_with_grouped_gemv(monkeypatch):
+def test_qmm_agrees_with_grouped_gemv(knobs):
     """The matrix-core kernels and the grouped fp32 GEMV both meet the bar; their difference is
     fp32 rounding order only (relative L2 difference at the 1e-6 level)."""
     shape, k, T = dict(hidden=1024, ffn=1536, n_experts=8, shared=True), 2, 48
     layer = synth.moe_layer(shape, "q4_k", seed=402, tag="qmm-vs-gemv")
     x = synth.normal_f32(synth.rng(402, "x"), (T, shape["hidden"]))
-    _tile_env(monkeypatch, 2)
+    _tile_env(knobs, 2)
     _, y_q, (wq, lq) = check_moe("q4_k", shape, layer, x, k)
-    monkeypatch.setenv("TQ_MOE_QMM", "0")
+    knobs("moe_qmm", 0)
     _, y_g, (wg, lg) = check_moe("q4_k", shape, layer, x, k)
     print(f"qmm worst {wq:.3g} l2 {lq:.3g}; grouped GEMV worst {wg:.3g} l2 {lg:.3g}")
     d = float(np.linalg.norm(y_q - y_g) / np.linalg.norm(y_g))
@@ -62,10 +62,10 @@ def test_qmm_agrees_with_grouped_gemv(monkeypatch):
     assert wq < 0.05 and lq < 1e-5
 
 
-def test_qmm_rows_of_any_scale(monkeypatch):
+def test_qmm_rows_of_any_scale(knobs):
     """Each activation row is rescaled by its own power of two: rows of magnitude 1e-12 and 1e12,
     an all-zero row and a row with one huge element keep fp32 accuracy."""
-    _tile_env(monkeypatch, 1)
+    _tile_env(knobs, 1)
     shape, k, T = dict(hidden=512, ffn=512, n_experts=4, shared=True), 2, 12
     layer = synth.moe_layer(shape, "q4_k", seed=403, tag="qmm-scale")
     x = synth.normal_f32(synth.rng(403, "x"), (T, shape["hidden"]))
@@ -80,15 +80,15 @@ def test_qmm_rows_of_any_scale(monkeypatch):
     assert np.all(np.isfinite(y))
 
 
-def test_qmm_workspace_sizes_differ_by_tile(monkeypatch):
+def test_qmm_workspace_sizes_differ_by_tile(knobs):
     """The chunk table grows when chunks hold 16 rather than 32 positions (fp32 path forced: at
     100 routed tokens per expert the automatic choice is the bf16 prefill path)."""
     shape = dict(hidden=512, ffn=512, n_experts=4, shared=False)
     layer = synth.moe_layer(shape, "q4_k", seed=404, tag="qmm-ws")
-    _tile_env(monkeypatch, 1)
+    _tile_env(knobs, 1)
     moe = _layer_to_device("q4_k", shape, layer, 2, path=tq.PATH_F32)
     w1 = moe.workspace_bytes(200)
-    _tile_env(monkeypatch, 2)
+    _tile_env(knobs, 2)
     w2 = moe.workspace_bytes(200)
     assert w1 > w2 > 0
     y = host(moe(dev(synth.normal_f32(synth.rng(404, "x"), (200, 512)))))
@@ -135,13 +135,13 @@ def test_qmm_dense_multi_and_swiglu_bitwise():
     assert np.array_equal(h, host(tq.swiglu(gg, uu)))
 
 
-def test_qmm_dense_agrees_with_fp32_gemv(monkeypatch):
-    """Matrix-core path vs the fp32 multi-token GEMV (TQ_GEMV_QMM=0): fp32 rounding apart."""
+def test_qmm_dense_agrees_with_fp32_gemv(knobs):
+    """Matrix-core path vs the fp32 multi-token GEMV (TQ_KNOB_GEMV_QMM = 0): fp32 rounding apart."""
     n, k, batch = 512, 8192, 8
     g = synth.rng(412, "dense-vs")
     w, x = dev(synth.blob("q4_k", g, n, k)), dev(synth.normal_f32(g, (batch, k)))
     a = host(tq.gemv("q4_k", w, n, k, x))
-    monkeypatch.setenv("TQ_GEMV_QMM", "0")
+    knobs("gemv_qmm", 0)
     b = host(tq.gemv("q4_k", w, n, k, x))
     assert np.linalg.norm(a - b) / np.linalg.norm(b) < 1e-6
 
