@@ -44,7 +44,10 @@ __device__ __forceinline__ void load_lds16(const void *g, uint32_t lds_base) {
 
 // An empty use of a loaded value. The pipelined kernels issue the same loads on every step (past
 // the end they repeat the last block) because their hand-counted vmcnt waits depend on it; the
-// results of the last such loads are never read, and without a use the compiler would drop them.
+// results of the last such loads are never read, and without a use the compiler would drop them,
+// which would shrink the number of loads in flight below what a wait count assumes (a barrier
+// would then pass before the last tile had landed). Every register set a pipeline loads into must
+// get a keep_alive after the pipeline's last step.
 template <typename T>
 __device__ __forceinline__ void keep_alive(const T &v) {
   asm volatile("" : : "v"(v));

@@ -104,7 +104,9 @@ __global__ __launch_bounds__(256) void k_chunk_table(const int *__restrict__ act
 // lane's 32 quant bytes.
 struct RawRow {
   u32x4 head, q0, q1;
+  static constexpr int kLoads = 3;  // load_raw issues one 16-byte load per field
 };
+static_assert(sizeof(RawRow) == RawRow::kLoads * sizeof(u32x4), "one load per field of RawRow");
 
 __device__ __forceinline__ void load_raw(const uint8_t *row, int kb, int c, RawRow &r) {
   const uint8_t *b = row + (int64_t)kb * 144;
@@ -182,10 +184,15 @@ __device__ __forceinline__ void prefill_tiles(const PrefillArgs &a, uint8_t *__r
   // compiler does not track them: it cannot tell the three token buffers apart and would
   // otherwise wait for these loads before every LDS read. Their completion is awaited
   // explicitly (barrier_after_vmem) before the step that reads them.
+  // the vector-memory loads of one step: the weights of two rows (load_w) and 2 NT token pieces
+  // (stage), issued unconditionally; each step's barrier leaves exactly one step's worth (the
+  // next step's) in flight, so the count must follow the loop bounds of both lambdas
+  constexpr int kRows = 2, kStageLoads = 2 * NT;
+  constexpr int kStepLoads = kRows * RawRow::kLoads + kStageLoads;
   auto stage = [&](uint8_t *tok, int st) {
     const uint32_t b = __builtin_amdgcn_readfirstlane(lds_address(tok + 4 * wave * kRowStride));
 #pragma unroll
-    for (int i = 0; i < 2 * NT; ++i)
+    for (int i = 0; i < kStageLoads; ++i)
       load_lds16(src[i] + 128 * st, b + 16 * i * kRowStride);
   };
 
@@ -202,9 +209,9 @@ __device__ __forceinline__ void prefill_tiles(const PrefillArgs &a, uint8_t *__r
   // Weights and tokens both run two steps ahead: raw[j] holds the weights of the steps st with
   // st % 3 == j, tok_j their tokens.
   RawRow raw[3][2];
-  auto load_w = [&](RawRow (&r)[2], int st) {
+  auto load_w = [&](RawRow (&r)[kRows], int st) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) load_raw(wrow[q], st >> 1, 2 * (st & 1) + kg, r[q]);
+    for (int q = 0; q < kRows; ++q) load_raw(wrow[q], st >> 1, 2 * (st & 1) + kg, r[q]);
   };
   load_w(raw[0], 0);
   stage(tok0, 0);
@@ -223,7 +230,8 @@ __device__ __forceinline__ void prefill_tiles(const PrefillArgs &a, uint8_t *__r
     // Then a plain barrier (__syncthreads would add a release fence, i.e. a wait for every load
     // in flight, the two steps ahead included): after it every wave's tokens of step st are in
     // LDS and every wave has finished reading `fill` (its tiles of step st-1).
-    barrier_after_vmem<6 + 2 * NT>();
+    static_assert(kStepLoads == 6 + 2 * NT, "two rows of three loads plus two per token tile");
+    barrier_after_vmem<kStepLoads>();
     const int c = 2 * (st & 1) + kg;  // the lane's group in block st/2
     const RawRow (&cur)[2] = rc;
     const GroupScale gs[2] = {group_scale(cur[0], c, unit_inv), group_scale(cur[1], c, unit_inv)};

@@ -152,7 +152,9 @@ __device__ __forceinline__ u32x2 gload8(const void *p) { return *(gu32x2)p; }
 // 32 quant bytes.
 struct QRow {
   u32x4 head, q0, q1;
+  static constexpr int kLoads = 3;  // qrow_load issues one 16-byte load per field
 };
+static_assert(sizeof(QRow) == QRow::kLoads * sizeof(u32x4), "one load per field of QRow");
 
 __device__ __forceinline__ void qrow_load(const uint8_t *row, int kb, int g, QRow &r) {
   const uint8_t *b = row + (int64_t)kb * 144;
@@ -254,9 +256,14 @@ __device__ __forceinline__ void qmm_tiles(const SplitRows &x, uint8_t *__restric
         load_lds16(xsrc[i] + (int64_t)kb * kXBlockBytes,
                    lds0 + buf * kBuf + (4 * i + wave) * kXBlockBytes);
   };
-  auto load_w = [&](QRow (&r)[2], u32x2 (&ax)[NT], int kb) {
-    qrow_load(wrow[0], kb, g, r[0]);
-    qrow_load(wrow[1], kb, g, r[1]);
+  // the vector-memory loads one load_w issues: two weight rows, then one 8-byte load of the
+  // sums per token tile; the barrier of each step leaves exactly these (of the next block) in
+  // flight, so the count below must follow the loop bounds here
+  constexpr int kRows = 2;
+  constexpr int kWLoads = kRows * QRow::kLoads + NT;
+  auto load_w = [&](QRow (&r)[kRows], u32x2 (&ax)[NT], int kb) {
+#pragma unroll
+    for (int q = 0; q < kRows; ++q) qrow_load(wrow[q], kb, g, r[q]);
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) ax[tt] = gload8(asrc[tt] + (int64_t)kb * kAuxBytes);
   };
@@ -284,7 +291,8 @@ __device__ __forceinline__ void qmm_tiles(const SplitRows &x, uint8_t *__restric
     // the same loads (past the end they repeat the last block into registers and a buffer nobody
     // reads), so leaving the 6 + NT newest in flight is exact on every path. After the barrier
     // every wave's rows of block st are in LDS and every wave is done reading block st-1's buffer.
-    barrier_after_vmem<6 + NT>();
+    static_assert(kWLoads == 6 + NT, "two rows of three loads plus one per token tile");
+    barrier_after_vmem<kWLoads>();
     const uint8_t *buf = rd + (st & 1) * kBuf;
     auto read_a = [&](int tt, int s, half8 &h, half8 &l) {
       const uint8_t *p = buf + tt * 16 * kXBlockBytes + 16 * ((8 * g + s) ^ t16);
