@@ -59,6 +59,9 @@ def _args():
                    help="deepseek-host cache sweep: experts prefetched per call (each value is "
                         "swept with every slot count)")
     p.add_argument("--seed", type=int, default=42)
+    p.add_argument("--knob", action="append", default=[], metavar="NAME=VALUE",
+                   help="override a library tuning knob (tq.KNOBS) for a tuning run; the "
+                        "defaults are the production choices")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget of the oracle sample")
@@ -969,6 +972,9 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
+    for kv in args.knob:
+        name, value = kv.split("=", 1)
+        tq.set_knob(name, int(value))
     other = {"deepseek-host": host_bench, "llama70b": llama70b_bench,
              "c1": c1_bench}.get(args.workload)
     if other is None and args.workload != "llama8b":
