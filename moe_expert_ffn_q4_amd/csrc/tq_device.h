@@ -77,12 +77,14 @@ __device__ __forceinline__ int wave_index() {
 }
 
 // Completion counters of the k-sliced products: the workgroup that finishes a row group's last k
-// slice adds the slices' partial sums. A counter word is (tag | arrivals): the tag is the launch's
-// token (never zero) shifted past 16 count bits, and the token differs for every launch the host
-// makes (call_tag()), so whatever bytes a fresh workspace holds never pass for this launch's
-// word. The last workgroup sets its word back to zero (done_arrivals), because a launch recorded
-// in a HIP graph keeps its token on every replay: each replay then starts from zero, which no
-// token matches. Nothing has to be cleared by the caller.
+// slice adds the slices' partial sums. Every arrival adds D = (token << 16) + 1 to its row group's
+// 8-byte word, the token being the launch's (never zero, different for every launch the host
+// makes: call_tag()). A word that only this launch's arrivals have touched since it was zero
+// therefore holds exactly count * D (mod 2^64), and one fetch-add both counts an arrival and
+// shows that; whatever bytes a fresh workspace holds pass that test only by a 2^-48 chance. The
+// last workgroup sets its word back to zero (done_arrivals): a launch recorded in a HIP graph
+// keeps its token on every replay, and zero is 0 * D for any token. Nothing has to be cleared by
+// the caller.
 struct Arrivals {
   unsigned long long *ctr;  // one 8-byte word per row group
   unsigned long long tag;   // token << 16
@@ -91,21 +93,23 @@ constexpr unsigned long long kArrivalCountMask = 0xFFFFull;
 
 // Counts the calling workgroup on row group g and returns true for the one that brings the count
 // to `parts` (< 65536). One thread calls it, after the workgroup's partial sums have completed at
-// agent scope. A workgroup whose add lands on another call's word turns it into this call's word
-// with a count of one, or, when another workgroup of this call has done that in the meantime,
-// counts itself again on that word (its add on the old word is dropped with the old word).
+// agent scope. An add that lands on a word that is not count * D (bytes another call or another
+// use of the memory left) turns it into 1 * D by compare-and-swap, or, when another workgroup of
+// this launch has done that in the meantime, counts itself on that word (its add on the old word
+// is dropped with the old word).
 __device__ inline bool arrive_last(const Arrivals &a, int g, unsigned parts) {
   unsigned long long *p = a.ctr + g;
-  unsigned long long w =
-      __hip_atomic_fetch_add(p, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if ((w & ~kArrivalCountMask) != a.tag) {
-    w += 1ull;  // what the word holds if nobody else touched it
+  const unsigned long long D = a.tag | 1ull;
+  auto ours = [D](unsigned long long v) { return v == (v & kArrivalCountMask) * D; };
+  unsigned long long w = __hip_atomic_fetch_add(p, D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!ours(w)) {
+    w += D;  // what the word holds if nobody else touched it
     for (;;) {
-      if (__hip_atomic_compare_exchange_strong(p, &w, a.tag | 1ull, __ATOMIC_RELAXED,
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      if (__hip_atomic_compare_exchange_strong(p, &w, D, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT))
         return parts == 1u;
-      if ((w & ~kArrivalCountMask) == a.tag) {  // claimed by another workgroup of this call
-        w = __hip_atomic_fetch_add(p, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (ours(w)) {  // claimed by another workgroup of this launch
+        w = __hip_atomic_fetch_add(p, D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
     }
