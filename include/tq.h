@@ -404,8 +404,11 @@ enum {
   TQ_KNOB_COMBINE4 = 22, /* combine by 16-byte column runs: 1 on (default), 0 element-wise */
   TQ_KNOB_FUSE_COMBINE = 23, /* one token: combine inside the down launch: 1 on (default), 0 a combine launch */
   TQ_KNOB_GEMV_QMM = 24, /* Q4_K GEMV of 2..32 tokens on the fp16 matrix cores: 1 on (default), 0 off */
-  TQ_KNOB_QMM_UPK = 25, /* fp16 matrix-core dense kernel: blocks per k slice (4) */
-  TQ_KNOB_COUNT = 26
+  TQ_KNOB_QMM_UPK = 25, /* fp16 matrix-core dense kernel with a split launch: blocks per k slice (4) */
+  TQ_KNOB_QMM_INLINE = 26, /* Q4_K GEMV of 2..16 tokens: activations split inside the product kernel: 1 on (default), 0 a split launch first */
+  TQ_KNOB_QMM_INLINE_UPK = 27, /* that kernel: blocks per k slice, 2 or 4 (0: 2 for k <= 4096, else 4) */
+  TQ_KNOB_QMM_INLINE_NR = 28, /* that kernel: 16-row weight tiles per wave of a product without SwiGLU, 1 (default) or 2 */
+  TQ_KNOB_COUNT = 29
 };
 int tq_tuning_set(int knob, int value);
 int tq_tuning_get(int knob);

@@ -442,6 +442,9 @@ KNOBS = {
     "fuse_combine": 23,
     "gemv_qmm": 24,
     "qmm_upk": 25,
+    "qmm_inline": 26,
+    "qmm_inline_upk": 27,
+    "qmm_inline_nr": 28,
 }
 
 

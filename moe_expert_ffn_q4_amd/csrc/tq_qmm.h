@@ -66,7 +66,8 @@ struct QmmDense {
   int64_t row_bytes;
 };
 bool qmm_dense_ok(int fmt, int64_t k, int64_t batch);
-// Workspace after the completion counters: the split activations and the k-slice partial sums.
+// Workspace after the completion counters: the k-slice partial sums (and, for the kernel that
+// reads split rows, the split activations), enough for any launch shape the knobs can pick.
 size_t qmm_dense_bytes(int64_t rows, int64_t k, int64_t batch, bool swiglu);
 // The k dimension is cut into slices of a fixed number of blocks (a function of k only, so every
 // row is summed in the same order whatever the launch); the last workgroup of a row tile to finish

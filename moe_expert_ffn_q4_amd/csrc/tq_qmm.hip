@@ -19,6 +19,10 @@
 //   k_qmm<true>      per (chunk of <= 16 NT positions, 64 ffn columns): gate and up products,
 //                    h = silu(gate) * up, fp32 [position][ffn]
 //   k_qmm<false>     per (chunk, 128 hidden rows): down product, o fp32 [position][hidden]
+//   k_qmm_dense      dense products of 2..32 tokens on split rows (k slices, the last workgroup
+//                    of a row tile adds them)
+//   k_qmm_dense2     dense products of 2..16 tokens, the activations split inside the kernel
+//                    with one power of two per (token, block)
 //
 // Matrix-core layout (v_mfma_f32_16x16x32_f16). A = 16 token rows x 32 k from LDS, B = 32 k x 16
 // weight rows built in registers; lane l holds weight row l % 16 and k group g = l / 16, and
@@ -619,6 +623,269 @@ __global__ __launch_bounds__(256) void k_qmm_dense(QmmDense m, SplitRows x, int 
     qmm_tiles<GU, (NTMAX > 1 ? 2 : 1), NTMAX>(x, xbuf, rowidx, B, kblocks, wrow, kb0, steps, epi);
 }
 
+// ---- dense products with the activations split in the kernel ------------------------------------
+// The same products without a split launch. A workgroup owns one row tile and one k slice of at
+// most UPK blocks. It requests the slice's fp32 activations, then all of the slice's weights;
+// while the weights are in flight it splits the activations into LDS (each (token, block) scaled
+// by its own power of two, which puts the block's largest magnitude into [2^14, 2^15)) and meets
+// the other waves at one barrier; the blocks are then multiplied back to back, each block's sums
+// folded with its own 2^-e. NR 16-row weight tiles per wave (gate / up: always the pair). RB LDS
+// token rows per block: 8 (up to 8 tokens; operand rows 8..15 repeat rows 0..7 and their outputs
+// are never stored) or 16.
+template <int RB, int UPK>
+struct DenseLds {
+  static constexpr int kX = UPK * RB * kXBlockBytes;  // split blocks [block][row][1 KB]
+  static constexpr int kAux = UPK * RB * kAuxBytes;   // sub-block sums [block][row][32 B]
+  static constexpr int kUs = UPK * RB * 4;            // 2^-e [block][row]
+  static constexpr int kBytes = kX + kAux + kUs;
+};
+constexpr int kMaxSlicesInline = 32;
+
+// Wave-wide maximum (every lane gets it); exact in any order.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) v = fmaxf(v, xor_recv(v, d));
+  return v;
+}
+
+// Splits the (block, token) pair `pair` of the slice, whose 256 fp32 values the wave holds as
+// lane l's float4 l, into LDS: scaled hi / lo halves in the operand order with the row's piece
+// swizzle, the sub-block sums and the pair's 2^-e.
+template <int RB, int UPK>
+__device__ __forceinline__ void dense_split_pair(float4 v, int b, int t, uint8_t *lds) {
+  using L = DenseLds<RB, UPK>;
+  const int lane = threadIdx.x & 63;
+  const float mx = wave_max(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  int e = 0;
+  if (mx > 0.f) {
+    int ex;
+    frexpf(mx, &ex);  // mx in [2^(ex-1), 2^ex)
+    e = 15 - ex;
+    if (e > 126) e = 126;
+  }
+  const float s = ldexpf(1.f, e);
+  const float a[4] = {v.x * s, v.y * s, v.z * s, v.w * s};
+  _Float16 hi[4], lo[4];
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hi[i] = (_Float16)a[i];
+    lo[i] = (_Float16)(a[i] - (float)hi[i]);
+    sum += (float)hi[i] + (float)lo[i];
+  }
+  // lane l holds values 4l .. 4l+3: half (l & 1) of run l / 2, stored in the order 0,2,1,3
+  const half4 h4 = {hi[0], hi[2], hi[1], hi[3]}, l4 = {lo[0], lo[2], lo[1], lo[3]};
+  const int row = b * RB + t;
+  uint8_t *xr = lds + row * kXBlockBytes + 16 * ((lane >> 1) ^ t) + 8 * (lane & 1);
+  *reinterpret_cast<half4 *>(xr) = h4;
+  *reinterpret_cast<half4 *>(xr + 512) = l4;
+  // sub-block j = lanes 8j .. 8j+7
+  sum += xor_recv(sum, 1);
+  sum += xor_recv(sum, 2);
+  sum += xor_recv(sum, 4);
+  if ((lane & 7) == 0) {
+    const int j = lane >> 3;
+    const float s6 = sum * 0x1p-6f;
+    const _Float16 sh = (_Float16)s6, sl = (_Float16)(s6 - (float)sh);
+    _Float16 *ap = reinterpret_cast<_Float16 *>(lds + L::kX + row * kAuxBytes);
+    ap[perm8(j)] = sh;
+    ap[8 + perm8(j)] = sl;
+  }
+  if (lane == 0) reinterpret_cast<float *>(lds + L::kX + L::kAux)[row] = ldexpf(1.f, -e);
+}
+
+// Loops f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>).
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(const F &f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// Sums of one (row tile, k slice), [token][kPer]: gate columns 0..63 and up 64..127, or the
+// tile's 64 NR rows. With one slice the sums are the results.
+template <bool GU, int NR>
+struct Dense2Tile {
+  static constexpr int kRows = GU ? 64 : 64 * NR;  // outputs (columns) per tile
+  static constexpr int kPer = GU ? 128 : 64 * NR;  // partial sums per token
+  static __device__ __forceinline__ int pos(int r, int wave, int t16) {
+    return GU ? r * 64 + 16 * wave + t16 : 16 * NR * wave + 16 * r + t16;
+  }
+};
+
+template <bool GU, int NR, int RB, int UPK>
+__global__ __launch_bounds__(256) void k_qmm_dense2(QmmDense m, const float *__restrict__ x, int B,
+                                                    int kblocks, int ksplit, float *partial,
+                                                    Arrivals arr) {
+  static_assert(!GU || NR == 2, "a gate/up tile holds the gate and the up rows");
+  static_assert(RB == 8 || RB == 16, "token rows per block");
+  using L = DenseLds<RB, UPK>;
+  using T = Dense2Tile<GU, NR>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[L::kBytes];
+  __shared__ int is_last;
+  const int tile = blockIdx.x / ksplit, ks = blockIdx.x - tile * ksplit;
+  const int kb0 = ks * UPK, steps = min(UPK, kblocks - kb0);
+  const int lane = threadIdx.x & 63, t16 = lane & 15, g = lane >> 4, wave = wave_index();
+  const int64_t ldx = (int64_t)kblocks * 256;
+
+  // 1. the slice's activations: wave w takes the pairs 4 j + w (block b = pair / RB, token
+  // t = pair % RB), lane l the values 4l .. 4l+3 of the block (1 KB per pair, coalesced)
+  constexpr int kIt = RB * UPK / 4;
+  float4 xv[kIt];
+#pragma unroll
+  for (int j = 0; j < kIt; ++j) {
+    const int pair = 4 * j + wave, b = pair / RB, t = pair % RB;
+    if (t < B && b < steps)
+      xv[j] = *reinterpret_cast<const float4 *>(x + t * ldx + (int64_t)(kb0 + b) * 256 + 4 * lane);
+    else
+      xv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. every block of the slice for the lane's weight rows (past the slice's end: its last
+  // block again, never used)
+  const uint8_t *wrow[NR];
+  if (GU) {
+    const int c = min(tile * 64 + wave * 16 + t16, m.cum[1] - 1);
+    wrow[0] = m.w[0] + (int64_t)c * m.row_bytes + (int64_t)kb0 * 144;
+    if constexpr (NR > 1) wrow[NR - 1] = m.w[1] + (int64_t)c * m.row_bytes + (int64_t)kb0 * 144;
+  } else {
+    const int total = m.cum[m.nparts];
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+      wrow[r] = dense_row(m, min(tile * T::kRows + wave * 16 * NR + 16 * r + t16, total - 1)) +
+                (int64_t)kb0 * 144;
+  }
+  QRow w[UPK][NR];
+#pragma unroll
+  for (int b = 0; b < UPK; ++b)
+#pragma unroll
+    for (int r = 0; r < NR; ++r) qrow_load(wrow[r], min(b, steps - 1), g, w[b][r]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. split into LDS (waits for the activations only), then one barrier
+#pragma unroll
+  for (int j = 0; j < kIt; ++j) {
+    const int pair = 4 * j + wave, b = pair / RB, t = pair % RB;
+    if (t < B && b < steps) dense_split_pair<RB, UPK>(xv[j], b, t, lds);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+
+  // 4. the blocks; operand row = t16 % RB
+  const int row = t16 & (RB - 1);
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) acc[r] = zero;
+#pragma unroll
+  for (int b = 0; b < UPK; ++b) {
+    if (b >= steps) break;
+    const uint8_t *xb = lds + (b * RB + row) * kXBlockBytes;
+    const half4 am = *reinterpret_cast<const half4 *>(lds + L::kX + (b * RB + row) * kAuxBytes + 8 * g);
+    const f32x4 us = *reinterpret_cast<const f32x4 *>(lds + L::kX + L::kAux +
+                                                      (b * RB + ((4 * g) & (RB - 1))) * 4);
+    QScale qs[NR];
+    f32x4 dm[NR], dq[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      qs[r] = qscale(w[b][r], g);
+      dm[r] = __builtin_amdgcn_mfma_f32_16x16x16f16(am, qs[r].m, zero, 0, 0, 0);
+    }
+    static_for<8>([&](auto S_) {
+      constexpr int S = decltype(S_)::value;
+      const uint8_t *p = xb + 16 * ((8 * g + S) ^ row);
+      const half8 ah = *reinterpret_cast<const half8 *>(p);
+      const half8 al = *reinterpret_cast<const half8 *>(p + 512);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const half8 bq = qb<S>(w[b][r], S < 4 ? qs[r].sc_lo : qs[r].sc_hi);
+        dq[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, S == 0 ? zero : dq[r], 0, 0, 0);
+        dq[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, dq[r], 0, 0, 0);
+      }
+    });
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[r][i] = __builtin_fmaf(us[i], __builtin_fmaf(qs[r].d, dq[r][i], qs[r].ndmin * dm[r][i]),
+                                   acc[r][i]);
+  }
+
+  // 5. results (one slice) or this slice's sums and, for the tile's last workgroup, the total
+  const int n = GU ? m.cum[1] : m.cum[m.nparts];
+  auto store = [&](int tok, int vrow, float v) {
+    if (vrow < n) {
+      const DensePart q = dense_part(m, vrow);
+      pick4(m.y[0], m.y[1], m.y[2], m.y[3], q.p)[(int64_t)tok * (q.last - q.first) +
+                                                  (vrow - q.first)] = v;
+    }
+  };
+  if (ksplit == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = 4 * g + i;
+      if (tok >= B) continue;
+      if (GU) {
+        const int col = tile * 64 + 16 * wave + t16;
+        if (col < n) m.y[0][(int64_t)tok * n + col] = silu_mul(acc[0][i], acc[NR - 1][i]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) store(tok, tile * T::kRows + T::pos(r, wave, t16), acc[r][i]);
+      }
+    }
+    return;
+  }
+  float *mine = partial + ((int64_t)tile * ksplit + ks) * B * T::kPer;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tok = 4 * g + i;
+    if (tok >= B) continue;
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+      __hip_atomic_store(mine + tok * T::kPer + T::pos(r, wave, t16), acc[r][i], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  if (threadIdx.x == 0) is_last = arrive_last(arr, tile, (unsigned)ksplit);
+  __syncthreads();
+  if (!is_last) return;
+  const float *base = partial + (int64_t)tile * ksplit * B * T::kPer;
+  const int64_t sstride = (int64_t)B * T::kPer;
+  for (int idx = threadIdx.x; idx < B * T::kRows; idx += blockDim.x) {
+    const int tok = idx / T::kRows, rt = idx - tok * T::kRows;
+    const float *pt = base + tok * T::kPer + rt;
+    float s0 = 0.f, s1 = 0.f;
+    for (int q0 = 0; q0 < ksplit; q0 += 8) {  // eight slices' values in flight, added in order
+      float v0[8], v1[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const bool in = q0 + q < ksplit;
+        v0[q] = in ? __hip_atomic_load(pt + (q0 + q) * sstride, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT)
+                   : 0.f;
+        v1[q] = GU && in ? __hip_atomic_load(pt + (q0 + q) * sstride + 64, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT)
+                         : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (q0 + q < ksplit) {
+          s0 += v0[q];
+          s1 += v1[q];
+        }
+    }
+    if (GU) {
+      const int col = tile * 64 + rt;
+      if (col < n) m.y[0][(int64_t)tok * n + col] = silu_mul(s0, s1);
+    } else {
+      store(tok, tile * T::kRows + rt, s0);
+    }
+  }
+  if (threadIdx.x == 0) done_arrivals(arr, tile);
+}
+
 // ---- host side ----------------------------------------------------------------------------------
 
 int qmm_chunk_rows(int nt_max) { return 16 * nt_max; }
@@ -720,14 +987,81 @@ static int dense_upk(int64_t k) {
 
 static int64_t dense_tiles(int64_t rows, bool swiglu) { return swiglu ? (rows + 63) / 64 : (rows + 127) / 128; }
 
+// The in-kernel split: blocks per k slice, a function of k only (so that one-launch multi and
+// SwiGLU calls stay bitwise equal to single products), and the weight tiles per wave.
+struct Dense2Plan {
+  int upk, nr, rb, ksplit;
+  int64_t tiles;
+};
+static Dense2Plan dense2_plan(int64_t rows, int64_t k, int64_t batch, bool swiglu, int nr_force) {
+  const int nblk = (int)(k / 256);
+  Dense2Plan p;
+  p.upk = knob(TQ_KNOB_QMM_INLINE_UPK, 0);
+  if (p.upk != 2 && p.upk != 4) p.upk = nblk <= 16 ? 2 : 4;
+  p.ksplit = (nblk + p.upk - 1) / p.upk;
+  p.rb = batch <= 8 ? 8 : 16;
+  p.nr = swiglu ? 2 : nr_force ? nr_force : knob(TQ_KNOB_QMM_INLINE_NR, 0);
+  if (p.nr != 1 && p.nr != 2) p.nr = 1;  // measured on the 8B shapes at batch 8: 2.34 against 2.55 ms per step for 2
+  p.tiles = swiglu ? (rows + 63) / 64 : (rows + 64 * p.nr - 1) / (64 * p.nr);
+  return p;
+}
+static size_t dense2_partial_bytes(const Dense2Plan &p, int64_t batch, bool swiglu) {
+  if (p.ksplit == 1) return 0;
+  const int64_t per = swiglu ? 128 : 64 * p.nr;
+  return (size_t)align256(p.tiles * p.ksplit * batch * per * 4);
+}
+// Up to 16 tokens, 16-byte aligned activations and at most kMaxSlicesInline slices.
+static bool dense2_ok(int64_t k, const float *x, int64_t batch) {
+  if (!knob(TQ_KNOB_QMM_INLINE, 1) || batch > 16 || ((uintptr_t)x & 15) != 0) return false;
+  return dense2_plan(256, k, batch, false, 1).ksplit <= kMaxSlicesInline;
+}
+
 size_t qmm_dense_bytes(int64_t rows, int64_t k, int64_t batch, bool swiglu) {
   const int64_t nblk = k / 256, upk = dense_upk(k), ksplit = (nblk + upk - 1) / upk;
   const int64_t tiles = dense_tiles(rows, swiglu);
-  return split_rows_bytes(batch, k) + (ksplit > 1 ? (size_t)align256(tiles * ksplit * batch * 128 * 4) : 0);
+  size_t need = split_rows_bytes(batch, k) +
+                (ksplit > 1 ? (size_t)align256(tiles * ksplit * batch * 128 * 4) : 0);
+  if (batch <= 16)  // either launch shape of the in-kernel split, whichever the knobs pick
+    for (int nr = 1; nr <= 2; ++nr) {
+      const size_t b = dense2_partial_bytes(dense2_plan(rows, k, batch, swiglu, nr), batch, swiglu);
+      need = b > need ? b : need;
+    }
+  return need;
+}
+
+template <bool GU, int NR, int RB, int UPK>
+static void dense2_launch(const QmmDense &m, const float *x, int B, int nblk, const Dense2Plan &p,
+                          float *partial, Arrivals arr, hipStream_t st) {
+  hipLaunchKernelGGL((k_qmm_dense2<GU, NR, RB, UPK>), dim3((unsigned)(p.tiles * p.ksplit)),
+                     dim3(256), 0, st, m, x, B, nblk, p.ksplit, partial, arr);
+}
+template <bool GU, int NR>
+static void dense2_launch_nr(const QmmDense &m, const float *x, int B, int nblk,
+                             const Dense2Plan &p, float *partial, Arrivals arr, hipStream_t st) {
+  if (p.rb == 8 && p.upk == 2) dense2_launch<GU, NR, 8, 2>(m, x, B, nblk, p, partial, arr, st);
+  else if (p.rb == 8) dense2_launch<GU, NR, 8, 4>(m, x, B, nblk, p, partial, arr, st);
+  else if (p.upk == 2) dense2_launch<GU, NR, 16, 2>(m, x, B, nblk, p, partial, arr, st);
+  else dense2_launch<GU, NR, 16, 4>(m, x, B, nblk, p, partial, arr, st);
+}
+
+static int launch_qmm_dense2(const QmmDense &m, int64_t k, const float *x, int64_t batch, char *ws,
+                             unsigned long long *counters, int max_counters, hipStream_t st) {
+  const bool gu = m.swiglu != 0;
+  const int64_t rows = gu ? m.cum[1] : m.cum[m.nparts];
+  const Dense2Plan p = dense2_plan(rows, k, batch, gu, 0);
+  if ((p.ksplit > 1 && p.tiles > max_counters) || p.ksplit > kMaxSlicesInline) return -2;
+  const Arrivals arr{counters, p.ksplit > 1 ? call_tag() : 0ull};
+  float *partial = (float *)ws;
+  const int B = (int)batch, nblk = (int)(k / 256);
+  if (gu) dense2_launch_nr<true, 2>(m, x, B, nblk, p, partial, arr, st);
+  else if (p.nr == 2) dense2_launch_nr<false, 2>(m, x, B, nblk, p, partial, arr, st);
+  else dense2_launch_nr<false, 1>(m, x, B, nblk, p, partial, arr, st);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_qmm_dense(const QmmDense &m, int64_t k, const float *x, int64_t batch, char *ws,
                      unsigned long long *counters, int max_counters, hipStream_t st) {
+  if (dense2_ok(k, x, batch)) return launch_qmm_dense2(m, k, x, batch, ws, counters, max_counters, st);
   const int64_t rows = m.swiglu ? m.cum[1] : m.cum[m.nparts];
   const int nblk = (int)(k / 256), upk = dense_upk(k), ksplit = (nblk + upk - 1) / upk;
   const int64_t tiles = dense_tiles(rows, m.swiglu != 0);

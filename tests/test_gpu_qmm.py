@@ -155,3 +155,87 @@ def test_qmm_dense_without_workspace():
     y = host(tq.gemv("q4_k", dev(w), n, k, dev(x), ws=False))
     ref, mag = oracle.gemv("q4_k", w, n, k, x)
     assert_product_close(y, ref, mag, what="dense no-ws")
+
+
+# ---- the in-kernel split (2..16 tokens): every launch shape -----------------------------------
+
+INLINE_SHAPES = [(300, 4096, 2), (1000, 2048, 8), (64, 14336, 8), (257, 512, 16), (130, 4608, 9),
+                 (70, 768, 5), (129, 1280, 3)]
+
+
+@pytest.mark.parametrize("upk,nr", [(2, 1), (2, 2), (4, 1), (4, 2)])
+@pytest.mark.parametrize("n,k,batch", INLINE_SHAPES)
+def test_qmm_dense_inline_launch_shapes(knobs, upk, nr, n, k, batch):
+    """Slices of 2 or 4 blocks (a ragged last slice where the block count is not a multiple),
+    one or two 16-row weight tiles per wave, 8 or 16 token rows per block, ragged row tiles; every
+    output against the oracle, at fp32 level, and repeatable bitwise."""
+    knobs("qmm_inline_upk", upk)
+    knobs("qmm_inline_nr", nr)
+    _case("qmm-inline", upk, nr, n, k, batch)
+    g = synth.rng(415, "inline", n, k, batch)
+    w = synth.blob("q4_k", g, n, k)
+    x = synth.normal_f32(g, (batch, k))
+    y = host(tq.gemv("q4_k", dev(w), n, k, dev(x)))
+    ref, mag = oracle.gemv("q4_k", w, n, k, x)
+    worst = assert_product_close(y, ref, mag, what=f"inline {n}x{k} b{batch} upk{upk} nr{nr}")
+    assert worst < 0.05, worst
+    y2 = host(tq.gemv("q4_k", dev(w), n, k, dev(x)))
+    assert np.array_equal(y, y2), "not deterministic"
+
+
+@pytest.mark.parametrize("upk", [2, 4])
+@pytest.mark.parametrize("F,k,batch", [(448, 4096, 8), (200, 1536, 13), (64, 2304, 2)])
+def test_qmm_dense_inline_swiglu_and_multi(knobs, upk, F, k, batch):
+    """gate|up + SwiGLU and a three-matrix launch against the single products of the same
+    slices, bitwise; the single products against the oracle."""
+    knobs("qmm_inline_upk", upk)
+    _case("qmm-inline-fused", upk, F, k, batch)
+    g = synth.rng(416, "inline-fused", F, k, batch)
+    wg, wu = synth.blob("q4_k", g, F, k), synth.blob("q4_k", g, F, k)
+    xh = synth.normal_f32(g, (batch, k))
+    x = dev(xh)
+    gg = tq.gemv("q4_k", dev(wg), F, k, x)
+    uu = tq.gemv("q4_k", dev(wu), F, k, x)
+    ref, mag = oracle.gemv("q4_k", wg, F, k, xh)
+    assert assert_product_close(host(gg), ref, mag, what="gate") < 0.05
+    h = host(tq.gemv_swiglu("q4_k", dev(wg), dev(wu), F, k, x))
+    assert np.array_equal(h, host(tq.swiglu(gg, uu)))
+    ns = [F, 96, 33]
+    ws = [wg, synth.blob("q4_k", g, 96, k), synth.blob("q4_k", g, 33, k)]
+    outs = tq.gemv_multi("q4_k", [dev(w) for w in ws], ns, k, x)
+    for w, n, o in zip(ws, ns, outs):
+        assert np.array_equal(host(o), host(tq.gemv("q4_k", dev(w), n, k, x)))
+
+
+def test_qmm_dense_inline_blocks_of_any_scale():
+    """Each (token, 256-value block) gets its own power of two: blocks of magnitude 1e-12 and
+    1e12 in one row, an all-zero block, one huge element, a row at 2^-100 and one at 1e30 keep
+    fp32 accuracy."""
+    n, k, batch = 256, 2048, 7
+    g = synth.rng(417, "inline-scale")
+    w = synth.blob("q4_k", g, n, k)
+    x = synth.normal_f32(g, (batch, k))
+    x[0, :256] *= np.float32(1e-12)
+    x[0, 256:512] *= np.float32(1e12)
+    x[1, 512:768] = 0.0
+    x[2, 1000] = np.float32(3e4)
+    x[3] *= np.float32(2.0 ** -100)
+    x[4] *= np.float32(1e30)
+    x[5, 1792:] *= np.float32(1e-30)
+    _case("qmm-inline-scale")
+    y = host(tq.gemv("q4_k", dev(w), n, k, dev(x)))
+    ref, mag = oracle.gemv("q4_k", w, n, k, x)
+    worst = assert_product_close(y, ref, mag, what="inline any-scale")
+    assert worst < 0.05, worst
+    assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("n,k,batch", [(1000, 4096, 8), (96, 3072, 12)])
+def test_qmm_dense_inline_agrees_with_split_launch(knobs, n, k, batch):
+    """The in-kernel split against the separate split launch (per-row scale): fp32 rounding apart."""
+    g = synth.rng(418, "inline-vs-split", n, k, batch)
+    w, x = dev(synth.blob("q4_k", g, n, k)), dev(synth.normal_f32(g, (batch, k)))
+    a = host(tq.gemv("q4_k", w, n, k, x))
+    knobs("qmm_inline", 0)
+    b = host(tq.gemv("q4_k", w, n, k, x))
+    assert np.linalg.norm(a - b) / np.linalg.norm(b) < 1e-6
