@@ -511,8 +511,8 @@ struct DenseEpi {
     const int vrow = tile * 128 + rt;
     if (vrow < m->cum[m->nparts]) {
       const DensePart q = dense_part(*m, vrow);
-      pick4(m->y[0], m->y[1], m->y[2], m->y[3], q.p)[(int64_t)tok * (q.last - q.first) +
-                                                      (vrow - q.first)] = v;
+      gstore(pick4(m->y[0], m->y[1], m->y[2], m->y[3], q.p) + (int64_t)tok * (q.last - q.first) +
+                 (vrow - q.first), v);
     }
   }
 
@@ -632,30 +632,38 @@ __global__ __launch_bounds__(256) void k_qmm_dense(QmmDense m, SplitRows x, int 
 // folded with its own 2^-e. NR 16-row weight tiles per wave (gate / up: always the pair). RB LDS
 // token rows per block: 8 (up to 8 tokens; operand rows 8..15 repeat rows 0..7 and their outputs
 // are never stored) or 16.
-template <int RB, int UPK>
-struct DenseLds {
-  static constexpr int kX = UPK * RB * kXBlockBytes;  // split blocks [block][row][1 KB]
-  static constexpr int kAux = UPK * RB * kAuxBytes;   // sub-block sums [block][row][32 B]
-  static constexpr int kUs = UPK * RB * 4;            // 2^-e [block][row]
-  static constexpr int kBytes = kX + kAux + kUs;
-};
-constexpr int kMaxSlicesInline = 32;
-
-// Wave-wide maximum (every lane gets it); exact in any order.
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) v = fmaxf(v, xor_recv(v, d));
-  return v;
+// Largest value over each 32-lane half of the wave (every lane of the half gets it): quad
+// exchanges and row rotations by 4 and 8 give the maximum over a row of 16 lanes, a swap of
+// neighbouring rows the maximum over two. Register moves only, no LDS.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xF, 0xF, false));
+}
+__device__ __forceinline__ float half_wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  v = fmaxf(v, dpp_f<0x124>(v));  // row_ror:4
+  v = fmaxf(v, dpp_f<0x128>(v));  // row_ror:8
+  const auto sw = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v),
+                                                   __builtin_bit_cast(unsigned, v), false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)sw[0]), __builtin_bit_cast(float, (unsigned)sw[1]));
 }
 
-// Splits the (block, token) pair `pair` of the slice, whose 256 fp32 values the wave holds as
-// lane l's float4 l, into LDS: scaled hi / lo halves in the operand order with the row's piece
-// swizzle, the sub-block sums and the pair's 2^-e.
-template <int RB, int UPK>
-__device__ __forceinline__ void dense_split_pair(float4 v, int b, int t, uint8_t *lds) {
-  using L = DenseLds<RB, UPK>;
-  const int lane = threadIdx.x & 63;
-  const float mx = wave_max(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+// Splits one (block, token) pair of activations into LDS. A half wave holds the pair's 256
+// fp32 values, lane q of the half values 8q .. 8q+7 (run q of the block). The pair's power of
+// two 2^e puts its largest magnitude (a half-wave maximum) into [2^14, 2^15); the scaled values
+// go to xr, the pair's 1 KB row (hi halves, then lo halves at +512, each run of 8 in the order
+// 0,2,1,3,4,6,5,7, run q stored at 16-byte piece q ^ swz); 2^-6 times each sub-block's sum of
+// the scaled values (a quad's sum of its fp32 values, times 2^e) to ar (hi halves, then lo,
+// sub-blocks in the same order); and 2^-e to *us.
+__device__ __forceinline__ void split_pair_half(float4 v0, float4 v1, int swz, uint8_t *xr,
+                                                uint8_t *ar, float *us) {
+  const int q = threadIdx.x & 31;
+  const float mx = half_wave_max(fmaxf(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)),
+                                             fmaxf(fabsf(v0.z), fabsf(v0.w))),
+                                       fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)),
+                                             fmaxf(fabsf(v1.z), fabsf(v1.w)))));
   int e = 0;
   if (mx > 0.f) {
     int ex;
@@ -664,35 +672,40 @@ __device__ __forceinline__ void dense_split_pair(float4 v, int b, int t, uint8_t
     if (e > 126) e = 126;
   }
   const float s = ldexpf(1.f, e);
-  const float a[4] = {v.x * s, v.y * s, v.z * s, v.w * s};
-  _Float16 hi[4], lo[4];
-  float sum = 0.f;
+  const float a[8] = {v0.x * s, v0.y * s, v0.z * s, v0.w * s, v1.x * s, v1.y * s, v1.z * s, v1.w * s};
+  half8 h8, l8;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    hi[i] = (_Float16)a[i];
-    lo[i] = (_Float16)(a[i] - (float)hi[i]);
-    sum += (float)hi[i] + (float)lo[i];
+  for (int i = 0; i < 8; ++i) {
+    const _Float16 hi = (_Float16)a[perm8(i)];
+    h8[i] = hi;
+    l8[i] = (_Float16)(a[perm8(i)] - (float)hi);
   }
-  // lane l holds values 4l .. 4l+3: half (l & 1) of run l / 2, stored in the order 0,2,1,3
-  const half4 h4 = {hi[0], hi[2], hi[1], hi[3]}, l4 = {lo[0], lo[2], lo[1], lo[3]};
-  const int row = b * RB + t;
-  uint8_t *xr = lds + row * kXBlockBytes + 16 * ((lane >> 1) ^ t) + 8 * (lane & 1);
-  *reinterpret_cast<half4 *>(xr) = h4;
-  *reinterpret_cast<half4 *>(xr + 512) = l4;
-  // sub-block j = lanes 8j .. 8j+7
-  sum += xor_recv(sum, 1);
-  sum += xor_recv(sum, 2);
-  sum += xor_recv(sum, 4);
-  if ((lane & 7) == 0) {
-    const int j = lane >> 3;
-    const float s6 = sum * 0x1p-6f;
+  uint8_t *p = xr + 16 * (q ^ swz);
+  *reinterpret_cast<half8 *>(p) = h8;
+  *reinterpret_cast<half8 *>(p + 512) = l8;
+  // sub-block j = runs 4j .. 4j+3: a quad
+  float sum = ((v0.x + v0.y) + (v0.z + v0.w)) + ((v1.x + v1.y) + (v1.z + v1.w));
+  sum += dpp_f<0xB1>(sum);
+  sum += dpp_f<0x4E>(sum);
+  if ((q & 3) == 0) {
+    const int j = q >> 2;
+    const float s6 = sum * s * 0x1p-6f;
     const _Float16 sh = (_Float16)s6, sl = (_Float16)(s6 - (float)sh);
-    _Float16 *ap = reinterpret_cast<_Float16 *>(lds + L::kX + row * kAuxBytes);
+    _Float16 *ap = reinterpret_cast<_Float16 *>(ar);
     ap[perm8(j)] = sh;
     ap[8 + perm8(j)] = sl;
   }
-  if (lane == 0) reinterpret_cast<float *>(lds + L::kX + L::kAux)[row] = ldexpf(1.f, -e);
+  if (q == 0) *us = ldexpf(1.f, -e);
 }
+
+template <int RB, int UPK>
+struct DenseLds {
+  static constexpr int kX = UPK * RB * kXBlockBytes;  // split blocks [block][row][1 KB]
+  static constexpr int kAux = UPK * RB * kAuxBytes;   // sub-block sums [block][row][32 B]
+  static constexpr int kUs = UPK * RB * 4;            // 2^-e [block][row]
+  static constexpr int kBytes = kX + kAux + kUs;
+};
+constexpr int kMaxSlicesInline = 32;
 
 // Loops f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>).
 template <int N, int I = 0, class F>
@@ -729,17 +742,29 @@ __global__ __launch_bounds__(256) void k_qmm_dense2(QmmDense m, const float *__r
   const int lane = threadIdx.x & 63, t16 = lane & 15, g = lane >> 4, wave = wave_index();
   const int64_t ldx = (int64_t)kblocks * 256;
 
-  // 1. the slice's activations: wave w takes the pairs 4 j + w (block b = pair / RB, token
-  // t = pair % RB), lane l the values 4l .. 4l+3 of the block (1 KB per pair, coalesced)
-  constexpr int kIt = RB * UPK / 4;
-  float4 xv[kIt];
+  // 1. the slice's activations: pair p = b B + t (block b, token t) goes to half wave p % 8,
+  // lane q of the half taking values 8q .. 8q+7 of it (1 KB per pair, coalesced); (b, t) are
+  // stepped by 8 pairs without a division
+  constexpr int kIt = RB * UPK / 8;
+  const int hw = 2 * wave + (lane >> 5), q32 = lane & 31;
+  const int step_b = 8 / B, step_t = 8 - step_b * B;
+  int pb = hw / B, pt = hw - (hw / B) * B;
+  float4 xv[kIt][2];
 #pragma unroll
   for (int j = 0; j < kIt; ++j) {
-    const int pair = 4 * j + wave, b = pair / RB, t = pair % RB;
-    if (t < B && b < steps)
-      xv[j] = *reinterpret_cast<const float4 *>(x + t * ldx + (int64_t)(kb0 + b) * 256 + 4 * lane);
-    else
-      xv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (pb < steps) {
+      const float *src = x + pt * ldx + (int64_t)(kb0 + pb) * 256 + 8 * q32;
+      xv[j][0] = *reinterpret_cast<const float4 *>(src);
+      xv[j][1] = *reinterpret_cast<const float4 *>(src + 4);
+    } else {
+      xv[j][0] = xv[j][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    pt += step_t;
+    pb += step_b;
+    if (pt >= B) {
+      pt -= B;
+      ++pb;
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -765,10 +790,22 @@ __global__ __launch_bounds__(256) void k_qmm_dense2(QmmDense m, const float *__r
   __builtin_amdgcn_sched_barrier(0);
 
   // 3. split into LDS (waits for the activations only), then one barrier
+  pb = hw / B;
+  pt = hw - pb * B;
 #pragma unroll
   for (int j = 0; j < kIt; ++j) {
-    const int pair = 4 * j + wave, b = pair / RB, t = pair % RB;
-    if (t < B && b < steps) dense_split_pair<RB, UPK>(xv[j], b, t, lds);
+    if (pb < steps) {
+      const int row = pb * RB + pt;
+      split_pair_half(xv[j][0], xv[j][1], pt, lds + row * kXBlockBytes,
+                      lds + L::kX + row * kAuxBytes,
+                      reinterpret_cast<float *>(lds + L::kX + L::kAux) + row);
+    }
+    pt += step_t;
+    pb += step_b;
+    if (pt >= B) {
+      pt -= B;
+      ++pb;
+    }
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 
@@ -817,8 +854,8 @@ __global__ __launch_bounds__(256) void k_qmm_dense2(QmmDense m, const float *__r
   auto store = [&](int tok, int vrow, float v) {
     if (vrow < n) {
       const DensePart q = dense_part(m, vrow);
-      pick4(m.y[0], m.y[1], m.y[2], m.y[3], q.p)[(int64_t)tok * (q.last - q.first) +
-                                                  (vrow - q.first)] = v;
+      gstore(pick4(m.y[0], m.y[1], m.y[2], m.y[3], q.p) + (int64_t)tok * (q.last - q.first) +
+                 (vrow - q.first), v);
     }
   };
   if (ksplit == 1) {
