@@ -202,8 +202,8 @@ static bool use_i8s(int fmt, int64_t rows, int64_t k, const float *x, int64_t ba
   return i8s_gemv_ok(fmt, k, batch) && ((uintptr_t)x & 15) == 0 && rows < (1ll << 30);
 }
 
-static int launch_i8(const KlMap &m, int64_t k, const float *x, void *ws, hipStream_t s) {
-  return launch_gemv_i8(m, k, x, (float *)((char *)ws + kCounterBytes), (unsigned long long *)ws,
+static int launch_i8(int fmt, const KlMap &m, int64_t k, const float *x, void *ws, hipStream_t s) {
+  return launch_gemv_i8(fmt, m, k, x, (float *)((char *)ws + kCounterBytes), (unsigned long long *)ws,
                         (int)(kCounterBytes / 8), s);
 }
 
@@ -710,7 +710,7 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, in
     m.total = (int)n;
     m.row_bytes = rb;
     if (i8s) return launch_gemv_i8s(m, k, x, s);
-    if (i8) return launch_i8(m, k, x, ws, s);
+    if (i8) return launch_i8(fmt, m, k, x, ws, s);
     return launch_kl(m, k, x, s);
   }
   switch (fmt) {
@@ -763,7 +763,7 @@ int launch_gemv_multi(int fmt, int nparts, const void *const *w, const int64_t *
     m.row_bytes = k / fmt_block_weights(fmt) * fmt_block_bytes(fmt);
     if (f32m) return launch_f32m(fmt, m, k, x, batch, ws, s);
     if (i8s) return launch_gemv_i8s(m, k, x, s);
-    if (i8) return launch_i8(m, k, x, ws, s);
+    if (i8) return launch_i8(fmt, m, k, x, ws, s);
     return launch_kl(m, k, x, s);
   }
   for (int p = 0; p < nparts; ++p) {  // one launch per matrix, in order on the stream
@@ -824,7 +824,7 @@ int launch_gemv_swiglu(int fmt, const void *wg, const void *wu, int64_t n, int64
     m.cum[1] = m.total;
     m.row_bytes = rb;
     if (i8s) return launch_gemv_i8s(m, k, x, s);
-    if (i8) return launch_i8(m, k, x, ws, s);
+    if (i8) return launch_i8(fmt, m, k, x, ws, s);
     return launch_kl(m, k, x, s);
   }
   if (use_qmm(fmt, n, k, x, batch, ws, ws_bytes, true)) {

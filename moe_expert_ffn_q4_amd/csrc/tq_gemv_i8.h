@@ -1,4 +1,4 @@
-// tq_gemv_i8.h -- batch-1 Q4_K GEMV on the int8 matrix cores (internal to libtq).
+// tq_gemv_i8.h -- batch-1 Q4_K and Q8_0 GEMV on the int8 matrix cores (internal to libtq).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -144,16 +144,76 @@ __device__ __forceinline__ float i8_block(const u32x4 &head, const u32x4 (&q)[4]
   return __builtin_fmaf(d * us, bs, -dmin * us * ms);
 }
 
+// ---- Q8_0 on the same matrix cores ----
+// Eight Q8_0 blocks (fp16 d, 32 int8 quants: 34 bytes each) make one 256-weight unit of 272
+// bytes, and one 32-k step of the matrix cores is one block: the quants are int8 operands as they
+// are. Lane (row n, half h) needs bytes 34 j + 2 + 16 h .. +15 of the unit for block j: a
+// dword-aligned 16-byte load for odd j, and for even j (2 bytes past a dword) the 16 bytes before
+// it plus the next dword, realigned in registers. Its fold covers blocks 2 q + h, q = 0..3, whose
+// scales come out of the same loads: d of an even block is the first half-word of its first
+// load, d of an odd block the last half-word of the extra dword of the block before it (the
+// h = 1 lane's).
+struct Q8Unit {
+  u32x4 p[8];
+  uint32_t tail[4];  // the dword after the even blocks' 16 bytes
+  static constexpr int kLoads = 12;
+};
+
+__device__ __forceinline__ void q8_load_unit(Q8Unit &u, const uint8_t *unit, int h) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j & 1) {
+      u.p[j] = *(gu32x4a4)(unit + 34 * j + 2 + 16 * h);
+    } else {
+      u.p[j] = *(gu32x4a4)(unit + 34 * j + 16 * h);
+      u.tail[j >> 1] = *(const __attribute__((address_space(1))) uint32_t *)(unit + 34 * j + 16 * h + 16);
+    }
+  }
+}
+
+// The unit's products: the digits' sums of each block recombined (C0 + 2^7 C1 exactly in int32,
+// C2 + 2^7 C3 the same, then one fp32 FMA: |C| <= 32 * 64 * 128), times the block's d, added over
+// the lane's four blocks and scaled by the unit's 2^-e.
+__device__ __forceinline__ float q8_i8_unit(const Q8Unit &u, const u32x4 &xa, float us,
+                                            int my_blk, int h) {
+  const i32x16 zero = {};
+  i32x16 C;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    u32x4 bq = u.p[j];
+    if (!(j & 1)) {
+      const uint32_t t = u.tail[j >> 1];
+      bq = (u32x4){shift2(u.p[j].x, u.p[j].y), shift2(u.p[j].y, u.p[j].z),
+                   shift2(u.p[j].z, u.p[j].w), shift2(u.p[j].w, t)};
+    }
+    const u32x4 a = my_blk == j ? xa : (u32x4){0u, 0u, 0u, 0u};
+    C = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
+                                              __builtin_bit_cast(i32x4, bq), j == 0 ? zero : C,
+                                              0, 0, 0);
+  }
+  float bs = 0.f;
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    // rows 8 qq + 4h + digit of the accumulator: block 2 qq + h, digits 0..3
+    const int lo = C[4 * qq] + (C[4 * qq + 1] << 7);
+    const int hi = C[4 * qq + 2] + (C[4 * qq + 3] << 7);
+    const float f = __builtin_fmaf((float)hi, 0x1p14f, (float)lo);
+    const uint32_t dbits = h ? (u.tail[qq] >> 16) : (u.p[2 * qq].x & 0xFFFFu);
+    bs = __builtin_fmaf(half_bits_to_float(dbits), f, bs);
+  }
+  return bs * us;
+}
 
 // Shapes the int8 kernel takes: Q4_K, one token, k a multiple of 256, 16384 <= k <= 32768 (all
-// k <= 32768 with TQ_KNOB_GEMV_I8 = 2).
+// k <= 32768 with TQ_KNOB_GEMV_I8 = 2); Q8_0, one token, k a multiple of 256 up to 32768
+// (TQ_KNOB_GEMV_I8 = 0: never).
 bool i8_gemv_ok(int fmt, int64_t k, int64_t batch);
 // Workspace after the completion counters: the k slices' partial sums of `rows` rows (0 when k
 // is one slice).
 size_t i8_workspace_bytes(int64_t rows, int64_t k);
 // The rows of m against x [k] (16-byte aligned). partial: i8_workspace_bytes(m.total, k) bytes;
 // counters: one 8-byte word per row group (Arrivals; max_counters of them), any contents.
-int launch_gemv_i8(const KlMap &m, int64_t k, const float *x, float *partial,
+int launch_gemv_i8(int fmt, const KlMap &m, int64_t k, const float *x, float *partial,
                    unsigned long long *counters, int max_counters, hipStream_t s);
 
 // Streaming form (no workspace; opt-in with TQ_KNOB_GEMV_I8S = 1): Q4_K, one token, k a multiple of 256

@@ -1,4 +1,5 @@
-// tq_gemv_i8.hip -- batch-1 Q4_K GEMV with the multiply-adds on the int8 matrix cores.
+// tq_gemv_i8.hip -- batch-1 Q4_K and Q8_0 GEMV with the multiply-adds on the int8 matrix cores
+// (Q8_0: see the unit functions in tq_gemv_i8.h).
 //
 // Per 256-weight block of a row (d, dmin, sub-block scales sc_j and mins m_j, quants q) the product
 // with x is  d * sum_j sc_j sum_{k in j} q_k x_k  -  dmin * sum_j m_j S_j  (S_j = sum of x over
@@ -36,9 +37,46 @@ namespace tq {
 // Output of virtual row v (multi: the part it falls in).
 __device__ __forceinline__ void i8_store(const KlMap &m, int v, float s) { *m.out(v) = s; }
 
+// The 256-weight unit of each format: its bytes in a row, the lane's loads and its products.
+template <int FMT>
+struct I8Fmt;
+template <>
+struct I8Fmt<FMT_Q4_K> {
+  static constexpr int kUnitBytes = 144;
+  struct Blk {
+    u32x4 head, q[4];
+  };
+  static __device__ __forceinline__ void load(Blk &b, const uint8_t *p, int h) {
+    b.head = gload(p);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) b.q[c] = gload(p + 16 + 32 * c + 16 * h);
+  }
+  static __device__ __forceinline__ float compute(const Blk &b, const uint8_t *l, int n, int h) {
+    const u32x4 xa = *reinterpret_cast<const u32x4 *>(l + n * 32 + 16 * h);
+    const u32x4 S = *reinterpret_cast<const u32x4 *>(l + kDigitBytes + 16 * h);
+    const float us = *reinterpret_cast<const float *>(l + kDigitBytes + 32);
+    return i8_block(b.head, b.q, xa, S, us, n >> 2, h);
+  }
+};
+template <>
+struct I8Fmt<FMT_Q8_0> {
+  static constexpr int kUnitBytes = 272;
+  using Blk = Q8Unit;
+  static __device__ __forceinline__ void load(Blk &b, const uint8_t *p, int h) {
+    q8_load_unit(b, p, h);
+  }
+  static __device__ __forceinline__ float compute(const Blk &b, const uint8_t *l, int n, int h) {
+    const u32x4 xa = *reinterpret_cast<const u32x4 *>(l + n * 32 + 16 * h);
+    const float us = *reinterpret_cast<const float *>(l + kDigitBytes + 32);
+    return q8_i8_unit(b, xa, us, n >> 2, h);
+  }
+};
+
+template <int FMT>
 __global__ __launch_bounds__(256) void k_gemv_i8(KlMap m, const float *__restrict__ x, int nblk,
                                                  int upk, int ksplit, float *__restrict__ partial,
                                                  Arrivals arr) {
+  using F = I8Fmt<FMT>;
   __shared__ __attribute__((aligned(16))) uint8_t xl[kMaxSliceBlocks * kLdsBlock];
   __shared__ float red[4][32];
   __shared__ int is_last;
@@ -48,23 +86,10 @@ __global__ __launch_bounds__(256) void k_gemv_i8(KlMap m, const float *__restric
   const int lane = threadIdx.x & 63, w = wave_index();
   const int n = lane & 31, h = lane >> 5;
   const int r0 = grp * 32 * W + 32 * w;
-  const uint8_t *row = m.row(min(r0 + n, m.total - 1)) + (int64_t)kb0 * 144;
-  struct Blk {
-    u32x4 head, q[4];
-  };
-  auto load = [&](Blk &b, int kb) {
-    const uint8_t *p = row + (int64_t)kb * 144;
-    b.head = gload(p);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) b.q[c] = gload(p + 16 + 32 * c + 16 * h);
-  };
-  auto compute = [&](const Blk &b, int kb) {
-    const uint8_t *l = xl + kb * kLdsBlock;
-    const u32x4 xa = *reinterpret_cast<const u32x4 *>(l + n * 32 + 16 * h);
-    const u32x4 S = *reinterpret_cast<const u32x4 *>(l + kDigitBytes + 16 * h);
-    const float us = *reinterpret_cast<const float *>(l + kDigitBytes + 32);
-    return i8_block(b.head, b.q, xa, S, us, n >> 2, h);
-  };
+  const uint8_t *row = m.row(min(r0 + n, m.total - 1)) + (int64_t)kb0 * F::kUnitBytes;
+  using Blk = typename F::Blk;
+  auto load = [&](Blk &b, int kb) { F::load(b, row + (int64_t)kb * F::kUnitBytes, h); };
+  auto compute = [&](const Blk &b, int kb) { return F::compute(b, xl + kb * kLdsBlock, n, h); };
   // the first two blocks' weights are requested before the digits are made, so both latencies
   // overlap; then two blocks stay in flight ahead of the one being computed
   Blk b0, b1;
@@ -222,10 +247,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_i8s(KlMap m, const float *__re
 // work per weight hold it back there. TQ_KNOB_GEMV_I8: 0 never, 2 every such shape (tests, tuning).
 bool i8_gemv_ok(int fmt, int64_t k, int64_t batch) {
   const int mode = knob(TQ_KNOB_GEMV_I8, 1);
-  if (mode == 0 || fmt != FMT_Q4_K || batch != 1 || k % 256 != 0 || k < 256 ||
-      k > 256 * kMaxSliceBlocks * kMaxSlices)
+  if (mode == 0 || (fmt != FMT_Q4_K && fmt != FMT_Q8_0) || batch != 1 || k % 256 != 0 ||
+      k < 256 || k > 256 * kMaxSliceBlocks * kMaxSlices)
     return false;
-  return mode == 2 || k >= 16384;
+  return fmt == FMT_Q8_0 || mode == 2 || k >= 16384;
 }
 
 // Blocks per k slice, a function of k only: at least four, at most 8 slices.
@@ -251,15 +276,20 @@ size_t i8_workspace_bytes(int64_t rows, int64_t k) {
   return (size_t)align256(groups * ksplit * 32 * W * 4);
 }
 
-int launch_gemv_i8(const KlMap &m, int64_t k, const float *x, float *partial,
+int launch_gemv_i8(int fmt, const KlMap &m, int64_t k, const float *x, float *partial,
                    unsigned long long *counters, int max_counters, hipStream_t s) {
   const int nblk = (int)(k / 256), upk = i8_upk(k), ksplit = (nblk + upk - 1) / upk;
   if (upk > kMaxSliceBlocks || ksplit > kMaxSlices) return -2;
   const int W = i8_tiles_per_wg(m.total, ksplit);
   const int groups = (m.total + 32 * W - 1) / (32 * W);
   if (ksplit > 1 && groups > max_counters) return -2;
-  hipLaunchKernelGGL(k_gemv_i8, dim3((unsigned)(groups * ksplit)), dim3(64 * W), 0, s, m, x, nblk,
-                     upk, ksplit, partial, Arrivals{counters, ksplit > 1 ? call_tag() : 0ull});
+  const Arrivals arr{counters, ksplit > 1 ? call_tag() : 0ull};
+  if (fmt == FMT_Q8_0)
+    hipLaunchKernelGGL(k_gemv_i8<FMT_Q8_0>, dim3((unsigned)(groups * ksplit)), dim3(64 * W), 0, s,
+                       m, x, nblk, upk, ksplit, partial, arr);
+  else
+    hipLaunchKernelGGL(k_gemv_i8<FMT_Q4_K>, dim3((unsigned)(groups * ksplit)), dim3(64 * W), 0, s,
+                       m, x, nblk, upk, ksplit, partial, arr);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

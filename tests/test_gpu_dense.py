@@ -255,3 +255,68 @@ def test_gemv_lane_groups_bitwise(knobs, n, k):
     h = host(tq.gemv_swiglu("q4_k", dev(wg), dev(wu), F, k, xd))
     gg, uu = tq.gemv("q4_k", dev(wg), F, k, xd), tq.gemv("q4_k", dev(wu), F, k, xd)
     assert np.array_equal(h, host(tq.swiglu(gg, uu)))
+
+
+# ---- Q8_0 at batch 1 on the int8 matrix cores -----------------------------------------------------
+
+@pytest.mark.parametrize("n,k", [(1000, 8192), (64, 256), (333, 28672), (77, 512), (130, 2304),
+                                 (4096, 1024)])
+def test_q8_0_int8_matrix_cores(knobs, n, k):
+    """One token of Q8_0 on the int8 matrix cores (8 blocks of 34 bytes per 256-weight unit, the
+    even blocks realigned in registers): one slice (k = 256, 512, 1024), several with a ragged
+    last slice (k = 2304, 28672); every output against the oracle at fp32 level, and against
+    the lane-per-row fp32 kernel (TQ_KNOB_GEMV_I8 = 0)."""
+    _print_case("q8_0 int8", n, k)
+    g = synth.rng(109, "q8i8", n, k)
+    w = synth.blob("q8_0", g, n, k)
+    x = synth.normal_f32(g, (1, k))
+    wd, xd = dev(w), dev(x)
+    y = host(tq.gemv("q8_0", wd, n, k, xd))
+    ref, mag = oracle.gemv("q8_0", w, n, k, x)
+    worst = assert_product_close(y, ref, mag, what=f"q8_0 {n}x{k}")
+    assert worst < 0.05, worst
+    assert np.array_equal(y, host(tq.gemv("q8_0", wd, n, k, xd))), "not deterministic"
+    knobs("gemv_i8", 0)
+    y0 = host(tq.gemv("q8_0", wd, n, k, xd))
+    assert np.linalg.norm(y - y0) / np.linalg.norm(y0) < 1e-6
+
+
+def test_q8_0_int8_extremes():
+    """Quants at -128 and 127 in every block, fp16 scales at their largest and in the subnormal
+    range, and activation blocks of 1e-30, 1e20 and zero: the digit sums stay exact and the fold
+    stays within the bar."""
+    n, k = 96, 2048
+    _print_case("q8_0 int8 extremes")
+    g = synth.rng(110, "q8i8-ext")
+    w = synth.blob("q8_0", g, n, k)
+    blk = w.reshape(-1, 34)
+    blk[0::3, 2:] = np.uint8(0x80)  # -128
+    blk[1::3, 2:] = np.uint8(0x7F)  # 127
+    blk[0::5, 0:2] = np.frombuffer(np.float16(65504.0).tobytes(), np.uint8)
+    blk[1::7, 0:2] = np.frombuffer(np.float16(2.0 ** -20).tobytes(), np.uint8)
+    x = synth.normal_f32(g, (1, k))
+    x[0, :256] *= np.float32(1e-30)
+    x[0, 256:512] = 0.0
+    x[0, 512:768] *= np.float32(1e20)
+    y = host(tq.gemv("q8_0", dev(w), n, k, dev(x)))
+    ref, mag = oracle.gemv("q8_0", w, n, k, x)
+    assert_product_close(y, ref, mag, what="q8_0 extremes")
+
+
+def test_q8_0_int8_multi_and_swiglu_bitwise():
+    """Q8_0 one-token multi and gate|up + SwiGLU launches on the int8 matrix cores give bitwise
+    the single products (k slices set by k alone)."""
+    k = 4096
+    g = synth.rng(111, "q8i8-multi")
+    ns = [512, 128, 96]
+    ws = [synth.blob("q8_0", g, n, k) for n in ns]
+    x = dev(synth.normal_f32(g, (1, k)))
+    outs = tq.gemv_multi("q8_0", [dev(w) for w in ws], ns, k, x)
+    for w, n, o in zip(ws, ns, outs):
+        assert np.array_equal(host(o), host(tq.gemv("q8_0", dev(w), n, k, x)))
+    F = 320
+    wg, wu = synth.blob("q8_0", g, F, k), synth.blob("q8_0", g, F, k)
+    h = host(tq.gemv_swiglu("q8_0", dev(wg), dev(wu), F, k, x))
+    gg = tq.gemv("q8_0", dev(wg), F, k, x)
+    uu = tq.gemv("q8_0", dev(wu), F, k, x)
+    assert np.array_equal(h, host(tq.swiglu(gg, uu)))

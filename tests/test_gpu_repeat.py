@@ -46,16 +46,16 @@ def test_repeat_qmm_dense(n, k, batch):
     _repeat(lambda: tq.gemv("q4_k", w, n, k, x, out=y, ws=ws), y)
 
 
-def test_repeat_gemv_i8():
-    """k_gemv_i8 (Q4_K, one token, k >= 16384)."""
-    n, k = 3000, 16384
-    _case("repeat gemv_i8", n, k)
-    g = synth.rng(82, "rep-i8")
-    w = dev(synth.blob("q4_k", g, n, k))
+@pytest.mark.parametrize("t,n,k", [("q4_k", 3000, 16384), ("q8_0", 3000, 8192)])
+def test_repeat_gemv_i8(t, n, k):
+    """k_gemv_i8 (Q4_K from k = 16384, Q8_0: one token)."""
+    _case("repeat gemv_i8", t, n, k)
+    g = synth.rng(82, "rep-i8", t)
+    w = dev(synth.blob(t, g, n, k))
     x = dev(synth.normal_f32(g, (1, k)))
     y = torch.empty((1, n), dtype=torch.float32, device="cuda:0")
-    ws = torch.zeros(tq.gemv_workspace_bytes("q4_k", n, k, 1), dtype=torch.uint8, device="cuda:0")
-    _repeat(lambda: tq.gemv("q4_k", w, n, k, x, out=y, ws=ws), y)
+    ws = torch.zeros(tq.gemv_workspace_bytes(t, n, k, 1), dtype=torch.uint8, device="cuda:0")
+    _repeat(lambda: tq.gemv(t, w, n, k, x, out=y, ws=ws), y)
 
 
 @pytest.mark.parametrize("path,T", [(tq.PATH_F32, 16), (tq.PATH_F32, 64),
