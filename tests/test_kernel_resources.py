@@ -13,11 +13,13 @@ from moe_expert_ffn_q4_amd import build
 HOT = [
     (r"k_gemv_klILi4E", 2),          # batch-1 Q4_K GEMV, lanes along k
     (r"k_moe_klILi4E", 2),           # one-token MoE experts
-    (r"k_gemv_i8E", 4),              # batch-1 Q4_K GEMV, int8 matrix cores, sliced k
+    (r"k_gemv_i8ILi1E", 4),          # batch-1 Q4_K GEMV, int8 matrix cores, sliced k
+    (r"k_gemv_i8ILi3E", 3),          # batch-1 Q8_0 GEMV, int8 matrix cores, sliced k
     (r"k_gemv_i8sI", 2),             # the streaming form
     (r"k_gemm_f32m_q8", 4),          # Q8_0 batches, fp32 matrix cores
     (r"k_gemm_f32m_q6", 2),          # Q6_K batches
     (r"k_qmm_denseI", 1),            # dense few-token Q4_K products, fp16 matrix cores
+    (r"k_qmm_dense2I", 2),           # the same with the activations split in the kernel
     (r"k_qmmILb", 1),                # MoE few-token products
     (r"k_prefillI", 1),              # prompt-sized MoE products, bf16 matrix cores
     (r"k_gemvILi[123]ELi[1248]E", 1),  # fp32 lane-per-row GEMV
