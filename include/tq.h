@@ -387,28 +387,23 @@ enum {
   TQ_KNOB_KL_TARGET_WAVES = 5, /* lanes-along-k kernel: waves the launch aims for (2048) */
   TQ_KNOB_GEMM_F32M = 6, /* Q6_K / Q8_0 batches on the fp32 matrix cores: 1 default shapes, 0 never, 2 every batch */
   TQ_KNOB_F32M_UPK = 7, /* fp32 matrix-core kernel: blocks per k slice (8) */
-  TQ_KNOB_GEMV_I8 = 8, /* int8 matrix-core batch-1 Q4_K GEMV: 1 from k = 16384 (default), 0 never, 2 always */
+  TQ_KNOB_GEMV_I8 = 8, /* int8 matrix-core batch-1 GEMV: 1 Q4_K from k = 16384 and Q8_0 always (default), 0 never, 2 Q4_K always too */
   TQ_KNOB_I8_UPK = 9, /* int8 matrix-core kernel: blocks per k slice (4) */
-  TQ_KNOB_GEMV_I8S = 10, /* streaming int8 GEMV: 0 off (default), 1 on */
-  TQ_KNOB_I8S_NW = 11, /* streaming int8 GEMV: waves per workgroup (8) */
-  TQ_KNOB_I8S_D = 12, /* streaming int8 GEMV: blocks in flight per wave (4) */
-  TQ_KNOB_I8S_KS = 13, /* streaming int8 GEMV: k parts (0: chosen from k) */
-  TQ_KNOB_I8S_PART = 14, /* streaming int8 GEMV: least blocks per k part (4) */
-  TQ_KNOB_MOE_QMM = 15, /* MoE steps of 2+ tokens on the fp16 matrix cores: 1 on (default), 0 grouped fp32 GEMV */
-  TQ_KNOB_QMM_NT = 16, /* fp16 matrix-core MoE kernel: chunks of 16 (1) or 32 (2) positions (0: chosen from the mean tokens per expert) */
-  TQ_KNOB_MOE_NT = 17, /* grouped fp32 MoE GEMV: token tile 1, 2, 4 or 8 (0: chosen from the mean tokens per expert) */
-  TQ_KNOB_ROUTER_KL = 18, /* router for up to 8 tokens with lanes along the hidden dimension: 1 on (default), 0 off */
-  TQ_KNOB_ROUTER_STEPS = 19, /* that router: 256-value steps per hidden slice (1) */
-  TQ_KNOB_ROUTER_MF = 20, /* router for more than 8 tokens and 64+ experts on the fp32 matrix cores: 1 on (default), 0 off */
-  TQ_KNOB_GROUP1 = 21, /* one token: grouping written by the top-k kernel: 1 on (default), 0 the grouping kernel */
-  TQ_KNOB_COMBINE4 = 22, /* combine by 16-byte column runs: 1 on (default), 0 element-wise */
-  TQ_KNOB_FUSE_COMBINE = 23, /* one token: combine inside the down launch: 1 on (default), 0 a combine launch */
-  TQ_KNOB_GEMV_QMM = 24, /* Q4_K GEMV of 2..32 tokens on the fp16 matrix cores: 1 on (default), 0 off */
-  TQ_KNOB_QMM_UPK = 25, /* fp16 matrix-core dense kernel with a split launch: blocks per k slice (4) */
-  TQ_KNOB_QMM_INLINE = 26, /* Q4_K GEMV of 2..16 tokens: activations split inside the product kernel: 1 on (default), 0 a split launch first */
-  TQ_KNOB_QMM_INLINE_UPK = 27, /* that kernel: blocks per k slice, 2 or 4 (0: 2 for k <= 4096, else 4) */
-  TQ_KNOB_QMM_INLINE_NR = 28, /* that kernel: 16-row weight tiles per wave of a product without SwiGLU, 1 (default) or 2 */
-  TQ_KNOB_COUNT = 29
+  TQ_KNOB_MOE_QMM = 10, /* MoE steps of 2+ tokens on the fp16 matrix cores: 1 on (default), 0 grouped fp32 GEMV */
+  TQ_KNOB_QMM_NT = 11, /* fp16 matrix-core MoE kernel: chunks of 16 (1) or 32 (2) positions (0: chosen from the mean tokens per expert) */
+  TQ_KNOB_MOE_NT = 12, /* grouped fp32 MoE GEMV: token tile 1, 2, 4 or 8 (0: chosen from the mean tokens per expert) */
+  TQ_KNOB_ROUTER_KL = 13, /* router for up to 8 tokens with lanes along the hidden dimension: 1 on (default), 0 off */
+  TQ_KNOB_ROUTER_STEPS = 14, /* that router: 256-value steps per hidden slice (1) */
+  TQ_KNOB_ROUTER_MF = 15, /* router for more than 8 tokens and 64+ experts on the fp32 matrix cores: 1 on (default), 0 off */
+  TQ_KNOB_GROUP1 = 16, /* one token: grouping written by the top-k kernel: 1 on (default), 0 the grouping kernel */
+  TQ_KNOB_COMBINE4 = 17, /* combine by 16-byte column runs: 1 on (default), 0 element-wise */
+  TQ_KNOB_FUSE_COMBINE = 18, /* one token: combine inside the down launch: 1 on (default), 0 a combine launch */
+  TQ_KNOB_GEMV_QMM = 19, /* Q4_K GEMV of 2..32 tokens on the fp16 matrix cores: 1 on (default), 0 off */
+  TQ_KNOB_QMM_UPK = 20, /* fp16 matrix-core dense kernel with a split launch: blocks per k slice (4) */
+  TQ_KNOB_QMM_INLINE = 21, /* Q4_K GEMV of 2..16 tokens: activations split inside the product kernel: 1 on (default), 0 a split launch first */
+  TQ_KNOB_QMM_INLINE_UPK = 22, /* that kernel: blocks per k slice, 2 or 4 (0: 2 for k <= 4096, else 4) */
+  TQ_KNOB_QMM_INLINE_NR = 23, /* that kernel: 16-row weight tiles per wave of a product without SwiGLU, 1 (default) or 2 */
+  TQ_KNOB_COUNT = 24
 };
 int tq_tuning_set(int knob, int value);
 int tq_tuning_get(int knob);

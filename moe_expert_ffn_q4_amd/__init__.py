@@ -426,25 +426,20 @@ KNOBS = {
     "f32m_upk": 7,
     "gemv_i8": 8,
     "i8_upk": 9,
-    "gemv_i8s": 10,
-    "i8s_nw": 11,
-    "i8s_d": 12,
-    "i8s_ks": 13,
-    "i8s_part": 14,
-    "moe_qmm": 15,
-    "qmm_nt": 16,
-    "moe_nt": 17,
-    "router_kl": 18,
-    "router_steps": 19,
-    "router_mf": 20,
-    "group1": 21,
-    "combine4": 22,
-    "fuse_combine": 23,
-    "gemv_qmm": 24,
-    "qmm_upk": 25,
-    "qmm_inline": 26,
-    "qmm_inline_upk": 27,
-    "qmm_inline_nr": 28,
+    "moe_qmm": 10,
+    "qmm_nt": 11,
+    "moe_nt": 12,
+    "router_kl": 13,
+    "router_steps": 14,
+    "router_mf": 15,
+    "group1": 16,
+    "combine4": 17,
+    "fuse_combine": 18,
+    "gemv_qmm": 19,
+    "qmm_upk": 20,
+    "qmm_inline": 21,
+    "qmm_inline_upk": 22,
+    "qmm_inline_nr": 23,
 }
 
 
@@ -459,7 +454,7 @@ def get_knob(name: str) -> int:
 
 
 class knobs:
-    """Context manager: knobs(gemv_i8=2, gemv_i8s=0) sets overrides and restores the previous
+    """Context manager: knobs(gemv_i8=2, kl_rows=2) sets overrides and restores the previous
     values on exit."""
 
     def __init__(self, **values):

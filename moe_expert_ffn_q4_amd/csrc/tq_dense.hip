@@ -197,10 +197,6 @@ static int launch_f32m(int fmt, const KlMap &m, int64_t k, const float *x, int64
                           (unsigned long long *)ws, (int)(kCounterBytes / 8), s);
 }
 
-// The streaming int8 path needs no workspace, only a 16-byte aligned x.
-static bool use_i8s(int fmt, int64_t rows, int64_t k, const float *x, int64_t batch) {
-  return i8s_gemv_ok(fmt, k, batch) && ((uintptr_t)x & 15) == 0 && rows < (1ll << 30);
-}
 
 static int launch_i8(int fmt, const KlMap &m, int64_t k, const float *x, void *ws, hipStream_t s) {
   return launch_gemv_i8(fmt, m, k, x, (float *)((char *)ws + kCounterBytes), (unsigned long long *)ws,
@@ -699,9 +695,8 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, in
     m.row_bytes = rb;
     return launch_f32m(fmt, m, k, x, batch, ws, s);
   }
-  const bool i8s = use_i8s(fmt, n, k, x, batch);
-  const bool i8 = !i8s && use_i8(fmt, n, k, x, batch, ws, ws_bytes);
-  if (i8s || i8 || klane_ok(fmt, k, x, batch)) {
+  const bool i8 = use_i8(fmt, n, k, x, batch, ws, ws_bytes);
+  if (i8 || klane_ok(fmt, k, x, batch)) {
     KlMap m{};
     m.w[0] = wb;
     m.y[0] = y;
@@ -709,7 +704,6 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, in
     m.nparts = 1;
     m.total = (int)n;
     m.row_bytes = rb;
-    if (i8s) return launch_gemv_i8s(m, k, x, s);
     if (i8) return launch_i8(fmt, m, k, x, ws, s);
     return launch_kl(m, k, x, s);
   }
@@ -749,9 +743,8 @@ int launch_gemv_multi(int fmt, int nparts, const void *const *w, const int64_t *
                             (unsigned long long *)ws, (int)(kCounterBytes / 8), s);
   }
   const bool f32m = use_f32m(fmt, total, k, x, batch, ws, ws_bytes);
-  const bool i8s = !f32m && use_i8s(fmt, total, k, x, batch);
-  const bool i8 = !f32m && !i8s && use_i8(fmt, total, k, x, batch, ws, ws_bytes);
-  if ((f32m || i8s || i8 || klane_ok(fmt, k, x, batch)) && nparts <= 4 && total < (1ll << 30)) {
+  const bool i8 = !f32m && use_i8(fmt, total, k, x, batch, ws, ws_bytes);
+  if ((f32m || i8 || klane_ok(fmt, k, x, batch)) && nparts <= 4 && total < (1ll << 30)) {
     KlMap m{};
     for (int p = 0; p < nparts; ++p) {
       m.w[p] = (const uint8_t *)w[p];
@@ -762,7 +755,6 @@ int launch_gemv_multi(int fmt, int nparts, const void *const *w, const int64_t *
     m.total = (int)total;
     m.row_bytes = k / fmt_block_weights(fmt) * fmt_block_bytes(fmt);
     if (f32m) return launch_f32m(fmt, m, k, x, batch, ws, s);
-    if (i8s) return launch_gemv_i8s(m, k, x, s);
     if (i8) return launch_i8(fmt, m, k, x, ws, s);
     return launch_kl(m, k, x, s);
   }
@@ -811,9 +803,8 @@ int launch_gemv_swiglu(int fmt, const void *wg, const void *wu, int64_t n, int64
     m.row_bytes = rb;
     return launch_f32m(fmt, m, k, x, batch, ws, s);
   }
-  const bool i8s = use_i8s(fmt, 2 * n, k, x, batch);
-  const bool i8 = !i8s && use_i8(fmt, 2 * n, k, x, batch, ws, ws_bytes);
-  if ((i8s || i8 || klane_ok(fmt, k, x, batch)) && n < (1ll << 29)) {
+  const bool i8 = use_i8(fmt, 2 * n, k, x, batch, ws, ws_bytes);
+  if ((i8 || klane_ok(fmt, k, x, batch)) && n < (1ll << 29)) {
     KlMap m{};
     m.w[0] = (const uint8_t *)wg;
     m.w[1] = (const uint8_t *)wu;
@@ -823,7 +814,6 @@ int launch_gemv_swiglu(int fmt, const void *wg, const void *wu, int64_t n, int64
     m.total = (int)(2 * n);
     m.cum[1] = m.total;
     m.row_bytes = rb;
-    if (i8s) return launch_gemv_i8s(m, k, x, s);
     if (i8) return launch_i8(fmt, m, k, x, ws, s);
     return launch_kl(m, k, x, s);
   }

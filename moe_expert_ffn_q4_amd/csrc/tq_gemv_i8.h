@@ -216,10 +216,4 @@ size_t i8_workspace_bytes(int64_t rows, int64_t k);
 int launch_gemv_i8(int fmt, const KlMap &m, int64_t k, const float *x, float *partial,
                    unsigned long long *counters, int max_counters, hipStream_t s);
 
-// Streaming form (no workspace; opt-in with TQ_KNOB_GEMV_I8S = 1): Q4_K, one token, k a multiple of 256
-// up to 16384; all of x is made
-// into digits in each workgroup's LDS and the k parts of a row tile are added inside the workgroup.
-bool i8s_gemv_ok(int fmt, int64_t k, int64_t batch);
-int launch_gemv_i8s(const KlMap &m, int64_t k, const float *x, hipStream_t s);
-
 }  // namespace tq

@@ -160,84 +160,6 @@ __global__ __launch_bounds__(256) void k_gemv_i8(KlMap m, const float *__restric
   if (threadIdx.x == 0) done_arrivals(arr, grp);
 }
 
-// Streaming form for k up to 16384 (no cross-workgroup reduction): a workgroup of NW waves turns
-// all of x into digits in LDS once, then each wave streams one 32-row tile over one of KS equal k
-// parts with D blocks of loads in flight (the first D requested before the digits are made), so
-// the weights flow like a plain read; the KS parts of a tile are added in part order through LDS.
-struct I8Blk {
-  u32x4 head, q[4];
-};
-
-__device__ __forceinline__ void i8_load_blk(I8Blk &b, const uint8_t *p, int h) {
-  b.head = gload(p);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) b.q[c] = gload(p + 16 + 32 * c + 16 * h);
-}
-
-__device__ __forceinline__ float i8_compute_blk(const I8Blk &b, const uint8_t *l, int n, int h) {
-  const u32x4 xa = *reinterpret_cast<const u32x4 *>(l + n * 32 + 16 * h);
-  const u32x4 S = *reinterpret_cast<const u32x4 *>(l + kDigitBytes + 16 * h);
-  const float us = *reinterpret_cast<const float *>(l + kDigitBytes + 32);
-  return i8_block(b.head, b.q, xa, S, us, n >> 2, h);
-}
-
-template <int NW, int D>
-__global__ __launch_bounds__(64 * NW) void k_gemv_i8s(KlMap m, const float *__restrict__ x, int nb,
-                                                       int ks) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t xl[];  // nb records, then NW x 32 sums
-  float *red = reinterpret_cast<float *>(xl + (size_t)nb * kLdsBlock);
-  const int tw = NW / ks;  // tiles per workgroup
-  const int lane = threadIdx.x & 63, w = wave_index();
-  const int n = lane & 31, h = lane >> 5;
-  const int t = w / ks, part = w - t * ks;
-  const int r0 = ((int)blockIdx.x * tw + t) * 32;
-  const int nbp = (nb + ks - 1) / ks;
-  const int kb0 = part * nbp;
-  const int nbw = max(0, min(nbp, nb - kb0));
-  const uint8_t *row = m.row(min(r0 + n, m.total - 1)) + (int64_t)kb0 * 144;
-  I8Blk buf[D];
-#pragma unroll
-  for (int u = 0; u < D; ++u)
-    if (u < nbw) i8_load_blk(buf[u], row + (int64_t)u * 144, h);
-  // all of x as digits (16 threads per block; groups of 16 stay active together)
-  for (int i = threadIdx.x; i < 16 * nb; i += blockDim.x)
-    make_digits(x + (int64_t)(i >> 4) * 256, i & 15, xl + (size_t)(i >> 4) * kLdsBlock);
-  __syncthreads();
-  float acc = 0.f;
-  for (int base = 0; base < nbw; base += D) {
-#pragma unroll
-    for (int u = 0; u < D; ++u) {
-      const int i = base + u;
-      if (i < nbw) {
-        acc += i8_compute_blk(buf[u], xl + (size_t)(kb0 + i) * kLdsBlock, n, h);
-        if (i + D < nbw) i8_load_blk(buf[u], row + (int64_t)(i + D) * 144, h);
-      }
-    }
-  }
-  acc += __shfl_xor(acc, 32);  // the two sub-block parities of the row
-  if (h == 0) red[w * 32 + n] = acc;
-  __syncthreads();
-  const int i = (int)threadIdx.x;
-  if (m.swiglu) {  // (gate, up) row pairs
-    if (i < tw * 16) {
-      const int tt = i >> 4, pr = 2 * (i & 15);
-      float g = 0.f, u = 0.f;
-      for (int q = 0; q < ks; ++q) {
-        g += red[(tt * ks + q) * 32 + pr];
-        u += red[(tt * ks + q) * 32 + pr + 1];
-      }
-      const int v = ((int)blockIdx.x * tw + tt) * 32 + pr;
-      if (v + 1 < m.total) m.y[0][v >> 1] = silu_mul(g, u);
-    }
-  } else if (i < tw * 32) {
-    const int tt = i >> 5, nn = i & 31;
-    float s = 0.f;
-    for (int q = 0; q < ks; ++q) s += red[(tt * ks + q) * 32 + nn];
-    const int v = ((int)blockIdx.x * tw + tt) * 32 + nn;
-    if (v < m.total) i8_store(m, v, s);
-  }
-}
-
 // ---- host side ----------------------------------------------------------------------------------
 
 // Q4_K, one token, k a multiple of 256 up to 32768; by default from k = 16384 on. Below that the
@@ -291,58 +213,6 @@ int launch_gemv_i8(int fmt, const KlMap &m, int64_t k, const float *x, float *pa
     hipLaunchKernelGGL(k_gemv_i8<FMT_Q4_K>, dim3((unsigned)(groups * ksplit)), dim3(64 * W), 0, s,
                        m, x, nblk, upk, ksplit, partial, arr);
   return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-// ---- streaming form ----------------------------------------------------------------------------
-
-// Opt-in (TQ_KNOB_GEMV_I8S = 1): on the 8B-shaped projections it is level with the lanes-along-k kernel
-// on q|k|v and o, 10% faster on gate|up and 35% slower on down (each workgroup makes the digits of
-// all of k, and 32-row tiles leave few workgroups on short matrices).
-bool i8s_gemv_ok(int fmt, int64_t k, int64_t batch) {
-  const int mode = knob(TQ_KNOB_GEMV_I8S, 0);
-  return mode != 0 && knob(TQ_KNOB_GEMV_I8, 1) != 0 && fmt == FMT_Q4_K && batch == 1 &&
-         k % 256 == 0 && k >= 256 && k <= 16384;
-}
-
-template <int NW, int D>
-static int launch_i8s_cfg(const KlMap &m, int nb, int ks, const float *x, hipStream_t s) {
-  const size_t lds = (size_t)nb * kLdsBlock + NW * 32 * 4;
-  if (lds > 65536) {
-    static const hipError_t attr = hipFuncSetAttribute(
-        (const void *)k_gemv_i8s<NW, D>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (attr != hipSuccess) return -1;
-  }
-  const int tw = NW / ks;
-  const int grid = (m.total + 32 * tw - 1) / (32 * tw);
-  hipLaunchKernelGGL((k_gemv_i8s<NW, D>), dim3((unsigned)grid), dim3(64 * NW), lds, s, m, x, nb, ks);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-// k parts per 32-row tile, from k alone (so a row's sum is formed the same way whatever the
-// matrix height or the call): the most parts, up to the workgroup's waves, that leave each part at
-// least TQ_KNOB_I8S_PART (4) blocks. Workgroup waves and blocks in flight: TQ_KNOB_I8S_NW / TQ_KNOB_I8S_D.
-int launch_gemv_i8s(const KlMap &m, int64_t k, const float *x, hipStream_t s) {
-  const int nb = (int)(k / 256);
-  const int nw_env = knob(TQ_KNOB_I8S_NW, 8);
-  const int d_env = knob(TQ_KNOB_I8S_D, 4);
-  const int ks_env = knob(TQ_KNOB_I8S_KS, 0);
-  const int part_min = clampi(knob(TQ_KNOB_I8S_PART, 4), 1, 64);
-  const int nw = nw_env == 4 || nw_env == 16 ? nw_env : 8;
-  int ks = 1;
-  if (ks_env > 0) {
-    ks = ks_env;
-  } else {
-    while (ks < nw && nb >= 2 * ks * part_min) ks *= 2;
-  }
-  ks = clampi(ks, 1, nw);
-  if (nw % ks) return -2;
-  if (nw == 4) return d_env == 2 ? launch_i8s_cfg<4, 2>(m, nb, ks, x, s)
-                                 : d_env == 6 ? launch_i8s_cfg<4, 6>(m, nb, ks, x, s)
-                                              : launch_i8s_cfg<4, 4>(m, nb, ks, x, s);
-  if (nw == 16) return launch_i8s_cfg<16, 2>(m, nb, ks, x, s);
-  return d_env == 2 ? launch_i8s_cfg<8, 2>(m, nb, ks, x, s)
-                    : d_env == 6 ? launch_i8s_cfg<8, 6>(m, nb, ks, x, s)
-                                 : launch_i8s_cfg<8, 4>(m, nb, ks, x, s);
 }
 
 }  // namespace tq

@@ -22,7 +22,6 @@ tq = pytest.importorskip("moe_expert_ffn_q4_amd")
 @pytest.fixture
 def i8(knobs):
     knobs("gemv_i8", 2)
-    knobs("gemv_i8s", 0)  # the k-sliced kernel, not the streaming one
 
 
 def _case(*a):
@@ -120,7 +119,6 @@ def test_i8_agrees_with_lanes_along_k(knobs):
     g = synth.rng(507, "i8-vs-kl")
     w, x = dev(synth.blob("q4_k", g, n, k)), dev(synth.normal_f32(g, (1, k)))
     knobs("gemv_i8", 2)
-    knobs("gemv_i8s", 0)
     a = host(tq.gemv("q4_k", w, n, k, x))
     knobs("gemv_i8", 0)
     b = host(tq.gemv("q4_k", w, n, k, x))

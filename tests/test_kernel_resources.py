@@ -15,7 +15,6 @@ HOT = [
     (r"k_moe_klILi4E", 2),           # one-token MoE experts
     (r"k_gemv_i8ILi1E", 4),          # batch-1 Q4_K GEMV, int8 matrix cores, sliced k
     (r"k_gemv_i8ILi3E", 3),          # batch-1 Q8_0 GEMV, int8 matrix cores, sliced k
-    (r"k_gemv_i8sI", 2),             # the streaming form
     (r"k_gemm_f32m_q8", 4),          # Q8_0 batches, fp32 matrix cores
     (r"k_gemm_f32m_q6", 2),          # Q6_K batches
     (r"k_qmm_denseI", 1),            # dense few-token Q4_K products, fp16 matrix cores
