@@ -29,6 +29,11 @@ BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of the MI355X
 GEMV_SOURCES = ("moe_expert_ffn_q4_amd/csrc/tq_dense.hip", "moe_expert_ffn_q4_amd/csrc/tq_gemv_core.h",
                 "moe_expert_ffn_q4_amd/csrc/tq_device.h")
 GEMV_COUNTERS = "profiles/k_gemv_kl_llama8b_b1_hbm_counters.txt"
+# The same for the few-token products of the batch-8 step (tq::k_qmm_dense2).
+QMM_SOURCES = ("moe_expert_ffn_q4_amd/csrc/tq_qmm.hip", "moe_expert_ffn_q4_amd/csrc/tq_qmm.h",
+               "moe_expert_ffn_q4_amd/csrc/tq_gemv_core.h", "moe_expert_ffn_q4_amd/csrc/tq_mfma.h",
+               "moe_expert_ffn_q4_amd/csrc/tq_device.h")
+B8_COUNTERS = "profiles/k_qmm_dense2_llama8b_b8_hbm_counters.txt"
 C1_COUNTERS = "profiles/k_gemv_kl_c1_4096x4096_hbm_counters.txt"
 METRIC = "Q4_K GEMV HBM GB/s (% of peak); decode tokens/s for 8B-shaped and MoE layers"
 
@@ -175,9 +180,9 @@ def llama8b_bytes_per_launch(synth, batch=1):
     return tot / len(launches)
 
 
-def summarize(kt_csv, fetch_csv, write_csv, workload="llama8b"):
-    """Text summary of the profiler's CSVs for the GEMV of the llama8b batch-1 step (or of the
-    c1 workload). FETCH_SIZE and WRITE_SIZE are scaled by what they read for the 1 GiB copy
+def summarize(kt_csv, fetch_csv, write_csv, workload="llama8b", batch=1):
+    """Text summary of the profiler's CSVs for the GEMV of the llama8b step at this batch (or of
+    the c1 workload). FETCH_SIZE and WRITE_SIZE are scaled by what they read for the 1 GiB copy
     (--calibrate-copy)."""
     import csv
     from collections import defaultdict
@@ -214,8 +219,9 @@ def summarize(kt_csv, fetch_csv, write_csv, workload="llama8b"):
     lines.append(f"{'kernel':<40s} {'grid':>8s} {'wg':>4s} {'n':>6s} {'FETCH_KiB':>11s} "
                  f"{'WRITE_KiB':>10s} {'bytes/launch (scaled)':>22s}")
     tot_bytes, tot_n = 0.0, 0
+    kern = "k_gemv_kl" if batch == 1 else "k_qmm_dense"
     for key in sorted(fetch, key=lambda k: -sum(fetch[k])):
-        if "k_gemv_kl" not in key[0]:
+        if kern not in key[0]:
             continue
         fv, wv = fetch[key], write.get(key, [0.0])
         fk, wk = sum(fv) / len(fv), sum(wv) / len(wv)
@@ -224,13 +230,13 @@ def summarize(kt_csv, fetch_csv, write_csv, workload="llama8b"):
         tot_n += len(fv)
         lines.append(f"{key[0][:40]:<40s} {key[1]:8d} {key[2]:4d} {len(fv):6d} {fk:11.1f} "
                      f"{wk:10.1f} {b:22.0f}")
-    algo = C1_BYTES_PER_LAUNCH if workload == "c1" else llama8b_bytes_per_launch(synth)
+    algo = C1_BYTES_PER_LAUNCH if workload == "c1" else llama8b_bytes_per_launch(synth, batch)
     traffic = tot_bytes / tot_n
     lines.append("")
     lines.append(f"algorithmic_bytes_per_launch: {algo:.0f}")
     lines.append(f"traffic_bytes_per_launch: {traffic:.0f}")
     lines.append(f"traffic_over_algorithmic: {traffic / algo:.4f}")
-    lines.append(f"kernel_source_sha256: {source_hash()}")
+    lines.append(f"kernel_source_sha256: {source_hash(GEMV_SOURCES if batch == 1 else QMM_SOURCES)}")
     return "\n".join(lines)
 
 
@@ -258,7 +264,7 @@ def kernel_summary(stats_csv, *counter_csvs):
     return "\n".join(lines)
 
 
-def recorded_traffic(summary=GEMV_COUNTERS):
+def recorded_traffic(summary=GEMV_COUNTERS, sources=GEMV_SOURCES):
     """HBM bytes per GEMV launch from a committed counter summary, or None when the kernel's
     sources have changed since the counters were taken (or there is no summary)."""
     path = os.path.join(ROOT, summary)
@@ -269,7 +275,7 @@ def recorded_traffic(summary=GEMV_COUNTERS):
         if ":" in line:
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256") != source_hash():
+    if fields.get("kernel_source_sha256") != source_hash(sources):
         return None
     return float(fields["traffic_bytes_per_launch"])
 
@@ -294,8 +300,10 @@ def gemv_kernel_name(tq, batch):
     its workspace (the int8 kernel takes k >= 16384 unless its knob is set to 2)."""
     if batch == 1:
         if tq.get_knob("gemv_i8") == 2:
-            return "tq_gemv Q4_K batch 1 (tq::k_gemv_i8, after tq::k_x_digits)"
+            return "tq_gemv Q4_K batch 1 (tq::k_gemv_i8)"
         return "tq_gemv Q4_K batch 1 (tq::k_gemv_kl)"
+    if batch <= 16 and tq.get_knob("gemv_qmm") != 0 and tq.get_knob("qmm_inline") != 0:
+        return f"tq_gemv Q4_K batch {batch} (tq::k_qmm_dense2, activations split in the kernel)"
     if batch <= 32 and tq.get_knob("gemv_qmm") != 0:
         return f"tq_gemv Q4_K batch {batch} (tq::k_qmm_dense, after tq::k_split_rows)"
     return f"tq_gemv Q4_K batch {batch} (tq::k_gemv)"
@@ -957,7 +965,7 @@ def calibrate_copy(torch):
 def main():
     args = _args()
     if args.summarize:
-        print(summarize(*args.summarize, workload=args.workload))
+        print(summarize(*args.summarize, workload=args.workload, batch=args.batch))
         return
     if args.kernel_summary:
         print(kernel_summary(*args.kernel_summary))
@@ -1020,7 +1028,8 @@ def main():
     avg_launch_s = sum(gper) / 1000 / (len(gper) * launches)
     achieved = kernel_bytes / launches / avg_launch_s / 1e9
     step_bytes = kernel_bytes
-    traffic = recorded_traffic() if args.batch == 1 else None
+    traffic = (recorded_traffic() if args.batch == 1 else
+               recorded_traffic(B8_COUNTERS, QMM_SOURCES) if args.batch == 8 else None)
 
     out = {
         "metric": METRIC,

@@ -254,7 +254,12 @@ __global__ __launch_bounds__(512) void k_gemv(const uint8_t *__restrict__ w, int
                                               float *__restrict__ partial, Arrivals arr) {
   extern __shared__ float lds[];
   __shared__ int is_last;
-  const int rg = blockIdx.x / ksplit, ks = blockIdx.x - rg * ksplit;
+  // blockIdx -> (row group, slice): XCD x takes the row groups r = x (mod 8) and runs all slices
+  // of one group back to back (the cache lines two neighbouring slices of a row share are then
+  // fetched once, into that XCD's L2)
+  const int xcd = blockIdx.x & 7, bi = blockIdx.x >> 3;
+  const int rg = xcd + 8 * (bi / ksplit), ks = bi % ksplit;
+  if (rg * 64 >= n) return;
   const int row0 = rg * 64;
   const int ku0 = ks * upk, ku1 = min(ku0 + upk, units);
   const float *xr[NT];
@@ -544,7 +549,8 @@ template <int FMT, int NT>
 static void launch_gemv_nt(const uint8_t *w, int64_t rb, int n, int units, const GemvPlan &p,
                            const float *x, int64_t ldx, float *y, int64_t ldy, float *partial,
                            unsigned long long *counters, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemv<FMT, NT>), dim3((unsigned)(p.rowgroups * p.ksplit)), dim3(64 * p.waves),
+  hipLaunchKernelGGL((k_gemv<FMT, NT>), dim3((unsigned)((p.rowgroups + 7) / 8 * 8 * p.ksplit)),
+                     dim3(64 * p.waves),
                      lds, s, w, rb, n, units, p.ksplit, p.upk, p.upw, x, ldx, y, ldy, partial,
                      Arrivals{counters, counters ? call_tag() : 0ull});
 }

@@ -209,7 +209,12 @@ __device__ __forceinline__ void f32m_body(const KlMap &m, const float *__restric
   constexpr int RT = kF32mRT;
   const int lane = threadIdx.x & 63, w = wave_index();
   const int t = lane & 15, g = lane >> 4;
-  const int grp = blockIdx.x / ksplit, ks = blockIdx.x - grp * ksplit;
+  // blockIdx -> (row group, slice): XCD x takes the row groups g = x (mod 8) and runs all slices
+  // of one group back to back (the cache lines two neighbouring slices of a row share are then
+  // fetched once, into that XCD's L2)
+  const int xcd = blockIdx.x & 7, bi = blockIdx.x >> 3;
+  const int grp = xcd + 8 * (bi / ksplit), ks = bi % ksplit;
+  if (grp * (64 * RT) >= m.total) return;  // the whole workgroup: no barrier has been passed
   const int kb0 = ks * upk, nb = min(upk, kblocks - kb0);
   const int rbase = grp * (64 * RT) + w * (16 * RT);
   const uint8_t *wrow[RT];
@@ -363,7 +368,7 @@ int launch_gemm_f32m(int fmt, const KlMap &m, int64_t k, const float *x, int64_t
   if (ksplit > kF32mMaxSlices) return -2;
   const int64_t groups = f32m_groups(m.total);
   if (ksplit > 1 && groups > max_counters) return -2;
-  const dim3 grid((unsigned)(groups * ksplit));
+  const dim3 grid((unsigned)((groups + 7) / 8 * 8 * ksplit));
   const Arrivals arr{counters, ksplit > 1 ? call_tag() : 0ull};
   if (fmt == FMT_Q6_K)
     hipLaunchKernelGGL(k_gemm_f32m_q6, grid, dim3(256), 0, s, m, x, (int)batch, nblk, ksplit, upk,

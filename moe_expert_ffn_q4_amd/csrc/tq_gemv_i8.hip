@@ -74,14 +74,19 @@ struct I8Fmt<FMT_Q8_0> {
 
 template <int FMT>
 __global__ __launch_bounds__(256) void k_gemv_i8(KlMap m, const float *__restrict__ x, int nblk,
-                                                 int upk, int ksplit, float *__restrict__ partial,
-                                                 Arrivals arr) {
+                                                 int upk, int ksplit, int groups,
+                                                 float *__restrict__ partial, Arrivals arr) {
   using F = I8Fmt<FMT>;
   __shared__ __attribute__((aligned(16))) uint8_t xl[kMaxSliceBlocks * kLdsBlock];
   __shared__ float red[4][32];
   __shared__ int is_last;
   const int W = blockDim.x >> 6;  // row tiles of this workgroup
-  const int grp = blockIdx.x / ksplit, ks = blockIdx.x - grp * ksplit;
+  // blockIdx -> (row group, slice): XCD x takes the row groups g = x (mod 8) and runs all slices
+  // of one group back to back, so the cache lines that neighbouring slices of a row share are
+  // fetched once, into that XCD's L2
+  const int xcd = blockIdx.x & 7, bi = blockIdx.x >> 3;
+  const int grp = xcd + 8 * (bi / ksplit), ks = bi % ksplit;
+  if (grp >= groups) return;
   const int kb0 = ks * upk, nb = min(upk, nblk - kb0);
   const int lane = threadIdx.x & 63, w = wave_index();
   const int n = lane & 31, h = lane >> 5;
@@ -206,12 +211,13 @@ int launch_gemv_i8(int fmt, const KlMap &m, int64_t k, const float *x, float *pa
   const int groups = (m.total + 32 * W - 1) / (32 * W);
   if (ksplit > 1 && groups > max_counters) return -2;
   const Arrivals arr{counters, ksplit > 1 ? call_tag() : 0ull};
+  const dim3 grid((unsigned)((groups + 7) / 8 * 8 * ksplit));
   if (fmt == FMT_Q8_0)
-    hipLaunchKernelGGL(k_gemv_i8<FMT_Q8_0>, dim3((unsigned)(groups * ksplit)), dim3(64 * W), 0, s,
-                       m, x, nblk, upk, ksplit, partial, arr);
+    hipLaunchKernelGGL(k_gemv_i8<FMT_Q8_0>, grid, dim3(64 * W), 0, s, m, x, nblk, upk, ksplit,
+                       groups, partial, arr);
   else
-    hipLaunchKernelGGL(k_gemv_i8<FMT_Q4_K>, dim3((unsigned)(groups * ksplit)), dim3(64 * W), 0, s,
-                       m, x, nblk, upk, ksplit, partial, arr);
+    hipLaunchKernelGGL(k_gemv_i8<FMT_Q4_K>, grid, dim3(64 * W), 0, s, m, x, nblk, upk, ksplit,
+                       groups, partial, arr);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -599,7 +599,12 @@ __global__ __launch_bounds__(256) void k_qmm_dense(QmmDense m, SplitRows x, int 
   __shared__ __attribute__((aligned(16))) uint8_t xbuf[2 * 16 * NTMAX * kXBlockBytes];
   __shared__ int rowidx[16 * NTMAX];
   __shared__ int is_last;
-  const int tile = blockIdx.x / ksplit, ks = blockIdx.x - tile * ksplit;
+  // blockIdx -> (tile, slice): XCD x takes the tiles t = x (mod 8) and runs all slices of one
+  // tile back to back (the cache lines two neighbouring slices of a row share are then fetched
+  // once, into that XCD's L2)
+  const int xcd = blockIdx.x & 7, bi = blockIdx.x >> 3;
+  const int tile = xcd + 8 * (bi / ksplit), ks = bi % ksplit;
+  if (tile * (GU ? 64 : 128) >= (GU ? m.cum[1] : m.cum[m.nparts])) return;
   const int kb0 = ks * upk, steps = min(upk, kblocks - kb0);
   if ((int)threadIdx.x < 16 * NTMAX) rowidx[threadIdx.x] = min((int)threadIdx.x, B - 1);
   const int t16 = threadIdx.x & 15, wave = wave_index();
@@ -729,15 +734,20 @@ struct Dense2Tile {
 
 template <bool GU, int NR, int RB, int UPK>
 __global__ __launch_bounds__(256) void k_qmm_dense2(QmmDense m, const float *__restrict__ x, int B,
-                                                    int kblocks, int ksplit, float *partial,
-                                                    Arrivals arr) {
+                                                    int kblocks, int ksplit, int tiles,
+                                                    float *partial, Arrivals arr) {
   static_assert(!GU || NR == 2, "a gate/up tile holds the gate and the up rows");
   static_assert(RB == 8 || RB == 16, "token rows per block");
   using L = DenseLds<RB, UPK>;
   using T = Dense2Tile<GU, NR>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[L::kBytes];
   __shared__ int is_last;
-  const int tile = blockIdx.x / ksplit, ks = blockIdx.x - tile * ksplit;
+  // blockIdx -> (tile, slice): XCD x (workgroups are dealt to the 8 XCDs round-robin) takes the
+  // tiles t = x (mod 8) and runs all slices of one tile back to back, so the cache lines that two
+  // neighbouring slices of a row share are fetched once, into that XCD's L2
+  const int xcd = blockIdx.x & 7, bi = blockIdx.x >> 3;
+  const int tile = xcd + 8 * (bi / ksplit), ks = bi % ksplit;
+  if (tile >= tiles) return;
   const int kb0 = ks * UPK, steps = min(UPK, kblocks - kb0);
   const int lane = threadIdx.x & 63, t16 = lane & 15, g = lane >> 4, wave = wave_index();
   const int64_t ldx = (int64_t)kblocks * 256;
@@ -1069,8 +1079,9 @@ size_t qmm_dense_bytes(int64_t rows, int64_t k, int64_t batch, bool swiglu) {
 template <bool GU, int NR, int RB, int UPK>
 static void dense2_launch(const QmmDense &m, const float *x, int B, int nblk, const Dense2Plan &p,
                           float *partial, Arrivals arr, hipStream_t st) {
-  hipLaunchKernelGGL((k_qmm_dense2<GU, NR, RB, UPK>), dim3((unsigned)(p.tiles * p.ksplit)),
-                     dim3(256), 0, st, m, x, B, nblk, p.ksplit, partial, arr);
+  hipLaunchKernelGGL((k_qmm_dense2<GU, NR, RB, UPK>),
+                     dim3((unsigned)((p.tiles + 7) / 8 * 8 * p.ksplit)), dim3(256), 0, st, m, x, B,
+                     nblk, p.ksplit, (int)p.tiles, partial, arr);
 }
 template <bool GU, int NR>
 static void dense2_launch_nr(const QmmDense &m, const float *x, int B, int nblk,
@@ -1106,7 +1117,7 @@ int launch_qmm_dense(const QmmDense &m, int64_t k, const float *x, int64_t batch
   const SplitRows xr = split_rows_at(ws, batch, k);
   float *partial = (float *)(ws + split_rows_bytes(batch, k));
   launch_split_rows(x, k, batch, k, xr, st);
-  const dim3 grid((unsigned)(tiles * ksplit));
+  const dim3 grid((unsigned)((tiles + 7) / 8 * 8 * ksplit));
   const int B = (int)batch;
   const Arrivals counters_arr{counters, ksplit > 1 ? call_tag() : 0ull};
   if (m.swiglu) {
