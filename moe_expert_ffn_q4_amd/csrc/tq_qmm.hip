@@ -819,16 +819,21 @@ __global__ __launch_bounds__(256) void k_qmm_dense2(QmmDense m, const float *__r
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 
-  // 4. the blocks; operand row = t16 % RB
+  // 4. the blocks; operand row = t16 % RB. With up to 8 tokens (RB = 8) the hi and lo halves of
+  // the activations share one operand: rows 0..7 hi of tokens 0..7, rows 8..15 their lo, one
+  // product per k step; the lanes holding rows 8..15 (g = 2, 3) carry no min term and add their
+  // sums to the lanes holding rows 0..7 at the end.
+  constexpr bool kPack = RB == 8;
   const int row = t16 & (RB - 1);
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  const bool min_lane = !kPack || g < 2;
   f32x4 acc[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) acc[r] = zero;
 #pragma unroll
   for (int b = 0; b < UPK; ++b) {
     if (b >= steps) break;
-    const uint8_t *xb = lds + (b * RB + row) * kXBlockBytes;
+    const uint8_t *xb = lds + (b * RB + row) * kXBlockBytes + (kPack ? 512 * (t16 >> 3) : 0);
     const half4 am = *reinterpret_cast<const half4 *>(lds + L::kX + (b * RB + row) * kAuxBytes + 8 * g);
     const f32x4 us = *reinterpret_cast<const f32x4 *>(lds + L::kX + L::kAux +
                                                       (b * RB + ((4 * g) & (RB - 1))) * 4);
@@ -843,20 +848,28 @@ __global__ __launch_bounds__(256) void k_qmm_dense2(QmmDense m, const float *__r
       constexpr int S = decltype(S_)::value;
       const uint8_t *p = xb + 16 * ((8 * g + S) ^ row);
       const half8 ah = *reinterpret_cast<const half8 *>(p);
-      const half8 al = *reinterpret_cast<const half8 *>(p + 512);
+      half8 al;
+      if constexpr (!kPack) al = *reinterpret_cast<const half8 *>(p + 512);
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         const half8 bq = qb<S>(w[b][r], S < 4 ? qs[r].sc_lo : qs[r].sc_hi);
         dq[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, S == 0 ? zero : dq[r], 0, 0, 0);
-        dq[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, dq[r], 0, 0, 0);
+        if constexpr (!kPack) dq[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, dq[r], 0, 0, 0);
       }
     });
 #pragma unroll
     for (int r = 0; r < NR; ++r)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        acc[r][i] = __builtin_fmaf(us[i], __builtin_fmaf(qs[r].d, dq[r][i], qs[r].ndmin * dm[r][i]),
-                                   acc[r][i]);
+        acc[r][i] = __builtin_fmaf(
+            us[i], __builtin_fmaf(qs[r].d, dq[r][i], min_lane ? qs[r].ndmin * dm[r][i] : 0.f),
+            acc[r][i]);
+  }
+  if constexpr (kPack) {  // the lo halves' sums (lanes 32..63) onto the hi halves' (lanes 0..31)
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[r][i] += xor_recv(acc[r][i], 32);
   }
 
   // 5. results (one slice) or this slice's sums and, for the tile's last workgroup, the total
