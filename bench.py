@@ -26,15 +26,16 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of the MI355X
 # Sources of the batch-1 Q4_K GEMV; the committed counter summary records their hash, and its
 # HBM traffic is reported only while the kernel is unchanged since the counters were taken.
-GEMV_SOURCES = ("moe_expert_ffn_q4_amd/csrc/tq_dense.hip", "moe_expert_ffn_q4_amd/csrc/tq_gemv_core.h",
+GEMV_SOURCES = ("moe_expert_ffn_q4_amd/csrc/tq_gemv_mf.hip", "moe_expert_ffn_q4_amd/csrc/tq_gemv_mf.h",
+                "moe_expert_ffn_q4_amd/csrc/tq_dense.hip", "moe_expert_ffn_q4_amd/csrc/tq_gemv_core.h",
                 "moe_expert_ffn_q4_amd/csrc/tq_device.h")
-GEMV_COUNTERS = "profiles/k_gemv_kl_llama8b_b1_hbm_counters.txt"
+GEMV_COUNTERS = "profiles/k_gemv_mf_llama8b_b1_hbm_counters.txt"
 # The same for the few-token products of the batch-8 step (tq::k_qmm_dense2).
 QMM_SOURCES = ("moe_expert_ffn_q4_amd/csrc/tq_qmm.hip", "moe_expert_ffn_q4_amd/csrc/tq_qmm.h",
                "moe_expert_ffn_q4_amd/csrc/tq_gemv_core.h", "moe_expert_ffn_q4_amd/csrc/tq_mfma.h",
                "moe_expert_ffn_q4_amd/csrc/tq_device.h")
 B8_COUNTERS = "profiles/k_qmm_dense2_llama8b_b8_hbm_counters.txt"
-C1_COUNTERS = "profiles/k_gemv_kl_c1_4096x4096_hbm_counters.txt"
+C1_COUNTERS = "profiles/k_gemv_mf_c1_4096x4096_hbm_counters.txt"
 METRIC = "Q4_K GEMV HBM GB/s (% of peak); decode tokens/s for 8B-shaped and MoE layers"
 
 
@@ -219,7 +220,7 @@ def summarize(kt_csv, fetch_csv, write_csv, workload="llama8b", batch=1):
     lines.append(f"{'kernel':<40s} {'grid':>8s} {'wg':>4s} {'n':>6s} {'FETCH_KiB':>11s} "
                  f"{'WRITE_KiB':>10s} {'bytes/launch (scaled)':>22s}")
     tot_bytes, tot_n = 0.0, 0
-    kern = "k_gemv_kl" if batch == 1 else "k_qmm_dense"
+    kern = b1_kernel() if batch == 1 else "k_qmm_dense"
     for key in sorted(fetch, key=lambda k: -sum(fetch[k])):
         if kern not in key[0]:
             continue
@@ -295,13 +296,21 @@ def build_dense_model(tq, synth, torch, batch, seed):
     return layers
 
 
+def b1_kernel(tq=None):
+    """The kernel of batch-1 Q4_K products with k < 16384 under the current knobs (the fp16
+    matrix-core kernel unless switched off; the int8 one takes k >= 16384 unless its knob is 2)."""
+    if tq is None:
+        import moe_expert_ffn_q4_amd as tq
+    if tq.get_knob("gemv_i8") == 2:
+        return "k_gemv_i8"
+    return "k_gemv_kl" if tq.get_knob("gemv_mf") == 0 else "k_gemv_mf"
+
+
 def gemv_kernel_name(tq, batch):
     """The kernel that tq_gemv runs for the 8B shapes (k = 4096 and 14336) at this batch, given
-    its workspace (the int8 kernel takes k >= 16384 unless its knob is set to 2)."""
+    its workspace."""
     if batch == 1:
-        if tq.get_knob("gemv_i8") == 2:
-            return "tq_gemv Q4_K batch 1 (tq::k_gemv_i8)"
-        return "tq_gemv Q4_K batch 1 (tq::k_gemv_kl)"
+        return f"tq_gemv Q4_K batch 1 (tq::{b1_kernel(tq)})"
     if batch <= 16 and tq.get_knob("gemv_qmm") != 0 and tq.get_knob("qmm_inline") != 0:
         return f"tq_gemv Q4_K batch {batch} (tq::k_qmm_dense2, activations split in the kernel)"
     if batch <= 32 and tq.get_knob("gemv_qmm") != 0:
@@ -679,7 +688,7 @@ def c1_bench(args, torch, tq, synth):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(C1_COUNTERS),
-                     "kernel": "tq_gemv Q4_K batch 1 (tq::k_gemv_kl)",
+                     "kernel": gemv_kernel_name(tq, 1),
                      "avg_launch_us": round(kernel_s * 1e6, 3)},
     }
     if not args.no_cpu_baseline:
@@ -775,7 +784,7 @@ def llama70b_bench(args, torch, tq, synth):
         # and time summed over the launches, i.e. per-launch bytes over the average launch time
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "Q4_K batch-1 layer (tq::k_gemv_kl; down on tq::k_gemv_i8)"},
+                     "kernel": f"Q4_K batch-1 layer (tq::{b1_kernel(tq)}; down on tq::k_gemv_i8)"},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = llama70b_cpu_baseline(host_q4k, args.cpu_seconds, tq, torch)

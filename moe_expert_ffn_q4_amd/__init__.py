@@ -440,6 +440,9 @@ KNOBS = {
     "qmm_inline": 21,
     "qmm_inline_upk": 22,
     "qmm_inline_nr": 23,
+    "gemv_mf": 24,
+    "mf_wgs": 25,
+    "mf_kb": 26,
 }
 
 

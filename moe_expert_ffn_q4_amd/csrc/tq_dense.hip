@@ -2,6 +2,7 @@
 #include "tq_gemv_core.h"
 #include "tq_gemm_f32m.h"
 #include "tq_gemv_i8.h"
+#include "tq_gemv_mf.h"
 #include "tq_qmm.h"
 #include "tq_launch.h"
 #include "tq_moe.h"
@@ -621,6 +622,7 @@ static void launch_kl_rg(const KlMap &m, int nblk, int waves, int target, const 
 }
 
 static int launch_kl(const KlMap &m, int64_t k, const float *x, hipStream_t s) {
+  if (mf_gemv_ok(k)) return launch_gemv_mf(m, k, x, s);
   const int nblk = (int)(k / 256);
   const int waves = (nblk + 15) / 16;
   const int kl_rows_env = knob(TQ_KNOB_KL_ROWS, 4);

@@ -239,6 +239,7 @@ def test_gemv_lane_groups_bitwise(knobs, n, k):
     partials are added in the same tree as with whole-wave rows (whose extra lanes add exact
     zeros), so the results are bitwise those of TQ_KNOB_KL_GROUPS = 1, and within the bar."""
     _print_case("kl-groups", n, k)
+    knobs("gemv_mf", 0)  # the lanes-along-k kernel (batch-1 Q4_K goes to the matrix cores by default)
     g = synth.rng(120, "kl-groups", n, k)
     w, x = synth.blob("q4_k", g, n, k), synth.normal_f32(g, (1, k))
     a = host(tq.gemv("q4_k", dev(w), n, k, dev(x)))

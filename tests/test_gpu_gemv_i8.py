@@ -121,5 +121,6 @@ def test_i8_agrees_with_lanes_along_k(knobs):
     knobs("gemv_i8", 2)
     a = host(tq.gemv("q4_k", w, n, k, x))
     knobs("gemv_i8", 0)
+    knobs("gemv_mf", 0)  # the lanes-along-k kernel, not the fp16 matrix-core one
     b = host(tq.gemv("q4_k", w, n, k, x))
     assert np.linalg.norm(a - b) / np.linalg.norm(b) < 1e-6
