@@ -443,6 +443,7 @@ KNOBS = {
     "gemv_mf": 24,
     "mf_wgs": 25,
     "mf_kb": 26,
+    "mf_deep": 27,
 }
 
 

@@ -29,6 +29,8 @@
 // row's sum is formed the same way whatever the matrix height, the part it falls in or the launch.
 #include <hip/hip_runtime.h>
 
+#include <utility>
+
 #include "tq_device.h"
 #include "tq_gemv_core.h"
 #include "tq_gemv_mf.h"
@@ -145,31 +147,37 @@ __device__ __forceinline__ mf_h8 mf_wop(uint32_t d0, uint32_t d1) {
 }
 
 // 3. one block: eight products into one tile, then the fold of the lane's two sub-blocks.
-// a_lo / a_hi: the lane's activation operands of products 0..3 / 4..7 (or the zero bytes),
-// sum_off: the block's [group] sums and scales.
-__device__ __forceinline__ float mf_block(const MfBlk &b, const uint8_t *lds, uint32_t a_lo,
-                                          uint32_t a_hi, uint32_t sum_off, const Q4kField &f0,
-                                          const Q4kField &f1) {
+// The lane's activation operands of one block (products 0..3 from its a_lo, 4..7 from its a_hi:
+// its own operand row, or the zero bytes) and the block's sums and scales of its group.
+struct MfAct {
   mf_h8 A[8];
+  mf_f4 sf;
+};
+__device__ __forceinline__ void mf_act_load(const uint8_t *lds, uint32_t a_lo, uint32_t a_hi,
+                                            uint32_t sum_off, MfAct &a) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    A[t] = *reinterpret_cast<const mf_h8 *>(lds + a_lo + 16 * t);
-    A[4 + t] = *reinterpret_cast<const mf_h8 *>(lds + a_hi + 16 * t);
+    a.A[t] = *reinterpret_cast<const mf_h8 *>(lds + a_lo + 16 * t);
+    a.A[4 + t] = *reinterpret_cast<const mf_h8 *>(lds + a_hi + 16 * t);
   }
-  const mf_f4 sf = *reinterpret_cast<const mf_f4 *>(lds + sum_off);
+  a.sf = *reinterpret_cast<const mf_f4 *>(lds + sum_off);
+}
+__device__ __forceinline__ float mf_block(const MfBlk &b, const MfAct &a, const Q4kField &f0,
+                                          const Q4kField &f1) {
   const uint32_t qd[8] = {b.qa.x, b.qa.y, b.qa.z, b.qa.w, b.qb.x, b.qb.y, b.qb.z, b.qb.w};
   mf_f4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int t = 0; t < 4; ++t)
-    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[t], mf_wop<false>(qd[2 * t], qd[2 * t + 1]), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.A[t], mf_wop<false>(qd[2 * t], qd[2 * t + 1]), c, 0, 0, 0);
 #pragma unroll
   for (int t = 0; t < 4; ++t)
-    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[4 + t], mf_wop<true>(qd[2 * t], qd[2 * t + 1]), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.A[4 + t], mf_wop<true>(qd[2 * t], qd[2 * t + 1]), c, 0, 0, 0);
   const uint32_t h0 = b.hdr.x;
   const float d24 = half_bits_to_float(h0) * 0x1p24f, dmin = half_bits_to_float(h0 >> 16);
   float sc_a, m_a, sc_b, m_b;
   q4k_scale_min_at(b.hdr.y, b.hdr.z, b.hdr.w, f0, sc_a, m_a);
   q4k_scale_min_at(b.hdr.y, b.hdr.z, b.hdr.w, f1, sc_b, m_b);
+  const mf_f4 sf = a.sf;
   const float pa = d24 * sc_a * sf[2], pb = d24 * sc_b * 0.0625f * sf[3];
   const float mn = __builtin_fmaf(m_a, sf[0], m_b * sf[1]);
   return __builtin_fmaf(pa, c[0] + c[1], __builtin_fmaf(pb, c[2] + c[3], -dmin * mn));
@@ -185,46 +193,70 @@ __device__ __forceinline__ void mf_load_tile(const KlMap &m, int tile, int b0, i
   for (int b = 0; b < KB; ++b) mf_load_blk(rp + min(b, nb - 1) * 144, g, buf[b]);
 }
 
+// The sum of v over lanes l and l ^ 16 (SWAP16) or l and l ^ 32, by a lane swap between rows
+// of 16 (or halves of 32) lanes: each lane gets its own value and its partner's, and their sum
+// is the same in both lanes.
+template <bool SWAP16>
+__device__ __forceinline__ float mf_pair_sum(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto sw = SWAP16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                         : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)sw[0]) + __builtin_bit_cast(float, (unsigned)sw[1]);
+}
+
+// One tile's blocks of the wave (the activation operands read from LDS per block: holding them
+// in registers across tiles measured no faster), then the sum over the lane's four groups.
 template <int KB>
 __device__ __forceinline__ void mf_tile(const MfBlk (&buf)[KB], int nb, const uint8_t *lds,
                                         uint32_t a_lo, uint32_t a_hi, uint32_t inc_lo,
                                         uint32_t inc_hi, uint32_t sum_off, const Q4kField &f0,
-                                        const Q4kField &f1, float *red, int n16, int g) {
+                                        const Q4kField &f1, float *red, int n16, int g,
+                                        bool keep) {
   float acc = 0.f;
 #pragma unroll
   for (int b = 0; b < KB; ++b)
-    if (b < nb)
-      acc += mf_block(buf[b], lds, a_lo + b * inc_lo, a_hi + b * inc_hi, sum_off + b * kMfSumLds,
-                      f0, f1);
-  acc += xor_recv(acc, 16);
-  acc += xor_recv(acc, 32);
-  if (g == 0) red[n16] = acc;
+    if (b < nb) {
+      MfAct a;
+      mf_act_load(lds, a_lo + b * inc_lo, a_hi + b * inc_hi, sum_off + b * kMfSumLds, a);
+      acc += mf_block(buf[b], a, f0, f1);
+    }
+  acc = mf_pair_sum<true>(acc);   // groups 0 + 1, 2 + 3
+  acc = mf_pair_sum<false>(acc);  // (0 + 1) + (2 + 3)
+  if (keep && g == 0) red[n16] = acc;
 }
 
-// Grid: G workgroups, workgroup w taking the 16-row tiles w, w + G, w + 2G, ... (at most
-// tiles_per_wg): at any time the workgroups stream neighbouring tiles, one window of the matrix.
-// blockDim = 64 * ceil(nblk / KB) (at most 16 waves, so at most 128 VGPRs a lane).
-template <int KB>
-__global__ __launch_bounds__(1024) void k_gemv_mf(KlMap m, int nblk, int tiles_per_wg,
-                                                  const float *__restrict__ x) {
+template <int N, class F, int... I>
+__device__ __forceinline__ void mf_unroll_(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, in order
+template <int N, class F>
+__device__ __forceinline__ void mf_unroll(F &&f) {
+  mf_unroll_<N>(f, std::make_integer_sequence<int, N>{});
+}
+
+// Grid: G workgroups, workgroup w taking the 16-row tiles w, w + G, w + 2G, ... (TPW of them, or
+// fewer for the grid's last workgroups): at any time the workgroups stream neighbouring tiles, one
+// window of the matrix. blockDim = 64 * ceil(nblk / KB): at most 16 waves (128 VGPRs a lane), at
+// most 8 when DEPTH = 2 (256). DEPTH 0 (one buffer): each tile after the first is loaded just
+// before its products.
+// The tiles' code is straight-line (TPW and the buffer of each tile fixed at compile time), with
+// the weights of the next DEPTH tiles in flight while a tile is computed: the compiler then counts
+// every load in flight and waits for each tile's own. (In a loop, loads carried across the back
+// edge and the joins of the buffers' values make it wait for all loads before the next prefetch.)
+// A workgroup with fewer than TPW tiles loads its last tile again for the missing ones and does
+// not keep their sums.
+template <int KB, int TPW, int DEPTH>
+__global__ __launch_bounds__(DEPTH > 1 ? 512 : 1024) void k_gemv_mf(KlMap m, int nblk,
+                                                                    const float *__restrict__ x) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63, wave = wave_index(), nw = blockDim.x >> 6;
   const int n16 = lane & 15, g = lane >> 4;
   const int ntiles = (m.total + 15) >> 4, G = gridDim.x;
-  const int nt = min(tiles_per_wg, (ntiles - (int)blockIdx.x + G - 1) / G);  // >= 1
+  const int nt = min(TPW, (ntiles - (int)blockIdx.x + G - 1) / G);  // >= 1
   const int b0 = wave * KB, nb = min(KB, nblk - b0);
   float *red = reinterpret_cast<float *>(lds + kMfZero + nblk * (kMfBlockLds + kMfSumLds));
   auto tile_of = [&](int i) { return (int)blockIdx.x + min(i, nt - 1) * G; };
-
-  // the activations' loads, then the first tile's weights, then the split (which waits for the
-  // activations only)
-  constexpr int MC = KB >= 2 ? KB / 2 : 1;  // cells per thread: 32 nblk cells, 64 ceil(nblk / KB) threads
-  MfCells<MC> cv;
-  mf_split_load<MC>(x, nblk, cv);
-  MfBlk va[KB];
-  mf_load_tile<KB>(m, tile_of(0), b0, nb, n16, g, va);
-  mf_split<MC>(cv, nblk, lds);
-  __syncthreads();
 
   // operand rows 4g, 4g+1 take sub-block 2g (products 0..3), rows 4g+2, 4g+3 sub-block 2g+1
   const Q4kField f0 = q4k_field(2 * g), f1 = q4k_field(2 * g + 1);
@@ -235,25 +267,28 @@ __global__ __launch_bounds__(1024) void k_gemv_mf(KlMap m, int nblk, int tiles_p
   const uint32_t sum_off = kMfZero + nblk * kMfBlockLds + (uint32_t)b0 * kMfSumLds + 16u * g;
   float *wred = red + wave * 16;
   const int wstride = nw * 16;
-  if constexpr (KB >= 4) {  // one buffer: such launches take one tile per workgroup
-    for (int i = 0; i < nt; ++i) {
-      if (i > 0) mf_load_tile<KB>(m, tile_of(i), b0, nb, n16, g, va);  // after this tile's waits
-      mf_tile<KB>(va, nb, lds, a_lo, a_hi, inc_lo, inc_hi, sum_off, f0, f1, wred + i * wstride,
-                  n16, g);
-    }
-  } else {  // the next tile's weights in flight while the current one is computed
-    // (the loads past the last tile re-read that tile: unconditional, as above)
-    MfBlk vb[KB];
-    for (int i = 0; i < nt; i += 2) {
-      mf_load_tile<KB>(m, tile_of(i + 1), b0, nb, n16, g, vb);
-      mf_tile<KB>(va, nb, lds, a_lo, a_hi, inc_lo, inc_hi, sum_off, f0, f1, wred + i * wstride,
-                  n16, g);
-      if (i + 1 >= nt) break;
-      mf_load_tile<KB>(m, tile_of(i + 2), b0, nb, n16, g, va);
-      mf_tile<KB>(vb, nb, lds, a_lo, a_hi, inc_lo, inc_hi, sum_off, f0, f1,
-                  wred + (i + 1) * wstride, n16, g);
-    }
-  }
+
+  // the activations' loads, the first DEPTH tiles' weights, then the split (waiting for the
+  // activations only)
+  constexpr int MC = KB >= 2 ? KB / 2 : 1;  // cells per thread: 32 nblk cells, 64 ceil(nblk / KB) threads
+  constexpr int NB = DEPTH + 1;             // weight buffers
+  constexpr int PRE = DEPTH > 1 ? DEPTH : 1;  // tiles loaded before the split
+  MfCells<MC> cv;
+  mf_split_load<MC>(x, nblk, cv);
+  MfBlk buf[NB][KB];
+  mf_unroll<PRE>([&](auto T) {
+    constexpr int t = decltype(T)::value;
+    if constexpr (t < TPW) mf_load_tile<KB>(m, tile_of(t), b0, nb, n16, g, buf[t % NB]);
+  });
+  mf_split<MC>(cv, nblk, lds);
+  __syncthreads();
+  mf_unroll<TPW>([&](auto T) {
+    constexpr int t = decltype(T)::value;
+    if constexpr (t + DEPTH < TPW && t + DEPTH >= PRE)  // (DEPTH 0: tile t, just before its use)
+      mf_load_tile<KB>(m, tile_of(t + DEPTH), b0, nb, n16, g, buf[(t + DEPTH) % NB]);
+    mf_tile<KB>(buf[t % NB], nb, lds, a_lo, a_hi, inc_lo, inc_hi, sum_off, f0, f1,
+                wred + t * wstride, n16, g, t < nt);
+  });
   __syncthreads();
 
   // 4. the rows: the waves' partial sums in wave order
@@ -299,23 +334,45 @@ bool mf_gemv_ok(int64_t k) {
   return kb <= 4 && mf_lds_bytes(nblk, (nblk + kb - 1) / kb, 1) <= 65536;
 }
 
+// Tiles per workgroup that have a kernel (the next one up is taken).
+constexpr int kMfTpw[] = {1, 2, 3, 4, 6, 7, 8, 12, 16};
+
+template <int KB, int DEPTH>
+static void mf_launch_kb(int tpw, dim3 gd, dim3 bd, int lds, hipStream_t s, const KlMap &m,
+                         int nblk, const float *x) {
+  switch (tpw) {
+#define TQ_MF(T) \
+  case T: hipLaunchKernelGGL((k_gemv_mf<KB, T, DEPTH>), gd, bd, lds, s, m, nblk, x); break;
+    TQ_MF(1) TQ_MF(2) TQ_MF(3) TQ_MF(4) TQ_MF(6) TQ_MF(7) TQ_MF(8) TQ_MF(12) TQ_MF(16)
+#undef TQ_MF
+  }
+}
+
 int launch_gemv_mf(const KlMap &m, int64_t k, const float *x, hipStream_t s) {
   const int nblk = (int)(k / 256);
   const int kb = mf_kb(nblk);
   const int waves = (nblk + kb - 1) / kb;
   const int ntiles = (m.total + 15) / 16;
   const int target = knob(TQ_KNOB_MF_WGS, 256);
-  int tpw = clampi(ntiles / (target > 0 ? target : 1), 1, 16);
-  while (tpw > 1 && mf_lds_bytes(nblk, waves, tpw) > 65536) --tpw;
+  const int want = clampi((ntiles + target - 1) / (target > 0 ? target : 1), 1, 16);
+  int ti = 0;
+  while (kMfTpw[ti] < want) ++ti;
+  while (ti > 0 && mf_lds_bytes(nblk, waves, kMfTpw[ti]) > 65536) --ti;
+  const int tpw = kMfTpw[ti];
   const int lds = mf_lds_bytes(nblk, waves, tpw);
   if (lds > 65536) return -2;
   const int grid = (ntiles + tpw - 1) / tpw;
+  const dim3 gd(grid), bd(64 * waves);
+  // two tiles ahead where the workgroup has several tiles and at most 8 waves (256 VGPRs a lane)
+  const bool deep = kb == 2 && waves <= 8 && tpw >= 3 && knob(TQ_KNOB_MF_DEEP, 1);
   if (kb == 1)
-    hipLaunchKernelGGL(k_gemv_mf<1>, dim3(grid), dim3(64 * waves), lds, s, m, nblk, tpw, x);
+    mf_launch_kb<1, 1>(tpw, gd, bd, lds, s, m, nblk, x);
+  else if (kb == 2 && deep)
+    mf_launch_kb<2, 2>(tpw, gd, bd, lds, s, m, nblk, x);
   else if (kb == 2)
-    hipLaunchKernelGGL(k_gemv_mf<2>, dim3(grid), dim3(64 * waves), lds, s, m, nblk, tpw, x);
+    mf_launch_kb<2, 1>(tpw, gd, bd, lds, s, m, nblk, x);
   else
-    hipLaunchKernelGGL(k_gemv_mf<4>, dim3(grid), dim3(64 * waves), lds, s, m, nblk, tpw, x);
+    mf_launch_kb<4, 0>(tpw, gd, bd, lds, s, m, nblk, x);  // one buffer (128 VGPRs)
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
