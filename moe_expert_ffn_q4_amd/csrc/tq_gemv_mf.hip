@@ -335,7 +335,7 @@ bool mf_gemv_ok(int64_t k) {
 }
 
 // Tiles per workgroup that have a kernel (the next one up is taken).
-constexpr int kMfTpw[] = {1, 2, 3, 4, 6, 7, 8, 12, 16};
+constexpr int kMfTpw[] = {1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16};
 
 template <int KB, int DEPTH>
 static void mf_launch_kb(int tpw, dim3 gd, dim3 bd, int lds, hipStream_t s, const KlMap &m,
@@ -343,7 +343,8 @@ static void mf_launch_kb(int tpw, dim3 gd, dim3 bd, int lds, hipStream_t s, cons
   switch (tpw) {
 #define TQ_MF(T) \
   case T: hipLaunchKernelGGL((k_gemv_mf<KB, T, DEPTH>), gd, bd, lds, s, m, nblk, x); break;
-    TQ_MF(1) TQ_MF(2) TQ_MF(3) TQ_MF(4) TQ_MF(6) TQ_MF(7) TQ_MF(8) TQ_MF(12) TQ_MF(16)
+    TQ_MF(1) TQ_MF(2) TQ_MF(3) TQ_MF(4) TQ_MF(5) TQ_MF(6) TQ_MF(7) TQ_MF(8) TQ_MF(10) TQ_MF(12)
+    TQ_MF(14) TQ_MF(16)
 #undef TQ_MF
   }
 }
