@@ -599,6 +599,11 @@ static bool klane_ok(int fmt, int64_t k, const float *x, int64_t batch) {
          k <= 8 * 4096;
 }
 
+// Batch-1 Q6_K shapes that the fp16 matrix-core kernel takes (rows of whole pairs of blocks).
+static bool mf6_ok(int fmt, int64_t k, const float *x, int64_t batch) {
+  return fmt == FMT_Q6_K && batch == 1 && ((uintptr_t)x & 15) == 0 && mf_gemv_ok(FMT_Q6_K, k);
+}
+
 // Lane groups per wave: 4 for k <= 1024, 2 for k <= 2048, else 1 (TQ_KNOB_KL_GROUPS = 1 turns them off).
 static int kl_groups(int nblk) {
   const int allow = knob(TQ_KNOB_KL_GROUPS, 4);
@@ -622,7 +627,7 @@ static void launch_kl_rg(const KlMap &m, int nblk, int waves, int target, const 
 }
 
 static int launch_kl(const KlMap &m, int64_t k, const float *x, hipStream_t s) {
-  if (mf_gemv_ok(k)) return launch_gemv_mf(m, k, x, s);
+  if (mf_gemv_ok(FMT_Q4_K, k)) return launch_gemv_mf(FMT_Q4_K, m, k, x, s);
   const int nblk = (int)(k / 256);
   const int waves = (nblk + 15) / 16;
   const int kl_rows_env = knob(TQ_KNOB_KL_ROWS, 4);
@@ -704,7 +709,8 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, in
     return launch_f32m(fmt, m, k, x, batch, ws, s);
   }
   const bool i8 = use_i8(fmt, n, k, x, batch, ws, ws_bytes);
-  if (i8 || klane_ok(fmt, k, x, batch)) {
+  const bool mf6 = mf6_ok(fmt, k, x, batch) && n < (1ll << 30);
+  if (i8 || klane_ok(fmt, k, x, batch) || mf6) {
     KlMap m{};
     m.w[0] = wb;
     m.y[0] = y;
@@ -713,6 +719,7 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, in
     m.total = (int)n;
     m.row_bytes = rb;
     if (i8) return launch_i8(fmt, m, k, x, ws, s);
+    if (mf6) return launch_gemv_mf(FMT_Q6_K, m, k, x, s);
     return launch_kl(m, k, x, s);
   }
   switch (fmt) {
@@ -752,7 +759,8 @@ int launch_gemv_multi(int fmt, int nparts, const void *const *w, const int64_t *
   }
   const bool f32m = use_f32m(fmt, total, k, x, batch, ws, ws_bytes);
   const bool i8 = !f32m && use_i8(fmt, total, k, x, batch, ws, ws_bytes);
-  if ((f32m || i8 || klane_ok(fmt, k, x, batch)) && nparts <= 4 && total < (1ll << 30)) {
+  const bool mf6 = !f32m && mf6_ok(fmt, k, x, batch);
+  if ((f32m || i8 || klane_ok(fmt, k, x, batch) || mf6) && nparts <= 4 && total < (1ll << 30)) {
     KlMap m{};
     for (int p = 0; p < nparts; ++p) {
       m.w[p] = (const uint8_t *)w[p];
@@ -764,6 +772,7 @@ int launch_gemv_multi(int fmt, int nparts, const void *const *w, const int64_t *
     m.row_bytes = k / fmt_block_weights(fmt) * fmt_block_bytes(fmt);
     if (f32m) return launch_f32m(fmt, m, k, x, batch, ws, s);
     if (i8) return launch_i8(fmt, m, k, x, ws, s);
+    if (mf6) return launch_gemv_mf(FMT_Q6_K, m, k, x, s);
     return launch_kl(m, k, x, s);
   }
   for (int p = 0; p < nparts; ++p) {  // one launch per matrix, in order on the stream
@@ -812,7 +821,8 @@ int launch_gemv_swiglu(int fmt, const void *wg, const void *wu, int64_t n, int64
     return launch_f32m(fmt, m, k, x, batch, ws, s);
   }
   const bool i8 = use_i8(fmt, 2 * n, k, x, batch, ws, ws_bytes);
-  if ((i8 || klane_ok(fmt, k, x, batch)) && n < (1ll << 29)) {
+  const bool mf6 = mf6_ok(fmt, k, x, batch);
+  if ((i8 || klane_ok(fmt, k, x, batch) || mf6) && n < (1ll << 29)) {
     KlMap m{};
     m.w[0] = (const uint8_t *)wg;
     m.w[1] = (const uint8_t *)wu;
@@ -823,6 +833,7 @@ int launch_gemv_swiglu(int fmt, const void *wg, const void *wu, int64_t n, int64
     m.cum[1] = m.total;
     m.row_bytes = rb;
     if (i8) return launch_i8(fmt, m, k, x, ws, s);
+    if (mf6) return launch_gemv_mf(FMT_Q6_K, m, k, x, s);
     return launch_kl(m, k, x, s);
   }
   if (use_qmm(fmt, n, k, x, batch, ws, ws_bytes, true)) {
@@ -849,7 +860,7 @@ int launch_gemv_swiglu(int fmt, const void *wg, const void *wu, int64_t n, int64
 }
 
 bool gemv_swiglu_fused(int fmt, int64_t k, const float *x, int64_t batch) {
-  return klane_ok(fmt, k, x, batch);
+  return klane_ok(fmt, k, x, batch) || mf6_ok(fmt, k, x, batch);
 }
 
 // ---- SwiGLU ------------------------------------------------------------------------------------

@@ -1,8 +1,8 @@
-// tq_gemv_mf.hip -- batch-1 Q4_K GEMV with the multiply-adds on the fp16 matrix cores.
+// tq_gemv_mf.hip -- batch-1 Q4_K and Q6_K GEMV with the multiply-adds on the fp16 matrix cores.
 //
-// Per 256-weight block of a row (d, dmin, sub-block scales sc_j and mins m_j, quants q) the product
-// with x is  d * sum_j sc_j sum_{k in j} q_k x_k  -  dmin * sum_j m_j S_j  (S_j = sum of x over
-// sub-block j, j = 0..7). The inner sums go to v_mfma_f32_16x16x32_f16:
+// Q4_K. Per 256-weight block of a row (d, dmin, sub-block scales sc_j and mins m_j, quants q) the
+// product with x is  d * sum_j sc_j sum_{k in j} q_k x_k  -  dmin * sum_j m_j S_j  (S_j = sum of x
+// over sub-block j, j = 0..7). The inner sums go to v_mfma_f32_16x16x32_f16:
 //   * weight operand (B, 32 k x 16 rows): the nibbles themselves, as fp16 subnormals q * 2^-24
 //     (a word masked with 0x000F000F is two of them; with 0x00F000F0, two of 16 q * 2^-24), so
 //     building it takes a few AND/shift operations per 8 weights and nothing else;
@@ -21,9 +21,25 @@
 // (with a factor 1/16 on the high-nibble sub-block). The products are exact (an fp16 subnormal
 // quant times an 11-bit fp16 value), they add in fp32, and x enters with 22 significant bits.
 //
+// Q6_K. Per block (d, sixteen int8 scales sc_j of 16-weight sub-blocks, quants q = low4 + 16 high2
+// in 0..63, weight i = 128 h + 32 r + l: low4 a nibble of ql[64 h + l + 32 (r % 2)], low for r < 2,
+// high2 bits 2r, 2r+1 of qh[32 h + l], sub-block j = i / 16) the product with x is
+//   d * sum_j sc_j (sum_{k in j} q_k x_k - 32 S_j).
+// Lane l (row n = l % 16, quarter g = l / 16) loads, of each 128-weight half h, ql bytes
+// 64 h + 16 g .. + 15 and the qh bytes of the same positions l (16 (g % 2) .. + 15): low nibbles of
+// r = g / 2 and high nibbles of r = g / 2 + 2. Product t (0..3) of half h takes positions
+// 16 (g % 2) + 8 (t % 2) .. + 7 of r = g / 2 + 2 (t / 2), i.e. sub-block 8 h + 4 (t / 2) + g, as two
+// products into the half's accumulator: the low nibbles (in place: 1 or 16 times the nibble) and
+// the high bits shifted to 16 (or 256) times their value, so both carry the same factor F (1 or
+// 16) of their sub-block. Operand rows 2 jj + h' (jj = j - 8 h) separate the half's 8 sub-blocks;
+// the output lane holds sub-blocks 2 g, 2 g + 1 of each half (F = 16 for g >= 2) and folds
+//   d * sc_j (2^24 / F * f_j (C_hi + C_lo) - 32 S_j).
+// Rows start on a dword (k a multiple of 512): an even block starts on a dword, an odd one two bytes
+// past one, and its pieces are loaded from the dword below and realigned in registers.
+//
 // Work split: a workgroup takes whole 16-row tiles and all of k. It first splits x into the
 // operand layout in LDS (with the zero bytes the empty operand rows read), then wave w streams
-// blocks [w KB, w KB + KB) of its tiles, the next tile's weights loaded while it computes the
+// blocks [w KB, w KB + KB) of its tiles, the next tiles' weights loaded while it computes the
 // current one, and leaves one partial sum per row in LDS; after one barrier the workgroup adds the
 // waves' partial sums in wave order and stores the rows. Nothing is split across workgroups, so a
 // row's sum is formed the same way whatever the matrix height, the part it falls in or the launch.
@@ -41,27 +57,224 @@ namespace tq {
 typedef _Float16 mf_h8 __attribute__((ext_vector_type(8)));
 typedef float mf_f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMfZero = 64;         // zero bytes at the start of LDS
-constexpr int kMfBlockLds = 1024;   // one block's activation operands: 8 sub-blocks x hi/lo x 4 x 16 B
-constexpr int kMfSumLds = 64;       // one block's [group][S_2g, S_2g+1, f_2g, f_2g+1]
-
-// LDS bytes of a workgroup: zeros, operands, sums and scales, the waves' partial sums.
-__host__ __device__ inline int mf_lds_bytes(int nblk, int waves, int tiles) {
-  return kMfZero + nblk * (kMfBlockLds + kMfSumLds) + tiles * waves * 16 * 4;
+template <class F, int... I>
+__device__ __forceinline__ void static_for_mf_(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, in order
+template <int N, class F>
+__device__ __forceinline__ void static_for_mf(F &&f) {
+  static_for_mf_(f, std::make_integer_sequence<int, N>{});
 }
 
-// One block of one row as the lane loads it: header (d, dmin, packed scales) and its group's 32
-// quant bytes.
-struct MfBlk {
-  u32x4 hdr, qa, qb;
+constexpr int kMfZero = 64;         // zero bytes at the start of LDS
+constexpr int kMfBlockLds = 1024;   // one block's activation operands: 256 values x hi/lo x 2 B
+
+// The activation operands and sums of one block in LDS, and the lane's part of a block.
+template <int FMT>
+struct MfFmt;
+
+__device__ __forceinline__ mf_f4 mf_lds4(const uint8_t *lds, uint32_t off) {
+  return *reinterpret_cast<const mf_f4 *>(lds + off);
+}
+__device__ __forceinline__ mf_h8 mf_lds_op(const uint8_t *lds, uint32_t off) {
+  return *reinterpret_cast<const mf_h8 *>(lds + off);
+}
+__device__ __forceinline__ mf_f4 mf_mfma(mf_h8 a, u32x4 b, mf_f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(mf_h8, b), c, 0, 0, 0);
+}
+
+// ---- Q4_K ----
+template <>
+struct MfFmt<FMT_Q4_K> {
+  static constexpr int kBytes = 144;  // block bytes in a row
+  static constexpr int kSub = 8;      // sub-blocks of 32 weights
+  static constexpr int kSumLds = 64;  // per block: [group g][S_2g, S_2g+1, f_2g, f_2g+1]
+  // cell (sub-block j, hi/lo h, quarter u) of a block's operands
+  static __device__ int cell_off(int j, int h, int u) { return (8 * j + 4 * h + u) * 16; }
+  // header (d, dmin, packed scales) and the group's 32 quant bytes
+  struct Blk {
+    u32x4 hdr, qa, qb;
+  };
+  struct Lane {
+    Q4kField f0, f1;
+    uint32_t a_lo, a_hi, inc_lo, inc_hi, sum_off;
+  };
+  // operand rows 4g, 4g+1 take sub-block 2g (products 0..3), rows 4g+2, 4g+3 sub-block 2g+1
+  static __device__ Lane lane(int n16, int g, int b0, int nblk) {
+    Lane L;
+    L.f0 = q4k_field(2 * g);
+    L.f1 = q4k_field(2 * g + 1);
+    const bool mlo = (n16 >> 1) == 2 * g, mhi = (n16 >> 1) == 2 * g + 1;
+    const uint32_t own = kMfZero + (uint32_t)b0 * kMfBlockLds + 64u * n16;
+    L.a_lo = mlo ? own : 0u;
+    L.a_hi = mhi ? own : 0u;
+    L.inc_lo = mlo ? kMfBlockLds : 0u;
+    L.inc_hi = mhi ? kMfBlockLds : 0u;
+    L.sum_off = kMfZero + nblk * kMfBlockLds + (uint32_t)b0 * kSumLds + 16u * g;
+    return L;
+  }
+  // the block slot past the wave's last block re-reads that block
+  static __device__ int clamp_block(int b, int nb) { return min(b, nb - 1); }
+  template <int B>
+  static __device__ void load(const uint8_t *p, int g, Blk &b) {
+    b.hdr = gload(p);
+    b.qa = gload(p + 16 + 32 * g);
+    b.qb = gload(p + 32 + 32 * g);
+  }
+  // The weight operand from the lane's two quant dwords (low or high nibbles).
+  template <bool HIGH>
+  static __device__ u32x4 wop(uint32_t d0, uint32_t d1) {
+    constexpr uint32_t M = HIGH ? 0x00F000F0u : 0x000F000Fu;
+    return u32x4{d0 & M, (d0 >> 8) & M, d1 & M, (d1 >> 8) & M};
+  }
+  // eight products into one tile, then the fold of the lane's two sub-blocks
+  template <int B>
+  static __device__ float block(const Blk &b, const uint8_t *lds, const Lane &L) {
+    mf_h8 A[8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      A[t] = mf_lds_op(lds, L.a_lo + B * L.inc_lo + 16 * t);
+      A[4 + t] = mf_lds_op(lds, L.a_hi + B * L.inc_hi + 16 * t);
+    }
+    const mf_f4 sf = mf_lds4(lds, L.sum_off + B * kSumLds);
+    const uint32_t qd[8] = {b.qa.x, b.qa.y, b.qa.z, b.qa.w, b.qb.x, b.qb.y, b.qb.z, b.qb.w};
+    mf_f4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) c = mf_mfma(A[t], wop<false>(qd[2 * t], qd[2 * t + 1]), c);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) c = mf_mfma(A[4 + t], wop<true>(qd[2 * t], qd[2 * t + 1]), c);
+    const uint32_t h0 = b.hdr.x;
+    const float d24 = half_bits_to_float(h0) * 0x1p24f, dmin = half_bits_to_float(h0 >> 16);
+    float sc_a, m_a, sc_b, m_b;
+    q4k_scale_min_at(b.hdr.y, b.hdr.z, b.hdr.w, L.f0, sc_a, m_a);
+    q4k_scale_min_at(b.hdr.y, b.hdr.z, b.hdr.w, L.f1, sc_b, m_b);
+    const float pa = d24 * sc_a * sf[2], pb = d24 * sc_b * 0.0625f * sf[3];
+    const float mn = __builtin_fmaf(m_a, sf[0], m_b * sf[1]);
+    return __builtin_fmaf(pa, c[0] + c[1], __builtin_fmaf(pb, c[2] + c[3], -dmin * mn));
+  }
 };
 
-// 1. x -> operand layout. Cell c = (block b, sub-block j, quarter u) holds positions 8u .. 8u + 7
-// of the sub-block, in the order the weight operand takes them (a masked word holds the nibbles of
-// bytes 0 and 2, the word shifted by 8 those of bytes 1 and 3): 0 2 1 3 4 6 5 7. Thread t takes
-// cells t, t + blockDim, ... (at most MC); four neighbouring threads take the four quarters of one
-// sub-block, and whole quads are in or out of range together. The values are loaded before the
-// weights (mf_split_load), so that the split waits only for them.
+// ---- Q6_K ----
+template <>
+struct MfFmt<FMT_Q6_K> {
+  static constexpr int kBytes = 210;
+  static constexpr int kSub = 16;      // sub-blocks of 16 weights
+  static constexpr int kSumLds = 128;  // per block: [half h][g][S_j, S_j+1, f_j, f_j+1], j = 8h + 2g
+  static __device__ int cell_off(int j, int h, int u) { return (4 * j + 2 * h + u) * 16; }
+  // pieces: ql of half 0 and 1, qh of half 0 and 1, scales; for an odd block each loaded from two
+  // bytes below with the dword after it (e), realigned at use; e[4] also holds d (even: d in its
+  // low half, odd: in its high half)
+  struct Blk {
+    u32x4 c[5];
+    uint32_t e[5];
+  };
+  struct Lane {
+    uint32_t a0, a1, incb0, incb1, inch0, inch1, sum_off, sh, shr, sc_bit;
+    int sc_hi;       // the scale dword of half h is 2h + sc_hi
+    float k24f;      // 2^24 / F
+    int g;
+  };
+  // Operand row i = 2 jj + h' of a half takes sub-block jj: products 0, 1 of the half give quarter g
+  // sub-block g, products 2, 3 sub-block 4 + g; lane (i, g) reads its row's cell for the products
+  // whose quarter-g sub-block is i / 2, the zero bytes for the others.
+  static __device__ Lane lane(int n16, int g, int b0, int nblk) {
+    Lane L;
+    const bool m0 = (n16 >> 1) == g, m1 = (n16 >> 1) == 4 + g;
+    const uint32_t own = kMfZero + (uint32_t)b0 * kMfBlockLds + 32u * n16;
+    L.a0 = m0 ? own : 0u;
+    L.a1 = m1 ? own : 0u;
+    L.incb0 = m0 ? kMfBlockLds : 0u;
+    L.incb1 = m1 ? kMfBlockLds : 0u;
+    L.inch0 = m0 ? 512u : 0u;
+    L.inch1 = m1 ? 512u : 0u;
+    L.sum_off = kMfZero + nblk * kMfBlockLds + (uint32_t)b0 * kSumLds + 16u * g;
+    L.sh = (g >> 1) ? 2u : 4u;  // high bits 2r, 2r+1 of r = g/2 (+2) to bits 4, 5 (8, 9)
+    L.shr = 8u - L.sh;
+    L.sc_bit = 16u * (g & 1);
+    L.sc_hi = g >> 1;
+    L.k24f = g >= 2 ? 0x1p20f : 0x1p24f;
+    L.g = g;
+    return L;
+  }
+  // (the wave's blocks start at an even index and nb is even: the slot keeps its parity)
+  static __device__ int clamp_block(int b, int nb) { return b < nb ? b : nb - 2 + (b & 1); }
+  static __device__ uint32_t off(int i, int g) {
+    return i < 2 ? 64 * i + 16 * g : i < 4 ? 128 + 32 * (i - 2) + 16 * (g & 1) : 192;
+  }
+  template <int B>
+  static __device__ void load(const uint8_t *p, int g, Blk &b) {
+    if constexpr ((B & 1) == 0) {
+#pragma unroll
+      for (int i = 0; i < 5; ++i) b.c[i] = *(gu32x4a4)(p + off(i, g));
+      b.e[4] = *(const __attribute__((address_space(1))) uint32_t *)(p + 208);
+    } else {
+      const uint8_t *q = p - 2;
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        b.c[i] = *(gu32x4a4)(q + off(i, g));
+        b.e[i] = *(const __attribute__((address_space(1))) uint32_t *)(q + off(i, g) + 16);
+      }
+    }
+  }
+  template <int B>
+  static __device__ u32x4 piece(const Blk &b, int i) {
+    if constexpr ((B & 1) == 0) {
+      return b.c[i];
+    } else {
+      const u32x4 w = b.c[i];
+      return u32x4{shift2(w.x, w.y), shift2(w.y, w.z), shift2(w.z, w.w), shift2(w.w, b.e[i])};
+    }
+  }
+  template <int B>
+  static __device__ float block(const Blk &b, const uint8_t *lds, const Lane &L) {
+    const u32x4 sc = piece<B>(b, 4);
+    const float d = half_bits_to_float((B & 1) ? b.e[4] >> 16 : b.e[4]);
+    float acc = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4 ql = piece<B>(b, h), qh = piece<B>(b, 2 + h);
+      const uint32_t a0 = L.a0 + B * L.incb0 + h * L.inch0, a1 = L.a1 + B * L.incb1 + h * L.inch1;
+      const mf_f4 sf = mf_lds4(lds, L.sum_off + B * kSumLds + 64 * h);
+      mf_f4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint32_t l0 = ql[2 * u], l1 = ql[2 * u + 1], l0s = l0 >> 8, l1s = l1 >> 8;
+        const uint32_t hq0 = qh[2 * u], hq1 = qh[2 * u + 1];
+        const uint32_t h0l = hq0 << L.sh, h0r = hq0 >> L.shr, h1l = hq1 << L.sh, h1r = hq1 >> L.shr;
+#pragma unroll
+        for (int ts = 0; ts < 2; ++ts) {  // r = g/2 (low nibbles, high bits x16), r = g/2 + 2 (x16)
+          const uint32_t ML = ts ? 0x00F000F0u : 0x000F000Fu, MH = ts ? 0x03000300u : 0x00300030u;
+          const mf_h8 A = mf_lds_op(lds, (ts ? a1 : a0) + 16 * u);
+          c = mf_mfma(A, u32x4{l0 & ML, l0s & ML, l1 & ML, l1s & ML}, c);
+          c = mf_mfma(A, u32x4{h0l & MH, h0r & MH, h1l & MH, h1r & MH}, c);
+        }
+      }
+      // sub-blocks j = 8h + 2g + s (s = 0, 1): scale bytes 2 (g % 2) + s of dword 2h + g / 2
+      const uint32_t sd = L.sc_hi ? sc[2 * h + 1] : sc[2 * h];
+      // (the builtin's result type is unsigned: the sign-extended field is read back as int)
+      const float s0 = (float)(int)__builtin_amdgcn_sbfe(sd, L.sc_bit, 8);
+      const float s1 = (float)(int)__builtin_amdgcn_sbfe(sd, L.sc_bit + 8, 8);
+      const float t0 = __builtin_fmaf(L.k24f * sf[2], c[0] + c[1], -32.f * sf[0]);
+      const float t1 = __builtin_fmaf(L.k24f * sf[3], c[2] + c[3], -32.f * sf[1]);
+      acc = __builtin_fmaf(s0, t0, __builtin_fmaf(s1, t1, acc));
+    }
+    return d * acc;
+  }
+};
+
+// LDS bytes of a workgroup: zeros, operands, sums and scales, the waves' partial sums.
+template <int FMT>
+__host__ __device__ inline int mf_lds_bytes(int nblk, int waves, int tiles) {
+  return kMfZero + nblk * (kMfBlockLds + MfFmt<FMT>::kSumLds) + tiles * waves * 16 * 4;
+}
+
+// 1. x -> operand layout. Cell c = (block b, sub-block j, part u) holds 8 values of the sub-block,
+// in the order the weight operand takes them (a masked word holds the nibbles of bytes 0 and 2, the
+// word shifted by 8 those of bytes 1 and 3): 0 2 1 3 4 6 5 7. Thread t takes cells t, t + blockDim,
+// ... (at most MC); the neighbouring threads of one sub-block (4 for Q4_K, 2 for Q6_K) are in or
+// out of range together. The values are loaded before the weights (mf_split_load), so that the
+// split waits only for them.
 template <int MC>
 struct MfCells {
   float4 v[MC][2];
@@ -77,8 +290,10 @@ __device__ __forceinline__ void mf_split_load(const float *__restrict__ x, int n
     c.v[i][1] = src[1];
   }
 }
-template <int MC>
+template <int FMT, int MC>
 __device__ __forceinline__ void mf_split(const MfCells<MC> &cv, int nblk, uint8_t *lds) {
+  using F = MfFmt<FMT>;
+  constexpr int kCells = 32 / F::kSub;  // cells per sub-block
   if (threadIdx.x < kMfZero / 16) *reinterpret_cast<u32x4 *>(lds + 16 * threadIdx.x) = u32x4{0, 0, 0, 0};
   const int cells = nblk * 32;
   uint8_t *ops = lds + kMfZero;
@@ -91,7 +306,7 @@ __device__ __forceinline__ void mf_split(const MfCells<MC> &cv, int nblk, uint8_
     float m = fmaxf(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))),
                     fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
     m = fmaxf(m, xor_recv(m, 1));
-    m = fmaxf(m, xor_recv(m, 2));
+    if constexpr (kCells == 4) m = fmaxf(m, xor_recv(m, 2));
     int e = 0;
     if (m > 0.f) {
       int ex;
@@ -116,81 +331,33 @@ __device__ __forceinline__ void mf_split(const MfCells<MC> &cv, int nblk, uint8_
       hi[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hf[2 * k], hf[2 * k + 1]));
       lo[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lf[2 * k], lf[2 * k + 1]));
     }
-    const int b = c >> 5, j = (c >> 2) & 7, u = c & 3;
-    uint8_t *dst = ops + b * kMfBlockLds + (4 * (2 * j) + u) * 16;
-    *reinterpret_cast<u32x4 *>(dst) = hi;
-    *reinterpret_cast<u32x4 *>(dst + 64) = lo;
+    const int b = c >> 5, j = (c & 31) / kCells, u = c % kCells;
+    uint8_t *blk = ops + b * kMfBlockLds;
+    *reinterpret_cast<u32x4 *>(blk + F::cell_off(j, 0, u)) = hi;
+    *reinterpret_cast<u32x4 *>(blk + F::cell_off(j, 1, u)) = lo;
     float sum = ((v0.x + v0.y) + (v0.z + v0.w)) + ((v1.x + v1.y) + (v1.z + v1.w));
     sum += xor_recv(sum, 1);
-    sum += xor_recv(sum, 2);
-    if (u == 0) {
-      float *q = sums + b * 16 + (j >> 1) * 4;
+    if constexpr (kCells == 4) sum += xor_recv(sum, 2);
+    if (u == 0) {  // sums [j / 2][S_j, S_j^1, f_j, f_j^1] (pairs of neighbouring sub-blocks)
+      float *q = sums + b * (F::kSumLds / 4) + (j >> 1) * 4;
       q[j & 1] = sum;
       q[2 + (j & 1)] = ldexpf(1.f, -e);
     }
   }
 }
 
-// 2. the lane's loads of one block of its tile row
-__device__ __forceinline__ void mf_load_blk(const uint8_t *p, int g, MfBlk &b) {
-  b.hdr = gload(p);
-  b.qa = gload(p + 16 + 32 * g);
-  b.qb = gload(p + 32 + 32 * g);
-}
-
-// The weight operand of product t from the lane's two quant dwords (low or high nibbles).
-template <bool HIGH>
-__device__ __forceinline__ mf_h8 mf_wop(uint32_t d0, uint32_t d1) {
-  constexpr uint32_t M = HIGH ? 0x00F000F0u : 0x000F000Fu;
-  const u32x4 v = {d0 & M, (d0 >> 8) & M, d1 & M, (d1 >> 8) & M};
-  return __builtin_bit_cast(mf_h8, v);
-}
-
-// 3. one block: eight products into one tile, then the fold of the lane's two sub-blocks.
-// The lane's activation operands of one block (products 0..3 from its a_lo, 4..7 from its a_hi:
-// its own operand row, or the zero bytes) and the block's sums and scales of its group.
-struct MfAct {
-  mf_h8 A[8];
-  mf_f4 sf;
-};
-__device__ __forceinline__ void mf_act_load(const uint8_t *lds, uint32_t a_lo, uint32_t a_hi,
-                                            uint32_t sum_off, MfAct &a) {
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    a.A[t] = *reinterpret_cast<const mf_h8 *>(lds + a_lo + 16 * t);
-    a.A[4 + t] = *reinterpret_cast<const mf_h8 *>(lds + a_hi + 16 * t);
-  }
-  a.sf = *reinterpret_cast<const mf_f4 *>(lds + sum_off);
-}
-__device__ __forceinline__ float mf_block(const MfBlk &b, const MfAct &a, const Q4kField &f0,
-                                          const Q4kField &f1) {
-  const uint32_t qd[8] = {b.qa.x, b.qa.y, b.qa.z, b.qa.w, b.qb.x, b.qb.y, b.qb.z, b.qb.w};
-  mf_f4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.A[t], mf_wop<false>(qd[2 * t], qd[2 * t + 1]), c, 0, 0, 0);
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.A[4 + t], mf_wop<true>(qd[2 * t], qd[2 * t + 1]), c, 0, 0, 0);
-  const uint32_t h0 = b.hdr.x;
-  const float d24 = half_bits_to_float(h0) * 0x1p24f, dmin = half_bits_to_float(h0 >> 16);
-  float sc_a, m_a, sc_b, m_b;
-  q4k_scale_min_at(b.hdr.y, b.hdr.z, b.hdr.w, f0, sc_a, m_a);
-  q4k_scale_min_at(b.hdr.y, b.hdr.z, b.hdr.w, f1, sc_b, m_b);
-  const mf_f4 sf = a.sf;
-  const float pa = d24 * sc_a * sf[2], pb = d24 * sc_b * 0.0625f * sf[3];
-  const float mn = __builtin_fmaf(m_a, sf[0], m_b * sf[1]);
-  return __builtin_fmaf(pa, c[0] + c[1], __builtin_fmaf(pb, c[2] + c[3], -dmin * mn));
-}
-
-// Every block slot is loaded (past the wave's last block: that block again), so that no load sits
-// behind a branch: the compiler then counts the loads in flight and waits for each block's own.
-template <int KB>
+// 2. the lane's loads of its tile row. Every block slot is loaded (past the wave's last block: a
+// block again), so that no load sits behind a branch: the compiler then counts the loads in
+// flight and waits for each block's own.
+template <int FMT, int KB>
 __device__ __forceinline__ void mf_load_tile(const KlMap &m, int tile, int b0, int nb, int n16,
-                                             int g, MfBlk (&buf)[KB]) {
-  const uint8_t *rp = m.row(min(tile * 16 + n16, m.total - 1)) + (int64_t)b0 * 144;
-#pragma unroll
-  for (int b = 0; b < KB; ++b) mf_load_blk(rp + min(b, nb - 1) * 144, g, buf[b]);
+                                             int g, typename MfFmt<FMT>::Blk (&buf)[KB]) {
+  using F = MfFmt<FMT>;
+  const uint8_t *rp = m.row(min(tile * 16 + n16, m.total - 1)) + (int64_t)b0 * F::kBytes;
+  static_for_mf<KB>([&](auto B) {
+    constexpr int b = decltype(B)::value;
+    F::template load<b>(rp + F::clamp_block(b, nb) * F::kBytes, g, buf[b]);
+  });
 }
 
 // The sum of v over lanes l and l ^ 16 (SWAP16) or l and l ^ 32, by a lane swap between rows
@@ -204,67 +371,46 @@ __device__ __forceinline__ float mf_pair_sum(float v) {
   return __builtin_bit_cast(float, (unsigned)sw[0]) + __builtin_bit_cast(float, (unsigned)sw[1]);
 }
 
-// One tile's blocks of the wave (the activation operands read from LDS per block: holding them
-// in registers across tiles measured no faster), then the sum over the lane's four groups.
-template <int KB>
-__device__ __forceinline__ void mf_tile(const MfBlk (&buf)[KB], int nb, const uint8_t *lds,
-                                        uint32_t a_lo, uint32_t a_hi, uint32_t inc_lo,
-                                        uint32_t inc_hi, uint32_t sum_off, const Q4kField &f0,
-                                        const Q4kField &f1, float *red, int n16, int g,
-                                        bool keep) {
+// 3. one tile's blocks of the wave (the activation operands read from LDS per block: holding them
+// in registers across tiles measured no faster), then the sum over the lane's four groups
+template <int FMT, int KB>
+__device__ __forceinline__ void mf_tile(const typename MfFmt<FMT>::Blk (&buf)[KB], int nb,
+                                        const uint8_t *lds, const typename MfFmt<FMT>::Lane &L,
+                                        float *red, int n16, int g, bool keep) {
   float acc = 0.f;
-#pragma unroll
-  for (int b = 0; b < KB; ++b)
-    if (b < nb) {
-      MfAct a;
-      mf_act_load(lds, a_lo + b * inc_lo, a_hi + b * inc_hi, sum_off + b * kMfSumLds, a);
-      acc += mf_block(buf[b], a, f0, f1);
-    }
+  static_for_mf<KB>([&](auto B) {
+    constexpr int b = decltype(B)::value;
+    if (b < nb) acc += MfFmt<FMT>::template block<b>(buf[b], lds, L);
+  });
   acc = mf_pair_sum<true>(acc);   // groups 0 + 1, 2 + 3
   acc = mf_pair_sum<false>(acc);  // (0 + 1) + (2 + 3)
   if (keep && g == 0) red[n16] = acc;
 }
 
-template <int N, class F, int... I>
-__device__ __forceinline__ void mf_unroll_(F &&f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-// f(std::integral_constant<int, i>) for i = 0 .. N-1, in order
-template <int N, class F>
-__device__ __forceinline__ void mf_unroll(F &&f) {
-  mf_unroll_<N>(f, std::make_integer_sequence<int, N>{});
-}
-
 // Grid: G workgroups, workgroup w taking the 16-row tiles w, w + G, w + 2G, ... (TPW of them, or
 // fewer for the grid's last workgroups): at any time the workgroups stream neighbouring tiles, one
 // window of the matrix. blockDim = 64 * ceil(nblk / KB): at most 16 waves (128 VGPRs a lane), at
-// most 8 when DEPTH = 2 (256). DEPTH 0 (one buffer): each tile after the first is loaded just
-// before its products.
+// most 8 when BIG (256). DEPTH 0 (one buffer): each tile after the first is loaded just before its
+// products.
 // The tiles' code is straight-line (TPW and the buffer of each tile fixed at compile time), with
 // the weights of the next DEPTH tiles in flight while a tile is computed: the compiler then counts
 // every load in flight and waits for each tile's own. (In a loop, loads carried across the back
 // edge and the joins of the buffers' values make it wait for all loads before the next prefetch.)
 // A workgroup with fewer than TPW tiles loads its last tile again for the missing ones and does
 // not keep their sums.
-template <int KB, int TPW, int DEPTH>
-__global__ __launch_bounds__(DEPTH > 1 ? 512 : 1024) void k_gemv_mf(KlMap m, int nblk,
-                                                                    const float *__restrict__ x) {
+template <int FMT, int KB, int TPW, int DEPTH, bool BIG>
+__global__ __launch_bounds__(BIG ? 512 : 1024) void k_gemv_mf(KlMap m, int nblk,
+                                                              const float *__restrict__ x) {
+  using F = MfFmt<FMT>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63, wave = wave_index(), nw = blockDim.x >> 6;
   const int n16 = lane & 15, g = lane >> 4;
   const int ntiles = (m.total + 15) >> 4, G = gridDim.x;
   const int nt = min(TPW, (ntiles - (int)blockIdx.x + G - 1) / G);  // >= 1
   const int b0 = wave * KB, nb = min(KB, nblk - b0);
-  float *red = reinterpret_cast<float *>(lds + kMfZero + nblk * (kMfBlockLds + kMfSumLds));
+  float *red = reinterpret_cast<float *>(lds + kMfZero + nblk * (kMfBlockLds + F::kSumLds));
   auto tile_of = [&](int i) { return (int)blockIdx.x + min(i, nt - 1) * G; };
-
-  // operand rows 4g, 4g+1 take sub-block 2g (products 0..3), rows 4g+2, 4g+3 sub-block 2g+1
-  const Q4kField f0 = q4k_field(2 * g), f1 = q4k_field(2 * g + 1);
-  const bool mlo = (n16 >> 1) == 2 * g, mhi = (n16 >> 1) == 2 * g + 1;
-  const uint32_t own = kMfZero + (uint32_t)b0 * kMfBlockLds + 64u * n16;
-  const uint32_t a_lo = mlo ? own : 0u, a_hi = mhi ? own : 0u;
-  const uint32_t inc_lo = mlo ? kMfBlockLds : 0u, inc_hi = mhi ? kMfBlockLds : 0u;
-  const uint32_t sum_off = kMfZero + nblk * kMfBlockLds + (uint32_t)b0 * kMfSumLds + 16u * g;
+  const typename F::Lane L = F::lane(n16, g, b0, nblk);
   float *wred = red + wave * 16;
   const int wstride = nw * 16;
 
@@ -275,19 +421,18 @@ __global__ __launch_bounds__(DEPTH > 1 ? 512 : 1024) void k_gemv_mf(KlMap m, int
   constexpr int PRE = DEPTH > 1 ? DEPTH : 1;  // tiles loaded before the split
   MfCells<MC> cv;
   mf_split_load<MC>(x, nblk, cv);
-  MfBlk buf[NB][KB];
-  mf_unroll<PRE>([&](auto T) {
+  typename F::Blk buf[NB][KB];
+  static_for_mf<PRE>([&](auto T) {
     constexpr int t = decltype(T)::value;
-    if constexpr (t < TPW) mf_load_tile<KB>(m, tile_of(t), b0, nb, n16, g, buf[t % NB]);
+    if constexpr (t < TPW) mf_load_tile<FMT, KB>(m, tile_of(t), b0, nb, n16, g, buf[t % NB]);
   });
-  mf_split<MC>(cv, nblk, lds);
+  mf_split<FMT, MC>(cv, nblk, lds);
   __syncthreads();
-  mf_unroll<TPW>([&](auto T) {
+  static_for_mf<TPW>([&](auto T) {
     constexpr int t = decltype(T)::value;
     if constexpr (t + DEPTH < TPW && t + DEPTH >= PRE)  // (DEPTH 0: tile t, just before its use)
-      mf_load_tile<KB>(m, tile_of(t + DEPTH), b0, nb, n16, g, buf[(t + DEPTH) % NB]);
-    mf_tile<KB>(buf[t % NB], nb, lds, a_lo, a_hi, inc_lo, inc_hi, sum_off, f0, f1,
-                wred + t * wstride, n16, g, t < nt);
+      mf_load_tile<FMT, KB>(m, tile_of(t + DEPTH), b0, nb, n16, g, buf[(t + DEPTH) % NB]);
+    mf_tile<FMT, KB>(buf[t % NB], nb, lds, L, wred + t * wstride, n16, g, t < nt);
   });
   __syncthreads();
 
@@ -319,61 +464,82 @@ __global__ __launch_bounds__(DEPTH > 1 ? 512 : 1024) void k_gemv_mf(KlMap m, int
 
 // ---- host side ----------------------------------------------------------------------------------
 
-// Blocks per wave: 1 up to k = 2048, 2 up to k = 8192, else 4 (at most 16 waves, k < 16384).
-static int mf_kb(int nblk) {
+// Blocks per wave. Q4_K: 1 up to k = 2048, 2 up to k = 8192, else 4 (at most 16 waves, k < 16384).
+// Q6_K (a block's pieces take 20-25 registers): 2 up to k = 4096, else 4 (at most 8 waves).
+static int mf_kb(int fmt, int nblk) {
   const int v = knob(TQ_KNOB_MF_KB, 0);
+  if (fmt == FMT_Q6_K) {
+    int kb = v == 2 || v == 4 ? v : nblk <= 16 ? 2 : 4;
+    while ((nblk + kb - 1) / kb > 8) kb *= 2;
+    return kb;
+  }
   int kb = v == 1 || v == 2 || v == 4 ? v : nblk <= 8 ? 1 : nblk <= 32 ? 2 : 4;
   while ((nblk + kb - 1) / kb > 16) kb *= 2;
   return kb;
 }
 
-// k < 16384 whose operands fit 64 KB of LDS with one tile per workgroup (k <= 15104)
-bool mf_gemv_ok(int64_t k) {
+static int mf_lds(int fmt, int nblk, int waves, int tiles) {
+  return fmt == FMT_Q6_K ? mf_lds_bytes<FMT_Q6_K>(nblk, waves, tiles)
+                         : mf_lds_bytes<FMT_Q4_K>(nblk, waves, tiles);
+}
+
+// Q4_K: k < 16384 whose operands fit 64 KB of LDS with one tile per workgroup (k <= 14336).
+// Q6_K: k a multiple of 512 up to 8192.
+bool mf_gemv_ok(int fmt, int64_t k) {
   if (!knob(TQ_KNOB_GEMV_MF, 1) || k % 256 != 0 || k < 256 || k >= 16384) return false;
-  const int nblk = (int)(k / 256), kb = mf_kb(nblk);
-  return kb <= 4 && mf_lds_bytes(nblk, (nblk + kb - 1) / kb, 1) <= 65536;
+  if (fmt != FMT_Q4_K && fmt != FMT_Q6_K) return false;
+  if (fmt == FMT_Q6_K && (k % 512 != 0 || k > 8192)) return false;
+  const int nblk = (int)(k / 256), kb = mf_kb(fmt, nblk);
+  return kb <= 4 && mf_lds(fmt, nblk, (nblk + kb - 1) / kb, 1) <= 65536;
 }
 
 // Tiles per workgroup that have a kernel (the next one up is taken).
 constexpr int kMfTpw[] = {1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16};
 
-template <int KB, int DEPTH>
+template <int FMT, int KB, int DEPTH, bool BIG>
 static void mf_launch_kb(int tpw, dim3 gd, dim3 bd, int lds, hipStream_t s, const KlMap &m,
                          int nblk, const float *x) {
   switch (tpw) {
 #define TQ_MF(T) \
-  case T: hipLaunchKernelGGL((k_gemv_mf<KB, T, DEPTH>), gd, bd, lds, s, m, nblk, x); break;
+  case T: hipLaunchKernelGGL((k_gemv_mf<FMT, KB, T, DEPTH, BIG>), gd, bd, lds, s, m, nblk, x); break;
     TQ_MF(1) TQ_MF(2) TQ_MF(3) TQ_MF(4) TQ_MF(5) TQ_MF(6) TQ_MF(7) TQ_MF(8) TQ_MF(10) TQ_MF(12)
     TQ_MF(14) TQ_MF(16)
 #undef TQ_MF
   }
 }
 
-int launch_gemv_mf(const KlMap &m, int64_t k, const float *x, hipStream_t s) {
+int launch_gemv_mf(int fmt, const KlMap &m, int64_t k, const float *x, hipStream_t s) {
   const int nblk = (int)(k / 256);
-  const int kb = mf_kb(nblk);
+  const int kb = mf_kb(fmt, nblk);
   const int waves = (nblk + kb - 1) / kb;
   const int ntiles = (m.total + 15) / 16;
   const int target = knob(TQ_KNOB_MF_WGS, 256);
   const int want = clampi((ntiles + target - 1) / (target > 0 ? target : 1), 1, 16);
   int ti = 0;
   while (kMfTpw[ti] < want) ++ti;
-  while (ti > 0 && mf_lds_bytes(nblk, waves, kMfTpw[ti]) > 65536) --ti;
+  while (ti > 0 && mf_lds(fmt, nblk, waves, kMfTpw[ti]) > 65536) --ti;
   const int tpw = kMfTpw[ti];
-  const int lds = mf_lds_bytes(nblk, waves, tpw);
+  const int lds = mf_lds(fmt, nblk, waves, tpw);
   if (lds > 65536) return -2;
   const int grid = (ntiles + tpw - 1) / tpw;
   const dim3 gd(grid), bd(64 * waves);
+  if (fmt == FMT_Q6_K) {  // at most 8 waves: one buffer at 4 blocks a wave, else two
+    if (kb == 2)
+      mf_launch_kb<FMT_Q6_K, 2, 1, true>(tpw, gd, bd, lds, s, m, nblk, x);
+    else
+      mf_launch_kb<FMT_Q6_K, 4, 0, true>(tpw, gd, bd, lds, s, m, nblk, x);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   // two tiles ahead where the workgroup has several tiles and at most 8 waves (256 VGPRs a lane)
   const bool deep = kb == 2 && waves <= 8 && tpw >= 3 && knob(TQ_KNOB_MF_DEEP, 1);
   if (kb == 1)
-    mf_launch_kb<1, 1>(tpw, gd, bd, lds, s, m, nblk, x);
+    mf_launch_kb<FMT_Q4_K, 1, 1, false>(tpw, gd, bd, lds, s, m, nblk, x);
   else if (kb == 2 && deep)
-    mf_launch_kb<2, 2>(tpw, gd, bd, lds, s, m, nblk, x);
+    mf_launch_kb<FMT_Q4_K, 2, 2, true>(tpw, gd, bd, lds, s, m, nblk, x);
   else if (kb == 2)
-    mf_launch_kb<2, 1>(tpw, gd, bd, lds, s, m, nblk, x);
+    mf_launch_kb<FMT_Q4_K, 2, 1, false>(tpw, gd, bd, lds, s, m, nblk, x);
   else
-    mf_launch_kb<4, 0>(tpw, gd, bd, lds, s, m, nblk, x);  // one buffer (128 VGPRs)
+    mf_launch_kb<FMT_Q4_K, 4, 0, false>(tpw, gd, bd, lds, s, m, nblk, x);  // one buffer (128 VGPRs)
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -151,3 +151,82 @@ def test_mf_graph_replay():
             assert np.array_equal(host(y), eager)
     ref, mag = oracle.gemv("q4_k", w, n, k, x)
     assert_product_close(eager, ref, mag, what="mf graph")
+
+
+# ---- Q6_K ----------------------------------------------------------------------------------------
+# k a multiple of 512 up to 8192: k = 512 one wave of two blocks; 3072 (12 blocks, 6 waves); 4096
+# (8 waves of 2); 4608 (18 blocks: 4 a wave, the last wave 2); 8192 (8 waves of 4). Odd blocks sit
+# two bytes off a dword.
+SHAPES6 = [(1, 512), (37, 3072), (300, 4096), (17, 4608), (1000, 8192), (4099, 8192)]
+
+
+@pytest.mark.parametrize("n,k", SHAPES6)
+def test_mf_q6_k_against_oracle(knobs, n, k):
+    _case("mf q6_k", n, k)
+    g = synth.rng(140, "mf6", n, k)
+    w, x = synth.blob("q6_k", g, n, k), synth.normal_f32(g, (1, k))
+    wd, xd = dev(w), dev(x)
+    y = host(tq.gemv("q6_k", wd, n, k, xd))
+    ref, mag = oracle.gemv("q6_k", w, n, k, x)
+    worst = assert_product_close(y, ref, mag, what=f"mf q6_k {n}x{k}")
+    assert worst < 0.05, worst
+    assert np.array_equal(y, host(tq.gemv("q6_k", wd, n, k, xd))), "not deterministic"
+    knobs("gemv_mf", 0)  # the lane-per-row fp32 kernel
+    y0 = host(tq.gemv("q6_k", wd, n, k, xd))
+    assert_product_close(y0, ref, mag, what=f"k_gemv q6_k {n}x{k}")
+    assert np.linalg.norm(y - y0) <= 2e-5 * np.linalg.norm(y0) + 1e-30
+
+
+@pytest.mark.parametrize("wgs", [1, 5, 64])
+def test_mf_q6_k_tiles_per_workgroup_bitwise(knobs, wgs):
+    n, k = 1001, 8192
+    _case("mf q6_k tiles", wgs)
+    g = synth.rng(141, "mf6-tiles")
+    w, x = synth.blob("q6_k", g, n, k), synth.normal_f32(g, (1, k))
+    wd, xd = dev(w), dev(x)
+    a = host(tq.gemv("q6_k", wd, n, k, xd))
+    knobs("mf_wgs", wgs)
+    assert np.array_equal(a, host(tq.gemv("q6_k", wd, n, k, xd)))
+
+
+def test_mf_q6_k_multi_and_swiglu_bitwise():
+    """Q6_K one-token multi and gate|up + SwiGLU launches (now one launch each) equal the single
+    products bit for bit."""
+    _case("mf q6_k multi swiglu")
+    k = 4096
+    g = synth.rng(142, "mf6-multi")
+    ns = [100, 37, 250]
+    ws = [synth.blob("q6_k", g, n, k) for n in ns]
+    x = dev(synth.normal_f32(g, (1, k)))
+    outs = tq.gemv_multi("q6_k", [dev(w) for w in ws], ns, k, x)
+    for w, n, o in zip(ws, ns, outs):
+        assert np.array_equal(host(o), host(tq.gemv("q6_k", dev(w), n, k, x)))
+    F = 301
+    wg, wu = synth.blob("q6_k", g, F, k), synth.blob("q6_k", g, F, k)
+    h = host(tq.gemv_swiglu("q6_k", dev(wg), dev(wu), F, k, x))
+    gg = tq.gemv("q6_k", dev(wg), F, k, x)
+    uu = tq.gemv("q6_k", dev(wu), F, k, x)
+    assert np.array_equal(h, host(tq.swiglu(gg, uu)))
+
+
+def test_mf_q6_k_extremes():
+    """Scales -128 and 127, quants 0 and 63 (q - 32 at both ends), d at the largest and subnormal
+    fp16, and activation sub-blocks at 1e-30, zero and 1e20: every output within the bar."""
+    n, k = 96, 4096
+    _case("mf q6_k extremes")
+    g = synth.rng(143, "mf6-ext")
+    w = synth.blob("q6_k", g, n, k)
+    blk = w.reshape(-1, 210)
+    blk[0::3, 192:208] = np.uint8(0x80)  # -128
+    blk[1::3, 192:208] = np.uint8(0x7F)  # 127
+    blk[2::5, 0:192] = np.uint8(0xFF)    # q = 63
+    blk[3::5, 0:192] = np.uint8(0x00)    # q = 0
+    blk[0::7, 208:210] = np.frombuffer(np.float16(65504.0).tobytes(), np.uint8)
+    blk[1::11, 208:210] = np.frombuffer(np.float16(2.0 ** -20).tobytes(), np.uint8)
+    x = synth.normal_f32(g, (1, k))
+    x[0, 0:256] *= np.float32(1e-30)
+    x[0, 512:528] = 0.0
+    x[0, 768:1024] *= np.float32(1e20)
+    y = host(tq.gemv("q6_k", dev(w), n, k, dev(x)))
+    ref, mag = oracle.gemv("q6_k", w, n, k, x)
+    assert_product_close(y, ref, mag, what="mf q6_k extremes")
