@@ -406,7 +406,7 @@ enum {
   TQ_KNOB_GEMV_MF = 24, /* batch-1 Q4_K GEMV on the fp16 matrix cores (k < 16384): 1 on (default), 0 the lanes-along-k kernel */
   TQ_KNOB_MF_WGS = 25, /* that kernel: workgroups the launch aims for (256: one per CU, several tiles each) */
   TQ_KNOB_MF_KB = 26, /* that kernel: blocks per wave, 1, 2 or 4 (0: from k) */
-  TQ_KNOB_MF_DEEP = 27, /* that kernel: two tiles in flight ahead of the one computed where a workgroup has 3+ tiles and at most 8 waves, 1 (default) or 0 one */
+  TQ_KNOB_MF_DEEP = 27, /* that kernel: more tiles in flight (Q4_K: two ahead where a workgroup has 3+ tiles and at most 8 waves; Q6_K: one ahead at 4 blocks a wave), 1 (default) or 0 */
   TQ_KNOB_COUNT = 28
 };
 int tq_tuning_set(int knob, int value);

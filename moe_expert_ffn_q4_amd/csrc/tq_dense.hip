@@ -178,6 +178,21 @@ static bool use_i8(int fmt, int64_t rows, int64_t k, const float *x, int64_t bat
          rows < (1ll << 30);
 }
 
+// Batch-1 Q6_K shapes that the fp16 matrix-core kernel takes (rows of whole pairs of blocks) in
+// one k slice, and single products of longer rows in k slices (with the workspace).
+static bool mf6_ok(int fmt, int64_t k, const float *x, int64_t batch) {
+  return fmt == FMT_Q6_K && batch == 1 && ((uintptr_t)x & 15) == 0 && mf_gemv_ok(FMT_Q6_K, k);
+}
+static size_t mf6s_ws_bytes(int fmt, int64_t rows, int64_t k, int64_t batch) {
+  if (fmt != FMT_Q6_K || batch != 1 || !mf_gemv_sliced(FMT_Q6_K, k)) return 0;
+  return kCounterBytes + mf_workspace_bytes(FMT_Q6_K, rows, k);
+}
+static bool use_mf6s(int fmt, int64_t rows, int64_t k, const float *x, int64_t batch,
+                     const void *ws, size_t ws_bytes) {
+  const size_t need = mf6s_ws_bytes(fmt, rows, k, batch);
+  return need && ws != nullptr && ws_bytes >= need && ((uintptr_t)x & 15) == 0;
+}
+
 // Q6_K / Q8_0 batches on the fp32 matrix cores: workspace (counters, slice sums) when k is sliced.
 static size_t f32m_ws_bytes(int fmt, int64_t rows, int64_t k, int64_t batch) {
   if (!f32m_ok(fmt, k, batch)) return 0;
@@ -230,8 +245,8 @@ static size_t max3(size_t a, size_t b, size_t c) { return a > b ? (a > c ? a : c
 size_t gemv_workspace_bytes(int fmt, int64_t n, int64_t k, int64_t batch) {
   const size_t a = max3(split_workspace_bytes(fmt, n, k), i8_ws_bytes(fmt, n, k, batch),
                         qmm_workspace_bytes(fmt, n, k, batch, false));
-  const size_t b = f32m_ws_bytes(fmt, n, k, batch);
-  return a > b ? a : b;
+  const size_t b = f32m_ws_bytes(fmt, n, k, batch), c = mf6s_ws_bytes(fmt, n, k, batch);
+  return max3(a, b, c);
 }
 
 static QmmDense dense_map(int nparts, const void *const *w, const int64_t *n, float *const *y,
@@ -599,10 +614,6 @@ static bool klane_ok(int fmt, int64_t k, const float *x, int64_t batch) {
          k <= 8 * 4096;
 }
 
-// Batch-1 Q6_K shapes that the fp16 matrix-core kernel takes (rows of whole pairs of blocks).
-static bool mf6_ok(int fmt, int64_t k, const float *x, int64_t batch) {
-  return fmt == FMT_Q6_K && batch == 1 && ((uintptr_t)x & 15) == 0 && mf_gemv_ok(FMT_Q6_K, k);
-}
 
 // Lane groups per wave: 4 for k <= 1024, 2 for k <= 2048, else 1 (TQ_KNOB_KL_GROUPS = 1 turns them off).
 static int kl_groups(int nblk) {
@@ -627,7 +638,7 @@ static void launch_kl_rg(const KlMap &m, int nblk, int waves, int target, const 
 }
 
 static int launch_kl(const KlMap &m, int64_t k, const float *x, hipStream_t s) {
-  if (mf_gemv_ok(FMT_Q4_K, k)) return launch_gemv_mf(FMT_Q4_K, m, k, x, s);
+  if (mf_gemv_ok(FMT_Q4_K, k)) return launch_gemv_mf(FMT_Q4_K, m, k, x, nullptr, nullptr, 0, s);
   const int nblk = (int)(k / 256);
   const int waves = (nblk + 15) / 16;
   const int kl_rows_env = knob(TQ_KNOB_KL_ROWS, 4);
@@ -710,7 +721,8 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, in
   }
   const bool i8 = use_i8(fmt, n, k, x, batch, ws, ws_bytes);
   const bool mf6 = mf6_ok(fmt, k, x, batch) && n < (1ll << 30);
-  if (i8 || klane_ok(fmt, k, x, batch) || mf6) {
+  const bool mf6s = !mf6 && use_mf6s(fmt, n, k, x, batch, ws, ws_bytes) && n < (1ll << 30);
+  if (i8 || klane_ok(fmt, k, x, batch) || mf6 || mf6s) {
     KlMap m{};
     m.w[0] = wb;
     m.y[0] = y;
@@ -719,7 +731,10 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, in
     m.total = (int)n;
     m.row_bytes = rb;
     if (i8) return launch_i8(fmt, m, k, x, ws, s);
-    if (mf6) return launch_gemv_mf(FMT_Q6_K, m, k, x, s);
+    if (mf6) return launch_gemv_mf(FMT_Q6_K, m, k, x, nullptr, nullptr, 0, s);
+    if (mf6s)
+      return launch_gemv_mf(FMT_Q6_K, m, k, x, (float *)((char *)ws + kCounterBytes),
+                            (unsigned long long *)ws, (int)(kCounterBytes / 8), s);
     return launch_kl(m, k, x, s);
   }
   switch (fmt) {
@@ -772,7 +787,7 @@ int launch_gemv_multi(int fmt, int nparts, const void *const *w, const int64_t *
     m.row_bytes = k / fmt_block_weights(fmt) * fmt_block_bytes(fmt);
     if (f32m) return launch_f32m(fmt, m, k, x, batch, ws, s);
     if (i8) return launch_i8(fmt, m, k, x, ws, s);
-    if (mf6) return launch_gemv_mf(FMT_Q6_K, m, k, x, s);
+    if (mf6) return launch_gemv_mf(FMT_Q6_K, m, k, x, nullptr, nullptr, 0, s);
     return launch_kl(m, k, x, s);
   }
   for (int p = 0; p < nparts; ++p) {  // one launch per matrix, in order on the stream
@@ -833,7 +848,7 @@ int launch_gemv_swiglu(int fmt, const void *wg, const void *wu, int64_t n, int64
     m.cum[1] = m.total;
     m.row_bytes = rb;
     if (i8) return launch_i8(fmt, m, k, x, ws, s);
-    if (mf6) return launch_gemv_mf(FMT_Q6_K, m, k, x, s);
+    if (mf6) return launch_gemv_mf(FMT_Q6_K, m, k, x, nullptr, nullptr, 0, s);
     return launch_kl(m, k, x, s);
   }
   if (use_qmm(fmt, n, k, x, batch, ws, ws_bytes, true)) {

@@ -8,12 +8,18 @@
 
 namespace tq {
 
-// Format and row length k that the kernel takes (the activation operands of all of k sit in one
-// workgroup's LDS: Q4_K k a multiple of 256 up to 14336, Q6_K a multiple of 512 up to 8192) and its
-// knob.
+// Format and row length k that the kernel takes in one slice (the activation operands of all of
+// k sit in one workgroup's LDS: Q4_K k a multiple of 256 up to 14336, Q6_K a multiple of 512 up to
+// 8192), and longer Q6_K rows that it takes in k slices (k a multiple of 512 cut into 2..8 equal
+// slices of at most 8192, whose sums meet through the workspace). Both honour the knob.
 bool mf_gemv_ok(int fmt, int64_t k);
-// All rows of m (single, multi or SwiGLU pairs) against x (16-byte aligned). 0, -1 (launch error)
-// or -2 (LDS).
-int launch_gemv_mf(int fmt, const KlMap &m, int64_t k, const float *x, hipStream_t s);
+bool mf_gemv_sliced(int fmt, int64_t k);
+// Workspace bytes (after the counters) of a sliced launch of `rows` rows; 0 when not sliced.
+size_t mf_workspace_bytes(int fmt, int64_t rows, int64_t k);
+// All rows of m (single, multi or SwiGLU pairs) against x (16-byte aligned). Sliced launches need
+// partial (mf_workspace_bytes) and one counter per tile set. 0, -1 (launch error) or -2 (shape,
+// LDS or workspace).
+int launch_gemv_mf(int fmt, const KlMap &m, int64_t k, const float *x, float *partial,
+                   unsigned long long *counters, int max_counters, hipStream_t s);
 
 }  // namespace tq

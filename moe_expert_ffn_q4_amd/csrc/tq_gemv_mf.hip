@@ -353,7 +353,7 @@ template <int FMT, int KB>
 __device__ __forceinline__ void mf_load_tile(const KlMap &m, int tile, int b0, int nb, int n16,
                                              int g, typename MfFmt<FMT>::Blk (&buf)[KB]) {
   using F = MfFmt<FMT>;
-  const uint8_t *rp = m.row(min(tile * 16 + n16, m.total - 1)) + (int64_t)b0 * F::kBytes;
+  const uint8_t *rp = m.row(min(tile * 16 + n16, m.total - 1)) + (int64_t)b0 * F::kBytes;  // b0: block in the row
   static_for_mf<KB>([&](auto B) {
     constexpr int b = decltype(B)::value;
     F::template load<b>(rp + F::clamp_block(b, nb) * F::kBytes, g, buf[b]);
@@ -398,18 +398,29 @@ __device__ __forceinline__ void mf_tile(const typename MfFmt<FMT>::Blk (&buf)[KB
 // edge and the joins of the buffers' values make it wait for all loads before the next prefetch.)
 // A workgroup with fewer than TPW tiles loads its last tile again for the missing ones and does
 // not keep their sums.
+//
+// k slices (ksplit > 1, k too long for one workgroup's LDS): workgroup (set gi, slice s) takes
+// the tiles of set gi over blocks [s sb, s sb + sb) only (sb blocks in every slice), stores its
+// rows' sums device-coherently to `partial` and counts itself on set gi's arrival word; the last
+// slice to arrive adds the ksplit sums in slice order and stores the rows.
 template <int FMT, int KB, int TPW, int DEPTH, bool BIG>
-__global__ __launch_bounds__(BIG ? 512 : 1024) void k_gemv_mf(KlMap m, int nblk,
-                                                              const float *__restrict__ x) {
+__global__ __launch_bounds__(BIG ? 512 : 1024) void k_gemv_mf(KlMap m, int sb, int ksplit,
+                                                              const float *__restrict__ xall,
+                                                              float *partial, Arrivals arr) {
   using F = MfFmt<FMT>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ int is_last;
   const int lane = threadIdx.x & 63, wave = wave_index(), nw = blockDim.x >> 6;
   const int n16 = lane & 15, g = lane >> 4;
-  const int ntiles = (m.total + 15) >> 4, G = gridDim.x;
-  const int nt = min(TPW, (ntiles - (int)blockIdx.x + G - 1) / G);  // >= 1
+  const int slice = (int)blockIdx.x % ksplit, gi = (int)blockIdx.x / ksplit;
+  const int ntiles = (m.total + 15) >> 4, G = (int)gridDim.x / ksplit;
+  const int nt = min(TPW, (ntiles - gi + G - 1) / G);  // >= 1
+  const int nblk = sb;                                  // blocks of this slice
+  const float *x = xall + (int64_t)slice * sb * 256;
   const int b0 = wave * KB, nb = min(KB, nblk - b0);
+  const int rb0 = slice * sb + b0;                      // the wave's first block in the row
   float *red = reinterpret_cast<float *>(lds + kMfZero + nblk * (kMfBlockLds + F::kSumLds));
-  auto tile_of = [&](int i) { return (int)blockIdx.x + min(i, nt - 1) * G; };
+  auto tile_of = [&](int i) { return gi + min(i, nt - 1) * G; };
   const typename F::Lane L = F::lane(n16, g, b0, nblk);
   float *wred = red + wave * 16;
   const int wstride = nw * 16;
@@ -424,42 +435,60 @@ __global__ __launch_bounds__(BIG ? 512 : 1024) void k_gemv_mf(KlMap m, int nblk,
   typename F::Blk buf[NB][KB];
   static_for_mf<PRE>([&](auto T) {
     constexpr int t = decltype(T)::value;
-    if constexpr (t < TPW) mf_load_tile<FMT, KB>(m, tile_of(t), b0, nb, n16, g, buf[t % NB]);
+    if constexpr (t < TPW) mf_load_tile<FMT, KB>(m, tile_of(t), rb0, nb, n16, g, buf[t % NB]);
   });
   mf_split<FMT, MC>(cv, nblk, lds);
   __syncthreads();
   static_for_mf<TPW>([&](auto T) {
     constexpr int t = decltype(T)::value;
     if constexpr (t + DEPTH < TPW && t + DEPTH >= PRE)  // (DEPTH 0: tile t, just before its use)
-      mf_load_tile<FMT, KB>(m, tile_of(t + DEPTH), b0, nb, n16, g, buf[(t + DEPTH) % NB]);
+      mf_load_tile<FMT, KB>(m, tile_of(t + DEPTH), rb0, nb, n16, g, buf[(t + DEPTH) % NB]);
     mf_tile<FMT, KB>(buf[t % NB], nb, lds, L, wred + t * wstride, n16, g, t < nt);
   });
   __syncthreads();
 
-  // 4. the rows: the waves' partial sums in wave order
+  // 4. the rows: the waves' partial sums in wave order (and, with k slices, the slices' sums in
+  // slice order)
   const int rows = nt * 16;
+  auto wave_sum = [&](int i) {
+    const float *r = red + (i >> 4) * wstride + (i & 15);
+    float v = 0.f;
+    for (int w = 0; w < nw; ++w) v += r[w * 16];
+    return v;
+  };
+  const float *total = nullptr;  // with slices: the row's slice sums, ksplit apart
+  if (ksplit > 1) {
+    float *mine = partial + ((int64_t)gi * ksplit + slice) * TPW * 16;
+    for (int i = threadIdx.x; i < rows; i += blockDim.x)
+      __hip_atomic_store(mine + i, wave_sum(i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores have completed
+    __syncthreads();
+    if (threadIdx.x == 0) is_last = arrive_last(arr, gi, (unsigned)ksplit);
+    __syncthreads();
+    if (!is_last) return;
+    total = partial + (int64_t)gi * ksplit * TPW * 16;
+  }
+  auto row_sum = [&](int i) {
+    if (!total) return wave_sum(i);
+    float v = 0.f;
+    for (int q = 0; q < ksplit; ++q)
+      v += __hip_atomic_load(total + q * TPW * 16 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return v;
+  };
   if (m.swiglu) {  // virtual rows (gate r, up r) pairs; tiles start at even rows
     for (int i = 2 * (int)threadIdx.x; i < rows; i += 2 * (int)blockDim.x) {
       const int v = tile_of(i >> 4) * 16 + (i & 15);
       if (v >= m.total) continue;
-      const float *r = red + (i >> 4) * wstride + (i & 15);
-      float gs = 0.f, us = 0.f;
-      for (int w = 0; w < nw; ++w) {
-        gs += r[w * 16];
-        us += r[w * 16 + 1];
-      }
-      gstore(m.swiglu_out(v >> 1), silu_mul(gs, us));
+      gstore(m.swiglu_out(v >> 1), silu_mul(row_sum(i), row_sum(i + 1)));
     }
   } else {
     for (int i = threadIdx.x; i < rows; i += blockDim.x) {
       const int v = tile_of(i >> 4) * 16 + (i & 15);
       if (v >= m.total) continue;
-      const float *r = red + (i >> 4) * wstride + (i & 15);
-      float s = 0.f;
-      for (int w = 0; w < nw; ++w) s += r[w * 16];
-      m.put(v, s);
+      m.put(v, row_sum(i));
     }
   }
+  if (total && threadIdx.x == 0) done_arrivals(arr, gi);
 }
 
 // ---- host side ----------------------------------------------------------------------------------
@@ -483,63 +512,108 @@ static int mf_lds(int fmt, int nblk, int waves, int tiles) {
                          : mf_lds_bytes<FMT_Q4_K>(nblk, waves, tiles);
 }
 
-// Q4_K: k < 16384 whose operands fit 64 KB of LDS with one tile per workgroup (k <= 14336).
-// Q6_K: k a multiple of 512 up to 8192.
-bool mf_gemv_ok(int fmt, int64_t k) {
-  if (!knob(TQ_KNOB_GEMV_MF, 1) || k % 256 != 0 || k < 256 || k >= 16384) return false;
-  if (fmt != FMT_Q4_K && fmt != FMT_Q6_K) return false;
-  if (fmt == FMT_Q6_K && (k % 512 != 0 || k > 8192)) return false;
-  const int nblk = (int)(k / 256), kb = mf_kb(fmt, nblk);
-  return kb <= 4 && mf_lds(fmt, nblk, (nblk + kb - 1) / kb, 1) <= 65536;
-}
-
 // Tiles per workgroup that have a kernel (the next one up is taken).
 constexpr int kMfTpw[] = {1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16};
 
+// The launch of rows x k: blocks per slice sb and slices (a slice takes all of k when its operands
+// fit 64 KB of LDS: Q4_K up to k = 14336, Q6_K up to 8192; longer Q6_K rows, k a multiple of 512,
+// go in 2..8 equal slices of an even number of blocks, at most 32), blocks per wave, waves, tiles
+// per workgroup, grid.
+struct MfPlan {
+  int sb, ksplit, kb, waves, tpw, sets, lds;
+};
+static bool mf_plan(int fmt, int64_t rows, int64_t k, MfPlan &p) {
+  if (!knob(TQ_KNOB_GEMV_MF, 1) || k % 256 != 0 || k < 256 || rows < 1 || rows >= (1ll << 30))
+    return false;
+  if (fmt != FMT_Q4_K && fmt != FMT_Q6_K) return false;
+  const int nblk = (int)(k / 256);
+  p.ksplit = 1;
+  p.sb = nblk;
+  if (fmt == FMT_Q6_K) {
+    if (k % 512 != 0) return false;
+    if (nblk > 32) {
+      p.ksplit = 0;
+      for (int q = 2; q <= 8 && !p.ksplit; ++q)
+        if (nblk % q == 0 && (nblk / q) % 2 == 0 && nblk / q <= 32) p.ksplit = q;
+      if (!p.ksplit) return false;
+      p.sb = nblk / p.ksplit;
+    }
+  } else if (k >= 16384) {
+    return false;
+  }
+  p.kb = mf_kb(fmt, p.sb);
+  if (p.kb > 4) return false;
+  p.waves = (p.sb + p.kb - 1) / p.kb;
+  const int64_t ntiles = (rows + 15) / 16;
+  const int target = knob(TQ_KNOB_MF_WGS, 256);
+  const int64_t want = (ntiles * p.ksplit + target - 1) / (target > 0 ? target : 1);
+  int ti = 0;
+  while (ti < 11 && kMfTpw[ti] < want) ++ti;
+  while (ti > 0 && mf_lds(fmt, p.sb, p.waves, kMfTpw[ti]) > 65536) --ti;
+  p.tpw = kMfTpw[ti];
+  p.lds = mf_lds(fmt, p.sb, p.waves, p.tpw);
+  p.sets = (int)((ntiles + p.tpw - 1) / p.tpw);
+  return p.lds <= 65536;
+}
+
+bool mf_gemv_ok(int fmt, int64_t k) {
+  MfPlan p;
+  return mf_plan(fmt, 16, k, p) && p.ksplit == 1;
+}
+
+bool mf_gemv_sliced(int fmt, int64_t k) {
+  MfPlan p;
+  return mf_plan(fmt, 16, k, p) && p.ksplit > 1;
+}
+
+size_t mf_workspace_bytes(int fmt, int64_t rows, int64_t k) {
+  MfPlan p;
+  if (!mf_plan(fmt, rows, k, p) || p.ksplit == 1) return 0;
+  return (size_t)align256((int64_t)p.sets * p.ksplit * p.tpw * 16 * 4);
+}
+
 template <int FMT, int KB, int DEPTH, bool BIG>
-static void mf_launch_kb(int tpw, dim3 gd, dim3 bd, int lds, hipStream_t s, const KlMap &m,
-                         int nblk, const float *x) {
-  switch (tpw) {
-#define TQ_MF(T) \
-  case T: hipLaunchKernelGGL((k_gemv_mf<FMT, KB, T, DEPTH, BIG>), gd, bd, lds, s, m, nblk, x); break;
+static void mf_launch_kb(const MfPlan &p, hipStream_t s, const KlMap &m, const float *x,
+                         float *partial, Arrivals arr) {
+  const dim3 gd(p.sets * p.ksplit), bd(64 * p.waves);
+  switch (p.tpw) {
+#define TQ_MF(T)                                                                               \
+  case T:                                                                                      \
+    hipLaunchKernelGGL((k_gemv_mf<FMT, KB, T, DEPTH, BIG>), gd, bd, p.lds, s, m, p.sb, p.ksplit, \
+                       x, partial, arr);                                                       \
+    break;
     TQ_MF(1) TQ_MF(2) TQ_MF(3) TQ_MF(4) TQ_MF(5) TQ_MF(6) TQ_MF(7) TQ_MF(8) TQ_MF(10) TQ_MF(12)
     TQ_MF(14) TQ_MF(16)
 #undef TQ_MF
   }
 }
 
-int launch_gemv_mf(int fmt, const KlMap &m, int64_t k, const float *x, hipStream_t s) {
-  const int nblk = (int)(k / 256);
-  const int kb = mf_kb(fmt, nblk);
-  const int waves = (nblk + kb - 1) / kb;
-  const int ntiles = (m.total + 15) / 16;
-  const int target = knob(TQ_KNOB_MF_WGS, 256);
-  const int want = clampi((ntiles + target - 1) / (target > 0 ? target : 1), 1, 16);
-  int ti = 0;
-  while (kMfTpw[ti] < want) ++ti;
-  while (ti > 0 && mf_lds(fmt, nblk, waves, kMfTpw[ti]) > 65536) --ti;
-  const int tpw = kMfTpw[ti];
-  const int lds = mf_lds(fmt, nblk, waves, tpw);
-  if (lds > 65536) return -2;
-  const int grid = (ntiles + tpw - 1) / tpw;
-  const dim3 gd(grid), bd(64 * waves);
-  if (fmt == FMT_Q6_K) {  // at most 8 waves: one buffer at 4 blocks a wave, else two
-    if (kb == 2)
-      mf_launch_kb<FMT_Q6_K, 2, 1, true>(tpw, gd, bd, lds, s, m, nblk, x);
+int launch_gemv_mf(int fmt, const KlMap &m, int64_t k, const float *x, float *partial,
+                   unsigned long long *counters, int max_counters, hipStream_t s) {
+  MfPlan p;
+  if (!mf_plan(fmt, m.total, k, p)) return -2;
+  if (p.ksplit > 1 && (!partial || !counters || p.sets > max_counters)) return -2;
+  const Arrivals arr{counters, p.ksplit > 1 ? call_tag() : 0ull};
+  if (fmt == FMT_Q6_K) {  // at most 8 waves (256 VGPRs): two buffers (235 VGPRs at 4 blocks a wave)
+    if (p.kb == 2)
+      mf_launch_kb<FMT_Q6_K, 2, 1, true>(p, s, m, x, partial, arr);
+    else if (p.tpw >= 2 && knob(TQ_KNOB_MF_DEEP, 1))
+      mf_launch_kb<FMT_Q6_K, 4, 1, true>(p, s, m, x, partial, arr);
     else
-      mf_launch_kb<FMT_Q6_K, 4, 0, true>(tpw, gd, bd, lds, s, m, nblk, x);
+      mf_launch_kb<FMT_Q6_K, 4, 0, true>(p, s, m, x, partial, arr);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
   // two tiles ahead where the workgroup has several tiles and at most 8 waves (256 VGPRs a lane)
-  const bool deep = kb == 2 && waves <= 8 && tpw >= 3 && knob(TQ_KNOB_MF_DEEP, 1);
-  if (kb == 1)
-    mf_launch_kb<FMT_Q4_K, 1, 1, false>(tpw, gd, bd, lds, s, m, nblk, x);
-  else if (kb == 2 && deep)
-    mf_launch_kb<FMT_Q4_K, 2, 2, true>(tpw, gd, bd, lds, s, m, nblk, x);
-  else if (kb == 2)
-    mf_launch_kb<FMT_Q4_K, 2, 1, false>(tpw, gd, bd, lds, s, m, nblk, x);
+  // (three or four tiles ahead measured slower)
+  const bool deep = p.kb == 2 && p.waves <= 8 && p.tpw >= 3 && knob(TQ_KNOB_MF_DEEP, 1);
+  if (p.kb == 1)
+    mf_launch_kb<FMT_Q4_K, 1, 1, false>(p, s, m, x, partial, arr);
+  else if (p.kb == 2 && deep)
+    mf_launch_kb<FMT_Q4_K, 2, 2, true>(p, s, m, x, partial, arr);
+  else if (p.kb == 2)
+    mf_launch_kb<FMT_Q4_K, 2, 1, false>(p, s, m, x, partial, arr);
   else
-    mf_launch_kb<FMT_Q4_K, 4, 0, false>(tpw, gd, bd, lds, s, m, nblk, x);  // one buffer (128 VGPRs)
+    mf_launch_kb<FMT_Q4_K, 4, 0, false>(p, s, m, x, partial, arr);  // one buffer (128 VGPRs)
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

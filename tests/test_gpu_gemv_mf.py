@@ -230,3 +230,32 @@ def test_mf_q6_k_extremes():
     y = host(tq.gemv("q6_k", dev(w), n, k, dev(x)))
     ref, mag = oracle.gemv("q6_k", w, n, k, x)
     assert_product_close(y, ref, mag, what="mf q6_k extremes")
+
+
+# Longer Q6_K rows in k slices (equal slices of an even number of blocks, at most 32): k = 9216
+# (2 x 18), 11264 (2 x 22), 16384 (2 x 32), 28672 (4 x 28, the 70B-shaped down projection).
+SLICED6 = [(37, 9216), (300, 11264), (17, 16384), (1000, 28672)]
+
+
+@pytest.mark.parametrize("n,k", SLICED6)
+def test_mf_q6_k_k_slices(knobs, n, k):
+    """The slices' sums meet through the workspace (arrival counters, the last slice adds them in
+    slice order): within the bar, deterministic, and the same with a workspace full of random
+    bytes; without a workspace the lane-per-row kernel runs instead."""
+    _case("mf q6_k slices", n, k)
+    g = synth.rng(144, "mf6-slices", n, k)
+    w, x = synth.blob("q6_k", g, n, k), synth.normal_f32(g, (1, k))
+    wd, xd = dev(w), dev(x)
+    nbytes = tq.gemv_workspace_bytes("q6_k", n, k, 1)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda:0")
+    y = host(tq.gemv("q6_k", wd, n, k, xd, ws=ws))
+    ref, mag = oracle.gemv("q6_k", w, n, k, x)
+    worst = assert_product_close(y, ref, mag, what=f"mf q6_k slices {n}x{k}")
+    assert worst < 0.05, worst
+    ws.copy_(torch.from_numpy(g.integers(0, 256, nbytes, dtype=np.uint8)).to(ws.device))
+    assert np.array_equal(y, host(tq.gemv("q6_k", wd, n, k, xd, ws=ws)))
+    y0 = host(tq.gemv("q6_k", wd, n, k, xd, ws=False))
+    assert_product_close(y0, ref, mag, what=f"no workspace {n}x{k}")
+    knobs("gemv_mf", 0)
+    y1 = host(tq.gemv("q6_k", wd, n, k, xd, ws=ws))
+    assert np.linalg.norm(y - y1) <= 2e-5 * np.linalg.norm(y1) + 1e-30

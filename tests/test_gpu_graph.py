@@ -110,6 +110,7 @@ K_SPLIT = [("q4_k", 600, 16384, 1),   # int8 matrix cores, k slices
            ("q8_0", 500, 8192, 4),    # fp32 matrix cores, k slices
            ("q8_0", 700, 8192, 1),    # int8 matrix cores (Q8_0), k slices
            ("q6_k", 400, 8192, 1),    # fp16 matrix cores (Q6_K)
+           ("q6_k", 300, 16384, 1),   # fp16 matrix cores (Q6_K), two k slices
            ("q6_k", 200, 4096, 3)]    # lane-per-row GEMV, 3 tokens, k split
 
 
