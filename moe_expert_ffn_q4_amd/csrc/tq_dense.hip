@@ -183,9 +183,11 @@ static bool use_i8(int fmt, int64_t rows, int64_t k, const float *x, int64_t bat
 static bool mf6_ok(int fmt, int64_t k, const float *x, int64_t batch) {
   return fmt == FMT_Q6_K && batch == 1 && ((uintptr_t)x & 15) == 0 && mf_gemv_ok(FMT_Q6_K, k);
 }
+// (Q4_K rows of 16384 and more: the int8 kernel unless TQ_KNOB_GEMV_MF is 2)
 static size_t mf6s_ws_bytes(int fmt, int64_t rows, int64_t k, int64_t batch) {
-  if (fmt != FMT_Q6_K || batch != 1 || !mf_gemv_sliced(FMT_Q6_K, k)) return 0;
-  return kCounterBytes + mf_workspace_bytes(FMT_Q6_K, rows, k);
+  const bool q4 = fmt == FMT_Q4_K && knob(TQ_KNOB_GEMV_MF, 1) == 2;
+  if ((fmt != FMT_Q6_K && !q4) || batch != 1 || !mf_gemv_sliced(fmt, k)) return 0;
+  return kCounterBytes + mf_workspace_bytes(fmt, rows, k);
 }
 static bool use_mf6s(int fmt, int64_t rows, int64_t k, const float *x, int64_t batch,
                      const void *ws, size_t ws_bytes) {
@@ -719,9 +721,9 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, in
     m.row_bytes = rb;
     return launch_f32m(fmt, m, k, x, batch, ws, s);
   }
-  const bool i8 = use_i8(fmt, n, k, x, batch, ws, ws_bytes);
+  const bool mf6s = use_mf6s(fmt, n, k, x, batch, ws, ws_bytes) && n < (1ll << 30);
+  const bool i8 = !mf6s && use_i8(fmt, n, k, x, batch, ws, ws_bytes);
   const bool mf6 = mf6_ok(fmt, k, x, batch) && n < (1ll << 30);
-  const bool mf6s = !mf6 && use_mf6s(fmt, n, k, x, batch, ws, ws_bytes) && n < (1ll << 30);
   if (i8 || klane_ok(fmt, k, x, batch) || mf6 || mf6s) {
     KlMap m{};
     m.w[0] = wb;
@@ -733,7 +735,7 @@ int launch_gemv(int fmt, const void *w, int64_t n, int64_t k, const float *x, in
     if (i8) return launch_i8(fmt, m, k, x, ws, s);
     if (mf6) return launch_gemv_mf(FMT_Q6_K, m, k, x, nullptr, nullptr, 0, s);
     if (mf6s)
-      return launch_gemv_mf(FMT_Q6_K, m, k, x, (float *)((char *)ws + kCounterBytes),
+      return launch_gemv_mf(fmt, m, k, x, (float *)((char *)ws + kCounterBytes),
                             (unsigned long long *)ws, (int)(kCounterBytes / 8), s);
     return launch_kl(m, k, x, s);
   }

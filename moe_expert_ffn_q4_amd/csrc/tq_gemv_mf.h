@@ -10,8 +10,9 @@ namespace tq {
 
 // Format and row length k that the kernel takes in one slice (the activation operands of all of
 // k sit in one workgroup's LDS: Q4_K k a multiple of 256 up to 14336, Q6_K a multiple of 512 up to
-// 8192), and longer Q6_K rows that it takes in k slices (k a multiple of 512 cut into 2..8 equal
-// slices of at most 8192, whose sums meet through the workspace). Both honour the knob.
+// 8192), and longer rows that it takes in k slices (cut into 2..8 equal slices of at most 8192,
+// Q6_K slices of an even number of blocks, whose sums meet through the workspace). Both honour
+// the knob.
 bool mf_gemv_ok(int fmt, int64_t k);
 bool mf_gemv_sliced(int fmt, int64_t k);
 // Workspace bytes (after the counters) of a sliced launch of `rows` rows; 0 when not sliced.

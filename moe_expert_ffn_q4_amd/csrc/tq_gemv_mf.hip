@@ -529,17 +529,15 @@ static bool mf_plan(int fmt, int64_t rows, int64_t k, MfPlan &p) {
   const int nblk = (int)(k / 256);
   p.ksplit = 1;
   p.sb = nblk;
-  if (fmt == FMT_Q6_K) {
-    if (k % 512 != 0) return false;
-    if (nblk > 32) {
-      p.ksplit = 0;
-      for (int q = 2; q <= 8 && !p.ksplit; ++q)
-        if (nblk % q == 0 && (nblk / q) % 2 == 0 && nblk / q <= 32) p.ksplit = q;
-      if (!p.ksplit) return false;
-      p.sb = nblk / p.ksplit;
-    }
-  } else if (k >= 16384) {
-    return false;
+  // longest slice: Q6_K 32 blocks (an even number), Q4_K all of k below 16384, else 32
+  const bool q6 = fmt == FMT_Q6_K;
+  if (q6 && k % 512 != 0) return false;
+  if ((q6 && nblk > 32) || (!q6 && nblk >= 64)) {
+    p.ksplit = 0;
+    for (int q = 2; q <= 8 && !p.ksplit; ++q)
+      if (nblk % q == 0 && (!q6 || (nblk / q) % 2 == 0) && nblk / q <= 32) p.ksplit = q;
+    if (!p.ksplit) return false;
+    p.sb = nblk / p.ksplit;
   }
   p.kb = mf_kb(fmt, p.sb);
   if (p.kb > 4) return false;

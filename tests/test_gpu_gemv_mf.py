@@ -259,3 +259,23 @@ def test_mf_q6_k_k_slices(knobs, n, k):
     knobs("gemv_mf", 0)
     y1 = host(tq.gemv("q6_k", wd, n, k, xd, ws=ws))
     assert np.linalg.norm(y - y1) <= 2e-5 * np.linalg.norm(y1) + 1e-30
+
+
+@pytest.mark.parametrize("n,k", [(300, 16384), (1000, 28672)])
+def test_mf_q4_k_k_slices(knobs, n, k):
+    """Q4_K rows from k = 16384 in k slices (TQ_KNOB_GEMV_MF = 2; the default there is the int8
+    kernel): within the bar and within 2e-5 of the int8 kernel."""
+    _case("mf q4_k slices", n, k)
+    g = synth.rng(145, "mf4-slices", n, k)
+    w, x = synth.blob("q4_k", g, n, k), synth.normal_f32(g, (1, k))
+    wd, xd = dev(w), dev(x)
+    knobs("gemv_mf", 2)
+    ws = torch.zeros(tq.gemv_workspace_bytes("q4_k", n, k, 1), dtype=torch.uint8, device="cuda:0")
+    y = host(tq.gemv("q4_k", wd, n, k, xd, ws=ws))
+    ref, mag = oracle.gemv("q4_k", w, n, k, x)
+    worst = assert_product_close(y, ref, mag, what=f"mf q4_k slices {n}x{k}")
+    assert worst < 0.05, worst
+    knobs("gemv_mf", 1)
+    ws2 = torch.zeros(tq.gemv_workspace_bytes("q4_k", n, k, 1), dtype=torch.uint8, device="cuda:0")
+    y8 = host(tq.gemv("q4_k", wd, n, k, xd, ws=ws2))
+    assert np.linalg.norm(y - y8) <= 2e-5 * np.linalg.norm(y8) + 1e-30
