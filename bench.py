@@ -570,6 +570,9 @@ def moe_bench(args, torch, tq, synth):
         if T > 1 and tq.get_knob("moe_qmm") != 0:
             kern = ("tq_moe_ffn expert stage: k_qmm gate/up+SwiGLU and down on the fp16 matrix "
                     "cores, fp32-accurate (with the row splits and the chunk table)")
+        elif T == 1 and tq.get_knob("moe_mf") != 0:
+            kern = ("tq_moe_ffn expert stage: k_moe_mf gate/up+SwiGLU and down on the fp16 matrix "
+                    "cores (combine in the down launch)")
         elif T == 1:
             kern = "tq_moe_ffn expert stage: k_moe_kl gate/up+SwiGLU and down"
         else:

@@ -444,6 +444,7 @@ KNOBS = {
     "mf_wgs": 25,
     "mf_kb": 26,
     "mf_deep": 27,
+    "moe_mf": 28,
 }
 
 

@@ -448,41 +448,6 @@ __global__ __launch_bounds__(512) void k_gemv_kl(KlMap m, int nblk, int rows_per
   kl_body<R, G, KlMap>(m, nblk, rb, re, x, red);
 }
 
-// Rows of one expert's matrices for the one-token MoE kernel: two pointers and no arrays (a
-// general row map built inside a kernel and indexed at run time is kept in scratch memory).
-// A pointer that is the same in every lane, moved to scalar registers.
-__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
-  const uint64_t u = (uint64_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u),
-                 hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-  return (const uint8_t *)(((uint64_t)hi << 32) | lo);
-}
-
-struct MoeRowMap {
-  const uint8_t *w0, *w1;  // gate, up (gate_up) or down, unused
-  float *y;
-  int swiglu, total;
-  int64_t row_bytes;
-  int coherent;  // sums stored at device scope (read back in the same launch)
-  // The gate / up pick is a select between two scalar registers (opaque to the compiler): left
-  // to itself it makes a two-entry table of the pointers per lane in LDS and reads it back before
-  // every pass's loads.
-  __device__ __forceinline__ const uint8_t *row(int v) const {
-    const uint8_t *p0 = uniform_ptr(w0), *p1 = uniform_ptr(w1);
-    asm("" : "+s"(p0), "+s"(p1));
-    return swiglu ? ((v & 1) ? p1 : p0) + (int64_t)(v >> 1) * row_bytes
-                  : p0 + (int64_t)v * row_bytes;
-  }
-  __device__ __forceinline__ float *swiglu_out(int j) const { return y + j; }
-  __device__ __forceinline__ float *out(int v) const { return y + v; }
-  __device__ __forceinline__ void put(int v, float s) const {
-    if (coherent)
-      __hip_atomic_store(y + v, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else
-      gstore(y + v, s);
-  }
-};
-
 // The combine of a one-token layer inside the down launch: each workgroup counts itself on its
 // row range's counter once its sums are stored (device-scope stores, awaited before counting);
 // the last of the active slots to arrive adds, for each of the range's rows, the slots in order
@@ -497,18 +462,7 @@ __device__ __forceinline__ void moe_kl_combine(const MoeKlArgs &a, int rb, int r
            (unsigned)(*a.n_active - 1);
   __syncthreads();
   if (!last) return;
-  for (int c = rb + (int)threadIdx.x; c < re; c += blockDim.x) {
-    float acc = 0.f;
-    for (int j = 0; j < a.topk; ++j) {
-      const float v = __hip_atomic_load(a.out + (int64_t)a.inv[j] * a.ldo + c, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
-      acc = __builtin_fmaf(a.wts[j], 0.f + v, acc);
-    }
-    if (a.has_shared)
-      acc += 0.f + __hip_atomic_load(a.out + (int64_t)a.Tk * a.ldo + c, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-    a.fuse_y[c] = acc;
-  }
+  for (int c = rb + (int)threadIdx.x; c < re; c += blockDim.x) a.fuse_y[c] = moe_combine_value(a, c);
 }
 
 // The same kernel over the experts of a one-token MoE step: workgroup b works on active slot

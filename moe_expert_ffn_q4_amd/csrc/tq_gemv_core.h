@@ -715,6 +715,41 @@ struct KlMap {
   }
 };
 
+// A pointer that is the same in every lane, moved to scalar registers.
+__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
+  const uint64_t u = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u),
+                 hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const uint8_t *)(((uint64_t)hi << 32) | lo);
+}
+
+// Rows of one expert's matrices for the one-token MoE kernel: two pointers and no arrays (a
+// general row map built inside a kernel and indexed at run time is kept in scratch memory).
+struct MoeRowMap {
+  const uint8_t *w0, *w1;  // gate, up (gate_up) or down, unused
+  float *y;
+  int swiglu, total;
+  int64_t row_bytes;
+  int coherent;  // sums stored at device scope (read back in the same launch)
+  // The gate / up pick is a select between two scalar registers (opaque to the compiler): left
+  // to itself it makes a two-entry table of the pointers per lane in LDS and reads it back before
+  // every pass's loads.
+  __device__ __forceinline__ const uint8_t *row(int v) const {
+    const uint8_t *p0 = uniform_ptr(w0), *p1 = uniform_ptr(w1);
+    asm("" : "+s"(p0), "+s"(p1));
+    return swiglu ? ((v & 1) ? p1 : p0) + (int64_t)(v >> 1) * row_bytes
+                  : p0 + (int64_t)v * row_bytes;
+  }
+  __device__ __forceinline__ float *swiglu_out(int j) const { return y + j; }
+  __device__ __forceinline__ float *out(int v) const { return y + v; }
+  __device__ __forceinline__ void put(int v, float s) const {
+    if (coherent)
+      __hip_atomic_store(y + v, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      gstore(y + v, s);
+  }
+};
+
 template <int R, class Map>
 __device__ __forceinline__ void kl_load_rows(const Map &m, int r0, int boff, int c,
                                              u32x4 (&v)[R][3]) {

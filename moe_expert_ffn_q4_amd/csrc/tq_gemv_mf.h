@@ -23,4 +23,11 @@ size_t mf_workspace_bytes(int fmt, int64_t rows, int64_t k);
 int launch_gemv_mf(int fmt, const KlMap &m, int64_t k, const float *x, float *partial,
                    unsigned long long *counters, int max_counters, hipStream_t s);
 
+struct MoeKlArgs;
+// One-token MoE step on the same kernel (Q4_K, hidden and ffn each taken in one slice; honours
+// the knob), and the launch over nslots active slots (gate/up or down as MoeKlArgs says; with the
+// combine fused, a.ctr holds at least a.ctr_cap >= one counter per tile set). 0, -1 or -2 (shape).
+bool moe_mf_ok(int fmt, int64_t hidden, int64_t ffn);
+int launch_moe_mf(const MoeKlArgs &a, int64_t k, int nslots, hipStream_t s);
+
 }  // namespace tq

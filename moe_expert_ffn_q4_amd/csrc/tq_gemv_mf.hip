@@ -51,6 +51,7 @@
 #include "tq_gemv_core.h"
 #include "tq_gemv_mf.h"
 #include "tq_launch.h"
+#include "tq_moe.h"
 
 namespace tq {
 
@@ -349,8 +350,8 @@ __device__ __forceinline__ void mf_split(const MfCells<MC> &cv, int nblk, uint8_
 // 2. the lane's loads of its tile row. Every block slot is loaded (past the wave's last block: a
 // block again), so that no load sits behind a branch: the compiler then counts the loads in
 // flight and waits for each block's own.
-template <int FMT, int KB>
-__device__ __forceinline__ void mf_load_tile(const KlMap &m, int tile, int b0, int nb, int n16,
+template <int FMT, int KB, class Map>
+__device__ __forceinline__ void mf_load_tile(const Map &m, int tile, int b0, int nb, int n16,
                                              int g, typename MfFmt<FMT>::Blk (&buf)[KB]) {
   using F = MfFmt<FMT>;
   const uint8_t *rp = m.row(min(tile * 16 + n16, m.total - 1)) + (int64_t)b0 * F::kBytes;  // b0: block in the row
@@ -403,17 +404,19 @@ __device__ __forceinline__ void mf_tile(const typename MfFmt<FMT>::Blk (&buf)[KB
 // the tiles of set gi over blocks [s sb, s sb + sb) only (sb blocks in every slice), stores its
 // rows' sums device-coherently to `partial` and counts itself on set gi's arrival word; the last
 // slice to arrive adds the ksplit sums in slice order and stores the rows.
-template <int FMT, int KB, int TPW, int DEPTH, bool BIG>
-__global__ __launch_bounds__(BIG ? 512 : 1024) void k_gemv_mf(KlMap m, int sb, int ksplit,
-                                                              const float *__restrict__ xall,
-                                                              float *partial, Arrivals arr) {
+//
+// The body of one workgroup: tile set gi of G, k slice `slice` of ksplit, over rows of any row map
+// (a matrix, or one expert's matrices). Returns false where a slice that was not the last to
+// arrive has left its sums to another workgroup.
+template <int FMT, int KB, int TPW, int DEPTH, class Map>
+__device__ __forceinline__ bool mf_body(const Map &m, int gi, int G, int sb, int ksplit, int slice,
+                                        const float *__restrict__ xall, float *partial,
+                                        const Arrivals &arr, uint8_t *lds) {
   using F = MfFmt<FMT>;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int is_last;
   const int lane = threadIdx.x & 63, wave = wave_index(), nw = blockDim.x >> 6;
   const int n16 = lane & 15, g = lane >> 4;
-  const int slice = (int)blockIdx.x % ksplit, gi = (int)blockIdx.x / ksplit;
-  const int ntiles = (m.total + 15) >> 4, G = (int)gridDim.x / ksplit;
+  const int ntiles = (m.total + 15) >> 4;
   const int nt = min(TPW, (ntiles - gi + G - 1) / G);  // >= 1
   const int nblk = sb;                                  // blocks of this slice
   const float *x = xall + (int64_t)slice * sb * 256;
@@ -465,7 +468,7 @@ __global__ __launch_bounds__(BIG ? 512 : 1024) void k_gemv_mf(KlMap m, int sb, i
     __syncthreads();
     if (threadIdx.x == 0) is_last = arrive_last(arr, gi, (unsigned)ksplit);
     __syncthreads();
-    if (!is_last) return;
+    if (!is_last) return false;
     total = partial + (int64_t)gi * ksplit * TPW * 16;
   }
   auto row_sum = [&](int i) {
@@ -489,6 +492,67 @@ __global__ __launch_bounds__(BIG ? 512 : 1024) void k_gemv_mf(KlMap m, int sb, i
     }
   }
   if (total && threadIdx.x == 0) done_arrivals(arr, gi);
+  return true;
+}
+
+template <int FMT, int KB, int TPW, int DEPTH, bool BIG>
+__global__ __launch_bounds__(BIG ? 512 : 1024) void k_gemv_mf(KlMap m, int sb, int ksplit,
+                                                              const float *__restrict__ xall,
+                                                              float *partial, Arrivals arr) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int slice = (int)blockIdx.x % ksplit, gi = (int)blockIdx.x / ksplit;
+  mf_body<FMT, KB, TPW, DEPTH>(m, gi, (int)gridDim.x / ksplit, sb, ksplit, slice, xall, partial,
+                               arr, lds);
+}
+
+// The same body over the experts of a one-token MoE step: workgroup b takes tile set b % sets of
+// active slot slot0 + b / sets (every active expert has that one token); gate/up: the expert's gate
+// and up rows interleaved with the SwiGLU in the epilogue, x = the token's activations, h out;
+// down: x = h of the slot's position, o out. With the combine fused into the down launch, each
+// workgroup then counts itself on its tile set's counter, and the last active slot to arrive adds,
+// for each row of the set, the slots in routing order and the shared expert (the combine kernel's
+// order). The gate/up launch's first workgroup clears the counters.
+template <int FMT, int KB, int TPW, int DEPTH, bool BIG>
+__global__ __launch_bounds__(BIG ? 512 : 1024) void k_moe_mf(MoeKlArgs a, int sets) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ int last;
+  if (a.nctr > 0 && blockIdx.x == 0)
+    for (int i = (int)threadIdx.x; i < a.nctr; i += blockDim.x)
+      __hip_atomic_store(a.ctr + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int slot = a.slot0 + (int)blockIdx.x / sets, gi = (int)blockIdx.x % sets;
+  if (slot >= *a.n_active) return;
+  const int e = a.act[slot], p = a.act[a.act_stride + slot];
+  if ((unsigned)e > (unsigned)a.E) return;  // never past the expert table (id E: shared expert)
+  const uint8_t *w[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int mat = a.gate_up ? q : 2;
+    if (e == a.E)
+      w[q] = (const uint8_t *)a.shared.m[mat];
+    else if (a.staging != nullptr)
+      w[q] = a.staging + (int64_t)slot * a.stage_stride + a.stage_off[mat];
+    else
+      w[q] = (const uint8_t *)a.experts[e].m[mat];
+  }
+  const MoeRowMap m{w[0], w[1], a.out + (int64_t)p * a.ldo, a.gate_up, a.rows, a.row_bytes,
+                    a.fuse_y != nullptr};
+  int64_t xrow = p;
+  if (a.gate_up) xrow = p >= a.Tk ? p - a.Tk : a.pairs[p] / a.topk;
+  mf_body<FMT, KB, TPW, DEPTH>(m, gi, sets, (int)(a.row_bytes / MfFmt<FMT>::kBytes), 1, 0,
+                               a.x + xrow * a.ldx, nullptr, Arrivals{}, lds);
+  if (a.fuse_y == nullptr) return;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's sums are stored
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(&a.ctr[gi], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           (unsigned)(*a.n_active - 1);
+  __syncthreads();
+  if (!last) return;
+  const int ntiles = (a.rows + 15) >> 4, nt = min(TPW, (ntiles - gi + sets - 1) / sets);
+  for (int i = (int)threadIdx.x; i < nt * 16; i += blockDim.x) {
+    const int c = (gi + (i >> 4) * sets) * 16 + (i & 15);
+    if (c < a.rows) a.fuse_y[c] = moe_combine_value(a, c);
+  }
 }
 
 // ---- host side ----------------------------------------------------------------------------------
@@ -522,7 +586,7 @@ constexpr int kMfTpw[] = {1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16};
 struct MfPlan {
   int sb, ksplit, kb, waves, tpw, sets, lds;
 };
-static bool mf_plan(int fmt, int64_t rows, int64_t k, MfPlan &p) {
+static bool mf_plan(int fmt, int64_t rows, int64_t k, MfPlan &p, int slots = 1) {
   if (!knob(TQ_KNOB_GEMV_MF, 1) || k % 256 != 0 || k < 256 || rows < 1 || rows >= (1ll << 30))
     return false;
   if (fmt != FMT_Q4_K && fmt != FMT_Q6_K) return false;
@@ -544,7 +608,7 @@ static bool mf_plan(int fmt, int64_t rows, int64_t k, MfPlan &p) {
   p.waves = (p.sb + p.kb - 1) / p.kb;
   const int64_t ntiles = (rows + 15) / 16;
   const int target = knob(TQ_KNOB_MF_WGS, 256);
-  const int64_t want = (ntiles * p.ksplit + target - 1) / (target > 0 ? target : 1);
+  const int64_t want = (ntiles * p.ksplit * slots + target - 1) / (target > 0 ? target : 1);
   int ti = 0;
   while (ti < 11 && kMfTpw[ti] < want) ++ti;
   while (ti > 0 && mf_lds(fmt, p.sb, p.waves, kMfTpw[ti]) > 65536) --ti;
@@ -570,20 +634,43 @@ size_t mf_workspace_bytes(int fmt, int64_t rows, int64_t k) {
   return (size_t)align256((int64_t)p.sets * p.ksplit * p.tpw * 16 * 4);
 }
 
-template <int FMT, int KB, int DEPTH, bool BIG>
-static void mf_launch_kb(const MfPlan &p, hipStream_t s, const KlMap &m, const float *x,
-                         float *partial, Arrivals arr) {
-  const dim3 gd(p.sets * p.ksplit), bd(64 * p.waves);
-  switch (p.tpw) {
-#define TQ_MF(T)                                                                               \
-  case T:                                                                                      \
-    hipLaunchKernelGGL((k_gemv_mf<FMT, KB, T, DEPTH, BIG>), gd, bd, p.lds, s, m, p.sb, p.ksplit, \
-                       x, partial, arr);                                                       \
+template <int V>
+using mf_c = std::integral_constant<int, V>;
+
+// Calls launch(FMT, KB, DEPTH, BIG, TPW) with plan p's kernel variant as compile-time constants.
+template <class L>
+static void mf_variant(int fmt, const MfPlan &p, L &&launch) {
+  auto by_tpw = [&](auto fmt_c, auto kb_c, auto depth_c, auto big_c) {
+    switch (p.tpw) {
+#define TQ_MF(T)                                \
+  case T:                                       \
+    launch(fmt_c, kb_c, depth_c, big_c, mf_c<T>{}); \
     break;
-    TQ_MF(1) TQ_MF(2) TQ_MF(3) TQ_MF(4) TQ_MF(5) TQ_MF(6) TQ_MF(7) TQ_MF(8) TQ_MF(10) TQ_MF(12)
-    TQ_MF(14) TQ_MF(16)
+      TQ_MF(1) TQ_MF(2) TQ_MF(3) TQ_MF(4) TQ_MF(5) TQ_MF(6) TQ_MF(7) TQ_MF(8) TQ_MF(10) TQ_MF(12)
+      TQ_MF(14) TQ_MF(16)
 #undef TQ_MF
+    }
+  };
+  if (fmt == FMT_Q6_K) {  // at most 8 waves (256 VGPRs): two buffers (235 VGPRs at 4 blocks a wave)
+    if (p.kb == 2)
+      by_tpw(mf_c<FMT_Q6_K>{}, mf_c<2>{}, mf_c<1>{}, mf_c<1>{});
+    else if (p.tpw >= 2 && knob(TQ_KNOB_MF_DEEP, 1))
+      by_tpw(mf_c<FMT_Q6_K>{}, mf_c<4>{}, mf_c<1>{}, mf_c<1>{});
+    else
+      by_tpw(mf_c<FMT_Q6_K>{}, mf_c<4>{}, mf_c<0>{}, mf_c<1>{});
+    return;
   }
+  // two tiles ahead where the workgroup has several tiles and at most 8 waves (256 VGPRs a lane)
+  // (three or four tiles ahead measured slower)
+  const bool deep = p.kb == 2 && p.waves <= 8 && p.tpw >= 3 && knob(TQ_KNOB_MF_DEEP, 1);
+  if (p.kb == 1)
+    by_tpw(mf_c<FMT_Q4_K>{}, mf_c<1>{}, mf_c<1>{}, mf_c<0>{});
+  else if (p.kb == 2 && deep)
+    by_tpw(mf_c<FMT_Q4_K>{}, mf_c<2>{}, mf_c<2>{}, mf_c<1>{});
+  else if (p.kb == 2)
+    by_tpw(mf_c<FMT_Q4_K>{}, mf_c<2>{}, mf_c<1>{}, mf_c<0>{});
+  else
+    by_tpw(mf_c<FMT_Q4_K>{}, mf_c<4>{}, mf_c<0>{}, mf_c<0>{});  // one buffer (128 VGPRs)
 }
 
 int launch_gemv_mf(int fmt, const KlMap &m, int64_t k, const float *x, float *partial,
@@ -592,26 +679,32 @@ int launch_gemv_mf(int fmt, const KlMap &m, int64_t k, const float *x, float *pa
   if (!mf_plan(fmt, m.total, k, p)) return -2;
   if (p.ksplit > 1 && (!partial || !counters || p.sets > max_counters)) return -2;
   const Arrivals arr{counters, p.ksplit > 1 ? call_tag() : 0ull};
-  if (fmt == FMT_Q6_K) {  // at most 8 waves (256 VGPRs): two buffers (235 VGPRs at 4 blocks a wave)
-    if (p.kb == 2)
-      mf_launch_kb<FMT_Q6_K, 2, 1, true>(p, s, m, x, partial, arr);
-    else if (p.tpw >= 2 && knob(TQ_KNOB_MF_DEEP, 1))
-      mf_launch_kb<FMT_Q6_K, 4, 1, true>(p, s, m, x, partial, arr);
-    else
-      mf_launch_kb<FMT_Q6_K, 4, 0, true>(p, s, m, x, partial, arr);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
-  }
-  // two tiles ahead where the workgroup has several tiles and at most 8 waves (256 VGPRs a lane)
-  // (three or four tiles ahead measured slower)
-  const bool deep = p.kb == 2 && p.waves <= 8 && p.tpw >= 3 && knob(TQ_KNOB_MF_DEEP, 1);
-  if (p.kb == 1)
-    mf_launch_kb<FMT_Q4_K, 1, 1, false>(p, s, m, x, partial, arr);
-  else if (p.kb == 2 && deep)
-    mf_launch_kb<FMT_Q4_K, 2, 2, true>(p, s, m, x, partial, arr);
-  else if (p.kb == 2)
-    mf_launch_kb<FMT_Q4_K, 2, 1, false>(p, s, m, x, partial, arr);
-  else
-    mf_launch_kb<FMT_Q4_K, 4, 0, false>(p, s, m, x, partial, arr);  // one buffer (128 VGPRs)
+  const dim3 gd(p.sets * p.ksplit), bd(64 * p.waves);
+  mf_variant(fmt, p, [&](auto F, auto KB, auto D, auto BIG, auto T) {
+    hipLaunchKernelGGL((k_gemv_mf<F(), KB(), T(), D(), (bool)BIG()>), gd, bd, p.lds, s, m, p.sb,
+                       p.ksplit, x, partial, arr);
+  });
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+bool moe_mf_ok(int fmt, int64_t hidden, int64_t ffn) {
+  MfPlan p;
+  return fmt == FMT_Q4_K && knob(TQ_KNOB_MOE_MF, 1) && mf_plan(fmt, 16, hidden, p) &&
+         p.ksplit == 1 && mf_plan(fmt, 16, ffn, p) && p.ksplit == 1;
+}
+
+int launch_moe_mf(const MoeKlArgs &a, int64_t k, int nslots, hipStream_t s) {
+  MfPlan p;
+  if (!moe_mf_ok(FMT_Q4_K, k, k) || nslots < 1 || a.row_bytes != k / 256 * 144 ||
+      ((uintptr_t)a.x & 15) != 0 || a.ldx % 4 != 0 || !mf_plan(FMT_Q4_K, a.rows, k, p, nslots))
+    return -2;
+  // the fused combine counts on one counter per tile set
+  if (a.fuse_y != nullptr && (a.ctr == nullptr || p.sets > a.ctr_cap)) return -2;
+  const dim3 gd((unsigned)(nslots * p.sets)), bd(64 * p.waves);
+  mf_variant(FMT_Q4_K, p, [&](auto F, auto KB, auto D, auto BIG, auto T) {
+    if constexpr (F() == FMT_Q4_K)
+      hipLaunchKernelGGL((k_moe_mf<F(), KB(), T(), D(), (bool)BIG()>), gd, bd, p.lds, s, a, p.sets);
+  });
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -67,11 +67,29 @@ struct MoeKlArgs {
   // One token with the combine fused into the down launch (all null / 0 otherwise):
   unsigned *ctr;      // arrival counters, one per row range of the down launch
   int nctr;           // gate/up: its first workgroup zeroes ctr[0 .. nctr)
+  int ctr_cap;        // counters at ctr
   float *fuse_y;      // down: y [hidden], written by the last workgroup of each row range
   const float *wts;   // the token's routing weights [topk]
   const int *inv;     // the positions of the token's slots [topk]
   int has_shared;     // the shared expert's output sits at position Tk
 };
+
+// Output value c of a fused one-token combine: the token's routed slots in routing order, each
+// times its weight, then the shared expert's row; the sums are read at device scope (they were
+// stored by other workgroups of the same launch).
+__device__ __forceinline__ float moe_combine_value(const MoeKlArgs &a, int c) {
+  float acc = 0.f;
+  for (int j = 0; j < a.topk; ++j) {
+    const float v = __hip_atomic_load(a.out + (int64_t)a.inv[j] * a.ldo + c, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+    acc = __builtin_fmaf(a.wts[j], 0.f + v, acc);
+  }
+  if (a.has_shared)
+    acc += 0.f + __hip_atomic_load(a.out + (int64_t)a.Tk * a.ldo + c, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+  return acc;
+}
+
 bool moe_klane_ok(int fmt, int64_t hidden, int64_t ffn, int64_t tokens);
 int launch_moe_kl(const MoeKlArgs &a, int64_t k, int nslots, hipStream_t s);
 

@@ -18,6 +18,7 @@
 #include <stdlib.h>
 
 #include "tq_gemv_core.h"
+#include "tq_gemv_mf.h"
 #include "tq_launch.h"
 #include "tq_moe.h"
 #include "tq_prefill.h"
@@ -1025,12 +1026,16 @@ int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
       if (!moe_fuse_combine_ok(p) || range != nullptr) return -2;
       g.ctr = d.ctr = (unsigned *)(ws + p.off_ctr);
       g.nctr = p.nctr;  // d.nctr stays 0: only the gate/up launch clears them
+      g.ctr_cap = d.ctr_cap = p.nctr;
       d.fuse_y = fuse_y;
       d.wts = (const float *)(ws + p.off_wts);
       d.inv = (const int *)(ws + p.off_inv);
       d.has_shared = s.has_shared ? 1 : 0;
     }
-    int rc = launch_moe_kl(g, s.hidden, nslots, st);
+    // the matrix-core kernel where it takes the shape, else lanes along k (the two launches may
+    // differ: either kind of down launch counts on counters the gate/up launch cleared)
+    int rc = launch_moe_mf(g, s.hidden, nslots, st);
+    if (rc == -2) rc = launch_moe_kl(g, s.hidden, nslots, st);
     if (rc) return rc;
     d.gate_up = 0;
     d.rows = (int)s.hidden;
@@ -1039,7 +1044,8 @@ int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
     d.ldx = s.ffn;
     d.out = (float *)(ws + p.off_o);
     d.ldo = s.hidden;
-    return launch_moe_kl(d, s.ffn, nslots, st);
+    rc = launch_moe_mf(d, s.ffn, nslots, st);
+    return rc == -2 ? launch_moe_kl(d, s.ffn, nslots, st) : rc;
   }
   // gate and up
   a.mat0 = 0;

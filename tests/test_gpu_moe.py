@@ -286,6 +286,7 @@ def test_moe_one_token_lane_groups_bitwise(knobs):
     layer = synth.moe_layer(shape, t, seed=215, tag="kl-groups")
     x = synth.normal_f32(synth.rng(215, "x"), (1, shape["hidden"]))
     _case("moe-kl-groups", shape, k)
+    knobs("moe_mf", 0)  # the lanes-along-k kernel
     moe, y, _ = check_moe(t, shape, layer, x, k)
     knobs("kl_groups", 1)
     y1, _ = _run(moe, x, shape["n_experts"], k)

@@ -16,6 +16,8 @@ HOT = [
     (r"k_gemv_mfILi2E", 2),                      # batch-1 Q6_K GEMV (8-wave workgroups)
     (r"k_gemv_klILi4E", 2),          # batch-1 Q4_K GEMV, lanes along k
     (r"k_moe_klILi4E", 2),           # one-token MoE experts
+    (r"k_moe_mfILi1ELi\d+ELi\d+ELi[01]E", 4),   # one-token MoE experts, fp16 matrix cores
+    (r"k_moe_mfILi1ELi\d+ELi\d+ELi2E", 3),      # the same, two tiles in flight
     (r"k_gemv_i8ILi1E", 4),          # batch-1 Q4_K GEMV, int8 matrix cores, sliced k
     (r"k_gemv_i8ILi3E", 3),          # batch-1 Q8_0 GEMV, int8 matrix cores, sliced k
     (r"k_gemm_f32m_q8", 4),          # Q8_0 batches, fp32 matrix cores
