@@ -445,6 +445,7 @@ KNOBS = {
     "mf_kb": 26,
     "mf_deep": 27,
     "moe_mf": 28,
+    "moe_route1": 29,
 }
 
 

@@ -742,21 +742,27 @@ int tq_moe_ffn_stages(const tq_moe_desc *d, const float *x, int64_t tokens, floa
     return fail(TQ_EINVAL, "tq_moe_ffn: expert_cache is not an initialized cache state");
   hipStream_t st = (hipStream_t)stream;
   char *ws = (char *)workspace;
-  if (stages & TQ_MOE_ROUTE) {
-    if (tq::launch_moe_routing(p, d->router_w, x, ws, st)) return launched(-1, "tq_moe_ffn routing");
-    if (routing_out) {
-      const int64_t T = tokens, E = s.n_experts, k = s.top_k;
-      struct { void *dst; int64_t off, bytes; } cp[] = {
-          {routing_out->topk_ids, p.off_ids, T * k * 4}, {routing_out->topk_w, p.off_wts, T * k * 4},
-          {routing_out->logits, p.off_logits, T * E * 4}, {routing_out->counts, p.off_counts, E * 4},
-          {routing_out->offsets, p.off_offsets, (E + 1) * 4}, {routing_out->pairs, p.off_pairs, T * k * 4}};
-      for (auto &c : cp)
-        if (c.dst && hipMemcpyAsync(c.dst, ws + c.off, (size_t)c.bytes, hipMemcpyDeviceToDevice, st) != hipSuccess)
-          return fail(TQ_EDEVICE, "tq_moe_ffn: routing copy failed");
-    }
-  }
-  // one token, every stage in this call: the combine runs inside the down launch
+  // one token, every stage in this call: the combine runs inside the down launch, and (matrix-core
+  // experts) the top-k selection inside the gate/up launch
   const bool fuse = stages == TQ_MOE_ALL && !s.experts_on_host && tq::moe_fuse_combine_ok(p);
+  const bool route1 = fuse && p.route1;
+  auto copy_routing = [&]() -> int {
+    if (!routing_out) return TQ_OK;
+    const int64_t T = tokens, E = s.n_experts, k = s.top_k;
+    struct { void *dst; int64_t off, bytes; } cp[] = {
+        {routing_out->topk_ids, p.off_ids, T * k * 4}, {routing_out->topk_w, p.off_wts, T * k * 4},
+        {routing_out->logits, p.off_logits, T * E * 4}, {routing_out->counts, p.off_counts, E * 4},
+        {routing_out->offsets, p.off_offsets, (E + 1) * 4}, {routing_out->pairs, p.off_pairs, T * k * 4}};
+    for (auto &c : cp)
+      if (c.dst && hipMemcpyAsync(c.dst, ws + c.off, (size_t)c.bytes, hipMemcpyDeviceToDevice, st) != hipSuccess)
+        return fail(TQ_EDEVICE, "tq_moe_ffn: routing copy failed");
+    return TQ_OK;
+  };
+  if (stages & TQ_MOE_ROUTE) {
+    if (tq::launch_moe_routing(p, d->router_w, x, ws, st, route1))
+      return launched(-1, "tq_moe_ffn routing");
+    if (!route1 && (rc = copy_routing()) != TQ_OK) return rc;
+  }
   if (stages & TQ_MOE_EXPERTS) {
     tq::MoeExpertPtrs shared{{d->shared.gate, d->shared.up, d->shared.down}};
     if (s.experts_on_host) {
@@ -764,8 +770,9 @@ int tq_moe_ffn_stages(const tq_moe_desc *d, const float *x, int64_t tokens, floa
       if (rc != TQ_OK) return rc;
     } else {
       rc = tq::launch_moe_experts(p, reinterpret_cast<const tq::MoeExpertPtrs *>(d->experts),
-                                  shared, nullptr, x, ws, st, nullptr, fuse ? y : nullptr);
+                                  shared, nullptr, x, ws, st, nullptr, fuse ? y : nullptr, route1);
       if (rc) return launched(rc, "tq_moe_ffn experts");
+      if (route1 && (rc = copy_routing()) != TQ_OK) return rc;
     }
   }
   if ((stages & TQ_MOE_COMBINE) && !fuse) {

@@ -511,7 +511,11 @@ __global__ __launch_bounds__(BIG ? 512 : 1024) void k_gemv_mf(KlMap m, int sb, i
 // down: x = h of the slot's position, o out. With the combine fused into the down launch, each
 // workgroup then counts itself on its tile set's counter, and the last active slot to arrive adds,
 // for each row of the set, the slots in routing order and the shared expert (the combine kernel's
-// order). The gate/up launch's first workgroup clears the counters.
+// order). The gate/up launch's first workgroup clears the counters. With route1 (one token, all
+// stages in one call) the gate/up launch also makes the top-k selection: every workgroup computes
+// it from the router's partial sums before its products (a few microseconds, in place of a launch
+// of its own and the gap before the next), and workgroup 0 stores the routing outputs, which the
+// down launch reads.
 template <int FMT, int KB, int TPW, int DEPTH, bool BIG>
 __global__ __launch_bounds__(BIG ? 512 : 1024) void k_moe_mf(MoeKlArgs a, int sets) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -520,8 +524,20 @@ __global__ __launch_bounds__(BIG ? 512 : 1024) void k_moe_mf(MoeKlArgs a, int se
     for (int i = (int)threadIdx.x; i < a.nctr; i += blockDim.x)
       __hip_atomic_store(a.ctr + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int slot = a.slot0 + (int)blockIdx.x / sets, gi = (int)blockIdx.x % sets;
-  if (slot >= *a.n_active) return;
-  const int e = a.act[slot], p = a.act[a.act_stride + slot];
+  int e, p;
+  int64_t xrow;
+  if (a.route1) {
+    // one token, the selection made here: slot r < topk takes the chosen expert of rank r (its
+    // position r), slot topk the shared expert (position topk); the token's row is row 0
+    e = route_one_token(a.route, a.topk, slot, blockIdx.x == 0);
+    p = slot < a.topk ? slot : a.Tk;
+    xrow = 0;
+  } else {
+    if (slot >= *a.n_active) return;
+    e = a.act[slot];
+    p = a.act[a.act_stride + slot];
+    xrow = !a.gate_up ? p : p >= a.Tk ? p - a.Tk : a.pairs[p] / a.topk;
+  }
   if ((unsigned)e > (unsigned)a.E) return;  // never past the expert table (id E: shared expert)
   const uint8_t *w[2];
 #pragma unroll
@@ -536,8 +552,6 @@ __global__ __launch_bounds__(BIG ? 512 : 1024) void k_moe_mf(MoeKlArgs a, int se
   }
   const MoeRowMap m{w[0], w[1], a.out + (int64_t)p * a.ldo, a.gate_up, a.rows, a.row_bytes,
                     a.fuse_y != nullptr};
-  int64_t xrow = p;
-  if (a.gate_up) xrow = p >= a.Tk ? p - a.Tk : a.pairs[p] / a.topk;
   mf_body<FMT, KB, TPW, DEPTH>(m, gi, sets, (int)(a.row_bytes / MfFmt<FMT>::kBytes), 1, 0,
                                a.x + xrow * a.ldx, nullptr, Arrivals{}, lds);
   if (a.fuse_y == nullptr) return;
@@ -586,7 +600,12 @@ constexpr int kMfTpw[] = {1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16};
 struct MfPlan {
   int sb, ksplit, kb, waves, tpw, sets, lds;
 };
-static bool mf_plan(int fmt, int64_t rows, int64_t k, MfPlan &p, int slots = 1) {
+// LDS beyond the dynamic part: the kernels' own __shared__ variables (k_moe_mf: the selection's
+// logits), kept out of the 64 KB a workgroup may take.
+constexpr int kMfStaticLds = 64, kMoeMfStaticLds = 1152;
+
+static bool mf_plan(int fmt, int64_t rows, int64_t k, MfPlan &p, int slots = 1,
+                    int static_lds = kMfStaticLds) {
   if (!knob(TQ_KNOB_GEMV_MF, 1) || k % 256 != 0 || k < 256 || rows < 1 || rows >= (1ll << 30))
     return false;
   if (fmt != FMT_Q4_K && fmt != FMT_Q6_K) return false;
@@ -611,11 +630,12 @@ static bool mf_plan(int fmt, int64_t rows, int64_t k, MfPlan &p, int slots = 1) 
   const int64_t want = (ntiles * p.ksplit * slots + target - 1) / (target > 0 ? target : 1);
   int ti = 0;
   while (ti < 11 && kMfTpw[ti] < want) ++ti;
-  while (ti > 0 && mf_lds(fmt, p.sb, p.waves, kMfTpw[ti]) > 65536) --ti;
+  const int cap = 65536 - static_lds;
+  while (ti > 0 && mf_lds(fmt, p.sb, p.waves, kMfTpw[ti]) > cap) --ti;
   p.tpw = kMfTpw[ti];
   p.lds = mf_lds(fmt, p.sb, p.waves, p.tpw);
   p.sets = (int)((ntiles + p.tpw - 1) / p.tpw);
-  return p.lds <= 65536;
+  return p.lds <= cap;
 }
 
 bool mf_gemv_ok(int fmt, int64_t k) {
@@ -689,17 +709,19 @@ int launch_gemv_mf(int fmt, const KlMap &m, int64_t k, const float *x, float *pa
 
 bool moe_mf_ok(int fmt, int64_t hidden, int64_t ffn) {
   MfPlan p;
-  return fmt == FMT_Q4_K && knob(TQ_KNOB_MOE_MF, 1) && mf_plan(fmt, 16, hidden, p) &&
-         p.ksplit == 1 && mf_plan(fmt, 16, ffn, p) && p.ksplit == 1;
+  return fmt == FMT_Q4_K && knob(TQ_KNOB_MOE_MF, 1) &&
+         mf_plan(fmt, 16, hidden, p, 1, kMoeMfStaticLds) && p.ksplit == 1 &&
+         mf_plan(fmt, 16, ffn, p, 1, kMoeMfStaticLds) && p.ksplit == 1;
 }
 
 int launch_moe_mf(const MoeKlArgs &a, int64_t k, int nslots, hipStream_t s) {
   MfPlan p;
   if (!moe_mf_ok(FMT_Q4_K, k, k) || nslots < 1 || a.row_bytes != k / 256 * 144 ||
-      ((uintptr_t)a.x & 15) != 0 || a.ldx % 4 != 0 || !mf_plan(FMT_Q4_K, a.rows, k, p, nslots))
+      ((uintptr_t)a.x & 15) != 0 || a.ldx % 4 != 0 || !mf_plan(FMT_Q4_K, a.rows, k, p, nslots, kMoeMfStaticLds))
     return -2;
-  // the fused combine counts on one counter per tile set
+  // the fused combine counts on one counter per tile set; the selection is made for slots from 0
   if (a.fuse_y != nullptr && (a.ctr == nullptr || p.sets > a.ctr_cap)) return -2;
+  if (a.route1 && (!a.gate_up || a.slot0 != 0 || a.route.E > 256 || nslots > a.topk + 1)) return -2;
   const dim3 gd((unsigned)(nslots * p.sets)), bd(64 * p.waves);
   mf_variant(FMT_Q4_K, p, [&](auto F, auto KB, auto D, auto BIG, auto T) {
     if constexpr (F() == FMT_Q4_K)

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tq_route.h"
+
 namespace tq {
 
 struct MoeExpertPtrs {
@@ -33,6 +35,8 @@ struct MoePlan {
   int router_kl;   // T <= 8: the lanes-along-hidden router (slices of whole 256-value steps)
   int router_mf;   // T > 8, E >= 64: the fp32 matrix-core router (slices of 16-value steps)
   int nctr;        // T = 1: arrival counters of the fused combine (0: none)
+  int route1;      // T = 1, E <= 256, matrix-core experts: the gate/up launch can make the
+                   // selection itself (no top-k launch) when a call runs every stage
   int gu_rg, gu_ks, gu_upk, gu_waves, gu_upw;
   int d_rg, d_ks, d_upk, d_waves, d_upw;
   int64_t off_rpart, off_logits, off_ids, off_wts, off_counts, off_offsets, off_pairs, off_inv,
@@ -46,8 +50,9 @@ struct MoePlan {
 
 MoePlan plan_moe(const MoeShape &s);
 size_t group_lds_bytes(int64_t T, int64_t E);
+// route1: the router's partial sums only (the gate/up launch makes the selection).
 int launch_moe_routing(const MoePlan &p, const float *router_w, const float *x, char *ws,
-                       hipStream_t st);
+                       hipStream_t st, bool route1 = false);
 // Arguments of the lanes-along-k kernel over the experts of a one-token step (Q4_K).
 struct MoeKlArgs {
   const MoeExpertPtrs *experts;
@@ -72,6 +77,10 @@ struct MoeKlArgs {
   const float *wts;   // the token's routing weights [topk]
   const int *inv;     // the positions of the token's slots [topk]
   int has_shared;     // the shared expert's output sits at position Tk
+  // One token, gate/up launch: every workgroup makes the selection from the router's partial sums
+  // (workgroup 0 stores the routing outputs); act, n_active and pairs are not read.
+  int route1;
+  Route1Args route;
 };
 
 // Output value c of a fused one-token combine: the token's routed slots in routing order, each
@@ -106,7 +115,7 @@ struct SlotRange {
 int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
                        const MoeExpertPtrs &shared, const uint8_t *staging, const float *x,
                        char *ws, hipStream_t st, const SlotRange *range = nullptr,
-                       float *fuse_y = nullptr);
+                       float *fuse_y = nullptr, bool route1 = false);
 // One-token layers on the lanes-along-k kernels: the combine can run inside the down launch
 // (launch_moe_experts with fuse_y = y; then no launch_moe_combine).
 bool moe_fuse_combine_ok(const MoePlan &p);

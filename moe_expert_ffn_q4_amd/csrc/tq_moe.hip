@@ -23,6 +23,7 @@
 #include "tq_moe.h"
 #include "tq_prefill.h"
 #include "tq_qmm.h"
+#include "tq_route.h"
 
 namespace tq {
 
@@ -68,54 +69,7 @@ __global__ __launch_bounds__(256) void k_router(const float *__restrict__ wr, in
   }
 }
 
-// ---- top-k and softmax weights -----------------------------------------------------------------
-// One wave per token. Each lane holds the logits of experts lane, lane+64, ...
 
-constexpr int kMaxHSplit = 32;  // hidden slices of the router's partial sums
-
-__device__ __forceinline__ bool better(float va, int ea, float vb, int eb) {
-  return va > vb || (va == vb && ea < eb);
-}
-
-// Keep the better of (v, e) and the pair DPP control CTRL brings from another lane of the row.
-template <int CTRL>
-__device__ __forceinline__ void argmax_dpp(float &v, int &e) {
-  const float ov = __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-  const int oe = __builtin_amdgcn_update_dpp(0, e, CTRL, 0xF, 0xF, false);
-  if (better(ov, oe, v, e)) {
-    v = ov;
-    e = oe;
-  }
-}
-
-// The wave's best (value, index) pair, in every lane. (value, index) with distinct indices is a
-// total order, so the result does not depend on the order of the comparisons. Within each row of
-// 16 lanes by DPP (swaps within quads, then the half-row and row mirrors), then the four rows'
-// results through readlane.
-__device__ __forceinline__ void wave_argmax(float &v, int &e) {
-  argmax_dpp<0xB1>(v, e);   // quad_perm [1, 0, 3, 2]
-  argmax_dpp<0x4E>(v, e);   // quad_perm [2, 3, 0, 1]
-  argmax_dpp<0x141>(v, e);  // row_half_mirror: lane i <-> 7 - i within 8
-  argmax_dpp<0x140>(v, e);  // row_mirror: lane i <-> 15 - i within 16
-  float bv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-  int be = __builtin_amdgcn_readlane(e, 0);
-#pragma unroll
-  for (int r = 1; r < 4; ++r) {
-    const float rv =
-        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16 * r));
-    const int re = __builtin_amdgcn_readlane(e, 16 * r);
-    if (better(rv, re, bv, be)) {
-      bv = rv;
-      be = re;
-    }
-  }
-  v = bv;
-  e = be;
-}
-
-// NV = expert slots per lane (E <= 64 NV). The code is kept short (rolled loops): one wave runs
-// it cold, so instruction fetch, not arithmetic, sets its time.
 // Router for decode-sized batches (T <= 8): lanes along the hidden dimension, so a wave's loads
 // of its expert rows are coalesced 1 KB runs, all of a slice's loads in flight at once. Workgroup
 // = 4 waves x 4 expert rows, one hidden slice of hpk values (a multiple of 256); each lane adds
@@ -251,14 +205,9 @@ __global__ __launch_bounds__(64) void k_router_mf(const float *__restrict__ wr, 
     }
 }
 
-// Grouping of a one-token batch, written by the top-k wave itself (no grouping launch): the same
-// outputs as k_group, whose stable scatter reduces for T = 1 to the rank of each chosen expert
-// among the chosen ones.
-struct Group1Out {
-  int *counts, *offsets, *pairs, *inv, *act, *n_active;
-  int act_stride, has_shared;
-};
 
+// ---- top-k and softmax weights -----------------------------------------------------------------
+// One wave per token (the selection itself: tq_route.h).
 template <int NV>
 __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, int T, int E,
                                               int hsplit, int topk, int renormalize,
@@ -308,83 +257,8 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ part, in
         for (int q = 0; q < HB; ++q) v[i] += h0 + q < hsplit ? b[i][q] : 0.f;
     }
   }
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    if (lane + 64 * i < E) logits[(int64_t)t * E + lane + 64 * i] = v[i];
-    else v[i] = -INFINITY;
-  }
-  // k rounds of a wave arg-max on (value, -index); round j's id is written at once, its
-  // exp(value - first value) kept by lane j and divided by the sum at the end (no read-back)
-  unsigned taken = 0;  // bit i: expert lane + 64 i already selected
-  float sel0 = 0.f, denom = 0.f, my_w = 0.f;
-  int my_id = 0x7FFFFFFF;  // lane j < topk: the id chosen in round j
-  for (int j = 0; j < topk; ++j) {
-    float bv = -INFINITY;
-    int be = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = lane + 64 * i;
-      // a NaN logit ranks below every number (ties to the lower index as usual), so the chosen
-      // id is always an unchosen expert in [0, E); its weight then comes out NaN
-      const float vi = v[i] == v[i] ? v[i] : -INFINITY;
-      if (e < E && !(taken >> i & 1u) && better(vi, e, bv, be)) {
-        bv = vi;
-        be = e;
-      }
-    }
-    wave_argmax(bv, be);
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (j == 0) sel0 = bv;
-    const float ej = expf(bv - sel0);
-    if (lane == j) {
-      my_id = be;
-      my_w = ej;
-    }
-    if (renormalize) denom += ej;
-    if (lane == 0) ids[(int64_t)t * topk + j] = be;
-  }
-  if (!renormalize) {
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-      if (lane + 64 * i < E) s += expf(v[i] - sel0);
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-    denom = s;
-  }
-  if (lane < topk) wts[(int64_t)t * topk + lane] = my_w / denom;
-  if (g1.counts != nullptr) {  // T = 1 (the launch has a single wave at work)
-    // rank of lane j's expert among the chosen ones: its position in expert order
-    int rank = 0;
-    for (int q = 0; q < topk; ++q) rank += __builtin_amdgcn_readlane(my_id, q) < my_id ? 1 : 0;
-    if (lane < topk) {
-      g1.pairs[rank] = lane;
-      g1.inv[lane] = rank;
-      g1.act[rank] = my_id;
-      g1.act[g1.act_stride + rank] = rank;
-      g1.act[2 * g1.act_stride + rank] = 1;
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E) {
-        int below = 0;
-        for (int q = 0; q < topk; ++q) below += __builtin_amdgcn_readlane(my_id, q) < e ? 1 : 0;
-        g1.counts[e] = (int)(taken >> i & 1u);
-        g1.offsets[e] = below;
-      }
-    }
-    if (lane == 0) {
-      g1.offsets[E] = topk;
-      int na = topk;
-      if (g1.has_shared) {  // the shared expert's one position, after the routed pairs
-        g1.act[na] = E;
-        g1.act[g1.act_stride + na] = topk;
-        g1.act[2 * g1.act_stride + na] = 1;
-        ++na;
-      }
-      *g1.n_active = na;
-    }
-  }
+  int my_id, rank;
+  topk_pick<NV>(v, lane, t, E, topk, renormalize, logits, ids, wts, g1, true, my_id, rank);
 }
 
 // ---- grouping --------------------------------------------------------------------------------------
@@ -813,6 +687,8 @@ MoePlan plan_moe(const MoeShape &s) {
   // one token: arrival counters for the combine fused into the down launch, one per row range
   // (a range holds at least 4 rows, so hidden / 4 + 1 always suffice)
   p.nctr = T == 1 && p.klane ? (int)(s.hidden / 4 + 1) : 0;
+  p.route1 = T == 1 && p.klane && E <= 256 && s.top_k <= E && knob(TQ_KNOB_MOE_ROUTE1, 1) != 0 &&
+             knob(TQ_KNOB_GROUP1, 1) != 0 && moe_mf_ok(s.type, s.hidden, s.ffn);
   p.off_ctr = take((int64_t)p.nctr * 4);
   p.stage_stride = align256(s.expert_bytes);
   p.off_stage = take(s.experts_on_host ? (int64_t)(p.max_active) * p.stage_stride : 0);
@@ -856,8 +732,22 @@ static int moe_gemv_dispatch(int fmt, const MoeGemvArgs &a, int nt, int nslots, 
   }
 }
 
+// The one-token grouping outputs in the workspace (written by the top-k wave).
+static Group1Out group1_out(const MoePlan &p, char *ws) {
+  Group1Out g1{};
+  g1.counts = (int *)(ws + p.off_counts);
+  g1.offsets = (int *)(ws + p.off_offsets);
+  g1.pairs = (int *)(ws + p.off_pairs);
+  g1.inv = (int *)(ws + p.off_inv);
+  g1.act = (int *)(ws + p.off_act);
+  g1.n_active = (int *)(ws + p.off_nact);
+  g1.act_stride = p.act_stride;
+  g1.has_shared = p.s.has_shared ? 1 : 0;
+  return g1;
+}
+
 int launch_moe_routing(const MoePlan &p, const float *router_w, const float *x, char *ws,
-                       hipStream_t st) {
+                       hipStream_t st, bool route1) {
   const MoeShape &s = p.s;
   const int E = (int)s.n_experts, H = (int)s.hidden, T = (int)s.tokens, k = (int)s.top_k;
   float *rpart = (float *)(ws + p.off_rpart);
@@ -874,21 +764,13 @@ int launch_moe_routing(const MoePlan &p, const float *router_w, const float *x, 
     hipLaunchKernelGGL(k_router, rgrid, dim3(256), 0, st, router_w, E, H, x, T, p.hsplit, p.hpk,
                        rpart);
   }
+  if (route1) return hipGetLastError() == hipSuccess ? 0 : -1;  // the selection: in the gate/up launch
   {
     const dim3 g((unsigned)((T + 3) / 4));
     float *lg = (float *)(ws + p.off_logits), *wt = (float *)(ws + p.off_wts);
     int *id = (int *)(ws + p.off_ids);
     Group1Out g1{};
-    if (T == 1 && knob(TQ_KNOB_GROUP1, 1) != 0) {
-      g1.counts = (int *)(ws + p.off_counts);
-      g1.offsets = (int *)(ws + p.off_offsets);
-      g1.pairs = (int *)(ws + p.off_pairs);
-      g1.inv = (int *)(ws + p.off_inv);
-      g1.act = (int *)(ws + p.off_act);
-      g1.n_active = (int *)(ws + p.off_nact);
-      g1.act_stride = p.act_stride;
-      g1.has_shared = s.has_shared ? 1 : 0;
-    }
+    if (T == 1 && knob(TQ_KNOB_GROUP1, 1) != 0) g1 = group1_out(p, ws);
     if (E <= 64)
       hipLaunchKernelGGL(k_topk<1>, g, dim3(256), 0, st, rpart, T, E, p.hsplit, k, s.renormalize, lg, id, wt, g1);
     else if (E <= 256)
@@ -937,7 +819,8 @@ bool moe_fuse_combine_ok(const MoePlan &p) {
 
 int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
                        const MoeExpertPtrs &shared, const uint8_t *staging, const float *x,
-                       char *ws, hipStream_t st, const SlotRange *range, float *fuse_y) {
+                       char *ws, hipStream_t st, const SlotRange *range, float *fuse_y,
+                       bool route1) {
   const MoeShape &s = p.s;
   const int E = (int)s.n_experts, T = (int)s.tokens, k = (int)s.top_k;
   MoeGemvArgs a{};
@@ -1032,11 +915,26 @@ int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
       d.inv = (const int *)(ws + p.off_inv);
       d.has_shared = s.has_shared ? 1 : 0;
     }
-    // the matrix-core kernel where it takes the shape, else lanes along k (the two launches may
-    // differ: either kind of down launch counts on counters the gate/up launch cleared)
-    int rc = launch_moe_mf(g, s.hidden, nslots, st);
-    if (rc == -2) rc = launch_moe_kl(g, s.hidden, nslots, st);
-    if (rc) return rc;
+    if (route1) {  // the selection made by the gate/up launch (matrix-core kernel only)
+      if (!p.route1 || range != nullptr || staging != nullptr || a.slot0 != 0) return -2;
+      g.route1 = 1;
+      g.route.part = (const float *)(ws + p.off_rpart);
+      g.route.E = E;
+      g.route.hsplit = p.hsplit;
+      g.route.renormalize = s.renormalize;
+      g.route.logits = (float *)(ws + p.off_logits);
+      g.route.wts = (float *)(ws + p.off_wts);
+      g.route.ids = (int *)(ws + p.off_ids);
+      g.route.g1 = group1_out(p, ws);
+      const int rc = launch_moe_mf(g, s.hidden, nslots, st);
+      if (rc) return rc;
+    } else {
+      // the matrix-core kernel where it takes the shape, else lanes along k (the two launches may
+      // differ: either kind of down launch counts on counters the gate/up launch cleared)
+      int rc = launch_moe_mf(g, s.hidden, nslots, st);
+      if (rc == -2) rc = launch_moe_kl(g, s.hidden, nslots, st);
+      if (rc) return rc;
+    }
     d.gate_up = 0;
     d.rows = (int)s.hidden;
     d.row_bytes = s.ffn / 256 * 144;
@@ -1044,7 +942,7 @@ int launch_moe_experts(const MoePlan &p, const MoeExpertPtrs *experts_dev,
     d.ldx = s.ffn;
     d.out = (float *)(ws + p.off_o);
     d.ldo = s.hidden;
-    rc = launch_moe_mf(d, s.ffn, nslots, st);
+    const int rc = launch_moe_mf(d, s.ffn, nslots, st);
     return rc == -2 ? launch_moe_kl(d, s.ffn, nslots, st) : rc;
   }
   // gate and up
