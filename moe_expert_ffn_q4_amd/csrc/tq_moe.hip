@@ -75,10 +75,13 @@ __global__ __launch_bounds__(256) void k_router(const float *__restrict__ wr, in
 // = 4 waves x 4 expert rows, one hidden slice of hpk values (a multiple of 256); each lane adds
 // its 4 values per 256-value step, then a halving butterfly over the wave leaves row r's slice sum
 // in lane 16 r. Output layout as k_router's (tile 0): part[(hs * 8 + t) * E + e].
+// NT = token rows the kernel carries (8, or 1 for one token: the same sums with an eighth of the
+// activation loads and accumulators).
+template <int NT>
 __global__ __launch_bounds__(256) void k_router_kl(const float *__restrict__ wr, int E, int H,
                                                    const float *__restrict__ x, int T, int hsplit,
                                                    int hpk, float *__restrict__ part) {
-  constexpr int RW = 4, NT = 8;
+  constexpr int RW = 4;
   const int rg = blockIdx.x / hsplit, hs = blockIdx.x - rg * hsplit;
   const int lane = threadIdx.x & 63, wave = wave_index();
   const int e0 = rg * 16 + wave * RW;
@@ -752,8 +755,13 @@ int launch_moe_routing(const MoePlan &p, const float *router_w, const float *x, 
   const int E = (int)s.n_experts, H = (int)s.hidden, T = (int)s.tokens, k = (int)s.top_k;
   float *rpart = (float *)(ws + p.off_rpart);
   if (p.router_kl && ((uintptr_t)x & 15) == 0 && ((uintptr_t)router_w & 15) == 0) {
-    hipLaunchKernelGGL(k_router_kl, dim3((unsigned)(((E + 15) / 16) * p.hsplit)), dim3(256), 0, st,
-                       router_w, E, H, x, T, p.hsplit, p.hpk, rpart);
+    const dim3 grid((unsigned)(((E + 15) / 16) * p.hsplit));
+    if (T == 1)
+      hipLaunchKernelGGL(k_router_kl<1>, grid, dim3(256), 0, st, router_w, E, H, x, T, p.hsplit,
+                         p.hpk, rpart);
+    else
+      hipLaunchKernelGGL(k_router_kl<8>, grid, dim3(256), 0, st, router_w, E, H, x, T, p.hsplit,
+                         p.hpk, rpart);
   } else if (p.router_mf && ((uintptr_t)x & 15) == 0 && ((uintptr_t)router_w & 15) == 0) {
     const int64_t groups = ((T + 63) / 64) * (int64_t)p.hsplit;
     const int64_t blocks = (groups + 7) / 8 * 8 * ((E + 63) / 64);
