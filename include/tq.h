@@ -409,7 +409,8 @@ enum {
   TQ_KNOB_MF_DEEP = 27, /* that kernel: more tiles in flight (Q4_K: two ahead where a workgroup has 3+ tiles and at most 8 waves; Q6_K: one ahead at 4 blocks a wave), 1 (default) or 0 */
   TQ_KNOB_MOE_MF = 28, /* one-token Q4_K MoE step: the experts' products on the fp16 matrix cores, 1 (default) or 0 (lanes along k) */
   TQ_KNOB_MOE_ROUTE1 = 29, /* one-token MoE step on the matrix-core kernel: the top-k selection inside the gate/up launch, 1 (default) or 0 (its own launch) */
-  TQ_KNOB_COUNT = 30
+  TQ_KNOB_F32M_T4 = 30, /* fp32 matrix-core kernel: 2..4 tokens on the 4x4x1 form (1, default) or padded to 16 tokens (0) */
+  TQ_KNOB_COUNT = 31
 };
 int tq_tuning_set(int knob, int value);
 int tq_tuning_get(int knob);

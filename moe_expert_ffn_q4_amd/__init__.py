@@ -446,6 +446,7 @@ KNOBS = {
     "mf_deep": 27,
     "moe_mf": 28,
     "moe_route1": 29,
+    "f32m_t4": 30,
 }
 
 

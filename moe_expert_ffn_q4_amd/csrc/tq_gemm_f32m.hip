@@ -13,6 +13,11 @@
 // supplies token t's x and weight row t's value at k = 64 g + s in step s = 0..63 of a block, so
 // each lane dequantizes one contiguous quarter of a block of its row and reads one contiguous
 // 64-value piece of one token row; it receives D[token 4 g + i][row t].
+// Up to 4 tokens (T4) the same lanes run v_mfma_f32_4x4x1f32 instead (16 blocks of 4 x 4 x 1, the
+// same rate per cycle, none of it spent on padding tokens): lane l = 16 g + t supplies, of block
+// b = l / 4, A_b[l % 4] = token (t % 4)'s x and B_b[l % 4] = weight row t's value, both at
+// k = 64 g + s, and receives D_b[token i][row t] for i = 0..3: the sum over quarter g of the block's
+// k, so the four quarters' sums (lanes t, t + 16, t + 32, t + 48) are added once at the end.
 // Work split: a workgroup of 4 waves covers 4 x RT x 16 rows and one k slice (blocks per slice a
 // function of k only); with several slices the last workgroup of a row group adds the slices in
 // slice order (device-coherent partial stores, agent-scope counter, reset afterwards).
@@ -84,8 +89,17 @@ __device__ __forceinline__ void f32m_x16(const float *xs, int j, float (&xv)[16]
   }
 }
 
+// One step of the matrix cores: 16 tokens x 4 k x 16 rows, or (T4) 16 blocks of 4 x 1 x 4.
+template <bool T4>
+__device__ __forceinline__ f32x4m f32m_mfma(float x, float w, f32x4m c) {
+  if constexpr (T4)
+    return __builtin_amdgcn_mfma_f32_4x4x1f32(x, w, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(x, w, c, 0, 0, 0);
+}
+
 // The tile's contribution of one block: 64 steps of the matrix cores; Q6_K folds d at the end.
-template <int FMT>
+template <int FMT, bool T4>
 __device__ __forceinline__ void f32m_block(const F32mRaw<FMT> (&raw)[kF32mRT], const float *xs,
                                            int g, f32x4m (&acc)[kF32mRT]) {
   const f32x4m zero = {0.f, 0.f, 0.f, 0.f};
@@ -106,7 +120,7 @@ __device__ __forceinline__ void f32m_block(const F32mRaw<FMT> (&raw)[kF32mRT], c
 #pragma unroll
           for (int r = 0; r < kF32mRT; ++r) {
             const int q = __builtin_amdgcn_sbfe(raw[r].v[o >> 2], 8 * (o & 3), 8);
-            acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[e], d[r] * (float)q, acc[r], 0, 0, 0);
+            acc[r] = f32m_mfma<T4>(xv[e], d[r] * (float)q, acc[r]);
           }
         }
       }
@@ -158,7 +172,7 @@ __device__ __forceinline__ void f32m_block(const F32mRaw<FMT> (&raw)[kF32mRT], c
 #pragma unroll
           for (int r = 0; r < kF32mRT; ++r) {
             const float v = __builtin_fmaf(byte_to_float(q4[r], e), scf[r], nscf[r]);
-            D[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[4 * e4 + e], v, D[r], 0, 0, 0);
+            D[r] = f32m_mfma<T4>(xv[4 * e4 + e], v, D[r]);
           }
         }
       }
@@ -200,7 +214,7 @@ __device__ __forceinline__ void f32m_store(const KlMap &m, int B, int rb, int t,
 
 constexpr int kF32mXRow = 260;  // LDS floats per token row of a block (+4: rows on distinct banks)
 
-template <int FMT>
+template <int FMT, bool T4>
 __device__ __forceinline__ void f32m_body(const KlMap &m, const float *__restrict__ x, int B,
                                           int kblocks, int ksplit, int upk,
                                           float *__restrict__ partial, const Arrivals &arr,
@@ -221,22 +235,23 @@ __device__ __forceinline__ void f32m_body(const KlMap &m, const float *__restric
 #pragma unroll
   for (int r = 0; r < RT; ++r) wrow[r] = m.row(min(rbase + 16 * r + t, m.total - 1));
 
-  // token rows of a block: 16 rows x 64 float4, four per thread (rows past the batch repeat the
-  // last token; their outputs are never stored)
+  // token rows of a block: 16 (T4: 4) rows x 64 float4, four (one) per thread (rows past the
+  // batch repeat the last token; their outputs are never stored)
   const int64_t xld = (int64_t)kblocks * 64;  // float4 per token row
+  constexpr int XJ = T4 ? 1 : 4;
   // (a native vector type: HIP's float4 struct kept this array in scratch memory, and every
   // fetch waited for its loads to store them there)
-  f32x4m xn[4];
+  f32x4m xn[XJ];
   auto fetch_x = [&](int kb) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < XJ; ++j) {
       const int idx = (int)threadIdx.x + 256 * j, tok = idx >> 6, c4 = idx & 63;
       xn[j] = reinterpret_cast<const f32x4m *>(x)[(int64_t)min(tok, B - 1) * xld + kb * 64 + c4];
     }
   };
   auto put_x = [&](int b) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < XJ; ++j) {
       const int idx = (int)threadIdx.x + 256 * j, tok = idx >> 6, c4 = idx & 63;
       *reinterpret_cast<f32x4m *>(&xsh[b][tok * kF32mXRow + 4 * c4]) = xn[j];
     }
@@ -251,7 +266,7 @@ __device__ __forceinline__ void f32m_body(const KlMap &m, const float *__restric
     for (int r = 0; r < RT; ++r) raw[r].load(wrow[r], kb, g);
   };
   auto compute = [&](const F32mRaw<FMT>(&raw)[RT], int b) {
-    f32m_block<FMT>(raw, &xsh[b][t * kF32mXRow + 64 * g], g, acc);
+    f32m_block<FMT, T4>(raw, &xsh[b][(T4 ? (t & 3) : t) * kF32mXRow + 64 * g], g, acc);
   };
   // Weights one block ahead in two register sets used in turn; token rows one block ahead in
   // registers, then in the other LDS buffer. The barrier at the end of block i makes block i+1's
@@ -279,6 +294,18 @@ __device__ __forceinline__ void f32m_body(const KlMap &m, const float *__restric
     if (++i >= nb) break;
   }
 
+  if constexpr (T4) {
+    // the four k quarters: (g0 + g1) + (g2 + g3), the same bits in every lane of a row; lanes with
+    // g = 0 then hold tokens 0..3 of row t, and the others' labels (tokens 4 g + i) are never
+    // stored (B <= 4)
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[r][i] += __shfl_xor(acc[r][i], 16);
+        acc[r][i] += __shfl_xor(acc[r][i], 32);
+      }
+  }
   if (ksplit == 1) {
 #pragma unroll
     for (int r = 0; r < RT; ++r) f32m_store(m, B, rbase + 16 * r, t, g, acc[r]);
@@ -314,34 +341,38 @@ __device__ __forceinline__ void f32m_body(const KlMap &m, const float *__restric
 
 // Q8_0 fits three waves per SIMD (the compiler then reaches four); Q6_K keeps two (at three its
 // two register sets of raw runs spill).
+template <bool T4>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_gemm_f32m_q8(
     KlMap m, const float *__restrict__ x, int B, int kblocks, int ksplit, int upk,
     float *__restrict__ partial, Arrivals arr) {
   __shared__ __attribute__((aligned(16))) float xsh[2][16 * kF32mXRow];
   __shared__ int is_last;
-  f32m_body<FMT_Q8_0>(m, x, B, kblocks, ksplit, upk, partial, arr, xsh, &is_last);
+  f32m_body<FMT_Q8_0, T4>(m, x, B, kblocks, ksplit, upk, partial, arr, xsh, &is_last);
 }
 
+template <bool T4>
 __global__ __launch_bounds__(256) void k_gemm_f32m_q6(KlMap m, const float *__restrict__ x, int B,
                                                       int kblocks, int ksplit, int upk,
                                                       float *__restrict__ partial,
                                                       Arrivals arr) {
   __shared__ __attribute__((aligned(16))) float xsh[2][16 * kF32mXRow];
   __shared__ int is_last;
-  f32m_body<FMT_Q6_K>(m, x, B, kblocks, ksplit, upk, partial, arr, xsh, &is_last);
+  f32m_body<FMT_Q6_K, T4>(m, x, B, kblocks, ksplit, upk, partial, arr, xsh, &is_last);
 }
 
 // ---- host side ----------------------------------------------------------------------------------
 
-// Q8_0 at 2..16 tokens, Q6_K (dword-aligned rows: k a multiple of 512) at 4..16 tokens, k up to
-// 65536 (on the 70B-shaped layer at batch 4 Q6_K takes 0.51 ms here against 0.60 ms on the fp32
-// vector GEMV; fewer tokens stay there). TQ_KNOB_GEMM_F32M = 0 turns the path off, =2 takes every batch
-// of 2..16 (tests).
+// Q8_0 at 2..16 tokens, Q6_K (dword-aligned rows: k a multiple of 512) at 2..16 tokens (4..16
+// without the 4-token form), k up to 65536. On the 70B-shaped gate and down matrices Q6_K at 2 / 3
+// / 4 tokens takes 207 / 198 / 206 and 91 / 88 / 89 us on the 4-token form against 202 / 266 / 345
+// and 101 / 136 / 175 us on the fp32 vector GEMV (and 258-261 / 115-120 us padded to 16 tokens).
+// TQ_KNOB_GEMM_F32M = 0 turns the path off, =2 takes every batch of 2..16 (tests).
 bool f32m_ok(int fmt, int64_t k, int64_t batch) {
   const int mode = knob(TQ_KNOB_GEMM_F32M, 1);
   if (mode == 0) return false;
   if (batch < 2 || batch > 16 || k <= 0 || k > 65536) return false;
-  if (fmt == FMT_Q6_K) return k % 512 == 0 && (batch >= 4 || mode == 2);
+  const bool t4 = batch <= 4 && knob(TQ_KNOB_F32M_T4, 1) != 0;
+  if (fmt == FMT_Q6_K) return k % 512 == 0 && (batch >= 4 || t4 || mode == 2);
   return fmt == FMT_Q8_0 && k % 256 == 0;
 }
 
@@ -370,12 +401,19 @@ int launch_gemm_f32m(int fmt, const KlMap &m, int64_t k, const float *x, int64_t
   if (ksplit > 1 && groups > max_counters) return -2;
   const dim3 grid((unsigned)((groups + 7) / 8 * 8 * ksplit));
   const Arrivals arr{counters, ksplit > 1 ? call_tag() : 0ull};
-  if (fmt == FMT_Q6_K)
-    hipLaunchKernelGGL(k_gemm_f32m_q6, grid, dim3(256), 0, s, m, x, (int)batch, nblk, ksplit, upk,
-                       partial, arr);
+  const bool t4 = batch <= 4 && knob(TQ_KNOB_F32M_T4, 1) != 0;
+  if (fmt == FMT_Q6_K && t4)
+    hipLaunchKernelGGL(k_gemm_f32m_q6<true>, grid, dim3(256), 0, s, m, x, (int)batch, nblk, ksplit,
+                       upk, partial, arr);
+  else if (fmt == FMT_Q6_K)
+    hipLaunchKernelGGL(k_gemm_f32m_q6<false>, grid, dim3(256), 0, s, m, x, (int)batch, nblk,
+                       ksplit, upk, partial, arr);
+  else if (t4)
+    hipLaunchKernelGGL(k_gemm_f32m_q8<true>, grid, dim3(256), 0, s, m, x, (int)batch, nblk, ksplit,
+                       upk, partial, arr);
   else
-    hipLaunchKernelGGL(k_gemm_f32m_q8, grid, dim3(256), 0, s, m, x, (int)batch, nblk, ksplit, upk,
-                       partial, arr);
+    hipLaunchKernelGGL(k_gemm_f32m_q8<false>, grid, dim3(256), 0, s, m, x, (int)batch, nblk,
+                       ksplit, upk, partial, arr);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -24,7 +24,8 @@ tq = pytest.importorskip("moe_expert_ffn_q4_amd")
 
 @pytest.fixture(autouse=True)
 def every_batch(knobs):
-    """Every batch of 2..16 on the matrix-core path (by default Q6_K takes it from 4 tokens)."""
+    """Every batch of 2..16 on the matrix-core path (by default Q6_K takes it from 2 tokens on the
+    4-token form, from 4 without it)."""
     knobs("gemm_f32m", 2)
 
 
@@ -83,10 +84,11 @@ def test_f32m_multi_and_swiglu_match_single_gemvs(t, k):
     assert_product_close(host(gg), ref, mag, what="gate")
 
 
-def test_f32m_workspace_any_contents_and_repeatable():
+@pytest.mark.parametrize("batch", [3, 6])
+def test_f32m_workspace_any_contents_and_repeatable(batch):
     """Sliced k: a workspace of random bytes gives the bits of a zeroed one, and repeated calls
-    on the same workspace give the same bits."""
-    t, n, k, batch = "q6_k", 300, 16384, 6
+    on the same workspace give the same bits (batch 3: the 4-token form)."""
+    t, n, k = "q6_k", 300, 16384
     g = synth.rng(704, "f32m-ws")
     w, x = dev(synth.blob(t, g, n, k)), dev(synth.normal_f32(g, (batch, k)))
     nbytes = max(tq.gemv_workspace_bytes(t, n, k, batch), 256)
@@ -98,12 +100,32 @@ def test_f32m_workspace_any_contents_and_repeatable():
 
 
 @pytest.mark.parametrize("t", ["q6_k", "q8_0"])
-def test_f32m_agrees_with_fp32_gemv(knobs, t):
+@pytest.mark.parametrize("batch", [2, 8])
+def test_f32m_agrees_with_fp32_gemv(knobs, t, batch):
     """The matrix-core path and the fp32 vector GEMV differ by fp32 rounding only."""
-    n, k, batch = 200, 4096, 8
+    n, k = 200, 4096
     g = synth.rng(705, "f32m-vs", t)
     w, x = dev(synth.blob(t, g, n, k)), dev(synth.normal_f32(g, (batch, k)))
     a = host(tq.gemv(t, w, n, k, x))
     knobs("gemm_f32m", 0)
     b = host(tq.gemv(t, w, n, k, x))
+    assert np.linalg.norm(a - b) / np.linalg.norm(b) < 1e-6
+
+
+@pytest.mark.parametrize("t", ["q6_k", "q8_0"])
+@pytest.mark.parametrize("batch", [2, 3, 4])
+@pytest.mark.parametrize("n,k", [(77, 3072), (300, 16384)])
+def test_f32m_four_token_form_agrees_with_padded_form(knobs, t, batch, n, k):
+    """Up to 4 tokens the 4x4x1 form (quarters of k summed at the end) and the 16-token form
+    (TQ_KNOB_F32M_T4 = 0) differ by fp32 rounding only; both within the oracle's bar."""
+    _case("f32m-t4", t, batch, n, k)
+    g = synth.rng(706, "f32m-t4", t, batch, n, k)
+    w = synth.blob(t, g, n, k)
+    x = synth.normal_f32(g, (batch, k))
+    a = host(tq.gemv(t, dev(w), n, k, dev(x)))
+    knobs("f32m_t4", 0)
+    b = host(tq.gemv(t, dev(w), n, k, dev(x)))
+    ref, mag = oracle.gemv(t, w, n, k, x)
+    assert assert_product_close(a, ref, mag, what="4-token form") < 0.05
+    assert assert_product_close(b, ref, mag, what="16-token form") < 0.05
     assert np.linalg.norm(a - b) / np.linalg.norm(b) < 1e-6

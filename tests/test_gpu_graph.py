@@ -111,12 +111,13 @@ K_SPLIT = [("q4_k", 600, 16384, 1),   # int8 matrix cores, k slices
            ("q8_0", 700, 8192, 1),    # int8 matrix cores (Q8_0), k slices
            ("q6_k", 400, 8192, 1),    # fp16 matrix cores (Q6_K)
            ("q6_k", 300, 16384, 1),   # fp16 matrix cores (Q6_K), two k slices
-           ("q6_k", 200, 4096, 3)]    # lane-per-row GEMV, 3 tokens, k split
+           ("q6_k", 200, 4096, 3),    # fp32 matrix cores, 4-token form, k slices
+           ("q4_0", 200, 8192, 3)]    # lane-per-row GEMV, 3 tokens, k split
 
 
 def test_graph_k_split_kernels_share_a_workspace():
-    """Every kernel that adds k slices through completion counters, captured as one graph of five
-    calls on one workspace; the workspace is overwritten with random bytes before every replay."""
+    """Every kernel that adds k slices through completion counters, captured as one graph of one
+    call each on one workspace; the workspace is overwritten with random bytes before every replay."""
     _case("graph k-split kernels")
     g = synth.rng(72, "graph-split")
     cases = []
