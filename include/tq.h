@@ -410,7 +410,8 @@ enum {
   TQ_KNOB_MOE_MF = 28, /* one-token Q4_K MoE step: the experts' products on the fp16 matrix cores, 1 (default) or 0 (lanes along k) */
   TQ_KNOB_MOE_ROUTE1 = 29, /* one-token MoE step on the matrix-core kernel: the top-k selection inside the gate/up launch, 1 (default) or 0 (its own launch) */
   TQ_KNOB_F32M_T4 = 30, /* fp32 matrix-core kernel: 2..4 tokens on the 4x4x1 form (1, default) or padded to 16 tokens (0) */
-  TQ_KNOB_COUNT = 31
+  TQ_KNOB_MF_KSPLIT = 31, /* fp16 matrix-core GEMV: k slices forced on single launches (0 = from k) */
+  TQ_KNOB_COUNT = 32
 };
 int tq_tuning_set(int knob, int value);
 int tq_tuning_get(int knob);

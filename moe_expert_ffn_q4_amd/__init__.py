@@ -447,6 +447,7 @@ KNOBS = {
     "moe_mf": 28,
     "moe_route1": 29,
     "f32m_t4": 30,
+    "mf_ksplit": 31,
 }
 
 

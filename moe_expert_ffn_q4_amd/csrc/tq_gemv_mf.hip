@@ -68,7 +68,13 @@ __device__ __forceinline__ void static_for_mf(F &&f) {
   static_for_mf_(f, std::make_integer_sequence<int, N>{});
 }
 
-constexpr int kMfZero = 64;         // zero bytes at the start of LDS
+// LDS starts with zero bytes [0, 96), which the lanes whose operand rows are empty read, and the
+// operands start at byte 192. The real rows' reads sit at 0 or 64 bytes past a 128-byte boundary
+// (Q4_K) or at 64 + 32 n16 (Q6_K); the empty lanes of the same instruction read the zeros at a
+// different 16-byte slot of that boundary (Q4_K at 32, Q6_K at 0 or 64 by the group's parity), so
+// they do not land on the banks of the lanes that read data.
+constexpr int kMfZero = 192;        // bytes before the operands (zeros in [0, 96))
+constexpr uint32_t kMfZeroQ4 = 32;  // the empty Q4_K lanes' reads: [32, 96)
 constexpr int kMfBlockLds = 1024;   // one block's activation operands: 256 values x hi/lo x 2 B
 
 // The activation operands and sums of one block in LDS, and the lane's part of a block.
@@ -108,8 +114,8 @@ struct MfFmt<FMT_Q4_K> {
     L.f1 = q4k_field(2 * g + 1);
     const bool mlo = (n16 >> 1) == 2 * g, mhi = (n16 >> 1) == 2 * g + 1;
     const uint32_t own = kMfZero + (uint32_t)b0 * kMfBlockLds + 64u * n16;
-    L.a_lo = mlo ? own : 0u;
-    L.a_hi = mhi ? own : 0u;
+    L.a_lo = mlo ? own : kMfZeroQ4;
+    L.a_hi = mhi ? own : kMfZeroQ4;
     L.inc_lo = mlo ? kMfBlockLds : 0u;
     L.inc_hi = mhi ? kMfBlockLds : 0u;
     L.sum_off = kMfZero + nblk * kMfBlockLds + (uint32_t)b0 * kSumLds + 16u * g;
@@ -183,8 +189,9 @@ struct MfFmt<FMT_Q6_K> {
     Lane L;
     const bool m0 = (n16 >> 1) == g, m1 = (n16 >> 1) == 4 + g;
     const uint32_t own = kMfZero + (uint32_t)b0 * kMfBlockLds + 32u * n16;
-    L.a0 = m0 ? own : 0u;
-    L.a1 = m1 ? own : 0u;
+    const uint32_t zero = 64u * (g & 1);  // [0, 32) or [64, 96)
+    L.a0 = m0 ? own : zero;
+    L.a1 = m1 ? own : zero;
     L.incb0 = m0 ? kMfBlockLds : 0u;
     L.incb1 = m1 ? kMfBlockLds : 0u;
     L.inch0 = m0 ? 512u : 0u;
@@ -621,6 +628,11 @@ static bool mf_plan(int fmt, int64_t rows, int64_t k, MfPlan &p, int slots = 1,
       if (nblk % q == 0 && (!q6 || (nblk / q) % 2 == 0) && nblk / q <= 32) p.ksplit = q;
     if (!p.ksplit) return false;
     p.sb = nblk / p.ksplit;
+  }
+  if (const int fk = knob(TQ_KNOB_MF_KSPLIT, 0); fk > 1 && p.ksplit == 1 && nblk % fk == 0 &&
+                                                 (!q6 || (nblk / fk) % 2 == 0)) {
+    p.ksplit = fk;  // tuning: forced slices
+    p.sb = nblk / fk;
   }
   p.kb = mf_kb(fmt, p.sb);
   if (p.kb > 4) return false;
