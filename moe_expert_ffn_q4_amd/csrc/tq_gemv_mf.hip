@@ -12,11 +12,16 @@
 //     only in the k positions that hold sub-block j's weights, so one product per 32 k separates all
 //     eight sub-blocks of a block in its output rows and a block's eight products accumulate into
 //     one 16x16 fp32 tile.
-// Lane l of the wave holds weight row n = l % 16 and group g = l / 16 of every block (quant bytes
-// 32 g .. 32 g + 31, i.e. sub-blocks 2 g and 2 g + 1); product t = 0..3 takes dwords 2t, 2t + 1 of
-// the group's low nibbles (sub-block 2 g), t = 4..7 the high nibbles (sub-block 2 g + 1). The output
-// lane l then holds operand rows 4 g .. 4 g + 3 of row n, i.e. exactly the hi and lo sums of the
-// two sub-blocks whose scales and mins sit in the header that lane loaded, and folds them:
+// Lane l of the wave holds weight row n = l % 16 and, with g = l / 16, quant bytes 16 g .. 16 g + 15
+// (piece P = 0) and 64 + 16 g .. 64 + 16 g + 15 (P = 1) of every block: the four lanes of a row
+// load 64 consecutive bytes per instruction, so each cache line of a block is requested by about
+// one load (whole 32-byte groups per lane put every line under all three loads). Piece P of lane g
+// holds half g % 2 of the 32-byte group 2 P + g / 2, i.e. positions 16 (g % 2) .. + 15 of
+// sub-blocks j = 4 P + 2 (g / 2) (low nibbles) and j + 1 (high nibbles); product (P, t, nibble)
+// takes the piece's dwords 2t, 2t + 1. Operand rows 2 j, 2 j + 1 are non-zero at the k positions
+// of the lanes holding sub-block j, so the output lane l still holds operand rows 4 g .. 4 g + 3
+// of row n, i.e. exactly the hi and lo sums of sub-blocks 2 g and 2 g + 1, whose scales and mins
+// sit in the header that lane loaded, and folds them:
 //   d * 2^24 * sc_j f_j (C_hi + C_lo) - dmin * m_j S_j     (f_j = 2^-e_j)
 // (with a factor 1/16 on the high-nibble sub-block). The products are exact (an fp16 subnormal
 // quant times an 11-bit fp16 value), they add in fp32, and x enters with 22 significant bits.
@@ -105,19 +110,21 @@ struct MfFmt<FMT_Q4_K> {
   };
   struct Lane {
     Q4kField f0, f1;
-    uint32_t a_lo, a_hi, inc_lo, inc_hi, sum_off;
+    uint32_t a[4], inc[4], sum_off;  // [2 P + nibble]
   };
-  // operand rows 4g, 4g+1 take sub-block 2g (products 0..3), rows 4g+2, 4g+3 sub-block 2g+1
+  // operand row n16 (sub-block n16 / 2, hi or lo) in the products of piece P and a nibble: the
+  // row's quarters 2 (g % 2), 2 (g % 2) + 1 where that sub-block is the lane's, the zeros elsewhere
   static __device__ Lane lane(int n16, int g, int b0, int nblk) {
     Lane L;
     L.f0 = q4k_field(2 * g);
     L.f1 = q4k_field(2 * g + 1);
-    const bool mlo = (n16 >> 1) == 2 * g, mhi = (n16 >> 1) == 2 * g + 1;
-    const uint32_t own = kMfZero + (uint32_t)b0 * kMfBlockLds + 64u * n16;
-    L.a_lo = mlo ? own : kMfZeroQ4;
-    L.a_hi = mhi ? own : kMfZeroQ4;
-    L.inc_lo = mlo ? kMfBlockLds : 0u;
-    L.inc_hi = mhi ? kMfBlockLds : 0u;
+    const uint32_t own = kMfZero + (uint32_t)b0 * kMfBlockLds + 64u * n16 + 32u * (g & 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool m = (n16 >> 1) == 4 * (i >> 1) + 2 * (g >> 1) + (i & 1);
+      L.a[i] = m ? own : kMfZeroQ4;
+      L.inc[i] = m ? kMfBlockLds : 0u;
+    }
     L.sum_off = kMfZero + nblk * kMfBlockLds + (uint32_t)b0 * kSumLds + 16u * g;
     return L;
   }
@@ -126,8 +133,8 @@ struct MfFmt<FMT_Q4_K> {
   template <int B>
   static __device__ void load(const uint8_t *p, int g, Blk &b) {
     b.hdr = gload(p);
-    b.qa = gload(p + 16 + 32 * g);
-    b.qb = gload(p + 32 + 32 * g);
+    b.qa = gload(p + 16 + 16 * g);
+    b.qb = gload(p + 80 + 16 * g);
   }
   // The weight operand from the lane's two quant dwords (low or high nibbles).
   template <bool HIGH>
@@ -138,19 +145,24 @@ struct MfFmt<FMT_Q4_K> {
   // eight products into one tile, then the fold of the lane's two sub-blocks
   template <int B>
   static __device__ float block(const Blk &b, const uint8_t *lds, const Lane &L) {
-    mf_h8 A[8];
+    mf_h8 A[8];  // [2 (2 P + nibble) + t]
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      A[t] = mf_lds_op(lds, L.a_lo + B * L.inc_lo + 16 * t);
-      A[4 + t] = mf_lds_op(lds, L.a_hi + B * L.inc_hi + 16 * t);
+    for (int i = 0; i < 4; ++i) {
+      A[2 * i] = mf_lds_op(lds, L.a[i] + B * L.inc[i]);
+      A[2 * i + 1] = mf_lds_op(lds, L.a[i] + B * L.inc[i] + 16);
     }
     const mf_f4 sf = mf_lds4(lds, L.sum_off + B * kSumLds);
     const uint32_t qd[8] = {b.qa.x, b.qa.y, b.qa.z, b.qa.w, b.qb.x, b.qb.y, b.qb.z, b.qb.w};
     mf_f4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) c = mf_mfma(A[t], wop<false>(qd[2 * t], qd[2 * t + 1]), c);
+    for (int i = 0; i < 4; ++i) {
+      const int P = i >> 1;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) c = mf_mfma(A[4 + t], wop<true>(qd[2 * t], qd[2 * t + 1]), c);
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t d0 = qd[4 * P + 2 * t], d1 = qd[4 * P + 2 * t + 1];
+        c = mf_mfma(A[2 * i + t], (i & 1) ? wop<true>(d0, d1) : wop<false>(d0, d1), c);
+      }
+    }
     const uint32_t h0 = b.hdr.x;
     const float d24 = half_bits_to_float(h0) * 0x1p24f, dmin = half_bits_to_float(h0 >> 16);
     float sc_a, m_a, sc_b, m_b;
