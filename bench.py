@@ -298,7 +298,7 @@ def build_dense_model(tq, synth, torch, batch, seed):
 
 def b1_kernel(tq=None):
     """The kernel of batch-1 Q4_K products with k < 16384 under the current knobs (the fp16
-    matrix-core kernel unless switched off; the int8 one takes k >= 16384 unless its knob is 2)."""
+    matrix-core kernel unless switched off; the int8 one only when its knob is 2)."""
     if tq is None:
         import moe_expert_ffn_q4_amd as tq
     if tq.get_knob("gemv_i8") == 2:
@@ -793,7 +793,7 @@ def llama70b_bench(args, torch, tq, synth):
         # and time summed over the launches, i.e. per-launch bytes over the average launch time
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": f"Q4_K batch-1 layer (tq::{b1_kernel(tq)}; down on tq::k_gemv_i8)"},
+                     "kernel": f"Q4_K batch-1 layer (tq::{b1_kernel(tq)}; down in k slices)"},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = llama70b_cpu_baseline(host_q4k, args.cpu_seconds, tq, torch)

@@ -403,7 +403,7 @@ enum {
   TQ_KNOB_QMM_INLINE = 21, /* Q4_K GEMV of 2..16 tokens: activations split inside the product kernel: 1 on (default), 0 a split launch first */
   TQ_KNOB_QMM_INLINE_UPK = 22, /* that kernel: blocks per k slice, 2 or 4 (0: 2 for k <= 4096, else 4) */
   TQ_KNOB_QMM_INLINE_NR = 23, /* that kernel: 16-row weight tiles per wave of a product without SwiGLU, 1 (default) or 2 */
-  TQ_KNOB_GEMV_MF = 24, /* batch-1 Q4_K (k < 16384) and Q6_K GEMV on the fp16 matrix cores: 1 on (default), 0 off, 2 also Q4_K from k = 16384 in k slices */
+  TQ_KNOB_GEMV_MF = 24, /* batch-1 Q4_K and Q6_K GEMV on the fp16 matrix cores: 2 (default) also single Q4_K products from k = 16384 in k slices (given the workspace), 1 only Q4_K k < 16384 (longer rows on the int8 kernel), 0 off */
   TQ_KNOB_MF_WGS = 25, /* that kernel: workgroups the launch aims for (256: one per CU, several tiles each) */
   TQ_KNOB_MF_KB = 26, /* that kernel: blocks per wave, 1, 2 or 4 (0: from k) */
   TQ_KNOB_MF_DEEP = 27, /* that kernel: more tiles in flight (Q4_K: two ahead where a workgroup has 3+ tiles and at most 8 waves; Q6_K: one ahead at 4 blocks a wave), 1 (default) or 0 */

@@ -183,9 +183,9 @@ static bool use_i8(int fmt, int64_t rows, int64_t k, const float *x, int64_t bat
 static bool mf6_ok(int fmt, int64_t k, const float *x, int64_t batch) {
   return fmt == FMT_Q6_K && batch == 1 && ((uintptr_t)x & 15) == 0 && mf_gemv_ok(FMT_Q6_K, k);
 }
-// (Q4_K rows of 16384 and more: the int8 kernel unless TQ_KNOB_GEMV_MF is 2)
+// (Q4_K rows of 16384 and more: in k slices unless TQ_KNOB_GEMV_MF is 1, then the int8 kernel)
 static size_t mf6s_ws_bytes(int fmt, int64_t rows, int64_t k, int64_t batch) {
-  const bool q4 = fmt == FMT_Q4_K && knob(TQ_KNOB_GEMV_MF, 1) == 2;
+  const bool q4 = fmt == FMT_Q4_K && knob(TQ_KNOB_GEMV_MF, 2) == 2;
   if ((fmt != FMT_Q6_K && !q4) || batch != 1 || !mf_gemv_sliced(fmt, k)) return 0;
   return kCounterBytes + mf_workspace_bytes(fmt, rows, k);
 }

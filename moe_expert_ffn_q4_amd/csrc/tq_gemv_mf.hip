@@ -625,7 +625,7 @@ constexpr int kMfStaticLds = 64, kMoeMfStaticLds = 1152;
 
 static bool mf_plan(int fmt, int64_t rows, int64_t k, MfPlan &p, int slots = 1,
                     int static_lds = kMfStaticLds) {
-  if (!knob(TQ_KNOB_GEMV_MF, 1) || k % 256 != 0 || k < 256 || rows < 1 || rows >= (1ll << 30))
+  if (!knob(TQ_KNOB_GEMV_MF, 2) || k % 256 != 0 || k < 256 || rows < 1 || rows >= (1ll << 30))
     return false;
   if (fmt != FMT_Q4_K && fmt != FMT_Q6_K) return false;
   const int nblk = (int)(k / 256);

@@ -41,8 +41,10 @@ def test_i8_gemv_random(i8, n, k):
     assert worst < 0.05, worst  # fp32 level, far inside the bar
 
 
-def test_i8_gemv_default_threshold():
-    """Without the override the kernel takes k > 16384 (and agrees with the oracle there)."""
+def test_i8_gemv_default_threshold(knobs):
+    """Without the override, and with the fp16 matrix-core kernel limited to unsliced rows
+    (TQ_KNOB_GEMV_MF = 1), the kernel takes k > 16384 (and agrees with the oracle there)."""
+    knobs("gemv_mf", 1)
     n, k = 40, 20480
     g = synth.rng(502, "i8-default")
     w = synth.blob("q4_k", g, n, k)

@@ -263,8 +263,8 @@ def test_mf_q6_k_k_slices(knobs, n, k):
 
 @pytest.mark.parametrize("n,k", [(300, 16384), (1000, 28672)])
 def test_mf_q4_k_k_slices(knobs, n, k):
-    """Q4_K rows from k = 16384 in k slices (TQ_KNOB_GEMV_MF = 2; the default there is the int8
-    kernel): within the bar and within 2e-5 of the int8 kernel."""
+    """Q4_K rows from k = 16384 in k slices (TQ_KNOB_GEMV_MF = 2, the default; 1 sends them to
+    the int8 kernel): within the bar and within 2e-5 of the int8 kernel."""
     _case("mf q4_k slices", n, k)
     g = synth.rng(145, "mf4-slices", n, k)
     w, x = synth.blob("q4_k", g, n, k), synth.normal_f32(g, (1, k))

@@ -105,7 +105,7 @@ def test_graph_llama8b_layer(batch):
     assert_product_close(got["down"], ref, mag, what="down (last replay)")
 
 
-K_SPLIT = [("q4_k", 600, 16384, 1),   # int8 matrix cores, k slices
+K_SPLIT = [("q4_k", 600, 16384, 1),   # fp16 matrix cores (Q4_K), k slices
            ("q4_k", 900, 4096, 8),    # fp16 matrix cores, k slices
            ("q8_0", 500, 8192, 4),    # fp32 matrix cores, k slices
            ("q8_0", 700, 8192, 1),    # int8 matrix cores (Q8_0), k slices

@@ -46,10 +46,13 @@ def test_repeat_qmm_dense(n, k, batch):
     _repeat(lambda: tq.gemv("q4_k", w, n, k, x, out=y, ws=ws), y)
 
 
-@pytest.mark.parametrize("t,n,k", [("q4_k", 3000, 16384), ("q8_0", 3000, 8192)])
-def test_repeat_gemv_i8(t, n, k):
-    """k_gemv_i8 (Q4_K from k = 16384, Q8_0: one token)."""
-    _case("repeat gemv_i8", t, n, k)
+@pytest.mark.parametrize("t,n,k,mf", [("q4_k", 3000, 16384, 1), ("q8_0", 3000, 8192, 2),
+                                       ("q4_k", 3000, 16384, 2)])
+def test_repeat_gemv_i8(knobs, t, n, k, mf):
+    """k_gemv_i8 (Q4_K from k = 16384 under TQ_KNOB_GEMV_MF = 1, Q8_0: one token) and, with the
+    knob at its default 2, the k-sliced fp16 matrix-core kernel on the same Q4_K rows."""
+    _case("repeat gemv_i8", t, n, k, mf)
+    knobs("gemv_mf", mf)
     g = synth.rng(82, "rep-i8", t)
     w = dev(synth.blob(t, g, n, k))
     x = dev(synth.normal_f32(g, (1, k)))

@@ -20,7 +20,7 @@ tq = pytest.importorskip("moe_expert_ffn_q4_amd")
 
 # (type, (n, k, batch) of the first call, (n, k, batch) of the second, smaller call)
 CASES = [
-    ("q4_k", (600, 16384, 1), (300, 16384, 1)),   # int8 matrix cores, k slices
+    ("q4_k", (600, 16384, 1), (300, 16384, 1)),   # fp16 matrix cores (Q4_K), k slices
     ("q4_k", (1000, 4096, 16), (200, 2048, 8)),   # fp16 matrix cores, k slices
     ("q8_0", (700, 8192, 8), (100, 4096, 4)),     # fp32 matrix cores, k slices
     ("q6_k", (500, 8192, 1), (130, 4096, 1)),     # lane-per-row GEMV, k split
