@@ -406,7 +406,7 @@ enum {
   TQ_KNOB_GEMV_MF = 24, /* batch-1 Q4_K and Q6_K GEMV on the fp16 matrix cores: 2 (default) also single Q4_K products from k = 16384 in k slices (given the workspace), 1 only Q4_K k < 16384 (longer rows on the int8 kernel), 0 off */
   TQ_KNOB_MF_WGS = 25, /* that kernel: workgroups the launch aims for (256: one per CU, several tiles each) */
   TQ_KNOB_MF_KB = 26, /* that kernel: blocks per wave, 1, 2 or 4 (0: from k) */
-  TQ_KNOB_MF_DEEP = 27, /* that kernel: more tiles in flight (Q4_K: two ahead where a workgroup has 3+ tiles and at most 8 waves; Q6_K: one ahead at 4 blocks a wave), 1 (default) or 0 */
+  TQ_KNOB_MF_DEEP = 27, /* that kernel: more tiles in flight: 1 (default) Q6_K one ahead at 4 blocks a wave, 2 also Q4_K two ahead where a workgroup has 3+ tiles and at most 8 waves, 0 neither */
   TQ_KNOB_MOE_MF = 28, /* one-token Q4_K MoE step: the experts' products on the fp16 matrix cores, 1 (default) or 0 (lanes along k) */
   TQ_KNOB_MOE_ROUTE1 = 29, /* one-token MoE step on the matrix-core kernel: the top-k selection inside the gate/up launch, 1 (default) or 0 (its own launch) */
   TQ_KNOB_F32M_T4 = 30, /* fp32 matrix-core kernel: 2..4 tokens on the 4x4x1 form (1, default) or padded to 16 tokens (0) */

@@ -698,7 +698,7 @@ static void mf_variant(int fmt, const MfPlan &p, L &&launch) {
   if (fmt == FMT_Q6_K) {  // at most 8 waves (256 VGPRs): two buffers (235 VGPRs at 4 blocks a wave)
     if (p.kb == 2)
       by_tpw(mf_c<FMT_Q6_K>{}, mf_c<2>{}, mf_c<1>{}, mf_c<1>{});
-    else if (p.tpw >= 2 && knob(TQ_KNOB_MF_DEEP, 1))
+    else if (p.tpw >= 2 && knob(TQ_KNOB_MF_DEEP, 1) != 0)
       by_tpw(mf_c<FMT_Q6_K>{}, mf_c<4>{}, mf_c<1>{}, mf_c<1>{});
     else
       by_tpw(mf_c<FMT_Q6_K>{}, mf_c<4>{}, mf_c<0>{}, mf_c<1>{});
@@ -706,7 +706,9 @@ static void mf_variant(int fmt, const MfPlan &p, L &&launch) {
   }
   // two tiles ahead where the workgroup has several tiles and at most 8 waves (256 VGPRs a lane)
   // (three or four tiles ahead measured slower)
-  const bool deep = p.kb == 2 && p.waves <= 8 && p.tpw >= 3 && knob(TQ_KNOB_MF_DEEP, 1);
+  // (one ahead by default: two ahead, with twice the registers and half the waves per SIMD, made
+  // the 8B-shaped gate|up launch slower once each load covered a 64-byte run)
+  const bool deep = p.kb == 2 && p.waves <= 8 && p.tpw >= 3 && knob(TQ_KNOB_MF_DEEP, 1) == 2;
   if (p.kb == 1)
     by_tpw(mf_c<FMT_Q4_K>{}, mf_c<1>{}, mf_c<1>{}, mf_c<0>{});
   else if (p.kb == 2 && deep)

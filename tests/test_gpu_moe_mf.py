@@ -47,7 +47,8 @@ def test_moe_mf_one_token(knobs, shape, k):
         xd = dev(x)
         _, y, _ = check_moe(t, shape, layer, x, k, moe=moe)
         assert np.array_equal(host(moe(xd, ws=ws)), y), f"call {i}: workspace given"
-        for name, v in (("mf_wgs", 16), ("mf_wgs", 1024), ("mf_deep", 0), ("fuse_combine", 0)):
+        for name, v in (("mf_wgs", 16), ("mf_wgs", 1024), ("mf_deep", 0), ("mf_deep", 2),
+                        ("fuse_combine", 0)):
             knobs(name, v)
             got = host(moe(xd, ws=ws))
             knobs(name, -1)
